@@ -1,0 +1,26 @@
+"""Plain, slow, fp64 CPU oracle for the Hyena forward operator and its 3D variant.
+
+TEST INFRASTRUCTURE ONLY. Only tests/, __graft_entry__.smoke() and bench.py's
+cpu_baseline leg may import or run anything in this package. The product path
+(subquadratic_sequence_amd) never imports it and shares no code with it.
+"""
+from .hyena_oracle import (  # noqa: F401
+    fft_radix2,
+    causal_conv_direct,
+    causal_conv_fft,
+    posenc,
+    implicit_filter,
+    short_conv,
+    hyena_fwd,
+    hyena_fwd_sampled,
+)
+from .hyena_nd_oracle import (  # noqa: F401
+    fftn3_radix2,
+    nd_offsets,
+    nd_filter,
+    nd_gate,
+    conv3d_direct,
+    conv3d_fft,
+    hyena_nd_fwd,
+    hyena_nd_fwd_sampled,
+)

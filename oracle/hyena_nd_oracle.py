@@ -1,0 +1,171 @@
+"""fp64 oracle for the 3D HyenaND operator (channels-last grids).
+
+TEST INFRASTRUCTURE ONLY: imported by tests/, __graft_entry__.smoke() and the
+cpu_baseline leg of bench.py, never by the product path.
+
+What it computes (HyenaND explainer, gist.science, "Methodology: HyenaND"):
+  * a global convolution evaluated natively on the 3D grid (Native ND
+    Convolution), non-circular, by zero padding the input to twice the grid
+    before the FFT ("Handling Boundaries");
+  * a continuous kernel given by a coordinate MLP with sine activations times a
+    window ("Kernel Synthesis"; here an exponential radial window);
+  * input dependence at the level of the whole sample ("Input-Dependent
+    Kernels"; here a sigmoid of a linear map of each channel's grid mean of u
+    scales the whole kernel of that channel);
+  * the same projection / gating recurrence as the 1D operator, without the
+    short convolution.
+
+Geometry: the kernel is defined on signed offsets d in [-G, G) per axis (G the
+grid size of that axis) at coordinates c = d / G, and
+out[p] = sum_{q in grid} g * K[p - q] * z[q] for p in the grid.  conv3d_fft stores
+the kernel wrapped (index d mod 2G) in a (2X, 2Y, 2Z) array, which makes the
+circular convolution of the zero-padded input exact on the kept grid.
+
+Window form, MLP width, gate form, coordinate scaling and initialisation are
+conventions of this implementation: parity unpinned for those conventions.
+"""
+from __future__ import annotations
+
+import numpy as np
+
+from .hyena_oracle import fft_radix2
+
+
+def fftn3_radix2(x, inverse: bool = False) -> np.ndarray:
+    """3D DFT over the last three axes, one textbook radix-2 pass per axis."""
+    a = np.asarray(x, dtype=np.complex128)
+    for ax in (-1, -2, -3):
+        a = np.moveaxis(fft_radix2(np.moveaxis(a, ax, -1), inverse=inverse), -1, ax)
+    return a
+
+
+def nd_offsets(X: int, Y: int, Z: int) -> np.ndarray:
+    """Normalised coordinates c = d / G of the signed offsets d in [-G, G) per axis.
+
+    Returns [2X, 2Y, 2Z, 3]; entry [i, j, k] is the offset (i - X, j - Y, k - Z).
+    """
+    cx = np.arange(-X, X, dtype=np.float64) / X
+    cy = np.arange(-Y, Y, dtype=np.float64) / Y
+    cz = np.arange(-Z, Z, dtype=np.float64) / Z
+    g = np.stack(np.meshgrid(cx, cy, cz, indexing="ij"), axis=-1)
+    return g
+
+
+def nd_filter(params: dict, X: int, Y: int, Z: int, N: int, C: int) -> np.ndarray:
+    """K[n, c, i, j, k] at offset (i - X, j - Y, k - Z):
+    K = exp(-a_c |coord|_2) * (W3^T sin(W2^T sin(W1^T coord + b1) + b2) + b3)[n*C + c].
+
+    Returns [N, C, 2X, 2Y, 2Z] float64 (offset-indexed, not wrapped).
+    """
+    f = lambda k: np.asarray(params[k], dtype=np.float64)  # noqa: E731
+    c = nd_offsets(X, Y, Z)
+    a1 = np.sin(c @ f("w1") + f("b1"))
+    a2 = np.sin(a1 @ f("w2") + f("b2"))
+    o = a2 @ f("w3") + f("b3")                                       # [2X,2Y,2Z,N*C]
+    r = np.sqrt(np.sum(c * c, axis=-1))
+    win = np.exp(-r[..., None] * f("decay"))                         # [2X,2Y,2Z,C]
+    K = o.reshape(o.shape[:3] + (N, C)) * win[..., None, :]
+    return np.ascontiguousarray(np.moveaxis(K, (3, 4), (0, 1)))
+
+
+def nd_gate(u, gate_a, gate_b) -> np.ndarray:
+    """g[b, n, c] = sigmoid(a[n, c] * mean_grid(u[b, ..., c]) + b[n, c])."""
+    u = np.asarray(u, dtype=np.float64)
+    m = u.mean(axis=(1, 2, 3))                                       # [B, C]
+    s = np.asarray(gate_a, np.float64)[None] * m[:, None, :] + np.asarray(gate_b, np.float64)[None]
+    return 1.0 / (1.0 + np.exp(-s))
+
+
+def conv3d_direct(K, z) -> np.ndarray:
+    """out[..., p] = sum_{q in grid} K[..., p - q + G] * z[..., q]  (definition).
+
+    K [..., 2X, 2Y, 2Z] offset-indexed; z [..., X, Y, Z].  O(G^6); for small grids.
+    """
+    K = np.asarray(K, dtype=np.float64)
+    z = np.asarray(z, dtype=np.float64)
+    X, Y, Z = z.shape[-3:]
+    out = np.zeros(np.broadcast_shapes(K.shape[:-3], z.shape[:-3]) + (X, Y, Z))
+    for qx in range(X):
+        for qy in range(Y):
+            for qz in range(Z):
+                # offsets p - q for all p: index (p - q) + G = p + (G - q)
+                kslab = K[..., X - qx:2 * X - qx, Y - qy:2 * Y - qy, Z - qz:2 * Z - qz]
+                out += kslab * z[..., qx, qy, qz][..., None, None, None]
+    return out
+
+
+def conv3d_fft(K, z) -> np.ndarray:
+    """Same result as conv3d_direct via a (2X, 2Y, 2Z) textbook FFT.
+
+    The offset-indexed kernel is wrapped (offset d stored at d mod 2G), the input
+    is zero padded to (2X, 2Y, 2Z), and the first X*Y*Z outputs are kept.
+    """
+    K = np.asarray(K, dtype=np.float64)
+    z = np.asarray(z, dtype=np.float64)
+    X, Y, Z = z.shape[-3:]
+    Kw = np.roll(K, shift=(-X, -Y, -Z), axis=(-3, -2, -1))
+    zp = np.zeros(z.shape[:-3] + (2 * X, 2 * Y, 2 * Z))
+    zp[..., :X, :Y, :Z] = z
+    c = fftn3_radix2(fftn3_radix2(Kw) * fftn3_radix2(zp), inverse=True)
+    return c[..., :X, :Y, :Z].real
+
+
+def _nd_project(u, w_in, C, N):
+    u = np.asarray(u, dtype=np.float64)
+    p = u @ np.asarray(w_in, dtype=np.float64)                       # [B,X,Y,Z,(N+1)C]
+    blocks = [np.ascontiguousarray(np.moveaxis(p[..., i * C:(i + 1) * C], -1, 1))
+              for i in range(N + 1)]                                 # [B, C, X, Y, Z]
+    return blocks[0], blocks[1:]
+
+
+def hyena_nd_fwd(u, w_in, dskip, gate_a, gate_b, w_out, K, conv: str = "fft") -> np.ndarray:
+    """y[B, X, Y, Z, C] of the 3D operator.
+
+    u [B,X,Y,Z,C]; w_in [C,(N+1)C]; dskip, gate_a, gate_b [N,C]; w_out [C,C];
+    K [N, C, 2X, 2Y, 2Z] (nd_filter).  conv: "direct" or "fft".
+    """
+    B, X, Y, Z, C = np.shape(u)
+    N = np.shape(dskip)[0]
+    convf = conv3d_direct if conv == "direct" else conv3d_fft
+    dskip = np.asarray(dskip, dtype=np.float64)
+    g = nd_gate(u, gate_a, gate_b)                                   # [B, N, C]
+    z, xs = _nd_project(u, w_in, C, N)
+    K = np.asarray(K, dtype=np.float64)
+    for n in range(N):
+        out = np.empty_like(z)
+        for b in range(B):
+            out[b] = convf(g[b, n][:, None, None, None] * K[n], z[b])
+        z = xs[n] * out + dskip[n][None, :, None, None, None] * z
+    return np.moveaxis(z, 1, -1) @ np.asarray(w_out, dtype=np.float64)
+
+
+def hyena_nd_fwd_sampled(u, w_in, dskip, gate_a, gate_b, w_out, K, points, chunk: int = 8) -> np.ndarray:
+    """y[:, points] for full-size grids.
+
+    Orders 1..N-1 run on the whole grid with conv3d_fft (channel chunks of
+    `chunk`); the last order is evaluated only at the sampled grid points by the
+    direct sum over the grid.  points [S, 3] integer grid coordinates.
+    Returns [B, S, C].
+    """
+    B, X, Y, Z, C = np.shape(u)
+    N = np.shape(dskip)[0]
+    dskip = np.asarray(dskip, dtype=np.float64)
+    g = nd_gate(u, gate_a, gate_b)
+    z, xs = _nd_project(u, w_in, C, N)
+    K = np.asarray(K, dtype=np.float64)
+    for n in range(N - 1):
+        out = np.empty_like(z)
+        for b in range(B):
+            for c0 in range(0, C, chunk):
+                gk = g[b, n, c0:c0 + chunk][:, None, None, None] * K[n, c0:c0 + chunk]
+                out[b, c0:c0 + chunk] = conv3d_fft(gk, z[b, c0:c0 + chunk])
+        z = xs[n] * out + dskip[n][None, :, None, None, None] * z
+    n = N - 1
+    pts = np.asarray(points, dtype=np.int64)
+    res = np.empty((B, len(pts), C))
+    for i, (px, py, pz) in enumerate(pts):
+        # K offsets p - q for q over the grid: index (p - q) + G, flipped slab
+        ks = K[n][:, px + X:px:-1, py + Y:py:-1, pz + Z:pz:-1]        # [C, X, Y, Z] over q
+        c = np.einsum("cxyz,bcxyz->bc", ks, z) * g[:, n, :]
+        res[:, i, :] = xs[n][:, :, px, py, pz] * c + dskip[n][None, :] * z[:, :, px, py, pz]
+    return res @ np.asarray(w_out, dtype=np.float64)

@@ -1,0 +1,207 @@
+"""fp64 oracle for the 1D Hyena operator.
+
+TEST INFRASTRUCTURE ONLY: imported by tests/, __graft_entry__.smoke() and the
+cpu_baseline leg of bench.py, never by the product path.
+
+What it computes (every step in float64, on the stored input values upcast to
+float64, with no intermediate rounding):
+
+  1. p = u W_in, split into column blocks (v, x^1, ..., x^N).
+  2. A causal depthwise short convolution of length 3 on every projected channel.
+  3. The implicit filters h^n_c(t) = window_c(t) * FFN(PosEnc(t))[(n-1)D + c]
+     (an MLP parameterises the long filter: TWIML #690 podcast, 4:29; the filter
+     is as long as the input: TWIML #690, 5:48).
+  4. The order-N recurrence z^1 = v, z^{n+1} = x^n * (h^n conv z^n) + D^n * z^n,
+     i.e. long convolutions interleaved with data-controlled gating (Hyena
+     Hierarchy abstract). The convolution is causal (next-token prediction
+     "causal style": TWIML #690, 20:00).
+  5. y = z^{N+1} W_out.
+
+The long convolution is evaluated either directly (the O(L^2) definition; TWIML
+#690, 5:48) or through the convolution theorem with a textbook radix-2 FFT of
+size 2L (zero padding to twice the length makes the circular convolution equal
+the linear one: HyenaND explainer, Methodology, "Handling Boundaries"; FFT
+convolution: TWIML #690, 6:27).
+
+Readings of points the pages leave open (positional-encoding frequencies, FFN
+initialisation, window decays, short-conv taps, skip placement, block order) are
+conventions of this implementation; the tests pin the code to those
+conventions, but no page fixes them: parity unpinned for those conventions.
+"""
+from __future__ import annotations
+
+import numpy as np
+
+
+# ---------------------------------------------------------------------------
+# Textbook FFT
+# ---------------------------------------------------------------------------
+
+def _bit_reverse_indices(n: int) -> np.ndarray:
+    bits = n.bit_length() - 1
+    idx = np.arange(n, dtype=np.int64)
+    rev = np.zeros(n, dtype=np.int64)
+    for b in range(bits):
+        rev |= ((idx >> b) & 1) << (bits - 1 - b)
+    return rev
+
+
+def fft_radix2(x, inverse: bool = False) -> np.ndarray:
+    """Iterative radix-2 Cooley-Tukey DFT along the last axis (power-of-two length).
+
+    Forward: X[k] = sum_n x[n] exp(-2 pi i n k / n_len). Inverse uses exp(+...)
+    and divides by n_len. Bit-reversal reordering, then log2(n) stages of
+    decimation-in-time butterflies X[k] = E[k] + w^k O[k], X[k+m] = E[k] - w^k O[k].
+    """
+    a = np.asarray(x, dtype=np.complex128)
+    n = a.shape[-1]
+    if n < 1 or n & (n - 1):
+        raise ValueError("length must be a power of two")
+    lead = a.shape[:-1]
+    a = a[..., _bit_reverse_indices(n)]
+    sign = 1.0 if inverse else -1.0
+    m = 1
+    while m < n:
+        w = np.exp(sign * 1j * np.pi * np.arange(m) / m)
+        g = a.reshape(lead + (n // (2 * m), 2, m))
+        even = g[..., 0, :]
+        odd = g[..., 1, :] * w
+        a = np.stack([even + odd, even - odd], axis=-2).reshape(lead + (n,))
+        m *= 2
+    if inverse:
+        a = a / n
+    return a
+
+
+# ---------------------------------------------------------------------------
+# Long causal convolution
+# ---------------------------------------------------------------------------
+
+def causal_conv_direct(h, z) -> np.ndarray:
+    """c[..., t] = sum_{s=0..t} h[..., s] * z[..., t - s]  (definition, O(L^2)).
+
+    h and z are broadcast against each other; the last axis is time.
+    """
+    h = np.asarray(h, dtype=np.float64)
+    z = np.asarray(z, dtype=np.float64)
+    L = z.shape[-1]
+    out = np.zeros(np.broadcast_shapes(h.shape, z.shape), dtype=np.float64)
+    for s in range(L):
+        out[..., s:] += h[..., s:s + 1] * z[..., :L - s]
+    return out
+
+
+def causal_conv_fft(h, z) -> np.ndarray:
+    """Same result as causal_conv_direct, via the convolution theorem.
+
+    Both operands are zero padded to 2L, transformed with fft_radix2, multiplied
+    pointwise, transformed back, and the first L samples are kept.
+    """
+    h = np.asarray(h, dtype=np.float64)
+    z = np.asarray(z, dtype=np.float64)
+    L = z.shape[-1]
+    hp = np.concatenate([h, np.zeros(h.shape[:-1] + (L,))], axis=-1)
+    zp = np.concatenate([z, np.zeros(z.shape[:-1] + (L,))], axis=-1)
+    c = fft_radix2(fft_radix2(hp) * fft_radix2(zp), inverse=True)
+    return c[..., :L].real
+
+
+# ---------------------------------------------------------------------------
+# Implicit filter
+# ---------------------------------------------------------------------------
+
+def posenc(L: int, K: int) -> np.ndarray:
+    """Features of position t: [tau, cos(2 pi k tau) for k=1..K, sin(2 pi k tau) for k=1..K],
+    with tau = t / L.  Returns [L, 1 + 2K]."""
+    tau = np.arange(L, dtype=np.float64) / L
+    ang = 2.0 * np.pi * np.outer(tau, np.arange(1, K + 1, dtype=np.float64))
+    return np.concatenate([tau[:, None], np.cos(ang), np.sin(ang)], axis=1)
+
+
+def implicit_filter(params: dict, L: int, N: int, D: int) -> np.ndarray:
+    """h[n, c, t] = exp(-a_c t / L) * o_t[n*D + c],
+    o_t = W3^T sin(W2^T sin(W1^T e_t + b1) + b2) + b3, e_t = posenc(t).
+
+    Returns [N, D, L] float64.
+    """
+    f = lambda k: np.asarray(params[k], dtype=np.float64)  # noqa: E731
+    e = posenc(L, int(params["K"]))
+    a1 = np.sin(e @ f("w1") + f("b1"))
+    a2 = np.sin(a1 @ f("w2") + f("b2"))
+    o = a2 @ f("w3") + f("b3")                               # [L, N*D]
+    tau = np.arange(L, dtype=np.float64) / L
+    window = np.exp(-np.outer(tau, f("decay")))              # [L, D]
+    h = o.reshape(L, N, D) * window[:, None, :]
+    return np.ascontiguousarray(h.transpose(1, 2, 0))
+
+
+# ---------------------------------------------------------------------------
+# Operator
+# ---------------------------------------------------------------------------
+
+def short_conv(p, w) -> np.ndarray:
+    """s[b, t, j] = w[j,0] p[b,t,j] + w[j,1] p[b,t-1,j] + w[j,2] p[b,t-2,j], p[t<0] = 0."""
+    p = np.asarray(p, dtype=np.float64)
+    w = np.asarray(w, dtype=np.float64)
+    s = w[:, 0] * p
+    s[:, 1:] += w[:, 1] * p[:, :-1]
+    s[:, 2:] += w[:, 2] * p[:, :-2]
+    return s
+
+
+def _project_and_gate_inputs(u, w_in, short_w, D, N):
+    u = np.asarray(u, dtype=np.float64)
+    p = u @ np.asarray(w_in, dtype=np.float64)               # [B, L, (N+1)D]
+    s = short_conv(p, short_w)
+    v = np.ascontiguousarray(s[..., :D].transpose(0, 2, 1))  # [B, D, L]
+    xs = [np.ascontiguousarray(s[..., (n + 1) * D:(n + 2) * D].transpose(0, 2, 1))
+          for n in range(N)]
+    return v, xs
+
+
+def hyena_fwd(u, w_in, short_w, dskip, w_out, h, conv: str = "auto") -> np.ndarray:
+    """y[B, L, D] of the order-N operator.
+
+    u [B, L, D]; w_in [D, (N+1)D]; short_w [(N+1)D, 3]; dskip [N, D];
+    w_out [D, D]; h [N, D, L] (implicit_filter).  conv: "direct", "fft" or
+    "auto" (direct up to L = 4096, FFT above).
+    """
+    B, L, D = np.shape(u)
+    N = np.shape(dskip)[0]
+    if conv == "auto":
+        conv = "direct" if L <= 4096 else "fft"
+    convf = causal_conv_direct if conv == "direct" else causal_conv_fft
+    dskip = np.asarray(dskip, dtype=np.float64)
+    h = np.asarray(h, dtype=np.float64)
+    z, xs = _project_and_gate_inputs(u, w_in, short_w, D, N)
+    for n in range(N):
+        c = convf(h[n][None], z)
+        z = xs[n] * c + dskip[n][None, :, None] * z
+    return z.transpose(0, 2, 1) @ np.asarray(w_out, dtype=np.float64)
+
+
+def hyena_fwd_sampled(u, w_in, short_w, dskip, w_out, h, t_samples, chunk: int = 64) -> np.ndarray:
+    """y[:, t_samples, :] for long sequences.
+
+    Orders 1..N-1 are computed for every t with causal_conv_fft (channel chunks
+    of `chunk` to bound memory); the last order is evaluated only at the sampled
+    times by the direct sum c(t) = sum_{s<=t} h(s) z(t-s).  Returns [B, S, D].
+    """
+    B, L, D = np.shape(u)
+    N = np.shape(dskip)[0]
+    dskip = np.asarray(dskip, dtype=np.float64)
+    h = np.asarray(h, dtype=np.float64)
+    t_samples = np.asarray(t_samples, dtype=np.int64)
+    z, xs = _project_and_gate_inputs(u, w_in, short_w, D, N)
+    for n in range(N - 1):
+        c = np.empty_like(z)
+        for c0 in range(0, D, chunk):
+            c[:, c0:c0 + chunk] = causal_conv_fft(h[n][None, c0:c0 + chunk], z[:, c0:c0 + chunk])
+        z = xs[n] * c + dskip[n][None, :, None] * z
+    n = N - 1
+    out = np.empty((B, len(t_samples), D))
+    for i, t in enumerate(t_samples):
+        # c[b, d] = sum_{s=0..t} h[n, d, s] * z[b, d, t - s]
+        c = np.einsum("ds,bds->bd", h[n, :, :t + 1], z[:, :, t::-1])
+        out[:, i, :] = xs[n][:, :, t] * c + dskip[n][None, :] * z[:, :, t]
+    return out @ np.asarray(w_out, dtype=np.float64)

@@ -1,0 +1,15 @@
+"""Seeded synthetic inputs shared by the oracle tests, the GPU tests and the benchmark.
+
+This package holds input recipes only (shapes, value distributions, seeds and the
+storage rounding of stored inputs). It computes nothing of the operator itself.
+"""
+from .inputs import (  # noqa: F401
+    Hyena1DInputs,
+    HyenaNDInputs,
+    CONFIGS,
+    bf16_round,
+    make_1d,
+    make_nd,
+    make_config,
+    sample_positions,
+)

@@ -1,0 +1,205 @@
+"""Input recipes for the Hyena operator workloads.
+
+Every array is drawn from ``numpy.random.default_rng(seed)`` in a fixed order, in
+float64, then stored as float32. For bf16 workloads the activations and the
+projection weights are rounded to bfloat16 (round to nearest even) and kept as
+float32 arrays whose values are exactly representable in bfloat16, so that the
+oracle (which upcasts the stored values to float64) and the GPU path (which
+consumes the bfloat16 bits) see identical numbers.
+
+Draw order (1D): u, w_in, short_w, dskip, w_out, w1, b1, w2, b2, w3, b3.
+Draw order (ND): u, w_in, dskip, gate_a, gate_b, w_out, w1, b1, w2, b2, w3, b3.
+The window decays are deterministic (no draw).
+
+The workloads stand in for the pages' data: a 2k language-model context
+(Hyena Hierarchy abstract), the 64k synthetic recall length (TWIML #690, 8:34),
+a 1M single-nucleotide DNA context over a four-letter alphabet (HyenaDNA
+abstract; TWIML #690, 19:09) and 3D volumes (HyenaND explainer, Results). No
+dataset item is reproduced; only shapes and value distributions are taken.
+"""
+from __future__ import annotations
+
+import math
+from dataclasses import dataclass, field
+
+import numpy as np
+
+# |ln 1e-2| / 1.5 and |ln 1e-2| / 0.3: the window reaches 1e-2 at tau = 1.5 ... 0.3.
+_DECAY_LO = math.log(100.0) / 1.5
+_DECAY_HI = math.log(100.0) / 0.3
+
+
+def bf16_round(x: np.ndarray) -> np.ndarray:
+    """Round float values to the nearest bfloat16 (ties to even); returns float32."""
+    f = np.ascontiguousarray(x, dtype=np.float32)
+    bits = f.view(np.uint32).astype(np.uint64)
+    bits = (bits + 0x7FFF + ((bits >> 16) & 1)) & 0xFFFF0000
+    return bits.astype(np.uint32).view(np.float32).reshape(f.shape)
+
+
+def decay_rates(n: int) -> np.ndarray:
+    """Window decay rates a_c, linearly spaced over the channels (slowest first)."""
+    if n == 1:
+        return np.array([_DECAY_LO], dtype=np.float32)
+    return np.linspace(_DECAY_LO, _DECAY_HI, n).astype(np.float32)
+
+
+def _uniform(rng, shape, bound):
+    return rng.uniform(-bound, bound, size=shape)
+
+
+@dataclass
+class Hyena1DInputs:
+    B: int
+    L: int
+    D: int
+    N: int
+    K: int          # positional-encoding frequencies (features = 1 + 2K)
+    W: int          # filter FFN width
+    dtype: str      # "f32" or "bf16": storage type of u, w_in, w_out, y
+    u: np.ndarray        # [B, L, D]
+    w_in: np.ndarray     # [D, (N+1)D]  column blocks (v, x^1..x^N)
+    short_w: np.ndarray  # [(N+1)D, 3]  taps for p_t, p_{t-1}, p_{t-2}
+    dskip: np.ndarray    # [N, D]
+    w_out: np.ndarray    # [D, D]
+    w1: np.ndarray       # [1+2K, W]
+    b1: np.ndarray       # [W]
+    w2: np.ndarray       # [W, W]
+    b2: np.ndarray       # [W]
+    w3: np.ndarray       # [W, N*D]
+    b3: np.ndarray       # [N*D]
+    decay: np.ndarray    # [D]
+    meta: dict = field(default_factory=dict)
+
+    @property
+    def filter_params(self):
+        return dict(K=self.K, w1=self.w1, b1=self.b1, w2=self.w2, b2=self.b2,
+                    w3=self.w3, b3=self.b3, decay=self.decay)
+
+
+@dataclass
+class HyenaNDInputs:
+    B: int
+    X: int
+    Y: int
+    Z: int
+    C: int
+    N: int
+    W: int
+    u: np.ndarray        # [B, X, Y, Z, C]
+    w_in: np.ndarray     # [C, (N+1)C]
+    dskip: np.ndarray    # [N, C]
+    gate_a: np.ndarray   # [N, C]
+    gate_b: np.ndarray   # [N, C]
+    w_out: np.ndarray    # [C, C]
+    w1: np.ndarray       # [3, W]
+    b1: np.ndarray       # [W]
+    w2: np.ndarray       # [W, W]
+    b2: np.ndarray       # [W]
+    w3: np.ndarray       # [W, N*C]
+    b3: np.ndarray       # [N*C]
+    decay: np.ndarray    # [C]
+    meta: dict = field(default_factory=dict)
+
+    @property
+    def filter_params(self):
+        return dict(w1=self.w1, b1=self.b1, w2=self.w2, b2=self.b2,
+                    w3=self.w3, b3=self.b3, decay=self.decay)
+
+
+def make_1d(seed: int, B: int, L: int, D: int, N: int = 2, K: int = 16, W: int = 64,
+            dtype: str = "f32", u_scale: float = 1.0, tokens: int = 0) -> Hyena1DInputs:
+    """Draw one 1D workload.
+
+    u ~ N(0, 1) * u_scale, or (tokens > 0) u = E[tok] with tok uniform over
+    `tokens` symbols and E ~ N(0, 1) of shape [tokens, D].
+    w_in, w_out ~ N(0, 1/D); short_w ~ U(-0.5, 0.5); dskip ~ N(0, 1);
+    FFN weights and biases ~ U(-1/sqrt(fan_in), 1/sqrt(fan_in)).
+    """
+    if dtype not in ("f32", "bf16"):
+        raise ValueError(dtype)
+    rng = np.random.default_rng(seed)
+    store = bf16_round if dtype == "bf16" else (lambda a: np.asarray(a, dtype=np.float32))
+    if tokens > 0:
+        tok = rng.integers(0, tokens, size=(B, L))
+        table = store(rng.standard_normal((tokens, D)))
+        u = table[tok]
+    else:
+        u = store(rng.standard_normal((B, L, D)) * u_scale)
+    sd = 1.0 / math.sqrt(D)
+    w_in = store(rng.standard_normal((D, (N + 1) * D)) * sd)
+    short_w = rng.uniform(-0.5, 0.5, size=((N + 1) * D, 3)).astype(np.float32)
+    dskip = rng.standard_normal((N, D)).astype(np.float32)
+    w_out = store(rng.standard_normal((D, D)) * sd)
+    F = 1 + 2 * K
+    w1 = _uniform(rng, (F, W), 1 / math.sqrt(F)).astype(np.float32)
+    b1 = _uniform(rng, (W,), 1 / math.sqrt(F)).astype(np.float32)
+    w2 = _uniform(rng, (W, W), 1 / math.sqrt(W)).astype(np.float32)
+    b2 = _uniform(rng, (W,), 1 / math.sqrt(W)).astype(np.float32)
+    w3 = _uniform(rng, (W, N * D), 1 / math.sqrt(W)).astype(np.float32)
+    b3 = _uniform(rng, (N * D,), 1 / math.sqrt(W)).astype(np.float32)
+    return Hyena1DInputs(B=B, L=L, D=D, N=N, K=K, W=W, dtype=dtype, u=u, w_in=w_in,
+                         short_w=short_w, dskip=dskip, w_out=w_out, w1=w1, b1=b1,
+                         w2=w2, b2=b2, w3=w3, b3=b3, decay=decay_rates(D),
+                         meta=dict(seed=seed, u_scale=u_scale, tokens=tokens))
+
+
+def make_nd(seed: int, B: int, X: int, Y: int, Z: int, C: int, N: int = 2, W: int = 64,
+            u_mean_spread: float = 0.0) -> HyenaNDInputs:
+    """Draw one 3D workload (fp32).
+
+    u ~ N(0, 1), plus an optional per-(sample, channel) offset ~ N(0, u_mean_spread^2)
+    so that the channel-mean gate sees means away from zero.
+    w_in, w_out ~ N(0, 1/C); dskip, gate_a, gate_b ~ N(0, 1);
+    MLP weights and biases ~ U(-1/sqrt(fan_in), 1/sqrt(fan_in)).
+    """
+    rng = np.random.default_rng(seed)
+    u = rng.standard_normal((B, X, Y, Z, C))
+    if u_mean_spread:
+        u = u + rng.standard_normal((B, 1, 1, 1, C)) * u_mean_spread
+    u = u.astype(np.float32)
+    sd = 1.0 / math.sqrt(C)
+    w_in = (rng.standard_normal((C, (N + 1) * C)) * sd).astype(np.float32)
+    dskip = rng.standard_normal((N, C)).astype(np.float32)
+    gate_a = rng.standard_normal((N, C)).astype(np.float32)
+    gate_b = rng.standard_normal((N, C)).astype(np.float32)
+    w_out = (rng.standard_normal((C, C)) * sd).astype(np.float32)
+    w1 = _uniform(rng, (3, W), 1 / math.sqrt(3)).astype(np.float32)
+    b1 = _uniform(rng, (W,), 1 / math.sqrt(3)).astype(np.float32)
+    w2 = _uniform(rng, (W, W), 1 / math.sqrt(W)).astype(np.float32)
+    b2 = _uniform(rng, (W,), 1 / math.sqrt(W)).astype(np.float32)
+    w3 = _uniform(rng, (W, N * C), 1 / math.sqrt(W)).astype(np.float32)
+    b3 = _uniform(rng, (N * C,), 1 / math.sqrt(W)).astype(np.float32)
+    return HyenaNDInputs(B=B, X=X, Y=Y, Z=Z, C=C, N=N, W=W, u=u, w_in=w_in, dskip=dskip,
+                         gate_a=gate_a, gate_b=gate_b, w_out=w_out, w1=w1, b1=b1, w2=w2,
+                         b2=b2, w3=w3, b3=b3, decay=decay_rates(C),
+                         meta=dict(seed=seed, u_mean_spread=u_mean_spread))
+
+
+# The five workloads. Names describe what each is; seeds are 1..5 in this order.
+CONFIGS = {
+    "order2_f32_L1k_D64": dict(kind="1d", seed=1, B=1, L=1024, D=64, N=2, K=8, dtype="f32"),
+    "order2_bf16_B8_L2k_D768": dict(kind="1d", seed=2, B=8, L=2048, D=768, N=2, K=16,
+                                    dtype="bf16", u_scale=1 / math.sqrt(768)),
+    "order2_bf16_L64k_D768": dict(kind="1d", seed=3, B=1, L=65536, D=768, N=2, K=16,
+                                  dtype="bf16", u_scale=1 / math.sqrt(768)),
+    "order2_bf16_L1M_D256_dna": dict(kind="1d", seed=4, B=1, L=1 << 20, D=256, N=2, K=16,
+                                     dtype="bf16", tokens=4),
+    "nd3d_f32_B2_C128_64cube": dict(kind="nd", seed=5, B=2, X=64, Y=64, Z=64, C=128, N=2),
+}
+
+
+def make_config(name: str):
+    cfg = dict(CONFIGS[name])
+    kind = cfg.pop("kind")
+    if kind == "1d":
+        return make_1d(**cfg)
+    return make_nd(**cfg)
+
+
+def sample_positions(L: int, count: int, seed: int = 0) -> np.ndarray:
+    """Sorted sample of time indices: both ends, the first few, and uniform draws."""
+    rng = np.random.default_rng(10_000 + seed)
+    fixed = [0, 1, 2, L // 2, L - 2, L - 1]
+    extra = rng.integers(0, L, size=max(0, count - len(fixed)))
+    return np.unique(np.clip(np.concatenate([fixed, extra]), 0, L - 1)).astype(np.int64)

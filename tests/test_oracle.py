@@ -1,0 +1,386 @@
+"""Pins of the fp64 oracle against things other than itself.
+
+Each test checks the oracle against a library routine (numpy.fft, numpy.convolve,
+numpy.cumsum, scipy.special.expit), a closed form, a brute-force sum, or an
+invariant the pages state (causality; zero padding to twice the length makes the
+FFT convolution non-circular; the convolution theorem).
+"""
+import math
+
+import numpy as np
+import pytest
+import scipy.special
+
+import oracle
+from synth import make_1d, make_nd
+
+RNG = np.random.default_rng(1234)
+
+
+def rel(a, b):
+    return float(np.max(np.abs(a - b)) / max(np.max(np.abs(b)), 1e-300))
+
+
+# --------------------------------------------------------------------------- FFT
+
+@pytest.mark.parametrize("n", [1, 2, 4, 8, 16, 64, 256, 1024, 4096])
+def test_fft_matches_numpy(n):
+    x = RNG.standard_normal((3, n)) + 1j * RNG.standard_normal((3, n))
+    assert rel(oracle.fft_radix2(x), np.fft.fft(x, axis=-1)) < 1e-12
+    assert rel(oracle.fft_radix2(x, inverse=True), np.fft.ifft(x, axis=-1)) < 1e-12
+
+
+def test_fft_parseval_and_hermitian():
+    x = RNG.standard_normal((2, 512))
+    X = oracle.fft_radix2(x)
+    n = x.shape[-1]
+    assert np.allclose(np.sum(np.abs(x) ** 2, -1), np.sum(np.abs(X) ** 2, -1) / n, rtol=1e-12)
+    k = np.arange(1, n)
+    assert np.allclose(X[:, n - k], np.conj(X[:, k]), rtol=0, atol=1e-10)
+
+
+def test_fft_rejects_non_power_of_two():
+    with pytest.raises(ValueError):
+        oracle.fft_radix2(np.ones(12))
+
+
+def test_fftn3_matches_numpy():
+    x = RNG.standard_normal((2, 4, 8, 16)) + 1j * RNG.standard_normal((2, 4, 8, 16))
+    assert rel(oracle.fftn3_radix2(x), np.fft.fftn(x, axes=(-3, -2, -1))) < 1e-12
+    assert rel(oracle.fftn3_radix2(x, inverse=True), np.fft.ifftn(x, axes=(-3, -2, -1))) < 1e-12
+
+
+# ------------------------------------------------------------------ convolution
+
+@pytest.mark.parametrize("L", [1, 2, 5, 37, 128])
+def test_direct_conv_is_truncated_np_convolve(L):
+    h = RNG.standard_normal((4, L))
+    z = RNG.standard_normal((4, L))
+    got = oracle.causal_conv_direct(h, z)
+    want = np.stack([np.convolve(h[i], z[i])[:L] for i in range(4)])
+    assert rel(got, want) < 1e-13
+
+
+@pytest.mark.parametrize("L", [1, 2, 4, 16, 128, 1024, 4096])
+def test_fft_conv_equals_direct_conv(L):
+    h = RNG.standard_normal((3, L))
+    z = RNG.standard_normal((2, 3, L))
+    assert rel(oracle.causal_conv_fft(h, z), oracle.causal_conv_direct(h, z)) < 1e-11
+
+
+def test_without_padding_the_fft_conv_wraps():
+    # Circular convolution of length L (no padding) = causal conv + wrapped tail.
+    L = 64
+    h = RNG.standard_normal(L)
+    z = RNG.standard_normal(L)
+    circ = oracle.fft_radix2(oracle.fft_radix2(h) * oracle.fft_radix2(z), inverse=True).real
+    full = np.convolve(h, z)
+    assert np.allclose(circ, full[:L] + np.concatenate([full[L:], [0.0]]), atol=1e-10)
+    assert not np.allclose(circ, oracle.causal_conv_direct(h, z), atol=1e-3)
+
+
+def test_constant_filter_is_prefix_sum():
+    z = RNG.standard_normal((2, 100))
+    assert rel(oracle.causal_conv_direct(np.ones(100), z), np.cumsum(z, axis=-1)) < 1e-13
+
+
+def test_geometric_filter_is_first_order_scan():
+    L, r = 256, 0.97
+    z = RNG.standard_normal(L)
+    c = np.zeros(L)
+    acc = 0.0
+    for t in range(L):
+        acc = r * acc + z[t]
+        c[t] = acc
+    h = r ** np.arange(L)
+    assert rel(oracle.causal_conv_fft(h, z), c) < 1e-11
+
+
+# ---------------------------------------------------------------- filter / PosEnc
+
+def test_posenc_frequencies_and_order():
+    L, K = 64, 5
+    e = oracle.posenc(L, K)
+    assert e.shape == (L, 1 + 2 * K)
+    assert np.allclose(e[:, 0], np.arange(L) / L)
+    for k in range(1, K + 1):
+        Fc = np.fft.fft(e[:, k])
+        Fs = np.fft.fft(e[:, K + k])
+        expect_c = np.zeros(L, complex)
+        expect_c[k] = expect_c[L - k] = L / 2
+        expect_s = np.zeros(L, complex)
+        expect_s[k], expect_s[L - k] = -1j * L / 2, 1j * L / 2
+        assert np.allclose(Fc, expect_c, atol=1e-9)
+        assert np.allclose(Fs, expect_s, atol=1e-9)
+
+
+def _filter_params(K, W, N, D, seed=0):
+    inp = make_1d(seed, 1, 8, D, N=N, K=K, W=W)
+    return dict(inp.filter_params)
+
+
+def test_window_decays_and_unit_start():
+    L, N, D = 256, 2, 8
+    p = _filter_params(4, 16, N, D)
+    p["w3"] = np.zeros_like(p["w3"])
+    p["b3"] = np.ones_like(p["b3"])
+    h = oracle.implicit_filter(p, L, N, D)
+    assert np.allclose(h[:, :, 0], 1.0)
+    ratio = h[:, :, 1:] / h[:, :, :-1]
+    assert np.allclose(ratio, ratio[:, :, :1])          # geometric in t
+    a = -np.log(ratio[0, :, 0]) * L
+    # decays spread from |ln 1e-2|/1.5 (first channel) to |ln 1e-2|/0.3 (last)
+    assert math.isclose(a[0] * 1.5, math.log(100), rel_tol=1e-6)
+    assert math.isclose(a[-1] * 0.3, math.log(100), rel_tol=1e-6)
+    assert np.all(np.diff(a) > 0)
+
+
+def test_filter_ffn_structure():
+    # w1 = 0, b1 = pi/2 -> first activation is 1; w2 = 0, b2 = beta -> second is sin(beta);
+    # output = sin(beta) * sum_j w3[j, :] + b3, times the window.
+    L, N, D, W = 32, 2, 4, 8
+    p = _filter_params(3, W, N, D)
+    p["w1"] = np.zeros_like(p["w1"])
+    p["b1"] = np.full_like(p["b1"], np.pi / 2)
+    p["w2"] = np.zeros_like(p["w2"])
+    p["b2"] = np.full_like(p["b2"], 0.3)
+    p["decay"] = np.zeros_like(p["decay"])
+    h = oracle.implicit_filter(p, L, N, D)
+    o = math.sin(0.3) * p["w3"].astype(np.float64).sum(0) + p["b3"]
+    assert np.allclose(h, o.reshape(N, D)[:, :, None] * np.ones(L), atol=1e-6)
+
+
+def test_filter_periodic_when_only_one_frequency_is_fed():
+    # Only the cos_2 and sin_2 features reach the FFN -> filter periodic with period L/2
+    # (window off); only cos_2 -> even around t = 0 (h(t) = h(L - t)).
+    L, K, N, D = 64, 4, 1, 4
+    p = _filter_params(K, 8, N, D)
+    p["decay"] = np.zeros_like(p["decay"])
+    keep = np.zeros_like(p["w1"])
+    keep[2] = p["w1"][2]
+    keep[K + 2] = p["w1"][K + 2]
+    p["w1"] = keep
+    h = oracle.implicit_filter(p, L, N, D)
+    assert np.allclose(h[..., : L // 2], h[..., L // 2:], atol=1e-12)
+    only_cos = np.zeros_like(keep)
+    only_cos[2] = keep[2]
+    p["w1"] = only_cos
+    h = oracle.implicit_filter(p, L, N, D)
+    t = np.arange(1, L)
+    assert np.allclose(h[..., t], h[..., L - t], atol=1e-12)
+
+
+# ---------------------------------------------------------------------- operator
+
+def _small(seed=7, B=2, L=64, D=8, N=2, K=4):
+    return make_1d(seed, B, L, D, N=N, K=K, W=16)
+
+
+def _proj_blocks(inp):
+    """Projected and short-convolved blocks computed with numpy.convolve."""
+    p = inp.u.astype(np.float64) @ inp.w_in.astype(np.float64)
+    B, L, J = p.shape
+    s = np.empty_like(p)
+    for b in range(B):
+        for j in range(J):
+            s[b, :, j] = np.convolve(p[b, :, j], inp.short_w[j].astype(np.float64))[:L]
+    D = inp.D
+    return [s[..., i * D:(i + 1) * D] for i in range(inp.N + 1)]
+
+
+def _run(inp, h, dskip=None, conv="direct", w_in=None):
+    return oracle.hyena_fwd(inp.u, inp.w_in if w_in is None else w_in, inp.short_w,
+                            inp.dskip if dskip is None else dskip, inp.w_out, h, conv=conv)
+
+
+def test_delta_filter_reduces_to_products():
+    inp = _small()
+    h = np.zeros((inp.N, inp.D, inp.L))
+    h[:, :, 0] = 1.0
+    y = _run(inp, h, dskip=np.zeros((inp.N, inp.D)))
+    v, x1, x2 = _proj_blocks(inp)
+    assert rel(y, (v * x1 * x2) @ inp.w_out.astype(np.float64)) < 1e-12
+
+
+def test_block_order_first_gate_is_block_one():
+    inp = _small()
+    h = np.zeros((inp.N, inp.D, inp.L))
+    h[0, :, 0] = 1.0
+    dskip = np.zeros((inp.N, inp.D))
+    dskip[1] = 1.0
+    y = _run(inp, h, dskip=dskip)
+    v, x1, _ = _proj_blocks(inp)
+    assert rel(y, (v * x1) @ inp.w_out.astype(np.float64)) < 1e-12
+
+
+def test_skip_only():
+    inp = _small()
+    y = _run(inp, np.zeros((inp.N, inp.D, inp.L)))
+    v = _proj_blocks(inp)[0]
+    d = inp.dskip.astype(np.float64)
+    assert rel(y, (d[0] * d[1] * v) @ inp.w_out.astype(np.float64)) < 1e-12
+
+
+def test_order_one_constant_filter_is_gated_prefix_sum():
+    inp = _small(N=1)
+    h = np.ones((1, inp.D, inp.L))
+    y = _run(inp, h, dskip=np.zeros((1, inp.D)))
+    v, x1 = _proj_blocks(inp)
+    assert rel(y, (x1 * np.cumsum(v, axis=1)) @ inp.w_out.astype(np.float64)) < 1e-12
+
+
+def test_causality():
+    inp = _small(L=48)
+    h = oracle.implicit_filter(inp.filter_params, inp.L, inp.N, inp.D)
+    y0 = _run(inp, h)
+    t0 = 20
+    u2 = inp.u.copy()
+    u2[:, t0] += 3.0
+    y1 = oracle.hyena_fwd(u2, inp.w_in, inp.short_w, inp.dskip, inp.w_out, h, conv="direct")
+    assert np.array_equal(y0[:, :t0], y1[:, :t0])
+    assert not np.allclose(y0[:, t0], y1[:, t0])
+
+
+def test_linear_in_v_block_for_fixed_gates():
+    inp = _small()
+    h = oracle.implicit_filter(inp.filter_params, inp.L, inp.N, inp.D)
+    D = inp.D
+    wa = inp.w_in.astype(np.float64).copy()
+    wb = wa.copy()
+    split = RNG.standard_normal((D, D))
+    wa[:, :D] = split
+    wb[:, :D] = inp.w_in[:, :D] - split
+    ysum = _run(inp, h, w_in=wa) + _run(inp, h, w_in=wb)
+    assert rel(ysum, _run(inp, h)) < 1e-11
+    w3 = inp.w_in.astype(np.float64).copy()
+    w3[:, :D] *= -2.5
+    assert rel(_run(inp, h, w_in=w3), -2.5 * _run(inp, h)) < 1e-12
+
+
+def test_fft_and_direct_paths_agree_on_operator():
+    inp = _small(L=256, D=16, N=3)
+    h = oracle.implicit_filter(inp.filter_params, inp.L, inp.N, inp.D)
+    assert rel(_run(inp, h, conv="fft"), _run(inp, h, conv="direct")) < 1e-11
+
+
+def test_sampled_equals_full():
+    inp = _small(L=128, D=8, N=2)
+    h = oracle.implicit_filter(inp.filter_params, inp.L, inp.N, inp.D)
+    full = _run(inp, h)
+    ts = np.array([0, 1, 2, 63, 100, 127])
+    samp = oracle.hyena_fwd_sampled(inp.u, inp.w_in, inp.short_w, inp.dskip, inp.w_out, h, ts, chunk=3)
+    assert rel(samp, full[:, ts]) < 1e-11
+
+
+# ---------------------------------------------------------------------------- ND
+
+def test_conv3d_fft_equals_direct_8cube():
+    K = RNG.standard_normal((2, 16, 16, 16))
+    z = RNG.standard_normal((2, 8, 8, 8))
+    assert rel(oracle.conv3d_fft(K, z), oracle.conv3d_direct(K, z)) < 1e-11
+
+
+def test_conv3d_non_cubic_grid():
+    K = RNG.standard_normal((8, 4, 16))
+    z = RNG.standard_normal((4, 2, 8))
+    assert rel(oracle.conv3d_fft(K, z), oracle.conv3d_direct(K, z)) < 1e-11
+
+
+def test_conv3d_delta_kernel_is_identity():
+    X = Y = Z = 8
+    K = np.zeros((2 * X, 2 * Y, 2 * Z))
+    K[X, Y, Z] = 1.0
+    z = RNG.standard_normal((X, Y, Z))
+    assert np.allclose(oracle.conv3d_direct(K, z), z, atol=0)
+    assert rel(oracle.conv3d_fft(K, z), z) < 1e-12
+
+
+def test_conv3d_separable_is_product_of_1d_convs():
+    X, Y, Z = 8, 4, 8
+    a, b, c = RNG.standard_normal(2 * X), RNG.standard_normal(2 * Y), RNG.standard_normal(2 * Z)
+    f, g, k = RNG.standard_normal(X), RNG.standard_normal(Y), RNG.standard_normal(Z)
+    K = a[:, None, None] * b[None, :, None] * c[None, None, :]
+    z = f[:, None, None] * g[None, :, None] * k[None, None, :]
+    ox = np.convolve(a, f)[X:2 * X]
+    oy = np.convolve(b, g)[Y:2 * Y]
+    oz = np.convolve(c, k)[Z:2 * Z]
+    want = ox[:, None, None] * oy[None, :, None] * oz[None, None, :]
+    assert rel(oracle.conv3d_direct(K, z), want) < 1e-12
+    assert rel(oracle.conv3d_fft(K, z), want) < 1e-11
+
+
+def test_nd_filter_radial_window():
+    X = Y = Z = 8
+    N, C = 2, 4
+    inp = make_nd(3, 1, X, Y, Z, C, N=N, W=8)
+    p = dict(inp.filter_params)
+    p["w3"] = np.zeros_like(p["w3"])
+    p["b3"] = np.ones_like(p["b3"])
+    K = oracle.nd_filter(p, X, Y, Z, N, C)
+    a = inp.decay.astype(np.float64)
+    assert np.allclose(K[:, :, X, Y, Z], 1.0)                      # offset 0
+    assert np.allclose(K[0, :, X + X // 2, Y, Z], np.exp(-a * 0.5))  # offset (G/2, 0, 0)
+    assert np.allclose(K[0, :, X, Y, Z + 3], np.exp(-a * 3 / Z))
+    # radial: symmetric under sign flips and axis permutations
+    inner = K[..., 1:, 1:, 1:]
+    assert np.allclose(inner, inner[..., ::-1, ::-1, ::-1])
+    assert np.allclose(inner, np.swapaxes(inner, -1, -3))
+
+
+def test_nd_gate_closed_form():
+    B, C, N = 2, 5, 2
+    m = RNG.standard_normal((B, C))
+    u = np.broadcast_to(m[:, None, None, None, :], (B, 4, 4, 4, C))
+    a = RNG.standard_normal((N, C))
+    b = RNG.standard_normal((N, C))
+    g = oracle.nd_gate(u, a, b)
+    want = scipy.special.expit(a[None] * m[:, None, :] + b[None])
+    assert rel(g, want) < 1e-14
+
+
+def _nd_blocks(inp):
+    p = inp.u.astype(np.float64) @ inp.w_in.astype(np.float64)
+    C = inp.C
+    return [p[..., i * C:(i + 1) * C] for i in range(inp.N + 1)]
+
+
+def test_nd_delta_kernel_closed_form():
+    X = Y = Z = 4
+    inp = make_nd(4, 2, X, Y, Z, 3, N=2, W=8, u_mean_spread=0.7)
+    K = np.zeros((2, 3, 2 * X, 2 * Y, 2 * Z))
+    K[:, :, X, Y, Z] = 1.0
+    y = oracle.hyena_nd_fwd(inp.u, inp.w_in, np.zeros((2, 3)), inp.gate_a, inp.gate_b,
+                            inp.w_out, K, conv="direct")
+    v, x1, x2 = _nd_blocks(inp)
+    m = inp.u.astype(np.float64).mean(axis=(1, 2, 3))
+    g1 = scipy.special.expit(inp.gate_a[0] * m + inp.gate_b[0])[:, None, None, None, :]
+    g2 = scipy.special.expit(inp.gate_a[1] * m + inp.gate_b[1])[:, None, None, None, :]
+    want = (x2 * g2 * x1 * g1 * v) @ inp.w_out.astype(np.float64)
+    assert rel(y, want) < 1e-12
+
+
+def test_nd_fft_equals_direct_and_sampled_equals_full():
+    X = Y = Z = 4
+    inp = make_nd(5, 2, X, Y, Z, 4, N=2, W=8, u_mean_spread=0.5)
+    K = oracle.nd_filter(inp.filter_params, X, Y, Z, 2, 4)
+    args = (inp.u, inp.w_in, inp.dskip, inp.gate_a, inp.gate_b, inp.w_out, K)
+    yd = oracle.hyena_nd_fwd(*args, conv="direct")
+    yf = oracle.hyena_nd_fwd(*args, conv="fft")
+    assert rel(yf, yd) < 1e-11
+    pts = np.array([[0, 0, 0], [3, 3, 3], [1, 2, 3], [3, 0, 2]])
+    ys = oracle.hyena_nd_fwd_sampled(*args, pts, chunk=3)
+    assert rel(ys, yd[:, pts[:, 0], pts[:, 1], pts[:, 2]]) < 1e-11
+
+
+def test_nd_causality_free_but_translation_equivariant_interior():
+    # A kernel supported near offset 0 and an input supported in the middle: shifting
+    # the input by one voxel shifts the output by one voxel (away from the borders).
+    X = Y = Z = 8
+    K = np.zeros((16, 16, 16))
+    K[X - 1:X + 2, Y - 1:Y + 2, Z - 1:Z + 2] = RNG.standard_normal((3, 3, 3))
+    z = np.zeros((X, Y, Z))
+    z[3, 3, 3] = 1.0
+    z[3, 4, 3] = -2.0
+    o1 = oracle.conv3d_fft(K, z)
+    o2 = oracle.conv3d_fft(K, np.roll(z, 1, axis=0))
+    assert np.allclose(np.roll(o1, 1, axis=0)[1:-1], o2[1:-1], atol=1e-12)
