@@ -1,0 +1,153 @@
+#!/usr/bin/env python3
+"""Benchmark of the Hyena forward hot path on one MI355X.
+
+    python bench.py [--steps K] [--warmup W] [--workload NAME] [--no-cpu-baseline]
+
+One step = one hyena_fwd call (in-projection, short convolutions, all orders of
+long FFT convolution with gating and skip, out-projection) over one batch of
+synthetic input already resident in HBM. The implicit filters are generated and
+their spectra cached once before timing (one cache per layer, reused by every
+call). Prints one JSON line on stdout; progress goes to stderr.
+
+Roofline: the FFT long-convolution stage is the dominant kernel sequence. Its
+duration comes from HIP events recorded on the launch stream around that stage
+(hyena_fwd_profiled), averaged over the timed steps; the algorithmic bytes per
+order are B*L*D*3*s + 8*D*(L+1) (read z^n and x^n, write z^{n+1}, read the
+filter spectrum), s the storage size of an activation.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+DEFAULT_WORKLOAD = "order2_bf16_L64k_D768"
+METRIC = "Hyena fwd tokens/sec at L=64k,D=768 (1 GPU); FFT-conv HBM GB/s % of peak"
+HBM_PEAK_GBS = 8000.0
+
+
+def log(msg):
+    print(msg, file=sys.stderr, flush=True)
+
+
+def conv_alg_bytes(B, L, D, N, s, lds_regime: bool) -> float:
+    if lds_regime:
+        # all orders fused on chip: read v and x^1..x^N, write z^{N+1}, read N spectra
+        return (N + 1) * B * L * D * s + B * L * D * s + N * 8.0 * D * (L + 1)
+    return N * (3.0 * B * L * D * s + 8.0 * D * (L + 1))
+
+
+def cpu_baseline(inp, budget_tokens: int):
+    """fp64 oracle on the first `budget_tokens` positions of the same workload.
+
+    By causality y[:, :T] depends only on u[:, :T] and on the first T filter taps,
+    so the oracle runs on that prefix with the full-length filters truncated to T
+    taps, FFT convolution path, one thread."""
+    import oracle
+    from threadpoolctl import threadpool_limits
+    T = min(budget_tokens, inp.L)
+    with threadpool_limits(limits=1):
+        t0 = time.perf_counter()
+        h = oracle.implicit_filter(inp.filter_params, inp.L, inp.N, inp.D)[:, :, :T]
+        oracle.hyena_fwd(inp.u[:, :T], inp.w_in, inp.short_w, inp.dskip, inp.w_out, h, conv="fft")
+        dt = time.perf_counter() - t0
+    return {"value": inp.B * T / dt, "unit": "tokens/s", "cores": 1, "kind": "oracle",
+            "sample": f"first {T} of {inp.L} positions x B={inp.B} (all {inp.D} channels), fp64 numpy, "
+                      f"FFT path, 1 thread, {dt:.1f} s"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default=DEFAULT_WORKLOAD)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-tokens", type=int, default=4096)
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only (asked for --gpus {args.gpus}); this path is built and "
+              f"measured on a single MI355X.", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import subquadratic_sequence_amd as hs
+    from synth import CONFIGS, make_config
+
+    cfg = CONFIGS[args.workload]
+    if cfg["kind"] != "1d":
+        raise SystemExit("bench.py times the 1D operator workloads")
+    log(f"generating inputs for {args.workload}")
+    inp = make_config(args.workload)
+    B, L, D, N = inp.B, inp.L, inp.D, inp.N
+    tdt = torch.bfloat16 if inp.dtype == "bf16" else torch.float32
+    s = 2 if inp.dtype == "bf16" else 4
+    dev = "cuda"
+    f = lambda a, d=torch.float32: torch.from_numpy(np.ascontiguousarray(a, np.float32)).to(dev, d)  # noqa: E731
+
+    layer = hs.HyenaLayer(L, D, N)
+    hs.hyena_filter_gen(layer, f(inp.w1), f(inp.b1), f(inp.w2), f(inp.b2), f(inp.w3), f(inp.b3), f(inp.decay),
+                        inp.K)
+    u, w_in, w_out = f(inp.u, tdt), f(inp.w_in, tdt), f(inp.w_out, tdt)
+    short_w, dskip = f(inp.short_w), f(inp.dskip)
+    y = torch.empty_like(u)
+    ws = torch.empty(hs.hyena_workspace_bytes(B, L, D, N, hs.HYENA_BF16 if s == 2 else hs.HYENA_F32),
+                     dtype=torch.uint8, device=dev)
+    torch.cuda.synchronize()
+    log(f"warmup {args.warmup}")
+    for _ in range(args.warmup):
+        hs.hyena_fwd(layer, u, w_in, short_w, dskip, w_out, y=y, ws=ws)
+    torch.cuda.synchronize()
+    log(f"timing {args.steps} steps")
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        hs.hyena_fwd(layer, u, w_in, short_w, dskip, w_out, y=y, ws=ws)
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    ms_per_step = 1e3 * elapsed / args.steps
+    value = B * L * args.steps / elapsed
+
+    # per-stage event times over the same number of steps
+    stages = np.zeros(3)
+    for _ in range(args.steps):
+        stages += np.array(hs.hyena_fwd_profiled(layer, u, w_in, short_w, dskip, w_out, y, ws))
+    stages /= args.steps
+    lds = L <= 4096
+    alg = conv_alg_bytes(B, L, D, N, s, lds)
+    achieved = alg / (stages[1] * 1e-3) / 1e9
+    log(f"stages ms: in-proj {stages[0]:.4f} conv {stages[1]:.4f} out-proj {stages[2]:.4f}")
+
+    out = {
+        "metric": METRIC,
+        "value": value,
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_per_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": inp.dtype,
+        "data": "synthetic",
+        "config": {"workload": args.workload, "B": B, "L": L, "D": D, "N": N},
+        "stage_ms": {"in_proj": stages[0], "fft_conv": stages[1], "out_proj": stages[2]},
+        "roofline": {"bound": "hbm", "kernel": "fft_conv stage (all orders)", "achieved": achieved,
+                     "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS,
+                     "alg_bytes": alg, "traffic": None},
+    }
+    if not args.no_cpu_baseline:
+        log("cpu baseline (oracle)")
+        out["cpu_baseline"] = cpu_baseline(inp, args.cpu_tokens)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

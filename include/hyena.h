@@ -1,0 +1,173 @@
+/*
+ * hyena.h - C ABI of libhyena.so, the forward hot path of the Hyena operator
+ * and of its 3D variant on AMD Instinct MI355X (gfx950).
+ *
+ * The operator (Hyena Hierarchy abstract, taxoreview.com page; French summary
+ * on summarizepaper.com, "Key points") interleaves implicitly parametrised long
+ * convolutions with data-controlled gating. This library computes, for order N:
+ *
+ *   p = u W_in, split into column blocks (v, x^1 .. x^N), each D wide
+ *   s = causal depthwise short convolution of length 3 of every column of p
+ *   z^1 = s_v;  z^{n+1} = s_{x^n} * (h^n conv z^n) + D^n * z^n   (n = 1..N)
+ *   y = z^{N+1} W_out
+ *
+ * where each h^n is a causal filter as long as the input (TWIML #690 podcast,
+ * 5:48) produced by an MLP of the position (TWIML #690, 4:29), applied through
+ * the convolution theorem (TWIML #690, 6:27) with zero padding to 2L
+ * (HyenaND explainer, gist.science, Methodology, "Handling Boundaries").
+ *
+ * Conventions used by every entry point
+ *  - All tensor arguments are DEVICE pointers, allocated and owned by the
+ *    caller (the library never allocates or frees device memory and keeps no
+ *    global device state; calls on different streams with different buffers
+ *    are independent).
+ *  - Row-major layouts; the last listed dimension is contiguous.
+ *  - Work is enqueued asynchronously on `stream`; nothing synchronises.
+ *  - Every argument is validated on the host before the first HIP call; an
+ *    invalid call returns an error code and enqueues nothing. A HIP failure
+ *    while enqueuing returns HYENA_ERR_HIP (work enqueued before it may run).
+ *  - Pointers must be 16-byte aligned.
+ */
+#ifndef HYENA_H
+#define HYENA_H
+
+#include <stddef.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Storage type of activations (u, y, intermediates) and projection weights.
+ * Arithmetic is always fp32 (accumulation included). */
+typedef enum { HYENA_F32 = 0, HYENA_BF16 = 1 } hyena_dtype;
+
+enum {
+  HYENA_OK = 0,
+  HYENA_ERR_INVALID_ARG = 1,     /* null/misaligned pointer, bad size or dtype */
+  HYENA_ERR_UNSUPPORTED = 2,     /* shape outside the supported ranges below */
+  HYENA_ERR_WORKSPACE = 3,       /* workspace or cache smaller than required */
+  HYENA_ERR_LAYER_MISMATCH = 4,  /* layer not built, or built for other sizes */
+  HYENA_ERR_HIP = 5              /* a HIP call failed (no device, launch error) */
+};
+
+/* Returns a static string describing a status code. */
+const char *hyena_status_str(int status);
+
+/* ------------------------------------------------------------------ 1D ---- */
+
+/* Parameters of the implicit filter (device pointers, fp32, row-major).
+ *   PosEnc(t) = [tau, cos(2 pi k tau)_{k=1..K}, sin(2 pi k tau)_{k=1..K}], tau = t/L
+ *   o_t = W3^T sin(W2^T sin(W1^T PosEnc(t) + b1) + b2) + b3        in R^{N*D}
+ *   h^n_c(t) = exp(-decay_c * tau) * o_t[(n-1)*D + c],  t = 0 .. L-1
+ * Shapes: w1 [1+2K][W], b1 [W], w2 [W][W], b2 [W], w3 [W][N*D], b3 [N*D],
+ * decay [D]. Supported: 1 <= K <= 32, 1 <= W <= 128. */
+typedef struct {
+  int pe_freqs;  /* K */
+  int width;     /* W */
+  const float *w1, *b1, *w2, *b2, *w3, *b3, *decay;
+} hyena_filter_params;
+
+/* Host-side handle of one layer's filter cache. The cache is caller-owned
+ * device memory of hyena_cache_bytes(L, D, N) bytes holding twiddle tables and
+ * the spectra of the zero-padded filters in an internal (opaque) order. It is
+ * shared by every batch and every hyena_fwd call of the layer. */
+typedef struct {
+  int L, D, N;
+  int built;            /* set to 1 by hyena_filter_gen */
+  void *cache;
+  size_t cache_bytes;
+} hyena_layer;
+
+/* Supported shapes: L a power of two in [16, 2^20]; D a multiple of 64 in
+ * [64, 8192]; 1 <= N <= 4; B >= 1 with B*L*(N+1)*D < 2^31.
+ * The size queries return 0 for unsupported shapes. */
+size_t hyena_cache_bytes(int L, int D, int N);
+size_t hyena_filter_workspace_bytes(int L, int D, int N);
+size_t hyena_workspace_bytes(int B, int L, int D, int N, int dtype);
+
+/* Fills the host struct (no HIP call). `cache` must hold hyena_cache_bytes. */
+int hyena_layer_init(hyena_layer *layer, int L, int D, int N, void *cache, size_t cache_bytes);
+
+/* Evaluates the implicit filters h^n for t in [0, L) and stores the spectra of
+ * [h^n, 0_L] (size-2L DFT) in layer->cache. If h_out is not NULL the filters are
+ * also written there as fp32 [N][D][L]. `ws` is scratch of at least
+ * hyena_filter_workspace_bytes(L, D, N) bytes. Sets layer->built = 1. */
+int hyena_filter_gen(hyena_layer *layer, const hyena_filter_params *p, float *h_out,
+                     void *ws, size_t ws_bytes, hipStream_t stream);
+
+/* Forward pass of one layer.
+ *   u       [B][L][D]        dtype
+ *   w_in    [D][(N+1)*D]     dtype, column blocks (v, x^1, .., x^N)
+ *   short_w [(N+1)*D][3]     fp32; tap k multiplies p_{t-k}, zero history
+ *   dskip   [N][D]           fp32
+ *   w_out   [D][D]           dtype
+ *   y       [B][L][D]        dtype (output; may not alias the inputs)
+ *   ws      scratch of at least hyena_workspace_bytes(B, L, D, N, dtype) bytes
+ * The layer must have been built by hyena_filter_gen for the same (L, D, N). */
+int hyena_fwd(const hyena_layer *layer, const void *u, const void *w_in,
+              const float *short_w, const float *dskip, const void *w_out,
+              int B, int dtype, void *y, void *ws, size_t ws_bytes, hipStream_t stream);
+
+/* Same launches as hyena_fwd, with HIP events recorded on `stream` between the
+ * stages; waits for the stream and writes the stage durations (host array of 3):
+ *   stage_ms[0] in-projection (weight transposes + GEMM),
+ *   stage_ms[1] long convolutions with gating (all orders),
+ *   stage_ms[2] out-projection.
+ * For measurement; unlike hyena_fwd it synchronises. */
+int hyena_fwd_profiled(const hyena_layer *layer, const void *u, const void *w_in,
+                       const float *short_w, const float *dskip, const void *w_out,
+                       int B, int dtype, void *y, void *ws, size_t ws_bytes, hipStream_t stream,
+                       float *stage_ms);
+
+/* ------------------------------------------------------------------ 3D ---- */
+/*
+ * HyenaND on 3D grids (HyenaND explainer, gist.science, "Methodology: HyenaND"):
+ * a global convolution on the native grid through a 3D FFT, non-circular by zero
+ * padding to twice the grid ("Handling Boundaries"), with a coordinate-MLP kernel
+ * times a window ("Kernel Synthesis") whose scale depends on the whole sample
+ * ("Input-Dependent Kernels"). Here:
+ *   K^n_c(d) = exp(-decay_c |c|_2) * (W3^T sin(W2^T sin(W1^T c + b1) + b2) + b3)[(n-1)C + c]
+ *     at coordinates c = (dx/X, dy/Y, dz/Z) of the offsets d in [-X,X)x[-Y,Y)x[-Z,Z);
+ *   g^n_{b,c} = sigmoid(gate_a[n][c] * mean_grid(u[b,...,c]) + gate_b[n][c]);
+ *   (K conv z)[p] = sum_{q in grid} g * K[p - q] z[q];
+ *   the same projection / gating recurrence as 1D, without the short convolution.
+ */
+typedef struct {
+  int width;     /* W, 1 <= W <= 128 */
+  const float *w1, *b1, *w2, *b2, *w3, *b3, *decay;  /* [3][W],[W],[W][W],[W],[W][N*C],[N*C],[C] */
+} hyena_nd_filter_params;
+
+typedef struct {
+  int X, Y, Z, C, N;
+  int built;
+  void *cache;
+  size_t cache_bytes;
+} hyena_nd_layer;
+
+/* Supported: X, Y, Z powers of two in [4, 64]; C a multiple of 64 in [64, 4096];
+ * 1 <= N <= 4; B >= 1. The size queries return 0 for unsupported shapes. */
+size_t hyena_nd_cache_bytes(int X, int Y, int Z, int C, int N);
+size_t hyena_nd_filter_workspace_bytes(int X, int Y, int Z, int C, int N);
+size_t hyena_nd_workspace_bytes(int B, int X, int Y, int Z, int C, int N);
+
+int hyena_nd_layer_init(hyena_nd_layer *layer, int X, int Y, int Z, int C, int N,
+                        void *cache, size_t cache_bytes);
+
+/* Evaluates K^n_c on the (2X, 2Y, 2Z) offset grid and caches its 3D spectrum.
+ * If k_out is not NULL the kernel is also written there as fp32
+ * [N][C][2X][2Y][2Z], entry [i][j][k] at offset (i - X, j - Y, k - Z). */
+int hyena_nd_filter_gen(hyena_nd_layer *layer, const hyena_nd_filter_params *p, float *k_out,
+                        void *ws, size_t ws_bytes, hipStream_t stream);
+
+/* Forward pass, fp32:
+ *   u, y [B][X][Y][Z][C]; w_in [C][(N+1)C]; dskip, gate_a, gate_b [N][C]; w_out [C][C]. */
+int hyena_nd_fwd(const hyena_nd_layer *layer, const float *u, const float *w_in,
+                 const float *dskip, const float *gate_a, const float *gate_b,
+                 const float *w_out, int B, float *y, void *ws, size_t ws_bytes,
+                 hipStream_t stream);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* HYENA_H */

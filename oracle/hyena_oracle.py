@@ -58,15 +58,15 @@ def fft_radix2(x, inverse: bool = False) -> np.ndarray:
     if n < 1 or n & (n - 1):
         raise ValueError("length must be a power of two")
     lead = a.shape[:-1]
-    a = a[..., _bit_reverse_indices(n)]
+    a = np.ascontiguousarray(a[..., _bit_reverse_indices(n)])
     sign = 1.0 if inverse else -1.0
     m = 1
     while m < n:
         w = np.exp(sign * 1j * np.pi * np.arange(m) / m)
-        g = a.reshape(lead + (n // (2 * m), 2, m))
-        even = g[..., 0, :]
-        odd = g[..., 1, :] * w
-        a = np.stack([even + odd, even - odd], axis=-2).reshape(lead + (n,))
+        g = a.reshape(lead + (n // (2 * m), 2, m))   # view: [group][even|odd half][k]
+        wo = g[..., 1, :] * w
+        g[..., 1, :] = g[..., 0, :] - wo
+        g[..., 0, :] += wo
         m *= 2
     if inverse:
         a = a / n

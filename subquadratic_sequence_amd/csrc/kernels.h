@@ -1,0 +1,71 @@
+// Internal launcher interface between the C ABI (api.cpp) and the kernels.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+
+namespace hy {
+
+// ---------------------------------------------------------------- GEMM
+// C = A * B with A [M][K], B given transposed as Bt [N][K], fp32 accumulation.
+// A_CM: A is channel-major [Bsz][K][Lseq] (element (m, k) at ((m / Lseq) K + k) Lseq + m % Lseq).
+// C_CM: C is written channel-major [Bsz][N][Lseq].
+struct GemmArgs {
+  const void* A;
+  const void* Bt;
+  void* C;
+  int M, N, K, Lseq;
+  bool a_cm, c_cm;
+};
+hipError_t gemm(const GemmArgs& g, bool bf16, hipStream_t s);
+// dst [cols][rows] = transpose of src [rows][cols] (storage type of the dtype)
+hipError_t transpose2d(const void* src, void* dst, int rows, int cols, bool bf16, hipStream_t s);
+
+// ---------------------------------------------------------- filter (1D)
+struct Filter1DArgs {
+  int L, D, NO, K, W;
+  const float *w1, *b1, *w2, *b2, *w3, *b3, *decay;
+  float* h;  // [NO][D][L]
+};
+hipError_t filter1d_mlp(const Filter1DArgs& a, hipStream_t s);
+// tw[m] = exp(-2 pi i m / n) for m in [0, count), computed in double
+hipError_t twiddles(float2* tw, int n, int count, hipStream_t s);
+
+// ------------------------------------------------------ LDS regime conv
+struct LdsConvArgs {
+  const void* p;          // [B][(NO+1)D][L]
+  const float* short_w;
+  const float* dskip;
+  const float4* pq;       // [NO][D/2][L+1]
+  const float2* tw;       // [2L]
+  void* zout;             // [B][D][L]
+  int B, L, D, NO;
+};
+hipError_t lds_conv(const LdsConvArgs& a, bool bf16, hipStream_t s);
+hipError_t lds_spec(const float* h, const float2* tw, float4* pq, int L, int D, int NO, hipStream_t s);
+size_t lds_conv_smem(int L);
+
+// --------------------------------------------------------- four-step
+struct FourStepTables {
+  const float2* w256;    // [256]
+  const float2* tw_lo;   // [1 << lo_bits]
+  const float2* tw_hi;   // [2L >> lo_bits]
+  const float2* tw_row;  // [N2]
+  int lo_bits;
+};
+struct FourStepConvArgs {
+  const void* p;
+  const float* short_w;
+  const float* dskip;
+  const float4* pq;      // [NO][D/2][129][N2]
+  void* z[2];            // ping-pong z^{n+1} buffers [B][D][L]
+  void* zfinal;          // z^{NO+1} [B][D][L]
+  float2* Y;             // intermediate [group_pairs][256][N2]
+  int B, L, D, NO;
+  int group_pairs;       // channel pairs per group (0: all)
+};
+hipError_t fourstep_conv(const FourStepTables& tb, const FourStepConvArgs& c, bool bf16, hipStream_t s);
+hipError_t fourstep_spec(const FourStepTables& tb, const float* h, float2* Y, float4* pq, int L, int D, int NO,
+                         hipStream_t s);
+
+}  // namespace hy

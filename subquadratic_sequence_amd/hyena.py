@@ -1,0 +1,231 @@
+"""ctypes binding of libhyena.so (argument marshalling only).
+
+Every step of the forward path runs in the library's HIP kernels; PyTorch only
+provides device memory and the current stream. If the library is missing this
+module raises instead of falling back to anything else.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libhyena.so")
+
+HYENA_F32 = 0
+HYENA_BF16 = 1
+STATUS = {0: "HYENA_OK", 1: "HYENA_ERR_INVALID_ARG", 2: "HYENA_ERR_UNSUPPORTED", 3: "HYENA_ERR_WORKSPACE",
+          4: "HYENA_ERR_LAYER_MISMATCH", 5: "HYENA_ERR_HIP"}
+
+_vp = ctypes.c_void_p
+_sz = ctypes.c_size_t
+_i = ctypes.c_int
+
+
+class FilterParams(ctypes.Structure):
+    _fields_ = [("pe_freqs", _i), ("width", _i), ("w1", _vp), ("b1", _vp), ("w2", _vp), ("b2", _vp),
+                ("w3", _vp), ("b3", _vp), ("decay", _vp)]
+
+
+class Layer(ctypes.Structure):
+    _fields_ = [("L", _i), ("D", _i), ("N", _i), ("built", _i), ("cache", _vp), ("cache_bytes", _sz)]
+
+
+class NDFilterParams(ctypes.Structure):
+    _fields_ = [("width", _i), ("w1", _vp), ("b1", _vp), ("w2", _vp), ("b2", _vp), ("w3", _vp), ("b3", _vp),
+                ("decay", _vp)]
+
+
+class NDLayer(ctypes.Structure):
+    _fields_ = [("X", _i), ("Y", _i), ("Z", _i), ("C", _i), ("N", _i), ("built", _i), ("cache", _vp),
+                ("cache_bytes", _sz)]
+
+
+# name -> (restype, argtypes)
+SIGNATURES = {
+    "hyena_status_str": (ctypes.c_char_p, [_i]),
+    "hyena_cache_bytes": (_sz, [_i, _i, _i]),
+    "hyena_filter_workspace_bytes": (_sz, [_i, _i, _i]),
+    "hyena_workspace_bytes": (_sz, [_i, _i, _i, _i, _i]),
+    "hyena_layer_init": (_i, [ctypes.POINTER(Layer), _i, _i, _i, _vp, _sz]),
+    "hyena_filter_gen": (_i, [ctypes.POINTER(Layer), ctypes.POINTER(FilterParams), _vp, _vp, _sz, _vp]),
+    "hyena_fwd": (_i, [ctypes.POINTER(Layer), _vp, _vp, _vp, _vp, _vp, _i, _i, _vp, _vp, _sz, _vp]),
+    "hyena_fwd_profiled": (_i, [ctypes.POINTER(Layer), _vp, _vp, _vp, _vp, _vp, _i, _i, _vp, _vp, _sz, _vp,
+                                ctypes.POINTER(ctypes.c_float)]),
+    "hyena_nd_cache_bytes": (_sz, [_i, _i, _i, _i, _i]),
+    "hyena_nd_filter_workspace_bytes": (_sz, [_i, _i, _i, _i, _i]),
+    "hyena_nd_workspace_bytes": (_sz, [_i, _i, _i, _i, _i, _i]),
+    "hyena_nd_layer_init": (_i, [ctypes.POINTER(NDLayer), _i, _i, _i, _i, _i, _vp, _sz]),
+    "hyena_nd_filter_gen": (_i, [ctypes.POINTER(NDLayer), ctypes.POINTER(NDFilterParams), _vp, _vp, _sz, _vp]),
+    "hyena_nd_fwd": (_i, [ctypes.POINTER(NDLayer), _vp, _vp, _vp, _vp, _vp, _vp, _i, _vp, _vp, _sz, _vp]),
+}
+
+_lib = None
+
+
+class HyenaError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        self.status = status
+        super().__init__(f"{where}: {STATUS.get(status, status)}")
+
+
+def lib() -> ctypes.CDLL:
+    """Loads libhyena.so (raises if it has not been built)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"{LIB_PATH} is not built; run `python -m subquadratic_sequence_amd.build`")
+        h = ctypes.CDLL(LIB_PATH)
+        for name, (res, args) in SIGNATURES.items():
+            f = getattr(h, name)
+            f.restype = res
+            f.argtypes = args
+        _lib = h
+    return _lib
+
+
+def _check(status: int, where: str):
+    if status != 0:
+        raise HyenaError(status, where)
+
+
+def _ptr(t):
+    if t is None:
+        return None
+    if not isinstance(t, torch.Tensor):
+        raise TypeError("expected a torch tensor")
+    if not t.is_contiguous():
+        raise ValueError("tensors must be contiguous")
+    return ctypes.c_void_p(t.data_ptr())
+
+
+def _stream():
+    return ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+
+
+def _dtype_code(t: torch.Tensor) -> int:
+    if t.dtype == torch.float32:
+        return HYENA_F32
+    if t.dtype == torch.bfloat16:
+        return HYENA_BF16
+    raise TypeError(f"unsupported dtype {t.dtype}")
+
+
+# ------------------------------------------------------------------ 1D
+
+
+def hyena_cache_bytes(L: int, D: int, N: int) -> int:
+    return lib().hyena_cache_bytes(L, D, N)
+
+
+def hyena_filter_workspace_bytes(L: int, D: int, N: int) -> int:
+    return lib().hyena_filter_workspace_bytes(L, D, N)
+
+
+def hyena_workspace_bytes(B: int, L: int, D: int, N: int, dtype: int) -> int:
+    return lib().hyena_workspace_bytes(B, L, D, N, dtype)
+
+
+class HyenaLayer:
+    """One layer's filter cache (device memory owned by this object)."""
+
+    def __init__(self, L: int, D: int, N: int, device="cuda"):
+        nbytes = hyena_cache_bytes(L, D, N)
+        if nbytes == 0:
+            raise HyenaError(2, "hyena_cache_bytes")
+        self.cache = torch.empty(nbytes, dtype=torch.uint8, device=device)
+        self.c = Layer()
+        _check(lib().hyena_layer_init(ctypes.byref(self.c), L, D, N, _ptr(self.cache), nbytes), "hyena_layer_init")
+        self.L, self.D, self.N = L, D, N
+
+
+def hyena_filter_gen(layer: HyenaLayer, w1, b1, w2, b2, w3, b3, decay, pe_freqs: int, h_out=None, ws=None):
+    """Generates the implicit filters and caches their spectra in layer.cache."""
+    width = w1.shape[1]
+    p = FilterParams(pe_freqs, width, _ptr(w1), _ptr(b1), _ptr(w2), _ptr(b2), _ptr(w3), _ptr(b3), _ptr(decay))
+    need = hyena_filter_workspace_bytes(layer.L, layer.D, layer.N)
+    if ws is None:
+        ws = torch.empty(need, dtype=torch.uint8, device=layer.cache.device)
+    st = lib().hyena_filter_gen(ctypes.byref(layer.c), ctypes.byref(p), _ptr(h_out), _ptr(ws), ws.numel(),
+                                _stream())
+    _check(st, "hyena_filter_gen")
+    return h_out
+
+
+def hyena_fwd(layer: HyenaLayer, u, w_in, short_w, dskip, w_out, y=None, ws=None):
+    """y = Hyena(u) for u [B, L, D] (float32 or bfloat16)."""
+    B = u.shape[0]
+    dt = _dtype_code(u)
+    if y is None:
+        y = torch.empty_like(u)
+    if ws is None:
+        need = hyena_workspace_bytes(B, layer.L, layer.D, layer.N, dt)
+        ws = torch.empty(max(need, 1), dtype=torch.uint8, device=u.device)
+    st = lib().hyena_fwd(ctypes.byref(layer.c), _ptr(u), _ptr(w_in), _ptr(short_w), _ptr(dskip), _ptr(w_out),
+                         B, dt, _ptr(y), _ptr(ws), ws.numel(), _stream())
+    _check(st, "hyena_fwd")
+    return y
+
+
+def hyena_fwd_profiled(layer: HyenaLayer, u, w_in, short_w, dskip, w_out, y, ws):
+    """hyena_fwd with per-stage HIP event times; returns [in-proj, conv, out-proj] in ms."""
+    B = u.shape[0]
+    ms = (ctypes.c_float * 3)()
+    st = lib().hyena_fwd_profiled(ctypes.byref(layer.c), _ptr(u), _ptr(w_in), _ptr(short_w), _ptr(dskip),
+                                  _ptr(w_out), B, _dtype_code(u), _ptr(y), _ptr(ws), ws.numel(), _stream(), ms)
+    _check(st, "hyena_fwd_profiled")
+    return [ms[0], ms[1], ms[2]]
+
+
+# ------------------------------------------------------------------ 3D
+
+
+def hyena_nd_cache_bytes(X, Y, Z, C, N) -> int:
+    return lib().hyena_nd_cache_bytes(X, Y, Z, C, N)
+
+
+def hyena_nd_filter_workspace_bytes(X, Y, Z, C, N) -> int:
+    return lib().hyena_nd_filter_workspace_bytes(X, Y, Z, C, N)
+
+
+def hyena_nd_workspace_bytes(B, X, Y, Z, C, N) -> int:
+    return lib().hyena_nd_workspace_bytes(B, X, Y, Z, C, N)
+
+
+class HyenaNDLayer:
+    def __init__(self, X: int, Y: int, Z: int, C: int, N: int, device="cuda"):
+        nbytes = hyena_nd_cache_bytes(X, Y, Z, C, N)
+        if nbytes == 0:
+            raise HyenaError(2, "hyena_nd_cache_bytes")
+        self.cache = torch.empty(nbytes, dtype=torch.uint8, device=device)
+        self.c = NDLayer()
+        _check(lib().hyena_nd_layer_init(ctypes.byref(self.c), X, Y, Z, C, N, _ptr(self.cache), nbytes),
+               "hyena_nd_layer_init")
+        self.X, self.Y, self.Z, self.C, self.N = X, Y, Z, C, N
+
+
+def hyena_nd_filter_gen(layer: HyenaNDLayer, w1, b1, w2, b2, w3, b3, decay, k_out=None, ws=None):
+    width = w1.shape[1]
+    p = NDFilterParams(width, _ptr(w1), _ptr(b1), _ptr(w2), _ptr(b2), _ptr(w3), _ptr(b3), _ptr(decay))
+    need = hyena_nd_filter_workspace_bytes(layer.X, layer.Y, layer.Z, layer.C, layer.N)
+    if ws is None:
+        ws = torch.empty(max(need, 1), dtype=torch.uint8, device=layer.cache.device)
+    st = lib().hyena_nd_filter_gen(ctypes.byref(layer.c), ctypes.byref(p), _ptr(k_out), _ptr(ws), ws.numel(),
+                                   _stream())
+    _check(st, "hyena_nd_filter_gen")
+    return k_out
+
+
+def hyena_nd_fwd(layer: HyenaNDLayer, u, w_in, dskip, gate_a, gate_b, w_out, y=None, ws=None):
+    B = u.shape[0]
+    if y is None:
+        y = torch.empty_like(u)
+    if ws is None:
+        need = hyena_nd_workspace_bytes(B, layer.X, layer.Y, layer.Z, layer.C, layer.N)
+        ws = torch.empty(max(need, 1), dtype=torch.uint8, device=u.device)
+    st = lib().hyena_nd_fwd(ctypes.byref(layer.c), _ptr(u), _ptr(w_in), _ptr(dskip), _ptr(gate_a), _ptr(gate_b),
+                            _ptr(w_out), B, _ptr(y), _ptr(ws), ws.numel(), _stream())
+    _check(st, "hyena_nd_fwd")
+    return y

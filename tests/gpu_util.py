@@ -1,0 +1,50 @@
+"""Helpers for the GPU tests: run the HIP path through the C ABI and the oracle
+on the same seeded inputs."""
+from __future__ import annotations
+
+import sys
+
+import numpy as np
+
+TOL = {"f32": 1e-4, "bf16": 2e-2}
+
+
+def say(msg: str):
+    print(msg, flush=True)
+    sys.stdout.flush()
+
+
+def rel_err(y, ref) -> float:
+    return float(np.max(np.abs(np.asarray(y, np.float64) - ref)) / max(np.max(np.abs(ref)), 1e-300))
+
+
+def to_dev(a, dtype=None, device="cuda"):
+    import torch
+    t = torch.from_numpy(np.ascontiguousarray(a, dtype=np.float32))
+    return t.to(device=device, dtype=dtype or torch.float32)
+
+
+def gpu_1d(inp, with_h: bool = False, layer=None):
+    """Runs hyena_filter_gen + hyena_fwd on cuda:0; returns y (float64 numpy) [and h]."""
+    import torch
+    import subquadratic_sequence_amd as hs
+    dt = torch.bfloat16 if inp.dtype == "bf16" else torch.float32
+    if layer is None:
+        layer = hs.HyenaLayer(inp.L, inp.D, inp.N)
+    h_out = torch.empty(inp.N, inp.D, inp.L, device="cuda") if with_h else None
+    hs.hyena_filter_gen(layer, to_dev(inp.w1), to_dev(inp.b1), to_dev(inp.w2), to_dev(inp.b2), to_dev(inp.w3),
+                        to_dev(inp.b3), to_dev(inp.decay), inp.K, h_out=h_out)
+    y = hs.hyena_fwd(layer, to_dev(inp.u, dt), to_dev(inp.w_in, dt), to_dev(inp.short_w), to_dev(inp.dskip),
+                     to_dev(inp.w_out, dt))
+    torch.cuda.synchronize()
+    yn = y.float().cpu().numpy().astype(np.float64)
+    if with_h:
+        return yn, h_out.cpu().numpy().astype(np.float64)
+    return yn
+
+
+def oracle_1d(inp, conv: str = "auto"):
+    import oracle
+    h = oracle.implicit_filter(inp.filter_params, inp.L, inp.N, inp.D)
+    y = oracle.hyena_fwd(inp.u, inp.w_in, inp.short_w, inp.dskip, inp.w_out, h, conv=conv)
+    return y, h

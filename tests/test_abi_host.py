@@ -1,0 +1,143 @@
+"""Host-side checks of libhyena.so: it loads, exports every declared entry point,
+answers size queries, and rejects invalid calls before touching HIP.
+
+No compute call is made here (no GPU in this environment)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "hyena.h")
+LIBPATH = os.path.join(ROOT, "subquadratic_sequence_amd", "libhyena.so")
+
+pytestmark = pytest.mark.skipif(not os.path.exists(LIBPATH), reason="libhyena.so not built")
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?\w+\s*\*?\s*(hyena_\w+)\s*\(", text, flags=re.M)))
+
+
+def test_header_declares_the_boundary():
+    names = declared_functions()
+    for want in ["hyena_filter_gen", "hyena_fwd", "hyena_nd_fwd", "hyena_nd_filter_gen", "hyena_cache_bytes",
+                 "hyena_workspace_bytes", "hyena_status_str"]:
+        assert want in names
+
+
+def test_every_declared_symbol_is_exported():
+    lib = ctypes.CDLL(LIBPATH)
+    for name in declared_functions():
+        assert hasattr(lib, name), name
+
+
+def test_binding_signatures_cover_the_header():
+    from subquadratic_sequence_amd import SIGNATURES
+    assert set(SIGNATURES) == set(declared_functions())
+
+
+@pytest.fixture(scope="module")
+def hy():
+    from subquadratic_sequence_amd import hyena
+    return hyena
+
+
+def test_status_strings(hy):
+    L = hy.lib()
+    assert L.hyena_status_str(0) == b"ok"
+    assert L.hyena_status_str(5) == b"HIP error"
+    assert L.hyena_status_str(99) == b"unknown status"
+
+
+@pytest.mark.parametrize("L,D,N", [(15, 64, 2), (24, 64, 2), (1 << 21, 64, 2), (1024, 32, 2), (1024, 96, 2),
+                                   (1024, 64, 0), (1024, 64, 5), (8, 64, 1)])
+def test_size_queries_reject_unsupported(hy, L, D, N):
+    assert hy.hyena_cache_bytes(L, D, N) == 0
+    assert hy.hyena_filter_workspace_bytes(L, D, N) == 0
+    assert hy.hyena_workspace_bytes(1, L, D, N, 0) == 0
+
+
+def test_size_queries_formulas(hy):
+    # LDS regime: twiddles (2L float2) + (P, Q) spectra: N * D/2 * (L+1) float4, 256-byte aligned pieces
+    L, D, N = 1024, 64, 2
+    al = lambda x: (x + 255) // 256 * 256  # noqa: E731
+    assert hy.hyena_cache_bytes(L, D, N) == al(2 * L * 8) + al(N * (D // 2) * (L + 1) * 16)
+    # four-step: 129 rows of N2 = 2L/256 per channel pair and order
+    L = 65536
+    n2 = 2 * L // 256
+    assert hy.hyena_cache_bytes(L, D, N) >= N * (D // 2) * 129 * n2 * 16
+    # workspace grows linearly with batch in its activation part
+    w1 = hy.hyena_workspace_bytes(1, 2048, 768, 2, 1)
+    w2 = hy.hyena_workspace_bytes(2, 2048, 768, 2, 1)
+    assert w2 > w1 > 0
+    assert hy.hyena_workspace_bytes(1, 2048, 768, 2, 7) == 0
+
+
+def _aligned_buffer(n):
+    buf = ctypes.create_string_buffer(n + 64)
+    addr = (ctypes.addressof(buf) + 63) // 64 * 64
+    return buf, ctypes.c_void_p(addr)
+
+
+def test_layer_init_validation(hy):
+    L = hy.lib()
+    layer = hy.Layer()
+    keep, p = _aligned_buffer(16)
+    assert L.hyena_layer_init(None, 1024, 64, 2, p, 1 << 30) == 1
+    assert L.hyena_layer_init(ctypes.byref(layer), 1000, 64, 2, p, 1 << 30) == 2
+    assert L.hyena_layer_init(ctypes.byref(layer), 1024, 64, 2, None, 1 << 30) == 1
+    assert L.hyena_layer_init(ctypes.byref(layer), 1024, 64, 2, ctypes.c_void_p(p.value + 4), 1 << 30) == 1
+    assert L.hyena_layer_init(ctypes.byref(layer), 1024, 64, 2, p, 16) == 3
+    assert L.hyena_layer_init(ctypes.byref(layer), 1024, 64, 2, p, 1 << 30) == 0
+    assert (layer.L, layer.D, layer.N, layer.built) == (1024, 64, 2, 0)
+
+
+def test_fwd_validation_before_any_hip_call(hy):
+    L = hy.lib()
+    keep, p = _aligned_buffer(16)
+    layer = hy.Layer()
+    assert L.hyena_layer_init(ctypes.byref(layer), 1024, 64, 2, p, 1 << 30) == 0
+    args = [p, p, p, p, p]
+    ws_need = hy.hyena_workspace_bytes(1, 1024, 64, 2, 0)
+    # not built -> layer mismatch
+    assert L.hyena_fwd(ctypes.byref(layer), *args, 1, 0, p, p, ws_need, None) == 4
+    layer.built = 1
+    # null input, bad dtype, bad batch, small workspace
+    assert L.hyena_fwd(ctypes.byref(layer), None, p, p, p, p, 1, 0, p, p, ws_need, None) == 1
+    assert L.hyena_fwd(ctypes.byref(layer), *args, 1, 3, p, p, ws_need, None) == 1
+    assert L.hyena_fwd(ctypes.byref(layer), *args, 0, 0, p, p, ws_need, None) == 1
+    assert L.hyena_fwd(ctypes.byref(layer), *args, 1, 0, p, p, ws_need - 1, None) == 3
+    # layer with a cache too small for its sizes
+    layer.cache_bytes = 16
+    assert L.hyena_fwd(ctypes.byref(layer), *args, 1, 0, p, p, ws_need, None) == 4
+
+
+def test_valid_call_without_device_reports_hip_error(hy):
+    import torch
+    if torch.cuda.is_available():
+        pytest.skip("a GPU is present")
+    L = hy.lib()
+    keep, p = _aligned_buffer(16)
+    layer = hy.Layer()
+    assert L.hyena_layer_init(ctypes.byref(layer), 1024, 64, 2, p, 1 << 30) == 0
+    layer.built = 1
+    ws_need = hy.hyena_workspace_bytes(1, 1024, 64, 2, 0)
+    assert L.hyena_fwd(ctypes.byref(layer), p, p, p, p, p, 1, 0, p, p, ws_need, None) == 5
+
+
+def test_filter_gen_validation(hy):
+    L = hy.lib()
+    keep, p = _aligned_buffer(16)
+    layer = hy.Layer()
+    assert L.hyena_layer_init(ctypes.byref(layer), 1024, 64, 2, p, 1 << 30) == 0
+    fp = hy.FilterParams(8, 64, p, p, p, p, p, p, p)
+    need = hy.hyena_filter_workspace_bytes(1024, 64, 2)
+    assert L.hyena_filter_gen(ctypes.byref(layer), None, None, p, need, None) == 1
+    bad = hy.FilterParams(0, 64, p, p, p, p, p, p, p)
+    assert L.hyena_filter_gen(ctypes.byref(layer), ctypes.byref(bad), None, p, need, None) == 2
+    bad = hy.FilterParams(8, 64, p, None, p, p, p, p, p)
+    assert L.hyena_filter_gen(ctypes.byref(layer), ctypes.byref(bad), None, p, need, None) == 1
+    assert L.hyena_filter_gen(ctypes.byref(layer), ctypes.byref(fp), None, p, need - 1, None) == 3

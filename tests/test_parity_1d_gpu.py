@@ -1,0 +1,120 @@
+"""Parity of the HIP path (through the C ABI) with the fp64 oracle, 1D operator.
+
+Bar: max |y - y_ref| / max |y_ref| <= 1e-4 (fp32 storage) or <= 2e-2 (bf16
+storage, fp32 compute), element by element over the whole output."""
+import numpy as np
+import pytest
+
+from synth import make_1d, make_config
+from tests.gpu_util import TOL, gpu_1d, oracle_1d, rel_err, say
+
+pytestmark = pytest.mark.gpu
+
+
+def _check(inp, conv="auto", tol=None):
+    say(f"case B={inp.B} L={inp.L} D={inp.D} N={inp.N} dtype={inp.dtype} seed={inp.meta['seed']}")
+    y = gpu_1d(inp)
+    ref, _ = oracle_1d(inp, conv=conv)
+    err = rel_err(y, ref)
+    say(f"  rel err {err:.3e}")
+    assert np.all(np.isfinite(y))
+    assert err <= (tol or TOL[inp.dtype]), err
+    return y, ref
+
+
+def test_filter_generator_matches_oracle():
+    inp = make_1d(11, 1, 1024, 64, N=2, K=8)
+    say("filter L=1024 D=64 N=2 K=8")
+    _, h = gpu_1d(inp, with_h=True)
+    _, href = oracle_1d(inp)
+    assert rel_err(h, href) < 1e-5
+
+
+def test_filter_generator_ragged_tile_and_wide_ffn():
+    # L = 16 < one 64-position tile; width 128 and K = 32 at the limits
+    inp = make_1d(12, 1, 16, 64, N=1, K=32, W=128)
+    say("filter L=16 D=64 N=1 K=32 W=128")
+    _, h = gpu_1d(inp, with_h=True)
+    _, href = oracle_1d(inp)
+    assert rel_err(h, href) < 1e-5
+
+
+def test_order2_f32_L1k_D64():
+    _check(make_config("order2_f32_L1k_D64"))
+
+
+SWEEP = [
+    # LDS regime (2L <= 8192)
+    (1, 16, 64, 2, "f32"), (3, 32, 64, 1, "f32"), (1, 64, 128, 3, "f32"), (2, 128, 64, 2, "f32"),
+    (1, 256, 64, 2, "f32"), (3, 512, 128, 2, "f32"), (1, 2048, 64, 3, "f32"), (2, 4096, 64, 2, "f32"),
+    (2, 1024, 128, 2, "bf16"), (1, 4096, 192, 4, "f32"),
+    # four-step regime (2L >= 16384): N2 = 64, 128, 256, 512
+    (1, 8192, 64, 2, "f32"), (3, 16384, 64, 1, "f32"), (1, 32768, 128, 2, "f32"), (1, 65536, 64, 2, "f32"),
+    (2, 16384, 64, 2, "bf16"),
+]
+
+
+@pytest.mark.parametrize("B,L,D,N,dt", SWEEP)
+def test_sweep(B, L, D, N, dt):
+    _check(make_1d(100 + L + D + N + B, B, L, D, N=N, K=8, dtype=dt))
+
+
+def test_four_step_long_N2_1024():
+    # 2L = 2^18: row DFTs of 1024 points
+    _check(make_1d(21, 1, 1 << 17, 64, N=2, K=16))
+
+
+def test_order2_bf16_B8_L2k_D768():
+    _check(make_config("order2_bf16_B8_L2k_D768"), conv="fft")
+
+
+def test_causality_on_gpu():
+    inp = make_1d(31, 1, 1024, 64, N=2, K=8)
+    y0 = gpu_1d(inp)
+    t0 = 300
+    inp.u = inp.u.copy()
+    inp.u[:, t0] += 5.0
+    y1 = gpu_1d(inp)
+    scale = np.max(np.abs(y0))
+    assert np.max(np.abs(y1[:, :t0] - y0[:, :t0])) <= 1e-5 * scale
+    assert np.max(np.abs(y1[:, t0] - y0[:, t0])) > 1e-2 * scale
+
+
+def test_delta_filter_closed_form_on_gpu():
+    # constant FFN output and a very fast window: h ~ delta_0, and D = 0
+    inp = make_1d(32, 2, 256, 64, N=2, K=8)
+    inp.w3 = np.zeros_like(inp.w3)
+    inp.b3 = np.ones_like(inp.b3)
+    inp.decay = np.full_like(inp.decay, 4.0e4)
+    inp.dskip = np.zeros_like(inp.dskip)
+    y = gpu_1d(inp)
+    p = inp.u.astype(np.float64) @ inp.w_in.astype(np.float64)
+    s = np.empty_like(p)
+    for j in range(p.shape[-1]):
+        for b in range(p.shape[0]):
+            s[b, :, j] = np.convolve(p[b, :, j], inp.short_w[j].astype(np.float64))[:inp.L]
+    D = inp.D
+    want = (s[..., :D] * s[..., D:2 * D] * s[..., 2 * D:]) @ inp.w_out.astype(np.float64)
+    assert rel_err(y, want) < 1e-4
+
+
+def test_linear_in_v_on_gpu():
+    inp = make_1d(33, 1, 2048, 64, N=2, K=8)
+    y = gpu_1d(inp)
+    D = inp.D
+    rng = np.random.default_rng(5)
+    split = (rng.standard_normal((D, D)) / 8).astype(np.float32)
+    a = make_1d(33, 1, 2048, 64, N=2, K=8)
+    b = make_1d(33, 1, 2048, 64, N=2, K=8)
+    a.w_in = inp.w_in.copy()
+    b.w_in = inp.w_in.copy()
+    a.w_in[:, :D] = split
+    b.w_in[:, :D] = inp.w_in[:, :D] - split
+    assert rel_err(gpu_1d(a) + gpu_1d(b), y) < 1e-4
+
+
+def test_deterministic():
+    inp = make_1d(34, 2, 16384, 64, N=2, K=8)
+    y0 = gpu_1d(inp)
+    y1 = gpu_1d(inp)
+    assert np.array_equal(y0, y1)
