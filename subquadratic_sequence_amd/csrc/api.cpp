@@ -4,6 +4,7 @@
 #include "../../include/hyena.h"
 
 #include <stdint.h>
+#include <stdlib.h>
 #include <string.h>
 
 #include "common.h"
@@ -46,7 +47,7 @@ CacheLayout cache_layout(int L, int D, int N) {
     c.pq = off;
     off = align_up(off + (size_t)N * (D / 2) * (L + 1) * 16, kAlign);
   } else {
-    c.N2 = (int)(n / 256);
+    c.N2 = (int)(n / hy::fourstep_n1(L));
     c.lo_bits = (ilog2((long long)n) + 1) / 2;
     c.w256 = off;
     off = align_up(off + 256 * 8, kAlign);
@@ -57,7 +58,7 @@ CacheLayout cache_layout(int L, int D, int N) {
     c.tw_row = off;
     off = align_up(off + (size_t)c.N2 * 8, kAlign);
     c.pq = off;
-    off = align_up(off + (size_t)N * (D / 2) * 129 * c.N2 * 16, kAlign);
+    off = align_up(off + (size_t)N * (D / 2) * (hy::fourstep_n1(L) / 2 + 1) * c.N2 * 16, kAlign);
   }
   c.total = off;
   return c;
@@ -123,11 +124,21 @@ int device_ok() {
   return HYENA_OK;
 }
 
-int group_pairs_default(int B, int L, int D) {
-  (void)B;
-  (void)L;
-  (void)D;
-  return 0;  // all pairs in one group
+// Tuning knobs (read once): HYENA_GROUP_PAIRS = channel pairs per four-step
+// group (0: all pairs in one group); HYENA_SPECTRUM_FP32 = 1 keeps the
+// four-step intermediate in fp32 for bf16 workloads.
+struct Tuning {
+  int group_pairs = 0;
+  bool y_bf16 = true;
+};
+const Tuning& tuning() {
+  static const Tuning t = [] {
+    Tuning r;
+    if (const char* s = getenv("HYENA_GROUP_PAIRS")) r.group_pairs = atoi(s);
+    if (const char* s = getenv("HYENA_SPECTRUM_FP32")) r.y_bf16 = atoi(s) == 0;
+    return r;
+  }();
+  return t;
 }
 
 }  // namespace
@@ -248,32 +259,33 @@ static int fwd_impl(const hyena_layer* layer, const void* u, const void* w_in, c
   if (ev) HY_CHECK_HIP(hipEventRecord(ev[0], stream));
   HY_CHECK_HIP(hy::transpose2d(w_in, wt_in, D, J, bf, stream));
   HY_CHECK_HIP(hy::transpose2d(w_out, wt_out, D, D, bf, stream));
-  hy::GemmArgs gi{u, wt_in, pbuf, B * L, J, D, L, false, true};
+  // in-projection with the short convolution in the epilogue: pbuf holds s
+  hy::GemmArgs gi{u, wt_in, pbuf, B * L, J, D, L, false, true, short_w};
   HY_CHECK_HIP(hy::gemm(gi, bf, stream));
   if (ev) HY_CHECK_HIP(hipEventRecord(ev[1], stream));
   if (cl.lds) {
-    hy::LdsConvArgs a{pbuf, short_w, dskip, reinterpret_cast<const float4*>(cb + cl.pq),
+    hy::LdsConvArgs a{pbuf, dskip, reinterpret_cast<const float4*>(cb + cl.pq),
                       reinterpret_cast<const float2*>(cb + cl.tw), zfin, B, L, D, N};
     HY_CHECK_HIP(hy::lds_conv(a, bf, stream));
   } else {
     hy::FourStepConvArgs a{};
-    a.p = pbuf;
-    a.short_w = short_w;
+    a.s = pbuf;
     a.dskip = dskip;
     a.pq = reinterpret_cast<const float4*>(cb + cl.pq);
     a.z[0] = wsb + fw.z0;
     a.z[1] = wsb + fw.z1;
     a.zfinal = zfin;
-    a.Y = reinterpret_cast<float2*>(wsb + fw.Y);
+    a.Y = wsb + fw.Y;
     a.B = B;
     a.L = L;
     a.D = D;
     a.NO = N;
-    a.group_pairs = group_pairs_default(B, L, D);
+    a.group_pairs = tuning().group_pairs;
+    a.y_bf16 = tuning().y_bf16;
     HY_CHECK_HIP(hy::fourstep_conv(tables(cl, layer->cache), a, bf, stream));
   }
   if (ev) HY_CHECK_HIP(hipEventRecord(ev[2], stream));
-  hy::GemmArgs go{zfin, wt_out, y, B * L, D, D, L, true, false};
+  hy::GemmArgs go{zfin, wt_out, y, B * L, D, D, L, true, false, nullptr};
   HY_CHECK_HIP(hy::gemm(go, bf, stream));
   if (ev) HY_CHECK_HIP(hipEventRecord(ev[3], stream));
   return HYENA_OK;

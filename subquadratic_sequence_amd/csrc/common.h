@@ -114,13 +114,35 @@ template <int R, bool INV> struct Dft {
 };
 
 // ----------------------------------------------------- Stockham FFT in LDS
+// LDS buffers holding FFT data use a padded layout: element i lives at
+// pad16(i) = i + i/16. Every 16 consecutive lanes of a stage then touch 16
+// distinct 8-byte slots modulo 16, i.e. all 32 banks, for both the strided
+// reads and the autosort writes of every radix-16 stage.
+__device__ __forceinline__ int pad16(int i) { return i + (i >> 4); }
+__host__ __device__ constexpr int padded_len(int n) { return n + n / 16; }
+
 // One workgroup-level N-point complex FFT (several independent ones when the
 // caller gives each group its own `buf`). `lt` is the thread index inside the
 // group (N/E threads per FFT, E values per thread). Stage with radix R and
 // current sub-length Ns:
-//   butterfly j in [0, N/R): inputs buf[j + r N/R]; twiddle W_{Ns R}^{r (j mod Ns)};
-//   R-point DFT; outputs buf[(j / Ns) Ns R + (j mod Ns) + r Ns]   (autosort).
+//   butterfly j in [0, N/R): inputs x[j + r N/R]; twiddle W_{Ns R}^{r (j mod Ns)};
+//   R-point DFT; outputs x[(j / Ns) Ns R + (j mod Ns) + r Ns]   (autosort).
 // tw[m] = W_N^m for m in [0, N). All group threads must call it (barriers).
+
+// twiddle powers w^r, r in [1, R): powers of two from the table, others as
+// one product of two of them (at most two roundings deep)
+template <int R>
+__device__ __forceinline__ void twiddle_powers(float2 (&w)[R], const float2* __restrict__ tw, int step) {
+#pragma unroll
+  for (int r = 1; r < R; ++r) {
+    if ((r & (r - 1)) == 0) {
+      w[r] = tw[r * step];
+    } else {
+      const int hb = 1 << (31 - __builtin_clz(r));
+      w[r] = cmul(w[hb], w[r - hb]);
+    }
+  }
+}
 
 template <int N, int E, int Ns, bool INV>
 __device__ __forceinline__ void stockham_stage(float2* buf, int lt, const float2* __restrict__ tw) {
@@ -132,16 +154,17 @@ __device__ __forceinline__ void stockham_stage(float2* buf, int lt, const float2
   for (int b = 0; b < NB; ++b) {
     const int j = lt + b * T;
 #pragma unroll
-    for (int r = 0; r < R; ++r) v[b][r] = buf[j + r * (N / R)];
+    for (int r = 0; r < R; ++r) v[b][r] = buf[pad16(j + r * (N / R))];
   }
 #pragma unroll
   for (int b = 0; b < NB; ++b) {
     const int j = lt + b * T;
     if (Ns > 1) {
       const int k = j % Ns;
-      const int step = k * (N / (Ns * R));
+      float2 w[R];
+      twiddle_powers<R>(w, tw, k * (N / (Ns * R)));
 #pragma unroll
-      for (int r = 1; r < R; ++r) v[b][r] = twmul<INV>(v[b][r], tw[r * step]);
+      for (int r = 1; r < R; ++r) v[b][r] = twmul<INV>(v[b][r], w[r]);
     }
     Dft<R, INV>::run(v[b]);
   }
@@ -152,7 +175,7 @@ __device__ __forceinline__ void stockham_stage(float2* buf, int lt, const float2
     const int k = j % Ns;
     const int base = (j / Ns) * Ns * R + k;
 #pragma unroll
-    for (int r = 0; r < R; ++r) buf[base + r * Ns] = v[b][r];
+    for (int r = 0; r < R; ++r) buf[pad16(base + r * Ns)] = v[b][r];
   }
   __syncthreads();
 }
@@ -168,11 +191,30 @@ template <int N, int E, bool INV> struct StockhamFrom<N, E, N, INV> {
   static __device__ __forceinline__ void run(float2*, int, const float2*) {}
 };
 
-// In-place N-point FFT of buf[0..N) (LDS), natural order in and out.
-// Requires a __syncthreads() between the last write to buf and the call.
+// In-place N-point FFT of the padded LDS buffer buf (element i at pad16(i)),
+// natural order in and out. Needs a __syncthreads() between the last write to
+// buf and the call; ends with one.
 template <int N, int E, bool INV>
 __device__ __forceinline__ void fft_lds(float2* buf, int lt, const float2* __restrict__ tw) {
   StockhamFrom<N, E, 1, INV>::run(buf, lt, tw);
+}
+
+// ------------------------------------------------ spectrum storage types
+// The four-step intermediate is stored as complex fp32 or, for bf16
+// workloads, as a pair of bf16 (real, imag) packed in 32 bits.
+struct cbf16 {
+  unsigned int v;
+};
+__device__ __forceinline__ float2 ldc(const float2* p) { return *p; }
+__device__ __forceinline__ void stc(float2* p, float2 x) { *p = x; }
+__device__ __forceinline__ float2 ldc(const cbf16* p) {
+  const unsigned int u = p->v;
+  return make_float2(__uint_as_float(u << 16), __uint_as_float(u & 0xFFFF0000u));
+}
+__device__ __forceinline__ void stc(cbf16* p, float2 x) {
+  const unsigned short lo = __builtin_bit_cast(unsigned short, (bf16)x.x);
+  const unsigned short hi = __builtin_bit_cast(unsigned short, (bf16)x.y);
+  p->v = (unsigned int)lo | ((unsigned int)hi << 16);
 }
 
 // ---------------------------------------------------------------- host side

@@ -14,14 +14,14 @@
 //  * 2L <= 8192: one workgroup keeps a channel pair in LDS for all orders
 //    (forward FFT, spectrum product, inverse FFT, gate, skip, next order), so
 //    only the last z^{N+1} is written to HBM.
-//  * 2L >= 16384: four-step FFT with N = 256 x N2 (t = N2 n1 + n2). A column
-//    pass does the 256-point DFTs over n1 (128 non-zero inputs) for blocks of 64
-//    columns, applies the cross twiddle W_N^{n2 k1} and writes the
-//    intermediate; a row pass does the N2-point DFT of rows k1 and 256 - k1
+//  * 2L >= 16384: four-step FFT with N = N1 x N2 (t = N2 n1 + n2, N1 = 64 or
+//    256). A column pass does the N1-point DFTs over n1 (N1/2 non-zero inputs)
+//    for blocks of 64 columns, applies the cross twiddle W_N^{n2 k1} and writes
+//    the intermediate; a row pass does the N2-point DFT of rows k1 and N1 - k1
 //    together (they hold the bins k and N - k), the spectrum product and the
-//    inverse row DFT; the next column pass inverts the columns (keeping the 128
-//    outputs t < L), gates, adds the skip, writes z^{n+1} once and, in the same
-//    registers, starts the forward column DFT of the next order.
+//    inverse row DFT; the next column pass inverts the columns (keeping the
+//    N1/2 outputs t < L), gates, adds the skip, writes z^{n+1} once and, from
+//    the same registers, starts the forward column DFT of the next order.
 #include "common.h"
 #include "kernels.h"
 
@@ -34,28 +34,21 @@ template <int N> struct LdsCfg {
   static constexpr int TG = N / E;                    // threads per FFT
   static constexpr int WG = TG > 256 ? TG : 256;      // threads per workgroup
   static constexpr int G = WG / TG;                   // channel pairs per workgroup
+  static constexpr int FB = padded_len(N);            // float2 per FFT buffer
+  static constexpr size_t LDS = (size_t)G * (FB * 8 + N * 4);
 };
-
-// causal length-3 short convolution of one projected channel at time t
-template <typename T>
-__device__ __forceinline__ float short_conv_at(const T* __restrict__ row, const float* __restrict__ w3, int t) {
-  float s = w3[0] * ldf(row + t);
-  if (t >= 1) s += w3[1] * ldf(row + t - 1);
-  if (t >= 2) s += w3[2] * ldf(row + t - 2);
-  return s;
-}
 
 template <typename T, int N>
 __global__ __launch_bounds__(LdsCfg<N>::WG) void fftconv_lds_kernel(
-    const T* __restrict__ p, const float* __restrict__ short_w, const float* __restrict__ dskip,
-    const float4* __restrict__ pq, const float2* __restrict__ tw, T* __restrict__ zout, int D, int NO) {
+    const T* __restrict__ sp, const float* __restrict__ dskip, const float4* __restrict__ pq,
+    const float2* __restrict__ tw, T* __restrict__ zout, int D, int NO) {
   using C = LdsCfg<N>;
   constexpr int L = N / 2;
   extern __shared__ float4 smem4[];
   float2* fbase = reinterpret_cast<float2*>(smem4);
-  float* zbase = reinterpret_cast<float*>(fbase + C::G * N);
+  float* zbase = reinterpret_cast<float*>(fbase + C::G * C::FB);
   const int g = threadIdx.x / C::TG, lt = threadIdx.x % C::TG;
-  float2* fb = fbase + g * N;
+  float2* fb = fbase + g * C::FB;
   float* za = zbase + g * N;  // z^n of channel a in [0, L), channel b in [L, 2L)
   float* zb = za + L;
   const int pr = blockIdx.x * C::G + g;
@@ -63,16 +56,16 @@ __global__ __launch_bounds__(LdsCfg<N>::WG) void fftconv_lds_kernel(
   const int b = pr / half, cp = pr % half;
   const int ca = 2 * cp, cb = ca + 1;
   const size_t J = (size_t)(NO + 1) * D;
-  const T* pb = p + (size_t)b * J * L;
+  const T* sb = sp + (size_t)b * J * L;  // short-convolved blocks (v, x^1, .., x^NO)
 
-  // z^1 = short conv of the v block
+  // z^1 = v block
   for (int t = lt; t < L; t += C::TG) {
-    float a = short_conv_at(pb + (size_t)ca * L, short_w + 3 * ca, t);
-    float c = short_conv_at(pb + (size_t)cb * L, short_w + 3 * cb, t);
+    float a = ldf(sb + (size_t)ca * L + t);
+    float c = ldf(sb + (size_t)cb * L + t);
     za[t] = a;
     zb[t] = c;
-    fb[t] = make_float2(a, c);
-    fb[t + L] = make_float2(0.f, 0.f);
+    fb[pad16(t)] = make_float2(a, c);
+    fb[pad16(t + L)] = make_float2(0.f, 0.f);
   }
   for (int n = 0; n < NO; ++n) {
     __syncthreads();
@@ -83,13 +76,10 @@ __global__ __launch_bounds__(LdsCfg<N>::WG) void fftconv_lds_kernel(
       float4 w = pqn[k];
       float2 P = make_float2(w.x, w.y), Q = make_float2(w.z, w.w);
       const int m = (N - k) & (N - 1);
-      float2 xk = fb[k], xm = fb[m];
+      float2 xk = fb[pad16(k)], xm = fb[pad16(m)];
       float2 yk = cadd(cmul(xk, P), cmul(conjf2(xm), Q));
-      if (m != k) {
-        float2 ym = cadd(cmulc(xm, P), cmulc(conjf2(xk), Q));
-        fb[m] = ym;
-      }
-      fb[k] = yk;
+      if (m != k) fb[pad16(m)] = cadd(cmulc(xm, P), cmulc(conjf2(xk), Q));
+      fb[pad16(k)] = yk;
     }
     __syncthreads();
     fft_lds<N, C::E, true>(fb, lt, tw);
@@ -98,9 +88,9 @@ __global__ __launch_bounds__(LdsCfg<N>::WG) void fftconv_lds_kernel(
     const float da = dskip[n * D + ca], db = dskip[n * D + cb];
     const bool last = (n == NO - 1);
     for (int t = lt; t < L; t += C::TG) {
-      float2 y = fb[t];
-      float xa = short_conv_at(pb + (size_t)(jx + ca) * L, short_w + 3 * (jx + ca), t);
-      float xb = short_conv_at(pb + (size_t)(jx + cb) * L, short_w + 3 * (jx + cb), t);
+      float2 y = fb[pad16(t)];
+      float xa = ldf(sb + (size_t)(jx + ca) * L + t);
+      float xb = ldf(sb + (size_t)(jx + cb) * L + t);
       float na = xa * y.x + da * za[t];
       float nb = xb * y.y + db * zb[t];
       if (last) {
@@ -109,8 +99,8 @@ __global__ __launch_bounds__(LdsCfg<N>::WG) void fftconv_lds_kernel(
       } else {
         za[t] = na;
         zb[t] = nb;
-        fb[t] = make_float2(na, nb);
-        fb[t + L] = make_float2(0.f, 0.f);
+        fb[pad16(t)] = make_float2(na, nb);
+        fb[pad16(t + L)] = make_float2(0.f, 0.f);
       }
     }
   }
@@ -123,7 +113,7 @@ __global__ __launch_bounds__(LdsCfg<N>::WG) void filter_spec_lds_kernel(
   using C = LdsCfg<N>;
   constexpr int L = N / 2;
   extern __shared__ float4 smem4[];
-  float2* fb = reinterpret_cast<float2*>(smem4) + (threadIdx.x / C::TG) * N;
+  float2* fb = reinterpret_cast<float2*>(smem4) + (threadIdx.x / C::TG) * C::FB;
   const int lt = threadIdx.x % C::TG;
   const int pr = blockIdx.x * C::G + threadIdx.x / C::TG;  // over NO * D/2
   const int half = D / 2;
@@ -131,36 +121,33 @@ __global__ __launch_bounds__(LdsCfg<N>::WG) void filter_spec_lds_kernel(
   const float* ha = h + ((size_t)n * D + 2 * cp) * L;
   const float* hb = ha + L;
   for (int t = lt; t < L; t += C::TG) {
-    fb[t] = make_float2(ha[t], hb[t]);
-    fb[t + L] = make_float2(0.f, 0.f);
+    fb[pad16(t)] = make_float2(ha[t], hb[t]);
+    fb[pad16(t + L)] = make_float2(0.f, 0.f);
   }
   __syncthreads();
   fft_lds<N, C::E, false>(fb, lt, tw);
-  const float s = 0.5f / (float)N;
+  const float s = 0.25f / (float)N;  // (1/2) * (1/2N) with 2 Ha, 2 Hb below
   float4* out = pq + (size_t)pr * (L + 1);
   for (int k = lt; k <= L; k += C::TG) {
-    float2 fk = fb[k], fm = conjf2(fb[(N - k) & (N - 1)]);
+    float2 fk = fb[pad16(k)], fm = conjf2(fb[pad16((N - k) & (N - 1))]);
     float2 ha2 = cadd(fk, fm);                 // 2 Ha
     float2 d = csub(fk, fm);                   // 2i Hb
     float2 hb2 = make_float2(d.y, -d.x);       // 2 Hb
     // P = (Ha + Hb) / 2N, Q = (Ha - Hb) / 2N
-    out[k] = make_float4(0.5f * s * (ha2.x + hb2.x), 0.5f * s * (ha2.y + hb2.y),
-                         0.5f * s * (ha2.x - hb2.x), 0.5f * s * (ha2.y - hb2.y));
+    out[k] = make_float4(s * (ha2.x + hb2.x), s * (ha2.y + hb2.y), s * (ha2.x - hb2.x), s * (ha2.y - hb2.y));
   }
 }
 
 // ============================================================ four-step
 
-constexpr int kN1 = 256;  // column DFT length
-constexpr int kCW = 64;   // columns per column-pass workgroup
+constexpr int kCW = 64;   // columns per column-pass workgroup (one per lane)
 
 struct ColArgs {
-  const void* p;          // projections [B][(NO+1)D][L] (storage type)
-  const float* short_w;   // [(NO+1)D][3]
+  const void* s;          // short-convolved projections [B][(NO+1)D][L] (storage type)
   const float* dskip;     // [NO][D]
   const void* zin;        // z^n [B][D][L] for n >= 1
   void* zout;             // z^{n+1} [B][D][L]
-  float2* Y;              // intermediate [pairs][256][N2]
+  void* Y;                // intermediate [pairs][N1][N2] (complex fp32 or bf16 pairs)
   const float* h;         // filter rows [NO][D][L] (filter mode)
   const float2* w256;     // W_256^m, m in [0, 256)
   const float2* tw_lo;    // W_N^m = tw_lo[m & lo_mask] * tw_hi[m >> lo_bits]
@@ -175,229 +162,335 @@ __device__ __forceinline__ float2 twN(const ColArgs& a, unsigned m) {
   return cmul(a.tw_lo[m & ((1u << a.lo_bits) - 1)], a.tw_hi[m >> a.lo_bits]);
 }
 
-// Forward column DFT. Thread (lane c, wave j) holds x[n1 = j + 16 r] in v[r]
-// (v[r] = 0 for r >= 8). Writes Y[k1][n2] * W_N^{n2 k1}.
-__device__ __forceinline__ void col_forward(const ColArgs& a, float2 (&v)[16], float2* S,
-                                            float2* Yp, int c, int w, int n2) {
+__device__ __forceinline__ float2 cvt2(float2 v) { return v; }
+__device__ __forceinline__ float2 cvt2(cbf16 v) {
+  return make_float2(__uint_as_float(v.v << 16), __uint_as_float(v.v & 0xFFFF0000u));
+}
+__device__ __forceinline__ float cvt1(float v) { return v; }
+__device__ __forceinline__ float cvt1(bf16 v) { return (float)v; }
+
+// Column DFT of N1 = R*R points, n1 = j + R r, k1 = ka + R kb.
+// Forward: thread (lane c, wave j) holds x[j + R r] in v[r] (zero for r >= R/2);
+// writes Y[k1][n2] * W_N^{n2 k1}.
+template <int R, typename YT>
+__device__ __forceinline__ void col_forward(const ColArgs& a, float2 (&v)[R], float2* S, YT* Yp, int c, int w,
+                                            int n2) {
+  constexpr int N1 = R * R;
   const unsigned N = 2u * (unsigned)a.L;
-  Dft<16, false>::run(v);
+  Dft<R, false>::run(v);
 #pragma unroll
-  for (int ka = 0; ka < 16; ++ka) {
-    if (ka) v[ka] = cmul(v[ka], a.w256[(w * ka) & 255]);
-    S[(w * 16 + ka) * kCW + c] = v[ka];
+  for (int ka = 0; ka < R; ++ka) {
+    if (ka) v[ka] = cmul(v[ka], a.w256[(w * ka * (256 / N1)) & 255]);
+    S[(w * R + ka) * kCW + c] = v[ka];
   }
   __syncthreads();
-  float2 u[16];
+  float2 u[R];
 #pragma unroll
-  for (int j = 0; j < 16; ++j) u[j] = S[(j * 16 + w) * kCW + c];
-  Dft<16, false>::run(u);
-  // k1 = w + 16 kb
+  for (int j = 0; j < R; ++j) u[j] = S[(j * R + w) * kCW + c];
+  Dft<R, false>::run(u);
+  // k1 = w + R kb
   float2 wk = twN(a, ((unsigned)n2 * (unsigned)w) & (N - 1));
-  const float2 ws = twN(a, ((unsigned)n2 * 16u) & (N - 1));
+  const float2 ws = twN(a, ((unsigned)n2 * (unsigned)R) & (N - 1));
 #pragma unroll
-  for (int kb = 0; kb < 16; ++kb) {
-    Yp[(size_t)(w + 16 * kb) * a.N2 + n2] = cmul(u[kb], wk);
+  for (int kb = 0; kb < R; ++kb) {
+    stc(Yp + (size_t)(w + R * kb) * a.N2 + n2, cmul(u[kb], wk));
     wk = cmul(wk, ws);
   }
 }
 
-// Inverse column DFT; returns out[n1 = w + 16 nb] in u[nb] for nb < 8.
-__device__ __forceinline__ void col_inverse(const ColArgs& a, float2 (&u)[16], float2* S,
-                                            const float2* Yp, int c, int w, int n2) {
+// Inverse column DFT of the loaded column y[kb] = Y[w + R kb][n2]; returns
+// out[n1 = w + R nb] in u[nb] (only nb < R/2 are needed).
+template <int R, typename YT>
+__device__ __forceinline__ void col_inverse(const ColArgs& a, float2 (&u)[R], float2* S, const YT (&y)[R], int c,
+                                            int w, int n2) {
+  constexpr int N1 = R * R;
   const unsigned N = 2u * (unsigned)a.L;
-  float2 v[16];
+  float2 v[R];
   float2 wk = twN(a, ((unsigned)n2 * (unsigned)w) & (N - 1));
-  const float2 ws = twN(a, ((unsigned)n2 * 16u) & (N - 1));
+  const float2 ws = twN(a, ((unsigned)n2 * (unsigned)R) & (N - 1));
 #pragma unroll
-  for (int kb = 0; kb < 16; ++kb) {
-    v[kb] = cmulc(Yp[(size_t)(w + 16 * kb) * a.N2 + n2], wk);
+  for (int kb = 0; kb < R; ++kb) {
+    v[kb] = cmulc(cvt2(y[kb]), wk);
     wk = cmul(wk, ws);
   }
-  Dft<16, true>::run(v);
+  Dft<R, true>::run(v);
 #pragma unroll
-  for (int na = 0; na < 16; ++na) {
-    if (na) v[na] = cmulc(v[na], a.w256[(w * na) & 255]);
-    S[(w * 16 + na) * kCW + c] = v[na];
+  for (int na = 0; na < R; ++na) {
+    if (na) v[na] = cmulc(v[na], a.w256[(w * na * (256 / N1)) & 255]);
+    S[(w * R + na) * kCW + c] = v[na];
   }
   __syncthreads();
 #pragma unroll
-  for (int ka = 0; ka < 16; ++ka) u[ka] = S[(ka * 16 + w) * kCW + c];
-  Dft<16, true>::run(u);
+  for (int ka = 0; ka < R; ++ka) u[ka] = S[(ka * R + w) * kCW + c];
+  Dft<R, true>::run(u);
 }
 
-template <typename T, int MODE>
-__global__ __launch_bounds__(1024) void colpass_kernel(ColArgs a) {
+// Persistent column pass: each workgroup walks items (channel pair, block of 64
+// columns) with a stride of gridDim.x and loads the next item's column data
+// into registers before working on the current one.
+template <typename T, typename YT, int R, int MODE>
+__global__ __launch_bounds__(64 * R) void colpass_kernel(ColArgs a, int nitems) {
+  constexpr int N1 = R * R, H = R / 2;
+  constexpr bool INVERSE = (MODE == COL_INV || MODE == COL_INV_FWD);
   extern __shared__ float4 smem4[];
   float2* S = reinterpret_cast<float2*>(smem4);
   const int c = threadIdx.x & 63, w = threadIdx.x >> 6;
-  const int n2 = blockIdx.x * kCW + c;
-  const int pr = blockIdx.y + a.pair_off;
   const int L = a.L, N2 = a.N2, D = a.D;
-  const int half = D / 2;
-  float2* Yp = a.Y + (size_t)blockIdx.y * kN1 * N2;
-  float2 v[16];
+  const int half = D / 2, ncb = N2 / kCW;
+  const size_t J = (size_t)(a.NO + 1) * D;
 
-  if (MODE == COL_FWD_H) {
-    const int n = pr / half, cp = pr % half;
-    const float* ha = a.h + ((size_t)n * D + 2 * cp) * L;
-    const float* hb = ha + L;
+  struct In {
+    YT y[R];        // inverse: column of the intermediate
+    T za[H], zb[H];  // forward of z^1: v block
+    float ha[H], hb[H];  // filter mode
+  };
+  auto load = [&](int item, In& in) {
+    const int pl = item / ncb;
+    const int n2 = (item - pl * ncb) * kCW + c;
+    const int pr = pl + a.pair_off;
+    if constexpr (MODE == COL_FWD_H) {
+      const int n = pr / half, cp = pr % half;
+      const float* ha = a.h + ((size_t)n * D + 2 * cp) * L;
 #pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      if (r < 8) {
-        const int t = N2 * (w + 16 * r) + n2;
-        v[r] = make_float2(ha[t], hb[t]);
-      } else {
-        v[r] = make_float2(0.f, 0.f);
+      for (int r = 0; r < H; ++r) {
+        const int t = N2 * (w + R * r) + n2;
+        in.ha[r] = ha[t];
+        in.hb[r] = ha[L + t];
       }
-    }
-    col_forward(a, v, S, Yp, c, w, n2);
-    return;
-  }
-
-  const int b = pr / half, cp = pr % half;
-  const int ca = 2 * cp, cb = ca + 1;
-  const T* pb = reinterpret_cast<const T*>(a.p) + (size_t)b * (a.NO + 1) * D * L;
-
-  if (MODE == COL_FWD_V) {
+    } else if constexpr (MODE == COL_FWD_V) {
+      const int b = pr / half, cp = pr % half;
+      const T* sv = reinterpret_cast<const T*>(a.s) + (size_t)b * J * L + (size_t)(2 * cp) * L;
 #pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      if (r < 8) {
-        const int t = N2 * (w + 16 * r) + n2;
-        v[r] = make_float2(short_conv_at(pb + (size_t)ca * L, a.short_w + 3 * ca, t),
-                           short_conv_at(pb + (size_t)cb * L, a.short_w + 3 * cb, t));
-      } else {
-        v[r] = make_float2(0.f, 0.f);
+      for (int r = 0; r < H; ++r) {
+        const int t = N2 * (w + R * r) + n2;
+        in.za[r] = sv[t];
+        in.zb[r] = sv[L + t];
       }
-    }
-    col_forward(a, v, S, Yp, c, w, n2);
-    return;
-  }
-
-  // inverse, gate, skip
-  float2 u[16];
-  col_inverse(a, u, S, Yp, c, w, n2);
-  const int n = a.n;
-  const int jx = (n + 1) * D;
-  const float da = a.dskip[n * D + ca], db = a.dskip[n * D + cb];
-  const T* zin = reinterpret_cast<const T*>(a.zin) + (size_t)b * D * L;
-  T* zo = reinterpret_cast<T*>(a.zout) + (size_t)b * D * L;
-#pragma unroll
-  for (int nb = 0; nb < 16; ++nb) {
-    if (nb < 8) {
-      const int t = N2 * (w + 16 * nb) + n2;
-      float xa = short_conv_at(pb + (size_t)(jx + ca) * L, a.short_w + 3 * (jx + ca), t);
-      float xb = short_conv_at(pb + (size_t)(jx + cb) * L, a.short_w + 3 * (jx + cb), t);
-      float zpa, zpb;
-      if (n == 0) {
-        zpa = short_conv_at(pb + (size_t)ca * L, a.short_w + 3 * ca, t);
-        zpb = short_conv_at(pb + (size_t)cb * L, a.short_w + 3 * cb, t);
-      } else {
-        zpa = ldf(zin + (size_t)ca * L + t);
-        zpb = ldf(zin + (size_t)cb * L + t);
-      }
-      float na = xa * u[nb].x + da * zpa;
-      float nbv = xb * u[nb].y + db * zpb;
-      stf(zo + (size_t)ca * L + t, na);
-      stf(zo + (size_t)cb * L + t, nbv);
-      v[nb] = make_float2(na, nbv);
     } else {
-      v[nb] = make_float2(0.f, 0.f);
+      const YT* Yp = reinterpret_cast<const YT*>(a.Y) + (size_t)pl * N1 * N2;
+#pragma unroll
+      for (int kb = 0; kb < R; ++kb) in.y[kb] = Yp[(size_t)(w + R * kb) * N2 + n2];
     }
-  }
-  if (MODE == COL_INV_FWD) {
-    __syncthreads();  // S is reused
-    col_forward(a, v, S, Yp, c, w, n2);
+  };
+
+  auto process = [&](int item, const In& in) {
+    const int pl = item / ncb;
+    const int n2 = (item - pl * ncb) * kCW + c;
+    const int pr = pl + a.pair_off;
+    YT* Yp = reinterpret_cast<YT*>(a.Y) + (size_t)pl * N1 * N2;
+    float2 v[R];
+    if constexpr (MODE == COL_FWD_H) {
+#pragma unroll
+      for (int r = 0; r < R; ++r) v[r] = r < H ? make_float2(in.ha[r], in.hb[r]) : make_float2(0.f, 0.f);
+      col_forward<R>(a, v, S, Yp, c, w, n2);
+    } else if constexpr (MODE == COL_FWD_V) {
+#pragma unroll
+      for (int r = 0; r < R; ++r) v[r] = r < H ? make_float2(cvt1(in.za[r]), cvt1(in.zb[r])) : make_float2(0.f, 0.f);
+      col_forward<R>(a, v, S, Yp, c, w, n2);
+    } else {
+      const int b = pr / half, cp = pr % half;
+      const int ca = 2 * cp, cb = ca + 1;
+      const int n = a.n;
+      const T* sb = reinterpret_cast<const T*>(a.s) + (size_t)b * J * L;
+      const T* sx = sb + (size_t)((n + 1) * D + ca) * L;
+      const T* zp = (n == 0) ? sb + (size_t)ca * L : reinterpret_cast<const T*>(a.zin) + ((size_t)b * D + ca) * L;
+      // gate inputs of this item: issued before the inverse DFT so that their
+      // latency overlaps it
+      T xa[H], xb[H], za[H], zb[H];
+#pragma unroll
+      for (int nb = 0; nb < H; ++nb) {
+        const int t = N2 * (w + R * nb) + n2;
+        xa[nb] = sx[t];
+        xb[nb] = sx[L + t];
+        za[nb] = zp[t];
+        zb[nb] = zp[L + t];
+      }
+      float2 u[R];
+      col_inverse<R>(a, u, S, in.y, c, w, n2);
+      const float da = a.dskip[n * D + ca], db = a.dskip[n * D + cb];
+      T* zo = reinterpret_cast<T*>(a.zout) + ((size_t)b * D + ca) * L;
+#pragma unroll
+      for (int nb = 0; nb < R; ++nb) {
+        if (nb < H) {
+          const int t = N2 * (w + R * nb) + n2;
+          const float na = cvt1(xa[nb]) * u[nb].x + da * cvt1(za[nb]);
+          const float nbv = cvt1(xb[nb]) * u[nb].y + db * cvt1(zb[nb]);
+          stf(zo + t, na);
+          stf(zo + L + t, nbv);
+          v[nb] = make_float2(na, nbv);
+        } else {
+          v[nb] = make_float2(0.f, 0.f);
+        }
+      }
+      if constexpr (MODE == COL_INV_FWD) {
+        __syncthreads();  // S is reused
+        col_forward<R>(a, v, S, Yp, c, w, n2);
+      }
+    }
+  };
+
+  int item = blockIdx.x;
+  if (item >= nitems) return;
+  In cur;
+  load(item, cur);
+  while (true) {
+    const int next = item + gridDim.x;
+    const bool more = next < nitems;
+    In nxt;
+    if (more) load(next, nxt);
+    process(item, cur);
+    if (!more) break;
+    cur = nxt;
+    item = next;
+    __syncthreads();  // S of this item fully read before the next one writes it
   }
 }
 
-// Row pass: N2-point DFTs of rows k1 and 256 - k1 (rows 0 and 128 for slot 0).
+// Row pass: N2-point DFTs of rows k1 and N1 - k1 (rows 0 and N1/2 for slot 0).
 template <int N2> struct RowCfg {
   static constexpr int E = 16;
-  static constexpr int TG = N2 / E;                    // threads per row
-  static constexpr int SP = N2 >= 4096 ? 1 : 4096 / N2;  // row pairs per workgroup
+  static constexpr int TG = N2 / E;                      // threads per row
+  static constexpr int SP = N2 >= 2048 ? 1 : 2048 / N2;  // row pairs per workgroup
   static constexpr int WG = SP * 2 * TG;
+  static constexpr int RB = padded_len(N2);              // float2 per row buffer
+  static constexpr size_t LDS = (size_t)SP * 2 * RB * 8;
+  static constexpr int PER = N2 / TG;                    // row elements per thread
 };
 
 enum { ROW_CONV = 0, ROW_SPEC = 1 };
 
-template <int N2, int MODE>
-__global__ __launch_bounds__(RowCfg<N2>::WG) void rowpass_kernel(float2* __restrict__ Y, float4* __restrict__ pq,
+// Persistent row pass; items are (channel pair, group of SP slots). The next
+// item's rows are loaded into registers before the current item is processed.
+template <typename YT, int N1, int N2, int MODE>
+__global__ __launch_bounds__(RowCfg<N2>::WG) void rowpass_kernel(YT* __restrict__ Y, float4* __restrict__ pq,
                                                                  const float2* __restrict__ tw_row, int pq_off,
-                                                                 int pair_off, int pq_mod) {
+                                                                 int pair_off, int pq_mod, int nitems) {
   using C = RowCfg<N2>;
+  constexpr int HALF = N1 / 2;
+  constexpr int PQROWS = HALF + 1;
+  constexpr int NSG = HALF / C::SP;  // slot groups per channel pair
+  constexpr int PER = C::PER;
   extern __shared__ float4 smem4[];
   float2* rows = reinterpret_cast<float2*>(smem4);
   const int r = threadIdx.x / C::TG, lt = threadIdx.x % C::TG;
-  const int s = blockIdx.x * C::SP + r / 2;      // slot 0..127
   const int isB = r & 1;
-  const int k1 = isB ? (s == 0 ? 128 : 256 - s) : s;
-  float2* Yr = Y + ((size_t)blockIdx.y * kN1 + k1) * N2;
-  float2* row = rows + r * N2;
-  for (int i = lt; i < N2; i += C::TG) row[i] = Yr[i];
-  __syncthreads();
-  fft_lds<N2, C::E, false>(row, lt, tw_row);
-  // (P, Q) rows of this channel pair: 129 rows of N2
-  // filters are shared by every batch: pair (b, cp) uses the rows of cp
-  float4* pqp = pq + ((size_t)pq_off + (blockIdx.y + pair_off) % pq_mod) * 129 * N2;
-  const float nrm = 0.25f / (float)(kN1 * N2);  // (1/2)(1/2N) with 2 Ha, 2 Hb below
-  if (s != 0) {
-    float2* ra = rows + (r & ~1) * N2;
-    float2* rb = ra + N2;
-    const float4* pqs = pqp + (size_t)s * N2;
-    for (int k2 = isB * C::TG + lt; k2 < N2; k2 += 2 * C::TG) {
-      const int m2 = N2 - 1 - k2;
-      float2 xk = ra[k2], xm = rb[m2];
-      if (MODE == ROW_CONV) {
-        float4 q = pqs[k2];
-        float2 P = make_float2(q.x, q.y), Q = make_float2(q.z, q.w);
-        ra[k2] = cadd(cmul(xk, P), cmul(conjf2(xm), Q));
-        rb[m2] = cadd(cmulc(xm, P), cmulc(conjf2(xk), Q));
-      } else {
-        float2 fm = conjf2(xm);
-        float2 ha2 = cadd(xk, fm), d = csub(xk, fm);
-        float2 hb2 = make_float2(d.y, -d.x);
-        pqp[(size_t)s * N2 + k2] = make_float4(nrm * (ha2.x + hb2.x), nrm * (ha2.y + hb2.y),
-                                               nrm * (ha2.x - hb2.x), nrm * (ha2.y - hb2.y));
+  float2* row = rows + r * C::RB;
+  const float nrm = 0.25f / (float)(N1 * N2);  // (1/2)(1/2N) with 2 Ha, 2 Hb below
+
+  auto row_of = [&](int item, int& pl, int& s) {
+    pl = item / NSG;
+    s = (item - pl * NSG) * C::SP + r / 2;   // slot 0 .. N1/2 - 1
+    return isB ? (s == 0 ? HALF : N1 - s) : s;
+  };
+  auto load = [&](int item, YT (&y)[PER]) {
+    int pl, s;
+    const int k1 = row_of(item, pl, s);
+    const YT* Yr = Y + ((size_t)pl * N1 + k1) * N2;
+#pragma unroll
+    for (int q = 0; q < PER; ++q) y[q] = Yr[lt + q * C::TG];
+  };
+
+  auto process = [&](int item, const YT (&y)[PER]) {
+    int pl, s;
+    const int k1 = row_of(item, pl, s);
+    // filters are shared by every batch: pair (b, cp) uses the rows of cp
+    float4* pqp = pq + ((size_t)pq_off + (pl + pair_off) % pq_mod) * PQROWS * N2;
+    // spectrum rows of this item, issued before the forward DFT
+    float4 pv[PER / 2];
+    if (MODE == ROW_CONV && s != 0) {
+      const float4* pqs = pqp + (size_t)s * N2;
+#pragma unroll
+      for (int q = 0; q < PER / 2; ++q) pv[q] = pqs[isB * C::TG + lt + q * 2 * C::TG];
+    }
+#pragma unroll
+    for (int q = 0; q < PER; ++q) row[pad16(lt + q * C::TG)] = cvt2(y[q]);
+    __syncthreads();
+    fft_lds<N2, C::E, false>(row, lt, tw_row);
+    if (s != 0) {
+      float2* ra = rows + (r & ~1) * C::RB;
+      float2* rb = ra + C::RB;
+#pragma unroll
+      for (int q = 0; q < PER / 2; ++q) {
+        const int k2 = isB * C::TG + lt + q * 2 * C::TG;
+        const int m2 = N2 - 1 - k2;
+        float2 xk = ra[pad16(k2)], xm = rb[pad16(m2)];
+        if (MODE == ROW_CONV) {
+          float2 P = make_float2(pv[q].x, pv[q].y), Q = make_float2(pv[q].z, pv[q].w);
+          ra[pad16(k2)] = cadd(cmul(xk, P), cmul(conjf2(xm), Q));
+          rb[pad16(m2)] = cadd(cmulc(xm, P), cmulc(conjf2(xk), Q));
+        } else {
+          float2 fm = conjf2(xm);
+          float2 ha2 = cadd(xk, fm), d = csub(xk, fm);
+          float2 hb2 = make_float2(d.y, -d.x);
+          pqp[(size_t)s * N2 + k2] = make_float4(nrm * (ha2.x + hb2.x), nrm * (ha2.y + hb2.y),
+                                                 nrm * (ha2.x - hb2.x), nrm * (ha2.y - hb2.y));
+        }
+      }
+    } else {
+      // row 0 pairs k2 with (N2 - k2) mod N2; row N1/2 pairs k2 with N2 - 1 - k2
+      const int pqrow = isB ? HALF : 0;
+      const float4* pqs = pqp + (size_t)pqrow * N2;
+      const int kend = (MODE == ROW_CONV) ? (isB ? N2 / 2 - 1 : N2 / 2) : N2 - 1;
+      for (int k2 = lt; k2 <= kend; k2 += C::TG) {
+        const int m2 = isB ? (N2 - 1 - k2) : ((N2 - k2) & (N2 - 1));
+        float2 xk = row[pad16(k2)], xm = row[pad16(m2)];
+        if (MODE == ROW_CONV) {
+          float4 q = pqs[k2];
+          float2 P = make_float2(q.x, q.y), Q = make_float2(q.z, q.w);
+          float2 yk = cadd(cmul(xk, P), cmul(conjf2(xm), Q));
+          if (m2 != k2) row[pad16(m2)] = cadd(cmulc(xm, P), cmulc(conjf2(xk), Q));
+          row[pad16(k2)] = yk;
+        } else {
+          float2 fm = conjf2(xm);
+          float2 ha2 = cadd(xk, fm), d = csub(xk, fm);
+          float2 hb2 = make_float2(d.y, -d.x);
+          pqp[(size_t)pqrow * N2 + k2] = make_float4(nrm * (ha2.x + hb2.x), nrm * (ha2.y + hb2.y),
+                                                     nrm * (ha2.x - hb2.x), nrm * (ha2.y - hb2.y));
+        }
       }
     }
-  } else {
-    // row 0 pairs k2 with (N2 - k2) mod N2; row 128 pairs k2 with N2 - 1 - k2
-    const int pqrow = isB ? 128 : 0;
-    const float4* pqs = pqp + (size_t)pqrow * N2;
-    const int kend = (MODE == ROW_CONV) ? (isB ? N2 / 2 - 1 : N2 / 2) : N2 - 1;
-    for (int k2 = lt; k2 <= kend; k2 += C::TG) {
-      const int m2 = isB ? (N2 - 1 - k2) : ((N2 - k2) & (N2 - 1));
-      float2 xk = row[k2], xm = row[m2];
-      if (MODE == ROW_CONV) {
-        float4 q = pqs[k2];
-        float2 P = make_float2(q.x, q.y), Q = make_float2(q.z, q.w);
-        float2 yk = cadd(cmul(xk, P), cmul(conjf2(xm), Q));
-        if (m2 != k2) row[m2] = cadd(cmulc(xm, P), cmulc(conjf2(xk), Q));
-        row[k2] = yk;
-      } else {
-        float2 fm = conjf2(xm);
-        float2 ha2 = cadd(xk, fm), d = csub(xk, fm);
-        float2 hb2 = make_float2(d.y, -d.x);
-        pqp[(size_t)pqrow * N2 + k2] = make_float4(nrm * (ha2.x + hb2.x), nrm * (ha2.y + hb2.y),
-                                                   nrm * (ha2.x - hb2.x), nrm * (ha2.y - hb2.y));
-      }
-    }
+    if (MODE == ROW_SPEC) return;
+    __syncthreads();
+    fft_lds<N2, C::E, true>(row, lt, tw_row);
+    YT* Yr = Y + ((size_t)pl * N1 + k1) * N2;
+#pragma unroll
+    for (int q = 0; q < PER; ++q) stc(Yr + lt + q * C::TG, row[pad16(lt + q * C::TG)]);
+  };
+
+  int item = blockIdx.x;
+  if (item >= nitems) return;
+  YT cur[PER];
+  load(item, cur);
+  while (true) {
+    const int next = item + gridDim.x;
+    const bool more = next < nitems;
+    YT nxt[PER];
+    if (more) load(next, nxt);
+    process(item, cur);
+    if (!more) break;
+#pragma unroll
+    for (int q = 0; q < PER; ++q) cur[q] = nxt[q];
+    item = next;
+    __syncthreads();  // rows of this item fully read before the next one writes them
   }
-  if (MODE == ROW_SPEC) return;
-  __syncthreads();
-  fft_lds<N2, C::E, true>(row, lt, tw_row);
-  for (int i = lt; i < N2; i += C::TG) Yr[i] = row[i];
 }
 
 // ============================================================ launchers
+
+static hipError_t allow_lds(const void* fn, size_t bytes) {
+  if (bytes <= 65536) return hipSuccess;
+  return hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)bytes);
+}
 
 template <typename T, int N>
 static hipError_t launch_lds_conv(const LdsConvArgs& a, hipStream_t s) {
   using C = LdsCfg<N>;
   const int pairs = a.B * a.D / 2;
-  const size_t lds = (size_t)C::G * N * 12;
-  hipLaunchKernelGGL((fftconv_lds_kernel<T, N>), dim3(pairs / C::G), dim3(C::WG), lds, s,
-                     (const T*)a.p, a.short_w, a.dskip, a.pq, a.tw, (T*)a.zout, a.D, a.NO);
+  auto fn = fftconv_lds_kernel<T, N>;
+  hipError_t e = allow_lds((const void*)fn, C::LDS);
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(fn, dim3(pairs / C::G), dim3(C::WG), C::LDS, s, (const T*)a.s, a.dskip, a.pq, a.tw,
+                     (T*)a.zout, a.D, a.NO);
   return hipGetLastError();
 }
 
@@ -405,8 +498,11 @@ template <int N>
 static hipError_t launch_lds_spec(const float* h, const float2* tw, float4* pq, int D, int NO, hipStream_t s) {
   using C = LdsCfg<N>;
   const int pairs = NO * D / 2;
-  hipLaunchKernelGGL((filter_spec_lds_kernel<N>), dim3(pairs / C::G), dim3(C::WG), (size_t)C::G * N * 8, s,
-                     h, tw, pq, D, NO);
+  const size_t lds = (size_t)C::G * C::FB * 8;
+  auto fn = filter_spec_lds_kernel<N>;
+  hipError_t e = allow_lds((const void*)fn, lds);
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(fn, dim3(pairs / C::G), dim3(C::WG), lds, s, h, tw, pq, D, NO);
   return hipGetLastError();
 }
 
@@ -448,77 +544,93 @@ hipError_t lds_spec(const float* h, const float2* tw, float4* pq, int L, int D, 
   return e;
 }
 
-size_t lds_conv_smem(int L) {
-  const int N = 2 * L;
-  int G = 1;
-#define CALLG(n) G = LdsCfg<n>::G
-  switch (N) {
-    case 32: CALLG(32); break;
-    case 64: CALLG(64); break;
-    case 128: CALLG(128); break;
-    case 256: CALLG(256); break;
-    case 512: CALLG(512); break;
-    case 1024: CALLG(1024); break;
-    case 2048: CALLG(2048); break;
-    case 4096: CALLG(4096); break;
-    case 8192: CALLG(8192); break;
-    default: return 0;
+// Workgroups of a persistent launch: as many as are resident at once.
+static int resident_grid(const void* fn, int block, size_t lds, int items) {
+  static int cus = 0;
+  if (cus == 0) {
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess ||
+        hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0)
+      cus = 256;
   }
-#undef CALLG
-  return (size_t)G * N * 12;
+  int per_cu = 0;
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, fn, block, lds) != hipSuccess || per_cu <= 0) per_cu = 1;
+  const long long g = (long long)cus * per_cu;
+  return (int)(g < items ? g : items);
 }
 
-static hipError_t launch_col(const ColArgs& a, int mode, bool is_bf16, int pairs, hipStream_t s) {
-  dim3 grid(a.N2 / kCW, pairs), block(1024);
-  const size_t lds = 16 * 16 * kCW * sizeof(float2);
-#define COLCASE(T, M) hipLaunchKernelGGL((colpass_kernel<T, M>), grid, block, lds, s, a)
-  if (is_bf16) {
-    switch (mode) {
-      case COL_FWD_V: COLCASE(bf16, COL_FWD_V); break;
-      case COL_FWD_H: COLCASE(bf16, COL_FWD_H); break;
-      case COL_INV: COLCASE(bf16, COL_INV); break;
-      default: COLCASE(bf16, COL_INV_FWD); break;
-    }
-  } else {
-    switch (mode) {
-      case COL_FWD_V: COLCASE(float, COL_FWD_V); break;
-      case COL_FWD_H: COLCASE(float, COL_FWD_H); break;
-      case COL_INV: COLCASE(float, COL_INV); break;
-      default: COLCASE(float, COL_INV_FWD); break;
-    }
-  }
-#undef COLCASE
+template <typename T, typename YT, int R, int M>
+static hipError_t launch_col_t(const ColArgs& a, int pairs, hipStream_t s) {
+  const size_t lds = (size_t)R * R * kCW * sizeof(float2);
+  auto fn = colpass_kernel<T, YT, R, M>;
+  hipError_t e = allow_lds((const void*)fn, lds);
+  if (e != hipSuccess) return e;
+  const int items = pairs * (a.N2 / kCW);
+  static int grid = 0;
+  if (grid == 0) grid = resident_grid((const void*)fn, 64 * R, lds, 1 << 30);
+  hipLaunchKernelGGL(fn, dim3(grid < items ? grid : items), dim3(64 * R), lds, s, a, items);
   return hipGetLastError();
 }
 
-template <int N2>
-static hipError_t launch_row_t(float2* Y, float4* pq, const float2* tw_row, int pq_off, int pair_off,
-                               int pq_mod, int pairs, int mode, hipStream_t s) {
+template <typename T, typename YT, int R>
+static hipError_t launch_col_r(const ColArgs& a, int mode, int pairs, hipStream_t s) {
+  switch (mode) {
+    case COL_FWD_V: return launch_col_t<T, YT, R, COL_FWD_V>(a, pairs, s);
+    case COL_FWD_H: return launch_col_t<float, float2, R, COL_FWD_H>(a, pairs, s);
+    case COL_INV: return launch_col_t<T, YT, R, COL_INV>(a, pairs, s);
+    default: return launch_col_t<T, YT, R, COL_INV_FWD>(a, pairs, s);
+  }
+}
+
+// act_bf16: activation storage; ybf: intermediate stored as bf16 pairs
+static hipError_t launch_col(const ColArgs& a, int N1, int mode, bool act_bf16, bool ybf, int pairs,
+                             hipStream_t s) {
+  if (N1 == 64) {
+    if (act_bf16) return ybf ? launch_col_r<bf16, cbf16, 8>(a, mode, pairs, s)
+                             : launch_col_r<bf16, float2, 8>(a, mode, pairs, s);
+    return launch_col_r<float, float2, 8>(a, mode, pairs, s);
+  }
+  if (N1 == 256) {
+    if (act_bf16) return ybf ? launch_col_r<bf16, cbf16, 16>(a, mode, pairs, s)
+                             : launch_col_r<bf16, float2, 16>(a, mode, pairs, s);
+    return launch_col_r<float, float2, 16>(a, mode, pairs, s);
+  }
+  return hipErrorInvalidValue;
+}
+
+template <typename YT, int N1, int N2>
+static hipError_t launch_row_t(void* Y, float4* pq, const float2* tw_row, int pq_off, int pair_off, int pq_mod,
+                               int pairs, int mode, hipStream_t s) {
   using C = RowCfg<N2>;
-  dim3 grid(128 / C::SP, pairs), block(C::WG);
-  const size_t lds = (size_t)C::SP * 2 * N2 * sizeof(float2);
-  if (mode == ROW_CONV)
-    hipLaunchKernelGGL((rowpass_kernel<N2, ROW_CONV>), grid, block, lds, s, Y, pq, tw_row, pq_off, pair_off, pq_mod);
-  else
-    hipLaunchKernelGGL((rowpass_kernel<N2, ROW_SPEC>), grid, block, lds, s, Y, pq, tw_row, pq_off, pair_off, pq_mod);
+  const int items = pairs * ((N1 / 2) / C::SP);
+  YT* y = static_cast<YT*>(Y);
+  auto fn = (mode == ROW_CONV) ? rowpass_kernel<YT, N1, N2, ROW_CONV> : rowpass_kernel<YT, N1, N2, ROW_SPEC>;
+  hipError_t e = allow_lds((const void*)fn, C::LDS);
+  if (e != hipSuccess) return e;
+  static int grid[2] = {0, 0};
+  int& g = grid[mode == ROW_CONV ? 0 : 1];
+  if (g == 0) g = resident_grid((const void*)fn, C::WG, C::LDS, 1 << 30);
+  hipLaunchKernelGGL(fn, dim3(g < items ? g : items), dim3(C::WG), C::LDS, s, y, pq, tw_row, pq_off, pair_off,
+                     pq_mod, items);
   return hipGetLastError();
 }
 
-static hipError_t launch_row(int N2, float2* Y, float4* pq, const float2* tw_row, int pq_off, int pair_off,
-                             int pq_mod, int pairs, int mode, hipStream_t s) {
-#define ROWCASE(n) case n: return launch_row_t<n>(Y, pq, tw_row, pq_off, pair_off, pq_mod, pairs, mode, s)
-  switch (N2) {
-    ROWCASE(64);
-    ROWCASE(128);
-    ROWCASE(256);
-    ROWCASE(512);
-    ROWCASE(1024);
-    ROWCASE(2048);
-    ROWCASE(4096);
-    ROWCASE(8192);
-    default: return hipErrorInvalidValue;
-  }
+template <typename YT>
+static hipError_t launch_row_y(int N1, int N2, void* Y, float4* pq, const float2* tw_row, int pq_off, int pair_off,
+                               int pq_mod, int pairs, int mode, hipStream_t s) {
+#define ROWCASE(n1, n2)                                                                                  \
+  if (N1 == n1 && N2 == n2)                                                                              \
+    return launch_row_t<YT, n1, n2>(Y, pq, tw_row, pq_off, pair_off, pq_mod, pairs, mode, s);
+  ROWCASE(64, 256)
+  ROWCASE(64, 512)
+  ROWCASE(64, 1024)
+  ROWCASE(64, 2048)
+  ROWCASE(256, 1024)
+  ROWCASE(256, 2048)
+  ROWCASE(256, 4096)
+  ROWCASE(256, 8192)
 #undef ROWCASE
+  return hipErrorInvalidValue;
 }
 
 static ColArgs col_args(const FourStepTables& tb, int L, int D, int NO) {
@@ -528,7 +640,7 @@ static ColArgs col_args(const FourStepTables& tb, int L, int D, int NO) {
   a.tw_hi = tb.tw_hi;
   a.lo_bits = tb.lo_bits;
   a.L = L;
-  a.N2 = 2 * L / kN1;
+  a.N2 = 2 * L / fourstep_n1(L);
   a.D = D;
   a.NO = NO;
   return a;
@@ -537,39 +649,44 @@ static ColArgs col_args(const FourStepTables& tb, int L, int D, int NO) {
 hipError_t fourstep_spec(const FourStepTables& tb, const float* h, float2* Y, float4* pq, int L, int D, int NO,
                          hipStream_t s) {
   ColArgs a = col_args(tb, L, D, NO);
+  const int N1 = fourstep_n1(L);
   a.h = h;
   a.Y = Y;
   const int pairs = NO * D / 2;
-  hipError_t e = launch_col(a, COL_FWD_H, false, pairs, s);
+  hipError_t e = launch_col(a, N1, COL_FWD_H, false, false, pairs, s);
   if (e != hipSuccess) return e;
-  return launch_row(a.N2, Y, pq, tb.tw_row, 0, 0, pairs, pairs, ROW_SPEC, s);
+  return launch_row_y<float2>(N1, a.N2, Y, pq, tb.tw_row, 0, 0, pairs, pairs, ROW_SPEC, s);
 }
 
 hipError_t fourstep_conv(const FourStepTables& tb, const FourStepConvArgs& c, bool is_bf16, hipStream_t s) {
   ColArgs a = col_args(tb, c.L, c.D, c.NO);
-  a.p = c.p;
-  a.short_w = c.short_w;
+  const int N1 = fourstep_n1(c.L);
+  a.s = c.s;
   a.dskip = c.dskip;
   a.Y = c.Y;
+  const bool ybf = is_bf16 && c.y_bf16;
   const int half = c.D / 2;
   const int pairs_all = c.B * half;
-  // Channel-pair groups bound the intermediate (8 * 2L bytes per pair) so that
-  // it can stay in the last-level cache between the passes of one group.
+  // Channel-pair groups bound the intermediate so that it can stay in the
+  // last-level cache between the passes of one group.
   const int gp = (c.group_pairs > 0 && c.group_pairs < pairs_all) ? c.group_pairs : pairs_all;
   for (int p0 = 0; p0 < pairs_all; p0 += gp) {
     const int np = (pairs_all - p0 < gp) ? pairs_all - p0 : gp;
     ColArgs g = a;
     g.pair_off = p0;
-    hipError_t e = launch_col(g, COL_FWD_V, is_bf16, np, s);
+    hipError_t e = launch_col(g, N1, COL_FWD_V, is_bf16, ybf, np, s);
     if (e != hipSuccess) return e;
     for (int n = 0; n < c.NO; ++n) {
-      e = launch_row(a.N2, c.Y, const_cast<float4*>(c.pq), tb.tw_row, n * half, p0, half, np, ROW_CONV, s);
+      e = ybf ? launch_row_y<cbf16>(N1, a.N2, c.Y, const_cast<float4*>(c.pq), tb.tw_row, n * half, p0, half, np,
+                                    ROW_CONV, s)
+              : launch_row_y<float2>(N1, a.N2, c.Y, const_cast<float4*>(c.pq), tb.tw_row, n * half, p0, half, np,
+                                     ROW_CONV, s);
       if (e != hipSuccess) return e;
       ColArgs gi = g;
       gi.n = n;
       gi.zin = (n == 0) ? nullptr : c.z[(n - 1) & 1];
       gi.zout = (n == c.NO - 1) ? c.zfinal : c.z[n & 1];
-      e = launch_col(gi, (n == c.NO - 1) ? COL_INV : COL_INV_FWD, is_bf16, np, s);
+      e = launch_col(gi, N1, (n == c.NO - 1) ? COL_INV : COL_INV_FWD, is_bf16, ybf, np, s);
       if (e != hipSuccess) return e;
     }
   }

@@ -8,6 +8,11 @@
 //    produces); tiles are loaded along M and transposed while stored to LDS.
 //  * C_CM: C is written channel-major [Bsz][N][Lseq] (the layout the long
 //    convolution consumes), staged through LDS for 16-byte stores.
+//  * SC (with C_CM): the causal length-3 depthwise short convolution along the
+//    sequence is applied in the epilogue, s_t = w0 p_t + w1 p_{t-1} + w2 p_{t-2}
+//    (zero history at the start of every sequence). M-tiles then overlap by 8
+//    rows: a tile computes rows [m0 - 8, m0 + 120) and writes [m0, m0 + 120), so
+//    the two previous rows of every written row are on chip.
 // bf16 storage uses v_mfma_f32_32x32x16_bf16, fp32 uses v_mfma_f32_32x32x2_f32;
 // accumulation is fp32 in both cases.
 #include "common.h"
@@ -28,9 +33,12 @@ template <typename T> struct GemmCfg {
 
 constexpr int kCsLd = GBM + 4;  // staging row (floats) for channel-major output
 
-template <typename T, bool A_CM, bool C_CM>
+constexpr int kScRows = 120;  // rows written per M-tile with the short-conv epilogue
+
+template <typename T, bool A_CM, bool C_CM, bool SC>
 __global__ __launch_bounds__(256, 2) void gemm_kernel(const T* __restrict__ A, const T* __restrict__ Bt,
-                                                      T* __restrict__ C, int M, int N, int K, int Lseq) {
+                                                      T* __restrict__ C, int M, int N, int K, int Lseq,
+                                                      const float* __restrict__ short_w) {
   using Cfg = GemmCfg<T>;
   constexpr int BK = Cfg::BK, LDK = Cfg::LDK, VEC = Cfg::VEC;
   constexpr int TILE_BYTES = 2 * GBM * LDK * (int)sizeof(T);
@@ -41,7 +49,8 @@ __global__ __launch_bounds__(256, 2) void gemm_kernel(const T* __restrict__ A, c
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int wm = wave >> 1, wn = wave & 1;
-  const int n0 = blockIdx.x * GBN, m0 = blockIdx.y * GBM;
+  const int n0 = blockIdx.x * GBN;
+  const int m0 = SC ? (int)blockIdx.y * kScRows - 8 : (int)blockIdx.y * GBM;  // first A row of the tile
 
   f32x16 acc[2][2];
 #pragma unroll
@@ -59,7 +68,8 @@ __global__ __launch_bounds__(256, 2) void gemm_kernel(const T* __restrict__ A, c
       if (!A_CM) {
         const int row = c >> 2, kc = (c & 3) * VEC;
         const int m = m0 + row;
-        ra[i] = (m < M) ? *reinterpret_cast<const uint4*>(A + (size_t)m * K + k0 + kc) : make_uint4(0, 0, 0, 0);
+        ra[i] = (m >= 0 && m < M) ? *reinterpret_cast<const uint4*>(A + (size_t)m * K + k0 + kc)
+                                  : make_uint4(0, 0, 0, 0);
       } else {
         constexpr int CPR = GBM / VEC;  // chunks per k-row
         const int k = c / CPR, mc = (c % CPR) * VEC;
@@ -171,24 +181,37 @@ __global__ __launch_bounds__(256, 2) void gemm_kernel(const T* __restrict__ A, c
           }
     }
     __syncthreads();
-    // 64 rows (n) x 128 (m) in chunks of 8 consecutive m
-#pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      const int c = tid + q * 256;
+    // 64 rows (n) x 128 (m) in chunks of 8 consecutive m; with SC the first
+    // chunk of every row (the 8 overlap rows) is not written
+    for (int c = tid; c < 64 * 16; c += 256) {
       const int nl = c >> 4, mc = (c & 15) * 8;
       const int n = n0 + h * 64 + nl, m = m0 + mc;
-      if (n < N && m < M) {
+      if (n < N && m < M && (!SC || mc >= 8)) {
         const int b = m / Lseq, t = m - b * Lseq;
         T* dst = C + ((size_t)b * N + n) * Lseq + t;
         const float* src = Cs + nl * kCsLd + mc;
-        if constexpr (sizeof(T) == 2) {
-          bf16x8 o;
+        float o[8];
+        if (SC) {
+          const float w0 = short_w[3 * n], w1 = short_w[3 * n + 1], w2 = short_w[3 * n + 2];
 #pragma unroll
-          for (int v = 0; v < 8; ++v) o[v] = (__bf16)src[v];
-          *reinterpret_cast<bf16x8*>(dst) = o;
+          for (int v = 0; v < 8; ++v) {
+            float s = w0 * src[v];
+            if (t + v >= 1) s += w1 * src[v - 1];
+            if (t + v >= 2) s += w2 * src[v - 2];
+            o[v] = s;
+          }
         } else {
-          *reinterpret_cast<float4*>(dst) = make_float4(src[0], src[1], src[2], src[3]);
-          *reinterpret_cast<float4*>(dst + 4) = make_float4(src[4], src[5], src[6], src[7]);
+#pragma unroll
+          for (int v = 0; v < 8; ++v) o[v] = src[v];
+        }
+        if constexpr (sizeof(T) == 2) {
+          bf16x8 ob;
+#pragma unroll
+          for (int v = 0; v < 8; ++v) ob[v] = (__bf16)o[v];
+          *reinterpret_cast<bf16x8*>(dst) = ob;
+        } else {
+          *reinterpret_cast<float4*>(dst) = make_float4(o[0], o[1], o[2], o[3]);
+          *reinterpret_cast<float4*>(dst + 4) = make_float4(o[4], o[5], o[6], o[7]);
         }
       }
     }
@@ -198,18 +221,27 @@ __global__ __launch_bounds__(256, 2) void gemm_kernel(const T* __restrict__ A, c
 
 template <typename T>
 static hipError_t launch_gemm(const GemmArgs& g, hipStream_t s) {
-  dim3 grid((g.N + GBN - 1) / GBN, (g.M + GBM - 1) / GBM), block(256);
+  const bool sc = g.short_w != nullptr;
+  const int mtiles = sc ? (g.M + kScRows - 1) / kScRows : (g.M + GBM - 1) / GBM;
+  dim3 grid((g.N + GBN - 1) / GBN, mtiles), block(256);
   const T* A = static_cast<const T*>(g.A);
   const T* B = static_cast<const T*>(g.Bt);
   T* C = static_cast<T*>(g.C);
-  if (g.a_cm && g.c_cm)
-    hipLaunchKernelGGL((gemm_kernel<T, true, true>), grid, block, 0, s, A, B, C, g.M, g.N, g.K, g.Lseq);
-  else if (g.a_cm)
-    hipLaunchKernelGGL((gemm_kernel<T, true, false>), grid, block, 0, s, A, B, C, g.M, g.N, g.K, g.Lseq);
-  else if (g.c_cm)
-    hipLaunchKernelGGL((gemm_kernel<T, false, true>), grid, block, 0, s, A, B, C, g.M, g.N, g.K, g.Lseq);
-  else
-    hipLaunchKernelGGL((gemm_kernel<T, false, false>), grid, block, 0, s, A, B, C, g.M, g.N, g.K, g.Lseq);
+#define GEMM_LAUNCH(acm, ccm, scv) \
+  hipLaunchKernelGGL((gemm_kernel<T, acm, ccm, scv>), grid, block, 0, s, A, B, C, g.M, g.N, g.K, g.Lseq, g.short_w)
+  if (sc) {
+    if (!g.c_cm || g.a_cm) return hipErrorInvalidValue;
+    GEMM_LAUNCH(false, true, true);
+  } else if (g.a_cm && g.c_cm) {
+    GEMM_LAUNCH(true, true, false);
+  } else if (g.a_cm) {
+    GEMM_LAUNCH(true, false, false);
+  } else if (g.c_cm) {
+    GEMM_LAUNCH(false, true, false);
+  } else {
+    GEMM_LAUNCH(false, false, false);
+  }
+#undef GEMM_LAUNCH
   return hipGetLastError();
 }
 

@@ -10,12 +10,15 @@ namespace hy {
 // C = A * B with A [M][K], B given transposed as Bt [N][K], fp32 accumulation.
 // A_CM: A is channel-major [Bsz][K][Lseq] (element (m, k) at ((m / Lseq) K + k) Lseq + m % Lseq).
 // C_CM: C is written channel-major [Bsz][N][Lseq].
+// short_w (optional, with C_CM): [N][3] causal short-convolution taps applied
+// along the sequence in the epilogue.
 struct GemmArgs {
   const void* A;
   const void* Bt;
   void* C;
   int M, N, K, Lseq;
   bool a_cm, c_cm;
+  const float* short_w;
 };
 hipError_t gemm(const GemmArgs& g, bool bf16, hipStream_t s);
 // dst [cols][rows] = transpose of src [rows][cols] (storage type of the dtype)
@@ -33,8 +36,7 @@ hipError_t twiddles(float2* tw, int n, int count, hipStream_t s);
 
 // ------------------------------------------------------ LDS regime conv
 struct LdsConvArgs {
-  const void* p;          // [B][(NO+1)D][L]
-  const float* short_w;
+  const void* s;          // short-convolved projections [B][(NO+1)D][L]
   const float* dskip;
   const float4* pq;       // [NO][D/2][L+1]
   const float2* tw;       // [2L]
@@ -46,6 +48,9 @@ hipError_t lds_spec(const float* h, const float2* tw, float4* pq, int L, int D, 
 size_t lds_conv_smem(int L);
 
 // --------------------------------------------------------- four-step
+// Column DFT length of the four-step decomposition 2L = N1 x N2.
+inline int fourstep_n1(int L) { return L <= 65536 ? 64 : 256; }
+
 struct FourStepTables {
   const float2* w256;    // [256]
   const float2* tw_lo;   // [1 << lo_bits]
@@ -54,15 +59,15 @@ struct FourStepTables {
   int lo_bits;
 };
 struct FourStepConvArgs {
-  const void* p;
-  const float* short_w;
+  const void* s;         // short-convolved projections [B][(NO+1)D][L]
   const float* dskip;
-  const float4* pq;      // [NO][D/2][129][N2]
+  const float4* pq;      // [NO][D/2][N1/2 + 1][N2]
   void* z[2];            // ping-pong z^{n+1} buffers [B][D][L]
   void* zfinal;          // z^{NO+1} [B][D][L]
-  float2* Y;             // intermediate [group_pairs][256][N2]
+  void* Y;               // intermediate [group_pairs][N1][N2]
   int B, L, D, NO;
   int group_pairs;       // channel pairs per group (0: all)
+  bool y_bf16;           // bf16 workloads: keep the intermediate as bf16 pairs
 };
 hipError_t fourstep_conv(const FourStepTables& tb, const FourStepConvArgs& c, bool bf16, hipStream_t s);
 hipError_t fourstep_spec(const FourStepTables& tb, const float* h, float2* Y, float4* pq, int L, int D, int NO,
