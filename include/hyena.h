@@ -145,7 +145,7 @@ typedef struct {
   size_t cache_bytes;
 } hyena_nd_layer;
 
-/* Supported: X, Y, Z powers of two in [4, 64]; C a multiple of 64 in [64, 4096];
+/* Supported: X, Y, Z powers of two in [4, 64] with Y = Z; C a multiple of 64 in [64, 4096];
  * 1 <= N <= 4; B >= 1. The size queries return 0 for unsupported shapes. */
 size_t hyena_nd_cache_bytes(int X, int Y, int Z, int C, int N);
 size_t hyena_nd_filter_workspace_bytes(int X, int Y, int Z, int C, int N);

@@ -73,4 +73,30 @@ hipError_t fourstep_conv(const FourStepTables& tb, const FourStepConvArgs& c, bo
 hipError_t fourstep_spec(const FourStepTables& tb, const float* h, float2* Y, float4* pq, int L, int D, int NO,
                          hipStream_t s);
 
+// --------------------------------------------------------------- 3D path
+struct NdFilterArgs {
+  int X, Y, Z, C, N, W;
+  const float *w1, *b1, *w2, *b2, *w3, *b3, *decay;
+  float* k;  // kernel on the offset grid [N][C][2X][2Y][2Z]
+};
+struct NdConvArgs {
+  int X, Y, Z, C, NO, B, n, npairs;
+  const float* p;        // projections [B][(NO+1)C][X*Y*Z] (channel-major)
+  const float* dskip;    // [NO][C]
+  const float* gate;     // [B][NO][C]
+  const float* zin;
+  float* zout;
+  float* zbuf[2];        // z^{n+1} ping-pong [B][C][V]
+  float* zfinal;         // z^{NO+1} [B][C][V]
+  float2* Yint;          // [ceil(B/2)][C][X][2Y][2Z]
+  float2* F;             // filter pairs [N*C/2][2X][2Y][2Z]
+  const float2* kh;      // half spectra [N*C][2X][2Y][Z+1]
+  const float2* tw128;   // W_128^m
+};
+hipError_t nd_filter(const NdFilterArgs& f, float2* F, float2* kh, const float2* tw128, hipStream_t s);
+hipError_t nd_gate(const float* u, float* part, const float* ga, const float* gb, float* gate, int B, int NO, int C,
+                   int V, hipStream_t s);
+size_t nd_gate_partial_floats(int B, int C, int V);
+hipError_t nd_conv(const NdConvArgs& a, hipStream_t s);
+
 }  // namespace hy

@@ -1,0 +1,503 @@
+// 3D (HyenaND) path on gfx950: coordinate-MLP kernel, channel-mean gate and the
+// zero-padded 3D FFT convolution with gating (HyenaND explainer, gist.science,
+// "Methodology: HyenaND": Native ND Convolution, Input-Dependent Kernels,
+// Kernel Synthesis, Handling Boundaries).
+//
+// Layouts: activations channel-major [B][C][X][Y][Z] (z contiguous); padded
+// transform size (MX, MY, MZ) = (2X, 2Y, 2Z), square planes (Y = Z).
+//
+// The gate g_{b,c} is one scalar per sample and channel, so it commutes with
+// the convolution and is applied to the convolution output in the spatial
+// domain. The same channel of two samples then travels as one complex field
+// z_{b0,c} + i z_{b1,c}: both halves are filtered by the same real kernel K_c,
+// so the spectrum product is a plain pointwise multiply by K^_c and the inverse
+// transform returns (K_c * z_{b0,c}) + i (K_c * z_{b1,c}). Each channel's
+// spectrum is read once for both samples.
+//
+// Per order: a plane pass (2D DFT over (y, z) of the X non-zero x-planes, with
+// the Y x Z non-zero block zero padded), a pencil pass (DFT over x, X non-zero
+// inputs, times K^_c, inverse DFT over x keeping x < X) and the inverse plane
+// pass (inverse 2D DFT, crop to Y x Z, gate, skip), which also starts the next
+// order's forward plane DFT from the same LDS plane.
+#include "common.h"
+#include "kernels.h"
+
+namespace hy {
+
+// ======================================================= coordinate MLP
+constexpr int kNP = 64;       // offset points per workgroup
+constexpr int kNdMaxW = 128;
+
+__global__ __launch_bounds__(256) void nd_mlp_kernel(NdFilterArgs a) {
+  __shared__ float cs[kNP][3];
+  __shared__ float rad[kNP];
+  __shared__ float h1[kNP][kNdMaxW + 1];
+  __shared__ float h2[kNP][kNdMaxW + 1];
+  const int MX = 2 * a.X, MY = 2 * a.Y, MZ = 2 * a.Z;
+  const int P = MX * MY * MZ;
+  const int p0 = blockIdx.x * kNP;
+  const int W = a.W, tid = threadIdx.x;
+  for (int t = tid; t < kNP; t += 256) {
+    const int pt = p0 + t;
+    const int k = pt % MZ, j = (pt / MZ) % MY, i = pt / (MZ * MY);
+    const float cx = (float)(i - a.X) / (float)a.X;
+    const float cy = (float)(j - a.Y) / (float)a.Y;
+    const float cz = (float)(k - a.Z) / (float)a.Z;
+    cs[t][0] = cx;
+    cs[t][1] = cy;
+    cs[t][2] = cz;
+    rad[t] = sqrtf(cx * cx + cy * cy + cz * cz);
+  }
+  __syncthreads();
+  for (int idx = tid; idx < kNP * W; idx += 256) {
+    const int t = idx / W, j = idx % W;
+    const float s = a.b1[j] + cs[t][0] * a.w1[j] + cs[t][1] * a.w1[W + j] + cs[t][2] * a.w1[2 * W + j];
+    h1[t][j] = sinf(s);
+  }
+  __syncthreads();
+  for (int idx = tid; idx < kNP * W; idx += 256) {
+    const int t = idx / W, j = idx % W;
+    float s = a.b2[j];
+    for (int f = 0; f < W; ++f) s += h1[t][f] * a.w2[f * W + j];
+    h2[t][j] = sinf(s);
+  }
+  __syncthreads();
+  const int NC = a.N * a.C;
+  for (int col = tid; col < NC; col += 256) {
+    float acc[kNP];
+    const float bias = a.b3[col];
+#pragma unroll
+    for (int t = 0; t < kNP; ++t) acc[t] = bias;
+    for (int j = 0; j < W; ++j) {
+      const float wv = a.w3[(size_t)j * NC + col];
+#pragma unroll
+      for (int t = 0; t < kNP; ++t) acc[t] += h2[t][j] * wv;
+    }
+    const float dc = a.decay[col % a.C];
+    float* dst = a.k + (size_t)col * P + p0;  // K[n][c][i][j][k], col = n C + c
+#pragma unroll
+    for (int t = 0; t < kNP; ++t) dst[t] = acc[t] * expf(-dc * rad[t]);
+  }
+}
+
+// Two channels of the offset-indexed kernel, wrapped (offset d stored at d mod 2G),
+// as one complex field per channel pair: F = K_{2cp} + i K_{2cp+1}.
+__global__ void nd_pack_kernel(const float* __restrict__ k, float2* __restrict__ F, int X, int Y, int Z,
+                               int npairs) {
+  const int MX = 2 * X, MY = 2 * Y, MZ = 2 * Z;
+  const size_t P = (size_t)MX * MY * MZ;
+  const size_t idx = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (idx >= P * npairs) return;
+  const size_t pr = idx / P, w = idx % P;
+  const int wz = (int)(w % MZ), wy = (int)((w / MZ) % MY), wx = (int)(w / ((size_t)MZ * MY));
+  const size_t o = ((size_t)((wx + X) % MX) * MY + (wy + Y) % MY) * MZ + (wz + Z) % MZ;
+  F[idx] = make_float2(k[(2 * pr) * P + o], k[(2 * pr + 1) * P + o]);
+}
+
+// Per-channel half spectra (kz in [0, Z]) from the spectra of the packed pairs:
+// Ha(k) = (F(k) + conj F(-k)) / 2, Hb(k) = (F(k) - conj F(-k)) / 2i, scaled by
+// 1 / (MX MY MZ) (the inverse transforms are unnormalised).
+__global__ void nd_split_kernel(const float2* __restrict__ F, float2* __restrict__ Kh, int X, int Y, int Z,
+                                int npairs) {
+  const int MX = 2 * X, MY = 2 * Y, MZ = 2 * Z, ZH = Z + 1;
+  const size_t PH = (size_t)MX * MY * ZH, P = (size_t)MX * MY * MZ;
+  const size_t idx = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (idx >= PH * npairs) return;
+  const size_t pr = idx / PH, w = idx % PH;
+  const int kz = (int)(w % ZH), ky = (int)((w / ZH) % MY), kx = (int)(w / ((size_t)ZH * MY));
+  const float2* Fp = F + pr * P;
+  const float2 fk = Fp[((size_t)kx * MY + ky) * MZ + kz];
+  const float2 fm = conjf2(Fp[((size_t)((MX - kx) % MX) * MY + (MY - ky) % MY) * MZ + (MZ - kz) % MZ]);
+  const float s = 0.5f / (float)P;
+  const float2 ha = cadd(fk, fm), d = csub(fk, fm);
+  Kh[(2 * pr) * PH + w] = make_float2(s * ha.x, s * ha.y);
+  Kh[(2 * pr + 1) * PH + w] = make_float2(s * d.y, -s * d.x);
+}
+
+// ================================================ FFT along LDS lines
+// M-point Stockham FFT of the line buf[base + i*stride], i in [0, M), by M/E
+// threads (lt); every thread of the workgroup calls it (barriers), `active`
+// selects the ones that own a line. tw128[m] = W_128^m.
+template <int M, int E, int Ns, bool INV>
+__device__ __forceinline__ void line_stage(float2* buf, int base, int stride, int lt, bool active,
+                                           const float2* __restrict__ tw128) {
+  constexpr int R = (E < M / Ns) ? E : M / Ns;
+  constexpr int NB = E / R;
+  constexpr int T = M / E;
+  float2 v[NB][R];
+  if (active) {
+#pragma unroll
+    for (int b = 0; b < NB; ++b) {
+      const int j = lt + b * T;
+#pragma unroll
+      for (int r = 0; r < R; ++r) v[b][r] = buf[base + (j + r * (M / R)) * stride];
+      if (Ns > 1) {
+        const int k = j % Ns;
+#pragma unroll
+        for (int r = 1; r < R; ++r) v[b][r] = twmul<INV>(v[b][r], tw128[r * k * (128 / (Ns * R))]);
+      }
+      Dft<R, INV>::run(v[b]);
+    }
+  }
+  __syncthreads();
+  if (active) {
+#pragma unroll
+    for (int b = 0; b < NB; ++b) {
+      const int j = lt + b * T;
+      const int base_o = (j / Ns) * Ns * R + j % Ns;
+#pragma unroll
+      for (int r = 0; r < R; ++r) buf[base + (base_o + r * Ns) * stride] = v[b][r];
+    }
+  }
+  __syncthreads();
+}
+
+template <int M, int E, int Ns, bool INV> struct LineFrom {
+  static __device__ __forceinline__ void run(float2* buf, int base, int stride, int lt, bool active,
+                                             const float2* tw) {
+    constexpr int R = (E < M / Ns) ? E : M / Ns;
+    line_stage<M, E, Ns, INV>(buf, base, stride, lt, active, tw);
+    LineFrom<M, E, Ns * R, INV>::run(buf, base, stride, lt, active, tw);
+  }
+};
+template <int M, int E, bool INV> struct LineFrom<M, E, M, INV> {
+  static __device__ __forceinline__ void run(float2*, int, int, int, bool, const float2*) {}
+};
+
+// ======================================================== plane pass
+// One workgroup per (sample pair or filter pair, channel, x-plane). The plane
+// (M x M complex, M = 2Y = 2Z) lives in LDS at [y][z] with row stride M + 1.
+// Thread t works on line t % nlines (one of the lines of a direction) as its
+// (t / nlines)-th FFT thread, so the 64 lanes of a wave sit on 64 lines.
+enum { PL_FWD_V = 0, PL_FWD_FULL = 1, PL_INV = 2, PL_INV_FWD = 3 };
+
+template <int M> struct PlaneCfg {
+  static constexpr int E = M >= 16 ? 16 : M;
+  static constexpr int T = M / E;       // threads per line
+  static constexpr int RS = M + 1;      // LDS row stride
+  static constexpr int THREADS = 1024;
+  static constexpr size_t LDS = (size_t)M * RS * 8;
+};
+
+template <int M, bool INV>
+__device__ __forceinline__ void plane_rows(float2* P, int nrows, const float2* tw) {
+  using C = PlaneCfg<M>;
+  const int line = threadIdx.x % M, lt = threadIdx.x / M;
+  // rows are lines of length M along z; nrows of them
+  const bool active = line < nrows && lt < C::T;
+  LineFrom<M, C::E, 1, INV>::run(P, line * C::RS, 1, lt, active, tw);
+}
+
+template <int M, bool INV>
+__device__ __forceinline__ void plane_cols(float2* P, const float2* tw) {
+  using C = PlaneCfg<M>;
+  const int line = threadIdx.x % M, lt = threadIdx.x / M;
+  const bool active = lt < C::T;
+  LineFrom<M, C::E, 1, INV>::run(P, line, C::RS, lt, active, tw);
+}
+
+template <int M, int MODE>
+__global__ __launch_bounds__(1024) void nd_plane_kernel(NdConvArgs a) {
+  using C = PlaneCfg<M>;
+  extern __shared__ float4 smem4[];
+  float2* P = reinterpret_cast<float2*>(smem4);
+  const int X = a.X, Y = a.Y, Z = a.Z;
+  const size_t V = (size_t)X * Y * Z;
+  const size_t plane = (size_t)M * M;
+  const int x = blockIdx.x;          // plane index
+  const int c = blockIdx.y;          // channel (or filter pair)
+  const int bp = blockIdx.z;         // sample pair (or order of the filter)
+  const int tid = threadIdx.x;
+
+  if constexpr (MODE == PL_FWD_FULL) {
+    // filter: full M x M complex plane, all 2X planes
+    float2* Fp = a.F + (((size_t)bp * a.npairs + c) * (2 * X) + x) * plane;
+    for (int i = tid; i < M * M; i += C::THREADS) P[(i / M) * C::RS + i % M] = Fp[i];
+    __syncthreads();
+    plane_rows<M, false>(P, M, a.tw128);
+    plane_cols<M, false>(P, a.tw128);
+    for (int i = tid; i < M * M; i += C::THREADS) Fp[i] = P[(i / M) * C::RS + i % M];
+    return;
+  }
+
+  const int b0 = 2 * bp, b1 = b0 + 1;
+  const bool has_b1 = b1 < a.B;
+  const int CC = a.C;
+  float2* Yp = a.Yint + (((size_t)bp * CC + c) * X + x) * plane;
+  const size_t J = (size_t)(a.NO + 1) * CC;
+  const float* s0 = a.p + (size_t)b0 * J * V;
+  const float* s1 = a.p + (size_t)(has_b1 ? b1 : b0) * J * V;
+  const size_t xoff = (size_t)x * Y * Z;
+
+  if constexpr (MODE == PL_FWD_V) {
+    const float* v0 = s0 + (size_t)c * V + xoff;
+    const float* v1 = s1 + (size_t)c * V + xoff;
+    for (int i = tid; i < M * M; i += C::THREADS) {
+      const int y = i / M, z = i % M;
+      float2 val = make_float2(0.f, 0.f);
+      if (y < Y && z < Z) val = make_float2(v0[y * Z + z], has_b1 ? v1[y * Z + z] : 0.f);
+      P[y * C::RS + z] = val;
+    }
+    __syncthreads();
+  } else {
+    for (int i = tid; i < M * M; i += C::THREADS) P[(i / M) * C::RS + i % M] = Yp[i];
+    __syncthreads();
+    plane_cols<M, true>(P, a.tw128);
+    plane_rows<M, true>(P, Y, a.tw128);
+    // gate and skip on the kept Y x Z block
+    const int n = a.n;
+    const float* x0 = s0 + (size_t)((n + 1) * CC + c) * V + xoff;
+    const float* x1 = s1 + (size_t)((n + 1) * CC + c) * V + xoff;
+    const float* z0 = (n == 0) ? s0 + (size_t)c * V + xoff : a.zin + ((size_t)b0 * CC + c) * V + xoff;
+    const float* z1 = (n == 0) ? s1 + (size_t)c * V + xoff
+                               : a.zin + ((size_t)(has_b1 ? b1 : b0) * CC + c) * V + xoff;
+    float* o0 = a.zout + ((size_t)b0 * CC + c) * V + xoff;
+    float* o1 = a.zout + ((size_t)(has_b1 ? b1 : b0) * CC + c) * V + xoff;
+    const float g0 = a.gate[((size_t)b0 * a.NO + n) * CC + c];
+    const float g1 = has_b1 ? a.gate[((size_t)b1 * a.NO + n) * CC + c] : 0.f;
+    const float dk = a.dskip[n * CC + c];
+    for (int i = tid; i < M * M; i += C::THREADS) {
+      const int y = i / M, z = i % M;
+      float2 nv = make_float2(0.f, 0.f);
+      if (y < Y && z < Z) {
+        const int q = y * Z + z;
+        const float2 cv = P[y * C::RS + z];
+        const float a0 = x0[q] * g0 * cv.x + dk * z0[q];
+        o0[q] = a0;
+        float a1 = 0.f;
+        if (has_b1) {
+          a1 = x1[q] * g1 * cv.y + dk * z1[q];
+          o1[q] = a1;
+        }
+        nv = make_float2(a0, a1);
+      }
+      if (MODE == PL_INV_FWD) P[y * C::RS + z] = nv;
+    }
+    if (MODE == PL_INV) return;
+    __syncthreads();
+  }
+  // forward plane DFT of the (zero padded) Y x Z block
+  plane_rows<M, false>(P, Y, a.tw128);
+  plane_cols<M, false>(P, a.tw128);
+  for (int i = tid; i < M * M; i += C::THREADS) Yp[i] = P[(i / M) * C::RS + i % M];
+}
+
+// ======================================================= pencil pass
+// DFT over x of 64 consecutive (ky, kz) pencils; N1 = 2X = RA * RB points,
+// n1 = j + RA r, k1 = ka + RB kb. Forward: threads (lane, j < RA) hold
+// x[j + RA r]; stage 2 threads (lane, ka < RB) end with X[ka + RB kb].
+enum { PN_CONV = 0, PN_FWD_FULL = 1 };
+
+template <int RA, int RB, int MODE>
+__global__ __launch_bounds__(64 * RA) void nd_pencil_kernel(NdConvArgs a) {
+  constexpr int N1 = RA * RB;
+  extern __shared__ float4 smem4[];
+  float2* S = reinterpret_cast<float2*>(smem4);  // [RA][RB][64] / [RB][RA][64]
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const int X = a.X, Y = a.Y, Z = a.Z;
+  const int MY = 2 * Y, MZ = 2 * Z, ZH = Z + 1;
+  const size_t plane = (size_t)MY * MZ;
+  const int f = blockIdx.x * 64 + lane;  // flattened (ky, kz)
+  const int c = blockIdx.y, bp = blockIdx.z;
+  const int nin = (MODE == PN_FWD_FULL) ? RB : RB / 2;  // non-zero r per thread
+  float2* base = (MODE == PN_FWD_FULL) ? a.F + (((size_t)bp * a.npairs + c) * N1) * plane
+                                       : a.Yint + (((size_t)bp * a.C + c) * X) * plane;
+  // forward stage 1: threads (lane, j)
+  float2 v[RB];
+#pragma unroll
+  for (int r = 0; r < RB; ++r) v[r] = (r < nin) ? base[(size_t)(w + RA * r) * plane + f] : make_float2(0.f, 0.f);
+  Dft<RB, false>::run(v);
+#pragma unroll
+  for (int ka = 0; ka < RB; ++ka) {
+    if (ka) v[ka] = cmul(v[ka], a.tw128[(w * ka * (128 / N1)) & 127]);
+    S[(w * RB + ka) * 64 + lane] = v[ka];
+  }
+  __syncthreads();
+  float2 u[RA];
+  const bool act2 = w < RB;  // stage-2 threads (lane, ka = w)
+  if (act2) {
+#pragma unroll
+    for (int j = 0; j < RA; ++j) u[j] = S[(j * RB + w) * 64 + lane];
+    Dft<RA, false>::run(u);
+  }
+  if constexpr (MODE == PN_FWD_FULL) {
+    if (act2) {
+#pragma unroll
+      for (int kb = 0; kb < RA; ++kb) base[(size_t)(w + RB * kb) * plane + f] = u[kb];
+    }
+    return;
+  }
+  if (act2) {
+    // times K^_c(kx, ky, kz); kz > Z from the conjugate symmetric half spectrum
+    const int ky = f / MZ, kz = f % MZ;
+    const float2* Kc = a.kh + (size_t)(a.n * a.C + c) * N1 * MY * ZH;
+    const bool lower = kz <= Z;
+    const int ky2 = lower ? ky : (MY - ky) % MY;
+    const int kz2 = lower ? kz : MZ - kz;
+#pragma unroll
+    for (int kb = 0; kb < RA; ++kb) {
+      const int kx = w + RB * kb;
+      const int kx2 = lower ? kx : (N1 - kx) % N1;
+      float2 kv = Kc[((size_t)kx2 * MY + ky2) * ZH + kz2];
+      if (!lower) kv = conjf2(kv);
+      u[kb] = cmul(u[kb], kv);
+    }
+    // inverse stage 1 on the same threads: IDFT over kb -> B[na]
+    Dft<RA, true>::run(u);
+#pragma unroll
+    for (int na = 0; na < RA; ++na) {
+      if (na) u[na] = cmulc(u[na], a.tw128[(w * na * (128 / N1)) & 127]);
+    }
+  }
+  __syncthreads();  // everyone finished reading S
+  if (act2) {
+#pragma unroll
+    for (int na = 0; na < RA; ++na) S[(w * RA + na) * 64 + lane] = u[na];
+  }
+  __syncthreads();
+  // inverse stage 2: threads (lane, na = w < RA), IDFT over ka -> x = na + RA nb
+  float2 q[RB];
+#pragma unroll
+  for (int ka = 0; ka < RB; ++ka) q[ka] = S[(ka * RA + w) * 64 + lane];
+  Dft<RB, true>::run(q);
+#pragma unroll
+  for (int nb = 0; nb < RB / 2; ++nb) base[(size_t)(w + RA * nb) * plane + f] = q[nb];
+}
+
+// ========================================================= channel mean
+__global__ __launch_bounds__(256) void nd_mean_partial_kernel(const float* __restrict__ u, float* __restrict__ part,
+                                                              int C, int V, int chunk) {
+  const int ch = blockIdx.x, b = blockIdx.y;
+  const float* ub = u + ((size_t)b * V + (size_t)ch * chunk) * C;
+  for (int c = threadIdx.x; c < C; c += 256) {
+    float s = 0.f;
+    for (int v = 0; v < chunk; ++v) s += ub[(size_t)v * C + c];
+    part[((size_t)b * gridDim.x + ch) * C + c] = s;
+  }
+}
+
+__global__ void nd_gate_kernel(const float* __restrict__ part, const float* __restrict__ ga,
+                               const float* __restrict__ gb, float* __restrict__ gate, int B, int NO, int C,
+                               int nch, int V) {
+  const int idx = blockIdx.x * blockDim.x + threadIdx.x;
+  if (idx >= B * NO * C) return;
+  const int c = idx % C, n = (idx / C) % NO, b = idx / (C * NO);
+  float s = 0.f;
+  for (int k = 0; k < nch; ++k) s += part[((size_t)b * nch + k) * C + c];
+  const float m = s / (float)V;
+  const float arg = ga[n * C + c] * m + gb[n * C + c];
+  gate[idx] = 1.f / (1.f + expf(-arg));
+}
+
+// ============================================================ launchers
+
+static hipError_t nd_allow_lds(const void* fn, size_t bytes) {
+  if (bytes <= 65536) return hipSuccess;
+  return hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)bytes);
+}
+
+template <int M, int MODE>
+static hipError_t launch_plane_t(const NdConvArgs& a, dim3 grid, hipStream_t s) {
+  using C = PlaneCfg<M>;
+  auto fn = nd_plane_kernel<M, MODE>;
+  hipError_t e = nd_allow_lds((const void*)fn, C::LDS);
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(fn, grid, dim3(C::THREADS), C::LDS, s, a);
+  return hipGetLastError();
+}
+
+template <int MODE>
+static hipError_t launch_plane(const NdConvArgs& a, dim3 grid, hipStream_t s) {
+  switch (2 * a.Y) {
+    case 8: return launch_plane_t<8, MODE>(a, grid, s);
+    case 16: return launch_plane_t<16, MODE>(a, grid, s);
+    case 32: return launch_plane_t<32, MODE>(a, grid, s);
+    case 64: return launch_plane_t<64, MODE>(a, grid, s);
+    case 128: return launch_plane_t<128, MODE>(a, grid, s);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+template <int RA, int RB, int MODE>
+static hipError_t launch_pencil_t(const NdConvArgs& a, dim3 grid, hipStream_t s) {
+  const size_t lds = (size_t)RA * RB * 64 * 8;
+  auto fn = nd_pencil_kernel<RA, RB, MODE>;
+  hipError_t e = nd_allow_lds((const void*)fn, lds);
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(fn, grid, dim3(64 * RA), lds, s, a);
+  return hipGetLastError();
+}
+
+template <int MODE>
+static hipError_t launch_pencil(const NdConvArgs& a, dim3 grid, hipStream_t s) {
+  switch (2 * a.X) {
+    case 8: return launch_pencil_t<4, 2, MODE>(a, grid, s);
+    case 16: return launch_pencil_t<4, 4, MODE>(a, grid, s);
+    case 32: return launch_pencil_t<8, 4, MODE>(a, grid, s);
+    case 64: return launch_pencil_t<8, 8, MODE>(a, grid, s);
+    case 128: return launch_pencil_t<16, 8, MODE>(a, grid, s);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+hipError_t nd_filter(const NdFilterArgs& f, float2* F, float2* kh, const float2* tw128, hipStream_t s) {
+  const int MX = 2 * f.X, MY = 2 * f.Y, MZ = 2 * f.Z;
+  const size_t P = (size_t)MX * MY * MZ;
+  hipLaunchKernelGGL(nd_mlp_kernel, dim3((unsigned)(P / kNP)), dim3(256), 0, s, f);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  const int npairs = f.N * f.C / 2;
+  const size_t tot = P * npairs;
+  hipLaunchKernelGGL(nd_pack_kernel, dim3((unsigned)((tot + 255) / 256)), dim3(256), 0, s, (const float*)f.k, F,
+                     f.X, f.Y, f.Z, npairs);
+  if ((e = hipGetLastError()) != hipSuccess) return e;
+  NdConvArgs a{};
+  a.X = f.X;
+  a.Y = f.Y;
+  a.Z = f.Z;
+  a.F = F;
+  a.npairs = npairs;
+  a.tw128 = tw128;
+  if ((e = launch_plane<PL_FWD_FULL>(a, dim3(MX, npairs, 1), s)) != hipSuccess) return e;
+  if ((e = launch_pencil<PN_FWD_FULL>(a, dim3((unsigned)(MY * MZ / 64), npairs, 1), s)) != hipSuccess) return e;
+  const size_t th = (size_t)MX * MY * (f.Z + 1) * npairs;
+  hipLaunchKernelGGL(nd_split_kernel, dim3((unsigned)((th + 255) / 256)), dim3(256), 0, s, (const float2*)F, kh,
+                     f.X, f.Y, f.Z, npairs);
+  return hipGetLastError();
+}
+
+hipError_t nd_gate(const float* u, float* part, const float* ga, const float* gb, float* gate, int B, int NO, int C,
+                   int V, hipStream_t s) {
+  const int nch = V < 512 ? V : 512;
+  hipLaunchKernelGGL(nd_mean_partial_kernel, dim3(nch, B), dim3(256), 0, s, u, part, C, V, V / nch);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  const int tot = B * NO * C;
+  hipLaunchKernelGGL(nd_gate_kernel, dim3((tot + 255) / 256), dim3(256), 0, s, (const float*)part, ga, gb, gate, B,
+                     NO, C, nch, V);
+  return hipGetLastError();
+}
+
+size_t nd_gate_partial_floats(int B, int C, int V) { return (size_t)B * (V < 512 ? V : 512) * C; }
+
+hipError_t nd_conv(const NdConvArgs& in, hipStream_t s) {
+  NdConvArgs a = in;
+  const int BP = (a.B + 1) / 2;
+  const unsigned nf = (unsigned)(4 * a.Y * a.Z / 64);
+  hipError_t e = launch_plane<PL_FWD_V>(a, dim3(a.X, a.C, BP), s);
+  if (e != hipSuccess) return e;
+  for (int n = 0; n < a.NO; ++n) {
+    a.n = n;
+    if ((e = launch_pencil<PN_CONV>(a, dim3(nf, a.C, BP), s)) != hipSuccess) return e;
+    a.zin = (n == 0) ? nullptr : in.zbuf[(n - 1) & 1];
+    a.zout = (n == a.NO - 1) ? in.zfinal : in.zbuf[n & 1];
+    if (n == a.NO - 1)
+      e = launch_plane<PL_INV>(a, dim3(a.X, a.C, BP), s);
+    else
+      e = launch_plane<PL_INV_FWD>(a, dim3(a.X, a.C, BP), s);
+    if (e != hipSuccess) return e;
+  }
+  return hipSuccess;
+}
+
+}  // namespace hy

@@ -1,18 +1,210 @@
-// C ABI of the 3D (HyenaND) path.
+// C ABI of the 3D (HyenaND) path: validation, memory layouts and the launch
+// sequence. Every check runs on the host before the first HIP call.
 #include "../../include/hyena.h"
+
+#include <stdint.h>
+
+#include "common.h"
+#include "kernels.h"
+
+using hy::align_up;
+
+namespace {
+
+constexpr size_t kAlign = 256;
+
+bool pow2_in(int v, int lo, int hi) { return v >= lo && v <= hi && (v & (v - 1)) == 0; }
+bool aligned16(const void* p) { return p != nullptr && ((uintptr_t)p & 15u) == 0; }
+
+bool nd_shape_ok(int X, int Y, int Z, int C, int N) {
+  return pow2_in(X, 4, 64) && pow2_in(Y, 4, 64) && Z == Y && C >= 64 && C <= 4096 && C % 64 == 0 && N >= 1 &&
+         N <= 4;
+}
+
+size_t pts(int X, int Y, int Z) { return (size_t)8 * X * Y * Z; }  // (2X)(2Y)(2Z)
+
+struct NdCache {
+  size_t tw, kh, total;
+};
+NdCache nd_cache(int X, int Y, int Z, int C, int N) {
+  NdCache c{};
+  size_t off = 0;
+  c.tw = off;
+  off = align_up(off + 128 * 8, kAlign);
+  c.kh = off;
+  off = align_up(off + (size_t)N * C * (2 * X) * (2 * Y) * (Z + 1) * 8, kAlign);
+  c.total = off;
+  return c;
+}
+
+struct NdFws {
+  size_t k, F, total;
+};
+NdFws nd_fws(int X, int Y, int Z, int C, int N) {
+  NdFws w{};
+  size_t off = 0;
+  w.k = off;
+  off = align_up(off + (size_t)N * C * pts(X, Y, Z) * 4, kAlign);
+  w.F = off;
+  off = align_up(off + (size_t)N * (C / 2) * pts(X, Y, Z) * 8, kAlign);
+  w.total = off;
+  return w;
+}
+
+struct NdWs {
+  size_t wt_in, wt_out, p, zfinal, z0, z1, Y, part, gate, total;
+};
+NdWs nd_ws(int B, int X, int Y, int Z, int C, int N) {
+  NdWs w{};
+  const size_t V = (size_t)X * Y * Z;
+  const size_t J = (size_t)(N + 1) * C;
+  size_t off = 0;
+  w.wt_in = off;
+  off = align_up(off + J * C * 4, kAlign);
+  w.wt_out = off;
+  off = align_up(off + (size_t)C * C * 4, kAlign);
+  w.p = off;
+  off = align_up(off + (size_t)B * J * V * 4, kAlign);
+  w.zfinal = off;
+  off = align_up(off + (size_t)B * C * V * 4, kAlign);
+  w.z0 = off;
+  off = align_up(off + (size_t)B * C * V * 4, kAlign);
+  w.z1 = off;
+  off = align_up(off + (size_t)B * C * V * 4, kAlign);
+  w.Y = off;
+  off = align_up(off + (size_t)((B + 1) / 2) * C * X * (4 * (size_t)Y * Z) * 8, kAlign);
+  w.part = off;
+  off = align_up(off + hy::nd_gate_partial_floats(B, C, (int)V) * 4, kAlign);
+  w.gate = off;
+  off = align_up(off + (size_t)B * N * C * 4, kAlign);
+  w.total = off;
+  return w;
+}
+
+int device_ok() {
+  int n = 0;
+  if (hipGetDeviceCount(&n) != hipSuccess || n <= 0) return HYENA_ERR_HIP;
+  return HYENA_OK;
+}
+
+}  // namespace
 
 extern "C" {
 
-size_t hyena_nd_cache_bytes(int, int, int, int, int) { return 0; }
-size_t hyena_nd_filter_workspace_bytes(int, int, int, int, int) { return 0; }
-size_t hyena_nd_workspace_bytes(int, int, int, int, int, int) { return 0; }
-int hyena_nd_layer_init(hyena_nd_layer*, int, int, int, int, int, void*, size_t) { return HYENA_ERR_UNSUPPORTED; }
-int hyena_nd_filter_gen(hyena_nd_layer*, const hyena_nd_filter_params*, float*, void*, size_t, hipStream_t) {
-  return HYENA_ERR_UNSUPPORTED;
+size_t hyena_nd_cache_bytes(int X, int Y, int Z, int C, int N) {
+  if (!nd_shape_ok(X, Y, Z, C, N)) return 0;
+  return nd_cache(X, Y, Z, C, N).total;
 }
-int hyena_nd_fwd(const hyena_nd_layer*, const float*, const float*, const float*, const float*, const float*,
-                 const float*, int, float*, void*, size_t, hipStream_t) {
-  return HYENA_ERR_UNSUPPORTED;
+
+size_t hyena_nd_filter_workspace_bytes(int X, int Y, int Z, int C, int N) {
+  if (!nd_shape_ok(X, Y, Z, C, N)) return 0;
+  return nd_fws(X, Y, Z, C, N).total;
+}
+
+size_t hyena_nd_workspace_bytes(int B, int X, int Y, int Z, int C, int N) {
+  if (!nd_shape_ok(X, Y, Z, C, N) || B < 1) return 0;
+  if ((long long)B * X * Y * Z * (N + 1) * C >= (1LL << 31)) return 0;
+  return nd_ws(B, X, Y, Z, C, N).total;
+}
+
+int hyena_nd_layer_init(hyena_nd_layer* layer, int X, int Y, int Z, int C, int N, void* cache, size_t cache_bytes) {
+  if (layer == nullptr) return HYENA_ERR_INVALID_ARG;
+  if (!nd_shape_ok(X, Y, Z, C, N)) return HYENA_ERR_UNSUPPORTED;
+  if (!aligned16(cache)) return HYENA_ERR_INVALID_ARG;
+  if (cache_bytes < nd_cache(X, Y, Z, C, N).total) return HYENA_ERR_WORKSPACE;
+  layer->X = X;
+  layer->Y = Y;
+  layer->Z = Z;
+  layer->C = C;
+  layer->N = N;
+  layer->built = 0;
+  layer->cache = cache;
+  layer->cache_bytes = cache_bytes;
+  return HYENA_OK;
+}
+
+int hyena_nd_filter_gen(hyena_nd_layer* layer, const hyena_nd_filter_params* p, float* k_out, void* ws,
+                        size_t ws_bytes, hipStream_t stream) {
+  if (layer == nullptr || p == nullptr) return HYENA_ERR_INVALID_ARG;
+  const int X = layer->X, Y = layer->Y, Z = layer->Z, C = layer->C, N = layer->N;
+  if (!nd_shape_ok(X, Y, Z, C, N)) return HYENA_ERR_UNSUPPORTED;
+  if (!aligned16(layer->cache)) return HYENA_ERR_INVALID_ARG;
+  const NdCache cl = nd_cache(X, Y, Z, C, N);
+  if (layer->cache_bytes < cl.total) return HYENA_ERR_WORKSPACE;
+  if (p->width < 1 || p->width > 128) return HYENA_ERR_UNSUPPORTED;
+  const void* ptrs[] = {p->w1, p->b1, p->w2, p->b2, p->w3, p->b3, p->decay, ws};
+  for (const void* q : ptrs)
+    if (!aligned16(q)) return HYENA_ERR_INVALID_ARG;
+  if (k_out != nullptr && !aligned16(k_out)) return HYENA_ERR_INVALID_ARG;
+  const NdFws fw = nd_fws(X, Y, Z, C, N);
+  if (ws_bytes < fw.total) return HYENA_ERR_WORKSPACE;
+  if (device_ok() != HYENA_OK) return HYENA_ERR_HIP;
+
+  char* wsb = static_cast<char*>(ws);
+  char* cb = static_cast<char*>(layer->cache);
+  layer->built = 0;
+  float2* tw = reinterpret_cast<float2*>(cb + cl.tw);
+  HY_CHECK_HIP(hy::twiddles(tw, 128, 128, stream));
+  hy::NdFilterArgs f{X, Y, Z, C, N, p->width, p->w1, p->b1, p->w2, p->b2, p->w3, p->b3, p->decay,
+                     k_out ? k_out : reinterpret_cast<float*>(wsb + fw.k)};
+  HY_CHECK_HIP(hy::nd_filter(f, reinterpret_cast<float2*>(wsb + fw.F), reinterpret_cast<float2*>(cb + cl.kh), tw,
+                             stream));
+  layer->built = 1;
+  return HYENA_OK;
+}
+
+int hyena_nd_fwd(const hyena_nd_layer* layer, const float* u, const float* w_in, const float* dskip,
+                 const float* gate_a, const float* gate_b, const float* w_out, int B, float* y, void* ws,
+                 size_t ws_bytes, hipStream_t stream) {
+  if (layer == nullptr) return HYENA_ERR_INVALID_ARG;
+  const void* ptrs[] = {u, w_in, dskip, gate_a, gate_b, w_out, y, ws};
+  for (const void* q : ptrs)
+    if (!aligned16(q)) return HYENA_ERR_INVALID_ARG;
+  if (B < 1) return HYENA_ERR_INVALID_ARG;
+  const int X = layer->X, Y = layer->Y, Z = layer->Z, C = layer->C, N = layer->N;
+  if (!nd_shape_ok(X, Y, Z, C, N)) return HYENA_ERR_UNSUPPORTED;
+  if (!layer->built || !aligned16(layer->cache)) return HYENA_ERR_LAYER_MISMATCH;
+  const NdCache cl = nd_cache(X, Y, Z, C, N);
+  if (layer->cache_bytes < cl.total) return HYENA_ERR_LAYER_MISMATCH;
+  if ((long long)B * X * Y * Z * (N + 1) * C >= (1LL << 31)) return HYENA_ERR_UNSUPPORTED;
+  const NdWs w = nd_ws(B, X, Y, Z, C, N);
+  if (ws_bytes < w.total) return HYENA_ERR_WORKSPACE;
+  if (device_ok() != HYENA_OK) return HYENA_ERR_HIP;
+
+  char* wsb = static_cast<char*>(ws);
+  char* cb = static_cast<char*>(layer->cache);
+  const int V = X * Y * Z, J = (N + 1) * C;
+  float* wt_in = reinterpret_cast<float*>(wsb + w.wt_in);
+  float* wt_out = reinterpret_cast<float*>(wsb + w.wt_out);
+  float* pbuf = reinterpret_cast<float*>(wsb + w.p);
+  float* zfin = reinterpret_cast<float*>(wsb + w.zfinal);
+  float* gate = reinterpret_cast<float*>(wsb + w.gate);
+
+  HY_CHECK_HIP(hy::nd_gate(u, reinterpret_cast<float*>(wsb + w.part), gate_a, gate_b, gate, B, N, C, V, stream));
+  HY_CHECK_HIP(hy::transpose2d(w_in, wt_in, C, J, false, stream));
+  HY_CHECK_HIP(hy::transpose2d(w_out, wt_out, C, C, false, stream));
+  hy::GemmArgs gi{u, wt_in, pbuf, B * V, J, C, V, false, true, nullptr};
+  HY_CHECK_HIP(hy::gemm(gi, false, stream));
+  hy::NdConvArgs a{};
+  a.X = X;
+  a.Y = Y;
+  a.Z = Z;
+  a.C = C;
+  a.NO = N;
+  a.B = B;
+  a.p = pbuf;
+  a.dskip = dskip;
+  a.gate = gate;
+  a.zbuf[0] = reinterpret_cast<float*>(wsb + w.z0);
+  a.zbuf[1] = reinterpret_cast<float*>(wsb + w.z1);
+  a.zfinal = zfin;
+  a.Yint = reinterpret_cast<float2*>(wsb + w.Y);
+  a.kh = reinterpret_cast<const float2*>(cb + cl.kh);
+  a.tw128 = reinterpret_cast<const float2*>(cb + cl.tw);
+  HY_CHECK_HIP(hy::nd_conv(a, stream));
+  hy::GemmArgs go{zfin, wt_out, y, B * V, C, C, V, true, false, nullptr};
+  HY_CHECK_HIP(hy::gemm(go, false, stream));
+  return HYENA_OK;
 }
 
 }  // extern "C"

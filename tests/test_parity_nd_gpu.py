@@ -1,0 +1,61 @@
+"""Parity of the 3D (HyenaND) HIP path (through the C ABI) with the fp64 oracle.
+
+Bar (fp32 storage): max |y - y_ref| / max |y_ref| <= 1e-4 over the whole output."""
+import numpy as np
+import pytest
+
+from synth import make_nd
+from tests.gpu_util import gpu_nd, oracle_nd, rel_err, say
+
+pytestmark = pytest.mark.gpu
+
+
+def _check(inp, tol=1e-4):
+    say(f"nd case B={inp.B} grid={inp.X}x{inp.Y}x{inp.Z} C={inp.C} N={inp.N} seed={inp.meta['seed']}")
+    y = gpu_nd(inp)
+    ref, _ = oracle_nd(inp)
+    err = rel_err(y, ref)
+    say(f"  rel err {err:.3e}")
+    assert np.all(np.isfinite(y))
+    assert err <= tol, err
+
+
+def test_nd_filter_matches_oracle():
+    inp = make_nd(41, 1, 8, 8, 8, 64, N=2, W=64)
+    say("nd filter 8^3 C=64 N=2")
+    _, k = gpu_nd(inp, with_k=True)
+    _, kref = oracle_nd(inp)
+    assert rel_err(k, kref) < 1e-5
+
+
+@pytest.mark.parametrize("B,X,Y,C,N,spread", [
+    (2, 4, 4, 64, 2, 0.5),     # smallest grid, gate exercised by mean offsets
+    (2, 8, 8, 64, 2, 0.5),
+    (1, 8, 8, 64, 2, 0.5),     # odd batch: the second half of the packed field is empty
+    (3, 8, 8, 64, 1, 0.0),
+    (2, 16, 8, 64, 2, 0.5),    # X != Y
+    (2, 8, 16, 128, 3, 0.5),
+    (2, 16, 16, 64, 2, 0.5),
+    (2, 32, 32, 64, 1, 0.5),
+])
+def test_nd_sweep(B, X, Y, C, N, spread):
+    _check(make_nd(200 + B + X + Y + C + N, B, X, Y, Y, C, N=N, W=64, u_mean_spread=spread))
+
+
+def test_nd_delta_kernel_closed_form():
+    # constant MLP output and a very fast radial window: K ~ delta at offset 0, D = 0
+    inp = make_nd(42, 2, 8, 8, 8, 64, N=2, W=32, u_mean_spread=0.7)
+    inp.w3 = np.zeros_like(inp.w3)
+    inp.b3 = np.ones_like(inp.b3)
+    inp.decay = np.full_like(inp.decay, 1.0e4)
+    inp.dskip = np.zeros_like(inp.dskip)
+    y = gpu_nd(inp)
+    import scipy.special
+    p = inp.u.astype(np.float64) @ inp.w_in.astype(np.float64)
+    C = inp.C
+    v, x1, x2 = p[..., :C], p[..., C:2 * C], p[..., 2 * C:]
+    m = inp.u.astype(np.float64).mean(axis=(1, 2, 3))
+    g1 = scipy.special.expit(inp.gate_a[0] * m + inp.gate_b[0])[:, None, None, None, :]
+    g2 = scipy.special.expit(inp.gate_a[1] * m + inp.gate_b[1])[:, None, None, None, :]
+    want = (x2 * g2 * x1 * g1 * v) @ inp.w_out.astype(np.float64)
+    assert rel_err(y, want) < 1e-4
