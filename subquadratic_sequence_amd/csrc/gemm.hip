@@ -3,7 +3,7 @@
 // The in-projection (u [B*L][D] times W_in) and the out-projection
 // (z [B][D][L] times W_out) are the only dense contractions of the operator.
 // C = A * B with B supplied transposed (Bt [N][K], K contiguous) so that both
-// MFMA operands are read from LDS as K-contiguous 16-byte fragments.
+// MFMA operands are read from LDS as K-contiguous fragments.
 //  * A_CM: A is channel-major [Bsz][K][Lseq] (the layout the long convolution
 //    produces); tiles are loaded along M and transposed while stored to LDS.
 //  * C_CM: C is written channel-major [Bsz][N][Lseq] (the layout the long
@@ -11,10 +11,14 @@
 //  * SC (with C_CM): the causal length-3 depthwise short convolution along the
 //    sequence is applied in the epilogue, s_t = w0 p_t + w1 p_{t-1} + w2 p_{t-2}
 //    (zero history at the start of every sequence). M-tiles then overlap by 8
-//    rows: a tile computes rows [m0 - 8, m0 + 120) and writes [m0, m0 + 120), so
+//    rows: a tile computes rows [m0 - 8, m0 + 248) and writes [m0, m0 + 248), so
 //    the two previous rows of every written row are on chip.
-// bf16 storage uses v_mfma_f32_32x32x16_bf16, fp32 uses v_mfma_f32_32x32x2_f32;
-// accumulation is fp32 in both cases.
+// Block tile 256 x 256, eight waves of 128 x 64 (8 accumulators of 32 x 32 per
+// wave, two waves per SIMD), K step of 64 bytes per row, LDS double buffered
+// with the next tile staged in registers. Tiles are numbered so that the
+// workgroups dispatched to one XCD walk the N-tiles of one M-tile together
+// (they share the A rows in that XCD's L2). bf16 storage uses v_mfma_f32_32x32x16_bf16, fp32 uses
+// v_mfma_f32_32x32x2_f32; accumulation is fp32 in both cases.
 #include "common.h"
 #include "kernels.h"
 
@@ -23,58 +27,78 @@ namespace hy {
 typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8;
 typedef __attribute__((ext_vector_type(16))) float f32x16;
 
-constexpr int GBM = 128, GBN = 128;
+constexpr int GBM = 256, GBN = 256;
+constexpr int kScRows = GBM - 8;  // rows written per M-tile with the short-conv epilogue
 
 template <typename T> struct GemmCfg {
   static constexpr int VEC = 16 / sizeof(T);    // elements per 16-byte chunk
   static constexpr int BK = 64 / sizeof(T);     // K elements per tile row (64 bytes)
   static constexpr int LDK = BK + VEC;          // padded LDS row (80 bytes)
+  static constexpr int TILE = GBM * LDK;        // elements per operand tile
+  static constexpr int CHUNKS = GBM * BK / VEC / 512;  // 16-byte chunks per thread per operand
 };
 
-constexpr int kCsLd = GBM + 4;  // staging row (floats) for channel-major output
+constexpr int kCsLd = GBM + 4;  // staging row (floats), channel-major output: [64 n][256 m]
+constexpr int kRmLd = 64 + 4;   // staging row (floats), row-major output: [256 m][64 n]
+constexpr size_t kTileBytes = 2 * 2 * GBM * 80;  // two buffers of A and B, 80-byte rows
+constexpr size_t kStageBytes = 64 * kCsLd * 4 > 256 * kRmLd * 4 ? 64 * kCsLd * 4 : 256 * kRmLd * 4;
+constexpr size_t kGemmLds = kTileBytes > kStageBytes ? kTileBytes : kStageBytes;
 
-constexpr int kScRows = 120;  // rows written per M-tile with the short-conv epilogue
+constexpr int kXcds = 8;
+
+// tile number of workgroup `bid` when consecutive workgroups go round robin to
+// the XCDs: XCD x receives the contiguous range of tile numbers it would get
+// from a blocked split of [0, total)
+__device__ __forceinline__ int xcd_tile(int bid, int total) {
+  const int q = total / kXcds, r = total % kXcds;
+  const int x = bid % kXcds, k = bid / kXcds;
+  return x < r ? x * (q + 1) + k : r * (q + 1) + (x - r) * q + k;
+}
 
 template <typename T, bool A_CM, bool C_CM, bool SC>
-__global__ __launch_bounds__(256, 2) void gemm_kernel(const T* __restrict__ A, const T* __restrict__ Bt,
+__global__ __launch_bounds__(512, 1) void gemm_kernel(const T* __restrict__ A, const T* __restrict__ Bt,
                                                       T* __restrict__ C, int M, int N, int K, int Lseq,
-                                                      const float* __restrict__ short_w) {
+                                                      const float* __restrict__ short_w, int ntn, int ntiles) {
   using Cfg = GemmCfg<T>;
-  constexpr int BK = Cfg::BK, LDK = Cfg::LDK, VEC = Cfg::VEC;
-  constexpr int TILE_BYTES = 2 * GBM * LDK * (int)sizeof(T);
-  constexpr int STAGE_BYTES = 64 * kCsLd * 4;
-  __shared__ __attribute__((aligned(16))) char smem[TILE_BYTES > STAGE_BYTES ? TILE_BYTES : STAGE_BYTES];
-  T* As = reinterpret_cast<T*>(smem);
-  T* Bs = As + GBM * LDK;
+  constexpr int BK = Cfg::BK, LDK = Cfg::LDK, VEC = Cfg::VEC, NCH = Cfg::CHUNKS;
+  extern __shared__ float4 smem4[];
+  char* smem = reinterpret_cast<char*>(smem4);
+  T* As0 = reinterpret_cast<T*>(smem);  // [2][GBM][LDK] then Bs [2][GBN][LDK]
+  T* Bs0 = As0 + 2 * Cfg::TILE;
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int wm = wave >> 1, wn = wave & 1;
-  const int n0 = blockIdx.x * GBN;
-  const int m0 = SC ? (int)blockIdx.y * kScRows - 8 : (int)blockIdx.y * GBM;  // first A row of the tile
+  const int wm = wave >> 2, wn = wave & 3;  // 2 x 4 waves of 128 x 64
+  const int tile = xcd_tile(blockIdx.x, ntiles);
+  const int tm = tile / ntn, tn = tile - tm * ntn;
+  const int n0 = tn * GBN;
+  const int m0 = SC ? tm * kScRows - 8 : tm * GBM;  // first A row of the tile
 
-  f32x16 acc[2][2];
+  f32x16 acc[4][2];
 #pragma unroll
-  for (int i = 0; i < 2; ++i)
+  for (int i = 0; i < 4; ++i)
 #pragma unroll
     for (int j = 0; j < 2; ++j)
 #pragma unroll
       for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.f;
 
-  uint4 ra[2], rb[2];
+  uint4 ra[NCH], rb[NCH];
   auto load_tile = [&](int k0) {
 #pragma unroll
-    for (int i = 0; i < 2; ++i) {
-      const int c = tid + i * 256;
+    for (int i = 0; i < NCH; ++i) {
+      const int c = tid + i * 512;
       if (!A_CM) {
         const int row = c >> 2, kc = (c & 3) * VEC;
         const int m = m0 + row;
         ra[i] = (m >= 0 && m < M) ? *reinterpret_cast<const uint4*>(A + (size_t)m * K + k0 + kc)
                                   : make_uint4(0, 0, 0, 0);
       } else {
+        // chunks of VEC consecutive m for one k; ra[2j] and ra[2j + 1] hold
+        // k = 2p and 2p + 1 of the same m chunk (pair p = tid + 512 j)
         constexpr int CPR = GBM / VEC;  // chunks per k-row
-        const int k = c / CPR, mc = (c % CPR) * VEC;
+        const int pair = tid + (i >> 1) * 512, hi = i & 1;
+        const int k = 2 * (pair / CPR) + hi, mc = (pair % CPR) * VEC;
         const int m = m0 + mc;
-        if (m < M) {
+        if (m >= 0 && m < M) {
           const int b = m / Lseq, t = m - b * Lseq;
           ra[i] = *reinterpret_cast<const uint4*>(A + ((size_t)b * K + k0 + k) * Lseq + t);
         } else {
@@ -86,19 +110,35 @@ __global__ __launch_bounds__(256, 2) void gemm_kernel(const T* __restrict__ A, c
       rb[i] = (n < N) ? *reinterpret_cast<const uint4*>(Bt + (size_t)n * K + k0 + kc) : make_uint4(0, 0, 0, 0);
     }
   };
-  auto store_tile = [&]() {
+  auto store_tile = [&](int buf) {
+    T* As = As0 + buf * Cfg::TILE;
+    T* Bs = Bs0 + buf * Cfg::TILE;
 #pragma unroll
-    for (int i = 0; i < 2; ++i) {
-      const int c = tid + i * 256;
+    for (int i = 0; i < NCH; ++i) {
+      const int c = tid + i * 512;
       if (!A_CM) {
         const int row = c >> 2, kc = (c & 3) * VEC;
         *reinterpret_cast<uint4*>(As + row * LDK + kc) = ra[i];
-      } else {
+      } else if (i % 2 == 0) {
+        // ra[i] holds k = 2p, ra[i + 1] holds k = 2p + 1 for the same m chunk:
+        // interleave them into 32-bit (bf16) or 64-bit (fp32) LDS writes
         constexpr int CPR = GBM / VEC;
-        const int k = c / CPR, mc = (c % CPR) * VEC;
-        const T* v = reinterpret_cast<const T*>(&ra[i]);
+        const int pair = tid + (i >> 1) * 512;
+        const int k = 2 * (pair / CPR), mc = (pair % CPR) * VEC;
+        if constexpr (sizeof(T) == 2) {
+          const unsigned short* lo = reinterpret_cast<const unsigned short*>(&ra[i]);
+          const unsigned short* hi = reinterpret_cast<const unsigned short*>(&ra[i + 1]);
 #pragma unroll
-        for (int q = 0; q < VEC; ++q) As[(mc + q) * LDK + k] = v[q];
+          for (int q = 0; q < VEC; ++q)
+            *reinterpret_cast<unsigned int*>(As + (mc + q) * LDK + k) =
+                (unsigned int)lo[q] | ((unsigned int)hi[q] << 16);
+        } else {
+          const float* lo = reinterpret_cast<const float*>(&ra[i]);
+          const float* hi = reinterpret_cast<const float*>(&ra[i + 1]);
+#pragma unroll
+          for (int q = 0; q < VEC; ++q)
+            *reinterpret_cast<float2*>(As + (mc + q) * LDK + k) = make_float2(lo[q], hi[q]);
+        }
       }
       const int row = c >> 2, kc = (c & 3) * VEC;
       *reinterpret_cast<uint4*>(Bs + row * LDK + kc) = rb[i];
@@ -107,22 +147,26 @@ __global__ __launch_bounds__(256, 2) void gemm_kernel(const T* __restrict__ A, c
 
   const int ktiles = K / BK;
   load_tile(0);
-  store_tile();
+  store_tile(0);
   __syncthreads();
   for (int kt = 0; kt < ktiles; ++kt) {
+    const int cur = kt & 1;
     if (kt + 1 < ktiles) load_tile((kt + 1) * BK);
-    const int ar = wm * 64 + (lane & 31), br = wn * 64 + (lane & 31);
+    const T* As = As0 + cur * Cfg::TILE;
+    const T* Bs = Bs0 + cur * Cfg::TILE;
+    const int ar = wm * 128 + (lane & 31), br = wn * 64 + (lane & 31);
     if constexpr (sizeof(T) == 2) {
 #pragma unroll
       for (int kk = 0; kk < BK; kk += 16) {
-        bf16x8 af[2], bfr[2];
+        bf16x8 af[4], bfr[2];
 #pragma unroll
-        for (int i = 0; i < 2; ++i) {
+        for (int i = 0; i < 4; ++i)
           af[i] = *reinterpret_cast<const bf16x8*>(As + (ar + i * 32) * LDK + kk + (lane >> 5) * 8);
-          bfr[i] = *reinterpret_cast<const bf16x8*>(Bs + (br + i * 32) * LDK + kk + (lane >> 5) * 8);
-        }
 #pragma unroll
-        for (int i = 0; i < 2; ++i)
+        for (int j = 0; j < 2; ++j)
+          bfr[j] = *reinterpret_cast<const bf16x8*>(Bs + (br + j * 32) * LDK + kk + (lane >> 5) * 8);
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
 #pragma unroll
           for (int j = 0; j < 2; ++j)
             acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[i], bfr[j], acc[i][j], 0, 0, 0);
@@ -130,88 +174,108 @@ __global__ __launch_bounds__(256, 2) void gemm_kernel(const T* __restrict__ A, c
     } else {
 #pragma unroll
       for (int kk = 0; kk < BK; kk += 2) {
-        float af[2], bfr[2];
+        float af[4], bfr[2];
 #pragma unroll
-        for (int i = 0; i < 2; ++i) {
-          af[i] = As[(ar + i * 32) * LDK + kk + (lane >> 5)];
-          bfr[i] = Bs[(br + i * 32) * LDK + kk + (lane >> 5)];
-        }
+        for (int i = 0; i < 4; ++i) af[i] = As[(ar + i * 32) * LDK + kk + (lane >> 5)];
 #pragma unroll
-        for (int i = 0; i < 2; ++i)
+        for (int j = 0; j < 2; ++j) bfr[j] = Bs[(br + j * 32) * LDK + kk + (lane >> 5)];
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
 #pragma unroll
           for (int j = 0; j < 2; ++j)
             acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x2f32(af[i], bfr[j], acc[i][j], 0, 0, 0);
       }
     }
+    if (kt + 1 < ktiles) store_tile(cur ^ 1);
     __syncthreads();
-    if (kt + 1 < ktiles) {
-      store_tile();
-      __syncthreads();
-    }
   }
 
   // Epilogue. Accumulator element e of lane l in block (i, j):
   //   row = i*32 + (e/4)*8 + (l/32)*4 + e%4, col = j*32 + l%32 (within the wave tile).
-  if (!C_CM) {
+  // Four rounds, one per 64-column quarter (the waves with wn == h hold it);
+  // the quarter is staged in LDS as fp32 and written with 16-byte stores.
+  float* Cs = reinterpret_cast<float*>(smem);
 #pragma unroll
-    for (int i = 0; i < 2; ++i)
-#pragma unroll
-      for (int j = 0; j < 2; ++j)
-#pragma unroll
-        for (int e = 0; e < 16; ++e) {
-          const int m = m0 + wm * 64 + i * 32 + (e >> 2) * 8 + (lane >> 5) * 4 + (e & 3);
-          const int n = n0 + wn * 64 + j * 32 + (lane & 31);
-          if (m < M && n < N) stf(C + (size_t)m * N + n, acc[i][j][e]);
-        }
-    return;
-  }
-  float* Cs = reinterpret_cast<float*>(smem);  // [64 n][kCsLd] for one half of the n range
-#pragma unroll
-  for (int h = 0; h < 2; ++h) {
+  for (int h = 0; h < 4; ++h) {
     if (wn == h) {
 #pragma unroll
-      for (int i = 0; i < 2; ++i)
+      for (int i = 0; i < 4; ++i)
 #pragma unroll
         for (int j = 0; j < 2; ++j)
 #pragma unroll
-          for (int e = 0; e < 16; ++e) {
-            const int ml = wm * 64 + i * 32 + (e >> 2) * 8 + (lane >> 5) * 4 + (e & 3);
+          for (int e4 = 0; e4 < 4; ++e4) {
+            const int ml = wm * 128 + i * 32 + e4 * 8 + (lane >> 5) * 4;
             const int nl = j * 32 + (lane & 31);
-            Cs[nl * kCsLd + ml] = acc[i][j][e];
+            const float4 q = make_float4(acc[i][j][4 * e4], acc[i][j][4 * e4 + 1], acc[i][j][4 * e4 + 2],
+                                         acc[i][j][4 * e4 + 3]);
+            if (C_CM) {
+              // [n][m]: the four rows of a lane are contiguous
+              *reinterpret_cast<float4*>(Cs + nl * kCsLd + ml) = q;
+            } else {
+              // [m][n]
+              Cs[(ml + 0) * kRmLd + nl] = q.x;
+              Cs[(ml + 1) * kRmLd + nl] = q.y;
+              Cs[(ml + 2) * kRmLd + nl] = q.z;
+              Cs[(ml + 3) * kRmLd + nl] = q.w;
+            }
           }
     }
     __syncthreads();
-    // 64 rows (n) x 128 (m) in chunks of 8 consecutive m; with SC the first
-    // chunk of every row (the 8 overlap rows) is not written
-    for (int c = tid; c < 64 * 16; c += 256) {
-      const int nl = c >> 4, mc = (c & 15) * 8;
-      const int n = n0 + h * 64 + nl, m = m0 + mc;
-      if (n < N && m < M && (!SC || mc >= 8)) {
-        const int b = m / Lseq, t = m - b * Lseq;
-        T* dst = C + ((size_t)b * N + n) * Lseq + t;
-        const float* src = Cs + nl * kCsLd + mc;
-        float o[8];
-        if (SC) {
-          const float w0 = short_w[3 * n], w1 = short_w[3 * n + 1], w2 = short_w[3 * n + 2];
+    if (C_CM) {
+      // 64 rows (n) x 256 (m) in chunks of 8 consecutive m; with SC the first
+      // chunk of every row (the 8 overlap rows) is not written
+      for (int c = tid; c < 64 * 32; c += 512) {
+        const int nl = c >> 5, mc = (c & 31) * 8;
+        const int n = n0 + h * 64 + nl, m = m0 + mc;
+        if (n < N && m >= 0 && m < M && (!SC || mc >= 8)) {
+          const int b = m / Lseq, t = m - b * Lseq;
+          T* dst = C + ((size_t)b * N + n) * Lseq + t;
+          const float* src = Cs + nl * kCsLd + mc;
+          const float4 s0 = *reinterpret_cast<const float4*>(src);
+          const float4 s1 = *reinterpret_cast<const float4*>(src + 4);
+          float o[8] = {s0.x, s0.y, s0.z, s0.w, s1.x, s1.y, s1.z, s1.w};
+          if (SC) {
+            const float w0 = short_w[3 * n], w1 = short_w[3 * n + 1], w2 = short_w[3 * n + 2];
+            const float pm1 = (t >= 1) ? src[-1] : 0.f, pm2 = (t >= 2) ? src[-2] : 0.f;
+            float prev1 = pm1, prev2 = pm2;
 #pragma unroll
-          for (int v = 0; v < 8; ++v) {
-            float s = w0 * src[v];
-            if (t + v >= 1) s += w1 * src[v - 1];
-            if (t + v >= 2) s += w2 * src[v - 2];
-            o[v] = s;
+            for (int v = 0; v < 8; ++v) {
+              const float cur = o[v];
+              o[v] = w0 * cur + w1 * prev1 + w2 * prev2;
+              prev2 = prev1;
+              prev1 = cur;
+            }
           }
-        } else {
+          if constexpr (sizeof(T) == 2) {
+            bf16x8 ob;
 #pragma unroll
-          for (int v = 0; v < 8; ++v) o[v] = src[v];
+            for (int v = 0; v < 8; ++v) ob[v] = (__bf16)o[v];
+            *reinterpret_cast<bf16x8*>(dst) = ob;
+          } else {
+            *reinterpret_cast<float4*>(dst) = make_float4(o[0], o[1], o[2], o[3]);
+            *reinterpret_cast<float4*>(dst + 4) = make_float4(o[4], o[5], o[6], o[7]);
+          }
         }
-        if constexpr (sizeof(T) == 2) {
-          bf16x8 ob;
-#pragma unroll
-          for (int v = 0; v < 8; ++v) ob[v] = (__bf16)o[v];
-          *reinterpret_cast<bf16x8*>(dst) = ob;
-        } else {
-          *reinterpret_cast<float4*>(dst) = make_float4(o[0], o[1], o[2], o[3]);
-          *reinterpret_cast<float4*>(dst + 4) = make_float4(o[4], o[5], o[6], o[7]);
+      }
+    } else {
+      // 256 rows (m) x 64 (n) in chunks of 8 consecutive n
+      for (int c = tid; c < 256 * 8; c += 512) {
+        const int ml = c >> 3, nc = (c & 7) * 8;
+        const int m = m0 + ml, n = n0 + h * 64 + nc;
+        if (m >= 0 && m < M && n < N) {
+          const float* src = Cs + ml * kRmLd + nc;
+          const float4 s0 = *reinterpret_cast<const float4*>(src);
+          const float4 s1 = *reinterpret_cast<const float4*>(src + 4);
+          T* dst = C + (size_t)m * N + n;
+          if constexpr (sizeof(T) == 2) {
+            bf16x8 ob;
+            ob[0] = (__bf16)s0.x; ob[1] = (__bf16)s0.y; ob[2] = (__bf16)s0.z; ob[3] = (__bf16)s0.w;
+            ob[4] = (__bf16)s1.x; ob[5] = (__bf16)s1.y; ob[6] = (__bf16)s1.z; ob[7] = (__bf16)s1.w;
+            *reinterpret_cast<bf16x8*>(dst) = ob;
+          } else {
+            *reinterpret_cast<float4*>(dst) = s0;
+            *reinterpret_cast<float4*>(dst + 4) = s1;
+          }
         }
       }
     }
@@ -223,12 +287,21 @@ template <typename T>
 static hipError_t launch_gemm(const GemmArgs& g, hipStream_t s) {
   const bool sc = g.short_w != nullptr;
   const int mtiles = sc ? (g.M + kScRows - 1) / kScRows : (g.M + GBM - 1) / GBM;
-  dim3 grid((g.N + GBN - 1) / GBN, mtiles), block(256);
+  const int ntn = (g.N + GBN - 1) / GBN;
+  const int ntiles = ntn * mtiles;
+  dim3 grid(ntiles), block(512);
   const T* A = static_cast<const T*>(g.A);
   const T* B = static_cast<const T*>(g.Bt);
   T* C = static_cast<T*>(g.C);
-#define GEMM_LAUNCH(acm, ccm, scv) \
-  hipLaunchKernelGGL((gemm_kernel<T, acm, ccm, scv>), grid, block, 0, s, A, B, C, g.M, g.N, g.K, g.Lseq, g.short_w)
+#define GEMM_LAUNCH(acm, ccm, scv)                                                                    \
+  do {                                                                                                \
+    auto fn = gemm_kernel<T, acm, ccm, scv>;                                                          \
+    hipError_t e = hipFuncSetAttribute((const void*)fn, hipFuncAttributeMaxDynamicSharedMemorySize,   \
+                                       (int)kGemmLds);                                                \
+    if (e != hipSuccess) return e;                                                                    \
+    hipLaunchKernelGGL(fn, grid, block, kGemmLds, s, A, B, C, g.M, g.N, g.K, g.Lseq, g.short_w, ntn, \
+                       ntiles);                                                                       \
+  } while (0)
   if (sc) {
     if (!g.c_cm || g.a_cm) return hipErrorInvalidValue;
     GEMM_LAUNCH(false, true, true);
