@@ -71,6 +71,9 @@ def main():
     ap.add_argument("--workload", default=DEFAULT_WORKLOAD)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-tokens", type=int, default=4096)
+    ap.add_argument("--calib-copy", type=int, default=0, metavar="MIB",
+                    help="only run a plain device copy of MIB MiB (reads and writes MIB MiB), for calibrating "
+                         "the FETCH_SIZE / WRITE_SIZE counters, and exit")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only (asked for --gpus {args.gpus}); this path is built and "
@@ -80,6 +83,16 @@ def main():
     import torch
     import subquadratic_sequence_amd as hs
     from synth import CONFIGS, make_config
+
+    if args.calib_copy:
+        n = args.calib_copy * (1 << 20) // 4
+        src = torch.ones(n, dtype=torch.float32, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            torch.mul(src, 1.0, out=dst)  # one elementwise kernel: reads and writes n * 4 bytes
+        torch.cuda.synchronize()
+        print(json.dumps({"calib_copy_bytes": n * 4}))
+        return
 
     cfg = CONFIGS[args.workload]
     if cfg["kind"] != "1d":

@@ -93,10 +93,12 @@ __global__ __launch_bounds__(512, 1) void gemm_kernel(const T* __restrict__ A, c
                                   : make_uint4(0, 0, 0, 0);
       } else {
         // chunks of VEC consecutive m for one k; ra[2j] and ra[2j + 1] hold
-        // k = 2p and 2p + 1 of the same m chunk (pair p = tid + 512 j)
-        constexpr int CPR = GBM / VEC;  // chunks per k-row
-        const int pair = tid + (i >> 1) * 512, hi = i & 1;
-        const int k = 2 * (pair / CPR) + hi, mc = (pair % CPR) * VEC;
+        // k = 2p and 2p + 1 of the same m chunk. Consecutive lanes take
+        // consecutive k pairs (then chunks), so the interleaved LDS writes of
+        // 16 lanes land on 16 consecutive words.
+        constexpr int KP = BK / 2;      // k pairs per tile
+        const int slot = tid + (i >> 1) * 512, hi = i & 1;
+        const int k = 2 * (slot % KP) + hi, mc = (slot / KP) * VEC;
         const int m = m0 + mc;
         if (m >= 0 && m < M) {
           const int b = m / Lseq, t = m - b * Lseq;
@@ -122,9 +124,9 @@ __global__ __launch_bounds__(512, 1) void gemm_kernel(const T* __restrict__ A, c
       } else if (i % 2 == 0) {
         // ra[i] holds k = 2p, ra[i + 1] holds k = 2p + 1 for the same m chunk:
         // interleave them into 32-bit (bf16) or 64-bit (fp32) LDS writes
-        constexpr int CPR = GBM / VEC;
-        const int pair = tid + (i >> 1) * 512;
-        const int k = 2 * (pair / CPR), mc = (pair % CPR) * VEC;
+        constexpr int KP = BK / 2;
+        const int slot = tid + (i >> 1) * 512;
+        const int k = 2 * (slot % KP), mc = (slot / KP) * VEC;
         if constexpr (sizeof(T) == 2) {
           const unsigned short* lo = reinterpret_cast<const unsigned short*>(&ra[i]);
           const unsigned short* hi = reinterpret_cast<const unsigned short*>(&ra[i + 1]);

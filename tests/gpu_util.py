@@ -2,6 +2,7 @@
 on the same seeded inputs."""
 from __future__ import annotations
 
+import os
 import sys
 
 import numpy as np
@@ -12,6 +13,10 @@ TOL = {"f32": 1e-4, "bf16": 2e-2}
 def say(msg: str):
     print(msg, flush=True)
     sys.stdout.flush()
+    path = os.environ.get("HYENA_TEST_LOG")
+    if path:
+        with open(path, "a") as f:
+            f.write(msg + "\n")
 
 
 def rel_err(y, ref) -> float:
