@@ -22,7 +22,7 @@ ARCH = "gfx950"
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = [
-    f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC",
+    f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC", "-fno-signed-zeros",
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
     "-Wno-unused-result", "-Wno-unused-command-line-argument",
 ]

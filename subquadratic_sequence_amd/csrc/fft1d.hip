@@ -22,6 +22,8 @@
 //    inverse row DFT; the next column pass inverts the columns (keeping the
 //    N1/2 outputs t < L), gates, adds the skip, writes z^{n+1} once and, from
 //    the same registers, starts the forward column DFT of the next order.
+#include <stdlib.h>
+
 #include "common.h"
 #include "kernels.h"
 
@@ -361,7 +363,7 @@ enum { ROW_CONV = 0, ROW_SPEC = 1 };
 
 // Persistent row pass; items are (channel pair, group of SP slots). The next
 // item's rows are loaded into registers before the current item is processed.
-template <typename YT, int N1, int N2, int MODE>
+template <typename YT, int N1, int N2, int MODE, bool PF, bool EPQ>
 __global__ __launch_bounds__(RowCfg<N2>::WG) void rowpass_kernel(YT* __restrict__ Y, float4* __restrict__ pq,
                                                                  const float2* __restrict__ tw_row, int pq_off,
                                                                  int pair_off, int pq_mod, int nitems) {
@@ -397,15 +399,19 @@ __global__ __launch_bounds__(RowCfg<N2>::WG) void rowpass_kernel(YT* __restrict_
     float4* pqp = pq + ((size_t)pq_off + (pl + pair_off) % pq_mod) * PQROWS * N2;
     // spectrum rows of this item, issued before the forward DFT
     float4 pv[PER / 2];
-    if (MODE == ROW_CONV && s != 0) {
-      const float4* pqs = pqp + (size_t)s * N2;
+    auto load_pq = [&]() {
+      if (MODE == ROW_CONV && s != 0) {
+        const float4* pqs = pqp + (size_t)s * N2;
 #pragma unroll
-      for (int q = 0; q < PER / 2; ++q) pv[q] = pqs[isB * C::TG + lt + q * 2 * C::TG];
-    }
+        for (int q = 0; q < PER / 2; ++q) pv[q] = pqs[isB * C::TG + lt + q * 2 * C::TG];
+      }
+    };
+    if (EPQ) load_pq();
 #pragma unroll
     for (int q = 0; q < PER; ++q) row[pad16(lt + q * C::TG)] = cvt2(y[q]);
     __syncthreads();
     fft_lds<N2, C::E, false>(row, lt, tw_row);
+    if (!EPQ) load_pq();
     if (s != 0) {
       float2* ra = rows + (r & ~1) * C::RB;
       float2* rb = ra + C::RB;
@@ -464,12 +470,18 @@ __global__ __launch_bounds__(RowCfg<N2>::WG) void rowpass_kernel(YT* __restrict_
   while (true) {
     const int next = item + gridDim.x;
     const bool more = next < nitems;
-    YT nxt[PER];
-    if (more) load(next, nxt);
-    process(item, cur);
-    if (!more) break;
+    if (PF) {
+      YT nxt[PER];
+      if (more) load(next, nxt);
+      process(item, cur);
+      if (!more) break;
 #pragma unroll
-    for (int q = 0; q < PER; ++q) cur[q] = nxt[q];
+      for (int q = 0; q < PER; ++q) cur[q] = nxt[q];
+    } else {
+      process(item, cur);
+      if (!more) break;
+      load(next, cur);
+    }
     item = next;
     __syncthreads();  // rows of this item fully read before the next one writes them
   }
@@ -604,7 +616,18 @@ static hipError_t launch_row_t(void* Y, float4* pq, const float2* tw_row, int pq
   using C = RowCfg<N2>;
   const int items = pairs * ((N1 / 2) / C::SP);
   YT* y = static_cast<YT*>(Y);
-  auto fn = (mode == ROW_CONV) ? rowpass_kernel<YT, N1, N2, ROW_CONV> : rowpass_kernel<YT, N1, N2, ROW_SPEC>;
+  // variant: bit 0 = prefetch the next item's rows, bit 1 = spectrum loads before the forward DFT
+  static const int variant = [] {
+    const char* v = getenv("HYENA_ROW_VARIANT");
+    return v ? atoi(v) & 3 : 3;
+  }();
+  using Fn = void (*)(YT*, float4*, const float2*, int, int, int, int);
+  Fn fn;
+  if (mode != ROW_CONV) fn = rowpass_kernel<YT, N1, N2, ROW_SPEC, true, false>;
+  else if (variant == 0) fn = rowpass_kernel<YT, N1, N2, ROW_CONV, false, false>;
+  else if (variant == 1) fn = rowpass_kernel<YT, N1, N2, ROW_CONV, true, false>;
+  else if (variant == 2) fn = rowpass_kernel<YT, N1, N2, ROW_CONV, false, true>;
+  else fn = rowpass_kernel<YT, N1, N2, ROW_CONV, true, true>;
   hipError_t e = allow_lds((const void*)fn, C::LDS);
   if (e != hipSuccess) return e;
   static int grid[2] = {0, 0};

@@ -19,6 +19,8 @@
 // workgroups dispatched to one XCD walk the N-tiles of one M-tile together
 // (they share the A rows in that XCD's L2). bf16 storage uses v_mfma_f32_32x32x16_bf16, fp32 uses
 // v_mfma_f32_32x32x2_f32; accumulation is fp32 in both cases.
+#include <type_traits>
+
 #include "common.h"
 #include "kernels.h"
 
@@ -81,82 +83,105 @@ __global__ __launch_bounds__(512, 1) void gemm_kernel(const T* __restrict__ A, c
 #pragma unroll
       for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.f;
 
-  uint4 ra[NCH], rb[NCH];
-  auto load_tile = [&](int k0) {
+  uint4 ra2[2][NCH], rb2[2][NCH];  // two K tiles in flight
+  // Per-thread global pointers, predicates and LDS offsets of the tile loads,
+  // computed once; each K step only advances the pointers.
+  const T* pa[NCH];
+  const T* pb[NCH];
+  bool va[NCH], vb[NCH];
+  int la[NCH], lb[NCH];
+  size_t a_step;  // elements between consecutive K tiles
+#pragma unroll
+  for (int i = 0; i < NCH; ++i) {
+    const int c = tid + i * 512;
+    const int row = c >> 2, kc = (c & 3) * VEC;
+    if (!A_CM) {
+      const int m = m0 + row;
+      va[i] = m >= 0 && m < M;
+      pa[i] = A + (size_t)(va[i] ? m : 0) * K + kc;
+      la[i] = row * LDK + kc;
+    } else {
+      // chunks of VEC consecutive m for one k; ra[2j] and ra[2j + 1] hold
+      // k = 2p and 2p + 1 of the same m chunk. Consecutive lanes take
+      // consecutive k pairs (then chunks), so the interleaved LDS writes of
+      // 16 lanes land on 16 consecutive words.
+      constexpr int KP = BK / 2;  // k pairs per tile
+      const int slot = tid + (i >> 1) * 512, hi = i & 1;
+      const int k = 2 * (slot % KP) + hi, mc = (slot / KP) * VEC;
+      const int m = m0 + mc;
+      va[i] = m >= 0 && m < M;
+      const int mm = va[i] ? m : 0;
+      const int b = mm / Lseq, t = mm - b * Lseq;
+      pa[i] = A + ((size_t)b * K + k) * Lseq + t;
+      la[i] = mc * LDK + (k & ~1);
+    }
+    const int n = n0 + row;
+    vb[i] = n < N;
+    pb[i] = Bt + (size_t)(vb[i] ? n : 0) * K + kc;
+    lb[i] = row * LDK + kc;
+  }
+  a_step = A_CM ? (size_t)BK * Lseq : (size_t)BK;
+
+  // The register set is always a compile-time constant so that ra2/rb2 stay in VGPRs.
+  auto load_tile = [&](auto set) {
+    uint4* ra = ra2[decltype(set)::value];
+    uint4* rb = rb2[decltype(set)::value];
 #pragma unroll
     for (int i = 0; i < NCH; ++i) {
-      const int c = tid + i * 512;
-      if (!A_CM) {
-        const int row = c >> 2, kc = (c & 3) * VEC;
-        const int m = m0 + row;
-        ra[i] = (m >= 0 && m < M) ? *reinterpret_cast<const uint4*>(A + (size_t)m * K + k0 + kc)
-                                  : make_uint4(0, 0, 0, 0);
-      } else {
-        // chunks of VEC consecutive m for one k; ra[2j] and ra[2j + 1] hold
-        // k = 2p and 2p + 1 of the same m chunk. Consecutive lanes take
-        // consecutive k pairs (then chunks), so the interleaved LDS writes of
-        // 16 lanes land on 16 consecutive words.
-        constexpr int KP = BK / 2;      // k pairs per tile
-        const int slot = tid + (i >> 1) * 512, hi = i & 1;
-        const int k = 2 * (slot % KP) + hi, mc = (slot / KP) * VEC;
-        const int m = m0 + mc;
-        if (m >= 0 && m < M) {
-          const int b = m / Lseq, t = m - b * Lseq;
-          ra[i] = *reinterpret_cast<const uint4*>(A + ((size_t)b * K + k0 + k) * Lseq + t);
-        } else {
-          ra[i] = make_uint4(0, 0, 0, 0);
-        }
-      }
-      const int row = c >> 2, kc = (c & 3) * VEC;
-      const int n = n0 + row;
-      rb[i] = (n < N) ? *reinterpret_cast<const uint4*>(Bt + (size_t)n * K + k0 + kc) : make_uint4(0, 0, 0, 0);
+      ra[i] = va[i] ? *reinterpret_cast<const uint4*>(pa[i]) : make_uint4(0, 0, 0, 0);
+      rb[i] = vb[i] ? *reinterpret_cast<const uint4*>(pb[i]) : make_uint4(0, 0, 0, 0);
+      pa[i] += a_step;
+      pb[i] += BK;
     }
   };
-  auto store_tile = [&](int buf) {
+  auto store_tile = [&](auto set) {
+    constexpr int buf = decltype(set)::value;
+    const uint4* ra = ra2[buf];
+    const uint4* rb = rb2[buf];
     T* As = As0 + buf * Cfg::TILE;
     T* Bs = Bs0 + buf * Cfg::TILE;
 #pragma unroll
     for (int i = 0; i < NCH; ++i) {
-      const int c = tid + i * 512;
       if (!A_CM) {
-        const int row = c >> 2, kc = (c & 3) * VEC;
-        *reinterpret_cast<uint4*>(As + row * LDK + kc) = ra[i];
+        *reinterpret_cast<uint4*>(As + la[i]) = ra[i];
       } else if (i % 2 == 0) {
         // ra[i] holds k = 2p, ra[i + 1] holds k = 2p + 1 for the same m chunk:
         // interleave them into 32-bit (bf16) or 64-bit (fp32) LDS writes
-        constexpr int KP = BK / 2;
-        const int slot = tid + (i >> 1) * 512;
-        const int k = 2 * (slot % KP), mc = (slot / KP) * VEC;
         if constexpr (sizeof(T) == 2) {
           const unsigned short* lo = reinterpret_cast<const unsigned short*>(&ra[i]);
           const unsigned short* hi = reinterpret_cast<const unsigned short*>(&ra[i + 1]);
 #pragma unroll
           for (int q = 0; q < VEC; ++q)
-            *reinterpret_cast<unsigned int*>(As + (mc + q) * LDK + k) =
+            *reinterpret_cast<unsigned int*>(As + la[i] + q * LDK) =
                 (unsigned int)lo[q] | ((unsigned int)hi[q] << 16);
         } else {
           const float* lo = reinterpret_cast<const float*>(&ra[i]);
           const float* hi = reinterpret_cast<const float*>(&ra[i + 1]);
 #pragma unroll
           for (int q = 0; q < VEC; ++q)
-            *reinterpret_cast<float2*>(As + (mc + q) * LDK + k) = make_float2(lo[q], hi[q]);
+            *reinterpret_cast<float2*>(As + la[i] + q * LDK) = make_float2(lo[q], hi[q]);
         }
       }
-      const int row = c >> 2, kc = (c & 3) * VEC;
-      *reinterpret_cast<uint4*>(Bs + row * LDK + kc) = rb[i];
+      *reinterpret_cast<uint4*>(Bs + lb[i]) = rb[i];
     }
   };
 
+  // Tile kt sits in LDS buffer kt & 1 and travels through register set
+  // kt & 1, loaded two steps before it is needed.
+  using Set0 = std::integral_constant<int, 0>;
+  using Set1 = std::integral_constant<int, 1>;
   const int ktiles = K / BK;
-  load_tile(0);
-  store_tile(0);
+  load_tile(Set0{});
+  store_tile(Set0{});
+  if (ktiles > 1) load_tile(Set1{});
   __syncthreads();
-  for (int kt = 0; kt < ktiles; ++kt) {
-    const int cur = kt & 1;
-    if (kt + 1 < ktiles) load_tile((kt + 1) * BK);
+  const int ar = wm * 128 + (lane & 31), br = wn * 64 + (lane & 31);
+  auto step = [&](int kt, auto cur_c) {
+    constexpr int cur = decltype(cur_c)::value;
+    using Other = std::integral_constant<int, cur ^ 1>;
+    if (kt + 2 < ktiles) load_tile(cur_c);  // this set went to LDS one step ago
     const T* As = As0 + cur * Cfg::TILE;
     const T* Bs = Bs0 + cur * Cfg::TILE;
-    const int ar = wm * 128 + (lane & 31), br = wn * 64 + (lane & 31);
     if constexpr (sizeof(T) == 2) {
 #pragma unroll
       for (int kk = 0; kk < BK; kk += 16) {
@@ -188,8 +213,12 @@ __global__ __launch_bounds__(512, 1) void gemm_kernel(const T* __restrict__ A, c
             acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x2f32(af[i], bfr[j], acc[i][j], 0, 0, 0);
       }
     }
-    if (kt + 1 < ktiles) store_tile(cur ^ 1);
+    if (kt + 1 < ktiles) store_tile(Other{});
     __syncthreads();
+  };
+  for (int kt = 0; kt < ktiles; kt += 2) {
+    step(kt, Set0{});
+    if (kt + 1 < ktiles) step(kt + 1, Set1{});
   }
 
   // Epilogue. Accumulator element e of lane l in block (i, j):
