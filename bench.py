@@ -10,8 +10,8 @@ their spectra cached once before timing (one cache per layer, reused by every
 call). Prints one JSON line on stdout; progress goes to stderr.
 
 Roofline: the FFT long-convolution stage is the dominant kernel sequence. Its
-duration comes from HIP events recorded on the launch stream around that stage
-(hyena_fwd_profiled), averaged over the timed steps; the algorithmic bytes per
+duration comes from HIP events that the library records on the launch stream at
+the stage boundaries of every timed step (hyena_fwd_profiled), averaged; the algorithmic bytes per
 order are B*L*D*3*s + 8*D*(L+1) (read z^n and x^n, write z^{n+1}, read the
 filter spectrum), s the storage size of an activation.
 """
@@ -29,6 +29,9 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 DEFAULT_WORKLOAD = "order2_bf16_L64k_D768"
+# Kernel sources of the long-convolution stage; a traffic figure measured on other
+# sources is stale and is not reported.
+CONV_SOURCES = ["fft1d.hip", "common.h", "kernels.h"]
 METRIC = "Hyena fwd tokens/sec at L=64k,D=768 (1 GPU); FFT-conv HBM GB/s % of peak"
 HBM_PEAK_GBS = 8000.0
 
@@ -42,6 +45,34 @@ def conv_alg_bytes(B, L, D, N, s, lds_regime: bool) -> float:
         # all orders fused on chip: read v and x^1..x^N, write z^{N+1}, read N spectra
         return (N + 1) * B * L * D * s + B * L * D * s + N * 8.0 * D * (L + 1)
     return N * (3.0 * B * L * D * s + 8.0 * D * (L + 1))
+
+
+def conv_source_hash() -> str:
+    import hashlib
+    hsh = hashlib.sha256()
+    for name in CONV_SOURCES:
+        with open(os.path.join(ROOT, "subquadratic_sequence_amd", "csrc", name), "rb") as fh:
+            hsh.update(fh.read())
+    return hsh.hexdigest()
+
+
+def measured_traffic(workload: str, path: str | None = None):
+    """HBM bytes per step of the long-convolution stage, from the rocprofv3
+    FETCH_SIZE / WRITE_SIZE summary under profiles/ (each counter scaled by what it
+    reads for a plain copy of known size). None if there is no summary for this
+    workload or the kernel sources changed since it was taken."""
+    path = path or os.path.join(ROOT, "profiles", f"hbm_traffic_{workload}.txt")
+    if not os.path.exists(path):
+        return None
+    kv = {}
+    with open(path) as fh:
+        for line in fh:
+            if line.startswith("@") and ":" in line:
+                k, v = line[1:].split(":", 1)
+                kv[k.strip()] = v.strip()
+    if kv.get("conv_source_sha256") != conv_source_hash():
+        return None
+    return float(kv["conv_stage_bytes_per_step"])
 
 
 def cpu_baseline(inp, budget_tokens: int):
@@ -70,7 +101,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default=DEFAULT_WORKLOAD)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-tokens", type=int, default=4096)
+    ap.add_argument("--cpu-tokens", type=int, default=16384)
     ap.add_argument("--calib-copy", type=int, default=0, metavar="MIB",
                     help="only run a plain device copy of MIB MiB (reads and writes MIB MiB), for calibrating "
                          "the FETCH_SIZE / WRITE_SIZE counters, and exit")
@@ -118,20 +149,22 @@ def main():
     for _ in range(args.warmup):
         hs.hyena_fwd(layer, u, w_in, short_w, dskip, w_out, y=y, ws=ws)
     torch.cuda.synchronize()
+    # Four HIP events per step mark the stage boundaries on the launch stream
+    # (recorded by the library between its launches, no synchronisation).
+    events = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
+    for evs in events:
+        for ev in evs:
+            ev.record()
+    torch.cuda.synchronize()
     log(f"timing {args.steps} steps")
     t0 = time.perf_counter()
-    for _ in range(args.steps):
-        hs.hyena_fwd(layer, u, w_in, short_w, dskip, w_out, y=y, ws=ws)
+    for k in range(args.steps):
+        hs.hyena_fwd_profiled(layer, u, w_in, short_w, dskip, w_out, y, ws, events[k])
     torch.cuda.synchronize()
     elapsed = time.perf_counter() - t0
     ms_per_step = 1e3 * elapsed / args.steps
     value = B * L * args.steps / elapsed
-
-    # per-stage event times over the same number of steps
-    stages = np.zeros(3)
-    for _ in range(args.steps):
-        stages += np.array(hs.hyena_fwd_profiled(layer, u, w_in, short_w, dskip, w_out, y, ws))
-    stages /= args.steps
+    stages = np.mean([[evs[i].elapsed_time(evs[i + 1]) for i in range(3)] for evs in events], axis=0)
     lds = L <= 4096
     alg = conv_alg_bytes(B, L, D, N, s, lds)
     achieved = alg / (stages[1] * 1e-3) / 1e9
@@ -154,7 +187,7 @@ def main():
         "stage_ms": {"in_proj": stages[0], "fft_conv": stages[1], "out_proj": stages[2]},
         "roofline": {"bound": "hbm", "kernel": "fft_conv stage (all orders)", "achieved": achieved,
                      "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS,
-                     "alg_bytes": alg, "traffic": None},
+                     "alg_bytes": alg, "traffic": measured_traffic(args.workload)},
     }
     if not args.no_cpu_baseline:
         log("cpu baseline (oracle)")

@@ -109,16 +109,18 @@ int hyena_fwd(const hyena_layer *layer, const void *u, const void *w_in,
               const float *short_w, const float *dskip, const void *w_out,
               int B, int dtype, void *y, void *ws, size_t ws_bytes, hipStream_t stream);
 
-/* Same launches as hyena_fwd, with HIP events recorded on `stream` between the
- * stages; waits for the stream and writes the stage durations (host array of 3):
- *   stage_ms[0] in-projection (weight transposes + GEMM),
- *   stage_ms[1] long convolutions with gating (all orders),
- *   stage_ms[2] out-projection.
- * For measurement; unlike hyena_fwd it synchronises. */
+/* Same launches as hyena_fwd, plus hipEventRecord(events[i], stream) at the four
+ * stage boundaries, for timing the stages on the launch stream:
+ *   events[0] before the in-projection,
+ *   events[1] after it (weight transposes, GEMM with the short convolutions),
+ *   events[2] after the long convolutions with gating (all orders),
+ *   events[3] after the out-projection.
+ * events: host array of 4 events the caller created (and destroys); nothing here
+ * synchronises. A null `events` is HYENA_ERR_INVALID_ARG. */
 int hyena_fwd_profiled(const hyena_layer *layer, const void *u, const void *w_in,
                        const float *short_w, const float *dskip, const void *w_out,
                        int B, int dtype, void *y, void *ws, size_t ws_bytes, hipStream_t stream,
-                       float *stage_ms);
+                       const hipEvent_t *events);
 
 /* ------------------------------------------------------------------ 3D ---- */
 /*

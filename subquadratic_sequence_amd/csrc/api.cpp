@@ -230,7 +230,7 @@ int hyena_filter_gen(hyena_layer* layer, const hyena_filter_params* p, float* h_
 
 static int fwd_impl(const hyena_layer* layer, const void* u, const void* w_in, const float* short_w,
                     const float* dskip, const void* w_out, int B, int dtype, void* y, void* ws, size_t ws_bytes,
-                    hipStream_t stream, hipEvent_t* ev) {
+                    hipStream_t stream, const hipEvent_t* ev) {
   if (layer == nullptr) return HYENA_ERR_INVALID_ARG;
   if (dtype != HYENA_F32 && dtype != HYENA_BF16) return HYENA_ERR_INVALID_ARG;
   const void* ptrs[] = {u, w_in, short_w, dskip, w_out, y, ws};
@@ -298,21 +298,9 @@ int hyena_fwd(const hyena_layer* layer, const void* u, const void* w_in, const f
 
 int hyena_fwd_profiled(const hyena_layer* layer, const void* u, const void* w_in, const float* short_w,
                        const float* dskip, const void* w_out, int B, int dtype, void* y, void* ws, size_t ws_bytes,
-                       hipStream_t stream, float* stage_ms) {
-  if (stage_ms == nullptr) return HYENA_ERR_INVALID_ARG;
-  hipEvent_t ev[4] = {};
-  for (int i = 0; i < 4; ++i) {
-    if (hipEventCreate(&ev[i]) != hipSuccess) {
-      for (int j = 0; j < i; ++j) (void)hipEventDestroy(ev[j]);
-      return HYENA_ERR_HIP;
-    }
-  }
-  int st = fwd_impl(layer, u, w_in, short_w, dskip, w_out, B, dtype, y, ws, ws_bytes, stream, ev);
-  if (st == HYENA_OK && hipEventSynchronize(ev[3]) != hipSuccess) st = HYENA_ERR_HIP;
-  for (int i = 0; st == HYENA_OK && i < 3; ++i)
-    if (hipEventElapsedTime(&stage_ms[i], ev[i], ev[i + 1]) != hipSuccess) st = HYENA_ERR_HIP;
-  for (int i = 0; i < 4; ++i) (void)hipEventDestroy(ev[i]);
-  return st;
+                       hipStream_t stream, const hipEvent_t* events) {
+  if (events == nullptr) return HYENA_ERR_INVALID_ARG;
+  return fwd_impl(layer, u, w_in, short_w, dskip, w_out, B, dtype, y, ws, ws_bytes, stream, events);
 }
 
 }  // extern "C"

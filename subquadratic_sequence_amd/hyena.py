@@ -53,7 +53,7 @@ SIGNATURES = {
     "hyena_filter_gen": (_i, [ctypes.POINTER(Layer), ctypes.POINTER(FilterParams), _vp, _vp, _sz, _vp]),
     "hyena_fwd": (_i, [ctypes.POINTER(Layer), _vp, _vp, _vp, _vp, _vp, _i, _i, _vp, _vp, _sz, _vp]),
     "hyena_fwd_profiled": (_i, [ctypes.POINTER(Layer), _vp, _vp, _vp, _vp, _vp, _i, _i, _vp, _vp, _sz, _vp,
-                                ctypes.POINTER(ctypes.c_float)]),
+                                ctypes.POINTER(_vp)]),
     "hyena_nd_cache_bytes": (_sz, [_i, _i, _i, _i, _i]),
     "hyena_nd_filter_workspace_bytes": (_sz, [_i, _i, _i, _i, _i]),
     "hyena_nd_workspace_bytes": (_sz, [_i, _i, _i, _i, _i, _i]),
@@ -169,14 +169,20 @@ def hyena_fwd(layer: HyenaLayer, u, w_in, short_w, dskip, w_out, y=None, ws=None
     return y
 
 
-def hyena_fwd_profiled(layer: HyenaLayer, u, w_in, short_w, dskip, w_out, y, ws):
-    """hyena_fwd with per-stage HIP event times; returns [in-proj, conv, out-proj] in ms."""
+def hyena_fwd_profiled(layer: HyenaLayer, u, w_in, short_w, dskip, w_out, y, ws, events):
+    """hyena_fwd that also records four torch.cuda.Event (enable_timing=True) at the
+    stage boundaries on the current stream: before the in-projection, after it,
+    after the long convolutions, after the out-projection. Does not synchronise."""
     B = u.shape[0]
-    ms = (ctypes.c_float * 3)()
+    if len(events) != 4:
+        raise ValueError("hyena_fwd_profiled takes 4 events")
+    for ev in events:
+        if not ev.cuda_event:  # torch creates the HIP event on its first record
+            ev.record()
+    handles = (_vp * 4)(*[ev.cuda_event for ev in events])
     st = lib().hyena_fwd_profiled(ctypes.byref(layer.c), _ptr(u), _ptr(w_in), _ptr(short_w), _ptr(dskip),
-                                  _ptr(w_out), B, _dtype_code(u), _ptr(y), _ptr(ws), ws.numel(), _stream(), ms)
+                                  _ptr(w_out), B, _dtype_code(u), _ptr(y), _ptr(ws), ws.numel(), _stream(), handles)
     _check(st, "hyena_fwd_profiled")
-    return [ms[0], ms[1], ms[2]]
 
 
 # ------------------------------------------------------------------ 3D

@@ -1,0 +1,39 @@
+"""Host logic of bench.py: the algorithmic byte count and the reading of the
+committed HBM-traffic summary (no GPU needed)."""
+import os
+import subprocess
+import sys
+
+import bench
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def test_conv_alg_bytes_four_step():
+    # two orders, each reads z^n and x^n and writes z^{n+1} (bf16) and reads one fp32 complex spectrum
+    B, L, D, N = 1, 65536, 768, 2
+    assert bench.conv_alg_bytes(B, L, D, N, 2, False) == 2 * (3 * B * L * D * 2 + 8 * D * (L + 1))
+
+
+def test_conv_alg_bytes_lds_regime():
+    B, L, D, N = 8, 2048, 768, 2
+    want = (N + 1) * B * L * D * 2 + B * L * D * 2 + N * 8 * D * (L + 1)
+    assert bench.conv_alg_bytes(B, L, D, N, 2, True) == want
+
+
+def test_traffic_summary_with_current_sources(tmp_path):
+    p = tmp_path / "t.txt"
+    p.write_text(f"text\n@conv_stage_bytes_per_step: 1.5e9\n@conv_source_sha256: {bench.conv_source_hash()}\n")
+    assert bench.measured_traffic("w", str(p)) == 1.5e9
+
+
+def test_traffic_summary_is_void_after_a_kernel_change(tmp_path):
+    p = tmp_path / "t.txt"
+    p.write_text("@conv_stage_bytes_per_step: 1.5e9\n@conv_source_sha256: 0000\n")
+    assert bench.measured_traffic("w", str(p)) is None
+    assert bench.measured_traffic("no_such_workload") is None
+
+
+def test_more_than_one_gpu_is_refused():
+    r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--gpus", "2"], capture_output=True, text=True)
+    assert r.returncode == 2 and "one GPU" in r.stderr
