@@ -349,142 +349,333 @@ __global__ __launch_bounds__(64 * R) void colpass_kernel(ColArgs a, int nitems) 
 }
 
 // Row pass: N2-point DFTs of rows k1 and N1 - k1 (rows 0 and N1/2 for slot 0).
+//
+// Each row is spread over T = N2/E threads, E elements per thread: the thread
+// of role l owns elements l + q*T (q < E), in registers before the first radix
+// stage and after the last; the stages in between exchange through the padded
+// LDS row. Row a (k1) sits in the lower 32 lanes of a wave, row b in the upper
+// 32, and the upper lane of role T - 1 - i pairs with the lower lane of role i:
+// bin N2 - 1 - k2 of row b, the partner of bin k2 of row a in the two-for-one
+// product, then lives in the lane 32 apart (slot E - 1 - q), one lane swap away.
 template <int N2> struct RowCfg {
   static constexpr int E = 16;
-  static constexpr int TG = N2 / E;                      // threads per row
+  static constexpr int T = N2 / E;                       // threads per row
   static constexpr int SP = N2 >= 2048 ? 1 : 2048 / N2;  // row pairs per workgroup
-  static constexpr int WG = SP * 2 * TG;
+  static constexpr int WG = SP * 2 * T;
   static constexpr int RB = padded_len(N2);              // float2 per row buffer
-  static constexpr size_t LDS = (size_t)SP * 2 * RB * 8;
-  static constexpr int PER = N2 / TG;                    // row elements per thread
+  // two LDS buffers per row (one barrier per radix stage) while they fit two
+  // workgroups per CU, else one buffer used in place
+  static constexpr int NBUF = (size_t)SP * 4 * RB * 8 <= 80 * 1024 ? 2 : 1;
+  static_assert(T % 16 == 0 && WG % 64 == 0, "row layout");
 };
 
 enum { ROW_CONV = 0, ROW_SPEC = 1 };
 
-// Persistent row pass; items are (channel pair, group of SP slots). The next
-// item's rows are loaded into registers before the current item is processed.
-template <typename YT, int N1, int N2, int MODE, bool PF, bool EPQ>
+// value of x held by the lane 32 apart
+__device__ __forceinline__ float xhalf(float x, bool upper) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(upper ? r[0] : r[1]);
+}
+
+// Base twiddles of the row DFT, loaded once per thread: for stage SI (Ns > 1)
+// and butterfly b, w[SI][b][p] = W_N^(k * 2^p) with k = ((l + b*T) mod Ns) *
+// N / (Ns*R). Keeping them in registers keeps vector-memory loads out of the
+// stages, so prefetches of the next item stay in flight through them.
+template <int E> struct RowTw {
+  float2 w[4][E][4];
+};
+
+template <int N, int E, int Ns, int SI> struct RowTwLoad {
+  static constexpr int R = (E < N / Ns) ? E : N / Ns;
+  static constexpr int NB = E / R;
+  static constexpr int T = N / E;
+  static constexpr bool LAST = Ns * R == N;
+  static __device__ __forceinline__ void run(RowTw<E>& tw, int l, const float2* __restrict__ tab) {
+    if constexpr (Ns > 1) {
+#pragma unroll
+      for (int b = 0; b < NB; ++b) {
+        const int k = ((l + b * T) % Ns) * (N / (Ns * R));
+#pragma unroll
+        for (int p = 0; (1 << p) < R; ++p) tw.w[SI][b][p] = tab[k << p];
+      }
+    }
+    if constexpr (!LAST) RowTwLoad<N, E, Ns * R, SI + 1>::run(tw, l, tab);
+  }
+};
+
+// One radix stage of the row DFT. Stages write alternately to the two LDS
+// buffers of the row (bufs[0], bufs[1]); W is the buffer this stage writes, and
+// the next stage reads it. A buffer is written again only two writes later,
+// after a barrier that every reader of its previous contents has passed, so one
+// barrier per stage suffices. With a single buffer (bufs[0] == bufs[1], ONE)
+// the stage also waits for all reads before it writes.
+template <int N, int E, int Ns, int SI, int W, bool INV, bool ONE>
+__device__ __forceinline__ void row_stage(float2 (&v)[E], float2* const (&bufs)[2], int l, const RowTw<E>& tw) {
+  constexpr int R = (E < N / Ns) ? E : N / Ns;
+  constexpr int NB = E / R;
+  constexpr int T = N / E;
+  constexpr bool FIRST = Ns == 1, LAST = Ns * R == N;
+  const float2* src = bufs[W ^ 1];
+  float2* dst = bufs[W];
+  // butterfly b, leg r works on element l + b*T + r*(N/R) = l + T*(b + r*NB)
+  float2 x[NB][R];
+#pragma unroll
+  for (int b = 0; b < NB; ++b)
+#pragma unroll
+    for (int r = 0; r < R; ++r) x[b][r] = FIRST ? v[b + r * NB] : src[pad16(l + b * T + r * (N / R))];
+#pragma unroll
+  for (int b = 0; b < NB; ++b) {
+    if constexpr (Ns > 1) {
+      // W^(k r): powers of two from the base registers, the rest as one product
+      float2 w[R];
+#pragma unroll
+      for (int r = 1; r < R; ++r) {
+        if ((r & (r - 1)) == 0) {
+          w[r] = tw.w[SI][b][__builtin_ctz(r)];
+        } else {
+          const int hb = 1 << (31 - __builtin_clz(r));
+          w[r] = cmul(w[hb], w[r - hb]);
+        }
+      }
+#pragma unroll
+      for (int r = 1; r < R; ++r) x[b][r] = twmul<INV>(x[b][r], w[r]);
+    }
+    Dft<R, INV>::run(x[b]);
+  }
+  if (LAST) {
+    // outputs land on element l + b*T + r*Ns = l + T*(b + r*NB)
+#pragma unroll
+    for (int b = 0; b < NB; ++b)
+#pragma unroll
+      for (int r = 0; r < R; ++r) v[b + r * NB] = x[b][r];
+  } else {
+    if (ONE) __syncthreads();
+#pragma unroll
+    for (int b = 0; b < NB; ++b) {
+      const int j = l + b * T;
+      const int base = (j / Ns) * Ns * R + j % Ns;
+#pragma unroll
+      for (int r = 0; r < R; ++r) dst[pad16(base + r * Ns)] = x[b][r];
+    }
+    __syncthreads();
+  }
+}
+
+// Runs the stages from Ns (stage number SI) on; W is the buffer the next write goes to.
+template <int N, int E, int Ns, int SI, int W, bool INV, bool ONE> struct RowFrom {
+  static constexpr int R = (E < N / Ns) ? E : N / Ns;
+  static constexpr bool LAST = Ns * R == N;
+  using Next = RowFrom<N, E, Ns * R, SI + 1, LAST ? W : (W ^ 1), INV, ONE>;
+  static constexpr int WEND = Next::WEND;
+  static __device__ __forceinline__ void run(float2 (&v)[E], float2* const (&bufs)[2], int l, const RowTw<E>& tw) {
+    row_stage<N, E, Ns, SI, W, INV, ONE>(v, bufs, l, tw);
+    Next::run(v, bufs, l, tw);
+  }
+};
+template <int N, int E, int SI, int W, bool INV, bool ONE> struct RowFrom<N, E, N, SI, W, INV, ONE> {
+  static constexpr int WEND = W;
+  static __device__ __forceinline__ void run(float2 (&)[E], float2* const (&)[2], int, const RowTw<E>&) {}
+};
+
+// Persistent row pass; items are (channel pair, group of SP slots). With PF the
+// next item's rows are loaded into registers when the current item starts and
+// its spectrum entries as soon as the current item's have been used, so both
+// have most of an item's work to arrive.
+template <typename YT, int N1, int N2, int MODE, bool PF>
 __global__ __launch_bounds__(RowCfg<N2>::WG) void rowpass_kernel(YT* __restrict__ Y, float4* __restrict__ pq,
                                                                  const float2* __restrict__ tw_row, int pq_off,
                                                                  int pair_off, int pq_mod, int nitems) {
   using C = RowCfg<N2>;
+  constexpr int E = C::E, T = C::T;
   constexpr int HALF = N1 / 2;
   constexpr int PQROWS = HALF + 1;
   constexpr int NSG = HALF / C::SP;  // slot groups per channel pair
-  constexpr int PER = C::PER;
-  extern __shared__ float4 smem4[];
-  float2* rows = reinterpret_cast<float2*>(smem4);
-  const int r = threadIdx.x / C::TG, lt = threadIdx.x % C::TG;
-  const int isB = r & 1;
-  float2* row = rows + r * C::RB;
+  __shared__ float2 rowbuf[C::SP * 2 * C::NBUF * C::RB];
+  const int g = (threadIdx.x >> 6) * 32 + (threadIdx.x & 31);  // row-pair lane index in the workgroup
+  const bool up = (threadIdx.x >> 5) & 1;                       // row b
+  const int slot = g / T, i = g % T;
+  const int l = up ? T - 1 - i : i;
+  float2* buf = rowbuf + (slot * 2 + (up ? 1 : 0)) * C::RB;
+  float2* const bufs[2] = {buf, C::NBUF == 2 ? buf + C::SP * 2 * C::RB : buf};
+  constexpr bool ONE = C::NBUF == 1;
+  using Fwd = RowFrom<N2, E, 1, 0, 0, false, ONE>;
+  using Inv = RowFrom<N2, E, 1, 0, Fwd::WEND, true, ONE>;
+  static_assert(ONE || Inv::WEND == 0, "each item starts writing buffer 0");
+  RowTw<E> tw;
+  RowTwLoad<N2, E, 1, 0>::run(tw, l, tw_row);
   const float nrm = 0.25f / (float)(N1 * N2);  // (1/2)(1/2N) with 2 Ha, 2 Hb below
 
-  auto row_of = [&](int item, int& pl, int& s) {
+  // slot s of an item: row a is k1 = s, row b is N1 - s (N1/2 for s = 0)
+  auto row_of = [&](int item, int& pl, int& sg, int& s) {
     pl = item / NSG;
-    s = (item - pl * NSG) * C::SP + r / 2;   // slot 0 .. N1/2 - 1
-    return isB ? (s == 0 ? HALF : N1 - s) : s;
+    sg = item - pl * NSG;
+    s = sg * C::SP + slot;
+    return up ? (s == 0 ? HALF : N1 - s) : s;
   };
-  auto load = [&](int item, YT (&y)[PER]) {
-    int pl, s;
-    const int k1 = row_of(item, pl, s);
+  // Spectrum entries i + T*e, e < E, of a row pair: slot q of row a uses entry
+  // q, slot q of row b entry E - 1 - q. The lower lane fetches entries e < E/2,
+  // the upper lane entries E - 1 - e, both as pr[e]; slot q < E/2 then finds
+  // its entry in its own pr[q], slot E - 1 - q in the other half's pr[q].
+  auto spectrum = [&](int pl, int s) {
+    // filters are shared by every batch: pair (b, cp) uses the rows of cp
+    return pq + ((size_t)pq_off + (pl + pair_off) % pq_mod) * PQROWS * N2 + (size_t)s * N2;
+  };
+  struct In {
+    YT y[E];
+  };
+  auto load = [&](int item, In& in) {
+    int pl, sg, s;
+    const int k1 = row_of(item, pl, sg, s);
     const YT* Yr = Y + ((size_t)pl * N1 + k1) * N2;
 #pragma unroll
-    for (int q = 0; q < PER; ++q) y[q] = Yr[lt + q * C::TG];
+    for (int q = 0; q < E; ++q) in.y[q] = Yr[l + q * T];
+  };
+  float4 pr[E / 2];
+  auto load_spectrum = [&](int item) {
+    if (MODE == ROW_CONV) {
+      int pl, sg, s;
+      row_of(item, pl, sg, s);
+      // slot 0 reads its spectrum rows in the LDS branch; load a valid row anyway
+      // so that the number of loads in flight does not depend on the item
+      const float4* pqs = spectrum(pl, s == 0 ? 1 : s) + i;
+#pragma unroll
+      for (int e = 0; e < E / 2; ++e) pr[e] = pqs[(up ? E - 1 - e : e) * T];
+    }
   };
 
-  auto process = [&](int item, const YT (&y)[PER]) {
-    int pl, s;
-    const int k1 = row_of(item, pl, s);
-    // filters are shared by every batch: pair (b, cp) uses the rows of cp
-    float4* pqp = pq + ((size_t)pq_off + (pl + pair_off) % pq_mod) * PQROWS * N2;
-    // spectrum rows of this item, issued before the forward DFT
-    float4 pv[PER / 2];
-    auto load_pq = [&]() {
-      if (MODE == ROW_CONV && s != 0) {
-        const float4* pqs = pqp + (size_t)s * N2;
+  auto process = [&](int item, const In& in, int next, bool more) {
+    int pl, sg, s;
+    const int k1 = row_of(item, pl, sg, s);
+    float4* pqp = spectrum(pl, 0);
+    float2 v[E];
 #pragma unroll
-        for (int q = 0; q < PER / 2; ++q) pv[q] = pqs[isB * C::TG + lt + q * 2 * C::TG];
-      }
-    };
-    if (EPQ) load_pq();
-#pragma unroll
-    for (int q = 0; q < PER; ++q) row[pad16(lt + q * C::TG)] = cvt2(y[q]);
-    __syncthreads();
-    fft_lds<N2, C::E, false>(row, lt, tw_row);
-    if (!EPQ) load_pq();
+    for (int q = 0; q < E; ++q) v[q] = cvt2(in.y[q]);
+    Fwd::run(v, bufs, l, tw);
     if (s != 0) {
-      float2* ra = rows + (r & ~1) * C::RB;
-      float2* rb = ra + C::RB;
+      // own bin (slot q) and the partner's (the other half's slot E - 1 - q),
+      // taken for q and E - 1 - q together before either is overwritten; row b
+      // uses conj(P), conj(Q)
+      const float sg_ = up ? -1.f : 1.f;
 #pragma unroll
-      for (int q = 0; q < PER / 2; ++q) {
-        const int k2 = isB * C::TG + lt + q * 2 * C::TG;
-        const int m2 = N2 - 1 - k2;
-        float2 xk = ra[pad16(k2)], xm = rb[pad16(m2)];
+      for (int q = 0; q < E / 2; ++q) {
+        const int q2 = E - 1 - q;
+        const float2 pm = make_float2(xhalf(v[q2].x, up), xhalf(v[q2].y, up));
+        const float2 pm2 = make_float2(xhalf(v[q].x, up), xhalf(v[q].y, up));
         if (MODE == ROW_CONV) {
-          float2 P = make_float2(pv[q].x, pv[q].y), Q = make_float2(pv[q].z, pv[q].w);
-          ra[pad16(k2)] = cadd(cmul(xk, P), cmul(conjf2(xm), Q));
-          rb[pad16(m2)] = cadd(cmulc(xm, P), cmulc(conjf2(xk), Q));
-        } else {
-          float2 fm = conjf2(xm);
-          float2 ha2 = cadd(xk, fm), d = csub(xk, fm);
-          float2 hb2 = make_float2(d.y, -d.x);
-          pqp[(size_t)s * N2 + k2] = make_float4(nrm * (ha2.x + hb2.x), nrm * (ha2.y + hb2.y),
-                                                 nrm * (ha2.x - hb2.x), nrm * (ha2.y - hb2.y));
-        }
-      }
-    } else {
-      // row 0 pairs k2 with (N2 - k2) mod N2; row N1/2 pairs k2 with N2 - 1 - k2
-      const int pqrow = isB ? HALF : 0;
-      const float4* pqs = pqp + (size_t)pqrow * N2;
-      const int kend = (MODE == ROW_CONV) ? (isB ? N2 / 2 - 1 : N2 / 2) : N2 - 1;
-      for (int k2 = lt; k2 <= kend; k2 += C::TG) {
-        const int m2 = isB ? (N2 - 1 - k2) : ((N2 - k2) & (N2 - 1));
-        float2 xk = row[pad16(k2)], xm = row[pad16(m2)];
-        if (MODE == ROW_CONV) {
-          float4 q = pqs[k2];
-          float2 P = make_float2(q.x, q.y), Q = make_float2(q.z, q.w);
-          float2 yk = cadd(cmul(xk, P), cmul(conjf2(xm), Q));
-          if (m2 != k2) row[pad16(m2)] = cadd(cmulc(xm, P), cmulc(conjf2(xk), Q));
-          row[pad16(k2)] = yk;
-        } else {
-          float2 fm = conjf2(xm);
-          float2 ha2 = cadd(xk, fm), d = csub(xk, fm);
-          float2 hb2 = make_float2(d.y, -d.x);
-          pqp[(size_t)pqrow * N2 + k2] = make_float4(nrm * (ha2.x + hb2.x), nrm * (ha2.y + hb2.y),
-                                                     nrm * (ha2.x - hb2.x), nrm * (ha2.y - hb2.y));
+          const float4 o = make_float4(xhalf(pr[q].x, up), xhalf(pr[q].y, up), xhalf(pr[q].z, up), xhalf(pr[q].w, up));
+          const float2 P = make_float2(pr[q].x, sg_ * pr[q].y), Q = make_float2(pr[q].z, sg_ * pr[q].w);
+          const float2 P2 = make_float2(o.x, sg_ * o.y), Q2 = make_float2(o.z, sg_ * o.w);
+          v[q] = cadd(cmul(v[q], P), cmul(conjf2(pm), Q));
+          v[q2] = cadd(cmul(v[q2], P2), cmul(conjf2(pm2), Q2));
+        } else if (!up) {
+#pragma unroll
+          for (int h = 0; h < 2; ++h) {
+            const float2 xk = h ? v[q2] : v[q], fm = conjf2(h ? pm2 : pm);
+            const float2 ha2 = cadd(xk, fm), d = csub(xk, fm);
+            const float2 hb2 = make_float2(d.y, -d.x);
+            pqp[(size_t)s * N2 + i + (h ? q2 : q) * T] =
+                make_float4(nrm * (ha2.x + hb2.x), nrm * (ha2.y + hb2.y), nrm * (ha2.x - hb2.x),
+                            nrm * (ha2.y - hb2.y));
+          }
         }
       }
     }
-    if (MODE == ROW_SPEC) return;
-    __syncthreads();
-    fft_lds<N2, C::E, true>(row, lt, tw_row);
+    // this item's spectrum entries have been used: fetch the next item's
+    if (PF) load_spectrum(more ? next : item);
+    if (sg == 0) {
+      // Workgroup-uniform branch: slot 0 holds rows 0 and N1/2, each paired with
+      // itself (row 0: k2 with (N2 - k2) mod N2; row N1/2: k2 with N2 - 1 - k2),
+      // so their bins meet in LDS.
+      __syncthreads();
+      if (s == 0) {
+#pragma unroll
+        for (int q = 0; q < E; ++q) buf[pad16(l + q * T)] = v[q];
+      }
+      __syncthreads();
+      if (s == 0) {
+        const int pqrow = up ? HALF : 0;
+        const float4* pqs = pqp + (size_t)pqrow * N2;
+        const int kend = (MODE == ROW_CONV) ? (up ? N2 / 2 - 1 : N2 / 2) : N2 - 1;
+        // fixed trip count (k2 = i + it*T <= kend), so that the loads in it are
+        // straight-line code the compiler can count
+        constexpr int KIT = (MODE == ROW_CONV) ? E / 2 + 1 : E;
+#pragma unroll
+        for (int it = 0; it < KIT; ++it) {
+          const int k2 = i + it * T;
+          if (k2 > kend) continue;
+          const int m2 = up ? (N2 - 1 - k2) : ((N2 - k2) & (N2 - 1));
+          const float2 xk = buf[pad16(k2)], xm = buf[pad16(m2)];
+          if (MODE == ROW_CONV) {
+            const float4 q4 = pqs[k2];
+            const float2 P = make_float2(q4.x, q4.y), Q = make_float2(q4.z, q4.w);
+            const float2 yk = cadd(cmul(xk, P), cmul(conjf2(xm), Q));
+            if (m2 != k2) buf[pad16(m2)] = cadd(cmulc(xm, P), cmulc(conjf2(xk), Q));
+            buf[pad16(k2)] = yk;
+          } else {
+            const float2 fm = conjf2(xm);
+            const float2 ha2 = cadd(xk, fm), d = csub(xk, fm);
+            const float2 hb2 = make_float2(d.y, -d.x);
+            pqp[(size_t)pqrow * N2 + k2] = make_float4(nrm * (ha2.x + hb2.x), nrm * (ha2.y + hb2.y),
+                                                       nrm * (ha2.x - hb2.x), nrm * (ha2.y - hb2.y));
+          }
+        }
+      }
+      __syncthreads();
+      if (MODE == ROW_CONV) {
+        if (s == 0) {
+#pragma unroll
+          for (int q = 0; q < E; ++q) v[q] = buf[pad16(l + q * T)];
+        }
+        __syncthreads();  // the inverse DFT writes this buffer next
+      }
+    }
+    if (MODE == ROW_SPEC) {
+      __syncthreads();  // the next item's first stage writes the buffer read last
+      return;
+    }
+    Inv::run(v, bufs, l, tw);
     YT* Yr = Y + ((size_t)pl * N1 + k1) * N2;
 #pragma unroll
-    for (int q = 0; q < PER; ++q) stc(Yr + lt + q * C::TG, row[pad16(lt + q * C::TG)]);
+    for (int q = 0; q < E; ++q) stc(Yr + l + q * T, v[q]);
   };
 
   int item = blockIdx.x;
   if (item >= nitems) return;
-  YT cur[PER];
-  load(item, cur);
-  while (true) {
-    const int next = item + gridDim.x;
-    const bool more = next < nitems;
-    if (PF) {
-      YT nxt[PER];
-      if (more) load(next, nxt);
-      process(item, cur);
+  load_spectrum(item);
+  if (PF) {
+    // two input sets used in turn, so that no register copy waits on the loads
+    // (the last item loads itself again: the loads stay unconditional, which
+    // keeps the compiler's count of outstanding loads exact)
+    In in0, in1;
+    load(item, in0);
+    while (true) {
+      int next = item + gridDim.x;
+      bool more = next < nitems;
+      load(more ? next : item, in1);
+      process(item, in0, next, more);
       if (!more) break;
-#pragma unroll
-      for (int q = 0; q < PER; ++q) cur[q] = nxt[q];
-    } else {
-      process(item, cur);
+      item = next;
+      next = item + gridDim.x;
+      more = next < nitems;
+      load(more ? next : item, in0);
+      process(item, in1, next, more);
       if (!more) break;
-      load(next, cur);
+      item = next;
     }
-    item = next;
-    __syncthreads();  // rows of this item fully read before the next one writes them
+  } else {
+    In cur;
+    while (true) {
+      const int next = item + gridDim.x;
+      const bool more = next < nitems;
+      load(item, cur);
+      if (item != blockIdx.x) load_spectrum(item);
+      process(item, cur, next, more);
+      if (!more) break;
+      item = next;
+    }
   }
+  // Between items: buffer 0, which the next item writes first, was last read
+  // before a barrier of this item (with one buffer every write waits for one).
 }
 
 // ============================================================ launchers
@@ -616,24 +807,22 @@ static hipError_t launch_row_t(void* Y, float4* pq, const float2* tw_row, int pq
   using C = RowCfg<N2>;
   const int items = pairs * ((N1 / 2) / C::SP);
   YT* y = static_cast<YT*>(Y);
-  // variant: bit 0 = prefetch the next item's rows, bit 1 = spectrum loads before the forward DFT
-  static const int variant = [] {
-    const char* v = getenv("HYENA_ROW_VARIANT");
-    return v ? atoi(v) & 3 : 3;
+  // HYENA_ROW_PREFETCH=1 fetches the next item's data one item ahead; it needs
+  // more registers than leave two waves per SIMD, and is slower
+  static const bool pf = [] {
+    const char* v = getenv("HYENA_ROW_PREFETCH");
+    return v ? atoi(v) != 0 : false;
   }();
   using Fn = void (*)(YT*, float4*, const float2*, int, int, int, int);
   Fn fn;
-  if (mode != ROW_CONV) fn = rowpass_kernel<YT, N1, N2, ROW_SPEC, true, false>;
-  else if (variant == 0) fn = rowpass_kernel<YT, N1, N2, ROW_CONV, false, false>;
-  else if (variant == 1) fn = rowpass_kernel<YT, N1, N2, ROW_CONV, true, false>;
-  else if (variant == 2) fn = rowpass_kernel<YT, N1, N2, ROW_CONV, false, true>;
-  else fn = rowpass_kernel<YT, N1, N2, ROW_CONV, true, true>;
-  hipError_t e = allow_lds((const void*)fn, C::LDS);
-  if (e != hipSuccess) return e;
+  if (mode != ROW_CONV) fn = rowpass_kernel<YT, N1, N2, ROW_SPEC, true>;
+  else if (pf) fn = rowpass_kernel<YT, N1, N2, ROW_CONV, true>;
+  else fn = rowpass_kernel<YT, N1, N2, ROW_CONV, false>;
+  // LDS is static in the kernel
   static int grid[2] = {0, 0};
   int& g = grid[mode == ROW_CONV ? 0 : 1];
-  if (g == 0) g = resident_grid((const void*)fn, C::WG, C::LDS, 1 << 30);
-  hipLaunchKernelGGL(fn, dim3(g < items ? g : items), dim3(C::WG), C::LDS, s, y, pq, tw_row, pq_off, pair_off,
+  if (g == 0) g = resident_grid((const void*)fn, C::WG, 0, 1 << 30);
+  hipLaunchKernelGGL(fn, dim3(g < items ? g : items), dim3(C::WG), 0, s, y, pq, tw_row, pq_off, pair_off,
                      pq_mod, items);
   return hipGetLastError();
 }
