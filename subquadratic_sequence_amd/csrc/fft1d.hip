@@ -160,10 +160,6 @@ struct ColArgs {
 
 enum { COL_FWD_V = 0, COL_FWD_H = 1, COL_INV = 2, COL_INV_FWD = 3 };
 
-__device__ __forceinline__ float2 twN(const ColArgs& a, unsigned m) {
-  return cmul(a.tw_lo[m & ((1u << a.lo_bits) - 1)], a.tw_hi[m >> a.lo_bits]);
-}
-
 __device__ __forceinline__ float2 cvt2(float2 v) { return v; }
 __device__ __forceinline__ float2 cvt2(cbf16 v) {
   return make_float2(__uint_as_float(v.v << 16), __uint_as_float(v.v & 0xFFFF0000u));
@@ -171,18 +167,30 @@ __device__ __forceinline__ float2 cvt2(cbf16 v) {
 __device__ __forceinline__ float cvt1(float v) { return v; }
 __device__ __forceinline__ float cvt1(bf16 v) { return (float)v; }
 
+// Twiddles of one column-pass item (column n2, wave w): W_N^(n2 w) and W_N^(n2 R),
+// each the product of two table entries (W_N^m = tw_lo[m & lo_mask] * tw_hi[m >> lo_bits]).
+struct ColTw {
+  float2 lo0, hi0, lo1, hi1;
+};
+__device__ __forceinline__ void col_tw_load(const ColArgs& a, ColTw& t, unsigned m0, unsigned m1) {
+  const unsigned mask = (1u << a.lo_bits) - 1;
+  t.lo0 = a.tw_lo[m0 & mask];
+  t.hi0 = a.tw_hi[m0 >> a.lo_bits];
+  t.lo1 = a.tw_lo[m1 & mask];
+  t.hi1 = a.tw_hi[m1 >> a.lo_bits];
+}
+
 // Column DFT of N1 = R*R points, n1 = j + R r, k1 = ka + R kb.
 // Forward: thread (lane c, wave j) holds x[j + R r] in v[r] (zero for r >= R/2);
-// writes Y[k1][n2] * W_N^{n2 k1}.
+// writes Y[k1][n2] * W_N^{n2 k1}. wr[ka] = W_N1^(w ka), the inner twiddles of
+// this wave.
 template <int R, typename YT>
 __device__ __forceinline__ void col_forward(const ColArgs& a, float2 (&v)[R], float2* S, YT* Yp, int c, int w,
-                                            int n2) {
-  constexpr int N1 = R * R;
-  const unsigned N = 2u * (unsigned)a.L;
+                                            int n2, const float2 (&wr)[R], const ColTw& t) {
   Dft<R, false>::run(v);
 #pragma unroll
   for (int ka = 0; ka < R; ++ka) {
-    if (ka) v[ka] = cmul(v[ka], a.w256[(w * ka * (256 / N1)) & 255]);
+    if (ka) v[ka] = cmul(v[ka], wr[ka]);
     S[(w * R + ka) * kCW + c] = v[ka];
   }
   __syncthreads();
@@ -191,8 +199,8 @@ __device__ __forceinline__ void col_forward(const ColArgs& a, float2 (&v)[R], fl
   for (int j = 0; j < R; ++j) u[j] = S[(j * R + w) * kCW + c];
   Dft<R, false>::run(u);
   // k1 = w + R kb
-  float2 wk = twN(a, ((unsigned)n2 * (unsigned)w) & (N - 1));
-  const float2 ws = twN(a, ((unsigned)n2 * (unsigned)R) & (N - 1));
+  float2 wk = cmul(t.lo0, t.hi0);
+  const float2 ws = cmul(t.lo1, t.hi1);
 #pragma unroll
   for (int kb = 0; kb < R; ++kb) {
     stc(Yp + (size_t)(w + R * kb) * a.N2 + n2, cmul(u[kb], wk));
@@ -203,13 +211,11 @@ __device__ __forceinline__ void col_forward(const ColArgs& a, float2 (&v)[R], fl
 // Inverse column DFT of the loaded column y[kb] = Y[w + R kb][n2]; returns
 // out[n1 = w + R nb] in u[nb] (only nb < R/2 are needed).
 template <int R, typename YT>
-__device__ __forceinline__ void col_inverse(const ColArgs& a, float2 (&u)[R], float2* S, const YT (&y)[R], int c,
-                                            int w, int n2) {
-  constexpr int N1 = R * R;
-  const unsigned N = 2u * (unsigned)a.L;
+__device__ __forceinline__ void col_inverse(float2 (&u)[R], float2* S, const YT (&y)[R], int c, int w,
+                                            const float2 (&wr)[R], const ColTw& t) {
   float2 v[R];
-  float2 wk = twN(a, ((unsigned)n2 * (unsigned)w) & (N - 1));
-  const float2 ws = twN(a, ((unsigned)n2 * (unsigned)R) & (N - 1));
+  float2 wk = cmul(t.lo0, t.hi0);
+  const float2 ws = cmul(t.lo1, t.hi1);
 #pragma unroll
   for (int kb = 0; kb < R; ++kb) {
     v[kb] = cmulc(cvt2(y[kb]), wk);
@@ -218,7 +224,7 @@ __device__ __forceinline__ void col_inverse(const ColArgs& a, float2 (&u)[R], fl
   Dft<R, true>::run(v);
 #pragma unroll
   for (int na = 0; na < R; ++na) {
-    if (na) v[na] = cmulc(v[na], a.w256[(w * na * (256 / N1)) & 255]);
+    if (na) v[na] = cmulc(v[na], wr[na]);
     S[(w * R + na) * kCW + c] = v[na];
   }
   __syncthreads();
@@ -228,8 +234,11 @@ __device__ __forceinline__ void col_inverse(const ColArgs& a, float2 (&u)[R], fl
 }
 
 // Persistent column pass: each workgroup walks items (channel pair, block of 64
-// columns) with a stride of gridDim.x and loads the next item's column data
-// into registers before working on the current one.
+// columns) with a stride of gridDim.x. Everything an item reads from memory
+// (its column of the intermediate or of the input, the gate and skip inputs,
+// its twiddles) is loaded into registers while the previous item is worked on,
+// and no other vector-memory load happens in between, so the in-order load
+// counter never makes the work wait for the prefetch.
 template <typename T, typename YT, int R, int MODE>
 __global__ __launch_bounds__(64 * R) void colpass_kernel(ColArgs a, int nitems) {
   constexpr int N1 = R * R, H = R / 2;
@@ -240,16 +249,25 @@ __global__ __launch_bounds__(64 * R) void colpass_kernel(ColArgs a, int nitems) 
   const int L = a.L, N2 = a.N2, D = a.D;
   const int half = D / 2, ncb = N2 / kCW;
   const size_t J = (size_t)(a.NO + 1) * D;
+  const unsigned N = 2u * (unsigned)L;
+  // inner twiddles W_N1^(w k) of this wave, fixed for the whole launch
+  float2 wr[R];
+#pragma unroll
+  for (int k = 0; k < R; ++k) wr[k] = a.w256[(w * k * (256 / N1)) & 255];
 
   struct In {
-    YT y[R];        // inverse: column of the intermediate
-    T za[H], zb[H];  // forward of z^1: v block
-    float ha[H], hb[H];  // filter mode
+    YT y[INVERSE ? R : 1];                    // inverse: column of the intermediate
+    T xa[INVERSE ? H : 1], xb[INVERSE ? H : 1];  // inverse: gates x^n
+    T za[H], zb[H];                           // z^n (forward of z^1: the v block)
+    float ha[MODE == COL_FWD_H ? H : 1], hb[MODE == COL_FWD_H ? H : 1];  // filter mode
+    float da, db;                             // inverse: skip weights D^n of the pair
+    ColTw tw;
   };
   auto load = [&](int item, In& in) {
     const int pl = item / ncb;
     const int n2 = (item - pl * ncb) * kCW + c;
     const int pr = pl + a.pair_off;
+    col_tw_load(a, in.tw, ((unsigned)n2 * (unsigned)w) & (N - 1), ((unsigned)n2 * (unsigned)R) & (N - 1));
     if constexpr (MODE == COL_FWD_H) {
       const int n = pr / half, cp = pr % half;
       const float* ha = a.h + ((size_t)n * D + 2 * cp) * L;
@@ -272,6 +290,22 @@ __global__ __launch_bounds__(64 * R) void colpass_kernel(ColArgs a, int nitems) 
       const YT* Yp = reinterpret_cast<const YT*>(a.Y) + (size_t)pl * N1 * N2;
 #pragma unroll
       for (int kb = 0; kb < R; ++kb) in.y[kb] = Yp[(size_t)(w + R * kb) * N2 + n2];
+      const int b = pr / half, cp = pr % half;
+      const int n = a.n;
+      const T* sb = reinterpret_cast<const T*>(a.s) + (size_t)b * J * L;
+      const T* sx = sb + (size_t)((n + 1) * D + 2 * cp) * L;
+      const T* zp = (n == 0) ? sb + (size_t)(2 * cp) * L
+                             : reinterpret_cast<const T*>(a.zin) + ((size_t)b * D + 2 * cp) * L;
+#pragma unroll
+      for (int nb = 0; nb < H; ++nb) {
+        const int t = N2 * (w + R * nb) + n2;
+        in.xa[nb] = sx[t];
+        in.xb[nb] = sx[L + t];
+        in.za[nb] = zp[t];
+        in.zb[nb] = zp[L + t];
+      }
+      in.da = a.dskip[n * D + 2 * cp];
+      in.db = a.dskip[n * D + 2 * cp + 1];
     }
   };
 
@@ -284,39 +318,24 @@ __global__ __launch_bounds__(64 * R) void colpass_kernel(ColArgs a, int nitems) 
     if constexpr (MODE == COL_FWD_H) {
 #pragma unroll
       for (int r = 0; r < R; ++r) v[r] = r < H ? make_float2(in.ha[r], in.hb[r]) : make_float2(0.f, 0.f);
-      col_forward<R>(a, v, S, Yp, c, w, n2);
+      col_forward<R>(a, v, S, Yp, c, w, n2, wr, in.tw);
     } else if constexpr (MODE == COL_FWD_V) {
 #pragma unroll
       for (int r = 0; r < R; ++r) v[r] = r < H ? make_float2(cvt1(in.za[r]), cvt1(in.zb[r])) : make_float2(0.f, 0.f);
-      col_forward<R>(a, v, S, Yp, c, w, n2);
+      col_forward<R>(a, v, S, Yp, c, w, n2, wr, in.tw);
     } else {
       const int b = pr / half, cp = pr % half;
-      const int ca = 2 * cp, cb = ca + 1;
-      const int n = a.n;
-      const T* sb = reinterpret_cast<const T*>(a.s) + (size_t)b * J * L;
-      const T* sx = sb + (size_t)((n + 1) * D + ca) * L;
-      const T* zp = (n == 0) ? sb + (size_t)ca * L : reinterpret_cast<const T*>(a.zin) + ((size_t)b * D + ca) * L;
-      // gate inputs of this item: issued before the inverse DFT so that their
-      // latency overlaps it
-      T xa[H], xb[H], za[H], zb[H];
-#pragma unroll
-      for (int nb = 0; nb < H; ++nb) {
-        const int t = N2 * (w + R * nb) + n2;
-        xa[nb] = sx[t];
-        xb[nb] = sx[L + t];
-        za[nb] = zp[t];
-        zb[nb] = zp[L + t];
-      }
+      const int ca = 2 * cp;
       float2 u[R];
-      col_inverse<R>(a, u, S, in.y, c, w, n2);
-      const float da = a.dskip[n * D + ca], db = a.dskip[n * D + cb];
+      col_inverse<R>(u, S, in.y, c, w, wr, in.tw);
+      const float da = in.da, db = in.db;
       T* zo = reinterpret_cast<T*>(a.zout) + ((size_t)b * D + ca) * L;
 #pragma unroll
       for (int nb = 0; nb < R; ++nb) {
         if (nb < H) {
           const int t = N2 * (w + R * nb) + n2;
-          const float na = cvt1(xa[nb]) * u[nb].x + da * cvt1(za[nb]);
-          const float nbv = cvt1(xb[nb]) * u[nb].y + db * cvt1(zb[nb]);
+          const float na = cvt1(in.xa[nb]) * u[nb].x + da * cvt1(in.za[nb]);
+          const float nbv = cvt1(in.xb[nb]) * u[nb].y + db * cvt1(in.zb[nb]);
           stf(zo + t, na);
           stf(zo + L + t, nbv);
           v[nb] = make_float2(na, nbv);
@@ -326,25 +345,32 @@ __global__ __launch_bounds__(64 * R) void colpass_kernel(ColArgs a, int nitems) 
       }
       if constexpr (MODE == COL_INV_FWD) {
         __syncthreads();  // S is reused
-        col_forward<R>(a, v, S, Yp, c, w, n2);
+        col_forward<R>(a, v, S, Yp, c, w, n2, wr, in.tw);
       }
     }
   };
 
+  // Two input sets used in turn (no register copy that would wait on the
+  // loads); the last item loads itself again so the loads stay unconditional.
   int item = blockIdx.x;
   if (item >= nitems) return;
-  In cur;
-  load(item, cur);
+  In in0, in1;
+  load(item, in0);
   while (true) {
-    const int next = item + gridDim.x;
-    const bool more = next < nitems;
-    In nxt;
-    if (more) load(next, nxt);
-    process(item, cur);
+    int next = item + gridDim.x;
+    bool more = next < nitems;
+    load(more ? next : item, in1);
+    process(item, in0);
     if (!more) break;
-    cur = nxt;
     item = next;
     __syncthreads();  // S of this item fully read before the next one writes it
+    next = item + gridDim.x;
+    more = next < nitems;
+    load(more ? next : item, in0);
+    process(item, in1);
+    if (!more) break;
+    item = next;
+    __syncthreads();
   }
 }
 
