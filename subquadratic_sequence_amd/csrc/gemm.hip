@@ -29,6 +29,8 @@ namespace hy {
 typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8;
 typedef __attribute__((ext_vector_type(16))) float f32x16;
 
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+
 constexpr int GBM = 256, GBN = 256;
 constexpr int kScRows = GBM - 8;  // rows written per M-tile with the short-conv epilogue
 
@@ -44,7 +46,8 @@ constexpr int kCsLd = GBM + 4;  // staging row (floats), channel-major output: [
 constexpr int kRmLd = 64 + 4;   // staging row (floats), row-major output: [256 m][64 n]
 constexpr size_t kTileBytes = 2 * 2 * GBM * 80;  // two buffers of A and B, 80-byte rows
 constexpr size_t kStageBytes = 64 * kCsLd * 4 > 256 * kRmLd * 4 ? 64 * kCsLd * 4 : 256 * kRmLd * 4;
-constexpr size_t kGemmLds = kTileBytes > kStageBytes ? kTileBytes : kStageBytes;
+constexpr size_t kGemmMain = kTileBytes > kStageBytes ? kTileBytes : kStageBytes;
+constexpr size_t kGemmLds = kGemmMain + GBN * 3 * 4;  // + short-conv taps of the tile's columns
 
 constexpr int kXcds = 8;
 
@@ -75,6 +78,12 @@ __global__ __launch_bounds__(512, 1) void gemm_kernel(const T* __restrict__ A, c
   const int n0 = tn * GBN;
   const int m0 = SC ? tm * kScRows - 8 : tm * GBM;  // first A row of the tile
 
+  // short-conv taps of this tile's columns, staged once (read by the epilogue)
+  float* sw = reinterpret_cast<float*>(smem + kGemmMain);
+  if (SC) {
+    for (int x = tid; x < GBN * 3; x += 512) sw[x] = (n0 * 3 + x < N * 3) ? short_w[n0 * 3 + x] : 0.f;
+  }
+
   f32x16 acc[4][2];
 #pragma unroll
   for (int i = 0; i < 4; ++i)
@@ -83,12 +92,11 @@ __global__ __launch_bounds__(512, 1) void gemm_kernel(const T* __restrict__ A, c
 #pragma unroll
       for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.f;
 
-  uint4 ra2[2][NCH], rb2[2][NCH];  // two K tiles in flight
+  u32x4 ra2[2][NCH], rb2[2][NCH];  // two K tiles in flight
   // Per-thread global pointers, predicates and LDS offsets of the tile loads,
   // computed once; each K step only advances the pointers.
   const T* pa[NCH];
   const T* pb[NCH];
-  bool va[NCH], vb[NCH];
   int la[NCH], lb[NCH];
   size_t a_step;  // elements between consecutive K tiles
 #pragma unroll
@@ -97,8 +105,11 @@ __global__ __launch_bounds__(512, 1) void gemm_kernel(const T* __restrict__ A, c
     const int row = c >> 2, kc = (c & 3) * VEC;
     if (!A_CM) {
       const int m = m0 + row;
-      va[i] = m >= 0 && m < M;
-      pa[i] = A + (size_t)(va[i] ? m : 0) * K + kc;
+      // rows outside [0, M) load row 0: they only feed output rows that are not
+      // stored (with the short convolution, rows before a sequence start are
+      // masked by position), and unconditional loads keep the compiler's count
+      // of loads in flight exact
+      pa[i] = A + (size_t)(m >= 0 && m < M ? m : 0) * K + kc;
       la[i] = row * LDK + kc;
     } else {
       // chunks of VEC consecutive m for one k; ra[2j] and ra[2j + 1] hold
@@ -109,60 +120,64 @@ __global__ __launch_bounds__(512, 1) void gemm_kernel(const T* __restrict__ A, c
       const int slot = tid + (i >> 1) * 512, hi = i & 1;
       const int k = 2 * (slot % KP) + hi, mc = (slot / KP) * VEC;
       const int m = m0 + mc;
-      va[i] = m >= 0 && m < M;
-      const int mm = va[i] ? m : 0;
+      const int mm = m >= 0 && m < M ? m : 0;
       const int b = mm / Lseq, t = mm - b * Lseq;
       pa[i] = A + ((size_t)b * K + k) * Lseq + t;
       la[i] = mc * LDK + (k & ~1);
     }
     const int n = n0 + row;
-    vb[i] = n < N;
-    pb[i] = Bt + (size_t)(vb[i] ? n : 0) * K + kc;
+    pb[i] = Bt + (size_t)(n < N ? n : 0) * K + kc;  // columns >= N are not stored
     lb[i] = row * LDK + kc;
   }
   a_step = A_CM ? (size_t)BK * Lseq : (size_t)BK;
 
   // The register set is always a compile-time constant so that ra2/rb2 stay in VGPRs.
+  // Loads and LDS stores are unconditional (past the last K tile the pointers
+  // stay on it and the extra copies go unused): with no branch around them the
+  // compiler waits for exactly the tile it stores, never for the one in flight.
+  int tiles_left = K / BK;  // tiles from the current pointer position on
   auto load_tile = [&](auto set) {
-    uint4* ra = ra2[decltype(set)::value];
-    uint4* rb = rb2[decltype(set)::value];
+    u32x4* ra = ra2[decltype(set)::value];
+    u32x4* rb = rb2[decltype(set)::value];
 #pragma unroll
     for (int i = 0; i < NCH; ++i) {
-      ra[i] = va[i] ? *reinterpret_cast<const uint4*>(pa[i]) : make_uint4(0, 0, 0, 0);
-      rb[i] = vb[i] ? *reinterpret_cast<const uint4*>(pb[i]) : make_uint4(0, 0, 0, 0);
-      pa[i] += a_step;
-      pb[i] += BK;
+      ra[i] = *reinterpret_cast<const u32x4*>(pa[i]);
+      rb[i] = *reinterpret_cast<const u32x4*>(pb[i]);
+      pa[i] += tiles_left > 1 ? a_step : 0;
+      pb[i] += tiles_left > 1 ? BK : 0;
     }
+    --tiles_left;
   };
   auto store_tile = [&](auto set) {
     constexpr int buf = decltype(set)::value;
-    const uint4* ra = ra2[buf];
-    const uint4* rb = rb2[buf];
+    const u32x4* ra = ra2[buf];
+    const u32x4* rb = rb2[buf];
     T* As = As0 + buf * Cfg::TILE;
     T* Bs = Bs0 + buf * Cfg::TILE;
 #pragma unroll
     for (int i = 0; i < NCH; ++i) {
       if (!A_CM) {
-        *reinterpret_cast<uint4*>(As + la[i]) = ra[i];
+        *reinterpret_cast<u32x4*>(As + la[i]) = ra[i];
       } else if (i % 2 == 0) {
         // ra[i] holds k = 2p, ra[i + 1] holds k = 2p + 1 for the same m chunk:
         // interleave them into 32-bit (bf16) or 64-bit (fp32) LDS writes
+        // (register values only: no pointer into the register arrays, which
+        // would send them to scratch)
         if constexpr (sizeof(T) == 2) {
-          const unsigned short* lo = reinterpret_cast<const unsigned short*>(&ra[i]);
-          const unsigned short* hi = reinterpret_cast<const unsigned short*>(&ra[i + 1]);
 #pragma unroll
-          for (int q = 0; q < VEC; ++q)
-            *reinterpret_cast<unsigned int*>(As + la[i] + q * LDK) =
-                (unsigned int)lo[q] | ((unsigned int)hi[q] << 16);
+          for (int q = 0; q < VEC; ++q) {
+            const unsigned lo = (ra[i][q >> 1] >> (16 * (q & 1))) & 0xFFFFu;
+            const unsigned hi = (ra[i + 1][q >> 1] >> (16 * (q & 1))) & 0xFFFFu;
+            *reinterpret_cast<unsigned int*>(As + la[i] + q * LDK) = lo | (hi << 16);
+          }
         } else {
-          const float* lo = reinterpret_cast<const float*>(&ra[i]);
-          const float* hi = reinterpret_cast<const float*>(&ra[i + 1]);
 #pragma unroll
           for (int q = 0; q < VEC; ++q)
-            *reinterpret_cast<float2*>(As + la[i] + q * LDK) = make_float2(lo[q], hi[q]);
+            *reinterpret_cast<float2*>(As + la[i] + q * LDK) =
+                make_float2(__uint_as_float(ra[i][q]), __uint_as_float(ra[i + 1][q]));
         }
       }
-      *reinterpret_cast<uint4*>(Bs + lb[i]) = rb[i];
+      *reinterpret_cast<u32x4*>(Bs + lb[i]) = rb[i];
     }
   };
 
@@ -173,13 +188,16 @@ __global__ __launch_bounds__(512, 1) void gemm_kernel(const T* __restrict__ A, c
   const int ktiles = K / BK;
   load_tile(Set0{});
   store_tile(Set0{});
-  if (ktiles > 1) load_tile(Set1{});
+  load_tile(Set1{});
   __syncthreads();
   const int ar = wm * 128 + (lane & 31), br = wn * 64 + (lane & 31);
   auto step = [&](int kt, auto cur_c) {
     constexpr int cur = decltype(cur_c)::value;
     using Other = std::integral_constant<int, cur ^ 1>;
-    if (kt + 2 < ktiles) load_tile(cur_c);  // this set went to LDS one step ago
+    load_tile(cur_c);  // tile kt + 2; this set went to LDS one step ago
+    // keep the loads at the top of the step (the scheduler would otherwise sink
+    // them toward their use and shorten the prefetch distance)
+    __builtin_amdgcn_sched_barrier(0);
     const T* As = As0 + cur * Cfg::TILE;
     const T* Bs = Bs0 + cur * Cfg::TILE;
     if constexpr (sizeof(T) == 2) {
@@ -213,12 +231,14 @@ __global__ __launch_bounds__(512, 1) void gemm_kernel(const T* __restrict__ A, c
             acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x2f32(af[i], bfr[j], acc[i][j], 0, 0, 0);
       }
     }
-    if (kt + 1 < ktiles) store_tile(Other{});
+    store_tile(Other{});  // tile kt + 1 (after the last step: unused)
     __syncthreads();
   };
+  // K is a multiple of 2 BK (checked by the launcher): both steps of an
+  // iteration always run, so no load is moved into a conditional block
   for (int kt = 0; kt < ktiles; kt += 2) {
     step(kt, Set0{});
-    if (kt + 1 < ktiles) step(kt + 1, Set1{});
+    step(kt + 1, Set1{});
   }
 
   // Epilogue. Accumulator element e of lane l in block (i, j):
@@ -266,7 +286,8 @@ __global__ __launch_bounds__(512, 1) void gemm_kernel(const T* __restrict__ A, c
           const float4 s1 = *reinterpret_cast<const float4*>(src + 4);
           float o[8] = {s0.x, s0.y, s0.z, s0.w, s1.x, s1.y, s1.z, s1.w};
           if (SC) {
-            const float w0 = short_w[3 * n], w1 = short_w[3 * n + 1], w2 = short_w[3 * n + 2];
+            const float* wn3 = sw + 3 * (n - n0);
+            const float w0 = wn3[0], w1 = wn3[1], w2 = wn3[2];
             const float pm1 = (t >= 1) ? src[-1] : 0.f, pm2 = (t >= 2) ? src[-2] : 0.f;
             float prev1 = pm1, prev2 = pm2;
 #pragma unroll
@@ -316,6 +337,7 @@ __global__ __launch_bounds__(512, 1) void gemm_kernel(const T* __restrict__ A, c
 
 template <typename T>
 static hipError_t launch_gemm(const GemmArgs& g, hipStream_t s) {
+  if (g.K <= 0 || g.K % (2 * GemmCfg<T>::BK) != 0) return hipErrorInvalidValue;  // K steps come in pairs
   const bool sc = g.short_w != nullptr;
   const int mtiles = sc ? (g.M + kScRows - 1) / kScRows : (g.M + GBM - 1) / GBM;
   const int ntn = (g.N + GBN - 1) / GBN;
