@@ -186,7 +186,7 @@ __device__ __forceinline__ void col_tw_load(const ColArgs& a, ColTw& t, unsigned
 // this wave.
 template <int R, typename YT>
 __device__ __forceinline__ void col_forward(const ColArgs& a, float2 (&v)[R], float2* S, YT* Yp, int c, int w,
-                                            int n2, const float2 (&wr)[R], const ColTw& t) {
+                                            int n2, const float2 (&wr)[R], float2 wk, float2 ws) {
   Dft<R, false>::run(v);
 #pragma unroll
   for (int ka = 0; ka < R; ++ka) {
@@ -198,9 +198,7 @@ __device__ __forceinline__ void col_forward(const ColArgs& a, float2 (&v)[R], fl
 #pragma unroll
   for (int j = 0; j < R; ++j) u[j] = S[(j * R + w) * kCW + c];
   Dft<R, false>::run(u);
-  // k1 = w + R kb
-  float2 wk = cmul(t.lo0, t.hi0);
-  const float2 ws = cmul(t.lo1, t.hi1);
+  // k1 = w + R kb: W_N^(n2 k1) = wk ws^kb
 #pragma unroll
   for (int kb = 0; kb < R; ++kb) {
     stc(Yp + (size_t)(w + R * kb) * a.N2 + n2, cmul(u[kb], wk));
@@ -208,17 +206,16 @@ __device__ __forceinline__ void col_forward(const ColArgs& a, float2 (&v)[R], fl
   }
 }
 
-// Inverse column DFT of the loaded column y[kb] = Y[w + R kb][n2]; returns
-// out[n1 = w + R nb] in u[nb] (only nb < R/2 are needed).
-template <int R, typename YT>
-__device__ __forceinline__ void col_inverse(float2 (&u)[R], float2* S, const YT (&y)[R], int c, int w,
-                                            const float2 (&wr)[R], const ColTw& t) {
+// Inverse column DFT of the column v0[kb] = Y[w + R kb][n2] (twiddles W_N^(n2 k1)
+// = wk ws^kb removed first); returns out[n1 = w + R nb] in u[nb] (only nb < R/2
+// are needed).
+template <int R>
+__device__ __forceinline__ void col_inverse(float2 (&u)[R], float2* S, const float2 (&v0)[R], int c, int w,
+                                            const float2 (&wr)[R], float2 wk, float2 ws) {
   float2 v[R];
-  float2 wk = cmul(t.lo0, t.hi0);
-  const float2 ws = cmul(t.lo1, t.hi1);
 #pragma unroll
   for (int kb = 0; kb < R; ++kb) {
-    v[kb] = cmulc(cvt2(y[kb]), wk);
+    v[kb] = cmulc(v0[kb], wk);
     wk = cmul(wk, ws);
   }
   Dft<R, true>::run(v);
@@ -236,9 +233,11 @@ __device__ __forceinline__ void col_inverse(float2 (&u)[R], float2* S, const YT 
 // Persistent column pass: each workgroup walks items (channel pair, block of 64
 // columns) with a stride of gridDim.x. Everything an item reads from memory
 // (its column of the intermediate or of the input, the gate and skip inputs,
-// its twiddles) is loaded into registers while the previous item is worked on,
-// and no other vector-memory load happens in between, so the in-order load
-// counter never makes the work wait for the prefetch.
+// its twiddles) is in registers when the item starts: each part of the next
+// item's data is loaded into the same registers as soon as the current item
+// has used that part, so one set of registers carries a whole item of
+// prefetch, and no other vector-memory load comes between a prefetch and its
+// use (the in-order load counter never makes the work wait for later loads).
 template <typename T, typename YT, int R, int MODE>
 __global__ __launch_bounds__(64 * R) void colpass_kernel(ColArgs a, int nitems) {
   constexpr int N1 = R * R, H = R / 2;
@@ -263,34 +262,49 @@ __global__ __launch_bounds__(64 * R) void colpass_kernel(ColArgs a, int nitems) 
     float da, db;                             // inverse: skip weights D^n of the pair
     ColTw tw;
   };
-  auto load = [&](int item, In& in) {
-    const int pl = item / ncb;
-    const int n2 = (item - pl * ncb) * kCW + c;
-    const int pr = pl + a.pair_off;
-    col_tw_load(a, in.tw, ((unsigned)n2 * (unsigned)w) & (N - 1), ((unsigned)n2 * (unsigned)R) & (N - 1));
+  struct Item {
+    int pl, n2, pr;
+  };
+  auto item_of = [&](int item) {
+    Item it;
+    it.pl = item / ncb;
+    it.n2 = (item - it.pl * ncb) * kCW + c;
+    it.pr = it.pl + a.pair_off;
+    return it;
+  };
+  auto load_tw = [&](const Item& it, In& in) {
+    col_tw_load(a, in.tw, ((unsigned)it.n2 * (unsigned)w) & (N - 1), ((unsigned)it.n2 * (unsigned)R) & (N - 1));
+  };
+  // first part: what the item's first transform reads
+  auto load_head = [&](const Item& it, In& in) {
     if constexpr (MODE == COL_FWD_H) {
-      const int n = pr / half, cp = pr % half;
+      const int n = it.pr / half, cp = it.pr % half;
       const float* ha = a.h + ((size_t)n * D + 2 * cp) * L;
 #pragma unroll
       for (int r = 0; r < H; ++r) {
-        const int t = N2 * (w + R * r) + n2;
+        const int t = N2 * (w + R * r) + it.n2;
         in.ha[r] = ha[t];
         in.hb[r] = ha[L + t];
       }
     } else if constexpr (MODE == COL_FWD_V) {
-      const int b = pr / half, cp = pr % half;
+      const int b = it.pr / half, cp = it.pr % half;
       const T* sv = reinterpret_cast<const T*>(a.s) + (size_t)b * J * L + (size_t)(2 * cp) * L;
 #pragma unroll
       for (int r = 0; r < H; ++r) {
-        const int t = N2 * (w + R * r) + n2;
+        const int t = N2 * (w + R * r) + it.n2;
         in.za[r] = sv[t];
         in.zb[r] = sv[L + t];
       }
     } else {
-      const YT* Yp = reinterpret_cast<const YT*>(a.Y) + (size_t)pl * N1 * N2;
+      const YT* Yp = reinterpret_cast<const YT*>(a.Y) + (size_t)it.pl * N1 * N2;
 #pragma unroll
-      for (int kb = 0; kb < R; ++kb) in.y[kb] = Yp[(size_t)(w + R * kb) * N2 + n2];
-      const int b = pr / half, cp = pr % half;
+      for (int kb = 0; kb < R; ++kb) in.y[kb] = Yp[(size_t)(w + R * kb) * N2 + it.n2];
+    }
+  };
+  // second part (inverse modes): gate and skip inputs
+  auto load_gate = [&](const Item& it, In& in) {
+    if constexpr (INVERSE) {
+      const int b = it.pr / half, cp = it.pr % half;
       const int n = a.n;
       const T* sb = reinterpret_cast<const T*>(a.s) + (size_t)b * J * L;
       const T* sx = sb + (size_t)((n + 1) * D + 2 * cp) * L;
@@ -298,7 +312,7 @@ __global__ __launch_bounds__(64 * R) void colpass_kernel(ColArgs a, int nitems) 
                              : reinterpret_cast<const T*>(a.zin) + ((size_t)b * D + 2 * cp) * L;
 #pragma unroll
       for (int nb = 0; nb < H; ++nb) {
-        const int t = N2 * (w + R * nb) + n2;
+        const int t = N2 * (w + R * nb) + it.n2;
         in.xa[nb] = sx[t];
         in.xb[nb] = sx[L + t];
         in.za[nb] = zp[t];
@@ -309,68 +323,77 @@ __global__ __launch_bounds__(64 * R) void colpass_kernel(ColArgs a, int nitems) 
     }
   };
 
-  auto process = [&](int item, const In& in) {
-    const int pl = item / ncb;
-    const int n2 = (item - pl * ncb) * kCW + c;
-    const int pr = pl + a.pair_off;
-    YT* Yp = reinterpret_cast<YT*>(a.Y) + (size_t)pl * N1 * N2;
+  // Processes item `item` from `in`, refilling `in` with item `nxt` part by part.
+  auto process = [&](int item, In& in, int nxt) {
+    const Item it = item_of(item), nt = item_of(nxt);
+    YT* Yp = reinterpret_cast<YT*>(a.Y) + (size_t)it.pl * N1 * N2;
+    // twiddles of this item, then fetch the next item's
+    const float2 wk = cmul(in.tw.lo0, in.tw.hi0), ws = cmul(in.tw.lo1, in.tw.hi1);
+    load_tw(nt, in);
     float2 v[R];
-    if constexpr (MODE == COL_FWD_H) {
+    if constexpr (MODE == COL_FWD_H || MODE == COL_FWD_V) {
 #pragma unroll
-      for (int r = 0; r < R; ++r) v[r] = r < H ? make_float2(in.ha[r], in.hb[r]) : make_float2(0.f, 0.f);
-      col_forward<R>(a, v, S, Yp, c, w, n2, wr, in.tw);
-    } else if constexpr (MODE == COL_FWD_V) {
-#pragma unroll
-      for (int r = 0; r < R; ++r) v[r] = r < H ? make_float2(cvt1(in.za[r]), cvt1(in.zb[r])) : make_float2(0.f, 0.f);
-      col_forward<R>(a, v, S, Yp, c, w, n2, wr, in.tw);
+      for (int r = 0; r < R; ++r) {
+        if (r < H)
+          v[r] = MODE == COL_FWD_H ? make_float2(in.ha[r], in.hb[r])
+                                   : make_float2(cvt1(in.za[r]), cvt1(in.zb[r]));
+        else
+          v[r] = make_float2(0.f, 0.f);
+      }
+      load_head(nt, in);
+      col_forward<R>(a, v, S, Yp, c, w, it.n2, wr, wk, ws);
     } else {
-      const int b = pr / half, cp = pr % half;
+      const int b = it.pr / half, cp = it.pr % half;
       const int ca = 2 * cp;
+#pragma unroll
+      for (int r = 0; r < R; ++r) v[r] = cvt2(in.y[r]);
+      load_head(nt, in);
       float2 u[R];
-      col_inverse<R>(u, S, in.y, c, w, wr, in.tw);
-      const float da = in.da, db = in.db;
+      col_inverse<R>(u, S, v, c, w, wr, wk, ws);
       T* zo = reinterpret_cast<T*>(a.zout) + ((size_t)b * D + ca) * L;
+      float na[H], nbv[H];
+#pragma unroll
+      for (int nb = 0; nb < H; ++nb) {
+        na[nb] = cvt1(in.xa[nb]) * u[nb].x + in.da * cvt1(in.za[nb]);
+        nbv[nb] = cvt1(in.xb[nb]) * u[nb].y + in.db * cvt1(in.zb[nb]);
+      }
+      load_gate(nt, in);
 #pragma unroll
       for (int nb = 0; nb < R; ++nb) {
         if (nb < H) {
-          const int t = N2 * (w + R * nb) + n2;
-          const float na = cvt1(in.xa[nb]) * u[nb].x + da * cvt1(in.za[nb]);
-          const float nbv = cvt1(in.xb[nb]) * u[nb].y + db * cvt1(in.zb[nb]);
-          stf(zo + t, na);
-          stf(zo + L + t, nbv);
-          v[nb] = make_float2(na, nbv);
+          const int t = N2 * (w + R * nb) + it.n2;
+          stf(zo + t, na[nb]);
+          stf(zo + L + t, nbv[nb]);
+          v[nb] = make_float2(na[nb], nbv[nb]);
         } else {
           v[nb] = make_float2(0.f, 0.f);
         }
       }
       if constexpr (MODE == COL_INV_FWD) {
         __syncthreads();  // S is reused
-        col_forward<R>(a, v, S, Yp, c, w, n2, wr, in.tw);
+        col_forward<R>(a, v, S, Yp, c, w, it.n2, wr, wk, ws);
       }
     }
   };
 
-  // Two input sets used in turn (no register copy that would wait on the
-  // loads); the last item loads itself again so the loads stay unconditional.
+  // The last item fetches itself again: the loads stay unconditional, which
+  // keeps the compiler's count of loads in flight exact.
   int item = blockIdx.x;
   if (item >= nitems) return;
-  In in0, in1;
-  load(item, in0);
+  In in;
+  {
+    const Item it = item_of(item);
+    load_tw(it, in);
+    load_head(it, in);
+    load_gate(it, in);
+  }
   while (true) {
-    int next = item + gridDim.x;
-    bool more = next < nitems;
-    load(more ? next : item, in1);
-    process(item, in0);
+    const int next = item + gridDim.x;
+    const bool more = next < nitems;
+    process(item, in, more ? next : item);
     if (!more) break;
     item = next;
     __syncthreads();  // S of this item fully read before the next one writes it
-    next = item + gridDim.x;
-    more = next < nitems;
-    load(more ? next : item, in0);
-    process(item, in1);
-    if (!more) break;
-    item = next;
-    __syncthreads();
   }
 }
 
