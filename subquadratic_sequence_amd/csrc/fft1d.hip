@@ -526,11 +526,8 @@ template <int N, int E, int SI, int W, bool INV, bool ONE> struct RowFrom<N, E, 
   static __device__ __forceinline__ void run(float2 (&)[E], float2* const (&)[2], int, const RowTw<E>&) {}
 };
 
-// Persistent row pass; items are (channel pair, group of SP slots). With PF the
-// next item's rows are loaded into registers when the current item starts and
-// its spectrum entries as soon as the current item's have been used, so both
-// have most of an item's work to arrive.
-template <typename YT, int N1, int N2, int MODE, bool PF>
+// Persistent row pass; items are (channel pair, group of SP slots).
+template <typename YT, int N1, int N2, int MODE, int PF>
 __global__ __launch_bounds__(RowCfg<N2>::WG) void rowpass_kernel(YT* __restrict__ Y, float4* __restrict__ pq,
                                                                  const float2* __restrict__ tw_row, int pq_off,
                                                                  int pair_off, int pq_mod, int nitems) {
@@ -592,13 +589,15 @@ __global__ __launch_bounds__(RowCfg<N2>::WG) void rowpass_kernel(YT* __restrict_
     }
   };
 
-  auto process = [&](int item, const In& in, int next, bool more) {
+  auto process = [&](int item, In& in, int next, bool more) {
     int pl, sg, s;
     const int k1 = row_of(item, pl, sg, s);
     float4* pqp = spectrum(pl, 0);
     float2 v[E];
 #pragma unroll
     for (int q = 0; q < E; ++q) v[q] = cvt2(in.y[q]);
+    // the rows are in v: fetch the next item's into the same registers
+    if (PF & 1) load(more ? next : item, in);
     Fwd::run(v, bufs, l, tw);
     if (s != 0) {
       // own bin (slot q) and the partner's (the other half's slot E - 1 - q),
@@ -630,7 +629,7 @@ __global__ __launch_bounds__(RowCfg<N2>::WG) void rowpass_kernel(YT* __restrict_
       }
     }
     // this item's spectrum entries have been used: fetch the next item's
-    if (PF) load_spectrum(more ? next : item);
+    if (PF & 2) load_spectrum(more ? next : item);
     if (sg == 0) {
       // Workgroup-uniform branch: slot 0 holds rows 0 and N1/2, each paired with
       // itself (row 0: k2 with (N2 - k2) mod N2; row N1/2: k2 with N2 - 1 - k2),
@@ -688,40 +687,25 @@ __global__ __launch_bounds__(RowCfg<N2>::WG) void rowpass_kernel(YT* __restrict_
     for (int q = 0; q < E; ++q) stc(Yr + l + q * T, v[q]);
   };
 
+  // With PF each part of the next item's data is fetched into the registers of
+  // the current item's as soon as that part has been used (the rows after the
+  // first radix stage has taken them, the spectrum entries after the product),
+  // so one register set carries a whole item of prefetch. The last item fetches
+  // itself again: the loads stay unconditional, which keeps the compiler's
+  // count of loads in flight exact.
   int item = blockIdx.x;
   if (item >= nitems) return;
+  In in;
+  load(item, in);
   load_spectrum(item);
-  if (PF) {
-    // two input sets used in turn, so that no register copy waits on the loads
-    // (the last item loads itself again: the loads stay unconditional, which
-    // keeps the compiler's count of outstanding loads exact)
-    In in0, in1;
-    load(item, in0);
-    while (true) {
-      int next = item + gridDim.x;
-      bool more = next < nitems;
-      load(more ? next : item, in1);
-      process(item, in0, next, more);
-      if (!more) break;
-      item = next;
-      next = item + gridDim.x;
-      more = next < nitems;
-      load(more ? next : item, in0);
-      process(item, in1, next, more);
-      if (!more) break;
-      item = next;
-    }
-  } else {
-    In cur;
-    while (true) {
-      const int next = item + gridDim.x;
-      const bool more = next < nitems;
-      load(item, cur);
-      if (item != blockIdx.x) load_spectrum(item);
-      process(item, cur, next, more);
-      if (!more) break;
-      item = next;
-    }
+  while (true) {
+    const int next = item + gridDim.x;
+    const bool more = next < nitems;
+    process(item, in, next, more);
+    if (!more) break;
+    item = next;
+    if (!(PF & 1)) load(item, in);
+    if (!(PF & 2)) load_spectrum(item);
   }
   // Between items: buffer 0, which the next item writes first, was last read
   // before a barrier of this item (with one buffer every write waits for one).
@@ -856,17 +840,20 @@ static hipError_t launch_row_t(void* Y, float4* pq, const float2* tw_row, int pq
   using C = RowCfg<N2>;
   const int items = pairs * ((N1 / 2) / C::SP);
   YT* y = static_cast<YT*>(Y);
-  // HYENA_ROW_PREFETCH=1 fetches the next item's data one item ahead; it needs
-  // more registers than leave two waves per SIMD, and is slower
-  static const bool pf = [] {
+  // HYENA_ROW_PREFETCH: bit 0 fetches the next item's rows early, bit 1 its
+  // spectrum entries; otherwise they are loaded when the item starts. Rows
+  // early (1) measures best; fetching the spectrum early is slower.
+  static const int pf = [] {
     const char* v = getenv("HYENA_ROW_PREFETCH");
-    return v ? atoi(v) != 0 : false;
+    return v ? atoi(v) & 3 : 1;
   }();
   using Fn = void (*)(YT*, float4*, const float2*, int, int, int, int);
   Fn fn;
-  if (mode != ROW_CONV) fn = rowpass_kernel<YT, N1, N2, ROW_SPEC, true>;
-  else if (pf) fn = rowpass_kernel<YT, N1, N2, ROW_CONV, true>;
-  else fn = rowpass_kernel<YT, N1, N2, ROW_CONV, false>;
+  if (mode != ROW_CONV) fn = rowpass_kernel<YT, N1, N2, ROW_SPEC, 0>;
+  else if (pf == 1) fn = rowpass_kernel<YT, N1, N2, ROW_CONV, 1>;
+  else if (pf == 2) fn = rowpass_kernel<YT, N1, N2, ROW_CONV, 2>;
+  else if (pf == 3) fn = rowpass_kernel<YT, N1, N2, ROW_CONV, 3>;
+  else fn = rowpass_kernel<YT, N1, N2, ROW_CONV, 0>;
   // LDS is static in the kernel
   static int grid[2] = {0, 0};
   int& g = grid[mode == ROW_CONV ? 0 : 1];
