@@ -142,7 +142,10 @@ __global__ __launch_bounds__(LdsCfg<N>::WG) void filter_spec_lds_kernel(
 
 // ============================================================ four-step
 
-constexpr int kCW = 64;   // columns per column-pass workgroup (one per lane)
+// Columns per column-pass item: 64 (one per lane, one wave per j) for R = 8;
+// 32 for R = 16, two j per wave, so that the workgroup has 512 threads (256
+// VGPRs each) instead of 1024.
+template <int R> constexpr int col_width() { return R >= 16 ? 32 : 64; }
 
 struct ColArgs {
   const void* s;          // short-convolved projections [B][(NO+1)D][L] (storage type)
@@ -187,6 +190,7 @@ __device__ __forceinline__ void col_tw_load(const ColArgs& a, ColTw& t, unsigned
 template <int R, typename YT>
 __device__ __forceinline__ void col_forward(const ColArgs& a, float2 (&v)[R], float2* S, YT* Yp, int c, int w,
                                             int n2, const float2 (&wr)[R], float2 wk, float2 ws) {
+  constexpr int kCW = col_width<R>();
   Dft<R, false>::run(v);
 #pragma unroll
   for (int ka = 0; ka < R; ++ka) {
@@ -212,6 +216,7 @@ __device__ __forceinline__ void col_forward(const ColArgs& a, float2 (&v)[R], fl
 template <int R>
 __device__ __forceinline__ void col_inverse(float2 (&u)[R], float2* S, const float2 (&v0)[R], int c, int w,
                                             const float2 (&wr)[R], float2 wk, float2 ws) {
+  constexpr int kCW = col_width<R>();
   float2 v[R];
 #pragma unroll
   for (int kb = 0; kb < R; ++kb) {
@@ -239,12 +244,14 @@ __device__ __forceinline__ void col_inverse(float2 (&u)[R], float2* S, const flo
 // prefetch, and no other vector-memory load comes between a prefetch and its
 // use (the in-order load counter never makes the work wait for later loads).
 template <typename T, typename YT, int R, int MODE>
-__global__ __launch_bounds__(64 * R) void colpass_kernel(ColArgs a, int nitems) {
+__global__ __launch_bounds__(R * col_width<R>()) void colpass_kernel(ColArgs a, int nitems) {
   constexpr int N1 = R * R, H = R / 2;
   constexpr bool INVERSE = (MODE == COL_INV || MODE == COL_INV_FWD);
   extern __shared__ float4 smem4[];
   float2* S = reinterpret_cast<float2*>(smem4);
-  const int c = threadIdx.x & 63, w = threadIdx.x >> 6;
+  // thread (j, c): row j of the R x R column DFT (w below), column c of the item
+  constexpr int kCW = col_width<R>();
+  const int c = threadIdx.x % kCW, w = threadIdx.x / kCW;
   const int L = a.L, N2 = a.N2, D = a.D;
   const int half = D / 2, ncb = N2 / kCW;
   const size_t J = (size_t)(a.NO + 1) * D;
@@ -426,26 +433,54 @@ __device__ __forceinline__ float xhalf(float x, bool upper) {
   return __uint_as_float(upper ? r[0] : r[1]);
 }
 
-// Base twiddles of the row DFT, loaded once per thread: for stage SI (Ns > 1)
-// and butterfly b, w[SI][b][p] = W_N^(k * 2^p) with k = ((l + b*T) mod Ns) *
-// N / (Ns*R). Keeping them in registers keeps vector-memory loads out of the
-// stages, so prefetches of the next item stay in flight through them.
-template <int E> struct RowTw {
-  float2 w[4][E][4];
+// Radix of the row DFT stage that starts at span Ns: the first stage takes the
+// factor left over by 16s (2048 = 8 * 16 * 16), the later stages, which need
+// twiddles, are radix 16.
+constexpr int row_radix(int N, int E, int Ns) {
+  if (Ns == 1) {
+    int r = N;
+    while (r > 16) r /= 16;
+    return r < E ? r : E;
+  }
+  return (16 < N / Ns) ? 16 : N / Ns;
+}
+
+// number of radix stages of an N-point row DFT
+constexpr int row_stages(int N, int E) {
+  int n = 0;
+  for (int ns = 1; ns < N; ns *= row_radix(N, E, ns)) ++n;
+  return n;
+}
+// largest butterfly count per thread over the stages after the first
+constexpr int row_nbmax(int N, int E) {
+  int m = 1;
+  for (int ns = row_radix(N, E, 1); ns < N; ns *= row_radix(N, E, ns)) {
+    const int nb = E / row_radix(N, E, ns);
+    m = nb > m ? nb : m;
+  }
+  return m;
+}
+// Sized exactly, so that the compiler keeps it in registers (CACHE false: the
+// stages read the twiddle table tab instead).
+template <int N, int E> struct RowTw {
+  static constexpr bool CACHE = true;
+  float2 w[CACHE ? row_stages(N, E) - 1 : 1][CACHE ? row_nbmax(N, E) : 1][4];
+  const float2* tab;
 };
 
 template <int N, int E, int Ns, int SI> struct RowTwLoad {
-  static constexpr int R = (E < N / Ns) ? E : N / Ns;
+  static constexpr int R = row_radix(N, E, Ns);
   static constexpr int NB = E / R;
   static constexpr int T = N / E;
   static constexpr bool LAST = Ns * R == N;
-  static __device__ __forceinline__ void run(RowTw<E>& tw, int l, const float2* __restrict__ tab) {
-    if constexpr (Ns > 1) {
+  static __device__ __forceinline__ void run(RowTw<N, E>& tw, int l, const float2* __restrict__ tab) {
+    tw.tab = tab;
+    if constexpr (Ns > 1 && RowTw<N, E>::CACHE) {
 #pragma unroll
       for (int b = 0; b < NB; ++b) {
         const int k = ((l + b * T) % Ns) * (N / (Ns * R));
 #pragma unroll
-        for (int p = 0; (1 << p) < R; ++p) tw.w[SI][b][p] = tab[k << p];
+        for (int p = 0; (1 << p) < R; ++p) tw.w[SI - 1][b][p] = tab[k << p];
       }
     }
     if constexpr (!LAST) RowTwLoad<N, E, Ns * R, SI + 1>::run(tw, l, tab);
@@ -459,8 +494,8 @@ template <int N, int E, int Ns, int SI> struct RowTwLoad {
 // barrier per stage suffices. With a single buffer (bufs[0] == bufs[1], ONE)
 // the stage also waits for all reads before it writes.
 template <int N, int E, int Ns, int SI, int W, bool INV, bool ONE>
-__device__ __forceinline__ void row_stage(float2 (&v)[E], float2* const (&bufs)[2], int l, const RowTw<E>& tw) {
-  constexpr int R = (E < N / Ns) ? E : N / Ns;
+__device__ __forceinline__ void row_stage(float2 (&v)[E], float2* const (&bufs)[2], int l, const RowTw<N, E>& tw) {
+  constexpr int R = row_radix(N, E, Ns);
   constexpr int NB = E / R;
   constexpr int T = N / E;
   constexpr bool FIRST = Ns == 1, LAST = Ns * R == N;
@@ -480,7 +515,10 @@ __device__ __forceinline__ void row_stage(float2 (&v)[E], float2* const (&bufs)[
 #pragma unroll
       for (int r = 1; r < R; ++r) {
         if ((r & (r - 1)) == 0) {
-          w[r] = tw.w[SI][b][__builtin_ctz(r)];
+          if constexpr (RowTw<N, E>::CACHE)
+            w[r] = tw.w[SI - 1][b][__builtin_ctz(r)];
+          else
+            w[r] = tw.tab[(((l + b * T) % Ns) * (N / (Ns * R))) << __builtin_ctz(r)];
         } else {
           const int hb = 1 << (31 - __builtin_clz(r));
           w[r] = cmul(w[hb], w[r - hb]);
@@ -512,18 +550,18 @@ __device__ __forceinline__ void row_stage(float2 (&v)[E], float2* const (&bufs)[
 
 // Runs the stages from Ns (stage number SI) on; W is the buffer the next write goes to.
 template <int N, int E, int Ns, int SI, int W, bool INV, bool ONE> struct RowFrom {
-  static constexpr int R = (E < N / Ns) ? E : N / Ns;
+  static constexpr int R = row_radix(N, E, Ns);
   static constexpr bool LAST = Ns * R == N;
   using Next = RowFrom<N, E, Ns * R, SI + 1, LAST ? W : (W ^ 1), INV, ONE>;
   static constexpr int WEND = Next::WEND;
-  static __device__ __forceinline__ void run(float2 (&v)[E], float2* const (&bufs)[2], int l, const RowTw<E>& tw) {
+  static __device__ __forceinline__ void run(float2 (&v)[E], float2* const (&bufs)[2], int l, const RowTw<N, E>& tw) {
     row_stage<N, E, Ns, SI, W, INV, ONE>(v, bufs, l, tw);
     Next::run(v, bufs, l, tw);
   }
 };
 template <int N, int E, int SI, int W, bool INV, bool ONE> struct RowFrom<N, E, N, SI, W, INV, ONE> {
   static constexpr int WEND = W;
-  static __device__ __forceinline__ void run(float2 (&)[E], float2* const (&)[2], int, const RowTw<E>&) {}
+  static __device__ __forceinline__ void run(float2 (&)[E], float2* const (&)[2], int, const RowTw<N, E>&) {}
 };
 
 // Persistent row pass; items are (channel pair, group of SP slots).
@@ -547,7 +585,7 @@ __global__ __launch_bounds__(RowCfg<N2>::WG) void rowpass_kernel(YT* __restrict_
   using Fwd = RowFrom<N2, E, 1, 0, 0, false, ONE>;
   using Inv = RowFrom<N2, E, 1, 0, Fwd::WEND, true, ONE>;
   static_assert(ONE || Inv::WEND == 0, "each item starts writing buffer 0");
-  RowTw<E> tw;
+  RowTw<N2, E> tw;
   RowTwLoad<N2, E, 1, 0>::run(tw, l, tw_row);
   const float nrm = 0.25f / (float)(N1 * N2);  // (1/2)(1/2N) with 2 Ha, 2 Hb below
 
@@ -577,6 +615,9 @@ __global__ __launch_bounds__(RowCfg<N2>::WG) void rowpass_kernel(YT* __restrict_
     for (int q = 0; q < E; ++q) in.y[q] = Yr[l + q * T];
   };
   float4 pr[E / 2];
+  // in 1024-thread workgroups (128 VGPRs) the spectrum entries are fetched
+  // after the forward DFT, so that they do not share registers with it
+  constexpr bool LATE_PQ = C::WG > 512 && !(PF & 2);
   auto load_spectrum = [&](int item) {
     if (MODE == ROW_CONV) {
       int pl, sg, s;
@@ -599,6 +640,7 @@ __global__ __launch_bounds__(RowCfg<N2>::WG) void rowpass_kernel(YT* __restrict_
     // the rows are in v: fetch the next item's into the same registers
     if (PF & 1) load(more ? next : item, in);
     Fwd::run(v, bufs, l, tw);
+    if (LATE_PQ) load_spectrum(item);
     if (s != 0) {
       // own bin (slot q) and the partner's (the other half's slot E - 1 - q),
       // taken for q and E - 1 - q together before either is overwritten; row b
@@ -697,7 +739,7 @@ __global__ __launch_bounds__(RowCfg<N2>::WG) void rowpass_kernel(YT* __restrict_
   if (item >= nitems) return;
   In in;
   load(item, in);
-  load_spectrum(item);
+  if (!LATE_PQ) load_spectrum(item);
   while (true) {
     const int next = item + gridDim.x;
     const bool more = next < nitems;
@@ -705,10 +747,132 @@ __global__ __launch_bounds__(RowCfg<N2>::WG) void rowpass_kernel(YT* __restrict_
     if (!more) break;
     item = next;
     if (!(PF & 1)) load(item, in);
-    if (!(PF & 2)) load_spectrum(item);
+    if (!(PF & 2) && !LATE_PQ) load_spectrum(item);
   }
   // Between items: buffer 0, which the next item writes first, was last read
   // before a barrier of this item (with one buffer every write waits for one).
+}
+
+// Row pass for 8192-point rows: a row pair in one workgroup would need 1024
+// threads (128 VGPRs each, too few), so 512 threads take the two rows one after
+// the other: forward DFT of row a into its LDS buffer, then of row b, the
+// spectrum product between the buffers, then the two inverse DFTs. Same work
+// items, layouts and results as rowpass_kernel.
+template <int N2> struct RowSeqCfg {
+  static constexpr int E = 16;
+  static constexpr int T = N2 / E;  // threads, one row at a time
+  static constexpr int RB = padded_len(N2);
+};
+
+template <typename YT, int N1, int N2, int MODE>
+__global__ __launch_bounds__(RowSeqCfg<N2>::T) void rowpass_seq_kernel(YT* __restrict__ Y, float4* __restrict__ pq,
+                                                                       const float2* __restrict__ tw_row, int pq_off,
+                                                                       int pair_off, int pq_mod, int nitems) {
+  using C = RowSeqCfg<N2>;
+  constexpr int E = C::E, T = C::T;
+  constexpr int HALF = N1 / 2;
+  constexpr int PQROWS = HALF + 1;
+  __shared__ float2 rowbuf[2 * C::RB];
+  float2* A = rowbuf;
+  float2* B = rowbuf + C::RB;
+  const int l = threadIdx.x;
+  using Fwd = RowFrom<N2, E, 1, 0, 0, false, true>;
+  using Inv = RowFrom<N2, E, 1, 0, 0, true, true>;
+  RowTw<N2, E> tw;
+  RowTwLoad<N2, E, 1, 0>::run(tw, l, tw_row);
+  const float nrm = 0.25f / (float)(N1 * N2);
+
+  for (int item = blockIdx.x; item < nitems; item += gridDim.x) {
+    const int pl = item / HALF, s = item - pl * HALF;
+    const int ka = s, kb = s == 0 ? HALF : N1 - s;
+    float4* pqp = pq + ((size_t)pq_off + (pl + pair_off) % pq_mod) * PQROWS * N2;
+    YT* Ya = Y + ((size_t)pl * N1 + ka) * N2;
+    YT* Yb = Y + ((size_t)pl * N1 + kb) * N2;
+    // forward DFTs, results to the row buffers in natural order (one row at a
+    // time: a rolled loop, so that the two rows' work is not interleaved)
+#pragma unroll 1
+    for (int h = 0; h < 2; ++h) {
+      float2* bf = h ? B : A;
+      const YT* Yr = h ? Yb : Ya;
+      float2* const bufs[2] = {bf, bf};
+      float2 v[E];
+#pragma unroll
+      for (int q = 0; q < E; ++q) v[q] = cvt2(Yr[l + q * T]);
+      Fwd::run(v, bufs, l, tw);
+      __syncthreads();  // the last stage's reads of bf are done
+#pragma unroll
+      for (int q = 0; q < E; ++q) bf[pad16(l + q * T)] = v[q];
+    }
+    __syncthreads();
+    // spectrum product: bin k2 of row a with bin N2 - 1 - k2 of row b (s != 0);
+    // rows 0 and N1/2 (s = 0) are each paired with themselves
+    if (s != 0) {
+      const float4* pqs = pqp + (size_t)s * N2;
+#pragma unroll
+      for (int q = 0; q < E; ++q) {
+        const int k2 = l + q * T, m2 = N2 - 1 - k2;
+        const float2 xk = A[pad16(k2)], xm = B[pad16(m2)];
+        const float4 w4 = pqs[k2];
+        if (MODE == ROW_CONV) {
+          const float2 P = make_float2(w4.x, w4.y), Q = make_float2(w4.z, w4.w);
+          A[pad16(k2)] = cadd(cmul(xk, P), cmul(conjf2(xm), Q));
+          B[pad16(m2)] = cadd(cmulc(xm, P), cmulc(conjf2(xk), Q));
+        } else {
+          const float2 fm = conjf2(xm);
+          const float2 ha2 = cadd(xk, fm), d = csub(xk, fm);
+          const float2 hb2 = make_float2(d.y, -d.x);
+          pqp[(size_t)s * N2 + k2] = make_float4(nrm * (ha2.x + hb2.x), nrm * (ha2.y + hb2.y),
+                                                 nrm * (ha2.x - hb2.x), nrm * (ha2.y - hb2.y));
+        }
+      }
+    } else {
+#pragma unroll 1
+      for (int h = 0; h < 2; ++h) {
+        float2* row = h ? B : A;
+        const int pqrow = h ? HALF : 0;
+        const float4* pqs = pqp + (size_t)pqrow * N2;
+        const int kend = (MODE == ROW_CONV) ? (h ? N2 / 2 - 1 : N2 / 2) : N2 - 1;
+        constexpr int KIT = (MODE == ROW_CONV) ? E / 2 + 1 : E;
+#pragma unroll
+        for (int it = 0; it < KIT; ++it) {
+          const int k2 = l + it * T;
+          if (k2 > kend) continue;
+          const int m2 = h ? (N2 - 1 - k2) : ((N2 - k2) & (N2 - 1));
+          const float2 xk = row[pad16(k2)], xm = row[pad16(m2)];
+          const float4 w4 = pqs[k2];
+          if (MODE == ROW_CONV) {
+            const float2 P = make_float2(w4.x, w4.y), Q = make_float2(w4.z, w4.w);
+            const float2 yk = cadd(cmul(xk, P), cmul(conjf2(xm), Q));
+            if (m2 != k2) row[pad16(m2)] = cadd(cmulc(xm, P), cmulc(conjf2(xk), Q));
+            row[pad16(k2)] = yk;
+          } else {
+            const float2 fm = conjf2(xm);
+            const float2 ha2 = cadd(xk, fm), d = csub(xk, fm);
+            const float2 hb2 = make_float2(d.y, -d.x);
+            pqp[(size_t)pqrow * N2 + k2] = make_float4(nrm * (ha2.x + hb2.x), nrm * (ha2.y + hb2.y),
+                                                       nrm * (ha2.x - hb2.x), nrm * (ha2.y - hb2.y));
+          }
+        }
+      }
+    }
+    __syncthreads();
+    if (MODE == ROW_CONV) {
+      // inverse DFTs, each from its row buffer, written back to the intermediate
+#pragma unroll 1
+      for (int h = 0; h < 2; ++h) {
+        float2* bf = h ? B : A;
+        YT* Yr = h ? Yb : Ya;
+        float2* const bufs[2] = {bf, bf};
+        float2 v[E];
+#pragma unroll
+        for (int q = 0; q < E; ++q) v[q] = bf[pad16(l + q * T)];
+        Inv::run(v, bufs, l, tw);  // its first write waits for a barrier
+#pragma unroll
+        for (int q = 0; q < E; ++q) stc(Yr + l + q * T, v[q]);
+      }
+    }
+    __syncthreads();  // the next item writes both buffers
+  }
 }
 
 // ============================================================ launchers
@@ -797,14 +961,15 @@ static int resident_grid(const void* fn, int block, size_t lds, int items) {
 
 template <typename T, typename YT, int R, int M>
 static hipError_t launch_col_t(const ColArgs& a, int pairs, hipStream_t s) {
+  constexpr int kCW = col_width<R>();
   const size_t lds = (size_t)R * R * kCW * sizeof(float2);
   auto fn = colpass_kernel<T, YT, R, M>;
   hipError_t e = allow_lds((const void*)fn, lds);
   if (e != hipSuccess) return e;
   const int items = pairs * (a.N2 / kCW);
   static int grid = 0;
-  if (grid == 0) grid = resident_grid((const void*)fn, 64 * R, lds, 1 << 30);
-  hipLaunchKernelGGL(fn, dim3(grid < items ? grid : items), dim3(64 * R), lds, s, a, items);
+  if (grid == 0) grid = resident_grid((const void*)fn, R * kCW, lds, 1 << 30);
+  hipLaunchKernelGGL(fn, dim3(grid < items ? grid : items), dim3(R * kCW), lds, s, a, items);
   return hipGetLastError();
 }
 
@@ -837,30 +1002,41 @@ static hipError_t launch_col(const ColArgs& a, int N1, int mode, bool act_bf16, 
 template <typename YT, int N1, int N2>
 static hipError_t launch_row_t(void* Y, float4* pq, const float2* tw_row, int pq_off, int pair_off, int pq_mod,
                                int pairs, int mode, hipStream_t s) {
-  using C = RowCfg<N2>;
-  const int items = pairs * ((N1 / 2) / C::SP);
   YT* y = static_cast<YT*>(Y);
-  // HYENA_ROW_PREFETCH: bit 0 fetches the next item's rows early, bit 1 its
-  // spectrum entries; otherwise they are loaded when the item starts. Rows
-  // early (1) measures best; fetching the spectrum early is slower.
-  static const int pf = [] {
-    const char* v = getenv("HYENA_ROW_PREFETCH");
-    return v ? atoi(v) & 3 : 1;
-  }();
-  using Fn = void (*)(YT*, float4*, const float2*, int, int, int, int);
-  Fn fn;
-  if (mode != ROW_CONV) fn = rowpass_kernel<YT, N1, N2, ROW_SPEC, 0>;
-  else if (pf == 1) fn = rowpass_kernel<YT, N1, N2, ROW_CONV, 1>;
-  else if (pf == 2) fn = rowpass_kernel<YT, N1, N2, ROW_CONV, 2>;
-  else if (pf == 3) fn = rowpass_kernel<YT, N1, N2, ROW_CONV, 3>;
-  else fn = rowpass_kernel<YT, N1, N2, ROW_CONV, 0>;
-  // LDS is static in the kernel
-  static int grid[2] = {0, 0};
-  int& g = grid[mode == ROW_CONV ? 0 : 1];
-  if (g == 0) g = resident_grid((const void*)fn, C::WG, 0, 1 << 30);
-  hipLaunchKernelGGL(fn, dim3(g < items ? g : items), dim3(C::WG), 0, s, y, pq, tw_row, pq_off, pair_off,
-                     pq_mod, items);
-  return hipGetLastError();
+  if constexpr (N2 >= 8192) {
+    const int items = pairs * (N1 / 2);
+    auto fn = mode == ROW_CONV ? rowpass_seq_kernel<YT, N1, N2, ROW_CONV> : rowpass_seq_kernel<YT, N1, N2, ROW_SPEC>;
+    static int grid[2] = {0, 0};
+    int& g = grid[mode == ROW_CONV ? 0 : 1];
+    if (g == 0) g = resident_grid((const void*)fn, RowSeqCfg<N2>::T, 0, 1 << 30);
+    hipLaunchKernelGGL(fn, dim3(g < items ? g : items), dim3(RowSeqCfg<N2>::T), 0, s, y, pq, tw_row, pq_off,
+                       pair_off, pq_mod, items);
+    return hipGetLastError();
+  } else {
+    using C = RowCfg<N2>;
+    const int items = pairs * ((N1 / 2) / C::SP);
+    // HYENA_ROW_PREFETCH: bit 0 fetches the next item's rows early, bit 1 its
+    // spectrum entries; otherwise they are loaded when the item starts. Rows
+    // early (1) measures best; fetching the spectrum early is slower.
+    static const int pf = [] {
+      const char* v = getenv("HYENA_ROW_PREFETCH");
+      return v ? atoi(v) & 3 : 1;
+    }();
+    using Fn = void (*)(YT*, float4*, const float2*, int, int, int, int);
+    Fn fn;
+    if (mode != ROW_CONV) fn = rowpass_kernel<YT, N1, N2, ROW_SPEC, 0>;
+    else if (pf == 1) fn = rowpass_kernel<YT, N1, N2, ROW_CONV, 1>;
+    else if (pf == 2) fn = rowpass_kernel<YT, N1, N2, ROW_CONV, 2>;
+    else if (pf == 3) fn = rowpass_kernel<YT, N1, N2, ROW_CONV, 3>;
+    else fn = rowpass_kernel<YT, N1, N2, ROW_CONV, 0>;
+    // LDS is static in the kernel
+    static int grid[2] = {0, 0};
+    int& g = grid[mode == ROW_CONV ? 0 : 1];
+    if (g == 0) g = resident_grid((const void*)fn, C::WG, 0, 1 << 30);
+    hipLaunchKernelGGL(fn, dim3(g < items ? g : items), dim3(C::WG), 0, s, y, pq, tw_row, pq_off, pair_off,
+                       pq_mod, items);
+    return hipGetLastError();
+  }
 }
 
 template <typename YT>

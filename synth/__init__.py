@@ -7,6 +7,7 @@ from .inputs import (  # noqa: F401
     Hyena1DInputs,
     HyenaNDInputs,
     CONFIGS,
+    TEST_SHAPES,
     bf16_round,
     make_1d,
     make_nd,

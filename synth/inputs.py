@@ -188,9 +188,17 @@ CONFIGS = {
     "nd3d_f32_B2_C128_64cube": dict(kind="nd", seed=5, B=2, X=64, Y=64, Z=64, C=128, N=2),
 }
 
+# Extra long-sequence test shapes (checked at sampled outputs): 256-point column
+# DFTs with 2048- and 4096-point rows, between the 64k and the 1M workloads.
+TEST_SHAPES = {
+    "order2_bf16_L256k_D64": dict(kind="1d", seed=31, B=1, L=1 << 18, D=64, N=2, K=16, dtype="bf16",
+                                  u_scale=1 / 8.0),
+    "order2_f32_L512k_D64": dict(kind="1d", seed=32, B=1, L=1 << 19, D=64, N=2, K=16, dtype="f32"),
+}
+
 
 def make_config(name: str):
-    cfg = dict(CONFIGS[name])
+    cfg = dict(CONFIGS[name] if name in CONFIGS else TEST_SHAPES[name])
     kind = cfg.pop("kind")
     if kind == "1d":
         return make_1d(**cfg)

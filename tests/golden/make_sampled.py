@@ -19,9 +19,9 @@ ROOT = os.path.dirname(os.path.dirname(HERE))
 sys.path.insert(0, ROOT)
 
 import oracle  # noqa: E402
-from synth import CONFIGS, make_config, sample_positions  # noqa: E402
+from synth import CONFIGS, TEST_SHAPES, make_config, sample_positions  # noqa: E402
 
-FULL = ["order2_bf16_L64k_D768", "order2_bf16_L1M_D256_dna", "nd3d_f32_B2_C128_64cube"]
+FULL = ["order2_bf16_L64k_D768", "order2_bf16_L1M_D256_dna", "nd3d_f32_B2_C128_64cube"] + list(TEST_SHAPES)
 COUNT = 24
 
 
@@ -34,7 +34,7 @@ def points_3d(X, Y, Z, count, seed):
 
 def make(name):
     t0 = time.time()
-    cfg = CONFIGS[name]
+    cfg = CONFIGS[name] if name in CONFIGS else TEST_SHAPES[name]
     inp = make_config(name)
     out = os.path.join(HERE, f"sampled_{name}.npz")
     if cfg["kind"] == "1d":

@@ -23,7 +23,8 @@ def _golden(name):
     return np.load(path, allow_pickle=False)
 
 
-@pytest.mark.parametrize("name", ["order2_bf16_L64k_D768", "order2_bf16_L1M_D256_dna"])
+@pytest.mark.parametrize("name", ["order2_bf16_L64k_D768", "order2_bf16_L1M_D256_dna", "order2_bf16_L256k_D64",
+                                  "order2_f32_L512k_D64"])
 def test_full_size_1d_sampled(name):
     g = _golden(name)
     inp = make_config(name)
