@@ -217,6 +217,55 @@ __device__ __forceinline__ void stc(cbf16* p, float2 x) {
   p->v = (unsigned int)lo | ((unsigned int)hi << 16);
 }
 
+// ------------------------------------------------ buffer-resource access
+// Raw buffer loads and stores: address = resource base + a 32-bit per-lane
+// offset + a 32-bit workgroup-uniform offset (held in a scalar register), so
+// that accesses whose addresses differ only by uniform amounts share one
+// per-lane offset and cost no per-access vector address arithmetic. Accesses
+// at or beyond `bytes` from the base read zero and write nothing.
+typedef __amdgpu_buffer_rsrc_t brsrc;
+__device__ __forceinline__ brsrc make_brsrc(const void* base, unsigned bytes) {
+  // word 3: 32-bit data format, the value used for untyped access on gfx9
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
+}
+template <typename V> struct BufIO;
+template <> struct BufIO<float> {
+  static __device__ __forceinline__ float ld(brsrc r, int vo, int so) {
+    return __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(r, vo, so, 0));
+  }
+  static __device__ __forceinline__ void st(brsrc r, int vo, int so, float x) {
+    __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(x), r, vo, so, 0);
+  }
+};
+template <> struct BufIO<bf16> {
+  static __device__ __forceinline__ bf16 ld(brsrc r, int vo, int so) {
+    return __builtin_bit_cast(bf16, __builtin_amdgcn_raw_buffer_load_b16(r, vo, so, 0));
+  }
+  static __device__ __forceinline__ void st(brsrc r, int vo, int so, float x) {
+    __builtin_amdgcn_raw_buffer_store_b16(__builtin_bit_cast(unsigned short, (bf16)x), r, vo, so, 0);
+  }
+};
+template <> struct BufIO<cbf16> {
+  static __device__ __forceinline__ cbf16 ld(brsrc r, int vo, int so) {
+    return cbf16{__builtin_amdgcn_raw_buffer_load_b32(r, vo, so, 0)};
+  }
+  static __device__ __forceinline__ void st(brsrc r, int vo, int so, float2 x) {
+    const unsigned short lo = __builtin_bit_cast(unsigned short, (bf16)x.x);
+    const unsigned short hi = __builtin_bit_cast(unsigned short, (bf16)x.y);
+    __builtin_amdgcn_raw_buffer_store_b32((unsigned int)lo | ((unsigned int)hi << 16), r, vo, so, 0);
+  }
+};
+template <> struct BufIO<float2> {
+  static __device__ __forceinline__ float2 ld(brsrc r, int vo, int so) {
+    const auto u = __builtin_amdgcn_raw_buffer_load_b64(r, vo, so, 0);
+    return make_float2(__uint_as_float(u[0]), __uint_as_float(u[1]));
+  }
+  static __device__ __forceinline__ void st(brsrc r, int vo, int so, float2 x) {
+    typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
+    __builtin_amdgcn_raw_buffer_store_b64(u32x2{__float_as_uint(x.x), __float_as_uint(x.y)}, r, vo, so, 0);
+  }
+};
+
 // ---------------------------------------------------------------- host side
 
 #define HY_CHECK_HIP(expr)                         \

@@ -185,11 +185,13 @@ __device__ __forceinline__ void col_tw_load(const ColArgs& a, ColTw& t, unsigned
 
 // Column DFT of N1 = R*R points, n1 = j + R r, k1 = ka + R kb.
 // Forward: thread (lane c, wave j) holds x[j + R r] in v[r] (zero for r >= R/2);
-// writes Y[k1][n2] * W_N^{n2 k1}. wr[ka] = W_N1^(w ka), the inner twiddles of
-// this wave.
+// writes Y[k1][n2] * W_N^{n2 k1} through the resource rY of the pair's
+// intermediate (per-lane offset voY of element (w, c), uniform offset soY of
+// the item's first column). wr[ka] = W_N1^(w ka), the inner twiddles of this
+// wave.
 template <int R, typename YT>
-__device__ __forceinline__ void col_forward(const ColArgs& a, float2 (&v)[R], float2* S, YT* Yp, int c, int w,
-                                            int n2, const float2 (&wr)[R], float2 wk, float2 ws) {
+__device__ __forceinline__ void col_forward(float2 (&v)[R], float2* S, brsrc rY, int voY, int soY, int N2, int c,
+                                            int w, const float2 (&wr)[R], float2 wk, float2 ws) {
   constexpr int kCW = col_width<R>();
   Dft<R, false>::run(v);
 #pragma unroll
@@ -205,7 +207,7 @@ __device__ __forceinline__ void col_forward(const ColArgs& a, float2 (&v)[R], fl
   // k1 = w + R kb: W_N^(n2 k1) = wk ws^kb
 #pragma unroll
   for (int kb = 0; kb < R; ++kb) {
-    stc(Yp + (size_t)(w + R * kb) * a.N2 + n2, cmul(u[kb], wk));
+    BufIO<YT>::st(rY, voY, soY + kb * R * N2 * (int)sizeof(YT), cmul(u[kb], wk));
     wk = cmul(wk, ws);
   }
 }
@@ -243,10 +245,14 @@ __device__ __forceinline__ void col_inverse(float2 (&u)[R], float2* S, const flo
 // has used that part, so one set of registers carries a whole item of
 // prefetch, and no other vector-memory load comes between a prefetch and its
 // use (the in-order load counter never makes the work wait for later loads).
+// Memory is reached through buffer resources over the item's channel pair:
+// every address is the thread's fixed offset (row w, column c of the item)
+// plus a workgroup-uniform offset.
 template <typename T, typename YT, int R, int MODE>
 __global__ __launch_bounds__(R * col_width<R>()) void colpass_kernel(ColArgs a, int nitems) {
   constexpr int N1 = R * R, H = R / 2;
   constexpr bool INVERSE = (MODE == COL_INV || MODE == COL_INV_FWD);
+  constexpr int sT = (int)sizeof(T), sY = (int)sizeof(YT);
   extern __shared__ float4 smem4[];
   float2* S = reinterpret_cast<float2*>(smem4);
   // thread (j, c): row j of the R x R column DFT (w below), column c of the item
@@ -256,6 +262,9 @@ __global__ __launch_bounds__(R * col_width<R>()) void colpass_kernel(ColArgs a, 
   const int half = D / 2, ncb = N2 / kCW;
   const size_t J = (size_t)(a.NO + 1) * D;
   const unsigned N = 2u * (unsigned)L;
+  // per-lane offsets of element (w N2 + c): in the time-domain rows and in the intermediate
+  const int lane_el = w * N2 + c;
+  const int voT = lane_el * sT, voY = lane_el * sY, voH = lane_el * 4;
   // inner twiddles W_N1^(w k) of this wave, fixed for the whole launch
   float2 wr[R];
 #pragma unroll
@@ -270,42 +279,50 @@ __global__ __launch_bounds__(R * col_width<R>()) void colpass_kernel(ColArgs a, 
     ColTw tw;
   };
   struct Item {
-    int pl, n2, pr;
+    int pl, cb, pr;
   };
   auto item_of = [&](int item) {
     Item it;
     it.pl = item / ncb;
-    it.n2 = (item - it.pl * ncb) * kCW + c;
+    it.cb = item - it.pl * ncb;
     it.pr = it.pl + a.pair_off;
     return it;
   };
+  // resource over rows row0 and row0 + 1 (the channel pair) of a [rows][L] array
+  auto pair_rows = [&](const void* base, size_t row0, int esize) {
+    return make_brsrc(static_cast<const char*>(base) + row0 * L * esize, 2u * (unsigned)L * esize);
+  };
+  auto inter = [&](const Item& it) {  // the pair's intermediate [N1][N2]
+    return make_brsrc(static_cast<const char*>(a.Y) + (size_t)it.pl * N1 * N2 * sY, (unsigned)(N1 * N2 * sY));
+  };
+  // uniform element offset of row w + R r (w = 0) of the item's columns
+  auto col0 = [&](const Item& it, int r) { return R * r * N2 + it.cb * kCW; };
   auto load_tw = [&](const Item& it, In& in) {
-    col_tw_load(a, in.tw, ((unsigned)it.n2 * (unsigned)w) & (N - 1), ((unsigned)it.n2 * (unsigned)R) & (N - 1));
+    const unsigned n2 = (unsigned)(it.cb * kCW + c);
+    col_tw_load(a, in.tw, (n2 * (unsigned)w) & (N - 1), (n2 * (unsigned)R) & (N - 1));
   };
   // first part: what the item's first transform reads
   auto load_head = [&](const Item& it, In& in) {
     if constexpr (MODE == COL_FWD_H) {
       const int n = it.pr / half, cp = it.pr % half;
-      const float* ha = a.h + ((size_t)n * D + 2 * cp) * L;
+      const brsrc rh = pair_rows(a.h, (size_t)n * D + 2 * cp, 4);
 #pragma unroll
       for (int r = 0; r < H; ++r) {
-        const int t = N2 * (w + R * r) + it.n2;
-        in.ha[r] = ha[t];
-        in.hb[r] = ha[L + t];
+        in.ha[r] = BufIO<float>::ld(rh, voH, col0(it, r) * 4);
+        in.hb[r] = BufIO<float>::ld(rh, voH, (col0(it, r) + L) * 4);
       }
     } else if constexpr (MODE == COL_FWD_V) {
       const int b = it.pr / half, cp = it.pr % half;
-      const T* sv = reinterpret_cast<const T*>(a.s) + (size_t)b * J * L + (size_t)(2 * cp) * L;
+      const brsrc rv = pair_rows(a.s, (size_t)b * J + 2 * cp, sT);
 #pragma unroll
       for (int r = 0; r < H; ++r) {
-        const int t = N2 * (w + R * r) + it.n2;
-        in.za[r] = sv[t];
-        in.zb[r] = sv[L + t];
+        in.za[r] = BufIO<T>::ld(rv, voT, col0(it, r) * sT);
+        in.zb[r] = BufIO<T>::ld(rv, voT, (col0(it, r) + L) * sT);
       }
     } else {
-      const YT* Yp = reinterpret_cast<const YT*>(a.Y) + (size_t)it.pl * N1 * N2;
+      const brsrc rY = inter(it);
 #pragma unroll
-      for (int kb = 0; kb < R; ++kb) in.y[kb] = Yp[(size_t)(w + R * kb) * N2 + it.n2];
+      for (int kb = 0; kb < R; ++kb) in.y[kb] = BufIO<YT>::ld(rY, voY, col0(it, kb) * sY);
     }
   };
   // second part (inverse modes): gate and skip inputs
@@ -313,17 +330,16 @@ __global__ __launch_bounds__(R * col_width<R>()) void colpass_kernel(ColArgs a, 
     if constexpr (INVERSE) {
       const int b = it.pr / half, cp = it.pr % half;
       const int n = a.n;
-      const T* sb = reinterpret_cast<const T*>(a.s) + (size_t)b * J * L;
-      const T* sx = sb + (size_t)((n + 1) * D + 2 * cp) * L;
-      const T* zp = (n == 0) ? sb + (size_t)(2 * cp) * L
-                             : reinterpret_cast<const T*>(a.zin) + ((size_t)b * D + 2 * cp) * L;
+      const brsrc rx = pair_rows(a.s, (size_t)b * J + (size_t)(n + 1) * D + 2 * cp, sT);
+      const brsrc rz = (n == 0) ? pair_rows(a.s, (size_t)b * J + 2 * cp, sT)
+                                : pair_rows(a.zin, (size_t)b * D + 2 * cp, sT);
 #pragma unroll
       for (int nb = 0; nb < H; ++nb) {
-        const int t = N2 * (w + R * nb) + it.n2;
-        in.xa[nb] = sx[t];
-        in.xb[nb] = sx[L + t];
-        in.za[nb] = zp[t];
-        in.zb[nb] = zp[L + t];
+        const int so = col0(it, nb) * sT, so1 = (col0(it, nb) + L) * sT;
+        in.xa[nb] = BufIO<T>::ld(rx, voT, so);
+        in.xb[nb] = BufIO<T>::ld(rx, voT, so1);
+        in.za[nb] = BufIO<T>::ld(rz, voT, so);
+        in.zb[nb] = BufIO<T>::ld(rz, voT, so1);
       }
       in.da = a.dskip[n * D + 2 * cp];
       in.db = a.dskip[n * D + 2 * cp + 1];
@@ -333,7 +349,8 @@ __global__ __launch_bounds__(R * col_width<R>()) void colpass_kernel(ColArgs a, 
   // Processes item `item` from `in`, refilling `in` with item `nxt` part by part.
   auto process = [&](int item, In& in, int nxt) {
     const Item it = item_of(item), nt = item_of(nxt);
-    YT* Yp = reinterpret_cast<YT*>(a.Y) + (size_t)it.pl * N1 * N2;
+    const brsrc rY = inter(it);
+    const int soY = it.cb * kCW * sY;
     // twiddles of this item, then fetch the next item's
     const float2 wk = cmul(in.tw.lo0, in.tw.hi0), ws = cmul(in.tw.lo1, in.tw.hi1);
     load_tw(nt, in);
@@ -348,16 +365,15 @@ __global__ __launch_bounds__(R * col_width<R>()) void colpass_kernel(ColArgs a, 
           v[r] = make_float2(0.f, 0.f);
       }
       load_head(nt, in);
-      col_forward<R>(a, v, S, Yp, c, w, it.n2, wr, wk, ws);
+      col_forward<R, YT>(v, S, rY, voY, soY, N2, c, w, wr, wk, ws);
     } else {
       const int b = it.pr / half, cp = it.pr % half;
-      const int ca = 2 * cp;
 #pragma unroll
       for (int r = 0; r < R; ++r) v[r] = cvt2(in.y[r]);
       load_head(nt, in);
       float2 u[R];
       col_inverse<R>(u, S, v, c, w, wr, wk, ws);
-      T* zo = reinterpret_cast<T*>(a.zout) + ((size_t)b * D + ca) * L;
+      const brsrc rzo = pair_rows(a.zout, (size_t)b * D + 2 * cp, sT);
       float na[H], nbv[H];
 #pragma unroll
       for (int nb = 0; nb < H; ++nb) {
@@ -368,9 +384,8 @@ __global__ __launch_bounds__(R * col_width<R>()) void colpass_kernel(ColArgs a, 
 #pragma unroll
       for (int nb = 0; nb < R; ++nb) {
         if (nb < H) {
-          const int t = N2 * (w + R * nb) + it.n2;
-          stf(zo + t, na[nb]);
-          stf(zo + L + t, nbv[nb]);
+          BufIO<T>::st(rzo, voT, col0(it, nb) * sT, na[nb]);
+          BufIO<T>::st(rzo, voT, (col0(it, nb) + L) * sT, nbv[nb]);
           v[nb] = make_float2(na[nb], nbv[nb]);
         } else {
           v[nb] = make_float2(0.f, 0.f);
@@ -378,7 +393,7 @@ __global__ __launch_bounds__(R * col_width<R>()) void colpass_kernel(ColArgs a, 
       }
       if constexpr (MODE == COL_INV_FWD) {
         __syncthreads();  // S is reused
-        col_forward<R>(a, v, S, Yp, c, w, it.n2, wr, wk, ws);
+        col_forward<R, YT>(v, S, rY, voY, soY, N2, c, w, wr, wk, ws);
       }
     }
   };
