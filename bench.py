@@ -13,7 +13,11 @@ Roofline: the FFT long-convolution stage is the dominant kernel sequence. Its
 duration comes from HIP events that the library records on the launch stream at
 the stage boundaries of every timed step (hyena_fwd_profiled), averaged; the algorithmic bytes per
 order are B*L*D*3*s + 8*D*(L+1) (read z^n and x^n, write z^{n+1}, read the
-filter spectrum), s the storage size of an activation.
+filter spectrum), s the storage size of an activation. Next to it: the
+projections' MFMA rate (2*M*N*K over their event time), the conv stage's VALU
+instruction and FLOP rates (per-step counts from the rocprofv3 counter summary
+under profiles/, over the live stage time), and the bandwidth of a plain device
+copy measured in the same run.
 """
 from __future__ import annotations
 
@@ -34,6 +38,12 @@ DEFAULT_WORKLOAD = "order2_bf16_L64k_D768"
 CONV_SOURCES = ["fft1d.hip", "common.h", "kernels.h"]
 METRIC = "Hyena fwd tokens/sec at L=64k,D=768 (1 GPU); FFT-conv HBM GB/s % of peak"
 HBM_PEAK_GBS = 8000.0
+MFMA_BF16_PEAK_TFLOPS = 2516.6  # 256 CUs x 2.4 GHz x 4096 flop/clk (dense)
+MFMA_F32_PEAK_TFLOPS = 157.3
+# VALU issue: each of the 4 SIMDs of a CU issues one wave64 instruction every 4
+# cycles, so 256 CUs x 2.4 GHz wave instructions per second
+VALU_PEAK_GINSTR = 256 * 2.4
+VALU_F32_PEAK_TFLOPS = 157.3  # packed fp32 FMA; unpacked code tops out at half
 
 
 def log(msg):
@@ -56,12 +66,9 @@ def conv_source_hash() -> str:
     return hsh.hexdigest()
 
 
-def measured_traffic(workload: str, path: str | None = None):
-    """HBM bytes per step of the long-convolution stage, from the rocprofv3
-    FETCH_SIZE / WRITE_SIZE summary under profiles/ (each counter scaled by what it
-    reads for a plain copy of known size). None if there is no summary for this
-    workload or the kernel sources changed since it was taken."""
-    path = path or os.path.join(ROOT, "profiles", f"hbm_traffic_{workload}.txt")
+def _profile_values(path: str):
+    """The '@key: value' lines of a profile summary, or None if the file is missing
+    or was measured on other kernel sources."""
     if not os.path.exists(path):
         return None
     kv = {}
@@ -72,7 +79,42 @@ def measured_traffic(workload: str, path: str | None = None):
                 kv[k.strip()] = v.strip()
     if kv.get("conv_source_sha256") != conv_source_hash():
         return None
-    return float(kv["conv_stage_bytes_per_step"])
+    return kv
+
+
+def measured_traffic(workload: str, path: str | None = None):
+    """HBM bytes per step of the long-convolution stage, from the rocprofv3
+    FETCH_SIZE / WRITE_SIZE summary under profiles/ (each counter scaled by what it
+    reads for a plain copy of known size). None if there is no summary for this
+    workload or the kernel sources changed since it was taken."""
+    kv = _profile_values(path or os.path.join(ROOT, "profiles", f"hbm_traffic_{workload}.txt"))
+    return None if kv is None else float(kv["conv_stage_bytes_per_step"])
+
+
+def measured_valu(workload: str, path: str | None = None):
+    """(VALU wave instructions, fp32 VALU FLOPs) per step of the long-convolution
+    stage, from the rocprofv3 SQ counter summary under profiles/; None as for
+    measured_traffic."""
+    kv = _profile_values(path or os.path.join(ROOT, "profiles", f"valu_mfma_{workload}.txt"))
+    if kv is None:
+        return None
+    return float(kv["conv_valu_instr_per_step"]), float(kv["conv_valu_flops_per_step"])
+
+
+def copy_probe(torch, mib: int = 1024, reps: int = 5) -> float:
+    """GB/s (bytes read + written) of a plain device copy of `mib` MiB."""
+    src = torch.ones(mib * (1 << 20) // 4, dtype=torch.float32, device="cuda")
+    dst = torch.empty_like(src)
+    dst.copy_(src)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(reps):
+        dst.copy_(src)
+    e1.record()
+    torch.cuda.synchronize()
+    gbs = 2.0 * src.numel() * 4 * reps / (e0.elapsed_time(e1) * 1e-3) / 1e9
+    del src, dst
+    return gbs
 
 
 def cpu_baseline(inp, budget_tokens: int):
@@ -165,10 +207,34 @@ def main():
     ms_per_step = 1e3 * elapsed / args.steps
     value = B * L * args.steps / elapsed
     stages = np.mean([[evs[i].elapsed_time(evs[i + 1]) for i in range(3)] for evs in events], axis=0)
+    step_ms = np.array([evs[0].elapsed_time(evs[3]) for evs in events])
     lds = L <= 4096
     alg = conv_alg_bytes(B, L, D, N, s, lds)
     achieved = alg / (stages[1] * 1e-3) / 1e9
     log(f"stages ms: in-proj {stages[0]:.4f} conv {stages[1]:.4f} out-proj {stages[2]:.4f}")
+
+    # filter generation (once per layer; outside the step) and a plain copy for scale
+    f0, f1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    f0.record()
+    hs.hyena_filter_gen(layer, f(inp.w1), f(inp.b1), f(inp.w2), f(inp.b2), f(inp.w3), f(inp.b3), f(inp.decay),
+                        inp.K)
+    f1.record()
+    torch.cuda.synchronize()
+    filter_gen_ms = f0.elapsed_time(f1)
+    copy_gbs = copy_probe(torch)
+
+    mfma_peak = MFMA_BF16_PEAK_TFLOPS if s == 2 else MFMA_F32_PEAK_TFLOPS
+    proj = {}
+    for name, n_out, k_in, ms in (("in_proj", (N + 1) * D, D, stages[0]), ("out_proj", D, D, stages[2])):
+        tf = 2.0 * B * L * n_out * k_in / (ms * 1e-3) / 1e12
+        proj[name] = {"tflops": tf, "peak": mfma_peak, "frac": tf / mfma_peak}
+    valu = measured_valu(args.workload)
+    conv_valu = None
+    if valu is not None:
+        gi = valu[0] / (stages[1] * 1e-3) / 1e9
+        tf = valu[1] / (stages[1] * 1e-3) / 1e12
+        conv_valu = {"bound": "alu", "achieved": gi, "peak": VALU_PEAK_GINSTR, "unit": "G wave-instr/s",
+                     "frac": gi / VALU_PEAK_GINSTR, "fp32_tflops": tf, "fp32_peak_tflops": VALU_F32_PEAK_TFLOPS}
 
     out = {
         "metric": METRIC,
@@ -185,9 +251,15 @@ def main():
         "data": "synthetic",
         "config": {"workload": args.workload, "B": B, "L": L, "D": D, "N": N},
         "stage_ms": {"in_proj": stages[0], "fft_conv": stages[1], "out_proj": stages[2]},
+        "step_ms_events": {"p10": float(np.percentile(step_ms, 10)), "p50": float(np.median(step_ms)),
+                           "p90": float(np.percentile(step_ms, 90))},
+        "filter_gen_ms": filter_gen_ms,
         "roofline": {"bound": "hbm", "kernel": "fft_conv stage (all orders)", "achieved": achieved,
                      "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS,
                      "alg_bytes": alg, "traffic": measured_traffic(args.workload)},
+        "conv_valu": conv_valu,
+        "projections_mfma": proj,
+        "copy_probe_gbs": copy_gbs,
     }
     if not args.no_cpu_baseline:
         log("cpu baseline (oracle)")

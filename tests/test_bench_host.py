@@ -1,5 +1,5 @@
 """Host logic of bench.py: the algorithmic byte count and the reading of the
-committed HBM-traffic summary (no GPU needed)."""
+committed HBM-traffic and VALU counter summaries (no GPU needed)."""
 import os
 import subprocess
 import sys
@@ -37,3 +37,17 @@ def test_traffic_summary_is_void_after_a_kernel_change(tmp_path):
 def test_more_than_one_gpu_is_refused():
     r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--gpus", "2"], capture_output=True, text=True)
     assert r.returncode == 2 and "one GPU" in r.stderr
+
+
+def test_valu_summary_with_current_sources(tmp_path):
+    p = tmp_path / "v.txt"
+    p.write_text("@conv_valu_instr_per_step: 2.5e8\n@conv_valu_flops_per_step: 1.6e10\n"
+                 f"@conv_source_sha256: {bench.conv_source_hash()}\n")
+    assert bench.measured_valu("w", str(p)) == (2.5e8, 1.6e10)
+
+
+def test_valu_summary_is_void_after_a_kernel_change(tmp_path):
+    p = tmp_path / "v.txt"
+    p.write_text("@conv_valu_instr_per_step: 2.5e8\n@conv_valu_flops_per_step: 1.6e10\n@conv_source_sha256: 0\n")
+    assert bench.measured_valu("w", str(p)) is None
+    assert bench.measured_valu("no_such_workload") is None
