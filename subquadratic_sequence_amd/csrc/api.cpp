@@ -14,6 +14,9 @@ using hy::align_up;
 
 namespace {
 
+// Default bound on the four-step intermediate of one channel-pair group, MB.
+constexpr int kGroupMB = 0;
+
 constexpr size_t kAlign = 256;
 constexpr int kLdsMaxL = 4096;  // 2L <= 8192 runs fully in LDS
 
@@ -125,20 +128,38 @@ int device_ok() {
 }
 
 // Tuning knobs (read once): HYENA_GROUP_PAIRS = channel pairs per four-step
-// group (0: all pairs in one group); HYENA_SPECTRUM_FP32 = 1 keeps the
-// four-step intermediate in fp32 for bf16 workloads.
+// group (overrides HYENA_GROUP_MB); HYENA_GROUP_MB = bound on the four-step
+// intermediate of one group, in MB (0: all pairs in one group); 
+// HYENA_SPECTRUM_FP32 = 1 keeps the four-step intermediate in fp32 for bf16
+// workloads.
 struct Tuning {
   int group_pairs = 0;
+  int group_mb = kGroupMB;
   bool y_bf16 = true;
 };
 const Tuning& tuning() {
   static const Tuning t = [] {
     Tuning r;
     if (const char* s = getenv("HYENA_GROUP_PAIRS")) r.group_pairs = atoi(s);
+    if (const char* s = getenv("HYENA_GROUP_MB")) r.group_mb = atoi(s);
     if (const char* s = getenv("HYENA_SPECTRUM_FP32")) r.y_bf16 = atoi(s) == 0;
     return r;
   }();
   return t;
+}
+
+// Channel pairs per four-step group: the passes of one group run back to back,
+// so a group whose intermediate fits the 256 MB last-level cache with room to
+// spare reads it back from there rather than from HBM. Groups are balanced.
+int group_pairs(int pairs_all, size_t y_bytes_per_pair) {
+  const Tuning& t = tuning();
+  if (t.group_pairs > 0) return t.group_pairs;
+  if (t.group_mb <= 0) return pairs_all;
+  const size_t cap = (size_t)t.group_mb << 20;
+  long long per = (long long)(cap / y_bytes_per_pair);
+  if (per < 1) per = 1;
+  const long long ng = (pairs_all + per - 1) / per;
+  return (int)((pairs_all + ng - 1) / ng);
 }
 
 }  // namespace
@@ -280,8 +301,8 @@ static int fwd_impl(const hyena_layer* layer, const void* u, const void* w_in, c
     a.L = L;
     a.D = D;
     a.NO = N;
-    a.group_pairs = tuning().group_pairs;
     a.y_bf16 = tuning().y_bf16;
+    a.group_pairs = group_pairs(B * (D / 2), (size_t)2 * L * (bf && a.y_bf16 ? 4 : 8));
     HY_CHECK_HIP(hy::fourstep_conv(tables(cl, layer->cache), a, bf, stream));
   }
   if (ev) HY_CHECK_HIP(hipEventRecord(ev[2], stream));
