@@ -24,6 +24,8 @@
 //    the same registers, starts the forward column DFT of the next order.
 #include <stdlib.h>
 
+#include <type_traits>
+
 #include "common.h"
 #include "kernels.h"
 
@@ -892,21 +894,160 @@ __global__ __launch_bounds__(RowSeqCfg<N2>::T) void rowpass_seq_kernel(YT* __res
 
 // ============================================================ launchers
 
+// ============================================================ LDS regime, register-resident
+
+// All orders of one channel pair in one thread group, for 1024 <= 2L <= 4096.
+// Same computation as fftconv_lds_kernel, laid out like the row pass: thread l
+// of a pair owns elements l + q T (q < E) in registers before the first radix
+// stage and after the last, the stages in between exchange through the padded
+// LDS buffers, and the stage twiddles are cached in registers. z^n at
+// t = l + q T (q < E/2, the positions t < L) stays in the registers of the
+// thread that feeds it to the forward transform and gates the inverse one.
+// Each order's filter spectrum entries are requested before its forward
+// transform and its gate inputs after it, so that their latency is covered.
+template <int N, int NBUF> struct LdsRegCfg {
+  static_assert(N >= 1024 && N <= 4096, "256-thread workgroups, two per CU");
+  static constexpr int E = 16;
+  static constexpr int T = N / E;                // threads per channel pair
+  static constexpr int WG = 256;                 // threads per workgroup
+  static constexpr int G = WG / T;               // channel pairs per workgroup
+  static constexpr int RB = padded_len(N);       // float2 per buffer
+  static constexpr size_t LDS = (size_t)G * NBUF * RB * sizeof(float2);
+};
+
+template <typename T, int N, int NBUF>
+__global__ __launch_bounds__(256, 2) void fftconv_lds_reg_kernel(
+    const T* __restrict__ sp, const float* __restrict__ dskip, const float4* __restrict__ pq,
+    const float2* __restrict__ twtab, T* __restrict__ zout, int D, int NO) {
+  using C = LdsRegCfg<N, NBUF>;
+  constexpr int E = C::E, TT = C::T, L = N / 2, H = E / 2;
+  constexpr int KIT = (L + 1 + TT - 1) / TT;  // spectrum entries k = l + i T <= L per thread
+  constexpr bool ONE = NBUF == 1;
+  extern __shared__ float4 smem4[];
+  const int g = threadIdx.x / TT, l = threadIdx.x % TT;
+  float2* buf = reinterpret_cast<float2*>(smem4) + (size_t)g * NBUF * C::RB;
+  float2* const bufs[2] = {buf, ONE ? buf : buf + C::RB};
+  using Fwd = RowFrom<N, E, 1, 0, 0, false, ONE>;
+  constexpr int WP = Fwd::WEND;  // buffer of the spectrum product (not read by the last forward stage)
+  using Inv = RowFrom<N, E, 1, 0, WP ^ 1, true, ONE>;
+  RowTw<N, E> tw;
+  RowTwLoad<N, E, 1, 0>::run(tw, l, twtab);
+
+  const int pr = blockIdx.x * C::G + g;
+  const int half = D / 2;
+  const int b = pr / half, cp = pr % half;
+  const int ca = 2 * cp, cb = ca + 1;
+  const size_t J = (size_t)(NO + 1) * D;
+  const T* sb = sp + (size_t)b * J * L;  // short-convolved blocks (v, x^1, .., x^NO)
+
+  float2 z[H];  // (z_a, z_b) at t = l + q T
+#pragma unroll
+  for (int q = 0; q < H; ++q) {
+    const int t = l + q * TT;
+    z[q] = make_float2(ldf(sb + (size_t)ca * L + t), ldf(sb + (size_t)cb * L + t));
+  }
+  for (int n = 0; n < NO; ++n) {
+    // this order's spectrum entries (k clamped to L: the extra entries go unused)
+    const float4* pqn = pq + ((size_t)n * half + cp) * (L + 1);
+    float4 pk[KIT];
+#pragma unroll
+    for (int i = 0; i < KIT; ++i) {
+      const int k = l + i * TT;
+      pk[i] = pqn[k <= L ? k : L];
+    }
+    const float da = dskip[n * D + ca], db = dskip[n * D + cb];
+
+    float2 v[E];
+#pragma unroll
+    for (int q = 0; q < E; ++q) v[q] = q < H ? z[q] : make_float2(0.f, 0.f);
+    Fwd::run(v, bufs, l, tw);
+    // this order's gates, needed after the product and the inverse transform
+    T xa[H], xb[H];
+    const T* sx = sb + (size_t)((n + 1) * D + ca) * L;
+#pragma unroll
+    for (int q = 0; q < H; ++q) {
+      xa[q] = sx[l + q * TT];
+      xb[q] = sx[L + l + q * TT];
+    }
+    // spectrum product on the bin pairs (k, N - k), k in [0, L], through LDS
+    float2* P = bufs[WP];
+    if (ONE) __syncthreads();
+#pragma unroll
+    for (int q = 0; q < E; ++q) P[pad16(l + q * TT)] = v[q];
+    __syncthreads();
+#pragma unroll
+    for (int i = 0; i < KIT; ++i) {
+      const int k = l + i * TT;
+      if (k <= L) {
+        const float2 Pk = make_float2(pk[i].x, pk[i].y), Qk = make_float2(pk[i].z, pk[i].w);
+        const int m = (N - k) & (N - 1);
+        const float2 xk = P[pad16(k)], xm = P[pad16(m)];
+        const float2 yk = cadd(cmul(xk, Pk), cmul(conjf2(xm), Qk));
+        if (m != k) P[pad16(m)] = cadd(cmulc(xm, Pk), cmulc(conjf2(xk), Qk));
+        P[pad16(k)] = yk;
+      }
+    }
+    __syncthreads();
+#pragma unroll
+    for (int q = 0; q < E; ++q) v[q] = P[pad16(l + q * TT)];
+    Inv::run(v, bufs, l, tw);
+    // gate + skip on t = l + q T < L
+    const bool last = (n == NO - 1);
+#pragma unroll
+    for (int q = 0; q < H; ++q) {
+      const float na = cvt1(xa[q]) * v[q].x + da * z[q].x;
+      const float nb = cvt1(xb[q]) * v[q].y + db * z[q].y;
+      if (last) {
+        const int t = l + q * TT;
+        stf(zout + ((size_t)b * D + ca) * L + t, na);
+        stf(zout + ((size_t)b * D + cb) * L + t, nb);
+      } else {
+        z[q] = make_float2(na, nb);
+      }
+    }
+    __syncthreads();  // the next order's first stage writes buffer 0 again
+  }
+}
+
 static hipError_t allow_lds(const void* fn, size_t bytes) {
   if (bytes <= 65536) return hipSuccess;
   return hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)bytes);
 }
 
+// LDS buffers per channel pair of the register-resident kernel (HYENA_LDS_NBUF:
+// 2 = one barrier per radix stage, 1 = half the LDS, two barriers per stage)
+static int lds_nbuf() {
+  static const int nb = [] {
+    const char* e = getenv("HYENA_LDS_NBUF");
+    return e && atoi(e) == 1 ? 1 : 2;
+  }();
+  return nb;
+}
+
 template <typename T, int N>
 static hipError_t launch_lds_conv(const LdsConvArgs& a, hipStream_t s) {
-  using C = LdsCfg<N>;
   const int pairs = a.B * a.D / 2;
-  auto fn = fftconv_lds_kernel<T, N>;
-  hipError_t e = allow_lds((const void*)fn, C::LDS);
-  if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(fn, dim3(pairs / C::G), dim3(C::WG), C::LDS, s, (const T*)a.s, a.dskip, a.pq, a.tw,
-                     (T*)a.zout, a.D, a.NO);
-  return hipGetLastError();
+  if constexpr (N >= 1024 && N <= 4096) {
+    auto go = [&](auto nbuf) -> hipError_t {
+      constexpr int NB = decltype(nbuf)::value;
+      using C = LdsRegCfg<N, NB>;
+      auto fn = fftconv_lds_reg_kernel<T, N, NB>;
+      hipError_t e = allow_lds((const void*)fn, C::LDS);
+      if (e != hipSuccess) return e;
+      hipLaunchKernelGGL(fn, dim3(pairs / C::G), dim3(C::WG), C::LDS, s, (const T*)a.s, a.dskip, a.pq, a.tw,
+                         (T*)a.zout, a.D, a.NO);
+      return hipGetLastError();
+    };
+    return lds_nbuf() == 1 ? go(std::integral_constant<int, 1>{}) : go(std::integral_constant<int, 2>{});
+  } else {
+    using C = LdsCfg<N>;
+    auto fn = fftconv_lds_kernel<T, N>;
+    hipError_t e = allow_lds((const void*)fn, C::LDS);
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(fn, dim3(pairs / C::G), dim3(C::WG), C::LDS, s, (const T*)a.s, a.dskip, a.pq, a.tw,
+                       (T*)a.zout, a.D, a.NO);
+    return hipGetLastError();
+  }
 }
 
 template <int N>

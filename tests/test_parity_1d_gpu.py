@@ -47,7 +47,7 @@ SWEEP = [
     # LDS regime (2L <= 8192)
     (1, 16, 64, 2, "f32"), (3, 32, 64, 1, "f32"), (1, 64, 128, 3, "f32"), (2, 128, 64, 2, "f32"),
     (1, 256, 64, 2, "f32"), (3, 512, 128, 2, "f32"), (1, 2048, 64, 3, "f32"), (2, 4096, 64, 2, "f32"),
-    (2, 1024, 128, 2, "bf16"), (1, 4096, 192, 4, "f32"),
+    (2, 1024, 128, 2, "bf16"), (1, 4096, 192, 4, "f32"), (2, 512, 64, 1, "bf16"), (1, 2048, 128, 4, "bf16"),
     # four-step regime (2L >= 16384): N2 = 64, 128, 256, 512
     (1, 8192, 64, 2, "f32"), (3, 16384, 64, 1, "f32"), (1, 32768, 128, 2, "f32"), (1, 65536, 64, 2, "f32"),
     (2, 16384, 64, 2, "bf16"),
