@@ -444,10 +444,11 @@ template <int N2> struct RowCfg {
 
 enum { ROW_CONV = 0, ROW_SPEC = 1 };
 
-// value of x held by the lane 32 apart
-__device__ __forceinline__ float xhalf(float x, bool upper) {
-  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-  return __uint_as_float(upper ? r[0] : r[1]);
+// value of x held by the lane 32 apart: a backward permute through the LDS
+// crossbar (an LDS-pipe instruction, no VALU work); `sw` is the byte address
+// 4 * (lane ^ 32)
+__device__ __forceinline__ float xhalf(float x, int sw) {
+  return __int_as_float(__builtin_amdgcn_ds_bpermute(sw, __float_as_int(x)));
 }
 
 // Radix of the row DFT stage that starts at span Ns: the first stage takes the
@@ -594,6 +595,7 @@ __global__ __launch_bounds__(RowCfg<N2>::WG) void rowpass_kernel(YT* __restrict_
   __shared__ float2 rowbuf[C::SP * 2 * C::NBUF * C::RB];
   const int g = (threadIdx.x >> 6) * 32 + (threadIdx.x & 31);  // row-pair lane index in the workgroup
   const bool up = (threadIdx.x >> 5) & 1;                       // row b
+  const int sw32 = 4 * ((int)(threadIdx.x & 63) ^ 32);            // byte address of the lane 32 apart
   const int slot = g / T, i = g % T;
   const int l = up ? T - 1 - i : i;
   float2* buf = rowbuf + (slot * 2 + (up ? 1 : 0)) * C::RB;
@@ -666,10 +668,11 @@ __global__ __launch_bounds__(RowCfg<N2>::WG) void rowpass_kernel(YT* __restrict_
 #pragma unroll
       for (int q = 0; q < E / 2; ++q) {
         const int q2 = E - 1 - q;
-        const float2 pm = make_float2(xhalf(v[q2].x, up), xhalf(v[q2].y, up));
-        const float2 pm2 = make_float2(xhalf(v[q].x, up), xhalf(v[q].y, up));
+        const float2 pm = make_float2(xhalf(v[q2].x, sw32), xhalf(v[q2].y, sw32));
+        const float2 pm2 = make_float2(xhalf(v[q].x, sw32), xhalf(v[q].y, sw32));
         if (MODE == ROW_CONV) {
-          const float4 o = make_float4(xhalf(pr[q].x, up), xhalf(pr[q].y, up), xhalf(pr[q].z, up), xhalf(pr[q].w, up));
+          const float4 o = make_float4(xhalf(pr[q].x, sw32), xhalf(pr[q].y, sw32), xhalf(pr[q].z, sw32),
+                                       xhalf(pr[q].w, sw32));
           const float2 P = make_float2(pr[q].x, sg_ * pr[q].y), Q = make_float2(pr[q].z, sg_ * pr[q].w);
           const float2 P2 = make_float2(o.x, sg_ * o.y), Q2 = make_float2(o.z, sg_ * o.w);
           v[q] = cadd(cmul(v[q], P), cmul(conjf2(pm), Q));
