@@ -14,8 +14,11 @@
 //    rows: a tile computes rows [m0 - 8, m0 + 248) and writes [m0, m0 + 248), so
 //    the two previous rows of every written row are on chip.
 // Block tile 256 x 256, eight waves of 128 x 64 (8 accumulators of 32 x 32 per
-// wave, two waves per SIMD), K step of 64 bytes per row, LDS double buffered
-// with the next tile staged in registers. Tiles are numbered so that the
+// wave, two waves per SIMD), K step of 64 bytes per row. Three LDS tile
+// buffers: while a step multiplies tile kt it already reads the first MMA
+// fragments of tile kt + 1 (stored one step earlier) and stores tile kt + 2
+// from registers, so that no step starts by waiting for all eight waves' LDS
+// reads; global loads run three tiles ahead through two register sets. Tiles are numbered so that the
 // workgroups dispatched to one XCD walk the N-tiles of one M-tile together
 // (they share the A rows in that XCD's L2). bf16 storage uses v_mfma_f32_32x32x16_bf16, fp32 uses
 // v_mfma_f32_32x32x2_f32; accumulation is fp32 in both cases.
@@ -44,7 +47,8 @@ template <typename T> struct GemmCfg {
 
 constexpr int kCsLd = GBM + 4;  // staging row (floats), channel-major output: [64 n][256 m]
 constexpr int kRmLd = 64 + 4;   // staging row (floats), row-major output: [256 m][64 n]
-constexpr size_t kTileBytes = 2 * 2 * GBM * 80;  // two buffers of A and B, 80-byte rows
+constexpr int kBufs = 3;                                 // LDS tile buffers
+constexpr size_t kTileBytes = kBufs * 2 * GBM * 80;  // A and B per buffer, 80-byte rows
 constexpr size_t kStageBytes = 64 * kCsLd * 4 > 256 * kRmLd * 4 ? 64 * kCsLd * 4 : 256 * kRmLd * 4;
 constexpr size_t kGemmMain = kTileBytes > kStageBytes ? kTileBytes : kStageBytes;
 constexpr size_t kGemmLds = kGemmMain + GBN * 3 * 4;  // + short-conv taps of the tile's columns
@@ -68,8 +72,8 @@ __global__ __launch_bounds__(512, 1) void gemm_kernel(const T* __restrict__ A, c
   constexpr int BK = Cfg::BK, LDK = Cfg::LDK, VEC = Cfg::VEC, NCH = Cfg::CHUNKS;
   extern __shared__ float4 smem4[];
   char* smem = reinterpret_cast<char*>(smem4);
-  T* As0 = reinterpret_cast<T*>(smem);  // [2][GBM][LDK] then Bs [2][GBN][LDK]
-  T* Bs0 = As0 + 2 * Cfg::TILE;
+  T* As0 = reinterpret_cast<T*>(smem);  // [kBufs][GBM][LDK] then Bs [kBufs][GBN][LDK]
+  T* Bs0 = As0 + kBufs * Cfg::TILE;
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int wm = wave >> 2, wn = wave & 3;  // 2 x 4 waves of 128 x 64
@@ -148,10 +152,11 @@ __global__ __launch_bounds__(512, 1) void gemm_kernel(const T* __restrict__ A, c
     }
     --tiles_left;
   };
-  auto store_tile = [&](auto set) {
-    constexpr int buf = decltype(set)::value;
-    const u32x4* ra = ra2[buf];
-    const u32x4* rb = rb2[buf];
+  // register set `set` -> LDS buffer `buf`
+  auto store_tile = [&](auto set, auto bufc) {
+    constexpr int sidx = decltype(set)::value, buf = decltype(bufc)::value;
+    const u32x4* ra = ra2[sidx];
+    const u32x4* rb = rb2[sidx];
     T* As = As0 + buf * Cfg::TILE;
     T* Bs = Bs0 + buf * Cfg::TILE;
 #pragma unroll
@@ -181,64 +186,88 @@ __global__ __launch_bounds__(512, 1) void gemm_kernel(const T* __restrict__ A, c
     }
   };
 
-  // Tile kt sits in LDS buffer kt & 1 and travels through register set
-  // kt & 1, loaded two steps before it is needed.
-  using Set0 = std::integral_constant<int, 0>;
-  using Set1 = std::integral_constant<int, 1>;
-  const int ktiles = K / BK;
-  load_tile(Set0{});
-  store_tile(Set0{});
-  load_tile(Set1{});
-  __syncthreads();
+  // MMA fragments of one 16 (bf16) or 2 (fp32) wide K slice: 4 of A, 2 of B
+  using FragT = std::conditional_t<sizeof(T) == 2, bf16x8, float>;
+  struct Frag {
+    FragT a[4], b[2];
+  };
   const int ar = wm * 128 + (lane & 31), br = wn * 64 + (lane & 31);
-  auto step = [&](int kt, auto cur_c) {
-    constexpr int cur = decltype(cur_c)::value;
-    using Other = std::integral_constant<int, cur ^ 1>;
-    load_tile(cur_c);  // tile kt + 2; this set went to LDS one step ago
+  constexpr int KS = sizeof(T) == 2 ? 16 : 2;  // K per MMA
+  auto read_frag = [&](Frag& f, int buf, int kk) {
+    const T* As = As0 + buf * Cfg::TILE;
+    const T* Bs = Bs0 + buf * Cfg::TILE;
+    if constexpr (sizeof(T) == 2) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        f.a[i] = *reinterpret_cast<const bf16x8*>(As + (ar + i * 32) * LDK + kk + (lane >> 5) * 8);
+#pragma unroll
+      for (int j = 0; j < 2; ++j)
+        f.b[j] = *reinterpret_cast<const bf16x8*>(Bs + (br + j * 32) * LDK + kk + (lane >> 5) * 8);
+    } else {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) f.a[i] = As[(ar + i * 32) * LDK + kk + (lane >> 5)];
+#pragma unroll
+      for (int j = 0; j < 2; ++j) f.b[j] = Bs[(br + j * 32) * LDK + kk + (lane >> 5)];
+    }
+  };
+  auto mma = [&](const Frag& f) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int j = 0; j < 2; ++j) {
+        if constexpr (sizeof(T) == 2)
+          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f.a[i], f.b[j], acc[i][j], 0, 0, 0);
+        else
+          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x2f32(f.a[i], f.b[j], acc[i][j], 0, 0, 0);
+      }
+  };
+
+  // Tile kt sits in LDS buffer kt % 3; it travels through register set kt & 1,
+  // loaded three steps before it is multiplied and stored to LDS two steps
+  // before. f0 holds the first K slice of the current tile on entry to a step.
+  using S0 = std::integral_constant<int, 0>;
+  using S1 = std::integral_constant<int, 1>;
+  const int ktiles = K / BK;
+  load_tile(S0{});
+  store_tile(S0{}, std::integral_constant<int, 0>{});
+  load_tile(S1{});
+  store_tile(S1{}, std::integral_constant<int, 1>{});
+  load_tile(S0{});
+  __syncthreads();
+  Frag f0;
+  read_frag(f0, 0, 0);
+  // step kt (compile-time phase P = kt % 6): multiply tile kt, read the first
+  // slice of tile kt + 1, store tile kt + 2, fetch tile kt + 3
+  auto step = [&](int kt, auto phase) {
+    constexpr int P = decltype(phase)::value;
+    constexpr int cur = P % 3, nxt = (P + 1) % 3, st = (P + 2) % 3;
+    load_tile(std::integral_constant<int, (P + 1) & 1>{});  // tile kt + 3
     // keep the loads at the top of the step (the scheduler would otherwise sink
     // them toward their use and shorten the prefetch distance)
     __builtin_amdgcn_sched_barrier(0);
-    const T* As = As0 + cur * Cfg::TILE;
-    const T* Bs = Bs0 + cur * Cfg::TILE;
-    if constexpr (sizeof(T) == 2) {
+    if (kt < ktiles) {  // the steps past the last tile only move data
 #pragma unroll
-      for (int kk = 0; kk < BK; kk += 16) {
-        bf16x8 af[4], bfr[2];
-#pragma unroll
-        for (int i = 0; i < 4; ++i)
-          af[i] = *reinterpret_cast<const bf16x8*>(As + (ar + i * 32) * LDK + kk + (lane >> 5) * 8);
-#pragma unroll
-        for (int j = 0; j < 2; ++j)
-          bfr[j] = *reinterpret_cast<const bf16x8*>(Bs + (br + j * 32) * LDK + kk + (lane >> 5) * 8);
-#pragma unroll
-        for (int i = 0; i < 4; ++i)
-#pragma unroll
-          for (int j = 0; j < 2; ++j)
-            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[i], bfr[j], acc[i][j], 0, 0, 0);
-      }
-    } else {
-#pragma unroll
-      for (int kk = 0; kk < BK; kk += 2) {
-        float af[4], bfr[2];
-#pragma unroll
-        for (int i = 0; i < 4; ++i) af[i] = As[(ar + i * 32) * LDK + kk + (lane >> 5)];
-#pragma unroll
-        for (int j = 0; j < 2; ++j) bfr[j] = Bs[(br + j * 32) * LDK + kk + (lane >> 5)];
-#pragma unroll
-        for (int i = 0; i < 4; ++i)
-#pragma unroll
-          for (int j = 0; j < 2; ++j)
-            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x2f32(af[i], bfr[j], acc[i][j], 0, 0, 0);
+      for (int kk = 0; kk < BK; kk += KS) {
+        Frag f;
+        if (kk + KS < BK) read_frag(f, cur, kk + KS);
+        else read_frag(f, nxt, 0);
+        mma(f0);
+        f0 = f;
       }
     }
-    store_tile(Other{});  // tile kt + 1 (after the last step: unused)
+    store_tile(std::integral_constant<int, P & 1>{}, std::integral_constant<int, st>{});  // tile kt + 2
     __syncthreads();
   };
-  // K is a multiple of 2 BK (checked by the launcher): both steps of an
-  // iteration always run, so no load is moved into a conditional block
-  for (int kt = 0; kt < ktiles; kt += 2) {
-    step(kt, Set0{});
-    step(kt + 1, Set1{});
+  // groups of six steps cover both periods (register set 2, LDS buffer 3); the
+  // loads and stores stay unconditional, which keeps the compiler's count of
+  // loads in flight exact
+  for (int kt = 0; kt < ktiles; kt += 6) {
+    step(kt, std::integral_constant<int, 0>{});
+    step(kt + 1, std::integral_constant<int, 1>{});
+    step(kt + 2, std::integral_constant<int, 2>{});
+    step(kt + 3, std::integral_constant<int, 3>{});
+    step(kt + 4, std::integral_constant<int, 4>{});
+    step(kt + 5, std::integral_constant<int, 5>{});
   }
 
   // Epilogue. Accumulator element e of lane l in block (i, j):
@@ -337,7 +366,7 @@ __global__ __launch_bounds__(512, 1) void gemm_kernel(const T* __restrict__ A, c
 
 template <typename T>
 static hipError_t launch_gemm(const GemmArgs& g, hipStream_t s) {
-  if (g.K <= 0 || g.K % (2 * GemmCfg<T>::BK) != 0) return hipErrorInvalidValue;  // K steps come in pairs
+  if (g.K <= 0 || g.K % GemmCfg<T>::BK != 0) return hipErrorInvalidValue;  // whole K tiles
   const bool sc = g.short_w != nullptr;
   const int mtiles = sc ? (g.M + kScRows - 1) / kScRows : (g.M + GBM - 1) / GBM;
   const int ntn = (g.N + GBN - 1) / GBN;
