@@ -802,22 +802,40 @@ __global__ __launch_bounds__(RowSeqCfg<N2>::T) void rowpass_seq_kernel(YT* __res
   RowTwLoad<N2, E, 1, 0>::run(tw, l, tw_row);
   const float nrm = 0.25f / (float)(N1 * N2);
 
+  // Each row is fetched one forward transform ahead, into one row's worth of
+  // registers: row b while row a is transformed, the next item's row a while
+  // row b is (the last item fetches itself again, so that the loads stay
+  // unconditional).
+  auto row_ptr = [&](int item, int h) {
+    const int pl = item / HALF, s = item - pl * HALF;
+    const int k1 = h ? (s == 0 ? HALF : N1 - s) : s;
+    return Y + ((size_t)pl * N1 + k1) * N2;
+  };
+  if ((int)blockIdx.x >= nitems) return;
+  YT rr[E];
+  {
+    const YT* Yr = row_ptr(blockIdx.x, 0);
+#pragma unroll
+    for (int q = 0; q < E; ++q) rr[q] = Yr[l + q * T];
+  }
   for (int item = blockIdx.x; item < nitems; item += gridDim.x) {
     const int pl = item / HALF, s = item - pl * HALF;
-    const int ka = s, kb = s == 0 ? HALF : N1 - s;
+    const int next = item + gridDim.x < nitems ? item + gridDim.x : item;
     float4* pqp = pq + ((size_t)pq_off + (pl + pair_off) % pq_mod) * PQROWS * N2;
-    YT* Ya = Y + ((size_t)pl * N1 + ka) * N2;
-    YT* Yb = Y + ((size_t)pl * N1 + kb) * N2;
+    YT* Ya = row_ptr(item, 0);
+    YT* Yb = row_ptr(item, 1);
     // forward DFTs, results to the row buffers in natural order (one row at a
     // time: a rolled loop, so that the two rows' work is not interleaved)
 #pragma unroll 1
     for (int h = 0; h < 2; ++h) {
       float2* bf = h ? B : A;
-      const YT* Yr = h ? Yb : Ya;
       float2* const bufs[2] = {bf, bf};
       float2 v[E];
 #pragma unroll
-      for (int q = 0; q < E; ++q) v[q] = cvt2(Yr[l + q * T]);
+      for (int q = 0; q < E; ++q) v[q] = cvt2(rr[q]);
+      const YT* Yn = h ? row_ptr(next, 0) : Yb;
+#pragma unroll
+      for (int q = 0; q < E; ++q) rr[q] = Yn[l + q * T];
       Fwd::run(v, bufs, l, tw);
       __syncthreads();  // the last stage's reads of bf are done
 #pragma unroll
