@@ -79,9 +79,146 @@ __global__ __launch_bounds__(256) void filter1d_mlp_kernel(Filter1DArgs a) {
   }
 }
 
+// The same MLP on the fp32 matrix cores (v_mfma_f32_32x32x2_f32, full fp32
+// products and sums), for FFN widths of 64 or 128. A workgroup (four waves)
+// takes 64 positions: the features, then each layer's activations, go to LDS
+// (two buffers: features then second layer in one, first layer in the other);
+// every layer is a [64 x K] x [K x cols] product in 32 x 32 blocks with the A
+// operand read from LDS. In the output layer a wave takes one 32-column block
+// (columns n D + c) for both 32-position halves at a time, with the whole
+// K x 32 slice of W3 in registers and the next block's slice in flight; the
+// block is windowed and written as 16-byte runs of positions.
+typedef __attribute__((ext_vector_type(16))) float f32x16;
+
+template <int WW>
+__global__ __launch_bounds__(256) void filter1d_mfma_kernel(Filter1DArgs a) {
+  constexpr int LDH = WW + 1;   // activation row stride (floats)
+  constexpr int KW = WW / 2;    // K steps of the hidden and output layers
+  __shared__ float buf0[kFT * (kMaxF + 2 > LDH ? kMaxF + 2 : LDH)];  // features, then layer 2
+  __shared__ float buf1[kFT * LDH];                                  // layer 1
+  const int t0 = blockIdx.x * kFT;
+  const int F = 1 + 2 * a.K, Fp = (F + 1) & ~1, L = a.L;
+  const int LDE = Fp + 1;  // feature row stride
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int r32 = lane & 31, k2 = lane >> 5;
+  for (int idx = tid; idx < kFT * Fp; idx += 256) {
+    const int tl = idx / Fp, f = idx % Fp;
+    const int t = t0 + tl;
+    float v = 0.f;
+    if (t < L && f < F) {
+      if (f == 0) {
+        v = (float)t / (float)L;
+      } else {
+        const int k = (f <= a.K) ? f : f - a.K;
+        // angle 2 pi k t / L reduced exactly: 2 pi m / L with m = (k t) mod L
+        const long long m = ((long long)k * t) % L;
+        float sv, cv;
+        sincospif(2.0f * (float)m / (float)L, &sv, &cv);
+        v = (f <= a.K) ? cv : sv;
+      }
+    }
+    buf0[tl * LDE + f] = v;
+  }
+  __syncthreads();
+  auto zero = [](f32x16& c) {
+#pragma unroll
+    for (int e = 0; e < 16; ++e) c[e] = 0.f;
+  };
+  // hidden layers: 2 x (WW / 32) blocks of 32 x 32 over the four waves
+  constexpr int NB = 2 * (WW / 32);
+  for (int blk = wave; blk < NB; blk += 4) {
+    const int rb = blk & 1, j = (blk >> 1) * 32 + r32;
+    f32x16 acc;
+    zero(acc);
+    // feature Fp - 1 (when F is odd) is zero; it meets weight row F - 1 again
+#pragma unroll 8
+    for (int k = 0; k < Fp; k += 2) {
+      const int f = k + k2;
+      acc = __builtin_amdgcn_mfma_f32_32x32x2f32(buf0[(rb * 32 + r32) * LDE + f],
+                                                 a.w1[(size_t)(f < F ? f : F - 1) * WW + j], acc, 0, 0, 0);
+    }
+    const float bj = a.b1[j];
+#pragma unroll
+    for (int e = 0; e < 16; ++e) buf1[(rb * 32 + (e >> 2) * 8 + k2 * 4 + (e & 3)) * LDH + j] = sinf(acc[e] + bj);
+  }
+  __syncthreads();
+  for (int blk = wave; blk < NB; blk += 4) {
+    const int rb = blk & 1, j = (blk >> 1) * 32 + r32;
+    f32x16 acc;
+    zero(acc);
+#pragma unroll
+    for (int k = 0; k < WW; k += 2)
+      acc = __builtin_amdgcn_mfma_f32_32x32x2f32(buf1[(rb * 32 + r32) * LDH + k + k2],
+                                                 a.w2[(size_t)(k + k2) * WW + j], acc, 0, 0, 0);
+    const float bj = a.b2[j];
+#pragma unroll
+    for (int e = 0; e < 16; ++e) buf0[(rb * 32 + (e >> 2) * 8 + k2 * 4 + (e & 3)) * LDH + j] = sinf(acc[e] + bj);
+  }
+  __syncthreads();
+  // output layer
+  const int ND = a.NO * a.D;
+  const int ncb = (ND + 31) / 32;
+  const float invL = 1.0f / (float)L;
+  float wv[KW];  // W3 rows k2, k2 + 2, ... of this lane's column
+  auto load_w3 = [&](int cb) {
+    const int col = cb * 32 + r32;
+    const float* w = a.w3 + (col < ND ? col : ND - 1) + (size_t)k2 * ND;
+#pragma unroll
+    for (int k = 0; k < KW; ++k) wv[k] = w[(size_t)(2 * k) * ND];
+  };
+  int cb = wave;
+  if (cb >= ncb) return;
+  load_w3(cb);
+  while (true) {
+    const int col = cb * 32 + r32;
+    const int colc = col < ND ? col : ND - 1;  // ragged last block: valid loads, no stores
+    f32x16 acc0, acc1;
+    zero(acc0);
+    zero(acc1);
+#pragma unroll
+    for (int k = 0; k < KW; ++k) {
+      acc0 = __builtin_amdgcn_mfma_f32_32x32x2f32(buf0[r32 * LDH + 2 * k + k2], wv[k], acc0, 0, 0, 0);
+      acc1 = __builtin_amdgcn_mfma_f32_32x32x2f32(buf0[(32 + r32) * LDH + 2 * k + k2], wv[k], acc1, 0, 0, 0);
+    }
+    const int nxt = cb + 4;
+    const bool more = nxt < ncb;
+    load_w3(more ? nxt : cb);  // the next block's slice (this one's again after the last: unused)
+    const float bias = a.b3[colc];
+    const float dc = a.decay[colc % a.D];
+    float* dst = a.h + (size_t)colc * L;  // h[n][c][t] with col = n D + c
+#pragma unroll
+    for (int rb = 0; rb < 2; ++rb) {
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const int t = t0 + rb * 32 + g * 8 + k2 * 4;  // four consecutive positions
+        float o[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          o[i] = ((rb ? acc1[4 * g + i] : acc0[4 * g + i]) + bias) * expf(-dc * (float)(t + i) * invL);
+        if (col < ND) {
+          if (t + 3 < L && (L & 3) == 0) {
+            *reinterpret_cast<float4*>(dst + t) = make_float4(o[0], o[1], o[2], o[3]);
+          } else {
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+              if (t + i < L) dst[t + i] = o[i];
+          }
+        }
+      }
+    }
+    if (!more) break;
+    cb = nxt;
+  }
+}
+
 hipError_t filter1d_mlp(const Filter1DArgs& a, hipStream_t s) {
   dim3 grid((a.L + kFT - 1) / kFT), block(256);
-  hipLaunchKernelGGL(filter1d_mlp_kernel, grid, block, 0, s, a);
+  if (a.W == 64 && 1 + 2 * a.K <= kMaxF)
+    hipLaunchKernelGGL(filter1d_mfma_kernel<64>, grid, block, 0, s, a);
+  else if (a.W == 128 && 1 + 2 * a.K <= kMaxF)
+    hipLaunchKernelGGL(filter1d_mfma_kernel<128>, grid, block, 0, s, a);
+  else
+    hipLaunchKernelGGL(filter1d_mlp_kernel, grid, block, 0, s, a);
   return hipGetLastError();
 }
 
