@@ -3,6 +3,9 @@
 
     python bench.py [--steps K] [--warmup W] [--workload NAME] [--no-cpu-baseline]
 
+The default workload is the 1D operator at B=1, L=64k, D=768, bf16; the 3D
+workload (--workload nd3d_f32_B2_C128_64cube) times hyena_nd_fwd the same way.
+
 One step = one hyena_fwd call (in-projection, short convolutions, all orders of
 long FFT convolution with gating and skip, out-projection) over one batch of
 synthetic input already resident in HBM. The implicit filters are generated and
@@ -36,6 +39,7 @@ DEFAULT_WORKLOAD = "order2_bf16_L64k_D768"
 # Kernel sources of the long-convolution stage; a traffic figure measured on other
 # sources is stale and is not reported.
 CONV_SOURCES = ["fft1d.hip", "common.h", "kernels.h"]
+ND_CONV_SOURCES = ["nd.hip", "common.h", "kernels.h"]
 METRIC = "Hyena fwd tokens/sec at L=64k,D=768 (1 GPU); FFT-conv HBM GB/s % of peak"
 HBM_PEAK_GBS = 8000.0
 MFMA_BF16_PEAK_TFLOPS = 2516.6  # 256 CUs x 2.4 GHz x 4096 flop/clk (dense)
@@ -57,16 +61,20 @@ def conv_alg_bytes(B, L, D, N, s, lds_regime: bool) -> float:
     return N * (3.0 * B * L * D * s + 8.0 * D * (L + 1))
 
 
-def conv_source_hash() -> str:
+def conv_source_hash(sources=None) -> str:
     import hashlib
     hsh = hashlib.sha256()
-    for name in CONV_SOURCES:
+    for name in sources or CONV_SOURCES:
         with open(os.path.join(ROOT, "subquadratic_sequence_amd", "csrc", name), "rb") as fh:
             hsh.update(fh.read())
     return hsh.hexdigest()
 
 
-def _profile_values(path: str):
+def _sources_of(workload: str):
+    return ND_CONV_SOURCES if workload.startswith("nd") else CONV_SOURCES
+
+
+def _profile_values(path: str, sources=None):
     """The '@key: value' lines of a profile summary, or None if the file is missing
     or was measured on other kernel sources."""
     if not os.path.exists(path):
@@ -77,7 +85,7 @@ def _profile_values(path: str):
             if line.startswith("@") and ":" in line:
                 k, v = line[1:].split(":", 1)
                 kv[k.strip()] = v.strip()
-    if kv.get("conv_source_sha256") != conv_source_hash():
+    if kv.get("conv_source_sha256") != conv_source_hash(sources):
         return None
     return kv
 
@@ -87,7 +95,7 @@ def measured_traffic(workload: str, path: str | None = None):
     FETCH_SIZE / WRITE_SIZE summary under profiles/ (each counter scaled by what it
     reads for a plain copy of known size). None if there is no summary for this
     workload or the kernel sources changed since it was taken."""
-    kv = _profile_values(path or os.path.join(ROOT, "profiles", f"hbm_traffic_{workload}.txt"))
+    kv = _profile_values(path or os.path.join(ROOT, "profiles", f"hbm_traffic_{workload}.txt"), _sources_of(workload))
     return None if kv is None else float(kv["conv_stage_bytes_per_step"])
 
 
@@ -95,7 +103,7 @@ def measured_valu(workload: str, path: str | None = None):
     """(VALU wave instructions, fp32 VALU FLOPs) per step of the long-convolution
     stage, from the rocprofv3 SQ counter summary under profiles/; None as for
     measured_traffic."""
-    kv = _profile_values(path or os.path.join(ROOT, "profiles", f"valu_mfma_{workload}.txt"))
+    kv = _profile_values(path or os.path.join(ROOT, "profiles", f"valu_mfma_{workload}.txt"), _sources_of(workload))
     if kv is None:
         return None
     return float(kv["conv_valu_instr_per_step"]), float(kv["conv_valu_flops_per_step"])
@@ -136,6 +144,121 @@ def cpu_baseline(inp, budget_tokens: int):
                       f"FFT path, 1 thread, {dt:.1f} s"}
 
 
+def nd_conv_alg_bytes(B, X, Y, Z, C, N) -> float:
+    """Per call: each order reads z^n and x^n and writes z^{n+1} (fp32 [B][C][X][Y][Z])
+    and reads the channel's half spectrum (complex fp32, (2X)(2Y)(Z+1) bins)."""
+    V = X * Y * Z
+    return N * (3.0 * B * C * V * 4 + 8.0 * C * (2 * X) * (2 * Y) * (Z + 1))
+
+
+def cpu_baseline_nd(inp, channels: int):
+    """fp64 oracle forward on one sample and the first `channels` channels (the
+    projections restricted to them), full grid, 1 thread, the kernel generated
+    before the timed region (as the GPU step uses a cached spectrum); voxel rate
+    scaled by channels / C."""
+    import oracle
+    from threadpoolctl import threadpool_limits
+    c = min(channels, inp.C)
+    N = inp.N
+    blocks = [inp.w_in[:c, j * inp.C:j * inp.C + c] for j in range(N + 1)]
+    w_in = np.concatenate(blocks, axis=1)
+    params = dict(inp.filter_params)
+    params["w3"] = np.concatenate([params["w3"][:, n * inp.C:n * inp.C + c] for n in range(N)], axis=1)
+    params["b3"] = np.concatenate([params["b3"][n * inp.C:n * inp.C + c] for n in range(N)])
+    params["decay"] = params["decay"][:c]
+    with threadpool_limits(limits=1):
+        K = oracle.nd_filter(params, inp.X, inp.Y, inp.Z, N, c)  # the layer's kernel: outside the step
+        t0 = time.perf_counter()
+        oracle.hyena_nd_fwd(inp.u[:1, ..., :c], w_in, inp.dskip[:, :c], inp.gate_a[:, :c], inp.gate_b[:, :c],
+                            inp.w_out[:c, :c], K, conv="fft")
+        dt = time.perf_counter() - t0
+    V = inp.X * inp.Y * inp.Z
+    return {"value": V / dt * c / inp.C, "unit": "voxels/s", "cores": 1, "kind": "oracle",
+            "sample": f"sample 0 of {inp.B}, channels 0..{c - 1} of {inp.C} (projections restricted to them), "
+                      f"full {inp.X}x{inp.Y}x{inp.Z} grid, fp64 numpy, FFT path (kernel generated beforehand), "
+                      f"1 thread, {dt:.1f} s; rate scaled by {c}/{inp.C}"}
+
+
+def main_nd(args, torch, hs, make_config):
+    log(f"generating inputs for {args.workload}")
+    inp = make_config(args.workload)
+    B, X, Y, Z, C, N = inp.B, inp.X, inp.Y, inp.Z, inp.C, inp.N
+    V = X * Y * Z
+    f = lambda a: torch.from_numpy(np.ascontiguousarray(a, np.float32)).to("cuda")  # noqa: E731
+    layer = hs.HyenaNDLayer(X, Y, Z, C, N)
+    fargs = [f(a) for a in (inp.w1, inp.b1, inp.w2, inp.b2, inp.w3, inp.b3, inp.decay)]
+    hs.hyena_nd_filter_gen(layer, *fargs)
+    u, w_in, dskip, ga, gb, w_out = (f(a) for a in (inp.u, inp.w_in, inp.dskip, inp.gate_a, inp.gate_b, inp.w_out))
+    y = torch.empty_like(u)
+    ws = torch.empty(hs.hyena_nd_workspace_bytes(B, X, Y, Z, C, N), dtype=torch.uint8, device="cuda")
+    torch.cuda.synchronize()
+    log(f"warmup {args.warmup}")
+    for _ in range(args.warmup):
+        hs.hyena_nd_fwd(layer, u, w_in, dskip, ga, gb, w_out, y=y, ws=ws)
+    torch.cuda.synchronize()
+    events = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
+    for evs in events:
+        for ev in evs:
+            ev.record()
+    torch.cuda.synchronize()
+    log(f"timing {args.steps} steps")
+    t0 = time.perf_counter()
+    for k in range(args.steps):
+        hs.hyena_nd_fwd_profiled(layer, u, w_in, dskip, ga, gb, w_out, y, ws, events[k])
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    stages = np.mean([[evs[i].elapsed_time(evs[i + 1]) for i in range(3)] for evs in events], axis=0)
+    step_ms = np.array([evs[0].elapsed_time(evs[3]) for evs in events])
+    log(f"stages ms: in-proj {stages[0]:.4f} conv {stages[1]:.4f} out-proj {stages[2]:.4f}")
+    f0, f1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    f0.record()
+    hs.hyena_nd_filter_gen(layer, *fargs)
+    f1.record()
+    torch.cuda.synchronize()
+    alg = nd_conv_alg_bytes(B, X, Y, Z, C, N)
+    achieved = alg / (stages[1] * 1e-3) / 1e9
+    proj = {}
+    for name, n_out, ms in (("in_proj", (N + 1) * C, stages[0]), ("out_proj", C, stages[2])):
+        tf = 2.0 * B * V * n_out * C / (ms * 1e-3) / 1e12
+        proj[name] = {"tflops": tf, "peak": MFMA_F32_PEAK_TFLOPS, "frac": tf / MFMA_F32_PEAK_TFLOPS}
+    valu = measured_valu(args.workload)
+    conv_valu = None
+    if valu is not None:
+        gi = valu[0] / (stages[1] * 1e-3) / 1e9
+        tf = valu[1] / (stages[1] * 1e-3) / 1e12
+        conv_valu = {"bound": "alu", "achieved": gi, "peak": VALU_PEAK_GINSTR, "unit": "G wave-instr/s",
+                     "frac": gi / VALU_PEAK_GINSTR, "fp32_tflops": tf, "fp32_peak_tflops": VALU_F32_PEAK_TFLOPS}
+    out = {
+        "metric": "HyenaND fwd voxels/sec (3D, B=2, C=128, 64^3, 1 GPU); 3D FFT-conv HBM GB/s % of peak",
+        "value": B * V * args.steps / elapsed,
+        "unit": "voxels/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": 1e3 * elapsed / args.steps,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {"workload": args.workload, "B": B, "X": X, "Y": Y, "Z": Z, "C": C, "N": N},
+        "stage_ms": {"in_proj": stages[0], "fft_conv": stages[1], "out_proj": stages[2]},
+        "step_ms_events": {"p10": float(np.percentile(step_ms, 10)), "p50": float(np.median(step_ms)),
+                           "p90": float(np.percentile(step_ms, 90))},
+        "filter_gen_ms": f0.elapsed_time(f1),
+        "roofline": {"bound": "hbm", "kernel": "3D fft_conv stage (all orders)", "achieved": achieved,
+                     "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS, "alg_bytes": alg,
+                     "traffic": measured_traffic(args.workload)},
+        "conv_valu": conv_valu,
+        "projections_mfma": proj,
+        "copy_probe_gbs": copy_probe(torch),
+    }
+    if not args.no_cpu_baseline:
+        log("cpu baseline (oracle)")
+        out["cpu_baseline"] = cpu_baseline_nd(inp, args.cpu_channels)
+    print(json.dumps(out), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -144,6 +267,7 @@ def main():
     ap.add_argument("--workload", default=DEFAULT_WORKLOAD)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-tokens", type=int, default=16384)
+    ap.add_argument("--cpu-channels", type=int, default=8, help="channels of the 3D oracle sample")
     ap.add_argument("--calib-copy", type=int, default=0, metavar="MIB",
                     help="only run a plain device copy of MIB MiB (reads and writes MIB MiB), for calibrating "
                          "the FETCH_SIZE / WRITE_SIZE counters, and exit")
@@ -168,8 +292,8 @@ def main():
         return
 
     cfg = CONFIGS[args.workload]
-    if cfg["kind"] != "1d":
-        raise SystemExit("bench.py times the 1D operator workloads")
+    if cfg["kind"] == "nd":
+        return main_nd(args, torch, hs, make_config)
     log(f"generating inputs for {args.workload}")
     inp = make_config(args.workload)
     B, L, D, N = inp.B, inp.L, inp.D, inp.N

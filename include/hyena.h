@@ -169,6 +169,19 @@ int hyena_nd_fwd(const hyena_nd_layer *layer, const float *u, const float *w_in,
                  const float *w_out, int B, float *y, void *ws, size_t ws_bytes,
                  hipStream_t stream);
 
+/* Same launches as hyena_nd_fwd, plus hipEventRecord(events[i], stream) at the four
+ * stage boundaries, for timing the stages on the launch stream:
+ *   events[0] before the channel means and gates,
+ *   events[1] after the in-projection (gates, weight transposes, GEMM),
+ *   events[2] after the 3D FFT convolutions with gating (all orders),
+ *   events[3] after the out-projection.
+ * events: host array of 4 events the caller created (and destroys); nothing here
+ * synchronises. A null `events` is HYENA_ERR_INVALID_ARG. */
+int hyena_nd_fwd_profiled(const hyena_nd_layer *layer, const float *u, const float *w_in,
+                          const float *dskip, const float *gate_a, const float *gate_b,
+                          const float *w_out, int B, float *y, void *ws, size_t ws_bytes,
+                          hipStream_t stream, const hipEvent_t *events);
+
 #ifdef __cplusplus
 }
 #endif

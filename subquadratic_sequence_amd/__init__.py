@@ -20,6 +20,7 @@ from .hyena import (  # noqa: F401
     hyena_nd_filter_gen,
     hyena_nd_filter_workspace_bytes,
     hyena_nd_fwd,
+    hyena_nd_fwd_profiled,
     hyena_nd_workspace_bytes,
     hyena_workspace_bytes,
     lib,

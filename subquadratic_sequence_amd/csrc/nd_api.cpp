@@ -153,9 +153,13 @@ int hyena_nd_filter_gen(hyena_nd_layer* layer, const hyena_nd_filter_params* p, 
   return HYENA_OK;
 }
 
-int hyena_nd_fwd(const hyena_nd_layer* layer, const float* u, const float* w_in, const float* dskip,
-                 const float* gate_a, const float* gate_b, const float* w_out, int B, float* y, void* ws,
-                 size_t ws_bytes, hipStream_t stream) {
+}  // extern "C"
+
+namespace {
+
+int nd_fwd_impl(const hyena_nd_layer* layer, const float* u, const float* w_in, const float* dskip,
+                const float* gate_a, const float* gate_b, const float* w_out, int B, float* y, void* ws,
+                size_t ws_bytes, hipStream_t stream, const hipEvent_t* ev) {
   if (layer == nullptr) return HYENA_ERR_INVALID_ARG;
   const void* ptrs[] = {u, w_in, dskip, gate_a, gate_b, w_out, y, ws};
   for (const void* q : ptrs)
@@ -180,11 +184,13 @@ int hyena_nd_fwd(const hyena_nd_layer* layer, const float* u, const float* w_in,
   float* zfin = reinterpret_cast<float*>(wsb + w.zfinal);
   float* gate = reinterpret_cast<float*>(wsb + w.gate);
 
+  if (ev) HY_CHECK_HIP(hipEventRecord(ev[0], stream));
   HY_CHECK_HIP(hy::nd_gate(u, reinterpret_cast<float*>(wsb + w.part), gate_a, gate_b, gate, B, N, C, V, stream));
   HY_CHECK_HIP(hy::transpose2d(w_in, wt_in, C, J, false, stream));
   HY_CHECK_HIP(hy::transpose2d(w_out, wt_out, C, C, false, stream));
   hy::GemmArgs gi{u, wt_in, pbuf, B * V, J, C, V, false, true, nullptr};
   HY_CHECK_HIP(hy::gemm(gi, false, stream));
+  if (ev) HY_CHECK_HIP(hipEventRecord(ev[1], stream));
   hy::NdConvArgs a{};
   a.X = X;
   a.Y = Y;
@@ -202,9 +208,28 @@ int hyena_nd_fwd(const hyena_nd_layer* layer, const float* u, const float* w_in,
   a.kh = reinterpret_cast<const float2*>(cb + cl.kh);
   a.tw128 = reinterpret_cast<const float2*>(cb + cl.tw);
   HY_CHECK_HIP(hy::nd_conv(a, stream));
+  if (ev) HY_CHECK_HIP(hipEventRecord(ev[2], stream));
   hy::GemmArgs go{zfin, wt_out, y, B * V, C, C, V, true, false, nullptr};
   HY_CHECK_HIP(hy::gemm(go, false, stream));
+  if (ev) HY_CHECK_HIP(hipEventRecord(ev[3], stream));
   return HYENA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int hyena_nd_fwd(const hyena_nd_layer* layer, const float* u, const float* w_in, const float* dskip,
+                 const float* gate_a, const float* gate_b, const float* w_out, int B, float* y, void* ws,
+                 size_t ws_bytes, hipStream_t stream) {
+  return nd_fwd_impl(layer, u, w_in, dskip, gate_a, gate_b, w_out, B, y, ws, ws_bytes, stream, nullptr);
+}
+
+int hyena_nd_fwd_profiled(const hyena_nd_layer* layer, const float* u, const float* w_in, const float* dskip,
+                          const float* gate_a, const float* gate_b, const float* w_out, int B, float* y, void* ws,
+                          size_t ws_bytes, hipStream_t stream, const hipEvent_t* events) {
+  if (events == nullptr) return HYENA_ERR_INVALID_ARG;
+  return nd_fwd_impl(layer, u, w_in, dskip, gate_a, gate_b, w_out, B, y, ws, ws_bytes, stream, events);
 }
 
 }  // extern "C"

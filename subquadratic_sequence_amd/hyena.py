@@ -60,6 +60,8 @@ SIGNATURES = {
     "hyena_nd_layer_init": (_i, [ctypes.POINTER(NDLayer), _i, _i, _i, _i, _i, _vp, _sz]),
     "hyena_nd_filter_gen": (_i, [ctypes.POINTER(NDLayer), ctypes.POINTER(NDFilterParams), _vp, _vp, _sz, _vp]),
     "hyena_nd_fwd": (_i, [ctypes.POINTER(NDLayer), _vp, _vp, _vp, _vp, _vp, _vp, _i, _vp, _vp, _sz, _vp]),
+    "hyena_nd_fwd_profiled": (_i, [ctypes.POINTER(NDLayer), _vp, _vp, _vp, _vp, _vp, _vp, _i, _vp, _vp, _sz, _vp,
+                                   ctypes.POINTER(_vp)]),
 }
 
 _lib = None
@@ -235,3 +237,20 @@ def hyena_nd_fwd(layer: HyenaNDLayer, u, w_in, dskip, gate_a, gate_b, w_out, y=N
                             _ptr(w_out), B, _ptr(y), _ptr(ws), ws.numel(), _stream())
     _check(st, "hyena_nd_fwd")
     return y
+
+
+def hyena_nd_fwd_profiled(layer: HyenaNDLayer, u, w_in, dskip, gate_a, gate_b, w_out, y, ws, events):
+    """hyena_nd_fwd that also records four torch.cuda.Event (enable_timing=True) at the
+    stage boundaries on the current stream: before the gates, after the
+    in-projection, after the 3D convolutions, after the out-projection. Does not
+    synchronise."""
+    B = u.shape[0]
+    if len(events) != 4:
+        raise ValueError("hyena_nd_fwd_profiled takes 4 events")
+    for ev in events:
+        if not ev.cuda_event:  # torch creates the HIP event on its first record
+            ev.record()
+    handles = (_vp * 4)(*[ev.cuda_event for ev in events])
+    st = lib().hyena_nd_fwd_profiled(ctypes.byref(layer.c), _ptr(u), _ptr(w_in), _ptr(dskip), _ptr(gate_a),
+                                     _ptr(gate_b), _ptr(w_out), B, _ptr(y), _ptr(ws), ws.numel(), _stream(), handles)
+    _check(st, "hyena_nd_fwd_profiled")

@@ -115,6 +115,18 @@ def test_fwd_validation_before_any_hip_call(hy):
     assert L.hyena_fwd(ctypes.byref(layer), *args, 1, 0, p, p, ws_need, None) == 4
 
 
+def test_profiled_entry_points_need_events(hy):
+    L = hy.lib()
+    keep, p = _aligned_buffer(16)
+    layer = hy.Layer()
+    assert L.hyena_layer_init(ctypes.byref(layer), 1024, 64, 2, p, 1 << 30) == 0
+    layer.built = 1
+    ws_need = hy.hyena_workspace_bytes(1, 1024, 64, 2, 0)
+    assert L.hyena_fwd_profiled(ctypes.byref(layer), p, p, p, p, p, 1, 0, p, p, ws_need, None, None) == 1
+    nd = hy.NDLayer()
+    assert L.hyena_nd_fwd_profiled(ctypes.byref(nd), p, p, p, p, p, p, 1, p, p, 1 << 30, None, None) == 1
+
+
 def test_valid_call_without_device_reports_hip_error(hy):
     import torch
     if torch.cuda.is_available():
