@@ -117,7 +117,9 @@ __global__ void nd_split_kernel(const float2* __restrict__ F, float2* __restrict
 // ================================================ FFT along LDS lines
 // M-point Stockham FFT of the line buf[base + i*stride], i in [0, M), by M/E
 // threads (lt); every thread of the workgroup calls it (barriers), `active`
-// selects the ones that own a line. tw128[m] = W_128^m.
+// selects the ones that own a line. tw128[m] = W_128^m, a copy in LDS (a table
+// lookup from global memory inside a stage would make the stage wait for every
+// load issued before it).
 template <int M, int E, int Ns, bool INV>
 __device__ __forceinline__ void line_stage(float2* buf, int base, int stride, int lt, bool active,
                                            const float2* __restrict__ tw128) {
@@ -176,7 +178,7 @@ template <int M> struct PlaneCfg {
   static constexpr int T = M / E;       // threads per line
   static constexpr int RS = M + 1;      // LDS row stride
   static constexpr int THREADS = 1024;
-  static constexpr size_t LDS = (size_t)M * RS * 8;
+  static constexpr size_t LDS = (size_t)M * RS * 8 + 128 * 8;  // plane + W_128 table
 };
 
 template <int M, bool INV>
@@ -201,6 +203,7 @@ __global__ __launch_bounds__(1024) void nd_plane_kernel(NdConvArgs a) {
   using C = PlaneCfg<M>;
   extern __shared__ float4 smem4[];
   float2* P = reinterpret_cast<float2*>(smem4);
+  float2* tw = P + M * C::RS;  // W_128^m, m < 128
   const int X = a.X, Y = a.Y, Z = a.Z;
   const size_t V = (size_t)X * Y * Z;
   const size_t plane = (size_t)M * M;
@@ -208,14 +211,15 @@ __global__ __launch_bounds__(1024) void nd_plane_kernel(NdConvArgs a) {
   const int c = blockIdx.y;          // channel (or filter pair)
   const int bp = blockIdx.z;         // sample pair (or order of the filter)
   const int tid = threadIdx.x;
+  if (tid < 128) tw[tid] = a.tw128[tid];  // visible after the barrier that follows the plane load
 
   if constexpr (MODE == PL_FWD_FULL) {
     // filter: full M x M complex plane, all 2X planes
     float2* Fp = a.F + (((size_t)bp * a.npairs + c) * (2 * X) + x) * plane;
     for (int i = tid; i < M * M; i += C::THREADS) P[(i / M) * C::RS + i % M] = Fp[i];
     __syncthreads();
-    plane_rows<M, false>(P, M, a.tw128);
-    plane_cols<M, false>(P, a.tw128);
+    plane_rows<M, false>(P, M, tw);
+    plane_cols<M, false>(P, tw);
     for (int i = tid; i < M * M; i += C::THREADS) Fp[i] = P[(i / M) * C::RS + i % M];
     return;
   }
@@ -242,8 +246,8 @@ __global__ __launch_bounds__(1024) void nd_plane_kernel(NdConvArgs a) {
   } else {
     for (int i = tid; i < M * M; i += C::THREADS) P[(i / M) * C::RS + i % M] = Yp[i];
     __syncthreads();
-    plane_cols<M, true>(P, a.tw128);
-    plane_rows<M, true>(P, Y, a.tw128);
+    plane_cols<M, true>(P, tw);
+    plane_rows<M, true>(P, Y, tw);
     // gate and skip on the kept Y x Z block
     const int n = a.n;
     const float* x0 = s0 + (size_t)((n + 1) * CC + c) * V + xoff;
@@ -277,8 +281,8 @@ __global__ __launch_bounds__(1024) void nd_plane_kernel(NdConvArgs a) {
     __syncthreads();
   }
   // forward plane DFT of the (zero padded) Y x Z block
-  plane_rows<M, false>(P, Y, a.tw128);
-  plane_cols<M, false>(P, a.tw128);
+  plane_rows<M, false>(P, Y, tw);
+  plane_cols<M, false>(P, tw);
   for (int i = tid; i < M * M; i += C::THREADS) Yp[i] = P[(i / M) * C::RS + i % M];
 }
 
@@ -362,6 +366,125 @@ __global__ __launch_bounds__(64 * RA) void nd_pencil_kernel(NdConvArgs a) {
   Dft<RB, true>::run(q);
 #pragma unroll
   for (int nb = 0; nb < RB / 2; ++nb) base[(size_t)(w + RA * nb) * plane + f] = q[nb];
+}
+
+// Persistent pencil pass for 2X = 128 (the 64^3 grids), conv mode: items are
+// (sample pair, channel, block of 64 pencils) walked with a stride of
+// gridDim.x by 512-thread workgroups (8 waves, two workgroups per CU). Same
+// decomposition as nd_pencil_kernel (n1 = j + 16 r, k1 = ka + 8 kb), with every
+// wave busy in both stages: stage 1 (x -> r) runs the DFT-8s of j = w and
+// j = w + 8, stage 2 the DFT-16 of ka = w. Each item's input column and
+// kernel spectrum entries are in registers when it starts: the next item's are
+// fetched as soon as the current one has used them (the last item fetches
+// itself again, so that the loads stay unconditional).
+__global__ __launch_bounds__(512) void nd_pencil128_kernel(NdConvArgs a, int nitems) {
+  constexpr int N1 = 128, RA = 16, RB = 8;
+  extern __shared__ float4 smem4[];
+  float2* S = reinterpret_cast<float2*>(smem4);  // [RA][RB][64] forward, [RB][RA][64] inverse
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const int X = a.X, Y = a.Y, Z = a.Z;
+  const int MY = 2 * Y, MZ = 2 * Z, ZH = Z + 1;
+  const size_t plane = (size_t)MY * MZ;
+  const int nfb = MY * MZ / 64;  // pencil blocks per channel
+  struct Item {
+    float2* base;        // Yint of (pair, channel), plane 0
+    const float2* Kc;    // half spectrum of (order, channel)
+    int f;               // this lane's pencil (ky, kz) = (f / MZ, f % MZ)
+  };
+  auto item_of = [&](int item) {
+    Item it;
+    const int fb = item % nfb, pc = item / nfb;  // pc = bp * C + c
+    const int c = pc % a.C;
+    it.base = a.Yint + (size_t)pc * X * plane;
+    it.Kc = a.kh + (size_t)(a.n * a.C + c) * N1 * MY * ZH;
+    it.f = fb * 64 + lane;
+    return it;
+  };
+  struct In {
+    float2 y[2][RB / 2];  // x = j + 16 r, j in {w, w + 8}, r < 4 (x < X = 64)
+    float2 k[RA];         // K^(kx = w + 8 kb, ky, kz), conjugated where taken from -k
+  };
+  auto load_y = [&](const Item& it, In& in) {
+#pragma unroll
+    for (int jj = 0; jj < 2; ++jj)
+#pragma unroll
+      for (int r = 0; r < RB / 2; ++r) in.y[jj][r] = it.base[(size_t)(w + 8 * jj + RA * r) * plane + it.f];
+  };
+  auto load_k = [&](const Item& it, In& in) {
+    const int ky = it.f / MZ, kz = it.f % MZ;
+    const bool lower = kz <= Z;
+    const int ky2 = lower ? ky : (MY - ky) % MY;
+    const int kz2 = lower ? kz : MZ - kz;
+#pragma unroll
+    for (int kb = 0; kb < RA; ++kb) {
+      const int kx = w + RB * kb;
+      const int kx2 = lower ? kx : (N1 - kx) % N1;
+      const float2 kv = it.Kc[((size_t)kx2 * MY + ky2) * ZH + kz2];
+      in.k[kb] = lower ? kv : conjf2(kv);
+    }
+  };
+
+  int item = blockIdx.x;
+  if (item >= nitems) return;
+  In in;
+  {
+    const Item it = item_of(item);
+    load_y(it, in);
+    load_k(it, in);
+  }
+  while (true) {
+    const int next = item + gridDim.x;
+    const bool more = next < nitems;
+    const Item it = item_of(item), nt = item_of(more ? next : item);
+    // forward stage 1: DFT-8 over r of j = w and w + 8, inner twiddles W_128^(j ka)
+    float2 v[2][RB];
+#pragma unroll
+    for (int jj = 0; jj < 2; ++jj)
+#pragma unroll
+      for (int r = 0; r < RB; ++r) v[jj][r] = r < RB / 2 ? in.y[jj][r] : make_float2(0.f, 0.f);
+    load_y(nt, in);
+#pragma unroll
+    for (int jj = 0; jj < 2; ++jj) {
+      const int j = w + 8 * jj;
+      Dft<RB, false>::run(v[jj]);
+#pragma unroll
+      for (int ka = 0; ka < RB; ++ka) {
+        if (ka) v[jj][ka] = cmul(v[jj][ka], a.tw128[(j * ka) & 127]);
+        S[(j * RB + ka) * 64 + lane] = v[jj][ka];
+      }
+    }
+    __syncthreads();
+    // stage 2: DFT-16 over j for ka = w: X[w + 8 kb]
+    float2 u[RA];
+#pragma unroll
+    for (int j = 0; j < RA; ++j) u[j] = S[(j * RB + w) * 64 + lane];
+    Dft<RA, false>::run(u);
+#pragma unroll
+    for (int kb = 0; kb < RA; ++kb) u[kb] = cmul(u[kb], in.k[kb]);
+    load_k(nt, in);
+    // inverse stage 2 on the same threads, then the inner twiddles
+    Dft<RA, true>::run(u);
+#pragma unroll
+    for (int na = 1; na < RA; ++na) u[na] = cmulc(u[na], a.tw128[(w * na) & 127]);
+    __syncthreads();  // everyone finished reading S
+#pragma unroll
+    for (int na = 0; na < RA; ++na) S[(w * RA + na) * 64 + lane] = u[na];
+    __syncthreads();
+    // inverse stage 1: DFT-8 over ka for na = w and w + 8 -> x = na + 16 nb, nb < 4
+#pragma unroll
+    for (int jj = 0; jj < 2; ++jj) {
+      const int na = w + 8 * jj;
+      float2 q[RB];
+#pragma unroll
+      for (int ka = 0; ka < RB; ++ka) q[ka] = S[(ka * RA + na) * 64 + lane];
+      Dft<RB, true>::run(q);
+#pragma unroll
+      for (int nb = 0; nb < RB / 2; ++nb) it.base[(size_t)(na + RA * nb) * plane + it.f] = q[nb];
+    }
+    if (!more) break;
+    item = next;
+    __syncthreads();  // S of this item fully read before the next one writes it
+  }
 }
 
 // ========================================================= channel mean
@@ -480,6 +603,24 @@ hipError_t nd_gate(const float* u, float* part, const float* ga, const float* gb
 
 size_t nd_gate_partial_floats(int B, int C, int V) { return (size_t)B * (V < 512 ? V : 512) * C; }
 
+static hipError_t launch_pencil128(const NdConvArgs& a, int nitems, hipStream_t s) {
+  const size_t lds = (size_t)16 * 8 * 64 * 8;
+  auto fn = nd_pencil128_kernel;
+  hipError_t e = nd_allow_lds((const void*)fn, lds);
+  if (e != hipSuccess) return e;
+  static int grid = 0;
+  if (grid == 0) {
+    int cus = 0, dev = 0, per_cu = 0;
+    if (hipGetDevice(&dev) != hipSuccess ||
+        hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0)
+      cus = 256;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, fn, 512, lds) != hipSuccess || per_cu <= 0) per_cu = 1;
+    grid = cus * per_cu;
+  }
+  hipLaunchKernelGGL(fn, dim3(grid < nitems ? grid : nitems), dim3(512), lds, s, a, nitems);
+  return hipGetLastError();
+}
+
 hipError_t nd_conv(const NdConvArgs& in, hipStream_t s) {
   NdConvArgs a = in;
   const int BP = (a.B + 1) / 2;
@@ -488,7 +629,12 @@ hipError_t nd_conv(const NdConvArgs& in, hipStream_t s) {
   if (e != hipSuccess) return e;
   for (int n = 0; n < a.NO; ++n) {
     a.n = n;
-    if ((e = launch_pencil<PN_CONV>(a, dim3(nf, a.C, BP), s)) != hipSuccess) return e;
+    if (2 * a.X == 128) {
+      e = launch_pencil128(a, (int)(nf * a.C * BP), s);
+    } else {
+      e = launch_pencil<PN_CONV>(a, dim3(nf, a.C, BP), s);
+    }
+    if (e != hipSuccess) return e;
     a.zin = (n == 0) ? nullptr : in.zbuf[(n - 1) & 1];
     a.zout = (n == a.NO - 1) ? in.zfinal : in.zbuf[n & 1];
     if (n == a.NO - 1)
