@@ -286,6 +286,157 @@ __global__ __launch_bounds__(1024) void nd_plane_kernel(NdConvArgs a) {
   for (int i = tid; i < M * M; i += C::THREADS) Yp[i] = P[(i / M) * C::RS + i % M];
 }
 
+// Persistent plane pass for M = 128 (the 64^3 grids): items (sample pair,
+// channel, x-plane) walked with a stride of gridDim.x, one 1024-thread
+// workgroup per CU (the padded plane takes 133 KB of LDS). The next item's
+// input (its intermediate plane, or its v block in the first forward) is
+// fetched into registers while the current one is transformed, and the gate
+// and skip inputs between the column and the row stages of the inverse.
+template <int MODE>
+__global__ __launch_bounds__(1024) void nd_plane128_kernel(NdConvArgs a, int nitems) {
+  constexpr int M = 128;
+  using C = PlaneCfg<M>;
+  constexpr int PER = M * M / C::THREADS;          // plane elements per thread (16)
+  constexpr int KEPT = M * M / 4 / C::THREADS;     // kept (y < Y, z < Z) positions per thread (4)
+  constexpr bool INV = MODE != PL_FWD_V;
+  extern __shared__ float4 smem4[];
+  float2* P = reinterpret_cast<float2*>(smem4);
+  float2* tw = P + M * C::RS;
+  const int X = a.X, Y = a.Y, Z = a.Z;  // Y = Z = 64
+  const size_t V = (size_t)X * Y * Z;
+  const size_t plane = (size_t)M * M;
+  const int tid = threadIdx.x;
+  if (tid < 128) tw[tid] = a.tw128[tid];
+  const int CC = a.C;
+  const size_t J = (size_t)(a.NO + 1) * CC;
+  struct Item {
+    int x, c, bp, b0, b1;
+    bool has_b1;
+  };
+  auto item_of = [&](int item) {
+    Item it;
+    it.x = item % X;
+    const int pc = item / X;
+    it.c = pc % CC;
+    it.bp = pc / CC;
+    it.b0 = 2 * it.bp;
+    it.has_b1 = it.b0 + 1 < a.B;
+    it.b1 = it.has_b1 ? it.b0 + 1 : it.b0;
+    return it;
+  };
+  // kept position q of this thread: i = tid + k * 1024 over the Y x Z block
+  auto kept = [&](int k) { return tid + k * C::THREADS; };
+  struct In {
+    float2 y[INV ? PER : 1];            // intermediate plane, element tid + k * 1024
+    float va[INV ? 1 : KEPT], vb[INV ? 1 : KEPT];  // v block of both samples (first forward)
+  };
+  auto load_in = [&](const Item& it, In& in) {
+    if constexpr (INV) {
+      const float2* Yp = a.Yint + (((size_t)it.bp * CC + it.c) * X + it.x) * plane;
+#pragma unroll
+      for (int k = 0; k < PER; ++k) in.y[k] = Yp[tid + k * C::THREADS];
+    } else {
+      const size_t xoff = (size_t)it.x * Y * Z;
+      const float* v0 = a.p + (size_t)it.b0 * J * V + (size_t)it.c * V + xoff;
+      const float* v1 = a.p + (size_t)it.b1 * J * V + (size_t)it.c * V + xoff;
+#pragma unroll
+      for (int k = 0; k < KEPT; ++k) {
+        in.va[k] = v0[kept(k)];
+        in.vb[k] = v1[kept(k)];
+      }
+    }
+  };
+
+  int item = blockIdx.x;
+  if (item >= nitems) return;
+  In in;
+  load_in(item_of(item), in);
+  while (true) {
+    const int next = item + gridDim.x;
+    const bool more = next < nitems;
+    const Item it = item_of(item);
+    float2* Yp = a.Yint + (((size_t)it.bp * CC + it.c) * X + it.x) * plane;
+    const size_t xoff = (size_t)it.x * Y * Z;
+    if constexpr (INV) {
+#pragma unroll
+      for (int k = 0; k < PER; ++k) {
+        const int i = tid + k * C::THREADS;
+        P[(i / M) * C::RS + i % M] = in.y[k];
+      }
+    } else {
+      for (int i = tid; i < M * M; i += C::THREADS) P[(i / M) * C::RS + i % M] = make_float2(0.f, 0.f);
+      __syncthreads();
+#pragma unroll
+      for (int k = 0; k < KEPT; ++k) {
+        const int q = kept(k), y = q / Z, z = q % Z;
+        P[y * C::RS + z] = make_float2(in.va[k], it.has_b1 ? in.vb[k] : 0.f);
+      }
+    }
+    load_in(item_of(more ? next : item), in);  // the last item fetches itself again
+    if constexpr (INV) {
+      // gate and skip inputs of the kept block, needed after the inverse transform
+      const int n = a.n;
+      const float* x0 = a.p + (size_t)it.b0 * J * V + (size_t)((n + 1) * CC + it.c) * V + xoff;
+      const float* x1 = a.p + (size_t)it.b1 * J * V + (size_t)((n + 1) * CC + it.c) * V + xoff;
+      const float* z0 = (n == 0) ? a.p + (size_t)it.b0 * J * V + (size_t)it.c * V + xoff
+                                 : a.zin + ((size_t)it.b0 * CC + it.c) * V + xoff;
+      const float* z1 = (n == 0) ? a.p + (size_t)it.b1 * J * V + (size_t)it.c * V + xoff
+                                 : a.zin + ((size_t)it.b1 * CC + it.c) * V + xoff;
+      __syncthreads();
+      plane_cols<M, true>(P, tw);
+      float gx0[KEPT], gx1[KEPT], gz0[KEPT], gz1[KEPT];
+#pragma unroll
+      for (int k = 0; k < KEPT; ++k) {
+        gx0[k] = x0[kept(k)];
+        gx1[k] = x1[kept(k)];
+        gz0[k] = z0[kept(k)];
+        gz1[k] = z1[kept(k)];
+      }
+      plane_rows<M, true>(P, Y, tw);
+      float* o0 = a.zout + ((size_t)it.b0 * CC + it.c) * V + xoff;
+      float* o1 = a.zout + ((size_t)it.b1 * CC + it.c) * V + xoff;
+      const float g0 = a.gate[((size_t)it.b0 * a.NO + n) * CC + it.c];
+      const float g1 = it.has_b1 ? a.gate[((size_t)it.b1 * a.NO + n) * CC + it.c] : 0.f;
+      const float dk = a.dskip[n * CC + it.c];
+      // rows y >= Y of the plane must be zero for the forward transform
+      if (MODE == PL_INV_FWD) {
+        for (int i = tid; i < (M - Y) * M; i += C::THREADS) P[(Y + i / M) * C::RS + i % M] = make_float2(0.f, 0.f);
+      }
+#pragma unroll
+      for (int k = 0; k < KEPT; ++k) {
+        const int q = kept(k), y = q / Z, z = q % Z;
+        const float2 cv = P[y * C::RS + z];
+        const float a0 = gx0[k] * g0 * cv.x + dk * gz0[k];
+        o0[q] = a0;
+        float a1 = 0.f;
+        if (it.has_b1) {
+          a1 = gx1[k] * g1 * cv.y + dk * gz1[k];
+          o1[q] = a1;
+        }
+        if (MODE == PL_INV_FWD) P[y * C::RS + z] = make_float2(a0, a1);
+      }
+      if (MODE == PL_INV_FWD) {
+        // columns z >= Z of the kept rows must be zero too
+        for (int i = tid; i < Y * (M - Z); i += C::THREADS) P[(i / (M - Z)) * C::RS + Z + i % (M - Z)] = make_float2(0.f, 0.f);
+      }
+    }
+    if (MODE != PL_INV) {
+      __syncthreads();
+      // forward plane DFT of the (zero padded) Y x Z block
+      plane_rows<M, false>(P, Y, tw);
+      plane_cols<M, false>(P, tw);
+#pragma unroll
+      for (int k = 0; k < PER; ++k) {
+        const int i = tid + k * C::THREADS;
+        Yp[i] = P[(i / M) * C::RS + i % M];
+      }
+    }
+    if (!more) break;
+    item = next;
+    __syncthreads();  // P fully read before the next item writes it
+  }
+}
+
 // ======================================================= pencil pass
 // DFT over x of 64 consecutive (ky, kz) pencils; N1 = 2X = RA * RB points,
 // n1 = j + RA r, k1 = ka + RB kb. Forward: threads (lane, j < RA) hold
@@ -603,6 +754,24 @@ hipError_t nd_gate(const float* u, float* part, const float* ga, const float* gb
 
 size_t nd_gate_partial_floats(int B, int C, int V) { return (size_t)B * (V < 512 ? V : 512) * C; }
 
+template <int MODE>
+static hipError_t launch_plane128(const NdConvArgs& a, int nitems, hipStream_t s) {
+  using C = PlaneCfg<128>;
+  auto fn = nd_plane128_kernel<MODE>;
+  hipError_t e = nd_allow_lds((const void*)fn, C::LDS);
+  if (e != hipSuccess) return e;
+  static int grid = 0;
+  if (grid == 0) {
+    int cus = 0, dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess ||
+        hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0)
+      cus = 256;
+    grid = cus;  // one 1024-thread workgroup per CU (LDS)
+  }
+  hipLaunchKernelGGL(fn, dim3(grid < nitems ? grid : nitems), dim3(C::THREADS), C::LDS, s, a, nitems);
+  return hipGetLastError();
+}
+
 static hipError_t launch_pencil128(const NdConvArgs& a, int nitems, hipStream_t s) {
   const size_t lds = (size_t)16 * 8 * 64 * 8;
   auto fn = nd_pencil128_kernel;
@@ -625,7 +794,9 @@ hipError_t nd_conv(const NdConvArgs& in, hipStream_t s) {
   NdConvArgs a = in;
   const int BP = (a.B + 1) / 2;
   const unsigned nf = (unsigned)(4 * a.Y * a.Z / 64);
-  hipError_t e = launch_plane<PL_FWD_V>(a, dim3(a.X, a.C, BP), s);
+  const bool p128 = 2 * a.Y == 128 && a.Y == a.Z;
+  const int nplanes = a.X * a.C * BP;
+  hipError_t e = p128 ? launch_plane128<PL_FWD_V>(a, nplanes, s) : launch_plane<PL_FWD_V>(a, dim3(a.X, a.C, BP), s);
   if (e != hipSuccess) return e;
   for (int n = 0; n < a.NO; ++n) {
     a.n = n;
@@ -638,9 +809,9 @@ hipError_t nd_conv(const NdConvArgs& in, hipStream_t s) {
     a.zin = (n == 0) ? nullptr : in.zbuf[(n - 1) & 1];
     a.zout = (n == a.NO - 1) ? in.zfinal : in.zbuf[n & 1];
     if (n == a.NO - 1)
-      e = launch_plane<PL_INV>(a, dim3(a.X, a.C, BP), s);
+      e = p128 ? launch_plane128<PL_INV>(a, nplanes, s) : launch_plane<PL_INV>(a, dim3(a.X, a.C, BP), s);
     else
-      e = launch_plane<PL_INV_FWD>(a, dim3(a.X, a.C, BP), s);
+      e = p128 ? launch_plane128<PL_INV_FWD>(a, nplanes, s) : launch_plane<PL_INV_FWD>(a, dim3(a.X, a.C, BP), s);
     if (e != hipSuccess) return e;
   }
   return hipSuccess;
