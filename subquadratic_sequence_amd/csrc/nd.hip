@@ -663,6 +663,60 @@ __global__ void nd_gate_kernel(const float* __restrict__ part, const float* __re
   gate[idx] = 1.f / (1.f + expf(-arg));
 }
 
+// Faster forms for C dividing 256 (C = 64, 128, 256): a voxel chunk of the
+// channels-last input is one contiguous run of chunk * C floats, read 256 at a
+// time with independent partial sums; thread t always meets channel t % C, and
+// the 256 / C threads of a channel are combined in LDS.
+__global__ __launch_bounds__(256) void nd_mean_partial256_kernel(const float* __restrict__ u, float* __restrict__ part,
+                                                                 int C, int V, int chunk) {
+  __shared__ float red[256];
+  const int ch = blockIdx.x, b = blockIdx.y, t = threadIdx.x;
+  const float* ub = u + ((size_t)b * V + (size_t)ch * chunk) * C;
+  const int n = chunk * C;
+  float s0 = 0.f, s1 = 0.f, s2 = 0.f, s3 = 0.f;
+  int i = t;
+  for (; i + 3 * 256 < n; i += 4 * 256) {
+    s0 += ub[i];
+    s1 += ub[i + 256];
+    s2 += ub[i + 2 * 256];
+    s3 += ub[i + 3 * 256];
+  }
+  for (; i < n; i += 256) s0 += ub[i];
+  red[t] = (s0 + s1) + (s2 + s3);
+  __syncthreads();
+  if (t < C) {
+    float s = 0.f;
+    for (int r = t; r < 256; r += C) s += red[r];
+    part[((size_t)b * gridDim.x + ch) * C + t] = s;
+  }
+}
+
+__global__ __launch_bounds__(256) void nd_gate256_kernel(const float* __restrict__ part, const float* __restrict__ ga,
+                                                         const float* __restrict__ gb, float* __restrict__ gate,
+                                                         int NO, int C, int nch, int V) {
+  __shared__ float red[256];
+  const int b = blockIdx.x, t = threadIdx.x;
+  const int c = t % C, R = 256 / C;
+  float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+  int k = t / C;
+  for (; k + 7 * R < nch; k += 8 * R) {
+#pragma unroll
+    for (int j = 0; j < 8; ++j) acc[j] += part[((size_t)b * nch + k + j * R) * C + c];
+  }
+  for (; k < nch; k += R) acc[0] += part[((size_t)b * nch + k) * C + c];
+  red[t] = ((acc[0] + acc[1]) + (acc[2] + acc[3])) + ((acc[4] + acc[5]) + (acc[6] + acc[7]));
+  __syncthreads();
+  if (t < C) {
+    float s = 0.f;
+    for (int r = t; r < 256; r += C) s += red[r];
+    const float m = s / (float)V;
+    for (int n = 0; n < NO; ++n) {
+      const float arg = ga[n * C + c] * m + gb[n * C + c];
+      gate[((size_t)b * NO + n) * C + c] = 1.f / (1.f + expf(-arg));
+    }
+  }
+}
+
 // ============================================================ launchers
 
 static hipError_t nd_allow_lds(const void* fn, size_t bytes) {
@@ -743,6 +797,13 @@ hipError_t nd_filter(const NdFilterArgs& f, float2* F, float2* kh, const float2*
 hipError_t nd_gate(const float* u, float* part, const float* ga, const float* gb, float* gate, int B, int NO, int C,
                    int V, hipStream_t s) {
   const int nch = V < 512 ? V : 512;
+  if (256 % C == 0) {
+    hipLaunchKernelGGL(nd_mean_partial256_kernel, dim3(nch, B), dim3(256), 0, s, u, part, C, V, V / nch);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(nd_gate256_kernel, dim3(B), dim3(256), 0, s, (const float*)part, ga, gb, gate, NO, C, nch, V);
+    return hipGetLastError();
+  }
   hipLaunchKernelGGL(nd_mean_partial_kernel, dim3(nch, B), dim3(256), 0, s, u, part, C, V, V / nch);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
