@@ -1,0 +1,64 @@
+"""The stage-event entry points (hyena_fwd_profiled, hyena_nd_fwd_profiled) run the
+same launches as the plain ones: identical outputs, and four events that bracket
+the stages in order."""
+import numpy as np
+import pytest
+
+from tests.gpu_util import say, to_dev
+from synth import make_1d, make_nd
+
+pytestmark = pytest.mark.gpu
+
+
+def _events(torch):
+    return [torch.cuda.Event(enable_timing=True) for _ in range(4)]
+
+
+def _check_events(evs):
+    t = [evs[0].elapsed_time(evs[i]) for i in range(1, 4)]
+    assert all(x >= 0 for x in t) and t[0] <= t[1] <= t[2], t
+
+
+@pytest.mark.parametrize("L,dt", [(1024, "f32"), (16384, "bf16")])
+def test_fwd_profiled_matches_fwd(L, dt):
+    import torch
+    import subquadratic_sequence_amd as hs
+    inp = make_1d(41 + L, 2, L, 64, N=2, K=8, dtype=dt)
+    say(f"case profiled 1D B=2 L={L} D=64 dtype={dt}")
+    tdt = torch.bfloat16 if dt == "bf16" else torch.float32
+    layer = hs.HyenaLayer(inp.L, inp.D, inp.N)
+    hs.hyena_filter_gen(layer, to_dev(inp.w1), to_dev(inp.b1), to_dev(inp.w2), to_dev(inp.b2), to_dev(inp.w3),
+                        to_dev(inp.b3), to_dev(inp.decay), inp.K)
+    u, w_in, w_out = to_dev(inp.u, tdt), to_dev(inp.w_in, tdt), to_dev(inp.w_out, tdt)
+    short_w, dskip = to_dev(inp.short_w), to_dev(inp.dskip)
+    y0 = hs.hyena_fwd(layer, u, w_in, short_w, dskip, w_out)
+    y1 = torch.empty_like(y0)
+    ws = torch.empty(hs.hyena_workspace_bytes(inp.B, inp.L, inp.D, inp.N, hs.HYENA_BF16 if dt == "bf16" else
+                                              hs.HYENA_F32), dtype=torch.uint8, device="cuda")
+    evs = _events(torch)
+    hs.hyena_fwd_profiled(layer, u, w_in, short_w, dskip, w_out, y1, ws, evs)
+    torch.cuda.synchronize()
+    assert torch.equal(y0, y1)
+    _check_events(evs)
+
+
+def test_nd_fwd_profiled_matches_nd_fwd():
+    import torch
+    import subquadratic_sequence_amd as hs
+    inp = make_nd(43, 2, 8, 8, 8, 64, N=2)
+    say("case profiled 3D B=2 8^3 C=64")
+    layer = hs.HyenaNDLayer(inp.X, inp.Y, inp.Z, inp.C, inp.N)
+    hs.hyena_nd_filter_gen(layer, to_dev(inp.w1), to_dev(inp.b1), to_dev(inp.w2), to_dev(inp.b2), to_dev(inp.w3),
+                           to_dev(inp.b3), to_dev(inp.decay))
+    u, w_in, dskip, ga, gb, w_out = (to_dev(a) for a in (inp.u, inp.w_in, inp.dskip, inp.gate_a, inp.gate_b,
+                                                          inp.w_out))
+    y0 = hs.hyena_nd_fwd(layer, u, w_in, dskip, ga, gb, w_out)
+    y1 = torch.empty_like(y0)
+    ws = torch.empty(hs.hyena_nd_workspace_bytes(inp.B, inp.X, inp.Y, inp.Z, inp.C, inp.N), dtype=torch.uint8,
+                     device="cuda")
+    evs = _events(torch)
+    hs.hyena_nd_fwd_profiled(layer, u, w_in, dskip, ga, gb, w_out, y1, ws, evs)
+    torch.cuda.synchronize()
+    assert torch.equal(y0, y1)
+    assert np.isfinite(y1.cpu().numpy()).all()
+    _check_events(evs)
