@@ -80,6 +80,115 @@ __global__ __launch_bounds__(256) void nd_mlp_kernel(NdFilterArgs a) {
   }
 }
 
+// The same MLP on the fp32 matrix cores (v_mfma_f32_32x32x2_f32, full fp32
+// products and sums), for widths 64 and 128: 64 offset points per workgroup of
+// four waves; each layer is a [64 x K] x [K x cols] product in 32 x 32 blocks
+// with the activations in LDS; in the output layer a wave takes one 32-column
+// block (columns n C + c) for both 32-point halves with the K x 32 slice of
+// W3 in registers and the next block's slice in flight.
+typedef __attribute__((ext_vector_type(16))) float f32x16;
+
+template <int WW>
+__global__ __launch_bounds__(256) void nd_mlp_mfma_kernel(NdFilterArgs a) {
+  constexpr int LDH = WW + 1;
+  constexpr int KW = WW / 2;
+  __shared__ float cs[kNP][5];  // the three coordinates, a zero pad column, the radius
+  __shared__ float buf0[kNP * LDH];  // layer 2
+  __shared__ float buf1[kNP * LDH];  // layer 1
+  const int MX = 2 * a.X, MY = 2 * a.Y, MZ = 2 * a.Z;
+  const int P = MX * MY * MZ;
+  const int p0 = blockIdx.x * kNP;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int r32 = lane & 31, k2 = lane >> 5;
+  for (int t = tid; t < kNP; t += 256) {
+    const int pt = p0 + t;
+    const int k = pt % MZ, j = (pt / MZ) % MY, i = pt / (MZ * MY);
+    const float cx = (float)(i - a.X) / (float)a.X;
+    const float cy = (float)(j - a.Y) / (float)a.Y;
+    const float cz = (float)(k - a.Z) / (float)a.Z;
+    cs[t][0] = cx;
+    cs[t][1] = cy;
+    cs[t][2] = cz;
+    cs[t][3] = 0.f;
+    cs[t][4] = sqrtf(cx * cx + cy * cy + cz * cz);
+  }
+  __syncthreads();
+  auto zero = [](f32x16& c) {
+#pragma unroll
+    for (int e = 0; e < 16; ++e) c[e] = 0.f;
+  };
+  constexpr int NB = 2 * (WW / 32);
+  for (int blk = wave; blk < NB; blk += 4) {
+    const int rb = blk & 1, j = (blk >> 1) * 32 + r32;
+    f32x16 acc;
+    zero(acc);
+#pragma unroll
+    for (int k = 0; k < 4; k += 2) {
+      const int f = k + k2;  // feature 3 is the zero pad; it meets weight row 2 again
+      acc = __builtin_amdgcn_mfma_f32_32x32x2f32(cs[rb * 32 + r32][f], a.w1[(size_t)(f < 3 ? f : 2) * WW + j], acc,
+                                                 0, 0, 0);
+    }
+    const float bj = a.b1[j];
+#pragma unroll
+    for (int e = 0; e < 16; ++e) buf1[(rb * 32 + (e >> 2) * 8 + k2 * 4 + (e & 3)) * LDH + j] = sinf(acc[e] + bj);
+  }
+  __syncthreads();
+  for (int blk = wave; blk < NB; blk += 4) {
+    const int rb = blk & 1, j = (blk >> 1) * 32 + r32;
+    f32x16 acc;
+    zero(acc);
+#pragma unroll
+    for (int k = 0; k < WW; k += 2)
+      acc = __builtin_amdgcn_mfma_f32_32x32x2f32(buf1[(rb * 32 + r32) * LDH + k + k2],
+                                                 a.w2[(size_t)(k + k2) * WW + j], acc, 0, 0, 0);
+    const float bj = a.b2[j];
+#pragma unroll
+    for (int e = 0; e < 16; ++e) buf0[(rb * 32 + (e >> 2) * 8 + k2 * 4 + (e & 3)) * LDH + j] = sinf(acc[e] + bj);
+  }
+  __syncthreads();
+  const int NC = a.N * a.C;  // a multiple of 64
+  const int ncb = NC / 32;
+  float wv[KW];
+  auto load_w3 = [&](int cb) {
+    const float* w = a.w3 + cb * 32 + r32 + (size_t)k2 * NC;
+#pragma unroll
+    for (int k = 0; k < KW; ++k) wv[k] = w[(size_t)(2 * k) * NC];
+  };
+  int cb = wave;
+  if (cb >= ncb) return;
+  load_w3(cb);
+  while (true) {
+    const int col = cb * 32 + r32;
+    f32x16 acc0, acc1;
+    zero(acc0);
+    zero(acc1);
+#pragma unroll
+    for (int k = 0; k < KW; ++k) {
+      acc0 = __builtin_amdgcn_mfma_f32_32x32x2f32(buf0[r32 * LDH + 2 * k + k2], wv[k], acc0, 0, 0, 0);
+      acc1 = __builtin_amdgcn_mfma_f32_32x32x2f32(buf0[(32 + r32) * LDH + 2 * k + k2], wv[k], acc1, 0, 0, 0);
+    }
+    const int nxt = cb + 4;
+    const bool more = nxt < ncb;
+    load_w3(more ? nxt : cb);  // the next block's slice (this one's again after the last: unused)
+    const float bias = a.b3[col];
+    const float dc = a.decay[col % a.C];
+    float* dst = a.k + (size_t)col * P + p0;  // K[n][c][i][j][k], col = n C + c
+#pragma unroll
+    for (int rb = 0; rb < 2; ++rb) {
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const int t = rb * 32 + g * 8 + k2 * 4;  // four consecutive points
+        float o[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) o[i] = ((rb ? acc1[4 * g + i] : acc0[4 * g + i]) + bias) * expf(-dc * cs[t + i][4]);
+        *reinterpret_cast<float4*>(dst + t) = make_float4(o[0], o[1], o[2], o[3]);
+      }
+    }
+    if (!more) break;
+    cb = nxt;
+  }
+}
+
 // Two channels of the offset-indexed kernel, wrapped (offset d stored at d mod 2G),
 // as one complex field per channel pair: F = K_{2cp} + i K_{2cp+1}.
 __global__ void nd_pack_kernel(const float* __restrict__ k, float2* __restrict__ F, int X, int Y, int Z,
@@ -775,7 +884,12 @@ static hipError_t launch_pencil(const NdConvArgs& a, dim3 grid, hipStream_t s) {
 hipError_t nd_filter(const NdFilterArgs& f, float2* F, float2* kh, const float2* tw128, hipStream_t s) {
   const int MX = 2 * f.X, MY = 2 * f.Y, MZ = 2 * f.Z;
   const size_t P = (size_t)MX * MY * MZ;
-  hipLaunchKernelGGL(nd_mlp_kernel, dim3((unsigned)(P / kNP)), dim3(256), 0, s, f);
+  if (f.W == 64)
+    hipLaunchKernelGGL(nd_mlp_mfma_kernel<64>, dim3((unsigned)(P / kNP)), dim3(256), 0, s, f);
+  else if (f.W == 128)
+    hipLaunchKernelGGL(nd_mlp_mfma_kernel<128>, dim3((unsigned)(P / kNP)), dim3(256), 0, s, f);
+  else
+    hipLaunchKernelGGL(nd_mlp_kernel, dim3((unsigned)(P / kNP)), dim3(256), 0, s, f);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   const int npairs = f.N * f.C / 2;
