@@ -21,6 +21,8 @@ from .hyena_nd_oracle import (  # noqa: F401
     nd_gate,
     conv3d_direct,
     conv3d_fft,
+    conv3d_circular_direct,
+    conv3d_circular_fft,
     hyena_nd_fwd,
     hyena_nd_fwd_sampled,
 )

@@ -15,11 +15,20 @@ What it computes (HyenaND explainer, gist.science, "Methodology: HyenaND"):
   * the same projection / gating recurrence as the 1D operator, without the
     short convolution.
 
-Geometry: the kernel is defined on signed offsets d in [-G, G) per axis (G the
-grid size of that axis) at coordinates c = d / G, and
-out[p] = sum_{q in grid} g * K[p - q] * z[q] for p in the grid.  conv3d_fft stores
-the kernel wrapped (index d mod 2G) in a (2X, 2Y, 2Z) array, which makes the
-circular convolution of the zero-padded input exact on the kept grid.
+Geometry, zero-padded boundary (non-circular, the default): the kernel is
+defined on signed offsets d in [-G, G) per axis (G the grid size of that axis)
+at coordinates c = d / G, and out[p] = sum_{q in grid} g * K[p - q] * z[q] for p
+in the grid.  conv3d_fft stores the kernel wrapped (index d mod 2G) in a
+(2X, 2Y, 2Z) array, which makes the circular convolution of the zero-padded
+input exact on the kept grid.
+
+Geometry, circular boundary (periodic grids; "Handling Boundaries" names both
+kinds): the kernel covers one period, signed offsets d in [-G/2, G/2) per axis
+at coordinates c = d / (G/2), so that in both modes the coordinates span
+[-1, 1) over the kernel's support; out[p] = sum_{q in grid} g * K[(p - q) mod G]
+* z[q] for every p, evaluated with an unpadded (X, Y, Z) FFT.  In both modes the
+offset-indexed arrays hold offset d at index d + M/2, M the transform length of
+the axis (2G padded, G circular).
 
 Window form, MLP width, gate form, coordinate scaling and initialisation are
 conventions of this implementation: parity unpinned for those conventions.
@@ -39,31 +48,35 @@ def fftn3_radix2(x, inverse: bool = False) -> np.ndarray:
     return a
 
 
-def nd_offsets(X: int, Y: int, Z: int) -> np.ndarray:
-    """Normalised coordinates c = d / G of the signed offsets d in [-G, G) per axis.
+def nd_offsets(X: int, Y: int, Z: int, circular: bool = False) -> np.ndarray:
+    """Coordinates of the kernel's signed offsets, [MX, MY, MZ, 3].
 
-    Returns [2X, 2Y, 2Z, 3]; entry [i, j, k] is the offset (i - X, j - Y, k - Z).
+    Zero-padded: M = 2G, offsets d in [-G, G), c = d / G.  Circular: M = G,
+    offsets d in [-G/2, G/2), c = d / (G/2).  Entry [i, j, k] is the offset
+    (i - MX/2, j - MY/2, k - MZ/2) in both modes.
     """
-    cx = np.arange(-X, X, dtype=np.float64) / X
-    cy = np.arange(-Y, Y, dtype=np.float64) / Y
-    cz = np.arange(-Z, Z, dtype=np.float64) / Z
-    g = np.stack(np.meshgrid(cx, cy, cz, indexing="ij"), axis=-1)
+    axes = []
+    for G in (X, Y, Z):
+        h = G // 2 if circular else G
+        axes.append(np.arange(-h, h, dtype=np.float64) / h)
+    g = np.stack(np.meshgrid(*axes, indexing="ij"), axis=-1)
     return g
 
 
-def nd_filter(params: dict, X: int, Y: int, Z: int, N: int, C: int) -> np.ndarray:
+def nd_filter(params: dict, X: int, Y: int, Z: int, N: int, C: int, circular: bool = False) -> np.ndarray:
     """K[n, c, i, j, k] at offset (i - X, j - Y, k - Z):
     K = exp(-a_c |coord|_2) * (W3^T sin(W2^T sin(W1^T coord + b1) + b2) + b3)[n*C + c].
 
-    Returns [N, C, 2X, 2Y, 2Z] float64 (offset-indexed, not wrapped).
+    Returns [N, C, MX, MY, MZ] float64 (offset-indexed, not wrapped): (2X, 2Y, 2Z)
+    zero-padded, (X, Y, Z) circular.
     """
     f = lambda k: np.asarray(params[k], dtype=np.float64)  # noqa: E731
-    c = nd_offsets(X, Y, Z)
+    c = nd_offsets(X, Y, Z, circular)
     a1 = np.sin(c @ f("w1") + f("b1"))
     a2 = np.sin(a1 @ f("w2") + f("b2"))
-    o = a2 @ f("w3") + f("b3")                                       # [2X,2Y,2Z,N*C]
+    o = a2 @ f("w3") + f("b3")                                       # [MX,MY,MZ,N*C]
     r = np.sqrt(np.sum(c * c, axis=-1))
-    win = np.exp(-r[..., None] * f("decay"))                         # [2X,2Y,2Z,C]
+    win = np.exp(-r[..., None] * f("decay"))                         # [MX,MY,MZ,C]
     K = o.reshape(o.shape[:3] + (N, C)) * win[..., None, :]
     return np.ascontiguousarray(np.moveaxis(K, (3, 4), (0, 1)))
 
@@ -110,6 +123,40 @@ def conv3d_fft(K, z) -> np.ndarray:
     return c[..., :X, :Y, :Z].real
 
 
+def conv3d_circular_direct(K, z) -> np.ndarray:
+    """out[..., p] = sum_{q in grid} K[..., (p - q) mod G as an offset] * z[..., q]  (definition).
+
+    K [..., X, Y, Z] offset-indexed (offset d at index d + G/2, d in [-G/2, G/2));
+    z [..., X, Y, Z].  The offset (p - q) mod G, taken in [-G/2, G/2), sits at
+    index (p - q + G/2) mod G.  O(G^6); for small grids.
+    """
+    K = np.asarray(K, dtype=np.float64)
+    z = np.asarray(z, dtype=np.float64)
+    X, Y, Z = z.shape[-3:]
+    out = np.zeros(np.broadcast_shapes(K.shape[:-3], z.shape[:-3]) + (X, Y, Z))
+    for qx in range(X):
+        for qy in range(Y):
+            for qz in range(Z):
+                # slab[p] = K[(p - q + G/2) mod G] = roll(K, q - G/2)[p]
+                slab = np.roll(K, shift=(qx - X // 2, qy - Y // 2, qz - Z // 2), axis=(-3, -2, -1))
+                out += slab * z[..., qx, qy, qz][..., None, None, None]
+    return out
+
+
+def conv3d_circular_fft(K, z) -> np.ndarray:
+    """Same result as conv3d_circular_direct via an (X, Y, Z) textbook FFT.
+
+    The offset-indexed kernel is wrapped (offset d stored at d mod G); no padding,
+    no crop: the DFT's own circular convolution is the periodic one.
+    """
+    K = np.asarray(K, dtype=np.float64)
+    z = np.asarray(z, dtype=np.float64)
+    X, Y, Z = z.shape[-3:]
+    Kw = np.roll(K, shift=(-(X // 2), -(Y // 2), -(Z // 2)), axis=(-3, -2, -1))
+    c = fftn3_radix2(fftn3_radix2(Kw) * fftn3_radix2(z), inverse=True)
+    return c.real
+
+
 def _nd_project(u, w_in, C, N):
     u = np.asarray(u, dtype=np.float64)
     p = u @ np.asarray(w_in, dtype=np.float64)                       # [B,X,Y,Z,(N+1)C]
@@ -118,15 +165,19 @@ def _nd_project(u, w_in, C, N):
     return blocks[0], blocks[1:]
 
 
-def hyena_nd_fwd(u, w_in, dskip, gate_a, gate_b, w_out, K, conv: str = "fft") -> np.ndarray:
+def hyena_nd_fwd(u, w_in, dskip, gate_a, gate_b, w_out, K, conv: str = "fft",
+                 circular: bool = False) -> np.ndarray:
     """y[B, X, Y, Z, C] of the 3D operator.
 
     u [B,X,Y,Z,C]; w_in [C,(N+1)C]; dskip, gate_a, gate_b [N,C]; w_out [C,C];
-    K [N, C, 2X, 2Y, 2Z] (nd_filter).  conv: "direct" or "fft".
+    K [N, C, MX, MY, MZ] (nd_filter with the same `circular`).  conv: "direct" or "fft".
     """
     B, X, Y, Z, C = np.shape(u)
     N = np.shape(dskip)[0]
-    convf = conv3d_direct if conv == "direct" else conv3d_fft
+    if circular:
+        convf = conv3d_circular_direct if conv == "direct" else conv3d_circular_fft
+    else:
+        convf = conv3d_direct if conv == "direct" else conv3d_fft
     dskip = np.asarray(dskip, dtype=np.float64)
     g = nd_gate(u, gate_a, gate_b)                                   # [B, N, C]
     z, xs = _nd_project(u, w_in, C, N)
@@ -139,13 +190,14 @@ def hyena_nd_fwd(u, w_in, dskip, gate_a, gate_b, w_out, K, conv: str = "fft") ->
     return np.moveaxis(z, 1, -1) @ np.asarray(w_out, dtype=np.float64)
 
 
-def hyena_nd_fwd_sampled(u, w_in, dskip, gate_a, gate_b, w_out, K, points, chunk: int = 8) -> np.ndarray:
+def hyena_nd_fwd_sampled(u, w_in, dskip, gate_a, gate_b, w_out, K, points, chunk: int = 8,
+                         circular: bool = False) -> np.ndarray:
     """y[:, points] for full-size grids.
 
-    Orders 1..N-1 run on the whole grid with conv3d_fft (channel chunks of
-    `chunk`); the last order is evaluated only at the sampled grid points by the
-    direct sum over the grid.  points [S, 3] integer grid coordinates.
-    Returns [B, S, C].
+    Orders 1..N-1 run on the whole grid with conv3d_fft / conv3d_circular_fft
+    (channel chunks of `chunk`); the last order is evaluated only at the sampled
+    grid points by the direct sum over the grid.  points [S, 3] integer grid
+    coordinates.  Returns [B, S, C].
     """
     B, X, Y, Z, C = np.shape(u)
     N = np.shape(dskip)[0]
@@ -158,14 +210,22 @@ def hyena_nd_fwd_sampled(u, w_in, dskip, gate_a, gate_b, w_out, K, points, chunk
         for b in range(B):
             for c0 in range(0, C, chunk):
                 gk = g[b, n, c0:c0 + chunk][:, None, None, None] * K[n, c0:c0 + chunk]
-                out[b, c0:c0 + chunk] = conv3d_fft(gk, z[b, c0:c0 + chunk])
+                convf = conv3d_circular_fft if circular else conv3d_fft
+                out[b, c0:c0 + chunk] = convf(gk, z[b, c0:c0 + chunk])
         z = xs[n] * out + dskip[n][None, :, None, None, None] * z
     n = N - 1
     pts = np.asarray(points, dtype=np.int64)
     res = np.empty((B, len(pts), C))
     for i, (px, py, pz) in enumerate(pts):
-        # K offsets p - q for q over the grid: index (p - q) + G, flipped slab
-        ks = K[n][:, px + X:px:-1, py + Y:py:-1, pz + Z:pz:-1]        # [C, X, Y, Z] over q
+        if circular:
+            # offset (p - q) mod G at index (p - q + G/2) mod G, for q over the grid
+            ix = (px - np.arange(X) + X // 2) % X
+            iy = (py - np.arange(Y) + Y // 2) % Y
+            iz = (pz - np.arange(Z) + Z // 2) % Z
+            ks = K[n][:, ix[:, None, None], iy[None, :, None], iz[None, None, :]]
+        else:
+            # K offsets p - q for q over the grid: index (p - q) + G, flipped slab
+            ks = K[n][:, px + X:px:-1, py + Y:py:-1, pz + Z:pz:-1]    # [C, X, Y, Z] over q
         c = np.einsum("cxyz,bcxyz->bc", ks, z) * g[:, n, :]
         res[:, i, :] = xs[n][:, :, px, py, pz] * c + dskip[n][None, :] * z[:, :, px, py, pz]
     return res @ np.asarray(w_out, dtype=np.float64)

@@ -384,3 +384,141 @@ def test_nd_causality_free_but_translation_equivariant_interior():
     o1 = oracle.conv3d_fft(K, z)
     o2 = oracle.conv3d_fft(K, np.roll(z, 1, axis=0))
     assert np.allclose(np.roll(o1, 1, axis=0)[1:-1], o2[1:-1], atol=1e-12)
+
+
+# ------------------------------------------------------------- ND, circular
+# Periodic grids (HyenaND explainer, "Handling Boundaries": circular convolution
+# for periodic physical systems). Offset-indexed kernels hold offset d at index
+# d + G/2, d in [-G/2, G/2).
+
+def _circ_conv_numpy(K, z):
+    """Circular convolution through numpy's FFT (a library routine, not the oracle's)."""
+    X, Y, Z = z.shape[-3:]
+    Kw = np.roll(K, shift=(-(X // 2), -(Y // 2), -(Z // 2)), axis=(-3, -2, -1))
+    return np.fft.ifftn(np.fft.fftn(Kw, axes=(-3, -2, -1)) * np.fft.fftn(z, axes=(-3, -2, -1)),
+                        axes=(-3, -2, -1)).real
+
+
+def test_conv3d_circular_fft_equals_direct():
+    K = RNG.standard_normal((2, 8, 8, 8))
+    z = RNG.standard_normal((2, 8, 8, 8))
+    assert rel(oracle.conv3d_circular_fft(K, z), oracle.conv3d_circular_direct(K, z)) < 1e-11
+    K = RNG.standard_normal((8, 4, 4))
+    z = RNG.standard_normal((8, 4, 4))
+    assert rel(oracle.conv3d_circular_fft(K, z), oracle.conv3d_circular_direct(K, z)) < 1e-11
+
+
+def test_conv3d_circular_matches_library_fft():
+    # an asymmetric kernel: a flipped offset or a wrong wrap direction fails here
+    K = RNG.standard_normal((3, 8, 4, 4))
+    z = RNG.standard_normal((3, 8, 4, 4))
+    assert rel(oracle.conv3d_circular_direct(K, z), _circ_conv_numpy(K, z)) < 1e-12
+
+
+def test_conv3d_circular_single_offset_is_a_roll():
+    # K = delta at offset d: out[p] = z[p - d] for every p (wrapping)
+    X, Y, Z = 8, 4, 4
+    z = RNG.standard_normal((X, Y, Z))
+    for d in [(0, 0, 0), (1, 0, 0), (-4, 1, -2), (3, -2, 1)]:
+        K = np.zeros((X, Y, Z))
+        K[d[0] + X // 2, d[1] + Y // 2, d[2] + Z // 2] = 1.0
+        want = np.roll(z, shift=d, axis=(0, 1, 2))
+        assert np.array_equal(oracle.conv3d_circular_direct(K, z), want)
+        assert rel(oracle.conv3d_circular_fft(K, z), want) < 1e-12
+
+
+def test_conv3d_circular_shift_equivariant_everywhere():
+    K = RNG.standard_normal((8, 8, 8))
+    z = RNG.standard_normal((8, 8, 8))
+    o = oracle.conv3d_circular_fft(K, z)
+    for s in [(1, 0, 0), (0, 3, 5), (7, 7, 1)]:
+        o2 = oracle.conv3d_circular_fft(K, np.roll(z, s, axis=(0, 1, 2)))
+        assert rel(o2, np.roll(o, s, axis=(0, 1, 2))) < 1e-12
+
+
+def test_conv3d_circular_separable_is_product_of_1d_circular_convs():
+    X, Y, Z = 8, 4, 8
+    a, b, c = RNG.standard_normal(X), RNG.standard_normal(Y), RNG.standard_normal(Z)
+    f, g, k = RNG.standard_normal(X), RNG.standard_normal(Y), RNG.standard_normal(Z)
+    K = a[:, None, None] * b[None, :, None] * c[None, None, :]
+    z = f[:, None, None] * g[None, :, None] * k[None, None, :]
+
+    def circ1(h, x):
+        G = len(x)
+        # out[p] = sum_q h[offset (p - q) mod G] x[q], offset index (p - q + G/2) mod G
+        return np.array([sum(h[(p - q + G // 2) % G] * x[q] for q in range(G)) for p in range(G)])
+
+    want = circ1(a, f)[:, None, None] * circ1(b, g)[None, :, None] * circ1(c, k)[None, None, :]
+    assert rel(oracle.conv3d_circular_direct(K, z), want) < 1e-12
+    assert rel(oracle.conv3d_circular_fft(K, z), want) < 1e-11
+
+
+def test_conv3d_circular_equals_linear_when_nothing_wraps():
+    # kernel within |d| <= 1 and input within [2, 6)^3 of an 8^3 grid: no sum
+    # crosses the boundary, so the periodic and the zero-padded results agree
+    G = 8
+    Kc = np.zeros((G, G, G))
+    Kc[G // 2 - 1:G // 2 + 2, G // 2 - 1:G // 2 + 2, G // 2 - 1:G // 2 + 2] = RNG.standard_normal((3, 3, 3))
+    Kp = np.zeros((2 * G, 2 * G, 2 * G))
+    Kp[G - 1:G + 2, G - 1:G + 2, G - 1:G + 2] = Kc[G // 2 - 1:G // 2 + 2, G // 2 - 1:G // 2 + 2, G // 2 - 1:G // 2 + 2]
+    z = np.zeros((G, G, G))
+    z[2:6, 2:6, 2:6] = RNG.standard_normal((4, 4, 4))
+    assert rel(oracle.conv3d_circular_direct(Kc, z), oracle.conv3d_direct(Kp, z)) < 1e-12
+
+
+def test_nd_offsets_circular_span_one_period():
+    X, Y, Z = 8, 4, 4
+    c = oracle.nd_offsets(X, Y, Z, circular=True)
+    assert c.shape == (X, Y, Z, 3)
+    assert np.array_equal(c[:, 0, 0, 0], np.arange(-4, 4) / 4.0)
+    assert np.array_equal(c[0, :, 0, 1], np.arange(-2, 2) / 2.0)
+    assert np.array_equal(c[X // 2, Y // 2, Z // 2], [0.0, 0.0, 0.0])   # offset 0 at index G/2
+    # the padded mode keeps its own grid: offsets [-G, G) at c = d / G
+    cp = oracle.nd_offsets(X, Y, Z)
+    assert cp.shape == (2 * X, 2 * Y, 2 * Z, 3)
+    assert np.array_equal(cp[:, 0, 0, 0], np.arange(-X, X) / X)
+
+
+def test_nd_filter_circular_window():
+    X = Y = Z = 8
+    N, C = 2, 4
+    inp = make_nd(3, 1, X, Y, Z, C, N=N, W=8)
+    p = dict(inp.filter_params)
+    p["w3"] = np.zeros_like(p["w3"])
+    p["b3"] = np.ones_like(p["b3"])
+    K = oracle.nd_filter(p, X, Y, Z, N, C, circular=True)
+    assert K.shape == (N, C, X, Y, Z)
+    a = inp.decay.astype(np.float64)
+    assert np.allclose(K[:, :, 4, 4, 4], 1.0)                         # offset 0
+    assert np.allclose(K[0, :, 6, 4, 4], np.exp(-a * 0.5))            # offset (2, 0, 0): c = 2/4
+    assert np.allclose(K[0, :, 0, 4, 4], np.exp(-a * 1.0))            # offset (-4, 0, 0): c = -1
+
+
+def test_nd_circular_operator_is_translation_equivariant():
+    # the gate sees grid means (unchanged by a roll) and the projections act per
+    # voxel, so rolling the input rolls the output of the whole operator exactly
+    X = Y = Z = 4
+    inp = make_nd(6, 2, X, Y, Z, 4, N=2, W=8, u_mean_spread=0.5)
+    K = oracle.nd_filter(inp.filter_params, X, Y, Z, 2, 4, circular=True)
+    rest = (inp.w_in, inp.dskip, inp.gate_a, inp.gate_b, inp.w_out, K)
+    y = oracle.hyena_nd_fwd(inp.u, *rest, circular=True)
+    s = (1, 2, 3)
+    y2 = oracle.hyena_nd_fwd(np.roll(inp.u, s, axis=(1, 2, 3)), *rest, circular=True)
+    assert rel(y2, np.roll(y, s, axis=(1, 2, 3))) < 1e-12
+
+
+def test_nd_circular_fft_equals_direct_and_sampled_equals_full():
+    X = Y = Z = 4
+    inp = make_nd(7, 3, X, Y, Z, 4, N=2, W=8, u_mean_spread=0.5)
+    K = oracle.nd_filter(inp.filter_params, X, Y, Z, 2, 4, circular=True)
+    args = (inp.u, inp.w_in, inp.dskip, inp.gate_a, inp.gate_b, inp.w_out, K)
+    yd = oracle.hyena_nd_fwd(*args, conv="direct", circular=True)
+    yf = oracle.hyena_nd_fwd(*args, conv="fft", circular=True)
+    assert rel(yf, yd) < 1e-11
+    pts = np.array([[0, 0, 0], [3, 3, 3], [1, 2, 3], [3, 0, 2]])
+    ys = oracle.hyena_nd_fwd_sampled(*args, pts, chunk=3, circular=True)
+    assert rel(ys, yd[:, pts[:, 0], pts[:, 1], pts[:, 2]]) < 1e-11
+    # the boundary matters: the zero-padded operator gives a different result
+    Kp = oracle.nd_filter(inp.filter_params, X, Y, Z, 2, 4)
+    yp = oracle.hyena_nd_fwd(*args[:-1], Kp)
+    assert rel(yp, yd) > 1e-3
