@@ -144,11 +144,13 @@ def cpu_baseline(inp, budget_tokens: int):
                       f"FFT path, 1 thread, {dt:.1f} s"}
 
 
-def nd_conv_alg_bytes(B, X, Y, Z, C, N) -> float:
+def nd_conv_alg_bytes(B, X, Y, Z, C, N, circular: bool = False) -> float:
     """Per call: each order reads z^n and x^n and writes z^{n+1} (fp32 [B][C][X][Y][Z])
-    and reads the channel's half spectrum (complex fp32, (2X)(2Y)(Z+1) bins)."""
+    and reads the channel's half spectrum (complex fp32, MX MY (MZ/2 + 1) bins with
+    (MX, MY, MZ) = (2X, 2Y, 2Z) zero padded, (X, Y, Z) circular)."""
     V = X * Y * Z
-    return N * (3.0 * B * C * V * 4 + 8.0 * C * (2 * X) * (2 * Y) * (Z + 1))
+    p = 1 if circular else 2
+    return N * (3.0 * B * C * V * 4 + 8.0 * C * (p * X) * (p * Y) * (p * Z // 2 + 1))
 
 
 def cpu_baseline_nd(inp, channels: int):
@@ -167,10 +169,11 @@ def cpu_baseline_nd(inp, channels: int):
     params["b3"] = np.concatenate([params["b3"][n * inp.C:n * inp.C + c] for n in range(N)])
     params["decay"] = params["decay"][:c]
     with threadpool_limits(limits=1):
-        K = oracle.nd_filter(params, inp.X, inp.Y, inp.Z, N, c)  # the layer's kernel: outside the step
+        # the layer's kernel: outside the step
+        K = oracle.nd_filter(params, inp.X, inp.Y, inp.Z, N, c, circular=inp.circular)
         t0 = time.perf_counter()
         oracle.hyena_nd_fwd(inp.u[:1, ..., :c], w_in, inp.dskip[:, :c], inp.gate_a[:, :c], inp.gate_b[:, :c],
-                            inp.w_out[:c, :c], K, conv="fft")
+                            inp.w_out[:c, :c], K, conv="fft", circular=inp.circular)
         dt = time.perf_counter() - t0
     V = inp.X * inp.Y * inp.Z
     return {"value": V / dt * c / inp.C, "unit": "voxels/s", "cores": 1, "kind": "oracle",
@@ -185,12 +188,13 @@ def main_nd(args, torch, hs, make_config):
     B, X, Y, Z, C, N = inp.B, inp.X, inp.Y, inp.Z, inp.C, inp.N
     V = X * Y * Z
     f = lambda a: torch.from_numpy(np.ascontiguousarray(a, np.float32)).to("cuda")  # noqa: E731
-    layer = hs.HyenaNDLayer(X, Y, Z, C, N)
+    bd = hs.ND_CIRCULAR if inp.circular else hs.ND_ZERO_PAD
+    layer = hs.HyenaNDLayer(X, Y, Z, C, N, boundary=bd)
     fargs = [f(a) for a in (inp.w1, inp.b1, inp.w2, inp.b2, inp.w3, inp.b3, inp.decay)]
     hs.hyena_nd_filter_gen(layer, *fargs)
     u, w_in, dskip, ga, gb, w_out = (f(a) for a in (inp.u, inp.w_in, inp.dskip, inp.gate_a, inp.gate_b, inp.w_out))
     y = torch.empty_like(u)
-    ws = torch.empty(hs.hyena_nd_workspace_bytes(B, X, Y, Z, C, N), dtype=torch.uint8, device="cuda")
+    ws = torch.empty(hs.hyena_nd_workspace_bytes_ex(B, X, Y, Z, C, N, bd), dtype=torch.uint8, device="cuda")
     torch.cuda.synchronize()
     log(f"warmup {args.warmup}")
     for _ in range(args.warmup):
@@ -215,7 +219,7 @@ def main_nd(args, torch, hs, make_config):
     hs.hyena_nd_filter_gen(layer, *fargs)
     f1.record()
     torch.cuda.synchronize()
-    alg = nd_conv_alg_bytes(B, X, Y, Z, C, N)
+    alg = nd_conv_alg_bytes(B, X, Y, Z, C, N, inp.circular)
     achieved = alg / (stages[1] * 1e-3) / 1e9
     proj = {}
     for name, n_out, ms in (("in_proj", (N + 1) * C, stages[0]), ("out_proj", C, stages[2])):
@@ -229,7 +233,8 @@ def main_nd(args, torch, hs, make_config):
         conv_valu = {"bound": "alu", "achieved": gi, "peak": VALU_PEAK_GINSTR, "unit": "G wave-instr/s",
                      "frac": gi / VALU_PEAK_GINSTR, "fp32_tflops": tf, "fp32_peak_tflops": VALU_F32_PEAK_TFLOPS}
     out = {
-        "metric": "HyenaND fwd voxels/sec (3D, B=2, C=128, 64^3, 1 GPU); 3D FFT-conv HBM GB/s % of peak",
+        "metric": (f"HyenaND fwd voxels/sec (3D, B={B}, C={C}, {X}x{Y}x{Z}"
+                   f"{', circular' if inp.circular else ''}, 1 GPU); 3D FFT-conv HBM GB/s % of peak"),
         "value": B * V * args.steps / elapsed,
         "unit": "voxels/s",
         "n_gpus": 1,
@@ -241,7 +246,8 @@ def main_nd(args, torch, hs, make_config):
         "vs_baseline": None,
         "dtype": "f32",
         "data": "synthetic",
-        "config": {"workload": args.workload, "B": B, "X": X, "Y": Y, "Z": Z, "C": C, "N": N},
+        "config": {"workload": args.workload, "B": B, "X": X, "Y": Y, "Z": Z, "C": C, "N": N,
+                   "boundary": "circular" if inp.circular else "zero-padded"},
         "stage_ms": {"in_proj": stages[0], "fft_conv": stages[1], "out_proj": stages[2]},
         "step_ms_events": {"p10": float(np.percentile(step_ms, 10)), "p50": float(np.median(step_ms)),
                            "p90": float(np.percentile(step_ms, 90))},
@@ -255,7 +261,7 @@ def main_nd(args, torch, hs, make_config):
     }
     if not args.no_cpu_baseline:
         log("cpu baseline (oracle)")
-        out["cpu_baseline"] = cpu_baseline_nd(inp, args.cpu_channels)
+        out["cpu_baseline"] = cpu_baseline_nd(inp, args.cpu_channels or (64 if inp.circular else 8))
     print(json.dumps(out), flush=True)
 
 
@@ -267,7 +273,8 @@ def main():
     ap.add_argument("--workload", default=DEFAULT_WORKLOAD)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-tokens", type=int, default=16384)
-    ap.add_argument("--cpu-channels", type=int, default=8, help="channels of the 3D oracle sample")
+    ap.add_argument("--cpu-channels", type=int, default=0,
+                    help="channels of the 3D oracle sample (default 8 zero padded, 64 circular)")
     ap.add_argument("--calib-copy", type=int, default=0, metavar="MIB",
                     help="only run a plain device copy of MIB MiB (reads and writes MIB MiB), for calibrating "
                          "the FETCH_SIZE / WRITE_SIZE counters, and exit")
@@ -279,7 +286,7 @@ def main():
 
     import torch
     import subquadratic_sequence_amd as hs
-    from synth import CONFIGS, make_config
+    from synth import CONFIGS, TEST_SHAPES, make_config
 
     if args.calib_copy:
         n = args.calib_copy * (1 << 20) // 4
@@ -291,7 +298,10 @@ def main():
         print(json.dumps({"calib_copy_bytes": n * 4}))
         return
 
-    cfg = CONFIGS[args.workload]
+    if args.workload not in CONFIGS and args.workload not in TEST_SHAPES:
+        print(f"unknown workload {args.workload}; one of {sorted(CONFIGS) + sorted(TEST_SHAPES)}", file=sys.stderr)
+        sys.exit(2)
+    cfg = CONFIGS.get(args.workload) or TEST_SHAPES[args.workload]
     if cfg["kind"] == "nd":
         return main_nd(args, torch, hs, make_config)
     log(f"generating inputs for {args.workload}")

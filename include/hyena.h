@@ -140,30 +140,54 @@ typedef struct {
   const float *w1, *b1, *w2, *b2, *w3, *b3, *decay;  /* [3][W],[W],[W][W],[W],[W][N*C],[N*C],[C] */
 } hyena_nd_filter_params;
 
+/* Boundary of the convolution ("Handling Boundaries" names both kinds):
+ *   HYENA_ND_ZERO_PAD  non-circular, as above (the default; transform (2X, 2Y, 2Z));
+ *   HYENA_ND_CIRCULAR  periodic grids: the kernel covers one period, offsets
+ *                      d in [-X/2,X/2)x[-Y/2,Y/2)x[-Z/2,Z/2) at coordinates
+ *                      c = (2dx/X, 2dy/Y, 2dz/Z), and
+ *                      (K conv z)[p] = sum_{q in grid} g * K[(p - q) mod (X,Y,Z)] z[q]
+ *                      for every p, through an unpadded (X, Y, Z) transform.
+ * In both modes the coordinates span [-1, 1) over the kernel's support. */
+typedef enum { HYENA_ND_ZERO_PAD = 0, HYENA_ND_CIRCULAR = 1 } hyena_nd_boundary;
+
 typedef struct {
   int X, Y, Z, C, N;
   int built;
   void *cache;
   size_t cache_bytes;
+  int boundary;  /* hyena_nd_boundary, set by the init call */
 } hyena_nd_layer;
 
-/* Supported: X, Y, Z powers of two in [4, 64] with Y = Z; C a multiple of 64 in [64, 4096];
- * 1 <= N <= 4; B >= 1. The size queries return 0 for unsupported shapes. */
+/* Supported: Y = Z; X, Y, Z powers of two in [4, 64] (zero padded) or in [8, 128]
+ * (circular); C a multiple of 64 in [64, 4096]; 1 <= N <= 4; B >= 1. The size
+ * queries return 0 for unsupported shapes or boundaries. The calls without _ex
+ * are the zero-padded boundary. */
 size_t hyena_nd_cache_bytes(int X, int Y, int Z, int C, int N);
 size_t hyena_nd_filter_workspace_bytes(int X, int Y, int Z, int C, int N);
 size_t hyena_nd_workspace_bytes(int B, int X, int Y, int Z, int C, int N);
+size_t hyena_nd_cache_bytes_ex(int X, int Y, int Z, int C, int N, int boundary);
+size_t hyena_nd_filter_workspace_bytes_ex(int X, int Y, int Z, int C, int N, int boundary);
+size_t hyena_nd_workspace_bytes_ex(int B, int X, int Y, int Z, int C, int N, int boundary);
 
 int hyena_nd_layer_init(hyena_nd_layer *layer, int X, int Y, int Z, int C, int N,
                         void *cache, size_t cache_bytes);
+/* As hyena_nd_layer_init with a boundary; HYENA_ERR_UNSUPPORTED for an unknown
+ * boundary or a shape outside its range. The cache must hold
+ * hyena_nd_cache_bytes_ex(..., boundary) bytes. */
+int hyena_nd_layer_init_ex(hyena_nd_layer *layer, int X, int Y, int Z, int C, int N, int boundary,
+                           void *cache, size_t cache_bytes);
 
-/* Evaluates K^n_c on the (2X, 2Y, 2Z) offset grid and caches its 3D spectrum.
- * If k_out is not NULL the kernel is also written there as fp32
- * [N][C][2X][2Y][2Z], entry [i][j][k] at offset (i - X, j - Y, k - Z). */
+/* Evaluates K^n_c on the layer's (MX, MY, MZ) offset grid, (2X, 2Y, 2Z) zero padded
+ * or (X, Y, Z) circular, and caches its 3D spectrum. If k_out is not NULL the
+ * kernel is also written there as fp32 [N][C][MX][MY][MZ], entry [i][j][k] at
+ * offset (i - MX/2, j - MY/2, k - MZ/2). ws must hold
+ * hyena_nd_filter_workspace_bytes_ex(..., layer->boundary) bytes. */
 int hyena_nd_filter_gen(hyena_nd_layer *layer, const hyena_nd_filter_params *p, float *k_out,
                         void *ws, size_t ws_bytes, hipStream_t stream);
 
-/* Forward pass, fp32:
- *   u, y [B][X][Y][Z][C]; w_in [C][(N+1)C]; dskip, gate_a, gate_b [N][C]; w_out [C][C]. */
+/* Forward pass, fp32, with the layer's boundary:
+ *   u, y [B][X][Y][Z][C]; w_in [C][(N+1)C]; dskip, gate_a, gate_b [N][C]; w_out [C][C].
+ * ws must hold hyena_nd_workspace_bytes_ex(B, ..., layer->boundary) bytes. */
 int hyena_nd_fwd(const hyena_nd_layer *layer, const float *u, const float *w_in,
                  const float *dskip, const float *gate_a, const float *gate_b,
                  const float *w_out, int B, float *y, void *ws, size_t ws_bytes,

@@ -10,6 +10,8 @@ from .hyena import (  # noqa: F401
     HyenaLayer,
     HyenaNDLayer,
     LIB_PATH,
+    ND_CIRCULAR,
+    ND_ZERO_PAD,
     SIGNATURES,
     hyena_cache_bytes,
     hyena_filter_gen,
@@ -17,11 +19,14 @@ from .hyena import (  # noqa: F401
     hyena_fwd,
     hyena_fwd_profiled,
     hyena_nd_cache_bytes,
+    hyena_nd_cache_bytes_ex,
     hyena_nd_filter_gen,
     hyena_nd_filter_workspace_bytes,
+    hyena_nd_filter_workspace_bytes_ex,
     hyena_nd_fwd,
     hyena_nd_fwd_profiled,
     hyena_nd_workspace_bytes,
+    hyena_nd_workspace_bytes_ex,
     hyena_workspace_bytes,
     lib,
 )

@@ -74,13 +74,18 @@ hipError_t fourstep_spec(const FourStepTables& tb, const float* h, float2* Y, fl
                          hipStream_t s);
 
 // --------------------------------------------------------------- 3D path
+// Transform sizes (MX, MY, MZ): (2X, 2Y, 2Z) for the zero-padded boundary,
+// (X, Y, Z) for the circular one; the kernel's offset grid has the same shape,
+// offset d at index d + M/2 per axis.
 struct NdFilterArgs {
   int X, Y, Z, C, N, W;
+  int MX, MY, MZ;
   const float *w1, *b1, *w2, *b2, *w3, *b3, *decay;
-  float* k;  // kernel on the offset grid [N][C][2X][2Y][2Z]
+  float* k;  // kernel on the offset grid [N][C][MX][MY][MZ]
 };
 struct NdConvArgs {
   int X, Y, Z, C, NO, B, n, npairs;
+  int MX, MY, MZ;
   const float* p;        // projections [B][(NO+1)C][X*Y*Z] (channel-major)
   const float* dskip;    // [NO][C]
   const float* gate;     // [B][NO][C]
@@ -88,9 +93,9 @@ struct NdConvArgs {
   float* zout;
   float* zbuf[2];        // z^{n+1} ping-pong [B][C][V]
   float* zfinal;         // z^{NO+1} [B][C][V]
-  float2* Yint;          // [ceil(B/2)][C][X][2Y][2Z]
-  float2* F;             // filter pairs [N*C/2][2X][2Y][2Z]
-  const float2* kh;      // half spectra [N*C][2X][2Y][Z+1]
+  float2* Yint;          // [ceil(B/2)][C][X][MY][MZ]
+  float2* F;             // filter pairs [N*C/2][MX][MY][MZ]
+  const float2* kh;      // half spectra [N*C][MX][MY][MZ/2+1]
   const float2* tw128;   // W_128^m
 };
 hipError_t nd_filter(const NdFilterArgs& f, float2* F, float2* kh, const float2* tw128, hipStream_t s);

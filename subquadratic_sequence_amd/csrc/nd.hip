@@ -1,10 +1,12 @@
 // 3D (HyenaND) path on gfx950: coordinate-MLP kernel, channel-mean gate and the
-// zero-padded 3D FFT convolution with gating (HyenaND explainer, gist.science,
-// "Methodology: HyenaND": Native ND Convolution, Input-Dependent Kernels,
-// Kernel Synthesis, Handling Boundaries).
+// 3D FFT convolution with gating, zero padded (non-circular) or periodic
+// (circular) (HyenaND explainer, gist.science, "Methodology: HyenaND": Native ND
+// Convolution, Input-Dependent Kernels, Kernel Synthesis, Handling Boundaries).
 //
-// Layouts: activations channel-major [B][C][X][Y][Z] (z contiguous); padded
-// transform size (MX, MY, MZ) = (2X, 2Y, 2Z), square planes (Y = Z).
+// Layouts: activations channel-major [B][C][X][Y][Z] (z contiguous); transform
+// size (MX, MY, MZ) = (2X, 2Y, 2Z) zero padded or (X, Y, Z) circular, square
+// planes (Y = Z). The kernel lives on the matching offset grid, offset d at
+// index d + M/2 per axis, at coordinates d / (M/2).
 //
 // The gate g_{b,c} is one scalar per sample and channel, so it commutes with
 // the convolution and is applied to the convolution output in the spatial
@@ -18,7 +20,8 @@
 // the Y x Z non-zero block zero padded), a pencil pass (DFT over x, X non-zero
 // inputs, times K^_c, inverse DFT over x keeping x < X) and the inverse plane
 // pass (inverse 2D DFT, crop to Y x Z, gate, skip), which also starts the next
-// order's forward plane DFT from the same LDS plane.
+// order's forward plane DFT from the same LDS plane. With the circular boundary
+// the same passes run with no zero padding and no crop (M = G).
 #include "common.h"
 #include "kernels.h"
 
@@ -33,16 +36,16 @@ __global__ __launch_bounds__(256) void nd_mlp_kernel(NdFilterArgs a) {
   __shared__ float rad[kNP];
   __shared__ float h1[kNP][kNdMaxW + 1];
   __shared__ float h2[kNP][kNdMaxW + 1];
-  const int MX = 2 * a.X, MY = 2 * a.Y, MZ = 2 * a.Z;
+  const int MX = a.MX, MY = a.MY, MZ = a.MZ;
   const int P = MX * MY * MZ;
   const int p0 = blockIdx.x * kNP;
   const int W = a.W, tid = threadIdx.x;
   for (int t = tid; t < kNP; t += 256) {
     const int pt = p0 + t;
     const int k = pt % MZ, j = (pt / MZ) % MY, i = pt / (MZ * MY);
-    const float cx = (float)(i - a.X) / (float)a.X;
-    const float cy = (float)(j - a.Y) / (float)a.Y;
-    const float cz = (float)(k - a.Z) / (float)a.Z;
+    const float cx = (float)(i - MX / 2) / (float)(MX / 2);
+    const float cy = (float)(j - MY / 2) / (float)(MY / 2);
+    const float cz = (float)(k - MZ / 2) / (float)(MZ / 2);
     cs[t][0] = cx;
     cs[t][1] = cy;
     cs[t][2] = cz;
@@ -95,7 +98,7 @@ __global__ __launch_bounds__(256) void nd_mlp_mfma_kernel(NdFilterArgs a) {
   __shared__ float cs[kNP][5];  // the three coordinates, a zero pad column, the radius
   __shared__ float buf0[kNP * LDH];  // layer 2
   __shared__ float buf1[kNP * LDH];  // layer 1
-  const int MX = 2 * a.X, MY = 2 * a.Y, MZ = 2 * a.Z;
+  const int MX = a.MX, MY = a.MY, MZ = a.MZ;
   const int P = MX * MY * MZ;
   const int p0 = blockIdx.x * kNP;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -103,9 +106,9 @@ __global__ __launch_bounds__(256) void nd_mlp_mfma_kernel(NdFilterArgs a) {
   for (int t = tid; t < kNP; t += 256) {
     const int pt = p0 + t;
     const int k = pt % MZ, j = (pt / MZ) % MY, i = pt / (MZ * MY);
-    const float cx = (float)(i - a.X) / (float)a.X;
-    const float cy = (float)(j - a.Y) / (float)a.Y;
-    const float cz = (float)(k - a.Z) / (float)a.Z;
+    const float cx = (float)(i - MX / 2) / (float)(MX / 2);
+    const float cy = (float)(j - MY / 2) / (float)(MY / 2);
+    const float cz = (float)(k - MZ / 2) / (float)(MZ / 2);
     cs[t][0] = cx;
     cs[t][1] = cy;
     cs[t][2] = cz;
@@ -189,26 +192,25 @@ __global__ __launch_bounds__(256) void nd_mlp_mfma_kernel(NdFilterArgs a) {
   }
 }
 
-// Two channels of the offset-indexed kernel, wrapped (offset d stored at d mod 2G),
+// Two channels of the offset-indexed kernel, wrapped (offset d stored at d mod M),
 // as one complex field per channel pair: F = K_{2cp} + i K_{2cp+1}.
-__global__ void nd_pack_kernel(const float* __restrict__ k, float2* __restrict__ F, int X, int Y, int Z,
+__global__ void nd_pack_kernel(const float* __restrict__ k, float2* __restrict__ F, int MX, int MY, int MZ,
                                int npairs) {
-  const int MX = 2 * X, MY = 2 * Y, MZ = 2 * Z;
   const size_t P = (size_t)MX * MY * MZ;
   const size_t idx = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
   if (idx >= P * npairs) return;
   const size_t pr = idx / P, w = idx % P;
   const int wz = (int)(w % MZ), wy = (int)((w / MZ) % MY), wx = (int)(w / ((size_t)MZ * MY));
-  const size_t o = ((size_t)((wx + X) % MX) * MY + (wy + Y) % MY) * MZ + (wz + Z) % MZ;
+  const size_t o = ((size_t)((wx + MX / 2) % MX) * MY + (wy + MY / 2) % MY) * MZ + (wz + MZ / 2) % MZ;
   F[idx] = make_float2(k[(2 * pr) * P + o], k[(2 * pr + 1) * P + o]);
 }
 
-// Per-channel half spectra (kz in [0, Z]) from the spectra of the packed pairs:
+// Per-channel half spectra (kz in [0, MZ/2]) from the spectra of the packed pairs:
 // Ha(k) = (F(k) + conj F(-k)) / 2, Hb(k) = (F(k) - conj F(-k)) / 2i, scaled by
 // 1 / (MX MY MZ) (the inverse transforms are unnormalised).
-__global__ void nd_split_kernel(const float2* __restrict__ F, float2* __restrict__ Kh, int X, int Y, int Z,
+__global__ void nd_split_kernel(const float2* __restrict__ F, float2* __restrict__ Kh, int MX, int MY, int MZ,
                                 int npairs) {
-  const int MX = 2 * X, MY = 2 * Y, MZ = 2 * Z, ZH = Z + 1;
+  const int ZH = MZ / 2 + 1;
   const size_t PH = (size_t)MX * MY * ZH, P = (size_t)MX * MY * MZ;
   const size_t idx = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
   if (idx >= PH * npairs) return;
@@ -277,7 +279,7 @@ template <int M, int E, bool INV> struct LineFrom<M, E, M, INV> {
 
 // ======================================================== plane pass
 // One workgroup per (sample pair or filter pair, channel, x-plane). The plane
-// (M x M complex, M = 2Y = 2Z) lives in LDS at [y][z] with row stride M + 1.
+// (M x M complex, M = MY = MZ) lives in LDS at [y][z] with row stride M + 1.
 // Thread t works on line t % nlines (one of the lines of a direction) as its
 // (t / nlines)-th FFT thread, so the 64 lanes of a wave sit on 64 lines.
 enum { PL_FWD_V = 0, PL_FWD_FULL = 1, PL_INV = 2, PL_INV_FWD = 3 };
@@ -323,8 +325,8 @@ __global__ __launch_bounds__(1024) void nd_plane_kernel(NdConvArgs a) {
   if (tid < 128) tw[tid] = a.tw128[tid];  // visible after the barrier that follows the plane load
 
   if constexpr (MODE == PL_FWD_FULL) {
-    // filter: full M x M complex plane, all 2X planes
-    float2* Fp = a.F + (((size_t)bp * a.npairs + c) * (2 * X) + x) * plane;
+    // filter: full M x M complex plane, all MX planes
+    float2* Fp = a.F + (((size_t)bp * a.npairs + c) * a.MX + x) * plane;
     for (int i = tid; i < M * M; i += C::THREADS) P[(i / M) * C::RS + i % M] = Fp[i];
     __syncthreads();
     plane_rows<M, false>(P, M, tw);
@@ -551,23 +553,24 @@ __global__ __launch_bounds__(1024) void nd_plane128_kernel(NdConvArgs a, int nit
 }
 
 // ======================================================= pencil pass
-// DFT over x of 64 consecutive (ky, kz) pencils; N1 = 2X = RA * RB points,
+// DFT over x of 64 consecutive (ky, kz) pencils; N1 = MX = RA * RB points,
 // n1 = j + RA r, k1 = ka + RB kb. Forward: threads (lane, j < RA) hold
-// x[j + RA r]; stage 2 threads (lane, ka < RB) end with X[ka + RB kb].
+// x[j + RA r]; stage 2 threads (lane, ka < RB) end with X[ka + RB kb]. PAD = 2
+// (zero padded: x < X = N1 / 2 non-zero and kept) or 1 (circular: all N1).
 enum { PN_CONV = 0, PN_FWD_FULL = 1 };
 
-template <int RA, int RB, int MODE>
+template <int RA, int RB, int MODE, int PAD>
 __global__ __launch_bounds__(64 * RA) void nd_pencil_kernel(NdConvArgs a) {
   constexpr int N1 = RA * RB;
   extern __shared__ float4 smem4[];
   float2* S = reinterpret_cast<float2*>(smem4);  // [RA][RB][64] / [RB][RA][64]
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
-  const int X = a.X, Y = a.Y, Z = a.Z;
-  const int MY = 2 * Y, MZ = 2 * Z, ZH = Z + 1;
+  const int X = a.X;
+  const int MY = a.MY, MZ = a.MZ, ZH = MZ / 2 + 1;
   const size_t plane = (size_t)MY * MZ;
   const int f = blockIdx.x * 64 + lane;  // flattened (ky, kz)
   const int c = blockIdx.y, bp = blockIdx.z;
-  const int nin = (MODE == PN_FWD_FULL) ? RB : RB / 2;  // non-zero r per thread
+  constexpr int nin = (MODE == PN_FWD_FULL) ? RB : RB / PAD;  // non-zero r per thread
   float2* base = (MODE == PN_FWD_FULL) ? a.F + (((size_t)bp * a.npairs + c) * N1) * plane
                                        : a.Yint + (((size_t)bp * a.C + c) * X) * plane;
   // forward stage 1: threads (lane, j)
@@ -599,7 +602,7 @@ __global__ __launch_bounds__(64 * RA) void nd_pencil_kernel(NdConvArgs a) {
     // times K^_c(kx, ky, kz); kz > Z from the conjugate symmetric half spectrum
     const int ky = f / MZ, kz = f % MZ;
     const float2* Kc = a.kh + (size_t)(a.n * a.C + c) * N1 * MY * ZH;
-    const bool lower = kz <= Z;
+    const bool lower = kz <= MZ / 2;
     const int ky2 = lower ? ky : (MY - ky) % MY;
     const int kz2 = lower ? kz : MZ - kz;
 #pragma unroll
@@ -629,7 +632,7 @@ __global__ __launch_bounds__(64 * RA) void nd_pencil_kernel(NdConvArgs a) {
   for (int ka = 0; ka < RB; ++ka) q[ka] = S[(ka * RA + w) * 64 + lane];
   Dft<RB, true>::run(q);
 #pragma unroll
-  for (int nb = 0; nb < RB / 2; ++nb) base[(size_t)(w + RA * nb) * plane + f] = q[nb];
+  for (int nb = 0; nb < RB / PAD; ++nb) base[(size_t)(w + RA * nb) * plane + f] = q[nb];
 }
 
 // Persistent pencil pass for 2X = 128 (the 64^3 grids), conv mode: items are
@@ -849,7 +852,7 @@ static hipError_t launch_plane_t(const NdConvArgs& a, dim3 grid, hipStream_t s) 
 
 template <int MODE>
 static hipError_t launch_plane(const NdConvArgs& a, dim3 grid, hipStream_t s) {
-  switch (2 * a.Y) {
+  switch (a.MY) {
     case 8: return launch_plane_t<8, MODE>(a, grid, s);
     case 16: return launch_plane_t<16, MODE>(a, grid, s);
     case 32: return launch_plane_t<32, MODE>(a, grid, s);
@@ -859,30 +862,37 @@ static hipError_t launch_plane(const NdConvArgs& a, dim3 grid, hipStream_t s) {
   }
 }
 
-template <int RA, int RB, int MODE>
+template <int RA, int RB, int MODE, int PAD>
 static hipError_t launch_pencil_t(const NdConvArgs& a, dim3 grid, hipStream_t s) {
   const size_t lds = (size_t)RA * RB * 64 * 8;
-  auto fn = nd_pencil_kernel<RA, RB, MODE>;
+  auto fn = nd_pencil_kernel<RA, RB, MODE, PAD>;
   hipError_t e = nd_allow_lds((const void*)fn, lds);
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(fn, grid, dim3(64 * RA), lds, s, a);
   return hipGetLastError();
 }
 
-template <int MODE>
-static hipError_t launch_pencil(const NdConvArgs& a, dim3 grid, hipStream_t s) {
-  switch (2 * a.X) {
-    case 8: return launch_pencil_t<4, 2, MODE>(a, grid, s);
-    case 16: return launch_pencil_t<4, 4, MODE>(a, grid, s);
-    case 32: return launch_pencil_t<8, 4, MODE>(a, grid, s);
-    case 64: return launch_pencil_t<8, 8, MODE>(a, grid, s);
-    case 128: return launch_pencil_t<16, 8, MODE>(a, grid, s);
+template <int MODE, int PAD>
+static hipError_t launch_pencil_p(const NdConvArgs& a, dim3 grid, hipStream_t s) {
+  switch (a.MX) {
+    case 8: return launch_pencil_t<4, 2, MODE, PAD>(a, grid, s);
+    case 16: return launch_pencil_t<4, 4, MODE, PAD>(a, grid, s);
+    case 32: return launch_pencil_t<8, 4, MODE, PAD>(a, grid, s);
+    case 64: return launch_pencil_t<8, 8, MODE, PAD>(a, grid, s);
+    case 128: return launch_pencil_t<16, 8, MODE, PAD>(a, grid, s);
     default: return hipErrorInvalidValue;
   }
 }
 
+template <int MODE>
+static hipError_t launch_pencil(const NdConvArgs& a, dim3 grid, hipStream_t s) {
+  // the filter transform has no zero half; the conv pass has one unless circular
+  if (MODE == PN_FWD_FULL || a.MX == a.X) return launch_pencil_p<MODE, 1>(a, grid, s);
+  return launch_pencil_p<MODE, 2>(a, grid, s);
+}
+
 hipError_t nd_filter(const NdFilterArgs& f, float2* F, float2* kh, const float2* tw128, hipStream_t s) {
-  const int MX = 2 * f.X, MY = 2 * f.Y, MZ = 2 * f.Z;
+  const int MX = f.MX, MY = f.MY, MZ = f.MZ;
   const size_t P = (size_t)MX * MY * MZ;
   if (f.W == 64)
     hipLaunchKernelGGL(nd_mlp_mfma_kernel<64>, dim3((unsigned)(P / kNP)), dim3(256), 0, s, f);
@@ -895,20 +905,23 @@ hipError_t nd_filter(const NdFilterArgs& f, float2* F, float2* kh, const float2*
   const int npairs = f.N * f.C / 2;
   const size_t tot = P * npairs;
   hipLaunchKernelGGL(nd_pack_kernel, dim3((unsigned)((tot + 255) / 256)), dim3(256), 0, s, (const float*)f.k, F,
-                     f.X, f.Y, f.Z, npairs);
+                     MX, MY, MZ, npairs);
   if ((e = hipGetLastError()) != hipSuccess) return e;
   NdConvArgs a{};
   a.X = f.X;
   a.Y = f.Y;
   a.Z = f.Z;
+  a.MX = MX;
+  a.MY = MY;
+  a.MZ = MZ;
   a.F = F;
   a.npairs = npairs;
   a.tw128 = tw128;
   if ((e = launch_plane<PL_FWD_FULL>(a, dim3(MX, npairs, 1), s)) != hipSuccess) return e;
   if ((e = launch_pencil<PN_FWD_FULL>(a, dim3((unsigned)(MY * MZ / 64), npairs, 1), s)) != hipSuccess) return e;
-  const size_t th = (size_t)MX * MY * (f.Z + 1) * npairs;
+  const size_t th = (size_t)MX * MY * (MZ / 2 + 1) * npairs;
   hipLaunchKernelGGL(nd_split_kernel, dim3((unsigned)((th + 255) / 256)), dim3(256), 0, s, (const float2*)F, kh,
-                     f.X, f.Y, f.Z, npairs);
+                     MX, MY, MZ, npairs);
   return hipGetLastError();
 }
 
@@ -972,14 +985,15 @@ static hipError_t launch_pencil128(const NdConvArgs& a, int nitems, hipStream_t 
 hipError_t nd_conv(const NdConvArgs& in, hipStream_t s) {
   NdConvArgs a = in;
   const int BP = (a.B + 1) / 2;
-  const unsigned nf = (unsigned)(4 * a.Y * a.Z / 64);
-  const bool p128 = 2 * a.Y == 128 && a.Y == a.Z;
+  const unsigned nf = (unsigned)(a.MY * a.MZ / 64);
+  // persistent kernels: the zero-padded 64^3 case (128-point axes, half of each kept)
+  const bool p128 = a.MY == 128 && a.MY == 2 * a.Y && a.Y == a.Z;
   const int nplanes = a.X * a.C * BP;
   hipError_t e = p128 ? launch_plane128<PL_FWD_V>(a, nplanes, s) : launch_plane<PL_FWD_V>(a, dim3(a.X, a.C, BP), s);
   if (e != hipSuccess) return e;
   for (int n = 0; n < a.NO; ++n) {
     a.n = n;
-    if (2 * a.X == 128) {
+    if (a.MX == 128 && a.MX == 2 * a.X) {
       e = launch_pencil128(a, (int)(nf * a.C * BP), s);
     } else {
       e = launch_pencil<PN_CONV>(a, dim3(nf, a.C, BP), s);

@@ -16,23 +16,35 @@ constexpr size_t kAlign = 256;
 bool pow2_in(int v, int lo, int hi) { return v >= lo && v <= hi && (v & (v - 1)) == 0; }
 bool aligned16(const void* p) { return p != nullptr && ((uintptr_t)p & 15u) == 0; }
 
-bool nd_shape_ok(int X, int Y, int Z, int C, int N) {
-  return pow2_in(X, 4, 64) && pow2_in(Y, 4, 64) && Z == Y && C >= 64 && C <= 4096 && C % 64 == 0 && N >= 1 &&
+bool boundary_ok(int bd) { return bd == HYENA_ND_ZERO_PAD || bd == HYENA_ND_CIRCULAR; }
+// transform length per grid length: 2 (zero padded) or 1 (circular)
+int pad_of(int bd) { return bd == HYENA_ND_CIRCULAR ? 1 : 2; }
+
+// Transform lengths up to 128 (the twiddle table W_128); at least 8 points per axis.
+bool nd_shape_ok(int X, int Y, int Z, int C, int N, int bd) {
+  if (!boundary_ok(bd)) return false;
+  const int lo = 8 / pad_of(bd), hi = 128 / pad_of(bd);
+  return pow2_in(X, lo, hi) && pow2_in(Y, lo, hi) && Z == Y && C >= 64 && C <= 4096 && C % 64 == 0 && N >= 1 &&
          N <= 4;
 }
 
-size_t pts(int X, int Y, int Z) { return (size_t)8 * X * Y * Z; }  // (2X)(2Y)(2Z)
+// transform points (MX)(MY)(MZ)
+size_t pts(int X, int Y, int Z, int bd) {
+  const size_t p = pad_of(bd);
+  return p * p * p * X * Y * Z;
+}
 
 struct NdCache {
   size_t tw, kh, total;
 };
-NdCache nd_cache(int X, int Y, int Z, int C, int N) {
+NdCache nd_cache(int X, int Y, int Z, int C, int N, int bd) {
+  const int p = pad_of(bd);
   NdCache c{};
   size_t off = 0;
   c.tw = off;
   off = align_up(off + 128 * 8, kAlign);
   c.kh = off;
-  off = align_up(off + (size_t)N * C * (2 * X) * (2 * Y) * (Z + 1) * 8, kAlign);
+  off = align_up(off + (size_t)N * C * (p * X) * (p * Y) * (p * Z / 2 + 1) * 8, kAlign);
   c.total = off;
   return c;
 }
@@ -40,13 +52,13 @@ NdCache nd_cache(int X, int Y, int Z, int C, int N) {
 struct NdFws {
   size_t k, F, total;
 };
-NdFws nd_fws(int X, int Y, int Z, int C, int N) {
+NdFws nd_fws(int X, int Y, int Z, int C, int N, int bd) {
   NdFws w{};
   size_t off = 0;
   w.k = off;
-  off = align_up(off + (size_t)N * C * pts(X, Y, Z) * 4, kAlign);
+  off = align_up(off + (size_t)N * C * pts(X, Y, Z, bd) * 4, kAlign);
   w.F = off;
-  off = align_up(off + (size_t)N * (C / 2) * pts(X, Y, Z) * 8, kAlign);
+  off = align_up(off + (size_t)N * (C / 2) * pts(X, Y, Z, bd) * 8, kAlign);
   w.total = off;
   return w;
 }
@@ -54,7 +66,8 @@ NdFws nd_fws(int X, int Y, int Z, int C, int N) {
 struct NdWs {
   size_t wt_in, wt_out, p, zfinal, z0, z1, Y, part, gate, total;
 };
-NdWs nd_ws(int B, int X, int Y, int Z, int C, int N) {
+NdWs nd_ws(int B, int X, int Y, int Z, int C, int N, int bd) {
+  const int pd = pad_of(bd);
   NdWs w{};
   const size_t V = (size_t)X * Y * Z;
   const size_t J = (size_t)(N + 1) * C;
@@ -72,7 +85,7 @@ NdWs nd_ws(int B, int X, int Y, int Z, int C, int N) {
   w.z1 = off;
   off = align_up(off + (size_t)B * C * V * 4, kAlign);
   w.Y = off;
-  off = align_up(off + (size_t)((B + 1) / 2) * C * X * (4 * (size_t)Y * Z) * 8, kAlign);
+  off = align_up(off + (size_t)((B + 1) / 2) * C * X * ((size_t)pd * Y * pd * Z) * 8, kAlign);
   w.part = off;
   off = align_up(off + hy::nd_gate_partial_floats(B, C, (int)V) * 4, kAlign);
   w.gate = off;
@@ -91,27 +104,40 @@ int device_ok() {
 
 extern "C" {
 
+size_t hyena_nd_cache_bytes_ex(int X, int Y, int Z, int C, int N, int boundary) {
+  if (!nd_shape_ok(X, Y, Z, C, N, boundary)) return 0;
+  return nd_cache(X, Y, Z, C, N, boundary).total;
+}
+
+size_t hyena_nd_filter_workspace_bytes_ex(int X, int Y, int Z, int C, int N, int boundary) {
+  if (!nd_shape_ok(X, Y, Z, C, N, boundary)) return 0;
+  return nd_fws(X, Y, Z, C, N, boundary).total;
+}
+
+size_t hyena_nd_workspace_bytes_ex(int B, int X, int Y, int Z, int C, int N, int boundary) {
+  if (!nd_shape_ok(X, Y, Z, C, N, boundary) || B < 1) return 0;
+  if ((long long)B * X * Y * Z * (N + 1) * C >= (1LL << 31)) return 0;
+  return nd_ws(B, X, Y, Z, C, N, boundary).total;
+}
+
 size_t hyena_nd_cache_bytes(int X, int Y, int Z, int C, int N) {
-  if (!nd_shape_ok(X, Y, Z, C, N)) return 0;
-  return nd_cache(X, Y, Z, C, N).total;
+  return hyena_nd_cache_bytes_ex(X, Y, Z, C, N, HYENA_ND_ZERO_PAD);
 }
 
 size_t hyena_nd_filter_workspace_bytes(int X, int Y, int Z, int C, int N) {
-  if (!nd_shape_ok(X, Y, Z, C, N)) return 0;
-  return nd_fws(X, Y, Z, C, N).total;
+  return hyena_nd_filter_workspace_bytes_ex(X, Y, Z, C, N, HYENA_ND_ZERO_PAD);
 }
 
 size_t hyena_nd_workspace_bytes(int B, int X, int Y, int Z, int C, int N) {
-  if (!nd_shape_ok(X, Y, Z, C, N) || B < 1) return 0;
-  if ((long long)B * X * Y * Z * (N + 1) * C >= (1LL << 31)) return 0;
-  return nd_ws(B, X, Y, Z, C, N).total;
+  return hyena_nd_workspace_bytes_ex(B, X, Y, Z, C, N, HYENA_ND_ZERO_PAD);
 }
 
-int hyena_nd_layer_init(hyena_nd_layer* layer, int X, int Y, int Z, int C, int N, void* cache, size_t cache_bytes) {
+int hyena_nd_layer_init_ex(hyena_nd_layer* layer, int X, int Y, int Z, int C, int N, int boundary, void* cache,
+                           size_t cache_bytes) {
   if (layer == nullptr) return HYENA_ERR_INVALID_ARG;
-  if (!nd_shape_ok(X, Y, Z, C, N)) return HYENA_ERR_UNSUPPORTED;
+  if (!nd_shape_ok(X, Y, Z, C, N, boundary)) return HYENA_ERR_UNSUPPORTED;
   if (!aligned16(cache)) return HYENA_ERR_INVALID_ARG;
-  if (cache_bytes < nd_cache(X, Y, Z, C, N).total) return HYENA_ERR_WORKSPACE;
+  if (cache_bytes < nd_cache(X, Y, Z, C, N, boundary).total) return HYENA_ERR_WORKSPACE;
   layer->X = X;
   layer->Y = Y;
   layer->Z = Z;
@@ -120,23 +146,28 @@ int hyena_nd_layer_init(hyena_nd_layer* layer, int X, int Y, int Z, int C, int N
   layer->built = 0;
   layer->cache = cache;
   layer->cache_bytes = cache_bytes;
+  layer->boundary = boundary;
   return HYENA_OK;
+}
+
+int hyena_nd_layer_init(hyena_nd_layer* layer, int X, int Y, int Z, int C, int N, void* cache, size_t cache_bytes) {
+  return hyena_nd_layer_init_ex(layer, X, Y, Z, C, N, HYENA_ND_ZERO_PAD, cache, cache_bytes);
 }
 
 int hyena_nd_filter_gen(hyena_nd_layer* layer, const hyena_nd_filter_params* p, float* k_out, void* ws,
                         size_t ws_bytes, hipStream_t stream) {
   if (layer == nullptr || p == nullptr) return HYENA_ERR_INVALID_ARG;
-  const int X = layer->X, Y = layer->Y, Z = layer->Z, C = layer->C, N = layer->N;
-  if (!nd_shape_ok(X, Y, Z, C, N)) return HYENA_ERR_UNSUPPORTED;
+  const int X = layer->X, Y = layer->Y, Z = layer->Z, C = layer->C, N = layer->N, bd = layer->boundary;
+  if (!nd_shape_ok(X, Y, Z, C, N, bd)) return HYENA_ERR_UNSUPPORTED;
   if (!aligned16(layer->cache)) return HYENA_ERR_INVALID_ARG;
-  const NdCache cl = nd_cache(X, Y, Z, C, N);
+  const NdCache cl = nd_cache(X, Y, Z, C, N, bd);
   if (layer->cache_bytes < cl.total) return HYENA_ERR_WORKSPACE;
   if (p->width < 1 || p->width > 128) return HYENA_ERR_UNSUPPORTED;
   const void* ptrs[] = {p->w1, p->b1, p->w2, p->b2, p->w3, p->b3, p->decay, ws};
   for (const void* q : ptrs)
     if (!aligned16(q)) return HYENA_ERR_INVALID_ARG;
   if (k_out != nullptr && !aligned16(k_out)) return HYENA_ERR_INVALID_ARG;
-  const NdFws fw = nd_fws(X, Y, Z, C, N);
+  const NdFws fw = nd_fws(X, Y, Z, C, N, bd);
   if (ws_bytes < fw.total) return HYENA_ERR_WORKSPACE;
   if (device_ok() != HYENA_OK) return HYENA_ERR_HIP;
 
@@ -145,7 +176,9 @@ int hyena_nd_filter_gen(hyena_nd_layer* layer, const hyena_nd_filter_params* p, 
   layer->built = 0;
   float2* tw = reinterpret_cast<float2*>(cb + cl.tw);
   HY_CHECK_HIP(hy::twiddles(tw, 128, 128, stream));
-  hy::NdFilterArgs f{X, Y, Z, C, N, p->width, p->w1, p->b1, p->w2, p->b2, p->w3, p->b3, p->decay,
+  const int pd = pad_of(bd);
+  hy::NdFilterArgs f{X,     Y,     Z,     C,     N,     p->width, pd * X,   pd * Y,
+                     pd * Z, p->w1, p->b1, p->w2, p->b2, p->w3,    p->b3,    p->decay,
                      k_out ? k_out : reinterpret_cast<float*>(wsb + fw.k)};
   HY_CHECK_HIP(hy::nd_filter(f, reinterpret_cast<float2*>(wsb + fw.F), reinterpret_cast<float2*>(cb + cl.kh), tw,
                              stream));
@@ -165,13 +198,13 @@ int nd_fwd_impl(const hyena_nd_layer* layer, const float* u, const float* w_in, 
   for (const void* q : ptrs)
     if (!aligned16(q)) return HYENA_ERR_INVALID_ARG;
   if (B < 1) return HYENA_ERR_INVALID_ARG;
-  const int X = layer->X, Y = layer->Y, Z = layer->Z, C = layer->C, N = layer->N;
-  if (!nd_shape_ok(X, Y, Z, C, N)) return HYENA_ERR_UNSUPPORTED;
+  const int X = layer->X, Y = layer->Y, Z = layer->Z, C = layer->C, N = layer->N, bd = layer->boundary;
+  if (!nd_shape_ok(X, Y, Z, C, N, bd)) return HYENA_ERR_UNSUPPORTED;
   if (!layer->built || !aligned16(layer->cache)) return HYENA_ERR_LAYER_MISMATCH;
-  const NdCache cl = nd_cache(X, Y, Z, C, N);
+  const NdCache cl = nd_cache(X, Y, Z, C, N, bd);
   if (layer->cache_bytes < cl.total) return HYENA_ERR_LAYER_MISMATCH;
   if ((long long)B * X * Y * Z * (N + 1) * C >= (1LL << 31)) return HYENA_ERR_UNSUPPORTED;
-  const NdWs w = nd_ws(B, X, Y, Z, C, N);
+  const NdWs w = nd_ws(B, X, Y, Z, C, N, bd);
   if (ws_bytes < w.total) return HYENA_ERR_WORKSPACE;
   if (device_ok() != HYENA_OK) return HYENA_ERR_HIP;
 
@@ -195,6 +228,9 @@ int nd_fwd_impl(const hyena_nd_layer* layer, const float* u, const float* w_in, 
   a.X = X;
   a.Y = Y;
   a.Z = Z;
+  a.MX = pad_of(bd) * X;
+  a.MY = pad_of(bd) * Y;
+  a.MZ = pad_of(bd) * Z;
   a.C = C;
   a.NO = N;
   a.B = B;

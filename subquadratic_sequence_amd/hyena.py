@@ -40,7 +40,12 @@ class NDFilterParams(ctypes.Structure):
 
 class NDLayer(ctypes.Structure):
     _fields_ = [("X", _i), ("Y", _i), ("Z", _i), ("C", _i), ("N", _i), ("built", _i), ("cache", _vp),
-                ("cache_bytes", _sz)]
+                ("cache_bytes", _sz), ("boundary", _i)]
+
+
+# hyena_nd_boundary
+ND_ZERO_PAD = 0
+ND_CIRCULAR = 1
 
 
 # name -> (restype, argtypes)
@@ -58,6 +63,10 @@ SIGNATURES = {
     "hyena_nd_filter_workspace_bytes": (_sz, [_i, _i, _i, _i, _i]),
     "hyena_nd_workspace_bytes": (_sz, [_i, _i, _i, _i, _i, _i]),
     "hyena_nd_layer_init": (_i, [ctypes.POINTER(NDLayer), _i, _i, _i, _i, _i, _vp, _sz]),
+    "hyena_nd_cache_bytes_ex": (_sz, [_i, _i, _i, _i, _i, _i]),
+    "hyena_nd_filter_workspace_bytes_ex": (_sz, [_i, _i, _i, _i, _i, _i]),
+    "hyena_nd_workspace_bytes_ex": (_sz, [_i, _i, _i, _i, _i, _i, _i]),
+    "hyena_nd_layer_init_ex": (_i, [ctypes.POINTER(NDLayer), _i, _i, _i, _i, _i, _i, _vp, _sz]),
     "hyena_nd_filter_gen": (_i, [ctypes.POINTER(NDLayer), ctypes.POINTER(NDFilterParams), _vp, _vp, _sz, _vp]),
     "hyena_nd_fwd": (_i, [ctypes.POINTER(NDLayer), _vp, _vp, _vp, _vp, _vp, _vp, _i, _vp, _vp, _sz, _vp]),
     "hyena_nd_fwd_profiled": (_i, [ctypes.POINTER(NDLayer), _vp, _vp, _vp, _vp, _vp, _vp, _i, _vp, _vp, _sz, _vp,
@@ -202,22 +211,37 @@ def hyena_nd_workspace_bytes(B, X, Y, Z, C, N) -> int:
     return lib().hyena_nd_workspace_bytes(B, X, Y, Z, C, N)
 
 
+def hyena_nd_cache_bytes_ex(X, Y, Z, C, N, boundary) -> int:
+    return lib().hyena_nd_cache_bytes_ex(X, Y, Z, C, N, boundary)
+
+
+def hyena_nd_filter_workspace_bytes_ex(X, Y, Z, C, N, boundary) -> int:
+    return lib().hyena_nd_filter_workspace_bytes_ex(X, Y, Z, C, N, boundary)
+
+
+def hyena_nd_workspace_bytes_ex(B, X, Y, Z, C, N, boundary) -> int:
+    return lib().hyena_nd_workspace_bytes_ex(B, X, Y, Z, C, N, boundary)
+
+
 class HyenaNDLayer:
-    def __init__(self, X: int, Y: int, Z: int, C: int, N: int, device="cuda"):
-        nbytes = hyena_nd_cache_bytes(X, Y, Z, C, N)
+    """3D layer; boundary ND_ZERO_PAD (non-circular, default) or ND_CIRCULAR."""
+
+    def __init__(self, X: int, Y: int, Z: int, C: int, N: int, device="cuda", boundary: int = ND_ZERO_PAD):
+        nbytes = hyena_nd_cache_bytes_ex(X, Y, Z, C, N, boundary)
         if nbytes == 0:
-            raise HyenaError(2, "hyena_nd_cache_bytes")
+            raise HyenaError(2, "hyena_nd_cache_bytes_ex")
         self.cache = torch.empty(nbytes, dtype=torch.uint8, device=device)
         self.c = NDLayer()
-        _check(lib().hyena_nd_layer_init(ctypes.byref(self.c), X, Y, Z, C, N, _ptr(self.cache), nbytes),
-               "hyena_nd_layer_init")
+        _check(lib().hyena_nd_layer_init_ex(ctypes.byref(self.c), X, Y, Z, C, N, boundary, _ptr(self.cache),
+                                            nbytes), "hyena_nd_layer_init_ex")
         self.X, self.Y, self.Z, self.C, self.N = X, Y, Z, C, N
+        self.boundary = boundary
 
 
 def hyena_nd_filter_gen(layer: HyenaNDLayer, w1, b1, w2, b2, w3, b3, decay, k_out=None, ws=None):
     width = w1.shape[1]
     p = NDFilterParams(width, _ptr(w1), _ptr(b1), _ptr(w2), _ptr(b2), _ptr(w3), _ptr(b3), _ptr(decay))
-    need = hyena_nd_filter_workspace_bytes(layer.X, layer.Y, layer.Z, layer.C, layer.N)
+    need = hyena_nd_filter_workspace_bytes_ex(layer.X, layer.Y, layer.Z, layer.C, layer.N, layer.boundary)
     if ws is None:
         ws = torch.empty(max(need, 1), dtype=torch.uint8, device=layer.cache.device)
     st = lib().hyena_nd_filter_gen(ctypes.byref(layer.c), ctypes.byref(p), _ptr(k_out), _ptr(ws), ws.numel(),
@@ -231,7 +255,7 @@ def hyena_nd_fwd(layer: HyenaNDLayer, u, w_in, dskip, gate_a, gate_b, w_out, y=N
     if y is None:
         y = torch.empty_like(u)
     if ws is None:
-        need = hyena_nd_workspace_bytes(B, layer.X, layer.Y, layer.Z, layer.C, layer.N)
+        need = hyena_nd_workspace_bytes_ex(B, layer.X, layer.Y, layer.Z, layer.C, layer.N, layer.boundary)
         ws = torch.empty(max(need, 1), dtype=torch.uint8, device=u.device)
     st = lib().hyena_nd_fwd(ctypes.byref(layer.c), _ptr(u), _ptr(w_in), _ptr(dskip), _ptr(gate_a), _ptr(gate_b),
                             _ptr(w_out), B, _ptr(y), _ptr(ws), ws.numel(), _stream())

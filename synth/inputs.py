@@ -99,6 +99,7 @@ class HyenaNDInputs:
     w3: np.ndarray       # [W, N*C]
     b3: np.ndarray       # [N*C]
     decay: np.ndarray    # [C]
+    circular: bool = False  # periodic grid (circular convolution) instead of zero padding
     meta: dict = field(default_factory=dict)
 
     @property
@@ -145,13 +146,14 @@ def make_1d(seed: int, B: int, L: int, D: int, N: int = 2, K: int = 16, W: int =
 
 
 def make_nd(seed: int, B: int, X: int, Y: int, Z: int, C: int, N: int = 2, W: int = 64,
-            u_mean_spread: float = 0.0) -> HyenaNDInputs:
+            u_mean_spread: float = 0.0, circular: bool = False) -> HyenaNDInputs:
     """Draw one 3D workload (fp32).
 
     u ~ N(0, 1), plus an optional per-(sample, channel) offset ~ N(0, u_mean_spread^2)
     so that the channel-mean gate sees means away from zero.
     w_in, w_out ~ N(0, 1/C); dskip, gate_a, gate_b ~ N(0, 1);
     MLP weights and biases ~ U(-1/sqrt(fan_in), 1/sqrt(fan_in)).
+    `circular` selects the periodic boundary; it changes no draw.
     """
     rng = np.random.default_rng(seed)
     u = rng.standard_normal((B, X, Y, Z, C))
@@ -172,7 +174,7 @@ def make_nd(seed: int, B: int, X: int, Y: int, Z: int, C: int, N: int = 2, W: in
     b3 = _uniform(rng, (N * C,), 1 / math.sqrt(W)).astype(np.float32)
     return HyenaNDInputs(B=B, X=X, Y=Y, Z=Z, C=C, N=N, W=W, u=u, w_in=w_in, dskip=dskip,
                          gate_a=gate_a, gate_b=gate_b, w_out=w_out, w1=w1, b1=b1, w2=w2,
-                         b2=b2, w3=w3, b3=b3, decay=decay_rates(C),
+                         b2=b2, w3=w3, b3=b3, decay=decay_rates(C), circular=circular,
                          meta=dict(seed=seed, u_mean_spread=u_mean_spread))
 
 
@@ -194,6 +196,11 @@ TEST_SHAPES = {
     "order2_bf16_L256k_D64": dict(kind="1d", seed=31, B=1, L=1 << 18, D=64, N=2, K=16, dtype="bf16",
                                   u_scale=1 / 8.0),
     "order2_f32_L512k_D64": dict(kind="1d", seed=32, B=1, L=1 << 19, D=64, N=2, K=16, dtype="f32"),
+    # periodic 3D grids (circular boundary): the 3D workload's inputs and shape
+    # with an unpadded 64^3 transform, and a 128^3 grid (128-point axes)
+    "nd3d_circ_f32_B2_C128_64cube": dict(kind="nd", seed=5, B=2, X=64, Y=64, Z=64, C=128, N=2, circular=True),
+    "nd3d_circ_f32_B1_C64_128cube": dict(kind="nd", seed=33, B=1, X=128, Y=128, Z=128, C=64, N=2,
+                                         circular=True),
 }
 
 

@@ -44,9 +44,9 @@ def make(name):
         np.savez(out, t=ts, y=y)
     else:
         pts = points_3d(inp.X, inp.Y, inp.Z, COUNT, cfg["seed"])
-        K = oracle.nd_filter(inp.filter_params, inp.X, inp.Y, inp.Z, inp.N, inp.C)
+        K = oracle.nd_filter(inp.filter_params, inp.X, inp.Y, inp.Z, inp.N, inp.C, circular=inp.circular)
         y = oracle.hyena_nd_fwd_sampled(inp.u, inp.w_in, inp.dskip, inp.gate_a, inp.gate_b, inp.w_out, K, pts,
-                                        chunk=4)
+                                        chunk=4, circular=inp.circular)
         np.savez(out, points=pts, y=y)
     print(f"{name}: wrote {out} in {time.time() - t0:.0f} s", flush=True)
 

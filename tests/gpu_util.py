@@ -59,10 +59,12 @@ def gpu_nd(inp, with_k: bool = False):
     """Runs hyena_nd_filter_gen + hyena_nd_fwd on cuda:0; returns y (float64 numpy) [and K]."""
     import torch
     import subquadratic_sequence_amd as hs
-    layer = hs.HyenaNDLayer(inp.X, inp.Y, inp.Z, inp.C, inp.N)
+    bd = hs.ND_CIRCULAR if inp.circular else hs.ND_ZERO_PAD
+    layer = hs.HyenaNDLayer(inp.X, inp.Y, inp.Z, inp.C, inp.N, boundary=bd)
+    pf = 1 if inp.circular else 2
     k_out = None
     if with_k:
-        k_out = torch.empty(inp.N, inp.C, 2 * inp.X, 2 * inp.Y, 2 * inp.Z, device="cuda")
+        k_out = torch.empty(inp.N, inp.C, pf * inp.X, pf * inp.Y, pf * inp.Z, device="cuda")
     hs.hyena_nd_filter_gen(layer, to_dev(inp.w1), to_dev(inp.b1), to_dev(inp.w2), to_dev(inp.b2), to_dev(inp.w3),
                            to_dev(inp.b3), to_dev(inp.decay), k_out=k_out)
     y = hs.hyena_nd_fwd(layer, to_dev(inp.u), to_dev(inp.w_in), to_dev(inp.dskip), to_dev(inp.gate_a),
@@ -76,6 +78,7 @@ def gpu_nd(inp, with_k: bool = False):
 
 def oracle_nd(inp, conv: str = "fft"):
     import oracle
-    K = oracle.nd_filter(inp.filter_params, inp.X, inp.Y, inp.Z, inp.N, inp.C)
-    y = oracle.hyena_nd_fwd(inp.u, inp.w_in, inp.dskip, inp.gate_a, inp.gate_b, inp.w_out, K, conv=conv)
+    K = oracle.nd_filter(inp.filter_params, inp.X, inp.Y, inp.Z, inp.N, inp.C, circular=inp.circular)
+    y = oracle.hyena_nd_fwd(inp.u, inp.w_in, inp.dskip, inp.gate_a, inp.gate_b, inp.w_out, K, conv=conv,
+                            circular=inp.circular)
     return y, K

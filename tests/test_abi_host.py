@@ -153,3 +153,48 @@ def test_filter_gen_validation(hy):
     bad = hy.FilterParams(8, 64, p, None, p, p, p, p, p)
     assert L.hyena_filter_gen(ctypes.byref(layer), ctypes.byref(bad), None, p, need, None) == 1
     assert L.hyena_filter_gen(ctypes.byref(layer), ctypes.byref(fp), None, p, need - 1, None) == 3
+
+
+# ------------------------------------------------------------- 3D boundary
+
+def test_nd_size_queries_by_boundary(hy):
+    al = lambda x: (x + 255) // 256 * 256  # noqa: E731
+    X = Y = Z = 64
+    C, N = 128, 2
+    # cache: W_128 table + half spectra N C MX MY (MZ/2 + 1) complex64
+    assert hy.hyena_nd_cache_bytes(X, Y, Z, C, N) == al(128 * 8) + al(N * C * 128 * 128 * 65 * 8)
+    assert hy.hyena_nd_cache_bytes_ex(X, Y, Z, C, N, hy.ND_ZERO_PAD) == hy.hyena_nd_cache_bytes(X, Y, Z, C, N)
+    assert hy.hyena_nd_cache_bytes_ex(X, Y, Z, C, N, hy.ND_CIRCULAR) == al(128 * 8) + al(N * C * 64 * 64 * 33 * 8)
+    # the circular transform has 8x fewer points: filter workspace and intermediate shrink
+    assert (hy.hyena_nd_filter_workspace_bytes_ex(X, Y, Z, C, N, hy.ND_CIRCULAR) * 8
+            == hy.hyena_nd_filter_workspace_bytes(X, Y, Z, C, N))
+    assert (hy.hyena_nd_workspace_bytes_ex(2, X, Y, Z, C, N, hy.ND_CIRCULAR)
+            < hy.hyena_nd_workspace_bytes(2, X, Y, Z, C, N))
+    # ranges: zero padded X in [4, 64], circular X in [8, 128]; Y = Z; unknown boundary
+    assert hy.hyena_nd_cache_bytes_ex(4, 4, 4, 64, 1, hy.ND_ZERO_PAD) > 0
+    assert hy.hyena_nd_cache_bytes_ex(4, 4, 4, 64, 1, hy.ND_CIRCULAR) == 0
+    assert hy.hyena_nd_cache_bytes_ex(128, 128, 128, 64, 1, hy.ND_ZERO_PAD) == 0
+    assert hy.hyena_nd_cache_bytes_ex(128, 128, 128, 64, 1, hy.ND_CIRCULAR) > 0
+    assert hy.hyena_nd_cache_bytes_ex(8, 8, 16, 64, 1, hy.ND_CIRCULAR) == 0
+    assert hy.hyena_nd_cache_bytes_ex(8, 8, 8, 64, 1, 2) == 0
+    assert hy.hyena_nd_workspace_bytes_ex(1, 8, 8, 8, 64, 1, -1) == 0
+
+
+def test_nd_layer_init_ex(hy):
+    L = hy.lib()
+    keep, p = _aligned_buffer(16)
+    nd = hy.NDLayer()
+    nd.boundary = 7
+    assert L.hyena_nd_layer_init(ctypes.byref(nd), 8, 8, 8, 64, 2, p, 1 << 30) == 0
+    assert nd.boundary == hy.ND_ZERO_PAD
+    assert L.hyena_nd_layer_init_ex(ctypes.byref(nd), 8, 8, 8, 64, 2, 3, p, 1 << 30) == 2
+    assert L.hyena_nd_layer_init_ex(ctypes.byref(nd), 8, 8, 8, 64, 2, hy.ND_CIRCULAR, p, 16) == 3
+    assert L.hyena_nd_layer_init_ex(ctypes.byref(nd), 8, 8, 8, 64, 2, hy.ND_CIRCULAR, p, 1 << 30) == 0
+    assert (nd.X, nd.C, nd.N, nd.built, nd.boundary) == (8, 64, 2, 0, hy.ND_CIRCULAR)
+    # the forward checks the workspace against the layer's own boundary
+    nd.built = 1
+    need = hy.hyena_nd_workspace_bytes_ex(1, 8, 8, 8, 64, 2, hy.ND_CIRCULAR)
+    assert L.hyena_nd_fwd(ctypes.byref(nd), p, p, p, p, p, p, 1, p, p, need - 1, None) == 3
+    # a boundary changed behind the library's back is refused
+    nd.boundary = 5
+    assert L.hyena_nd_fwd(ctypes.byref(nd), p, p, p, p, p, p, 1, p, p, need, None) == 2

@@ -51,3 +51,10 @@ def test_valu_summary_is_void_after_a_kernel_change(tmp_path):
     p.write_text("@conv_valu_instr_per_step: 2.5e8\n@conv_valu_flops_per_step: 1.6e10\n@conv_source_sha256: 0\n")
     assert bench.measured_valu("w", str(p)) is None
     assert bench.measured_valu("no_such_workload") is None
+
+
+def test_nd_alg_bytes_by_boundary():
+    B, G, C, N = 2, 64, 128, 2
+    V = G ** 3
+    assert bench.nd_conv_alg_bytes(B, G, G, G, C, N) == N * (3 * B * C * V * 4 + 8 * C * 128 * 128 * 65)
+    assert bench.nd_conv_alg_bytes(B, G, G, G, C, N, True) == N * (3 * B * C * V * 4 + 8 * C * 64 * 64 * 33)

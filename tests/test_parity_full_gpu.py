@@ -49,3 +49,18 @@ def test_full_size_nd_sampled():
     err = rel_err(ys, g["y"])
     say(f"  rel err at {len(p)} sampled points: {err:.3e}")
     assert err <= 1e-4, err
+
+
+@pytest.mark.parametrize("name", ["nd3d_circ_f32_B2_C128_64cube", "nd3d_circ_f32_B1_C64_128cube"])
+def test_full_size_nd_circular_sampled(name):
+    g = _golden(name)
+    inp = make_config(name)
+    assert inp.circular
+    say(f"full-size {name}")
+    y = gpu_nd(inp)
+    assert np.all(np.isfinite(y))
+    p = g["points"]
+    ys = y[:, p[:, 0], p[:, 1], p[:, 2], :]
+    err = rel_err(ys, g["y"])
+    say(f"  rel err at {len(p)} sampled points: {err:.3e}")
+    assert err <= 1e-4, err

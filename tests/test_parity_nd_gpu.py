@@ -59,3 +59,43 @@ def test_nd_delta_kernel_closed_form():
     g2 = scipy.special.expit(inp.gate_a[1] * m + inp.gate_b[1])[:, None, None, None, :]
     want = (x2 * g2 * x1 * g1 * v) @ inp.w_out.astype(np.float64)
     assert rel_err(y, want) < 1e-4
+
+
+# ------------------------------------------------------------- circular boundary
+
+def test_nd_circular_filter_matches_oracle():
+    inp = make_nd(43, 1, 8, 8, 8, 64, N=2, W=64, circular=True)
+    say("nd circular filter 8^3 C=64 N=2")
+    _, k = gpu_nd(inp, with_k=True)
+    _, kref = oracle_nd(inp)
+    assert k.shape == kref.shape == (2, 64, 8, 8, 8)
+    assert rel_err(k, kref) < 1e-5
+
+
+@pytest.mark.parametrize("B,X,Y,C,N,spread", [
+    (2, 8, 8, 64, 2, 0.5),     # smallest circular grid (8-point transforms)
+    (1, 8, 8, 64, 2, 0.5),     # odd batch
+    (3, 8, 8, 64, 1, 0.0),
+    (2, 16, 8, 64, 2, 0.5),    # X != Y
+    (2, 8, 16, 128, 3, 0.5),
+    (2, 16, 16, 64, 2, 0.5),
+    (2, 32, 32, 64, 1, 0.5),
+    (1, 64, 64, 64, 1, 0.5),   # 64-point planes and pencils
+])
+def test_nd_circular_sweep(B, X, Y, C, N, spread):
+    _check(make_nd(300 + B + X + Y + C + N, B, X, Y, Y, C, N=N, W=64, u_mean_spread=spread, circular=True))
+
+
+def test_nd_circular_translation_equivariance():
+    # periodic grid: rolling the input rolls the output, at every point
+    import torch
+    inp = make_nd(44, 2, 32, 32, 32, 64, N=2, W=64, u_mean_spread=0.5, circular=True)
+    say("nd circular roll 32^3 C=64")
+    y = gpu_nd(inp)
+    s = (5, 31, 17)
+    inp.u = np.ascontiguousarray(np.roll(inp.u, s, axis=(1, 2, 3)))
+    y2 = gpu_nd(inp)
+    torch.cuda.synchronize()
+    err = rel_err(y2, np.roll(y, s, axis=(1, 2, 3)))
+    say(f"  roll mismatch {err:.3e}")
+    assert err <= 1e-5
