@@ -22,6 +22,10 @@ in the grid.  conv3d_fft stores the kernel wrapped (index d mod 2G) in a
 (2X, 2Y, 2Z) array, which makes the circular convolution of the zero-padded
 input exact on the kept grid.
 
+2D grids (image planes) are the same operator with X = 1: every offset has
+dx = 0 (coordinate 0), so only the kernel's dx = 0 slice acts (the zero-padded
+array still holds the unused dx = -1 slice).
+
 Geometry, circular boundary (periodic grids; "Handling Boundaries" names both
 kinds): the kernel covers one period, signed offsets d in [-G/2, G/2) per axis
 at coordinates c = d / (G/2), so that in both modes the coordinates span
@@ -58,7 +62,8 @@ def nd_offsets(X: int, Y: int, Z: int, circular: bool = False) -> np.ndarray:
     axes = []
     for G in (X, Y, Z):
         h = G // 2 if circular else G
-        axes.append(np.arange(-h, h, dtype=np.float64) / h)
+        # a one-point periodic axis has the single offset 0 (coordinate 0)
+        axes.append(np.arange(-h, h, dtype=np.float64) / h if h else np.zeros(1))
     g = np.stack(np.meshgrid(*axes, indexing="ij"), axis=-1)
     return g
 

@@ -522,3 +522,56 @@ def test_nd_circular_fft_equals_direct_and_sampled_equals_full():
     Kp = oracle.nd_filter(inp.filter_params, X, Y, Z, 2, 4)
     yp = oracle.hyena_nd_fwd(*args[:-1], Kp)
     assert rel(yp, yd) > 1e-3
+
+
+# ---------------------------------------------------------------- ND, 2D grids
+# A 2D grid (image plane) is the 3D operator with X = 1 (HyenaND explainer,
+# "Native ND Convolution": grids of any dimension).
+
+def test_conv2d_zero_padded_matches_scipy():
+    import scipy.signal
+    Y, Z = 8, 4
+    K = RNG.standard_normal((2, 2 * Y, 2 * Z))      # x offsets -1, 0
+    z = RNG.standard_normal((1, Y, Z))
+    # out[p] = sum_q K0[p - q] z[q] with K0 the dx = 0 slice, offset d at index d + G
+    full = scipy.signal.convolve2d(K[1], z[0], mode="full")
+    want = full[Y:2 * Y, Z:2 * Z]
+    assert rel(oracle.conv3d_direct(K, z)[0], want) < 1e-12
+    assert rel(oracle.conv3d_fft(K, z)[0], want) < 1e-12
+
+
+def test_conv2d_circular_matches_library_fft():
+    Y, Z = 8, 4
+    K = RNG.standard_normal((1, Y, Z))
+    z = RNG.standard_normal((1, Y, Z))
+    Kw = np.roll(K[0], shift=(-(Y // 2), -(Z // 2)), axis=(0, 1))
+    want = np.fft.ifft2(np.fft.fft2(Kw) * np.fft.fft2(z[0])).real
+    assert rel(oracle.conv3d_circular_direct(K, z)[0], want) < 1e-12
+    assert rel(oracle.conv3d_circular_fft(K, z)[0], want) < 1e-12
+
+
+def test_nd_filter_2d_uses_x_coordinate_zero():
+    # with X = 1 the kernel's x coordinate is 0 (dx = 0 slice): the first MLP row
+    # (the x weights) cannot change it, in either boundary
+    Y = Z = 8
+    inp = make_nd(8, 1, 1, Y, Z, 4, N=2, W=8)
+    p = dict(inp.filter_params)
+    p2 = dict(p)
+    p2["w1"] = p["w1"].copy()
+    p2["w1"][0] += 3.0
+    for circ, sl in ((False, 1), (True, 0)):
+        Ka = oracle.nd_filter(p, 1, Y, Z, 2, 4, circular=circ)
+        Kb = oracle.nd_filter(p2, 1, Y, Z, 2, 4, circular=circ)
+        assert np.array_equal(Ka[:, :, sl], Kb[:, :, sl])
+        c = oracle.nd_offsets(1, Y, Z, circular=circ)
+        assert np.all(c[sl, ..., 0] == 0.0)
+
+
+def test_nd_2d_fft_equals_direct():
+    inp = make_nd(9, 2, 1, 8, 8, 4, N=2, W=8, u_mean_spread=0.5)
+    for circ in (False, True):
+        K = oracle.nd_filter(inp.filter_params, 1, 8, 8, 2, 4, circular=circ)
+        args = (inp.u, inp.w_in, inp.dskip, inp.gate_a, inp.gate_b, inp.w_out, K)
+        yd = oracle.hyena_nd_fwd(*args, conv="direct", circular=circ)
+        yf = oracle.hyena_nd_fwd(*args, conv="fft", circular=circ)
+        assert rel(yf, yd) < 1e-11
