@@ -161,7 +161,11 @@ typedef struct {
 /* Supported: Y = Z; X, Y, Z powers of two in [4, 64] (zero padded) or in [8, 128]
  * (circular); C a multiple of 64 in [64, 4096]; 1 <= N <= 4; B >= 1. The size
  * queries return 0 for unsupported shapes or boundaries. The calls without _ex
- * are the zero-padded boundary. */
+ * are the zero-padded boundary.
+ * X = 1 is a 2D grid (Y x Z; "Native ND Convolution" covers any dimension):
+ * every offset has dx = 0 (coordinate 0, so the x row of w1 does not act), the
+ * x axis is never padded, and u, y [B][1][Y][Z][C] are the same memory as
+ * [B][Y][Z][C]. All orders of a 2D grid run in one launch. */
 size_t hyena_nd_cache_bytes(int X, int Y, int Z, int C, int N);
 size_t hyena_nd_filter_workspace_bytes(int X, int Y, int Z, int C, int N);
 size_t hyena_nd_workspace_bytes(int B, int X, int Y, int Z, int C, int N);

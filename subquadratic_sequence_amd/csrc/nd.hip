@@ -43,7 +43,7 @@ __global__ __launch_bounds__(256) void nd_mlp_kernel(NdFilterArgs a) {
   for (int t = tid; t < kNP; t += 256) {
     const int pt = p0 + t;
     const int k = pt % MZ, j = (pt / MZ) % MY, i = pt / (MZ * MY);
-    const float cx = (float)(i - MX / 2) / (float)(MX / 2);
+    const float cx = MX > 1 ? (float)(i - MX / 2) / (float)(MX / 2) : 0.f;  // 2D grids: dx = 0
     const float cy = (float)(j - MY / 2) / (float)(MY / 2);
     const float cz = (float)(k - MZ / 2) / (float)(MZ / 2);
     cs[t][0] = cx;
@@ -106,7 +106,7 @@ __global__ __launch_bounds__(256) void nd_mlp_mfma_kernel(NdFilterArgs a) {
   for (int t = tid; t < kNP; t += 256) {
     const int pt = p0 + t;
     const int k = pt % MZ, j = (pt / MZ) % MY, i = pt / (MZ * MY);
-    const float cx = (float)(i - MX / 2) / (float)(MX / 2);
+    const float cx = MX > 1 ? (float)(i - MX / 2) / (float)(MX / 2) : 0.f;  // 2D grids: dx = 0
     const float cy = (float)(j - MY / 2) / (float)(MY / 2);
     const float cz = (float)(k - MZ / 2) / (float)(MZ / 2);
     cs[t][0] = cx;
@@ -833,6 +833,138 @@ __global__ __launch_bounds__(256) void nd_gate256_kernel(const float* __restrict
   }
 }
 
+// ================================================= 2D grids (X = 1)
+// A 2D grid (Y x Z, a single x-plane) has dx = 0 for every offset: the
+// transform over x is the identity, and each (sample pair, channel) plane runs
+// all orders in LDS: forward 2D DFT of the (zero padded) block, product with
+// the channel's half spectrum, inverse 2D DFT, crop, gate and skip, and the
+// next order from the same plane. HBM sees v, x^n, the spectra and z^{N+1}
+// only. Items (channel, sample pair), pair index fastest, are dealt so that the
+// workgroups of one XCD (blockIdx mod 8) take consecutive items: the pairs of
+// a channel read its spectrum through that XCD's L2.
+template <int M> struct Plane2dCfg {
+  static constexpr int E = PlaneCfg<M>::E;
+  static constexpr int LINE_THREADS = M * (M / E);  // every thread owns part of a line
+  static constexpr int THREADS = LINE_THREADS < 64 ? 64 : LINE_THREADS;
+  static constexpr int PER = M * M / THREADS;        // plane elements per thread
+};
+
+template <int M, bool CIRC>
+__global__ __launch_bounds__(Plane2dCfg<M>::THREADS) void nd_plane2d_kernel(NdConvArgs a, int per_xcd) {
+  using C = PlaneCfg<M>;
+  constexpr int NT = Plane2dCfg<M>::THREADS;
+  constexpr int PER = Plane2dCfg<M>::PER;
+  constexpr int KEPT = CIRC ? PER : (PER + 3) / 4;  // kept positions per thread (a quarter when padded)
+  constexpr int ZH = M / 2 + 1;
+  // Smaller planes fetch the spectrum entries before the forward transform and
+  // the gate inputs before the inverse; 128-point planes (1024 threads, 128
+  // registers each) fetch them where they are used.
+  constexpr bool EARLY = M < 128;
+  static_assert(PER * NT == M * M, "plane split");
+  extern __shared__ float4 smem4[];
+  float2* P = reinterpret_cast<float2*>(smem4);
+  float2* tw = P + M * C::RS;
+  const int tid = threadIdx.x;
+  const int BP = (a.B + 1) / 2, CC = a.C;
+  const int item = (int)(blockIdx.x % 8) * per_xcd + (int)(blockIdx.x / 8);
+  if (item >= BP * CC) return;  // the whole workgroup, before any barrier
+  for (int i = tid; i < 128; i += NT) tw[i] = a.tw128[i];
+  const int c = item / BP, bp = item % BP;
+  const int b0 = 2 * bp;
+  const bool has_b1 = b0 + 1 < a.B;
+  const int b1 = has_b1 ? b0 + 1 : b0;
+  const int Y = a.Y, Z = a.Z, V = Y * Z;
+  const size_t J = (size_t)(a.NO + 1) * CC;
+  const float* s0 = a.p + (size_t)b0 * J * V;
+  const float* s1 = a.p + (size_t)b1 * J * V;
+  // z^n of both samples at the kept positions q = tid + k NT (q < V), in registers
+  float z0[KEPT], z1[KEPT];
+#pragma unroll
+  for (int k = 0; k < KEPT; ++k) {
+    const int q = tid + k * NT;
+    z0[k] = q < V ? s0[(size_t)c * V + q] : 0.f;
+    z1[k] = (q < V && has_b1) ? s1[(size_t)c * V + q] : 0.f;
+  }
+  for (int n = 0; n < a.NO; ++n) {
+    // spectrum entries of this thread's bins i = tid + e NT; bins with kz > M/2
+    // come from the conjugate of bin -k
+    const float2* Kc = a.kh + (size_t)(n * CC + c) * M * ZH;
+    float2 kk[PER];
+    auto load_k = [&]() {
+#pragma unroll
+      for (int e = 0; e < PER; ++e) {
+        const int i = tid + e * NT;
+        const int ky = i / M, kz = i % M;
+        const bool lower = kz <= M / 2;
+        const int ky2 = lower ? ky : (M - ky) % M;
+        const int kz2 = lower ? kz : M - kz;
+        const float2 kv = Kc[ky2 * ZH + kz2];
+        kk[e] = lower ? kv : conjf2(kv);
+      }
+    };
+    if (EARLY) load_k();
+    if (!CIRC) {
+      for (int i = tid; i < M * M; i += NT) P[(i / M) * C::RS + i % M] = make_float2(0.f, 0.f);
+      __syncthreads();
+    }
+#pragma unroll
+    for (int k = 0; k < KEPT; ++k) {
+      const int q = tid + k * NT;
+      if (q < V) P[(q / Z) * C::RS + q % Z] = make_float2(z0[k], z1[k]);
+    }
+    __syncthreads();
+    plane_rows<M, false>(P, Y, tw);
+    plane_cols<M, false>(P, tw);
+    if (!EARLY) load_k();
+#pragma unroll
+    for (int e = 0; e < PER; ++e) {
+      const int i = tid + e * NT;
+      float2* pe = P + (i / M) * C::RS + i % M;
+      *pe = cmul(*pe, kk[e]);
+    }
+    // gate inputs, used after the inverse transform
+    const float* x0 = s0 + (size_t)((n + 1) * CC + c) * V;
+    const float* x1 = s1 + (size_t)((n + 1) * CC + c) * V;
+    float xa[KEPT], xb[KEPT];
+    auto load_x = [&]() {
+#pragma unroll
+      for (int k = 0; k < KEPT; ++k) {
+        const int q = tid + k * NT;
+        xa[k] = q < V ? x0[q] : 0.f;
+        xb[k] = q < V ? x1[q] : 0.f;
+      }
+    };
+    if (EARLY) load_x();
+    __syncthreads();
+    plane_cols<M, true>(P, tw);
+    plane_rows<M, true>(P, Y, tw);
+    if (!EARLY) load_x();
+    const float g0 = a.gate[((size_t)b0 * a.NO + n) * CC + c];
+    const float g1 = has_b1 ? a.gate[((size_t)b1 * a.NO + n) * CC + c] : 0.f;
+    const float dk = a.dskip[n * CC + c];
+#pragma unroll
+    for (int k = 0; k < KEPT; ++k) {
+      const int q = tid + k * NT;
+      if (q < V) {
+        const float2 cv = P[(q / Z) * C::RS + q % Z];
+        z0[k] = xa[k] * g0 * cv.x + dk * z0[k];
+        z1[k] = xb[k] * g1 * cv.y + dk * z1[k];
+      }
+    }
+    __syncthreads();  // the plane is refilled by the next order
+  }
+  float* o0 = a.zfinal + ((size_t)b0 * CC + c) * V;
+  float* o1 = a.zfinal + ((size_t)b1 * CC + c) * V;
+#pragma unroll
+  for (int k = 0; k < KEPT; ++k) {
+    const int q = tid + k * NT;
+    if (q < V) {
+      o0[q] = z0[k];
+      if (has_b1) o1[q] = z1[k];
+    }
+  }
+}
+
 // ============================================================ launchers
 
 static hipError_t nd_allow_lds(const void* fn, size_t bytes) {
@@ -918,7 +1050,9 @@ hipError_t nd_filter(const NdFilterArgs& f, float2* F, float2* kh, const float2*
   a.npairs = npairs;
   a.tw128 = tw128;
   if ((e = launch_plane<PL_FWD_FULL>(a, dim3(MX, npairs, 1), s)) != hipSuccess) return e;
-  if ((e = launch_pencil<PN_FWD_FULL>(a, dim3((unsigned)(MY * MZ / 64), npairs, 1), s)) != hipSuccess) return e;
+  // 2D grids (MX = 1): the transform over x is the identity
+  if (MX > 1 && (e = launch_pencil<PN_FWD_FULL>(a, dim3((unsigned)(MY * MZ / 64), npairs, 1), s)) != hipSuccess)
+    return e;
   const size_t th = (size_t)MX * MY * (MZ / 2 + 1) * npairs;
   hipLaunchKernelGGL(nd_split_kernel, dim3((unsigned)((th + 255) / 256)), dim3(256), 0, s, (const float2*)F, kh,
                      MX, MY, MZ, npairs);
@@ -982,8 +1116,37 @@ static hipError_t launch_pencil128(const NdConvArgs& a, int nitems, hipStream_t 
   return hipGetLastError();
 }
 
+template <int M, bool CIRC>
+static hipError_t launch_plane2d_t(const NdConvArgs& a, hipStream_t s) {
+  using C = PlaneCfg<M>;
+  auto fn = nd_plane2d_kernel<M, CIRC>;
+  hipError_t e = nd_allow_lds((const void*)fn, C::LDS);
+  if (e != hipSuccess) return e;
+  const int items = (a.B + 1) / 2 * a.C;
+  const int per_xcd = (items + 7) / 8;
+  hipLaunchKernelGGL(fn, dim3(8 * per_xcd), dim3(Plane2dCfg<M>::THREADS), C::LDS, s, a, per_xcd);
+  return hipGetLastError();
+}
+
+template <bool CIRC>
+static hipError_t launch_plane2d(const NdConvArgs& a, hipStream_t s) {
+  switch (a.MY) {
+    case 8: return launch_plane2d_t<8, CIRC>(a, s);
+    case 16: return launch_plane2d_t<16, CIRC>(a, s);
+    case 32: return launch_plane2d_t<32, CIRC>(a, s);
+    case 64: return launch_plane2d_t<64, CIRC>(a, s);
+    case 128: return launch_plane2d_t<128, CIRC>(a, s);
+    default: return hipErrorInvalidValue;
+  }
+}
+
 hipError_t nd_conv(const NdConvArgs& in, hipStream_t s) {
   NdConvArgs a = in;
+  if (a.X == 1) {
+    // 2D grid: all orders in one launch; the result goes to zfinal
+    a.zfinal = in.zfinal;
+    return a.MY == a.Y ? launch_plane2d<true>(a, s) : launch_plane2d<false>(a, s);
+  }
   const int BP = (a.B + 1) / 2;
   const unsigned nf = (unsigned)(a.MY * a.MZ / 64);
   // persistent kernels: the zero-padded 64^3 case (128-point axes, half of each kept)

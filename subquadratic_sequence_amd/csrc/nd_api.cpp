@@ -20,18 +20,22 @@ bool boundary_ok(int bd) { return bd == HYENA_ND_ZERO_PAD || bd == HYENA_ND_CIRC
 // transform length per grid length: 2 (zero padded) or 1 (circular)
 int pad_of(int bd) { return bd == HYENA_ND_CIRCULAR ? 1 : 2; }
 
-// Transform lengths up to 128 (the twiddle table W_128); at least 8 points per axis.
+// Transform lengths up to 128 (the twiddle table W_128); at least 8 points per
+// axis, except X = 1: a 2D grid (one x-plane, every offset with dx = 0).
 bool nd_shape_ok(int X, int Y, int Z, int C, int N, int bd) {
   if (!boundary_ok(bd)) return false;
   const int lo = 8 / pad_of(bd), hi = 128 / pad_of(bd);
-  return pow2_in(X, lo, hi) && pow2_in(Y, lo, hi) && Z == Y && C >= 64 && C <= 4096 && C % 64 == 0 && N >= 1 &&
-         N <= 4;
+  return (X == 1 || pow2_in(X, lo, hi)) && pow2_in(Y, lo, hi) && Z == Y && C >= 64 && C <= 4096 && C % 64 == 0 &&
+         N >= 1 && N <= 4;
 }
+
+// transform length along x: no padding of a one-point axis
+int mx_of(int X, int bd) { return X == 1 ? 1 : pad_of(bd) * X; }
 
 // transform points (MX)(MY)(MZ)
 size_t pts(int X, int Y, int Z, int bd) {
   const size_t p = pad_of(bd);
-  return p * p * p * X * Y * Z;
+  return (size_t)mx_of(X, bd) * p * p * Y * Z;
 }
 
 struct NdCache {
@@ -44,7 +48,7 @@ NdCache nd_cache(int X, int Y, int Z, int C, int N, int bd) {
   c.tw = off;
   off = align_up(off + 128 * 8, kAlign);
   c.kh = off;
-  off = align_up(off + (size_t)N * C * (p * X) * (p * Y) * (p * Z / 2 + 1) * 8, kAlign);
+  off = align_up(off + (size_t)N * C * mx_of(X, bd) * (p * Y) * (p * Z / 2 + 1) * 8, kAlign);
   c.total = off;
   return c;
 }
@@ -177,7 +181,7 @@ int hyena_nd_filter_gen(hyena_nd_layer* layer, const hyena_nd_filter_params* p, 
   float2* tw = reinterpret_cast<float2*>(cb + cl.tw);
   HY_CHECK_HIP(hy::twiddles(tw, 128, 128, stream));
   const int pd = pad_of(bd);
-  hy::NdFilterArgs f{X,     Y,     Z,     C,     N,     p->width, pd * X,   pd * Y,
+  hy::NdFilterArgs f{X,     Y,     Z,     C,     N,     p->width, mx_of(X, bd), pd * Y,
                      pd * Z, p->w1, p->b1, p->w2, p->b2, p->w3,    p->b3,    p->decay,
                      k_out ? k_out : reinterpret_cast<float*>(wsb + fw.k)};
   HY_CHECK_HIP(hy::nd_filter(f, reinterpret_cast<float2*>(wsb + fw.F), reinterpret_cast<float2*>(cb + cl.kh), tw,
@@ -228,7 +232,7 @@ int nd_fwd_impl(const hyena_nd_layer* layer, const float* u, const float* w_in, 
   a.X = X;
   a.Y = Y;
   a.Z = Z;
-  a.MX = pad_of(bd) * X;
+  a.MX = mx_of(X, bd);
   a.MY = pad_of(bd) * Y;
   a.MZ = pad_of(bd) * Z;
   a.C = C;

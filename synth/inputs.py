@@ -201,6 +201,8 @@ TEST_SHAPES = {
     "nd3d_circ_f32_B2_C128_64cube": dict(kind="nd", seed=5, B=2, X=64, Y=64, Z=64, C=128, N=2, circular=True),
     "nd3d_circ_f32_B1_C64_128cube": dict(kind="nd", seed=33, B=1, X=128, Y=128, Z=128, C=64, N=2,
                                          circular=True),
+    # 2D image grids (X = 1): 64 x 64 patch grids at a ViT-Small width, zero padded
+    "nd2d_f32_B8_C384_64sq": dict(kind="nd", seed=34, B=8, X=1, Y=64, Z=64, C=384, N=2),
 }
 
 

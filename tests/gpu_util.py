@@ -62,9 +62,10 @@ def gpu_nd(inp, with_k: bool = False):
     bd = hs.ND_CIRCULAR if inp.circular else hs.ND_ZERO_PAD
     layer = hs.HyenaNDLayer(inp.X, inp.Y, inp.Z, inp.C, inp.N, boundary=bd)
     pf = 1 if inp.circular else 2
+    mx = 1 if inp.X == 1 else pf * inp.X  # 2D grids: no padding of the one-point x axis
     k_out = None
     if with_k:
-        k_out = torch.empty(inp.N, inp.C, pf * inp.X, pf * inp.Y, pf * inp.Z, device="cuda")
+        k_out = torch.empty(inp.N, inp.C, mx, pf * inp.Y, pf * inp.Z, device="cuda")
     hs.hyena_nd_filter_gen(layer, to_dev(inp.w1), to_dev(inp.b1), to_dev(inp.w2), to_dev(inp.b2), to_dev(inp.w3),
                            to_dev(inp.b3), to_dev(inp.decay), k_out=k_out)
     y = hs.hyena_nd_fwd(layer, to_dev(inp.u), to_dev(inp.w_in), to_dev(inp.dskip), to_dev(inp.gate_a),

@@ -178,6 +178,11 @@ def test_nd_size_queries_by_boundary(hy):
     assert hy.hyena_nd_cache_bytes_ex(8, 8, 16, 64, 1, hy.ND_CIRCULAR) == 0
     assert hy.hyena_nd_cache_bytes_ex(8, 8, 8, 64, 1, 2) == 0
     assert hy.hyena_nd_workspace_bytes_ex(1, 8, 8, 8, 64, 1, -1) == 0
+    # 2D grids: X = 1 in both boundaries, no padding along x
+    assert hy.hyena_nd_cache_bytes(1, 64, 64, 64, 2) == al(128 * 8) + al(2 * 64 * 1 * 128 * 65 * 8)
+    assert hy.hyena_nd_cache_bytes_ex(1, 128, 128, 64, 2, hy.ND_CIRCULAR) == al(128 * 8) + al(2 * 64 * 128 * 65 * 8)
+    assert hy.hyena_nd_cache_bytes(2, 8, 8, 64, 2) == 0            # X = 2 is not a 2D grid
+    assert hy.hyena_nd_filter_workspace_bytes(1, 4, 4, 64, 1) > 0
 
 
 def test_nd_layer_init_ex(hy):

@@ -58,3 +58,11 @@ def test_nd_alg_bytes_by_boundary():
     V = G ** 3
     assert bench.nd_conv_alg_bytes(B, G, G, G, C, N) == N * (3 * B * C * V * 4 + 8 * C * 128 * 128 * 65)
     assert bench.nd_conv_alg_bytes(B, G, G, G, C, N, True) == N * (3 * B * C * V * 4 + 8 * C * 64 * 64 * 33)
+
+
+def test_nd_alg_bytes_2d_fused():
+    # 2D grid: v and x^1, x^2 read once, z^3 written once, two half spectra 128 x 65
+    B, Y, C, N = 8, 64, 384, 2
+    V = Y * Y
+    want = 4 * B * C * V * 4 + N * 8 * C * 128 * 65
+    assert bench.nd_conv_alg_bytes(B, 1, Y, Y, C, N) == want

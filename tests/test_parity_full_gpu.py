@@ -51,11 +51,12 @@ def test_full_size_nd_sampled():
     assert err <= 1e-4, err
 
 
-@pytest.mark.parametrize("name", ["nd3d_circ_f32_B2_C128_64cube", "nd3d_circ_f32_B1_C64_128cube"])
-def test_full_size_nd_circular_sampled(name):
+@pytest.mark.parametrize("name", ["nd3d_circ_f32_B2_C128_64cube", "nd3d_circ_f32_B1_C64_128cube",
+                                  "nd2d_f32_B8_C384_64sq"])
+def test_full_size_nd_other_sampled(name):
+    """Periodic 3D grids and the 2D image-grid workload."""
     g = _golden(name)
     inp = make_config(name)
-    assert inp.circular
     say(f"full-size {name}")
     y = gpu_nd(inp)
     assert np.all(np.isfinite(y))
