@@ -8,8 +8,12 @@ from .hyena_oracle import (  # noqa: F401
     fft_radix2,
     causal_conv_direct,
     causal_conv_fft,
+    noncausal_conv_direct,
+    noncausal_conv_fft,
     posenc,
+    posenc_at,
     implicit_filter,
+    implicit_filter_noncausal,
     short_conv,
     hyena_fwd,
     hyena_fwd_sampled,

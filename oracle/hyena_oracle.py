@@ -23,6 +23,13 @@ size 2L (zero padding to twice the length makes the circular convolution equal
 the linear one: HyenaND explainer, Methodology, "Handling Boundaries"; FFT
 convolution: TWIML #690, 6:27).
 
+Non-causal (bidirectional) variant: the pages only name causal use and
+bidirectional comparators, so its form here is a reading: the same generator
+evaluated at signed lags tau in [-(L-1), L-1] (PosEnc at tau / L, window
+exp(-a_c |tau| / L)), and c_t = sum_tau h(tau) z_{t - tau} with z zero outside
+[0, L); the 2L-point FFT with the filter wrapped (lag tau at tau mod 2L) gives it
+exactly. The short convolution keeps its causal taps.
+
 Readings of points the pages leave open (positional-encoding frequencies, FFN
 initialisation, window decays, short-conv taps, skip placement, block order) are
 conventions of this implementation; the tests pin the code to those
@@ -106,16 +113,65 @@ def causal_conv_fft(h, z) -> np.ndarray:
     return c[..., :L].real
 
 
+def noncausal_conv_direct(h2, z) -> np.ndarray:
+    """c[..., t] = sum_{tau=-(L-1)..L-1} h2[..., tau + L - 1] * z[..., t - tau], z = 0 outside [0, L)
+    (definition, O(L^2)).  h2 [..., 2L - 1] is lag-indexed: entry i holds lag i - (L - 1)."""
+    h2 = np.asarray(h2, dtype=np.float64)
+    z = np.asarray(z, dtype=np.float64)
+    L = z.shape[-1]
+    out = np.zeros(np.broadcast_shapes(h2.shape[:-1] + (L,), z.shape), dtype=np.float64)
+    for tau in range(-(L - 1), L):
+        hv = h2[..., tau + L - 1:tau + L]
+        if tau >= 0:
+            out[..., tau:] += hv * z[..., :L - tau]
+        else:
+            out[..., :L + tau] += hv * z[..., -tau:]
+    return out
+
+
+def noncausal_conv_fft(h2, z) -> np.ndarray:
+    """Same result as noncausal_conv_direct via a 2L-point FFT: the filter wrapped
+    (lag tau at index tau mod 2L, index L zero), the input zero padded to 2L, the
+    first L samples kept."""
+    h2 = np.asarray(h2, dtype=np.float64)
+    z = np.asarray(z, dtype=np.float64)
+    L = z.shape[-1]
+    hw = np.zeros(h2.shape[:-1] + (2 * L,))
+    hw[..., :L] = h2[..., L - 1:]                  # lags 0 .. L-1
+    hw[..., L + 1:] = h2[..., :L - 1]              # lags -(L-1) .. -1 at 2L + tau
+    zp = np.concatenate([z, np.zeros(z.shape[:-1] + (L,))], axis=-1)
+    c = fft_radix2(fft_radix2(hw) * fft_radix2(zp), inverse=True)
+    return c[..., :L].real
+
+
 # ---------------------------------------------------------------------------
 # Implicit filter
 # ---------------------------------------------------------------------------
 
-def posenc(L: int, K: int) -> np.ndarray:
-    """Features of position t: [tau, cos(2 pi k tau) for k=1..K, sin(2 pi k tau) for k=1..K],
-    with tau = t / L.  Returns [L, 1 + 2K]."""
-    tau = np.arange(L, dtype=np.float64) / L
+def posenc_at(tau, K: int) -> np.ndarray:
+    """Features [tau, cos(2 pi k tau) for k=1..K, sin(2 pi k tau) for k=1..K] at the
+    given normalised positions tau.  Returns [len(tau), 1 + 2K]."""
+    tau = np.asarray(tau, dtype=np.float64)
     ang = 2.0 * np.pi * np.outer(tau, np.arange(1, K + 1, dtype=np.float64))
     return np.concatenate([tau[:, None], np.cos(ang), np.sin(ang)], axis=1)
+
+
+def posenc(L: int, K: int) -> np.ndarray:
+    """Features of position t at tau = t / L, t in [0, L).  Returns [L, 1 + 2K]."""
+    return posenc_at(np.arange(L, dtype=np.float64) / L, K)
+
+
+def _filter_at(params: dict, tau, N: int, D: int) -> np.ndarray:
+    """exp(-a_c |tau|) * o(tau)[n*D + c] at positions tau (in units of L): [N, D, len(tau)]."""
+    f = lambda k: np.asarray(params[k], dtype=np.float64)  # noqa: E731
+    tau = np.asarray(tau, dtype=np.float64)
+    e = posenc_at(tau, int(params["K"]))
+    a1 = np.sin(e @ f("w1") + f("b1"))
+    a2 = np.sin(a1 @ f("w2") + f("b2"))
+    o = a2 @ f("w3") + f("b3")                               # [P, N*D]
+    window = np.exp(-np.outer(np.abs(tau), f("decay")))      # [P, D]
+    h = o.reshape(len(tau), N, D) * window[:, None, :]
+    return np.ascontiguousarray(h.transpose(1, 2, 0))
 
 
 def implicit_filter(params: dict, L: int, N: int, D: int) -> np.ndarray:
@@ -124,15 +180,16 @@ def implicit_filter(params: dict, L: int, N: int, D: int) -> np.ndarray:
 
     Returns [N, D, L] float64.
     """
-    f = lambda k: np.asarray(params[k], dtype=np.float64)  # noqa: E731
-    e = posenc(L, int(params["K"]))
-    a1 = np.sin(e @ f("w1") + f("b1"))
-    a2 = np.sin(a1 @ f("w2") + f("b2"))
-    o = a2 @ f("w3") + f("b3")                               # [L, N*D]
-    tau = np.arange(L, dtype=np.float64) / L
-    window = np.exp(-np.outer(tau, f("decay")))              # [L, D]
-    h = o.reshape(L, N, D) * window[:, None, :]
-    return np.ascontiguousarray(h.transpose(1, 2, 0))
+    return _filter_at(params, np.arange(L, dtype=np.float64) / L, N, D)
+
+
+def implicit_filter_noncausal(params: dict, L: int, N: int, D: int) -> np.ndarray:
+    """The same generator at the signed lags tau in [-(L-1), L-1]:
+    h[n, c, i] = exp(-a_c |tau| / L) * o(tau / L)[n*D + c] with tau = i - (L - 1).
+
+    Returns [N, D, 2L - 1] float64 (lag-indexed).
+    """
+    return _filter_at(params, np.arange(-(L - 1), L, dtype=np.float64) / L, N, D)
 
 
 # ---------------------------------------------------------------------------
@@ -159,18 +216,22 @@ def _project_and_gate_inputs(u, w_in, short_w, D, N):
     return v, xs
 
 
-def hyena_fwd(u, w_in, short_w, dskip, w_out, h, conv: str = "auto") -> np.ndarray:
+def hyena_fwd(u, w_in, short_w, dskip, w_out, h, conv: str = "auto", causal: bool = True) -> np.ndarray:
     """y[B, L, D] of the order-N operator.
 
     u [B, L, D]; w_in [D, (N+1)D]; short_w [(N+1)D, 3]; dskip [N, D];
-    w_out [D, D]; h [N, D, L] (implicit_filter).  conv: "direct", "fft" or
+    w_out [D, D]; h [N, D, L] (implicit_filter) or, with causal=False,
+    [N, D, 2L - 1] (implicit_filter_noncausal).  conv: "direct", "fft" or
     "auto" (direct up to L = 4096, FFT above).
     """
     B, L, D = np.shape(u)
     N = np.shape(dskip)[0]
     if conv == "auto":
         conv = "direct" if L <= 4096 else "fft"
-    convf = causal_conv_direct if conv == "direct" else causal_conv_fft
+    if causal:
+        convf = causal_conv_direct if conv == "direct" else causal_conv_fft
+    else:
+        convf = noncausal_conv_direct if conv == "direct" else noncausal_conv_fft
     dskip = np.asarray(dskip, dtype=np.float64)
     h = np.asarray(h, dtype=np.float64)
     z, xs = _project_and_gate_inputs(u, w_in, short_w, D, N)
@@ -180,12 +241,14 @@ def hyena_fwd(u, w_in, short_w, dskip, w_out, h, conv: str = "auto") -> np.ndarr
     return z.transpose(0, 2, 1) @ np.asarray(w_out, dtype=np.float64)
 
 
-def hyena_fwd_sampled(u, w_in, short_w, dskip, w_out, h, t_samples, chunk: int = 64) -> np.ndarray:
+def hyena_fwd_sampled(u, w_in, short_w, dskip, w_out, h, t_samples, chunk: int = 64,
+                      causal: bool = True) -> np.ndarray:
     """y[:, t_samples, :] for long sequences.
 
-    Orders 1..N-1 are computed for every t with causal_conv_fft (channel chunks
-    of `chunk` to bound memory); the last order is evaluated only at the sampled
-    times by the direct sum c(t) = sum_{s<=t} h(s) z(t-s).  Returns [B, S, D].
+    Orders 1..N-1 are computed for every t with causal_conv_fft /
+    noncausal_conv_fft (channel chunks of `chunk` to bound memory); the last
+    order is evaluated only at the sampled times by the direct sum
+    c(t) = sum_s h(t - s) z(s).  Returns [B, S, D].
     """
     B, L, D = np.shape(u)
     N = np.shape(dskip)[0]
@@ -196,12 +259,17 @@ def hyena_fwd_sampled(u, w_in, short_w, dskip, w_out, h, t_samples, chunk: int =
     for n in range(N - 1):
         c = np.empty_like(z)
         for c0 in range(0, D, chunk):
-            c[:, c0:c0 + chunk] = causal_conv_fft(h[n][None, c0:c0 + chunk], z[:, c0:c0 + chunk])
+            convf = causal_conv_fft if causal else noncausal_conv_fft
+            c[:, c0:c0 + chunk] = convf(h[n][None, c0:c0 + chunk], z[:, c0:c0 + chunk])
         z = xs[n] * c + dskip[n][None, :, None] * z
     n = N - 1
     out = np.empty((B, len(t_samples), D))
     for i, t in enumerate(t_samples):
-        # c[b, d] = sum_{s=0..t} h[n, d, s] * z[b, d, t - s]
-        c = np.einsum("ds,bds->bd", h[n, :, :t + 1], z[:, :, t::-1])
+        if causal:
+            # c[b, d] = sum_{s=0..t} h[n, d, s] * z[b, d, t - s]
+            c = np.einsum("ds,bds->bd", h[n, :, :t + 1], z[:, :, t::-1])
+        else:
+            # c[b, d] = sum_{s=0..L-1} h(t - s) z[b, d, s], lag t - s at index t - s + L - 1
+            c = np.einsum("ds,bds->bd", h[n, :, t:t + L][:, ::-1], z)
         out[:, i, :] = xs[n][:, :, t] * c + dskip[n][None, :] * z[:, :, t]
     return out @ np.asarray(w_out, dtype=np.float64)

@@ -575,3 +575,79 @@ def test_nd_2d_fft_equals_direct():
         yd = oracle.hyena_nd_fwd(*args, conv="direct", circular=circ)
         yf = oracle.hyena_nd_fwd(*args, conv="fft", circular=circ)
         assert rel(yf, yd) < 1e-11
+
+
+# --------------------------------------------------------- 1D, non-causal
+# Two-sided filters over lags (-L, L), the reading of the bidirectional case
+# (the pages name causal use and bidirectional comparators only).
+
+@pytest.mark.parametrize("L", [1, 2, 3, 8, 64, 257])
+def test_noncausal_conv_direct_matches_numpy_convolve(L):
+    h2 = RNG.standard_normal((3, 2 * L - 1))
+    z = RNG.standard_normal((3, L))
+    want = np.stack([np.convolve(h2[i], z[i])[L - 1:2 * L - 1] for i in range(3)])
+    assert rel(oracle.noncausal_conv_direct(h2, z), want) < 1e-12
+
+
+@pytest.mark.parametrize("L", [1, 2, 16, 128, 1024])
+def test_noncausal_conv_fft_equals_direct(L):
+    h2 = RNG.standard_normal((2, 2 * L - 1))
+    z = RNG.standard_normal((2, L))
+    assert rel(oracle.noncausal_conv_fft(h2, z), oracle.noncausal_conv_direct(h2, z)) < 1e-11
+
+
+def test_noncausal_with_one_sided_filter_is_causal():
+    L = 128
+    h = RNG.standard_normal((2, L))
+    h2 = np.concatenate([np.zeros((2, L - 1)), h], axis=1)     # negative lags zero
+    z = RNG.standard_normal((2, L))
+    assert rel(oracle.noncausal_conv_fft(h2, z), oracle.causal_conv_direct(h, z)) < 1e-11
+
+
+def test_noncausal_conv_time_reversal():
+    # reversing the input and the lags reverses the output
+    L = 50
+    h2 = RNG.standard_normal(2 * L - 1)
+    z = RNG.standard_normal(L)
+    c = oracle.noncausal_conv_direct(h2, z)
+    cr = oracle.noncausal_conv_direct(h2[::-1], z[::-1])
+    assert rel(cr, c[::-1]) < 1e-12
+
+
+def test_noncausal_filter_positive_lags_are_the_causal_filter():
+    inp = _small(L=64, D=8, N=2, K=4)
+    h = oracle.implicit_filter(inp.filter_params, 64, 2, 8)
+    h2 = oracle.implicit_filter_noncausal(inp.filter_params, 64, 2, 8)
+    assert h2.shape == (2, 8, 127)
+    assert np.array_equal(h2[..., 63:], h)
+
+
+def test_noncausal_filter_negative_lags_flip_the_odd_features():
+    # at -tau the features are [-tau, cos, -sin]: negating the weight rows of the
+    # odd features makes the causal generator produce h(-t); the window is |tau|
+    K = 4
+    inp = _small(L=64, D=8, N=2, K=K)
+    p = dict(inp.filter_params)
+    p["w1"] = np.asarray(p["w1"], np.float64).copy()
+    p["w1"][0] *= -1.0
+    p["w1"][1 + K:] *= -1.0
+    h_flip = oracle.implicit_filter(p, 64, 2, 8)                 # h at -t, t = 0..63
+    h2 = oracle.implicit_filter_noncausal(inp.filter_params, 64, 2, 8)
+    assert rel(h2[..., 63::-1], h_flip) < 1e-12
+
+
+def test_noncausal_operator_fft_equals_direct_and_sampled():
+    inp = _small(L=128, D=8, N=2)
+    h2 = oracle.implicit_filter_noncausal(inp.filter_params, inp.L, inp.N, inp.D)
+    args = (inp.u, inp.w_in, inp.short_w, inp.dskip, inp.w_out, h2)
+    yd = oracle.hyena_fwd(*args, conv="direct", causal=False)
+    yf = oracle.hyena_fwd(*args, conv="fft", causal=False)
+    assert rel(yf, yd) < 1e-11
+    ts = np.array([0, 1, 63, 100, 127])
+    ys = oracle.hyena_fwd_sampled(*args, ts, chunk=3, causal=False)
+    assert rel(ys, yd[:, ts]) < 1e-11
+    # the future reaches the past: unlike the causal operator
+    u2 = inp.u.copy()
+    u2[:, 100] += 1.0
+    y2 = oracle.hyena_fwd(u2, *args[1:], conv="direct", causal=False)
+    assert np.max(np.abs(y2[:, :99] - yd[:, :99])) > 1e-6
