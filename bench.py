@@ -130,17 +130,24 @@ def cpu_baseline(inp, budget_tokens: int):
 
     By causality y[:, :T] depends only on u[:, :T] and on the first T filter taps,
     so the oracle runs on that prefix with the full-length filters truncated to T
-    taps, FFT convolution path, one thread."""
+    taps, FFT convolution path, one thread. A non-causal layer has no such prefix
+    property: the oracle then runs the operator on a length-T sequence (the first
+    T inputs, filters generated for length T), the same work per token."""
     import oracle
     from threadpoolctl import threadpool_limits
     T = min(budget_tokens, inp.L)
     with threadpool_limits(limits=1):
         t0 = time.perf_counter()
-        h = oracle.implicit_filter(inp.filter_params, inp.L, inp.N, inp.D)[:, :, :T]
-        oracle.hyena_fwd(inp.u[:, :T], inp.w_in, inp.short_w, inp.dskip, inp.w_out, h, conv="fft")
+        if inp.causal:
+            h = oracle.implicit_filter(inp.filter_params, inp.L, inp.N, inp.D)[:, :, :T]
+        else:
+            h = oracle.implicit_filter_noncausal(inp.filter_params, T, inp.N, inp.D)
+        oracle.hyena_fwd(inp.u[:, :T], inp.w_in, inp.short_w, inp.dskip, inp.w_out, h, conv="fft",
+                         causal=inp.causal)
         dt = time.perf_counter() - t0
+    what = "first" if inp.causal else "a non-causal operator of length T on the first"
     return {"value": inp.B * T / dt, "unit": "tokens/s", "cores": 1, "kind": "oracle",
-            "sample": f"first {T} of {inp.L} positions x B={inp.B} (all {inp.D} channels), fp64 numpy, "
+            "sample": f"{what} {T} of {inp.L} positions x B={inp.B} (all {inp.D} channels), fp64 numpy, "
                       f"FFT path, 1 thread, {dt:.1f} s"}
 
 
@@ -323,7 +330,7 @@ def main():
     dev = "cuda"
     f = lambda a, d=torch.float32: torch.from_numpy(np.ascontiguousarray(a, np.float32)).to(dev, d)  # noqa: E731
 
-    layer = hs.HyenaLayer(L, D, N)
+    layer = hs.HyenaLayer(L, D, N, direction=hs.CAUSAL if inp.causal else hs.NONCAUSAL)
     hs.hyena_filter_gen(layer, f(inp.w1), f(inp.b1), f(inp.w2), f(inp.b2), f(inp.w3), f(inp.b3), f(inp.decay),
                         inp.K)
     u, w_in, w_out = f(inp.u, tdt), f(inp.w_in, tdt), f(inp.w_out, tdt)
@@ -382,7 +389,7 @@ def main():
                      "frac": gi / VALU_PEAK_GINSTR, "fp32_tflops": tf, "fp32_peak_tflops": VALU_F32_PEAK_TFLOPS}
 
     out = {
-        "metric": METRIC,
+        "metric": METRIC if inp.causal else METRIC + " [non-causal filters]",
         "value": value,
         "unit": "tokens/s",
         "n_gpus": 1,
@@ -394,7 +401,8 @@ def main():
         "vs_baseline": None,
         "dtype": inp.dtype,
         "data": "synthetic",
-        "config": {"workload": args.workload, "B": B, "L": L, "D": D, "N": N},
+        "config": {"workload": args.workload, "B": B, "L": L, "D": D, "N": N,
+                   "direction": "causal" if inp.causal else "non-causal"},
         "stage_ms": {"in_proj": stages[0], "fft_conv": stages[1], "out_proj": stages[2]},
         "step_ms_events": {"p10": float(np.percentile(step_ms, 10)), "p50": float(np.median(step_ms)),
                            "p90": float(np.percentile(step_ms, 90))},

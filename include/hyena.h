@@ -68,6 +68,16 @@ typedef struct {
   const float *w1, *b1, *w2, *b2, *w3, *b3, *decay;
 } hyena_filter_params;
 
+/* Direction of the long convolution.
+ *   HYENA_CAUSAL     c_t = sum_{s=0..t} h(s) z_{t-s} (the default).
+ *   HYENA_NONCAUSAL  two-sided filters: the same generator at the signed lags
+ *                    tau in [-(L-1), L-1] (PosEnc at tau/L, window
+ *                    exp(-decay_c |tau|/L)) and c_t = sum_tau h(tau) z_{t-tau},
+ *                    z zero outside [0, L). The pages name causal use and
+ *                    bidirectional comparators only; this is the reading taken.
+ *                    The short convolution keeps its causal taps. */
+typedef enum { HYENA_CAUSAL = 0, HYENA_NONCAUSAL = 1 } hyena_direction;
+
 /* Host-side handle of one layer's filter cache. The cache is caller-owned
  * device memory of hyena_cache_bytes(L, D, N) bytes holding twiddle tables and
  * the spectra of the zero-padded filters in an internal (opaque) order. It is
@@ -77,6 +87,7 @@ typedef struct {
   int built;            /* set to 1 by hyena_filter_gen */
   void *cache;
   size_t cache_bytes;
+  int direction;        /* hyena_direction, set by the init call */
 } hyena_layer;
 
 /* Supported shapes: L a power of two in [16, 2^20]; D a multiple of 64 in
@@ -85,14 +96,24 @@ typedef struct {
 size_t hyena_cache_bytes(int L, int D, int N);
 size_t hyena_filter_workspace_bytes(int L, int D, int N);
 size_t hyena_workspace_bytes(int B, int L, int D, int N, int dtype);
+/* Filter workspace for a direction (twice the filter buffer when non-causal);
+ * 0 for an unknown direction. The cache and forward sizes do not depend on it. */
+size_t hyena_filter_workspace_bytes_ex(int L, int D, int N, int direction);
 
-/* Fills the host struct (no HIP call). `cache` must hold hyena_cache_bytes. */
+/* Fills the host struct (no HIP call). `cache` must hold hyena_cache_bytes.
+ * hyena_layer_init is the causal direction; hyena_layer_init_ex takes one
+ * (HYENA_ERR_UNSUPPORTED for an unknown direction). */
 int hyena_layer_init(hyena_layer *layer, int L, int D, int N, void *cache, size_t cache_bytes);
+int hyena_layer_init_ex(hyena_layer *layer, int L, int D, int N, int direction, void *cache,
+                        size_t cache_bytes);
 
-/* Evaluates the implicit filters h^n for t in [0, L) and stores the spectra of
- * [h^n, 0_L] (size-2L DFT) in layer->cache. If h_out is not NULL the filters are
- * also written there as fp32 [N][D][L]. `ws` is scratch of at least
- * hyena_filter_workspace_bytes(L, D, N) bytes. Sets layer->built = 1. */
+/* Evaluates the implicit filters h^n and stores the spectra of their size-2L
+ * DFTs in layer->cache: causal, [h^n(0..L-1), 0_L]; non-causal, the two-sided
+ * filter wrapped (lag tau at tau mod 2L, entry L zero). If h_out is not NULL the
+ * filters are also written there as fp32 [N][D][L] (causal) or in that wrapped
+ * form [N][D][2L] (non-causal). `ws` is scratch of at least
+ * hyena_filter_workspace_bytes_ex(L, D, N, layer->direction) bytes. Sets
+ * layer->built = 1. */
 int hyena_filter_gen(hyena_layer *layer, const hyena_filter_params *p, float *h_out,
                      void *ws, size_t ws_bytes, hipStream_t stream);
 

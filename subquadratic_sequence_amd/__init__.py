@@ -4,6 +4,8 @@ The compute lives in libhyena.so (hand-written HIP kernels for gfx950 behind a C
 ABI, declared in include/hyena.h); this package is a thin ctypes binding.
 """
 from .hyena import (  # noqa: F401
+    CAUSAL,
+    NONCAUSAL,
     HYENA_BF16,
     HYENA_F32,
     HyenaError,
@@ -16,6 +18,7 @@ from .hyena import (  # noqa: F401
     hyena_cache_bytes,
     hyena_filter_gen,
     hyena_filter_workspace_bytes,
+    hyena_filter_workspace_bytes_ex,
     hyena_fwd,
     hyena_fwd_profiled,
     hyena_nd_cache_bytes,

@@ -79,14 +79,17 @@ hy::FourStepTables tables(const CacheLayout& c, void* cache) {
 }
 
 // ------------------------------------------------------------ workspace layouts
+bool direction_ok(int dir) { return dir == HYENA_CAUSAL || dir == HYENA_NONCAUSAL; }
+
 struct FilterWs {
   size_t h, Y, total;
 };
-FilterWs filter_ws(int L, int D, int N) {
+// h: [N][D][L] causal, [N][D][2L] (wrapped two-sided filter) non-causal
+FilterWs filter_ws(int L, int D, int N, int dir) {
   FilterWs w{};
   size_t off = 0;
   w.h = off;
-  off = align_up(off + (size_t)N * D * L * 4, kAlign);
+  off = align_up(off + (size_t)N * D * L * 4 * (dir == HYENA_NONCAUSAL ? 2 : 1), kAlign);
   w.Y = off;
   if (L > kLdsMaxL) off = align_up(off + (size_t)N * (D / 2) * 2 * (size_t)L * 8, kAlign);
   w.total = off;
@@ -183,9 +186,13 @@ size_t hyena_cache_bytes(int L, int D, int N) {
   return cache_layout(L, D, N).total;
 }
 
+size_t hyena_filter_workspace_bytes_ex(int L, int D, int N, int direction) {
+  if (!shape_ok(L, D, N) || !direction_ok(direction)) return 0;
+  return filter_ws(L, D, N, direction).total;
+}
+
 size_t hyena_filter_workspace_bytes(int L, int D, int N) {
-  if (!shape_ok(L, D, N)) return 0;
-  return filter_ws(L, D, N).total;
+  return hyena_filter_workspace_bytes_ex(L, D, N, HYENA_CAUSAL);
 }
 
 size_t hyena_workspace_bytes(int B, int L, int D, int N, int dtype) {
@@ -194,9 +201,9 @@ size_t hyena_workspace_bytes(int B, int L, int D, int N, int dtype) {
   return fwd_ws(B, L, D, N, dtype).total;
 }
 
-int hyena_layer_init(hyena_layer* layer, int L, int D, int N, void* cache, size_t cache_bytes) {
+int hyena_layer_init_ex(hyena_layer* layer, int L, int D, int N, int direction, void* cache, size_t cache_bytes) {
   if (layer == nullptr) return HYENA_ERR_INVALID_ARG;
-  if (!shape_ok(L, D, N)) return HYENA_ERR_UNSUPPORTED;
+  if (!shape_ok(L, D, N) || !direction_ok(direction)) return HYENA_ERR_UNSUPPORTED;
   if (!aligned16(cache)) return HYENA_ERR_INVALID_ARG;
   if (cache_bytes < cache_layout(L, D, N).total) return HYENA_ERR_WORKSPACE;
   layer->L = L;
@@ -205,14 +212,19 @@ int hyena_layer_init(hyena_layer* layer, int L, int D, int N, void* cache, size_
   layer->built = 0;
   layer->cache = cache;
   layer->cache_bytes = cache_bytes;
+  layer->direction = direction;
   return HYENA_OK;
+}
+
+int hyena_layer_init(hyena_layer* layer, int L, int D, int N, void* cache, size_t cache_bytes) {
+  return hyena_layer_init_ex(layer, L, D, N, HYENA_CAUSAL, cache, cache_bytes);
 }
 
 int hyena_filter_gen(hyena_layer* layer, const hyena_filter_params* p, float* h_out, void* ws, size_t ws_bytes,
                      hipStream_t stream) {
   if (layer == nullptr || p == nullptr) return HYENA_ERR_INVALID_ARG;
-  const int L = layer->L, D = layer->D, N = layer->N;
-  if (!shape_ok(L, D, N)) return HYENA_ERR_UNSUPPORTED;
+  const int L = layer->L, D = layer->D, N = layer->N, dir = layer->direction;
+  if (!shape_ok(L, D, N) || !direction_ok(dir)) return HYENA_ERR_UNSUPPORTED;
   if (!aligned16(layer->cache)) return HYENA_ERR_INVALID_ARG;
   const CacheLayout cl = cache_layout(L, D, N);
   if (layer->cache_bytes < cl.total) return HYENA_ERR_WORKSPACE;
@@ -221,21 +233,23 @@ int hyena_filter_gen(hyena_layer* layer, const hyena_filter_params* p, float* h_
   for (const void* q : ptrs)
     if (!aligned16(q)) return HYENA_ERR_INVALID_ARG;
   if (h_out != nullptr && !aligned16(h_out)) return HYENA_ERR_INVALID_ARG;
-  const FilterWs fw = filter_ws(L, D, N);
+  const FilterWs fw = filter_ws(L, D, N, dir);
   if (ws_bytes < fw.total) return HYENA_ERR_WORKSPACE;
   if (device_ok() != HYENA_OK) return HYENA_ERR_HIP;
 
   char* wsb = static_cast<char*>(ws);
   char* cb = static_cast<char*>(layer->cache);
   float* h = h_out ? h_out : reinterpret_cast<float*>(wsb + fw.h);
-  hy::Filter1DArgs fa{L, D, N, p->pe_freqs, p->width, p->w1, p->b1, p->w2, p->b2, p->w3, p->b3, p->decay, h};
+  const bool two_sided = dir == HYENA_NONCAUSAL;
+  hy::Filter1DArgs fa{L,     D,     N,     p->pe_freqs, p->width, p->w1,    p->b1,
+                      p->w2, p->b2, p->w3, p->b3,       p->decay, h,        two_sided ? 1 : 0};
   layer->built = 0;
   HY_CHECK_HIP(hy::filter1d_mlp(fa, stream));
   const int n = 2 * L;
   if (cl.lds) {
     float2* tw = reinterpret_cast<float2*>(cb + cl.tw);
     HY_CHECK_HIP(hy::twiddles(tw, n, n, stream));
-    HY_CHECK_HIP(hy::lds_spec(h, tw, reinterpret_cast<float4*>(cb + cl.pq), L, D, N, stream));
+    HY_CHECK_HIP(hy::lds_spec(h, tw, reinterpret_cast<float4*>(cb + cl.pq), L, D, N, two_sided, stream));
   } else {
     HY_CHECK_HIP(hy::twiddles(reinterpret_cast<float2*>(cb + cl.w256), 256, 256, stream));
     HY_CHECK_HIP(hy::twiddles(reinterpret_cast<float2*>(cb + cl.tw_lo), n, 1 << cl.lo_bits, stream));
@@ -243,7 +257,7 @@ int hyena_filter_gen(hyena_layer* layer, const hyena_filter_params* p, float* h_
     HY_CHECK_HIP(hy::twiddles(reinterpret_cast<float2*>(cb + cl.tw_hi), n >> cl.lo_bits, n >> cl.lo_bits, stream));
     HY_CHECK_HIP(hy::twiddles(reinterpret_cast<float2*>(cb + cl.tw_row), cl.N2, cl.N2, stream));
     HY_CHECK_HIP(hy::fourstep_spec(tables(cl, layer->cache), h, reinterpret_cast<float2*>(wsb + fw.Y),
-                                   reinterpret_cast<float4*>(cb + cl.pq), L, D, N, stream));
+                                   reinterpret_cast<float4*>(cb + cl.pq), L, D, N, two_sided, stream));
   }
   layer->built = 1;
   return HYENA_OK;

@@ -111,22 +111,24 @@ __global__ __launch_bounds__(LdsCfg<N>::WG) void fftconv_lds_kernel(
 }
 
 // Filter spectrum in the LDS regime: (h_a + i h_b) zero padded -> DFT -> (P, Q).
-template <int N>
+// WRAP: two-sided filters, rows of 2L already wrapped (no zero half).
+template <int N, bool WRAP>
 __global__ __launch_bounds__(LdsCfg<N>::WG) void filter_spec_lds_kernel(
     const float* __restrict__ h, const float2* __restrict__ tw, float4* __restrict__ pq, int D, int NO) {
   using C = LdsCfg<N>;
   constexpr int L = N / 2;
+  constexpr int RL = WRAP ? N : L;  // row length of h
   extern __shared__ float4 smem4[];
   float2* fb = reinterpret_cast<float2*>(smem4) + (threadIdx.x / C::TG) * C::FB;
   const int lt = threadIdx.x % C::TG;
   const int pr = blockIdx.x * C::G + threadIdx.x / C::TG;  // over NO * D/2
   const int half = D / 2;
   const int n = pr / half, cp = pr % half;
-  const float* ha = h + ((size_t)n * D + 2 * cp) * L;
-  const float* hb = ha + L;
+  const float* ha = h + ((size_t)n * D + 2 * cp) * RL;
+  const float* hb = ha + RL;
   for (int t = lt; t < L; t += C::TG) {
     fb[pad16(t)] = make_float2(ha[t], hb[t]);
-    fb[pad16(t + L)] = make_float2(0.f, 0.f);
+    fb[pad16(t + L)] = WRAP ? make_float2(ha[t + L], hb[t + L]) : make_float2(0.f, 0.f);
   }
   __syncthreads();
   fft_lds<N, C::E, false>(fb, lt, tw);
@@ -155,7 +157,7 @@ struct ColArgs {
   const void* zin;        // z^n [B][D][L] for n >= 1
   void* zout;             // z^{n+1} [B][D][L]
   void* Y;                // intermediate [pairs][N1][N2] (complex fp32 or bf16 pairs)
-  const float* h;         // filter rows [NO][D][L] (filter mode)
+  const float* h;         // filter rows [NO][D][L] (filter mode), [NO][D][2L] wrapped (two-sided)
   const float2* w256;     // W_256^m, m in [0, 256)
   const float2* tw_lo;    // W_N^m = tw_lo[m & lo_mask] * tw_hi[m >> lo_bits]
   const float2* tw_hi;
@@ -163,7 +165,8 @@ struct ColArgs {
   int pair_off;           // global index of the first channel pair of this launch
 };
 
-enum { COL_FWD_V = 0, COL_FWD_H = 1, COL_INV = 2, COL_INV_FWD = 3 };
+// COL_FWD_HW: forward column pass of two-sided filters (wrapped rows of 2L, no zero half)
+enum { COL_FWD_V = 0, COL_FWD_H = 1, COL_INV = 2, COL_INV_FWD = 3, COL_FWD_HW = 4 };
 
 __device__ __forceinline__ float2 cvt2(float2 v) { return v; }
 __device__ __forceinline__ float2 cvt2(cbf16 v) {
@@ -254,6 +257,8 @@ template <typename T, typename YT, int R, int MODE>
 __global__ __launch_bounds__(R * col_width<R>()) void colpass_kernel(ColArgs a, int nitems) {
   constexpr int N1 = R * R, H = R / 2;
   constexpr bool INVERSE = (MODE == COL_INV || MODE == COL_INV_FWD);
+  constexpr bool FILT = (MODE == COL_FWD_H || MODE == COL_FWD_HW);
+  constexpr int HF = MODE == COL_FWD_HW ? R : H;  // non-zero filter rows per thread
   constexpr int sT = (int)sizeof(T), sY = (int)sizeof(YT);
   extern __shared__ float4 smem4[];
   float2* S = reinterpret_cast<float2*>(smem4);
@@ -276,7 +281,7 @@ __global__ __launch_bounds__(R * col_width<R>()) void colpass_kernel(ColArgs a, 
     YT y[INVERSE ? R : 1];                    // inverse: column of the intermediate
     T xa[INVERSE ? H : 1], xb[INVERSE ? H : 1];  // inverse: gates x^n
     T za[H], zb[H];                           // z^n (forward of z^1: the v block)
-    float ha[MODE == COL_FWD_H ? H : 1], hb[MODE == COL_FWD_H ? H : 1];  // filter mode
+    float ha[FILT ? HF : 1], hb[FILT ? HF : 1];  // filter modes
     float da, db;                             // inverse: skip weights D^n of the pair
     ColTw tw;
   };
@@ -305,13 +310,14 @@ __global__ __launch_bounds__(R * col_width<R>()) void colpass_kernel(ColArgs a, 
   };
   // first part: what the item's first transform reads
   auto load_head = [&](const Item& it, In& in) {
-    if constexpr (MODE == COL_FWD_H) {
+    if constexpr (FILT) {
       const int n = it.pr / half, cp = it.pr % half;
-      const brsrc rh = pair_rows(a.h, (size_t)n * D + 2 * cp, 4);
+      const int RL = MODE == COL_FWD_HW ? 2 * L : L;  // filter row length
+      const brsrc rh = make_brsrc(a.h + ((size_t)n * D + 2 * cp) * RL, 2u * (unsigned)RL * 4);
 #pragma unroll
-      for (int r = 0; r < H; ++r) {
+      for (int r = 0; r < HF; ++r) {
         in.ha[r] = BufIO<float>::ld(rh, voH, col0(it, r) * 4);
-        in.hb[r] = BufIO<float>::ld(rh, voH, (col0(it, r) + L) * 4);
+        in.hb[r] = BufIO<float>::ld(rh, voH, (col0(it, r) + RL) * 4);
       }
     } else if constexpr (MODE == COL_FWD_V) {
       const int b = it.pr / half, cp = it.pr % half;
@@ -357,14 +363,13 @@ __global__ __launch_bounds__(R * col_width<R>()) void colpass_kernel(ColArgs a, 
     const float2 wk = cmul(in.tw.lo0, in.tw.hi0), ws = cmul(in.tw.lo1, in.tw.hi1);
     load_tw(nt, in);
     float2 v[R];
-    if constexpr (MODE == COL_FWD_H || MODE == COL_FWD_V) {
+    if constexpr (FILT || MODE == COL_FWD_V) {
 #pragma unroll
       for (int r = 0; r < R; ++r) {
-        if (r < H)
-          v[r] = MODE == COL_FWD_H ? make_float2(in.ha[r], in.hb[r])
-                                   : make_float2(cvt1(in.za[r]), cvt1(in.zb[r]));
+        if constexpr (FILT)
+          v[r] = r < HF ? make_float2(in.ha[r], in.hb[r]) : make_float2(0.f, 0.f);
         else
-          v[r] = make_float2(0.f, 0.f);
+          v[r] = r < H ? make_float2(cvt1(in.za[r]), cvt1(in.zb[r])) : make_float2(0.f, 0.f);
       }
       load_head(nt, in);
       col_forward<R, YT>(v, S, rY, voY, soY, N2, c, w, wr, wk, ws);
@@ -1072,11 +1077,12 @@ static hipError_t launch_lds_conv(const LdsConvArgs& a, hipStream_t s) {
 }
 
 template <int N>
-static hipError_t launch_lds_spec(const float* h, const float2* tw, float4* pq, int D, int NO, hipStream_t s) {
+static hipError_t launch_lds_spec(const float* h, const float2* tw, float4* pq, int D, int NO, bool wrapped,
+                                  hipStream_t s) {
   using C = LdsCfg<N>;
   const int pairs = NO * D / 2;
   const size_t lds = (size_t)C::G * C::FB * 8;
-  auto fn = filter_spec_lds_kernel<N>;
+  auto fn = wrapped ? filter_spec_lds_kernel<N, true> : filter_spec_lds_kernel<N, false>;
   hipError_t e = allow_lds((const void*)fn, lds);
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(fn, dim3(pairs / C::G), dim3(C::WG), lds, s, h, tw, pq, D, NO);
@@ -1112,10 +1118,11 @@ hipError_t lds_conv(const LdsConvArgs& a, bool is_bf16, hipStream_t s) {
   return e;
 }
 
-hipError_t lds_spec(const float* h, const float2* tw, float4* pq, int L, int D, int NO, hipStream_t s) {
+hipError_t lds_spec(const float* h, const float2* tw, float4* pq, int L, int D, int NO, bool wrapped,
+                    hipStream_t s) {
   const int N = 2 * L;
   hipError_t e = hipSuccess;
-#define CALLS(n) e = launch_lds_spec<n>(h, tw, pq, D, NO, s)
+#define CALLS(n) e = launch_lds_spec<n>(h, tw, pq, D, NO, wrapped, s)
   HY_LDS_SWITCH(N, CALLS)
 #undef CALLS
   return e;
@@ -1155,6 +1162,7 @@ static hipError_t launch_col_r(const ColArgs& a, int mode, int pairs, hipStream_
   switch (mode) {
     case COL_FWD_V: return launch_col_t<T, YT, R, COL_FWD_V>(a, pairs, s);
     case COL_FWD_H: return launch_col_t<float, float2, R, COL_FWD_H>(a, pairs, s);
+    case COL_FWD_HW: return launch_col_t<float, float2, R, COL_FWD_HW>(a, pairs, s);
     case COL_INV: return launch_col_t<T, YT, R, COL_INV>(a, pairs, s);
     default: return launch_col_t<T, YT, R, COL_INV_FWD>(a, pairs, s);
   }
@@ -1248,13 +1256,13 @@ static ColArgs col_args(const FourStepTables& tb, int L, int D, int NO) {
 }
 
 hipError_t fourstep_spec(const FourStepTables& tb, const float* h, float2* Y, float4* pq, int L, int D, int NO,
-                         hipStream_t s) {
+                         bool wrapped, hipStream_t s) {
   ColArgs a = col_args(tb, L, D, NO);
   const int N1 = fourstep_n1(L);
   a.h = h;
   a.Y = Y;
   const int pairs = NO * D / 2;
-  hipError_t e = launch_col(a, N1, COL_FWD_H, false, false, pairs, s);
+  hipError_t e = launch_col(a, N1, wrapped ? COL_FWD_HW : COL_FWD_H, false, false, pairs, s);
   if (e != hipSuccess) return e;
   return launch_row_y<float2>(N1, a.N2, Y, pq, tb.tw_row, 0, 0, pairs, pairs, ROW_SPEC, s);
 }

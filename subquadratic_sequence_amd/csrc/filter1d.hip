@@ -8,6 +8,13 @@
 // One workgroup evaluates a tile of 64 positions: features and both hidden
 // layers go to LDS, then every thread produces one output column for the 64
 // positions (the W x N*D output layer dominates the work).
+//
+// Non-causal layers evaluate the same generator at the signed lags of a
+// two-sided filter, written wrapped for the 2L-point transform: position
+// m in [0, 2L) holds lag m (m < L) or m - 2L (m > L), and m = L is zero. The
+// features at lag tau are [tau / L, cos, sin of 2 pi k tau / L] (the angles
+// equal those at m, the cosines and sines having period L) and the window is
+// exp(-decay |tau| / L).
 #include "common.h"
 #include "kernels.h"
 
@@ -23,14 +30,15 @@ __global__ __launch_bounds__(256) void filter1d_mlp_kernel(Filter1DArgs a) {
   __shared__ float h2[kFT][kMaxW + 1];
   const int t0 = blockIdx.x * kFT;
   const int F = 1 + 2 * a.K, W = a.W, L = a.L;
+  const int P = a.noncausal ? 2 * L : L;  // positions evaluated
   const int tid = threadIdx.x;
   for (int idx = tid; idx < kFT * F; idx += 256) {
     const int tl = idx / F, f = idx % F;
     const int t = t0 + tl;
     float v = 0.f;
-    if (t < L) {
+    if (t < P) {
       if (f == 0) {
-        v = (float)t / (float)L;
+        v = (float)(t > L ? t - 2 * L : t) / (float)L;
       } else {
         const int k = (f <= a.K) ? f : f - a.K;
         // angle 2 pi k t / L reduced exactly: 2 pi m / L with m = (k t) mod L
@@ -71,10 +79,12 @@ __global__ __launch_bounds__(256) void filter1d_mlp_kernel(Filter1DArgs a) {
     }
     const int c = col % a.D;
     const float dc = a.decay[c];
-    float* dst = a.h + (size_t)col * L + t0;   // h[n][c][t] with col = n D + c
+    float* dst = a.h + (size_t)col * P + t0;   // h[n][c][t] with col = n D + c
 #pragma unroll
     for (int tl = 0; tl < kFT; ++tl) {
-      if (t0 + tl < L) dst[tl] = acc[tl] * expf(-dc * (float)(t0 + tl) * invL);
+      const int t = t0 + tl;
+      const int lag = t > L ? 2 * L - t : t;   // |tau|
+      if (t < P) dst[tl] = (t == L && P > L) ? 0.f : acc[tl] * expf(-dc * (float)lag * invL);
     }
   }
 }
@@ -98,6 +108,7 @@ __global__ __launch_bounds__(256) void filter1d_mfma_kernel(Filter1DArgs a) {
   __shared__ float buf1[kFT * LDH];                                  // layer 1
   const int t0 = blockIdx.x * kFT;
   const int F = 1 + 2 * a.K, Fp = (F + 1) & ~1, L = a.L;
+  const int P = a.noncausal ? 2 * L : L;  // positions evaluated
   const int LDE = Fp + 1;  // feature row stride
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int r32 = lane & 31, k2 = lane >> 5;
@@ -105,9 +116,9 @@ __global__ __launch_bounds__(256) void filter1d_mfma_kernel(Filter1DArgs a) {
     const int tl = idx / Fp, f = idx % Fp;
     const int t = t0 + tl;
     float v = 0.f;
-    if (t < L && f < F) {
+    if (t < P && f < F) {
       if (f == 0) {
-        v = (float)t / (float)L;
+        v = (float)(t > L ? t - 2 * L : t) / (float)L;
       } else {
         const int k = (f <= a.K) ? f : f - a.K;
         // angle 2 pi k t / L reduced exactly: 2 pi m / L with m = (k t) mod L
@@ -185,7 +196,7 @@ __global__ __launch_bounds__(256) void filter1d_mfma_kernel(Filter1DArgs a) {
     load_w3(more ? nxt : cb);  // the next block's slice (this one's again after the last: unused)
     const float bias = a.b3[colc];
     const float dc = a.decay[colc % a.D];
-    float* dst = a.h + (size_t)colc * L;  // h[n][c][t] with col = n D + c
+    float* dst = a.h + (size_t)colc * P;  // h[n][c][t] with col = n D + c
 #pragma unroll
     for (int rb = 0; rb < 2; ++rb) {
 #pragma unroll
@@ -193,15 +204,18 @@ __global__ __launch_bounds__(256) void filter1d_mfma_kernel(Filter1DArgs a) {
         const int t = t0 + rb * 32 + g * 8 + k2 * 4;  // four consecutive positions
         float o[4];
 #pragma unroll
-        for (int i = 0; i < 4; ++i)
-          o[i] = ((rb ? acc1[4 * g + i] : acc0[4 * g + i]) + bias) * expf(-dc * (float)(t + i) * invL);
+        for (int i = 0; i < 4; ++i) {
+          const int lag = t + i > L ? 2 * L - (t + i) : t + i;  // |tau|
+          o[i] = ((rb ? acc1[4 * g + i] : acc0[4 * g + i]) + bias) * expf(-dc * (float)lag * invL);
+          if (t + i == L && P > L) o[i] = 0.f;
+        }
         if (col < ND) {
-          if (t + 3 < L && (L & 3) == 0) {
+          if (t + 3 < P && (P & 3) == 0) {
             *reinterpret_cast<float4*>(dst + t) = make_float4(o[0], o[1], o[2], o[3]);
           } else {
 #pragma unroll
             for (int i = 0; i < 4; ++i)
-              if (t + i < L) dst[t + i] = o[i];
+              if (t + i < P) dst[t + i] = o[i];
           }
         }
       }
@@ -212,7 +226,8 @@ __global__ __launch_bounds__(256) void filter1d_mfma_kernel(Filter1DArgs a) {
 }
 
 hipError_t filter1d_mlp(const Filter1DArgs& a, hipStream_t s) {
-  dim3 grid((a.L + kFT - 1) / kFT), block(256);
+  const int P = a.noncausal ? 2 * a.L : a.L;
+  dim3 grid((P + kFT - 1) / kFT), block(256);
   if (a.W == 64 && 1 + 2 * a.K <= kMaxF)
     hipLaunchKernelGGL(filter1d_mfma_kernel<64>, grid, block, 0, s, a);
   else if (a.W == 128 && 1 + 2 * a.K <= kMaxF)

@@ -28,7 +28,8 @@ hipError_t transpose2d(const void* src, void* dst, int rows, int cols, bool bf16
 struct Filter1DArgs {
   int L, D, NO, K, W;
   const float *w1, *b1, *w2, *b2, *w3, *b3, *decay;
-  float* h;  // [NO][D][L]
+  float* h;       // [NO][D][L], or [NO][D][2L] wrapped when noncausal
+  int noncausal;  // two-sided filter: position m holds lag m (m < L) or m - 2L (m > L); m = L is zero
 };
 hipError_t filter1d_mlp(const Filter1DArgs& a, hipStream_t s);
 // tw[m] = exp(-2 pi i m / n) for m in [0, count), computed in double
@@ -44,7 +45,9 @@ struct LdsConvArgs {
   int B, L, D, NO;
 };
 hipError_t lds_conv(const LdsConvArgs& a, bool bf16, hipStream_t s);
-hipError_t lds_spec(const float* h, const float2* tw, float4* pq, int L, int D, int NO, hipStream_t s);
+// h [NO][D][L] (zero padded to 2L here) or, wrapped, [NO][D][2L] (two-sided filters)
+hipError_t lds_spec(const float* h, const float2* tw, float4* pq, int L, int D, int NO, bool wrapped,
+                    hipStream_t s);
 size_t lds_conv_smem(int L);
 
 // --------------------------------------------------------- four-step
@@ -71,7 +74,7 @@ struct FourStepConvArgs {
 };
 hipError_t fourstep_conv(const FourStepTables& tb, const FourStepConvArgs& c, bool bf16, hipStream_t s);
 hipError_t fourstep_spec(const FourStepTables& tb, const float* h, float2* Y, float4* pq, int L, int D, int NO,
-                         hipStream_t s);
+                         bool wrapped, hipStream_t s);
 
 // --------------------------------------------------------------- 3D path
 // Transform sizes (MX, MY, MZ): (2X, 2Y, 2Z) for the zero-padded boundary,

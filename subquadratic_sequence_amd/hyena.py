@@ -30,7 +30,13 @@ class FilterParams(ctypes.Structure):
 
 
 class Layer(ctypes.Structure):
-    _fields_ = [("L", _i), ("D", _i), ("N", _i), ("built", _i), ("cache", _vp), ("cache_bytes", _sz)]
+    _fields_ = [("L", _i), ("D", _i), ("N", _i), ("built", _i), ("cache", _vp), ("cache_bytes", _sz),
+                ("direction", _i)]
+
+
+# hyena_direction
+CAUSAL = 0
+NONCAUSAL = 1
 
 
 class NDFilterParams(ctypes.Structure):
@@ -55,6 +61,8 @@ SIGNATURES = {
     "hyena_filter_workspace_bytes": (_sz, [_i, _i, _i]),
     "hyena_workspace_bytes": (_sz, [_i, _i, _i, _i, _i]),
     "hyena_layer_init": (_i, [ctypes.POINTER(Layer), _i, _i, _i, _vp, _sz]),
+    "hyena_layer_init_ex": (_i, [ctypes.POINTER(Layer), _i, _i, _i, _i, _vp, _sz]),
+    "hyena_filter_workspace_bytes_ex": (_sz, [_i, _i, _i, _i]),
     "hyena_filter_gen": (_i, [ctypes.POINTER(Layer), ctypes.POINTER(FilterParams), _vp, _vp, _sz, _vp]),
     "hyena_fwd": (_i, [ctypes.POINTER(Layer), _vp, _vp, _vp, _vp, _vp, _i, _i, _vp, _vp, _sz, _vp]),
     "hyena_fwd_profiled": (_i, [ctypes.POINTER(Layer), _vp, _vp, _vp, _vp, _vp, _i, _i, _vp, _vp, _sz, _vp,
@@ -135,28 +143,35 @@ def hyena_filter_workspace_bytes(L: int, D: int, N: int) -> int:
     return lib().hyena_filter_workspace_bytes(L, D, N)
 
 
+def hyena_filter_workspace_bytes_ex(L: int, D: int, N: int, direction: int) -> int:
+    return lib().hyena_filter_workspace_bytes_ex(L, D, N, direction)
+
+
 def hyena_workspace_bytes(B: int, L: int, D: int, N: int, dtype: int) -> int:
     return lib().hyena_workspace_bytes(B, L, D, N, dtype)
 
 
 class HyenaLayer:
-    """One layer's filter cache (device memory owned by this object)."""
+    """One layer's filter cache (device memory owned by this object); direction
+    CAUSAL (default) or NONCAUSAL (two-sided filters)."""
 
-    def __init__(self, L: int, D: int, N: int, device="cuda"):
+    def __init__(self, L: int, D: int, N: int, device="cuda", direction: int = CAUSAL):
         nbytes = hyena_cache_bytes(L, D, N)
         if nbytes == 0:
             raise HyenaError(2, "hyena_cache_bytes")
         self.cache = torch.empty(nbytes, dtype=torch.uint8, device=device)
         self.c = Layer()
-        _check(lib().hyena_layer_init(ctypes.byref(self.c), L, D, N, _ptr(self.cache), nbytes), "hyena_layer_init")
+        _check(lib().hyena_layer_init_ex(ctypes.byref(self.c), L, D, N, direction, _ptr(self.cache), nbytes),
+               "hyena_layer_init_ex")
         self.L, self.D, self.N = L, D, N
+        self.direction = direction
 
 
 def hyena_filter_gen(layer: HyenaLayer, w1, b1, w2, b2, w3, b3, decay, pe_freqs: int, h_out=None, ws=None):
     """Generates the implicit filters and caches their spectra in layer.cache."""
     width = w1.shape[1]
     p = FilterParams(pe_freqs, width, _ptr(w1), _ptr(b1), _ptr(w2), _ptr(b2), _ptr(w3), _ptr(b3), _ptr(decay))
-    need = hyena_filter_workspace_bytes(layer.L, layer.D, layer.N)
+    need = hyena_filter_workspace_bytes_ex(layer.L, layer.D, layer.N, layer.direction)
     if ws is None:
         ws = torch.empty(need, dtype=torch.uint8, device=layer.cache.device)
     st = lib().hyena_filter_gen(ctypes.byref(layer.c), ctypes.byref(p), _ptr(h_out), _ptr(ws), ws.numel(),

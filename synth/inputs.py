@@ -69,6 +69,7 @@ class Hyena1DInputs:
     w3: np.ndarray       # [W, N*D]
     b3: np.ndarray       # [N*D]
     decay: np.ndarray    # [D]
+    causal: bool = True  # False: two-sided (non-causal) long filters
     meta: dict = field(default_factory=dict)
 
     @property
@@ -109,13 +110,14 @@ class HyenaNDInputs:
 
 
 def make_1d(seed: int, B: int, L: int, D: int, N: int = 2, K: int = 16, W: int = 64,
-            dtype: str = "f32", u_scale: float = 1.0, tokens: int = 0) -> Hyena1DInputs:
+            dtype: str = "f32", u_scale: float = 1.0, tokens: int = 0, causal: bool = True) -> Hyena1DInputs:
     """Draw one 1D workload.
 
     u ~ N(0, 1) * u_scale, or (tokens > 0) u = E[tok] with tok uniform over
     `tokens` symbols and E ~ N(0, 1) of shape [tokens, D].
     w_in, w_out ~ N(0, 1/D); short_w ~ U(-0.5, 0.5); dskip ~ N(0, 1);
     FFN weights and biases ~ U(-1/sqrt(fan_in), 1/sqrt(fan_in)).
+    `causal` = False selects two-sided filters; it changes no draw.
     """
     if dtype not in ("f32", "bf16"):
         raise ValueError(dtype)
@@ -141,7 +143,7 @@ def make_1d(seed: int, B: int, L: int, D: int, N: int = 2, K: int = 16, W: int =
     b3 = _uniform(rng, (N * D,), 1 / math.sqrt(W)).astype(np.float32)
     return Hyena1DInputs(B=B, L=L, D=D, N=N, K=K, W=W, dtype=dtype, u=u, w_in=w_in,
                          short_w=short_w, dskip=dskip, w_out=w_out, w1=w1, b1=b1,
-                         w2=w2, b2=b2, w3=w3, b3=b3, decay=decay_rates(D),
+                         w2=w2, b2=b2, w3=w3, b3=b3, decay=decay_rates(D), causal=causal,
                          meta=dict(seed=seed, u_scale=u_scale, tokens=tokens))
 
 
@@ -201,6 +203,9 @@ TEST_SHAPES = {
     "nd3d_circ_f32_B2_C128_64cube": dict(kind="nd", seed=5, B=2, X=64, Y=64, Z=64, C=128, N=2, circular=True),
     "nd3d_circ_f32_B1_C64_128cube": dict(kind="nd", seed=33, B=1, X=128, Y=128, Z=128, C=64, N=2,
                                          circular=True),
+    # non-causal (two-sided filters): the 64k workload's inputs
+    "order2_bf16_L64k_D768_noncausal": dict(kind="1d", seed=3, B=1, L=65536, D=768, N=2, K=16, dtype="bf16",
+                                            u_scale=1 / math.sqrt(768), causal=False),
     # 2D image grids (X = 1): 64 x 64 patch grids at a ViT-Small width, zero padded
     "nd2d_f32_B8_C384_64sq": dict(kind="nd", seed=34, B=8, X=1, Y=64, Z=64, C=384, N=2),
 }

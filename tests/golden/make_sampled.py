@@ -39,8 +39,12 @@ def make(name):
     out = os.path.join(HERE, f"sampled_{name}.npz")
     if cfg["kind"] == "1d":
         ts = sample_positions(inp.L, COUNT, seed=cfg["seed"])
-        h = oracle.implicit_filter(inp.filter_params, inp.L, inp.N, inp.D)
-        y = oracle.hyena_fwd_sampled(inp.u, inp.w_in, inp.short_w, inp.dskip, inp.w_out, h, ts, chunk=16)
+        if inp.causal:
+            h = oracle.implicit_filter(inp.filter_params, inp.L, inp.N, inp.D)
+        else:
+            h = oracle.implicit_filter_noncausal(inp.filter_params, inp.L, inp.N, inp.D)
+        y = oracle.hyena_fwd_sampled(inp.u, inp.w_in, inp.short_w, inp.dskip, inp.w_out, h, ts, chunk=16,
+                                     causal=inp.causal)
         np.savez(out, t=ts, y=y)
     else:
         pts = points_3d(inp.X, inp.Y, inp.Z, COUNT, cfg["seed"])

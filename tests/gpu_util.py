@@ -35,8 +35,10 @@ def gpu_1d(inp, with_h: bool = False, layer=None):
     import subquadratic_sequence_amd as hs
     dt = torch.bfloat16 if inp.dtype == "bf16" else torch.float32
     if layer is None:
-        layer = hs.HyenaLayer(inp.L, inp.D, inp.N)
-    h_out = torch.empty(inp.N, inp.D, inp.L, device="cuda") if with_h else None
+        layer = hs.HyenaLayer(inp.L, inp.D, inp.N, direction=hs.CAUSAL if inp.causal else hs.NONCAUSAL)
+    # non-causal filters come back wrapped: [N][D][2L], lag tau at tau mod 2L
+    h_len = inp.L if inp.causal else 2 * inp.L
+    h_out = torch.empty(inp.N, inp.D, h_len, device="cuda") if with_h else None
     hs.hyena_filter_gen(layer, to_dev(inp.w1), to_dev(inp.b1), to_dev(inp.w2), to_dev(inp.b2), to_dev(inp.w3),
                         to_dev(inp.b3), to_dev(inp.decay), inp.K, h_out=h_out)
     y = hs.hyena_fwd(layer, to_dev(inp.u, dt), to_dev(inp.w_in, dt), to_dev(inp.short_w), to_dev(inp.dskip),
@@ -49,10 +51,23 @@ def gpu_1d(inp, with_h: bool = False, layer=None):
 
 
 def oracle_1d(inp, conv: str = "auto"):
+    """(y, h): h [N, D, L] causal, [N, D, 2L - 1] lag-indexed (lag i - (L-1)) non-causal."""
     import oracle
-    h = oracle.implicit_filter(inp.filter_params, inp.L, inp.N, inp.D)
-    y = oracle.hyena_fwd(inp.u, inp.w_in, inp.short_w, inp.dskip, inp.w_out, h, conv=conv)
+    if inp.causal:
+        h = oracle.implicit_filter(inp.filter_params, inp.L, inp.N, inp.D)
+    else:
+        h = oracle.implicit_filter_noncausal(inp.filter_params, inp.L, inp.N, inp.D)
+    y = oracle.hyena_fwd(inp.u, inp.w_in, inp.short_w, inp.dskip, inp.w_out, h, conv=conv, causal=inp.causal)
     return y, h
+
+
+def wrap_two_sided(h2):
+    """Lag-indexed [..., 2L-1] -> the wrapped [..., 2L] layout of the library's h_out."""
+    L = (h2.shape[-1] + 1) // 2
+    hw = np.zeros(h2.shape[:-1] + (2 * L,))
+    hw[..., :L] = h2[..., L - 1:]
+    hw[..., L + 1:] = h2[..., :L - 1]
+    return hw
 
 
 def gpu_nd(inp, with_k: bool = False):

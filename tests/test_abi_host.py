@@ -203,3 +203,28 @@ def test_nd_layer_init_ex(hy):
     # a boundary changed behind the library's back is refused
     nd.boundary = 5
     assert L.hyena_nd_fwd(ctypes.byref(nd), p, p, p, p, p, p, 1, p, p, need, None) == 2
+
+
+# ------------------------------------------------------------ 1D direction
+
+def test_direction_sizes_and_init(hy):
+    L = hy.lib()
+    assert hy.hyena_filter_workspace_bytes_ex(1024, 64, 2, hy.CAUSAL) == hy.hyena_filter_workspace_bytes(1024, 64, 2)
+    al = lambda x: (x + 255) // 256 * 256  # noqa: E731
+    # LDS regime: only the filter buffer, twice as long for two-sided filters
+    assert hy.hyena_filter_workspace_bytes_ex(1024, 64, 2, hy.NONCAUSAL) == al(2 * 64 * 2048 * 4)
+    assert hy.hyena_filter_workspace_bytes_ex(1024, 64, 2, 2) == 0
+    keep, p = _aligned_buffer(16)
+    layer = hy.Layer()
+    layer.direction = 9
+    assert L.hyena_layer_init(ctypes.byref(layer), 1024, 64, 2, p, 1 << 30) == 0
+    assert layer.direction == hy.CAUSAL
+    assert L.hyena_layer_init_ex(ctypes.byref(layer), 1024, 64, 2, 3, p, 1 << 30) == 2
+    assert L.hyena_layer_init_ex(ctypes.byref(layer), 1024, 64, 2, hy.NONCAUSAL, p, 1 << 30) == 0
+    assert layer.direction == hy.NONCAUSAL
+    # filter generation checks the workspace against the layer's direction, and its direction
+    fp = hy.FilterParams(8, 64, p, p, p, p, p, p, p)
+    need = hy.hyena_filter_workspace_bytes_ex(1024, 64, 2, hy.NONCAUSAL)
+    assert L.hyena_filter_gen(ctypes.byref(layer), ctypes.byref(fp), None, p, need - 1, None) == 3
+    layer.direction = 4
+    assert L.hyena_filter_gen(ctypes.byref(layer), ctypes.byref(fp), None, p, need, None) == 2

@@ -118,3 +118,40 @@ def test_deterministic():
     y0 = gpu_1d(inp)
     y1 = gpu_1d(inp)
     assert np.array_equal(y0, y1)
+
+
+# ------------------------------------------------------------ non-causal 1D
+
+@pytest.mark.parametrize("L,K,W", [(1024, 8, 64), (16, 32, 128), (8192, 16, 64)])
+def test_noncausal_filter_matches_oracle(L, K, W):
+    from tests.gpu_util import wrap_two_sided
+    inp = make_1d(13 + L, 1, L, 64, N=2, K=K, W=W, causal=False)
+    say(f"non-causal filter L={L} D=64 N=2 K={K} W={W}")
+    _, h = gpu_1d(inp, with_h=True)
+    _, href = oracle_1d(inp)
+    assert h.shape == (2, 64, 2 * L)
+    assert rel_err(h, wrap_two_sided(href)) < 1e-5
+
+
+NONCAUSAL = [
+    (1, 16, 64, 2, "f32"), (2, 64, 64, 2, "f32"), (2, 1024, 128, 2, "f32"), (1, 4096, 64, 3, "f32"),
+    (2, 2048, 128, 2, "bf16"),
+    # four-step regime
+    (1, 8192, 64, 2, "f32"), (2, 16384, 64, 1, "bf16"), (1, 65536, 64, 2, "f32"),
+]
+
+
+@pytest.mark.parametrize("B,L,D,N,dt", NONCAUSAL)
+def test_noncausal_sweep(B, L, D, N, dt):
+    _check(make_1d(700 + L + D + N + B, B, L, D, N=N, K=8, dtype=dt, causal=False))
+
+
+def test_noncausal_future_reaches_past_on_gpu():
+    inp = make_1d(35, 1, 1024, 64, N=2, K=8, causal=False)
+    y0 = gpu_1d(inp)
+    t0 = 700
+    inp.u = inp.u.copy()
+    inp.u[:, t0] += 5.0
+    y1 = gpu_1d(inp)
+    scale = np.max(np.abs(y0))
+    assert np.max(np.abs(y1[:, :t0 - 2] - y0[:, :t0 - 2])) > 1e-3 * scale

@@ -24,7 +24,7 @@ def _golden(name):
 
 
 @pytest.mark.parametrize("name", ["order2_bf16_L64k_D768", "order2_bf16_L1M_D256_dna", "order2_bf16_L256k_D64",
-                                  "order2_f32_L512k_D64"])
+                                  "order2_f32_L512k_D64", "order2_bf16_L64k_D768_noncausal"])
 def test_full_size_1d_sampled(name):
     g = _golden(name)
     inp = make_config(name)
