@@ -399,10 +399,11 @@ __global__ __launch_bounds__(1024) void nd_plane_kernel(NdConvArgs a) {
 
 // Persistent plane pass for M = 128 (the 64^3 grids): items (sample pair,
 // channel, x-plane) walked with a stride of gridDim.x, one 1024-thread
-// workgroup per CU (the padded plane takes 133 KB of LDS). The next item's
-// input (its intermediate plane, or its v block in the first forward) is
-// fetched into registers while the current one is transformed, and the gate
-// and skip inputs between the column and the row stages of the inverse.
+// workgroup per CU (the padded plane takes 133 KB of LDS). In the first forward
+// the next item's v block is fetched into registers while the current one is
+// transformed; the inverse passes fetch their plane when the item starts and
+// the gate and skip inputs during (or, fused with the next forward, after) the
+// inverse row stage.
 template <int MODE>
 __global__ __launch_bounds__(1024) void nd_plane128_kernel(NdConvArgs a, int nitems) {
   constexpr int M = 128;
@@ -410,6 +411,12 @@ __global__ __launch_bounds__(1024) void nd_plane128_kernel(NdConvArgs a, int nit
   constexpr int PER = M * M / C::THREADS;          // plane elements per thread (16)
   constexpr int KEPT = M * M / 4 / C::THREADS;     // kept (y < Y, z < Z) positions per thread (4)
   constexpr bool INV = MODE != PL_FWD_V;
+  // The first forward fetches the next item's v block during the current item.
+  // The inverse modes fetch their intermediate plane when the item starts:
+  // holding 16 complex values of prefetch through the transforms spills at 128
+  // registers, and the spill traffic (about 0.8 GB per pass at 64^3) costs more
+  // than the exposed load.
+  constexpr bool PREF = MODE == PL_FWD_V;
   extern __shared__ float4 smem4[];
   float2* P = reinterpret_cast<float2*>(smem4);
   float2* tw = P + M * C::RS;
@@ -461,13 +468,14 @@ __global__ __launch_bounds__(1024) void nd_plane128_kernel(NdConvArgs a, int nit
   int item = blockIdx.x;
   if (item >= nitems) return;
   In in;
-  load_in(item_of(item), in);
+  if (PREF) load_in(item_of(item), in);
   while (true) {
     const int next = item + gridDim.x;
     const bool more = next < nitems;
     const Item it = item_of(item);
     float2* Yp = a.Yint + (((size_t)it.bp * CC + it.c) * X + it.x) * plane;
     const size_t xoff = (size_t)it.x * Y * Z;
+    if (!PREF) load_in(it, in);
     if constexpr (INV) {
 #pragma unroll
       for (int k = 0; k < PER; ++k) {
@@ -486,7 +494,7 @@ __global__ __launch_bounds__(1024) void nd_plane128_kernel(NdConvArgs a, int nit
     // the next item's input (the last item fetches itself again); in the fused
     // inverse + forward mode only after the gate, which keeps the inverse stages
     // free of the prefetch registers
-    if (MODE != PL_INV_FWD) load_in(item_of(more ? next : item), in);
+    if (PREF && MODE != PL_INV_FWD) load_in(item_of(more ? next : item), in);
     if constexpr (INV) {
       // gate and skip inputs of the kept block, needed after the inverse transform
       const int n = a.n;
@@ -498,15 +506,22 @@ __global__ __launch_bounds__(1024) void nd_plane128_kernel(NdConvArgs a, int nit
                                  : a.zin + ((size_t)it.b1 * CC + it.c) * V + xoff;
       __syncthreads();
       plane_cols<M, true>(P, tw);
+      // gate inputs: fetched during the inverse row stage, or, in the fused
+      // inverse + forward mode (more live registers), after it
+      constexpr bool GLATE = MODE == PL_INV_FWD;
       float gx0[KEPT], gx1[KEPT], gz0[KEPT], gz1[KEPT];
+      auto load_gate = [&]() {
 #pragma unroll
-      for (int k = 0; k < KEPT; ++k) {
-        gx0[k] = x0[kept(k)];
-        gx1[k] = x1[kept(k)];
-        gz0[k] = z0[kept(k)];
-        gz1[k] = z1[kept(k)];
-      }
+        for (int k = 0; k < KEPT; ++k) {
+          gx0[k] = x0[kept(k)];
+          gx1[k] = x1[kept(k)];
+          gz0[k] = z0[kept(k)];
+          gz1[k] = z1[kept(k)];
+        }
+      };
+      if (!GLATE) load_gate();
       plane_rows<M, true>(P, Y, tw);
+      if (GLATE) load_gate();
       float* o0 = a.zout + ((size_t)it.b0 * CC + it.c) * V + xoff;
       float* o1 = a.zout + ((size_t)it.b1 * CC + it.c) * V + xoff;
       const float g0 = a.gate[((size_t)it.b0 * a.NO + n) * CC + it.c];
@@ -534,7 +549,7 @@ __global__ __launch_bounds__(1024) void nd_plane128_kernel(NdConvArgs a, int nit
         for (int i = tid; i < Y * (M - Z); i += C::THREADS) P[(i / (M - Z)) * C::RS + Z + i % (M - Z)] = make_float2(0.f, 0.f);
       }
     }
-    if (MODE == PL_INV_FWD) load_in(item_of(more ? next : item), in);
+    if (PREF && MODE == PL_INV_FWD) load_in(item_of(more ? next : item), in);
     if (MODE != PL_INV) {
       __syncthreads();
       // forward plane DFT of the (zero padded) Y x Z block
