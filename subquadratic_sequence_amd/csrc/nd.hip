@@ -781,17 +781,31 @@ __global__ __launch_bounds__(256) void nd_mean_partial_kernel(const float* __res
   }
 }
 
-__global__ void nd_gate_kernel(const float* __restrict__ part, const float* __restrict__ ga,
-                               const float* __restrict__ gb, float* __restrict__ gate, int B, int NO, int C,
-                               int nch, int V) {
-  const int idx = blockIdx.x * blockDim.x + threadIdx.x;
-  if (idx >= B * NO * C) return;
-  const int c = idx % C, n = (idx / C) % NO, b = idx / (C * NO);
-  float s = 0.f;
-  for (int k = 0; k < nch; ++k) s += part[((size_t)b * nch + k) * C + c];
-  const float m = s / (float)V;
-  const float arg = ga[n * C + c] * m + gb[n * C + c];
-  gate[idx] = 1.f / (1.f + expf(-arg));
+// Means and gates for any C (a multiple of 64): one workgroup per (sample,
+// block of 64 channels); four groups of 64 threads sum interleaved partial rows
+// with independent accumulators, combined in LDS.
+__global__ __launch_bounds__(256) void nd_gate_kernel(const float* __restrict__ part, const float* __restrict__ ga,
+                                                      const float* __restrict__ gb, float* __restrict__ gate, int NO,
+                                                      int C, int nch, int V) {
+  __shared__ float red[256];
+  const int t = threadIdx.x, b = blockIdx.y;
+  const int c = blockIdx.x * 64 + (t & 63), g = t >> 6;
+  float acc[4] = {0.f, 0.f, 0.f, 0.f};
+  int k = g;
+  for (; k + 12 < nch; k += 16) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) acc[j] += part[((size_t)b * nch + k + 4 * j) * C + c];
+  }
+  for (; k < nch; k += 4) acc[0] += part[((size_t)b * nch + k) * C + c];
+  red[t] = (acc[0] + acc[1]) + (acc[2] + acc[3]);
+  __syncthreads();
+  if (t < 64) {
+    const float m = ((red[t] + red[t + 64]) + (red[t + 128] + red[t + 192])) / (float)V;
+    for (int n = 0; n < NO; ++n) {
+      const float arg = ga[n * C + c] * m + gb[n * C + c];
+      gate[((size_t)b * NO + n) * C + c] = 1.f / (1.f + expf(-arg));
+    }
+  }
 }
 
 // Faster forms for C dividing 256 (C = 64, 128, 256): a voxel chunk of the
@@ -1087,9 +1101,8 @@ hipError_t nd_gate(const float* u, float* part, const float* ga, const float* gb
   hipLaunchKernelGGL(nd_mean_partial_kernel, dim3(nch, B), dim3(256), 0, s, u, part, C, V, V / nch);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  const int tot = B * NO * C;
-  hipLaunchKernelGGL(nd_gate_kernel, dim3((tot + 255) / 256), dim3(256), 0, s, (const float*)part, ga, gb, gate, B,
-                     NO, C, nch, V);
+  hipLaunchKernelGGL(nd_gate_kernel, dim3(C / 64, B), dim3(256), 0, s, (const float*)part, ga, gb, gate, NO, C, nch,
+                     V);
   return hipGetLastError();
 }
 

@@ -37,6 +37,7 @@ def test_nd_filter_matches_oracle():
     (2, 8, 16, 128, 3, 0.5),
     (2, 16, 16, 64, 2, 0.5),
     (2, 32, 32, 64, 1, 0.5),
+    (2, 8, 8, 192, 2, 0.5),    # C not dividing 256: the general mean / gate kernels
 ])
 def test_nd_sweep(B, X, Y, C, N, spread):
     _check(make_nd(200 + B + X + Y + C + N, B, X, Y, Y, C, N=N, W=64, u_mean_spread=spread))
@@ -126,6 +127,7 @@ def test_nd_2d_filter_matches_oracle():
     (2, 32, 64, 2, True),
     (3, 64, 64, 2, True),
     (2, 128, 64, 2, True),     # 128-point circular planes
+    (3, 16, 384, 2, False),    # C = 384 (general gate kernels)
 ])
 def test_nd_2d_sweep(B, Y, C, N, circ):
     _check(make_nd(500 + B + Y + C + N + 7 * circ, B, 1, Y, Y, C, N=N, W=64, u_mean_spread=0.5, circular=circ))
