@@ -288,7 +288,9 @@ template <int M> struct PlaneCfg {
   static constexpr int E = M >= 16 ? 16 : M;
   static constexpr int T = M / E;       // threads per line
   static constexpr int RS = M + 1;      // LDS row stride
-  static constexpr int THREADS = 1024;
+  // every thread owns part of a line in the line stages (at least one wave)
+  static constexpr int THREADS = M * T < 64 ? 64 : M * T;
+  static constexpr int PER = M * M / THREADS;  // plane elements per thread
   static constexpr size_t LDS = (size_t)M * RS * 8 + 128 * 8;  // plane + W_128 table
 };
 
@@ -309,9 +311,12 @@ __device__ __forceinline__ void plane_cols(float2* P, const float2* tw) {
   LineFrom<M, C::E, 1, INV>::run(P, line, C::RS, lt, active, tw);
 }
 
+// Plane element loops run a fixed count per thread (element tid + k THREADS),
+// unrolled, so that all of a thread's loads are in flight together.
 template <int M, int MODE>
-__global__ __launch_bounds__(1024) void nd_plane_kernel(NdConvArgs a) {
+__global__ __launch_bounds__(PlaneCfg<M>::THREADS) void nd_plane_kernel(NdConvArgs a) {
   using C = PlaneCfg<M>;
+  constexpr int PER = C::PER;
   extern __shared__ float4 smem4[];
   float2* P = reinterpret_cast<float2*>(smem4);
   float2* tw = P + M * C::RS;  // W_128^m, m < 128
@@ -322,16 +327,23 @@ __global__ __launch_bounds__(1024) void nd_plane_kernel(NdConvArgs a) {
   const int c = blockIdx.y;          // channel (or filter pair)
   const int bp = blockIdx.z;         // sample pair (or order of the filter)
   const int tid = threadIdx.x;
-  if (tid < 128) tw[tid] = a.tw128[tid];  // visible after the barrier that follows the plane load
+  for (int i = tid; i < 128; i += C::THREADS) tw[i] = a.tw128[i];  // visible after the next barrier
+  auto el = [&](int k) { return tid + k * C::THREADS; };           // this thread's k-th element
+  auto lds = [&](int i) { return (i / M) * C::RS + i % M; };
 
   if constexpr (MODE == PL_FWD_FULL) {
     // filter: full M x M complex plane, all MX planes
     float2* Fp = a.F + (((size_t)bp * a.npairs + c) * a.MX + x) * plane;
-    for (int i = tid; i < M * M; i += C::THREADS) P[(i / M) * C::RS + i % M] = Fp[i];
+    float2 t[PER];
+#pragma unroll
+    for (int k = 0; k < PER; ++k) t[k] = Fp[el(k)];
+#pragma unroll
+    for (int k = 0; k < PER; ++k) P[lds(el(k))] = t[k];
     __syncthreads();
     plane_rows<M, false>(P, M, tw);
     plane_cols<M, false>(P, tw);
-    for (int i = tid; i < M * M; i += C::THREADS) Fp[i] = P[(i / M) * C::RS + i % M];
+#pragma unroll
+    for (int k = 0; k < PER; ++k) Fp[el(k)] = P[lds(el(k))];
     return;
   }
 
@@ -347,15 +359,24 @@ __global__ __launch_bounds__(1024) void nd_plane_kernel(NdConvArgs a) {
   if constexpr (MODE == PL_FWD_V) {
     const float* v0 = s0 + (size_t)c * V + xoff;
     const float* v1 = s1 + (size_t)c * V + xoff;
-    for (int i = tid; i < M * M; i += C::THREADS) {
-      const int y = i / M, z = i % M;
-      float2 val = make_float2(0.f, 0.f);
-      if (y < Y && z < Z) val = make_float2(v0[y * Z + z], has_b1 ? v1[y * Z + z] : 0.f);
-      P[y * C::RS + z] = val;
+    float2 t[PER];
+#pragma unroll
+    for (int k = 0; k < PER; ++k) {
+      const int y = el(k) / M, z = el(k) % M;
+      t[k] = make_float2(0.f, 0.f);
+      if (y < Y && z < Z) t[k] = make_float2(v0[y * Z + z], has_b1 ? v1[y * Z + z] : 0.f);
     }
+#pragma unroll
+    for (int k = 0; k < PER; ++k) P[lds(el(k))] = t[k];
     __syncthreads();
   } else {
-    for (int i = tid; i < M * M; i += C::THREADS) P[(i / M) * C::RS + i % M] = Yp[i];
+    {
+      float2 t[PER];
+#pragma unroll
+      for (int k = 0; k < PER; ++k) t[k] = Yp[el(k)];
+#pragma unroll
+      for (int k = 0; k < PER; ++k) P[lds(el(k))] = t[k];
+    }
     __syncthreads();
     plane_cols<M, true>(P, tw);
     plane_rows<M, true>(P, Y, tw);
@@ -371,17 +392,38 @@ __global__ __launch_bounds__(1024) void nd_plane_kernel(NdConvArgs a) {
     const float g0 = a.gate[((size_t)b0 * a.NO + n) * CC + c];
     const float g1 = has_b1 ? a.gate[((size_t)b1 * a.NO + n) * CC + c] : 0.f;
     const float dk = a.dskip[n * CC + c];
-    for (int i = tid; i < M * M; i += C::THREADS) {
-      const int y = i / M, z = i % M;
+    // gate and skip inputs of this thread's kept elements: all loads first
+    // where the registers allow it (up to 256 threads: 256 registers each),
+    // else element by element
+    constexpr bool BATCH = C::THREADS <= 256;
+    constexpr int NB = BATCH ? PER : 1;
+    float gx0[NB], gx1[NB], gz0[NB], gz1[NB];
+    auto gate_in = [&](int k, int j) {
+      const int y = el(k) / M, z = el(k) % M;
+      const int q = (y < Y && z < Z) ? y * Z + z : 0;
+      gx0[j] = x0[q];
+      gz0[j] = z0[q];
+      gx1[j] = x1[q];
+      gz1[j] = z1[q];
+    };
+    if constexpr (BATCH) {
+#pragma unroll
+      for (int k = 0; k < PER; ++k) gate_in(k, k);
+    }
+#pragma unroll
+    for (int k = 0; k < PER; ++k) {
+      const int y = el(k) / M, z = el(k) % M;
+      const int j = BATCH ? k : 0;
+      if (!BATCH) gate_in(k, 0);
       float2 nv = make_float2(0.f, 0.f);
       if (y < Y && z < Z) {
         const int q = y * Z + z;
         const float2 cv = P[y * C::RS + z];
-        const float a0 = x0[q] * g0 * cv.x + dk * z0[q];
+        const float a0 = gx0[j] * g0 * cv.x + dk * gz0[j];
         o0[q] = a0;
         float a1 = 0.f;
         if (has_b1) {
-          a1 = x1[q] * g1 * cv.y + dk * z1[q];
+          a1 = gx1[j] * g1 * cv.y + dk * gz1[j];
           o1[q] = a1;
         }
         nv = make_float2(a0, a1);
@@ -394,7 +436,8 @@ __global__ __launch_bounds__(1024) void nd_plane_kernel(NdConvArgs a) {
   // forward plane DFT of the (zero padded) Y x Z block
   plane_rows<M, false>(P, Y, tw);
   plane_cols<M, false>(P, tw);
-  for (int i = tid; i < M * M; i += C::THREADS) Yp[i] = P[(i / M) * C::RS + i % M];
+#pragma unroll
+  for (int k = 0; k < PER; ++k) Yp[el(k)] = P[lds(el(k))];
 }
 
 // Persistent plane pass for M = 128 (the 64^3 grids): items (sample pair,
@@ -872,10 +915,8 @@ __global__ __launch_bounds__(256) void nd_gate256_kernel(const float* __restrict
 // workgroups of one XCD (blockIdx mod 8) take consecutive items: the pairs of
 // a channel read its spectrum through that XCD's L2.
 template <int M> struct Plane2dCfg {
-  static constexpr int E = PlaneCfg<M>::E;
-  static constexpr int LINE_THREADS = M * (M / E);  // every thread owns part of a line
-  static constexpr int THREADS = LINE_THREADS < 64 ? 64 : LINE_THREADS;
-  static constexpr int PER = M * M / THREADS;        // plane elements per thread
+  static constexpr int THREADS = PlaneCfg<M>::THREADS;
+  static constexpr int PER = PlaneCfg<M>::PER;  // plane elements per thread
 };
 
 template <int M, bool CIRC>
