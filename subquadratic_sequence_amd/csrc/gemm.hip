@@ -14,7 +14,9 @@
 //    rows: a tile computes rows [m0 - 8, m0 + 248) and writes [m0, m0 + 248), so
 //    the two previous rows of every written row are on chip.
 // Block tile 256 x 256, eight waves of 128 x 64 (8 accumulators of 32 x 32 per
-// wave, two waves per SIMD), K step of 64 bytes per row. Three LDS tile
+// wave, two waves per SIMD), K step of 64 bytes per row; for N that 256 does
+// not divide (the 3D projections: N = 3C, C) a 256 x 128 tile of eight waves of
+// 64 x 64 wastes fewer MFMA columns. Three LDS tile
 // buffers: while a step multiplies tile kt it already reads the first MMA
 // fragments of tile kt + 1 (stored one step earlier) and stores tile kt + 2
 // from registers, so that no step starts by waiting for all eight waves' LDS
@@ -45,6 +47,14 @@ template <typename T> struct GemmCfg {
   static constexpr int CHUNKS = GBM * BK / VEC / 512;  // 16-byte chunks per thread per operand
 };
 
+// Wave layout of a GBM x TN block tile: TN / 64 wave columns of 64, the eight
+// waves' rows split GBM (128 rows per wave for TN = 256, 64 for TN = 128).
+template <int TN> struct WaveCfg {
+  static constexpr int WCOLS = TN / 64;
+  static constexpr int WR = GBM * WCOLS / 8;  // rows per wave
+  static constexpr int MI = WR / 32;          // 32-row accumulator blocks per wave
+};
+
 constexpr int kCsLd = GBM + 4;  // staging row (floats), channel-major output: [64 n][256 m]
 constexpr int kRmLd = 64 + 4;   // staging row (floats), row-major output: [256 m][64 n]
 constexpr int kBufs = 3;                                 // LDS tile buffers
@@ -64,33 +74,36 @@ __device__ __forceinline__ int xcd_tile(int bid, int total) {
   return x < r ? x * (q + 1) + k : r * (q + 1) + (x - r) * q + k;
 }
 
-template <typename T, bool A_CM, bool C_CM, bool SC>
+template <typename T, bool A_CM, bool C_CM, bool SC, int TN = GBN>
 __global__ __launch_bounds__(512, 1) void gemm_kernel(const T* __restrict__ A, const T* __restrict__ Bt,
                                                       T* __restrict__ C, int M, int N, int K, int Lseq,
                                                       const float* __restrict__ short_w, int ntn, int ntiles) {
   using Cfg = GemmCfg<T>;
+  using WC = WaveCfg<TN>;
   constexpr int BK = Cfg::BK, LDK = Cfg::LDK, VEC = Cfg::VEC, NCH = Cfg::CHUNKS;
+  constexpr int NCHB = NCH * TN / GBN;  // 16-byte chunks per thread of the B tile
+  constexpr int MI = WC::MI;
   extern __shared__ float4 smem4[];
   char* smem = reinterpret_cast<char*>(smem4);
   T* As0 = reinterpret_cast<T*>(smem);  // [kBufs][GBM][LDK] then Bs [kBufs][GBN][LDK]
   T* Bs0 = As0 + kBufs * Cfg::TILE;
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int wm = wave >> 2, wn = wave & 3;  // 2 x 4 waves of 128 x 64
+  const int wm = wave / WC::WCOLS, wn = wave % WC::WCOLS;  // waves of WR x 64
   const int tile = xcd_tile(blockIdx.x, ntiles);
   const int tm = tile / ntn, tn = tile - tm * ntn;
-  const int n0 = tn * GBN;
+  const int n0 = tn * TN;
   const int m0 = SC ? tm * kScRows - 8 : tm * GBM;  // first A row of the tile
 
   // short-conv taps of this tile's columns, staged once (read by the epilogue)
   float* sw = reinterpret_cast<float*>(smem + kGemmMain);
   if (SC) {
-    for (int x = tid; x < GBN * 3; x += 512) sw[x] = (n0 * 3 + x < N * 3) ? short_w[n0 * 3 + x] : 0.f;
+    for (int x = tid; x < TN * 3; x += 512) sw[x] = (n0 * 3 + x < N * 3) ? short_w[n0 * 3 + x] : 0.f;
   }
 
-  f32x16 acc[4][2];
+  f32x16 acc[MI][2];
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
+  for (int i = 0; i < MI; ++i)
 #pragma unroll
     for (int j = 0; j < 2; ++j)
 #pragma unroll
@@ -129,9 +142,11 @@ __global__ __launch_bounds__(512, 1) void gemm_kernel(const T* __restrict__ A, c
       pa[i] = A + ((size_t)b * K + k) * Lseq + t;
       la[i] = mc * LDK + (k & ~1);
     }
-    const int n = n0 + row;
-    pb[i] = Bt + (size_t)(n < N ? n : 0) * K + kc;  // columns >= N are not stored
-    lb[i] = row * LDK + kc;
+    if (i < NCHB) {
+      const int n = n0 + row;
+      pb[i] = Bt + (size_t)(n < N ? n : 0) * K + kc;  // columns >= N are not stored
+      lb[i] = row * LDK + kc;
+    }
   }
   a_step = A_CM ? (size_t)BK * Lseq : (size_t)BK;
 
@@ -146,9 +161,11 @@ __global__ __launch_bounds__(512, 1) void gemm_kernel(const T* __restrict__ A, c
 #pragma unroll
     for (int i = 0; i < NCH; ++i) {
       ra[i] = *reinterpret_cast<const u32x4*>(pa[i]);
-      rb[i] = *reinterpret_cast<const u32x4*>(pb[i]);
       pa[i] += tiles_left > 1 ? a_step : 0;
-      pb[i] += tiles_left > 1 ? BK : 0;
+      if (i < NCHB) {
+        rb[i] = *reinterpret_cast<const u32x4*>(pb[i]);
+        pb[i] += tiles_left > 1 ? BK : 0;
+      }
     }
     --tiles_left;
   };
@@ -182,37 +199,37 @@ __global__ __launch_bounds__(512, 1) void gemm_kernel(const T* __restrict__ A, c
                 make_float2(__uint_as_float(ra[i][q]), __uint_as_float(ra[i + 1][q]));
         }
       }
-      *reinterpret_cast<u32x4*>(Bs + lb[i]) = rb[i];
+      if (i < NCHB) *reinterpret_cast<u32x4*>(Bs + lb[i]) = rb[i];
     }
   };
 
-  // MMA fragments of one 16 (bf16) or 2 (fp32) wide K slice: 4 of A, 2 of B
+  // MMA fragments of one 16 (bf16) or 2 (fp32) wide K slice: MI of A, 2 of B
   using FragT = std::conditional_t<sizeof(T) == 2, bf16x8, float>;
   struct Frag {
-    FragT a[4], b[2];
+    FragT a[MI], b[2];
   };
-  const int ar = wm * 128 + (lane & 31), br = wn * 64 + (lane & 31);
+  const int ar = wm * WC::WR + (lane & 31), br = wn * 64 + (lane & 31);
   constexpr int KS = sizeof(T) == 2 ? 16 : 2;  // K per MMA
   auto read_frag = [&](Frag& f, int buf, int kk) {
     const T* As = As0 + buf * Cfg::TILE;
     const T* Bs = Bs0 + buf * Cfg::TILE;
     if constexpr (sizeof(T) == 2) {
 #pragma unroll
-      for (int i = 0; i < 4; ++i)
+      for (int i = 0; i < MI; ++i)
         f.a[i] = *reinterpret_cast<const bf16x8*>(As + (ar + i * 32) * LDK + kk + (lane >> 5) * 8);
 #pragma unroll
       for (int j = 0; j < 2; ++j)
         f.b[j] = *reinterpret_cast<const bf16x8*>(Bs + (br + j * 32) * LDK + kk + (lane >> 5) * 8);
     } else {
 #pragma unroll
-      for (int i = 0; i < 4; ++i) f.a[i] = As[(ar + i * 32) * LDK + kk + (lane >> 5)];
+      for (int i = 0; i < MI; ++i) f.a[i] = As[(ar + i * 32) * LDK + kk + (lane >> 5)];
 #pragma unroll
       for (int j = 0; j < 2; ++j) f.b[j] = Bs[(br + j * 32) * LDK + kk + (lane >> 5)];
     }
   };
   auto mma = [&](const Frag& f) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
+    for (int i = 0; i < MI; ++i)
 #pragma unroll
       for (int j = 0; j < 2; ++j) {
         if constexpr (sizeof(T) == 2)
@@ -272,19 +289,19 @@ __global__ __launch_bounds__(512, 1) void gemm_kernel(const T* __restrict__ A, c
 
   // Epilogue. Accumulator element e of lane l in block (i, j):
   //   row = i*32 + (e/4)*8 + (l/32)*4 + e%4, col = j*32 + l%32 (within the wave tile).
-  // Four rounds, one per 64-column quarter (the waves with wn == h hold it);
-  // the quarter is staged in LDS as fp32 and written with 16-byte stores.
+  // One round per 64-column slice (the waves with wn == h hold it); the slice
+  // is staged in LDS as fp32 and written with 16-byte stores.
   float* Cs = reinterpret_cast<float*>(smem);
 #pragma unroll
-  for (int h = 0; h < 4; ++h) {
+  for (int h = 0; h < WC::WCOLS; ++h) {
     if (wn == h) {
 #pragma unroll
-      for (int i = 0; i < 4; ++i)
+      for (int i = 0; i < MI; ++i)
 #pragma unroll
         for (int j = 0; j < 2; ++j)
 #pragma unroll
           for (int e4 = 0; e4 < 4; ++e4) {
-            const int ml = wm * 128 + i * 32 + e4 * 8 + (lane >> 5) * 4;
+            const int ml = wm * WC::WR + i * 32 + e4 * 8 + (lane >> 5) * 4;
             const int nl = j * 32 + (lane & 31);
             const float4 q = make_float4(acc[i][j][4 * e4], acc[i][j][4 * e4 + 1], acc[i][j][4 * e4 + 2],
                                          acc[i][j][4 * e4 + 3]);
@@ -364,12 +381,12 @@ __global__ __launch_bounds__(512, 1) void gemm_kernel(const T* __restrict__ A, c
   }
 }
 
-template <typename T>
+template <typename T, int TN>
 static hipError_t launch_gemm(const GemmArgs& g, hipStream_t s) {
   if (g.K <= 0 || g.K % GemmCfg<T>::BK != 0) return hipErrorInvalidValue;  // whole K tiles
   const bool sc = g.short_w != nullptr;
   const int mtiles = sc ? (g.M + kScRows - 1) / kScRows : (g.M + GBM - 1) / GBM;
-  const int ntn = (g.N + GBN - 1) / GBN;
+  const int ntn = (g.N + TN - 1) / TN;
   const int ntiles = ntn * mtiles;
   dim3 grid(ntiles), block(512);
   const T* A = static_cast<const T*>(g.A);
@@ -377,7 +394,7 @@ static hipError_t launch_gemm(const GemmArgs& g, hipStream_t s) {
   T* C = static_cast<T*>(g.C);
 #define GEMM_LAUNCH(acm, ccm, scv)                                                                    \
   do {                                                                                                \
-    auto fn = gemm_kernel<T, acm, ccm, scv>;                                                          \
+    auto fn = gemm_kernel<T, acm, ccm, scv, TN>;                                                      \
     hipError_t e = hipFuncSetAttribute((const void*)fn, hipFuncAttributeMaxDynamicSharedMemorySize,   \
                                        (int)kGemmLds);                                                \
     if (e != hipSuccess) return e;                                                                    \
@@ -400,8 +417,11 @@ static hipError_t launch_gemm(const GemmArgs& g, hipStream_t s) {
   return hipGetLastError();
 }
 
+// 256-wide tiles unless 128-wide ones leave fewer unused columns
 hipError_t gemm(const GemmArgs& g, bool bf16, hipStream_t s) {
-  return bf16 ? launch_gemm<__bf16>(g, s) : launch_gemm<float>(g, s);
+  const int pad256 = (g.N + 255) / 256 * 256 - g.N, pad128 = (g.N + 127) / 128 * 128 - g.N;
+  if (pad128 < pad256) return bf16 ? launch_gemm<__bf16, 128>(g, s) : launch_gemm<float, 128>(g, s);
+  return bf16 ? launch_gemm<__bf16, 256>(g, s) : launch_gemm<float, 256>(g, s);
 }
 
 // ------------------------------------------------------------- transpose
