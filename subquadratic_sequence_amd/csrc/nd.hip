@@ -534,10 +534,8 @@ __global__ __launch_bounds__(1024) void nd_plane128_kernel(NdConvArgs a, int nit
         P[y * C::RS + z] = make_float2(in.va[k], it.has_b1 ? in.vb[k] : 0.f);
       }
     }
-    // the next item's input (the last item fetches itself again); in the fused
-    // inverse + forward mode only after the gate, which keeps the inverse stages
-    // free of the prefetch registers
-    if (PREF && MODE != PL_INV_FWD) load_in(item_of(more ? next : item), in);
+    // the next item's v block (the last item fetches itself again)
+    if (PREF) load_in(item_of(more ? next : item), in);
     if constexpr (INV) {
       // gate and skip inputs of the kept block, needed after the inverse transform
       const int n = a.n;
@@ -592,7 +590,6 @@ __global__ __launch_bounds__(1024) void nd_plane128_kernel(NdConvArgs a, int nit
         for (int i = tid; i < Y * (M - Z); i += C::THREADS) P[(i / (M - Z)) * C::RS + Z + i % (M - Z)] = make_float2(0.f, 0.f);
       }
     }
-    if (PREF && MODE == PL_INV_FWD) load_in(item_of(more ? next : item), in);
     if (MODE != PL_INV) {
       __syncthreads();
       // forward plane DFT of the (zero padded) Y x Z block
