@@ -42,19 +42,21 @@ def test_fwd_profiled_matches_fwd(L, dt):
     _check_events(evs)
 
 
-def test_nd_fwd_profiled_matches_nd_fwd():
+@pytest.mark.parametrize("X,Y,circ", [(8, 8, False), (16, 16, True), (1, 32, False), (1, 32, True)])
+def test_nd_fwd_profiled_matches_nd_fwd(X, Y, circ):
     import torch
     import subquadratic_sequence_amd as hs
-    inp = make_nd(43, 2, 8, 8, 8, 64, N=2)
-    say("case profiled 3D B=2 8^3 C=64")
-    layer = hs.HyenaNDLayer(inp.X, inp.Y, inp.Z, inp.C, inp.N)
+    inp = make_nd(43 + X + Y, 2, X, Y, Y, 64, N=2, circular=circ)
+    say(f"case profiled ND B=2 grid {X}x{Y}x{Y} C=64 circular={circ}")
+    bd = hs.ND_CIRCULAR if circ else hs.ND_ZERO_PAD
+    layer = hs.HyenaNDLayer(inp.X, inp.Y, inp.Z, inp.C, inp.N, boundary=bd)
     hs.hyena_nd_filter_gen(layer, to_dev(inp.w1), to_dev(inp.b1), to_dev(inp.w2), to_dev(inp.b2), to_dev(inp.w3),
                            to_dev(inp.b3), to_dev(inp.decay))
     u, w_in, dskip, ga, gb, w_out = (to_dev(a) for a in (inp.u, inp.w_in, inp.dskip, inp.gate_a, inp.gate_b,
                                                           inp.w_out))
     y0 = hs.hyena_nd_fwd(layer, u, w_in, dskip, ga, gb, w_out)
     y1 = torch.empty_like(y0)
-    ws = torch.empty(hs.hyena_nd_workspace_bytes(inp.B, inp.X, inp.Y, inp.Z, inp.C, inp.N), dtype=torch.uint8,
+    ws = torch.empty(hs.hyena_nd_workspace_bytes_ex(inp.B, inp.X, inp.Y, inp.Z, inp.C, inp.N, bd), dtype=torch.uint8,
                      device="cuda")
     evs = _events(torch)
     hs.hyena_nd_fwd_profiled(layer, u, w_in, dskip, ga, gb, w_out, y1, ws, evs)
