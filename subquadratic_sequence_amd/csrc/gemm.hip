@@ -15,8 +15,9 @@
 //    the two previous rows of every written row are on chip.
 // Block tile 256 x 256, eight waves of 128 x 64 (8 accumulators of 32 x 32 per
 // wave, two waves per SIMD), K step of 64 bytes per row; for N that 256 does
-// not divide (the 3D projections: N = 3C, C) a 256 x 128 tile of eight waves of
-// 64 x 64 wastes fewer MFMA columns. Three LDS tile
+// not divide a 256 x 128 tile of eight waves of 64 x 64 wastes fewer MFMA
+// columns, and fp32 products with a short K use 256 x 64 tiles (eight waves of
+// 32 x 64, registers and LDS for two workgroups per CU). Three LDS tile
 // buffers: while a step multiplies tile kt it already reads the first MMA
 // fragments of tile kt + 1 (stored one step earlier) and stores tile kt + 2
 // from registers, so that no step starts by waiting for all eight waves' LDS
@@ -58,10 +59,13 @@ template <int TN> struct WaveCfg {
 constexpr int kCsLd = GBM + 4;  // staging row (floats), channel-major output: [64 n][256 m]
 constexpr int kRmLd = 64 + 4;   // staging row (floats), row-major output: [256 m][64 n]
 constexpr int kBufs = 3;                                 // LDS tile buffers
-constexpr size_t kTileBytes = kBufs * 2 * GBM * 80;  // A and B per buffer, 80-byte rows
 constexpr size_t kStageBytes = 64 * kCsLd * 4 > 256 * kRmLd * 4 ? 64 * kCsLd * 4 : 256 * kRmLd * 4;
-constexpr size_t kGemmMain = kTileBytes > kStageBytes ? kTileBytes : kStageBytes;
-constexpr size_t kGemmLds = kGemmMain + GBN * 3 * 4;  // + short-conv taps of the tile's columns
+// A (GBM rows) and B (TN rows) tiles per buffer, 80-byte rows; the epilogue
+// staging reuses the space; then the short-conv taps of the tile's columns
+constexpr size_t gemm_main_bytes(int TN) {
+  return (size_t)kBufs * (GBM + TN) * 80 > kStageBytes ? (size_t)kBufs * (GBM + TN) * 80 : kStageBytes;
+}
+constexpr size_t gemm_lds_bytes(int TN) { return gemm_main_bytes(TN) + (size_t)TN * 3 * 4; }
 
 constexpr int kXcds = 8;
 
@@ -75,17 +79,19 @@ __device__ __forceinline__ int xcd_tile(int bid, int total) {
 }
 
 template <typename T, bool A_CM, bool C_CM, bool SC, int TN = GBN>
-__global__ __launch_bounds__(512, 1) void gemm_kernel(const T* __restrict__ A, const T* __restrict__ Bt,
+__global__ __launch_bounds__(512, TN == 64 ? 4 : 1) void gemm_kernel(const T* __restrict__ A, const T* __restrict__ Bt,
                                                       T* __restrict__ C, int M, int N, int K, int Lseq,
                                                       const float* __restrict__ short_w, int ntn, int ntiles) {
   using Cfg = GemmCfg<T>;
   using WC = WaveCfg<TN>;
   constexpr int BK = Cfg::BK, LDK = Cfg::LDK, VEC = Cfg::VEC, NCH = Cfg::CHUNKS;
-  constexpr int NCHB = NCH * TN / GBN;  // 16-byte chunks per thread of the B tile
+  constexpr int BCH = TN * BK / VEC;             // 16-byte chunks of the B tile
+  constexpr int NCHB = (BCH + 511) / 512;        // per thread (the last partly when BCH < 512)
+  constexpr bool BPART = BCH % 512 != 0;
   constexpr int MI = WC::MI;
   extern __shared__ float4 smem4[];
   char* smem = reinterpret_cast<char*>(smem4);
-  T* As0 = reinterpret_cast<T*>(smem);  // [kBufs][GBM][LDK] then Bs [kBufs][GBN][LDK]
+  T* As0 = reinterpret_cast<T*>(smem);  // [kBufs][GBM][LDK] then Bs [kBufs][TN][LDK]
   T* Bs0 = As0 + kBufs * Cfg::TILE;
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -96,7 +102,7 @@ __global__ __launch_bounds__(512, 1) void gemm_kernel(const T* __restrict__ A, c
   const int m0 = SC ? tm * kScRows - 8 : tm * GBM;  // first A row of the tile
 
   // short-conv taps of this tile's columns, staged once (read by the epilogue)
-  float* sw = reinterpret_cast<float*>(smem + kGemmMain);
+  float* sw = reinterpret_cast<float*>(smem + gemm_main_bytes(TN));
   if (SC) {
     for (int x = tid; x < TN * 3; x += 512) sw[x] = (n0 * 3 + x < N * 3) ? short_w[n0 * 3 + x] : 0.f;
   }
@@ -143,7 +149,7 @@ __global__ __launch_bounds__(512, 1) void gemm_kernel(const T* __restrict__ A, c
       la[i] = mc * LDK + (k & ~1);
     }
     if (i < NCHB) {
-      const int n = n0 + row;
+      const int n = n0 + (BPART && c >= BCH ? 0 : row);
       pb[i] = Bt + (size_t)(n < N ? n : 0) * K + kc;  // columns >= N are not stored
       lb[i] = row * LDK + kc;
     }
@@ -175,7 +181,7 @@ __global__ __launch_bounds__(512, 1) void gemm_kernel(const T* __restrict__ A, c
     const u32x4* ra = ra2[sidx];
     const u32x4* rb = rb2[sidx];
     T* As = As0 + buf * Cfg::TILE;
-    T* Bs = Bs0 + buf * Cfg::TILE;
+    T* Bs = Bs0 + buf * (TN * LDK);
 #pragma unroll
     for (int i = 0; i < NCH; ++i) {
       if (!A_CM) {
@@ -199,7 +205,7 @@ __global__ __launch_bounds__(512, 1) void gemm_kernel(const T* __restrict__ A, c
                 make_float2(__uint_as_float(ra[i][q]), __uint_as_float(ra[i + 1][q]));
         }
       }
-      if (i < NCHB) *reinterpret_cast<u32x4*>(Bs + lb[i]) = rb[i];
+      if (i < NCHB && (!BPART || tid + i * 512 < BCH)) *reinterpret_cast<u32x4*>(Bs + lb[i]) = rb[i];
     }
   };
 
@@ -212,7 +218,7 @@ __global__ __launch_bounds__(512, 1) void gemm_kernel(const T* __restrict__ A, c
   constexpr int KS = sizeof(T) == 2 ? 16 : 2;  // K per MMA
   auto read_frag = [&](Frag& f, int buf, int kk) {
     const T* As = As0 + buf * Cfg::TILE;
-    const T* Bs = Bs0 + buf * Cfg::TILE;
+    const T* Bs = Bs0 + buf * (TN * LDK);
     if constexpr (sizeof(T) == 2) {
 #pragma unroll
       for (int i = 0; i < MI; ++i)
@@ -396,10 +402,10 @@ static hipError_t launch_gemm(const GemmArgs& g, hipStream_t s) {
   do {                                                                                                \
     auto fn = gemm_kernel<T, acm, ccm, scv, TN>;                                                      \
     hipError_t e = hipFuncSetAttribute((const void*)fn, hipFuncAttributeMaxDynamicSharedMemorySize,   \
-                                       (int)kGemmLds);                                                \
+                                       (int)gemm_lds_bytes(TN));                                      \
     if (e != hipSuccess) return e;                                                                    \
-    hipLaunchKernelGGL(fn, grid, block, kGemmLds, s, A, B, C, g.M, g.N, g.K, g.Lseq, g.short_w, ntn, \
-                       ntiles);                                                                       \
+    hipLaunchKernelGGL(fn, grid, block, gemm_lds_bytes(TN), s, A, B, C, g.M, g.N, g.K, g.Lseq,        \
+                       g.short_w, ntn, ntiles);                                                       \
   } while (0)
   if (sc) {
     if (!g.c_cm || g.a_cm) return hipErrorInvalidValue;
@@ -417,8 +423,12 @@ static hipError_t launch_gemm(const GemmArgs& g, hipStream_t s) {
   return hipGetLastError();
 }
 
-// 256-wide tiles unless 128-wide ones leave fewer unused columns
+// fp32 with a short K (the 3D and 2D projections, K = C): 256 x 64 tiles, two
+// workgroups per CU, so that one's epilogue (a large share of the time when K
+// is short) overlaps the other's K loop. Otherwise 256-wide tiles unless
+// 128-wide ones leave fewer unused columns.
 hipError_t gemm(const GemmArgs& g, bool bf16, hipStream_t s) {
+  if (!bf16 && g.K <= 512) return launch_gemm<float, 64>(g, s);
   const int pad256 = (g.N + 255) / 256 * 256 - g.N, pad128 = (g.N + 127) / 128 * 128 - g.N;
   if (pad128 < pad256) return bf16 ? launch_gemm<__bf16, 128>(g, s) : launch_gemm<float, 128>(g, s);
   return bf16 ? launch_gemm<__bf16, 256>(g, s) : launch_gemm<float, 256>(g, s);
