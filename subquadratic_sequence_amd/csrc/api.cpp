@@ -36,7 +36,7 @@ bool shape_ok(int L, int D, int N) {
 struct CacheLayout {
   bool lds;
   int N2, lo_bits;
-  size_t tw, w256, tw_lo, tw_hi, tw_row, pq, total;
+  size_t tw, w256, tw_lo, tw_hi, tw_row, pq, pq_bf16, total;
 };
 
 CacheLayout cache_layout(int L, int D, int N) {
@@ -60,8 +60,12 @@ CacheLayout cache_layout(int L, int D, int N) {
     off = align_up(off + (n >> c.lo_bits) * 8, kAlign);
     c.tw_row = off;
     off = align_up(off + (size_t)c.N2 * 8, kAlign);
+    // filter spectra: fp32 (P, Q) entries, then a bf16 copy for the bf16 row passes
+    const size_t entries = (size_t)N * (D / 2) * (hy::fourstep_n1(L) / 2 + 1) * c.N2;
     c.pq = off;
-    off = align_up(off + (size_t)N * (D / 2) * (hy::fourstep_n1(L) / 2 + 1) * c.N2 * 16, kAlign);
+    off = align_up(off + entries * 16, kAlign);
+    c.pq_bf16 = off;
+    off = align_up(off + entries * 8, kAlign);
   }
   c.total = off;
   return c;
@@ -133,8 +137,8 @@ int device_ok() {
 // Tuning knobs (read once): HYENA_GROUP_PAIRS = channel pairs per four-step
 // group (overrides HYENA_GROUP_MB); HYENA_GROUP_MB = bound on the four-step
 // intermediate of one group, in MB (0: all pairs in one group); 
-// HYENA_SPECTRUM_FP32 = 1 keeps the four-step intermediate in fp32 for bf16
-// workloads.
+// HYENA_SPECTRUM_FP32 = 1 keeps the four-step intermediate, and the filter
+// spectra the row passes read, in fp32 for bf16 workloads.
 struct Tuning {
   int group_pairs = 0;
   int group_mb = kGroupMB;
@@ -257,7 +261,8 @@ int hyena_filter_gen(hyena_layer* layer, const hyena_filter_params* p, float* h_
     HY_CHECK_HIP(hy::twiddles(reinterpret_cast<float2*>(cb + cl.tw_hi), n >> cl.lo_bits, n >> cl.lo_bits, stream));
     HY_CHECK_HIP(hy::twiddles(reinterpret_cast<float2*>(cb + cl.tw_row), cl.N2, cl.N2, stream));
     HY_CHECK_HIP(hy::fourstep_spec(tables(cl, layer->cache), h, reinterpret_cast<float2*>(wsb + fw.Y),
-                                   reinterpret_cast<float4*>(cb + cl.pq), L, D, N, two_sided, stream));
+                                   reinterpret_cast<float4*>(cb + cl.pq), cb + cl.pq_bf16, L, D, N, two_sided,
+                                   stream));
   }
   layer->built = 1;
   return HYENA_OK;
@@ -307,6 +312,7 @@ static int fwd_impl(const hyena_layer* layer, const void* u, const void* w_in, c
     a.s = pbuf;
     a.dskip = dskip;
     a.pq = reinterpret_cast<const float4*>(cb + cl.pq);
+    a.pq_bf16 = cb + cl.pq_bf16;
     a.z[0] = wsb + fw.z0;
     a.z[1] = wsb + fw.z1;
     a.zfinal = zfin;

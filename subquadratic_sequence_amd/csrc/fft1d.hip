@@ -455,6 +455,14 @@ enum { ROW_CONV = 0, ROW_SPEC = 1 };
 __device__ __forceinline__ float xhalf(float x, int sw) {
   return __int_as_float(__builtin_amdgcn_ds_bpermute(sw, __float_as_int(x)));
 }
+__device__ __forceinline__ unsigned xhalf(unsigned x, int sw) {
+  return (unsigned)__builtin_amdgcn_ds_bpermute(sw, (int)x);
+}
+// a spectrum entry of the lane 32 apart, exchanged in its stored form
+__device__ __forceinline__ float4 xhalf(const float4& x, int sw) {
+  return make_float4(xhalf(x.x, sw), xhalf(x.y, sw), xhalf(x.z, sw), xhalf(x.w, sw));
+}
+__device__ __forceinline__ pq16 xhalf(const pq16& x, int sw) { return pq16{xhalf(x.p, sw), xhalf(x.q, sw)}; }
 
 // Radix of the row DFT stage that starts at span Ns: the first stage takes the
 // factor left over by 16s (2048 = 8 * 16 * 16), the later stages, which need
@@ -589,10 +597,11 @@ template <int N, int E, int SI, int W, bool INV, bool ONE> struct RowFrom<N, E, 
 
 // Persistent row pass; items are (channel pair, group of SP slots).
 template <typename YT, int N1, int N2, int MODE, int PF>
-__global__ __launch_bounds__(RowCfg<N2>::WG) void rowpass_kernel(YT* __restrict__ Y, float4* __restrict__ pq,
+__global__ __launch_bounds__(RowCfg<N2>::WG) void rowpass_kernel(YT* __restrict__ Y, typename PqOf<YT>::type* __restrict__ pq,
                                                                  const float2* __restrict__ tw_row, int pq_off,
                                                                  int pair_off, int pq_mod, int nitems) {
   using C = RowCfg<N2>;
+  using PT = typename PqOf<YT>::type;
   constexpr int E = C::E, T = C::T;
   constexpr int HALF = N1 / 2;
   constexpr int PQROWS = HALF + 1;
@@ -638,7 +647,7 @@ __global__ __launch_bounds__(RowCfg<N2>::WG) void rowpass_kernel(YT* __restrict_
 #pragma unroll
     for (int q = 0; q < E; ++q) in.y[q] = Yr[l + q * T];
   };
-  float4 pr[E / 2];
+  PT pr[E / 2];
   // in 1024-thread workgroups (128 VGPRs) the spectrum entries are fetched
   // after the forward DFT, so that they do not share registers with it
   constexpr bool LATE_PQ = C::WG > 512 && !(PF & 2);
@@ -648,7 +657,7 @@ __global__ __launch_bounds__(RowCfg<N2>::WG) void rowpass_kernel(YT* __restrict_
       row_of(item, pl, sg, s);
       // slot 0 reads its spectrum rows in the LDS branch; load a valid row anyway
       // so that the number of loads in flight does not depend on the item
-      const float4* pqs = spectrum(pl, s == 0 ? 1 : s) + i;
+      const PT* pqs = spectrum(pl, s == 0 ? 1 : s) + i;
 #pragma unroll
       for (int e = 0; e < E / 2; ++e) pr[e] = pqs[(up ? E - 1 - e : e) * T];
     }
@@ -657,7 +666,7 @@ __global__ __launch_bounds__(RowCfg<N2>::WG) void rowpass_kernel(YT* __restrict_
   auto process = [&](int item, In& in, int next, bool more) {
     int pl, sg, s;
     const int k1 = row_of(item, pl, sg, s);
-    float4* pqp = spectrum(pl, 0);
+    PT* pqp = spectrum(pl, 0);
     float2 v[E];
 #pragma unroll
     for (int q = 0; q < E; ++q) v[q] = cvt2(in.y[q]);
@@ -676,9 +685,8 @@ __global__ __launch_bounds__(RowCfg<N2>::WG) void rowpass_kernel(YT* __restrict_
         const float2 pm = make_float2(xhalf(v[q2].x, sw32), xhalf(v[q2].y, sw32));
         const float2 pm2 = make_float2(xhalf(v[q].x, sw32), xhalf(v[q].y, sw32));
         if (MODE == ROW_CONV) {
-          const float4 o = make_float4(xhalf(pr[q].x, sw32), xhalf(pr[q].y, sw32), xhalf(pr[q].z, sw32),
-                                       xhalf(pr[q].w, sw32));
-          const float2 P = make_float2(pr[q].x, sg_ * pr[q].y), Q = make_float2(pr[q].z, sg_ * pr[q].w);
+          const float4 o = ldpq(xhalf(pr[q], sw32)), w = ldpq(pr[q]);
+          const float2 P = make_float2(w.x, sg_ * w.y), Q = make_float2(w.z, sg_ * w.w);
           const float2 P2 = make_float2(o.x, sg_ * o.y), Q2 = make_float2(o.z, sg_ * o.w);
           v[q] = cadd(cmul(v[q], P), cmul(conjf2(pm), Q));
           v[q2] = cadd(cmul(v[q2], P2), cmul(conjf2(pm2), Q2));
@@ -688,9 +696,9 @@ __global__ __launch_bounds__(RowCfg<N2>::WG) void rowpass_kernel(YT* __restrict_
             const float2 xk = h ? v[q2] : v[q], fm = conjf2(h ? pm2 : pm);
             const float2 ha2 = cadd(xk, fm), d = csub(xk, fm);
             const float2 hb2 = make_float2(d.y, -d.x);
-            pqp[(size_t)s * N2 + i + (h ? q2 : q) * T] =
-                make_float4(nrm * (ha2.x + hb2.x), nrm * (ha2.y + hb2.y), nrm * (ha2.x - hb2.x),
-                            nrm * (ha2.y - hb2.y));
+            stpq(pqp + (size_t)s * N2 + i + (h ? q2 : q) * T,
+                 make_float4(nrm * (ha2.x + hb2.x), nrm * (ha2.y + hb2.y), nrm * (ha2.x - hb2.x),
+                             nrm * (ha2.y - hb2.y)));
           }
         }
       }
@@ -709,7 +717,7 @@ __global__ __launch_bounds__(RowCfg<N2>::WG) void rowpass_kernel(YT* __restrict_
       __syncthreads();
       if (s == 0) {
         const int pqrow = up ? HALF : 0;
-        const float4* pqs = pqp + (size_t)pqrow * N2;
+        const PT* pqs = pqp + (size_t)pqrow * N2;
         const int kend = (MODE == ROW_CONV) ? (up ? N2 / 2 - 1 : N2 / 2) : N2 - 1;
         // fixed trip count (k2 = i + it*T <= kend), so that the loads in it are
         // straight-line code the compiler can count
@@ -721,7 +729,7 @@ __global__ __launch_bounds__(RowCfg<N2>::WG) void rowpass_kernel(YT* __restrict_
           const int m2 = up ? (N2 - 1 - k2) : ((N2 - k2) & (N2 - 1));
           const float2 xk = buf[pad16(k2)], xm = buf[pad16(m2)];
           if (MODE == ROW_CONV) {
-            const float4 q4 = pqs[k2];
+            const float4 q4 = ldpq(pqs[k2]);
             const float2 P = make_float2(q4.x, q4.y), Q = make_float2(q4.z, q4.w);
             const float2 yk = cadd(cmul(xk, P), cmul(conjf2(xm), Q));
             if (m2 != k2) buf[pad16(m2)] = cadd(cmulc(xm, P), cmulc(conjf2(xk), Q));
@@ -730,8 +738,8 @@ __global__ __launch_bounds__(RowCfg<N2>::WG) void rowpass_kernel(YT* __restrict_
             const float2 fm = conjf2(xm);
             const float2 ha2 = cadd(xk, fm), d = csub(xk, fm);
             const float2 hb2 = make_float2(d.y, -d.x);
-            pqp[(size_t)pqrow * N2 + k2] = make_float4(nrm * (ha2.x + hb2.x), nrm * (ha2.y + hb2.y),
-                                                       nrm * (ha2.x - hb2.x), nrm * (ha2.y - hb2.y));
+            stpq(pqp + (size_t)pqrow * N2 + k2, make_float4(nrm * (ha2.x + hb2.x), nrm * (ha2.y + hb2.y),
+                                                           nrm * (ha2.x - hb2.x), nrm * (ha2.y - hb2.y)));
           }
         }
       }
@@ -790,10 +798,12 @@ template <int N2> struct RowSeqCfg {
 };
 
 template <typename YT, int N1, int N2, int MODE>
-__global__ __launch_bounds__(RowSeqCfg<N2>::T) void rowpass_seq_kernel(YT* __restrict__ Y, float4* __restrict__ pq,
+__global__ __launch_bounds__(RowSeqCfg<N2>::T) void rowpass_seq_kernel(YT* __restrict__ Y,
+                                                                       typename PqOf<YT>::type* __restrict__ pq,
                                                                        const float2* __restrict__ tw_row, int pq_off,
                                                                        int pair_off, int pq_mod, int nitems) {
   using C = RowSeqCfg<N2>;
+  using PT = typename PqOf<YT>::type;
   constexpr int E = C::E, T = C::T;
   constexpr int HALF = N1 / 2;
   constexpr int PQROWS = HALF + 1;
@@ -826,7 +836,7 @@ __global__ __launch_bounds__(RowSeqCfg<N2>::T) void rowpass_seq_kernel(YT* __res
   for (int item = blockIdx.x; item < nitems; item += gridDim.x) {
     const int pl = item / HALF, s = item - pl * HALF;
     const int next = item + gridDim.x < nitems ? item + gridDim.x : item;
-    float4* pqp = pq + ((size_t)pq_off + (pl + pair_off) % pq_mod) * PQROWS * N2;
+    PT* pqp = pq + ((size_t)pq_off + (pl + pair_off) % pq_mod) * PQROWS * N2;
     YT* Ya = row_ptr(item, 0);
     YT* Yb = row_ptr(item, 1);
     // forward DFTs, results to the row buffers in natural order (one row at a
@@ -850,12 +860,12 @@ __global__ __launch_bounds__(RowSeqCfg<N2>::T) void rowpass_seq_kernel(YT* __res
     // spectrum product: bin k2 of row a with bin N2 - 1 - k2 of row b (s != 0);
     // rows 0 and N1/2 (s = 0) are each paired with themselves
     if (s != 0) {
-      const float4* pqs = pqp + (size_t)s * N2;
+      const PT* pqs = pqp + (size_t)s * N2;
 #pragma unroll
       for (int q = 0; q < E; ++q) {
         const int k2 = l + q * T, m2 = N2 - 1 - k2;
         const float2 xk = A[pad16(k2)], xm = B[pad16(m2)];
-        const float4 w4 = pqs[k2];
+        const float4 w4 = ldpq(pqs[k2]);
         if (MODE == ROW_CONV) {
           const float2 P = make_float2(w4.x, w4.y), Q = make_float2(w4.z, w4.w);
           A[pad16(k2)] = cadd(cmul(xk, P), cmul(conjf2(xm), Q));
@@ -864,8 +874,8 @@ __global__ __launch_bounds__(RowSeqCfg<N2>::T) void rowpass_seq_kernel(YT* __res
           const float2 fm = conjf2(xm);
           const float2 ha2 = cadd(xk, fm), d = csub(xk, fm);
           const float2 hb2 = make_float2(d.y, -d.x);
-          pqp[(size_t)s * N2 + k2] = make_float4(nrm * (ha2.x + hb2.x), nrm * (ha2.y + hb2.y),
-                                                 nrm * (ha2.x - hb2.x), nrm * (ha2.y - hb2.y));
+          stpq(pqp + (size_t)s * N2 + k2, make_float4(nrm * (ha2.x + hb2.x), nrm * (ha2.y + hb2.y),
+                                                      nrm * (ha2.x - hb2.x), nrm * (ha2.y - hb2.y)));
         }
       }
     } else {
@@ -873,7 +883,7 @@ __global__ __launch_bounds__(RowSeqCfg<N2>::T) void rowpass_seq_kernel(YT* __res
       for (int h = 0; h < 2; ++h) {
         float2* row = h ? B : A;
         const int pqrow = h ? HALF : 0;
-        const float4* pqs = pqp + (size_t)pqrow * N2;
+        const PT* pqs = pqp + (size_t)pqrow * N2;
         const int kend = (MODE == ROW_CONV) ? (h ? N2 / 2 - 1 : N2 / 2) : N2 - 1;
         constexpr int KIT = (MODE == ROW_CONV) ? E / 2 + 1 : E;
 #pragma unroll
@@ -882,7 +892,7 @@ __global__ __launch_bounds__(RowSeqCfg<N2>::T) void rowpass_seq_kernel(YT* __res
           if (k2 > kend) continue;
           const int m2 = h ? (N2 - 1 - k2) : ((N2 - k2) & (N2 - 1));
           const float2 xk = row[pad16(k2)], xm = row[pad16(m2)];
-          const float4 w4 = pqs[k2];
+          const float4 w4 = ldpq(pqs[k2]);
           if (MODE == ROW_CONV) {
             const float2 P = make_float2(w4.x, w4.y), Q = make_float2(w4.z, w4.w);
             const float2 yk = cadd(cmul(xk, P), cmul(conjf2(xm), Q));
@@ -892,8 +902,8 @@ __global__ __launch_bounds__(RowSeqCfg<N2>::T) void rowpass_seq_kernel(YT* __res
             const float2 fm = conjf2(xm);
             const float2 ha2 = cadd(xk, fm), d = csub(xk, fm);
             const float2 hb2 = make_float2(d.y, -d.x);
-            pqp[(size_t)pqrow * N2 + k2] = make_float4(nrm * (ha2.x + hb2.x), nrm * (ha2.y + hb2.y),
-                                                       nrm * (ha2.x - hb2.x), nrm * (ha2.y - hb2.y));
+            stpq(pqp + (size_t)pqrow * N2 + k2, make_float4(nrm * (ha2.x + hb2.x), nrm * (ha2.y + hb2.y),
+                                                           nrm * (ha2.x - hb2.x), nrm * (ha2.y - hb2.y)));
           }
         }
       }
@@ -1185,9 +1195,11 @@ static hipError_t launch_col(const ColArgs& a, int N1, int mode, bool act_bf16, 
 }
 
 template <typename YT, int N1, int N2>
-static hipError_t launch_row_t(void* Y, float4* pq, const float2* tw_row, int pq_off, int pair_off, int pq_mod,
+static hipError_t launch_row_t(void* Y, void* pqv, const float2* tw_row, int pq_off, int pair_off, int pq_mod,
                                int pairs, int mode, hipStream_t s) {
+  using PT = typename PqOf<YT>::type;
   YT* y = static_cast<YT*>(Y);
+  PT* pq = static_cast<PT*>(pqv);
   if constexpr (N2 >= 8192) {
     const int items = pairs * (N1 / 2);
     auto fn = mode == ROW_CONV ? rowpass_seq_kernel<YT, N1, N2, ROW_CONV> : rowpass_seq_kernel<YT, N1, N2, ROW_SPEC>;
@@ -1207,7 +1219,7 @@ static hipError_t launch_row_t(void* Y, float4* pq, const float2* tw_row, int pq
       const char* v = getenv("HYENA_ROW_PREFETCH");
       return v ? atoi(v) & 3 : 1;
     }();
-    using Fn = void (*)(YT*, float4*, const float2*, int, int, int, int);
+    using Fn = void (*)(YT*, PT*, const float2*, int, int, int, int);
     Fn fn;
     if (mode != ROW_CONV) fn = rowpass_kernel<YT, N1, N2, ROW_SPEC, 0>;
     else if (pf == 1) fn = rowpass_kernel<YT, N1, N2, ROW_CONV, 1>;
@@ -1225,7 +1237,7 @@ static hipError_t launch_row_t(void* Y, float4* pq, const float2* tw_row, int pq
 }
 
 template <typename YT>
-static hipError_t launch_row_y(int N1, int N2, void* Y, float4* pq, const float2* tw_row, int pq_off, int pair_off,
+static hipError_t launch_row_y(int N1, int N2, void* Y, void* pq, const float2* tw_row, int pq_off, int pair_off,
                                int pq_mod, int pairs, int mode, hipStream_t s) {
 #define ROWCASE(n1, n2)                                                                                  \
   if (N1 == n1 && N2 == n2)                                                                              \
@@ -1255,8 +1267,15 @@ static ColArgs col_args(const FourStepTables& tb, int L, int D, int NO) {
   return a;
 }
 
-hipError_t fourstep_spec(const FourStepTables& tb, const float* h, float2* Y, float4* pq, int L, int D, int NO,
-                         bool wrapped, hipStream_t s) {
+// bf16 copy of the filter spectra (rounded to nearest even), read by the row
+// passes of bf16 workloads
+__global__ __launch_bounds__(256) void pq_bf16_kernel(const float4* __restrict__ in, pq16* __restrict__ out,
+                                                      size_t n) {
+  for (size_t k = blockIdx.x * (size_t)256 + threadIdx.x; k < n; k += (size_t)gridDim.x * 256) stpq(out + k, in[k]);
+}
+
+hipError_t fourstep_spec(const FourStepTables& tb, const float* h, float2* Y, float4* pq, void* pq_bf16, int L,
+                         int D, int NO, bool wrapped, hipStream_t s) {
   ColArgs a = col_args(tb, L, D, NO);
   const int N1 = fourstep_n1(L);
   a.h = h;
@@ -1264,7 +1283,11 @@ hipError_t fourstep_spec(const FourStepTables& tb, const float* h, float2* Y, fl
   const int pairs = NO * D / 2;
   hipError_t e = launch_col(a, N1, wrapped ? COL_FWD_HW : COL_FWD_H, false, false, pairs, s);
   if (e != hipSuccess) return e;
-  return launch_row_y<float2>(N1, a.N2, Y, pq, tb.tw_row, 0, 0, pairs, pairs, ROW_SPEC, s);
+  e = launch_row_y<float2>(N1, a.N2, Y, pq, tb.tw_row, 0, 0, pairs, pairs, ROW_SPEC, s);
+  if (e != hipSuccess) return e;
+  const size_t n = (size_t)pairs * (N1 / 2 + 1) * a.N2;
+  hipLaunchKernelGGL(pq_bf16_kernel, dim3(2048), dim3(256), 0, s, pq, static_cast<pq16*>(pq_bf16), n);
+  return hipGetLastError();
 }
 
 hipError_t fourstep_conv(const FourStepTables& tb, const FourStepConvArgs& c, bool is_bf16, hipStream_t s) {
@@ -1286,8 +1309,8 @@ hipError_t fourstep_conv(const FourStepTables& tb, const FourStepConvArgs& c, bo
     hipError_t e = launch_col(g, N1, COL_FWD_V, is_bf16, ybf, np, s);
     if (e != hipSuccess) return e;
     for (int n = 0; n < c.NO; ++n) {
-      e = ybf ? launch_row_y<cbf16>(N1, a.N2, c.Y, const_cast<float4*>(c.pq), tb.tw_row, n * half, p0, half, np,
-                                    ROW_CONV, s)
+      e = ybf ? launch_row_y<cbf16>(N1, a.N2, c.Y, const_cast<void*>(c.pq_bf16), tb.tw_row, n * half, p0, half,
+                                    np, ROW_CONV, s)
               : launch_row_y<float2>(N1, a.N2, c.Y, const_cast<float4*>(c.pq), tb.tw_row, n * half, p0, half, np,
                                      ROW_CONV, s);
       if (e != hipSuccess) return e;

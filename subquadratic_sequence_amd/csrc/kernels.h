@@ -65,6 +65,7 @@ struct FourStepConvArgs {
   const void* s;         // short-convolved projections [B][(NO+1)D][L]
   const float* dskip;
   const float4* pq;      // [NO][D/2][N1/2 + 1][N2]
+  const void* pq_bf16;   // the same entries as four bf16 (read with the bf16 intermediate)
   void* z[2];            // ping-pong z^{n+1} buffers [B][D][L]
   void* zfinal;          // z^{NO+1} [B][D][L]
   void* Y;               // intermediate [group_pairs][N1][N2]
@@ -73,8 +74,9 @@ struct FourStepConvArgs {
   bool y_bf16;           // bf16 workloads: keep the intermediate as bf16 pairs
 };
 hipError_t fourstep_conv(const FourStepTables& tb, const FourStepConvArgs& c, bool bf16, hipStream_t s);
-hipError_t fourstep_spec(const FourStepTables& tb, const float* h, float2* Y, float4* pq, int L, int D, int NO,
-                         bool wrapped, hipStream_t s);
+// filter spectra into pq (fp32) and pq_bf16 (the same entries as four bf16)
+hipError_t fourstep_spec(const FourStepTables& tb, const float* h, float2* Y, float4* pq, void* pq_bf16, int L,
+                         int D, int NO, bool wrapped, hipStream_t s);
 
 // --------------------------------------------------------------- 3D path
 // Transform sizes (MX, MY, MZ): (2X, 2Y, 2Z) for the zero-padded boundary,

@@ -65,10 +65,11 @@ def test_size_queries_formulas(hy):
     L, D, N = 1024, 64, 2
     al = lambda x: (x + 255) // 256 * 256  # noqa: E731
     assert hy.hyena_cache_bytes(L, D, N) == al(2 * L * 8) + al(N * (D // 2) * (L + 1) * 16)
-    # four-step at L = 64k (2L = 64 x 2048): 33 rows of N2 per channel pair and order
+    # four-step at L = 64k (2L = 64 x 2048): 33 rows of N2 per channel pair and order,
+    # (P, Q) in fp32 (16 bytes) and again in bf16 (8 bytes)
     L = 65536
     n2 = 2 * L // 64
-    assert hy.hyena_cache_bytes(L, D, N) >= N * (D // 2) * 33 * n2 * 16
+    assert hy.hyena_cache_bytes(L, D, N) >= N * (D // 2) * 33 * n2 * (16 + 8)
     # workspace grows linearly with batch in its activation part
     w1 = hy.hyena_workspace_bytes(1, 2048, 768, 2, 1)
     w2 = hy.hyena_workspace_bytes(2, 2048, 768, 2, 1)
