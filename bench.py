@@ -54,11 +54,20 @@ def log(msg):
     print(msg, file=sys.stderr, flush=True)
 
 
+def four_step_spectrum_bytes(s) -> float:
+    """Bytes per channel and bin of the filter spectra the four-step row passes
+    read: the half spectrum (L + 1 bins) as complex fp32, or as bf16 pairs for
+    bf16 workloads unless HYENA_SPECTRUM_FP32=1."""
+    if s == 2 and os.environ.get("HYENA_SPECTRUM_FP32", "0") in ("", "0"):
+        return 4.0
+    return 8.0
+
+
 def conv_alg_bytes(B, L, D, N, s, lds_regime: bool) -> float:
     if lds_regime:
         # all orders fused on chip: read v and x^1..x^N, write z^{N+1}, read N spectra
         return (N + 1) * B * L * D * s + B * L * D * s + N * 8.0 * D * (L + 1)
-    return N * (3.0 * B * L * D * s + 8.0 * D * (L + 1))
+    return N * (3.0 * B * L * D * s + four_step_spectrum_bytes(s) * D * (L + 1))
 
 
 def conv_source_hash(sources=None) -> str:

@@ -217,31 +217,6 @@ __device__ __forceinline__ void stc(cbf16* p, float2 x) {
   p->v = (unsigned int)lo | ((unsigned int)hi << 16);
 }
 
-// Filter spectrum entry (P, Q) of the four-step row pass: float4 (P.re, P.im,
-// Q.re, Q.im) or, next to a bf16 intermediate, the same four values as bf16 in
-// 64 bits (two cbf16 words).
-struct pq16 {
-  unsigned int p, q;
-};
-template <typename YT> struct PqOf {
-  using type = float4;
-};
-template <> struct PqOf<cbf16> {
-  using type = pq16;
-};
-__device__ __forceinline__ float4 ldpq(const float4& x) { return x; }
-__device__ __forceinline__ float4 ldpq(const pq16& x) {
-  return make_float4(__uint_as_float(x.p << 16), __uint_as_float(x.p & 0xFFFF0000u), __uint_as_float(x.q << 16),
-                     __uint_as_float(x.q & 0xFFFF0000u));
-}
-__device__ __forceinline__ void stpq(float4* p, float4 x) { *p = x; }
-__device__ __forceinline__ void stpq(pq16* p, float4 x) {
-  cbf16 a, b;
-  stc(&a, make_float2(x.x, x.y));
-  stc(&b, make_float2(x.z, x.w));
-  *p = pq16{a.v, b.v};
-}
-
 // ------------------------------------------------ buffer-resource access
 // Raw buffer loads and stores: address = resource base + a 32-bit per-lane
 // offset + a 32-bit workgroup-uniform offset (held in a scalar register), so

@@ -9,9 +9,14 @@ import bench
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 
 
-def test_conv_alg_bytes_four_step():
-    # two orders, each reads z^n and x^n and writes z^{n+1} (bf16) and reads one fp32 complex spectrum
+def test_conv_alg_bytes_four_step(monkeypatch):
+    # two orders, each reads z^n and x^n and writes z^{n+1} and reads one half spectrum
+    # per channel: bf16 complex with bf16 storage, fp32 complex otherwise or with the knob
     B, L, D, N = 1, 65536, 768, 2
+    monkeypatch.delenv("HYENA_SPECTRUM_FP32", raising=False)
+    assert bench.conv_alg_bytes(B, L, D, N, 2, False) == 2 * (3 * B * L * D * 2 + 4 * D * (L + 1))
+    assert bench.conv_alg_bytes(B, L, D, N, 4, False) == 2 * (3 * B * L * D * 4 + 8 * D * (L + 1))
+    monkeypatch.setenv("HYENA_SPECTRUM_FP32", "1")
     assert bench.conv_alg_bytes(B, L, D, N, 2, False) == 2 * (3 * B * L * D * 2 + 8 * D * (L + 1))
 
 
