@@ -30,3 +30,11 @@ from .hyena_nd_oracle import (  # noqa: F401
     hyena_nd_fwd,
     hyena_nd_fwd_sampled,
 )
+from .hyena_nd_film_oracle import (  # noqa: F401
+    film_control,
+    film_modulation,
+    nd_filter_film,
+    film_kernels,
+    hyena_nd_film_fwd,
+    hyena_nd_film_fwd_sampled,
+)

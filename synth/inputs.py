@@ -180,6 +180,51 @@ def make_nd(seed: int, B: int, X: int, Y: int, Z: int, C: int, N: int = 2, W: in
                          meta=dict(seed=seed, u_mean_spread=u_mean_spread))
 
 
+@dataclass
+class HyenaNDFilmInputs:
+    """A 3D workload with register-token conditioning (per-sample FiLM kernels)."""
+    base: HyenaNDInputs   # grid input, projections, skips, SIREN weights (decay and gates unused)
+    reg: np.ndarray       # [B, R, C] register activations
+    q: np.ndarray         # [C] register score vector
+    film_w: np.ndarray    # [4, C, W] gamma_1, beta_1, gamma_2, beta_2 projections of z
+    film_b: np.ndarray    # [4, W]
+    omega0: np.ndarray    # [W] first-layer frequency factors
+    window: np.ndarray    # [C] Gaussian window rates
+
+    def __getattr__(self, name):
+        if name == "base":
+            raise AttributeError(name)
+        return getattr(self.base, name)
+
+    @property
+    def film_filter_params(self):
+        b = self.base
+        return dict(w1=b.w1, b1=b.b1, w2=b.w2, b2=b.b2, w3=b.w3, b3=b.b3, omega0=self.omega0,
+                    window=self.window)
+
+
+def make_nd_film(seed: int, B: int, X: int, Y: int, Z: int, C: int, N: int = 2, W: int = 64, R: int = 4,
+                 circular: bool = False) -> HyenaNDFilmInputs:
+    """Draw one register-conditioned 3D workload (fp32).
+
+    The grid part is make_nd's (same seed). Then: reg ~ N(0, 1) [B, R, C];
+    q ~ N(0, 1/C); film_w ~ N(0, 0.25/C); film_b = (1, 0, 1, 0) per row plus
+    U(-0.1, 0.1), so that gamma stays near 1 and beta near 0; omega0 in four
+    blocks of W/4 units at 1, 3, 10 and 30 (frequency blocks across the hidden
+    units); window rates log-spaced over [0.5, 20] across the channels.
+    """
+    base = make_nd(seed, B, X, Y, Z, C, N=N, W=W, circular=circular)
+    rng = np.random.default_rng(seed + 7919)
+    reg = rng.standard_normal((B, R, C)).astype(np.float32)
+    q = (rng.standard_normal(C) / math.sqrt(C)).astype(np.float32)
+    film_w = (rng.standard_normal((4, C, W)) * (0.5 / math.sqrt(C))).astype(np.float32)
+    film_b = (np.array([1.0, 0.0, 1.0, 0.0])[:, None] + _uniform(rng, (4, W), 0.1)).astype(np.float32)
+    omega0 = np.repeat(np.array([1.0, 3.0, 10.0, 30.0]), -(-W // 4))[:W].astype(np.float32)
+    window = np.geomspace(0.5, 20.0, C).astype(np.float32)
+    return HyenaNDFilmInputs(base=base, reg=reg, q=q, film_w=film_w, film_b=film_b, omega0=omega0,
+                             window=window)
+
+
 # The five workloads. Names describe what each is; seeds are 1..5 in this order.
 CONFIGS = {
     "order2_f32_L1k_D64": dict(kind="1d", seed=1, B=1, L=1024, D=64, N=2, K=8, dtype="f32"),
