@@ -231,6 +231,61 @@ int hyena_nd_fwd_profiled(const hyena_nd_layer *layer, const float *u, const flo
                           const float *w_out, int B, float *y, void *ws, size_t ws_bytes,
                           hipStream_t stream, const hipEvent_t *events);
 
+/* ------------------------------------------------- 3D, register-conditioned ---- */
+/*
+ * HyenaND with the page's own input conditioning (HyenaND explainer,
+ * gist.science, "Methodology: HyenaND": Input-Dependent Kernels via Registers
+ * and FiLM; Kernel Synthesis; Kernel Parameterization). Per sample b, with the
+ * R register activations reg[b] [R][C] (the layer input at the register tokens):
+ *   w_r  = softmax over r of (reg[b][r] . q),  z = sum_r w_r reg[b][r]
+ *   gamma_l = film_w[2l-2]^T z + film_b[2l-2],  beta_l = film_w[2l-1]^T z + film_b[2l-1]
+ *   h_1 = sin(omega0 * gamma_1 * (W1^T c + b1) + beta_1)
+ *   h_2 = sin(gamma_2 * (W2^T h_1 + b2) + beta_2)
+ *   K^n_{b,c}(d) = exp(-a_c |c|^2) * (W3^T h_2 + b3)[(n-1)C + c]   (Gaussian window,
+ *                  a = hyena_nd_filter_params.decay)
+ * at the offsets and coordinates of the boundary (as hyena_nd_filter_gen), then
+ * the projection / recurrence of hyena_nd_fwd, each sample convolved with its own
+ * kernel and no channel-mean gate. The page gives the parts and their order,
+ * not these formulas: they are the plainest reading of it. The kernels depend on
+ * the input, so every call synthesises and transforms B of them.
+ */
+typedef struct {
+  int registers;        /* R, 1 <= R <= 1024 */
+  const float *q;       /* [C]     register score vector */
+  const float *film_w;  /* [4][C][W]  gamma_1, beta_1, gamma_2, beta_2 maps of z */
+  const float *film_b;  /* [4][W] */
+  const float *omega0;  /* [W]     first-layer frequency factors */
+} hyena_nd_film_params;
+
+/* Scratch for hyena_nd_film_fwd: the hyena_nd_fwd workspace, B kernel spectra
+ * (B N C MX MY (MZ/2+1) complex fp32), one kernel's synthesis buffers and the
+ * FiLM vectors. 0 for unsupported shapes (those of hyena_nd_workspace_bytes_ex,
+ * 1 <= width <= 128). */
+size_t hyena_nd_film_workspace_bytes(int B, int X, int Y, int Z, int C, int N, int width, int boundary);
+
+/* Forward pass of the register-conditioned layer. Shapes as hyena_nd_fwd, plus
+ *   p       SIREN weights (width W) and, in `decay`, the Gaussian window rates [C]
+ *   fp      register scoring and FiLM maps
+ *   reg     [B][R][C] fp32 register activations
+ *   k_out   NULL, or [B][N][C][MX][MY][MZ] fp32 receiving every sample's kernel on
+ *           the offset grid (as hyena_nd_filter_gen's k_out)
+ *   ws      scratch of hyena_nd_film_workspace_bytes(B, X, Y, Z, C, N, p->width, boundary)
+ * Pointers 16-byte aligned; y may not alias the inputs. Errors as hyena_nd_fwd. */
+int hyena_nd_film_fwd(int X, int Y, int Z, int C, int N, int boundary, const hyena_nd_filter_params *p,
+                      const hyena_nd_film_params *fp, const float *u, const float *reg, const float *w_in,
+                      const float *dskip, const float *w_out, int B, float *y, float *k_out, void *ws,
+                      size_t ws_bytes, hipStream_t stream);
+
+/* Same launches plus hipEventRecord(events[i], stream) at five points: [0] before
+ * the kernel synthesis, [1] after it (FiLM vectors, B MLP evaluations and 3D
+ * FFTs), [2] after the in-projection, [3] after the convolutions, [4] after the
+ * out-projection. A null `events` is HYENA_ERR_INVALID_ARG. */
+int hyena_nd_film_fwd_profiled(int X, int Y, int Z, int C, int N, int boundary, const hyena_nd_filter_params *p,
+                               const hyena_nd_film_params *fp, const float *u, const float *reg,
+                               const float *w_in, const float *dskip, const float *w_out, int B, float *y,
+                               float *k_out, void *ws, size_t ws_bytes, hipStream_t stream,
+                               const hipEvent_t *events);
+
 #ifdef __cplusplus
 }
 #endif

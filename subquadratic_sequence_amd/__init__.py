@@ -10,6 +10,7 @@ from .hyena import (  # noqa: F401
     HYENA_F32,
     HyenaError,
     HyenaLayer,
+    HyenaNDFilm,
     HyenaNDLayer,
     LIB_PATH,
     ND_CIRCULAR,
@@ -23,6 +24,9 @@ from .hyena import (  # noqa: F401
     hyena_fwd_profiled,
     hyena_nd_cache_bytes,
     hyena_nd_cache_bytes_ex,
+    hyena_nd_film_fwd,
+    hyena_nd_film_fwd_profiled,
+    hyena_nd_film_workspace_bytes,
     hyena_nd_filter_gen,
     hyena_nd_filter_workspace_bytes,
     hyena_nd_filter_workspace_bytes_ex,

@@ -87,7 +87,15 @@ struct NdFilterArgs {
   int MX, MY, MZ;
   const float *w1, *b1, *w2, *b2, *w3, *b3, *decay;
   float* k;  // kernel on the offset grid [N][C][MX][MY][MZ]
+  // register conditioning (null: the plain kernel with an exponential window):
+  // [4][W] = omega0 * gamma_1, beta_1, gamma_2, beta_2 of one sample; `decay`
+  // then holds the Gaussian window rates
+  const float* film = nullptr;
 };
+// control vector and FiLM vectors of every sample: mod [B][4][W]
+hipError_t nd_film_mod(const float* reg, const float* q, const float* film_w, const float* film_b,
+                       const float* omega0, float* mod, int B, int R, int C, int W, hipStream_t s);
+hipError_t fill(float* p, size_t n, float v, hipStream_t s);
 struct NdConvArgs {
   int X, Y, Z, C, NO, B, n, npairs;
   int MX, MY, MZ;

@@ -31,6 +31,11 @@ namespace hy {
 constexpr int kNP = 64;       // offset points per workgroup
 constexpr int kNdMaxW = 128;
 
+// FILM: the register-conditioned SIREN (each hidden pre-activation times the
+// sample's gamma, plus its beta; omega0 folded into the first layer's gamma) with
+// a Gaussian window exp(-a_c |c|^2); otherwise sin(W^T h + b) with the window
+// exp(-a_c |c|).
+template <bool FILM>
 __global__ __launch_bounds__(256) void nd_mlp_kernel(NdFilterArgs a) {
   __shared__ float cs[kNP][3];
   __shared__ float rad[kNP];
@@ -49,20 +54,21 @@ __global__ __launch_bounds__(256) void nd_mlp_kernel(NdFilterArgs a) {
     cs[t][0] = cx;
     cs[t][1] = cy;
     cs[t][2] = cz;
-    rad[t] = sqrtf(cx * cx + cy * cy + cz * cz);
+    const float r2 = cx * cx + cy * cy + cz * cz;
+    rad[t] = FILM ? r2 : sqrtf(r2);
   }
   __syncthreads();
   for (int idx = tid; idx < kNP * W; idx += 256) {
     const int t = idx / W, j = idx % W;
     const float s = a.b1[j] + cs[t][0] * a.w1[j] + cs[t][1] * a.w1[W + j] + cs[t][2] * a.w1[2 * W + j];
-    h1[t][j] = sinf(s);
+    h1[t][j] = FILM ? sinf(a.film[j] * s + a.film[W + j]) : sinf(s);
   }
   __syncthreads();
   for (int idx = tid; idx < kNP * W; idx += 256) {
     const int t = idx / W, j = idx % W;
     float s = a.b2[j];
     for (int f = 0; f < W; ++f) s += h1[t][f] * a.w2[f * W + j];
-    h2[t][j] = sinf(s);
+    h2[t][j] = FILM ? sinf(a.film[2 * W + j] * s + a.film[3 * W + j]) : sinf(s);
   }
   __syncthreads();
   const int NC = a.N * a.C;
@@ -91,11 +97,11 @@ __global__ __launch_bounds__(256) void nd_mlp_kernel(NdFilterArgs a) {
 // W3 in registers and the next block's slice in flight.
 typedef __attribute__((ext_vector_type(16))) float f32x16;
 
-template <int WW>
+template <int WW, bool FILM>
 __global__ __launch_bounds__(256) void nd_mlp_mfma_kernel(NdFilterArgs a) {
   constexpr int LDH = WW + 1;
   constexpr int KW = WW / 2;
-  __shared__ float cs[kNP][5];  // the three coordinates, a zero pad column, the radius
+  __shared__ float cs[kNP][5];  // the three coordinates, a zero pad column, the radius (FILM: its square)
   __shared__ float buf0[kNP * LDH];  // layer 2
   __shared__ float buf1[kNP * LDH];  // layer 1
   const int MX = a.MX, MY = a.MY, MZ = a.MZ;
@@ -113,7 +119,8 @@ __global__ __launch_bounds__(256) void nd_mlp_mfma_kernel(NdFilterArgs a) {
     cs[t][1] = cy;
     cs[t][2] = cz;
     cs[t][3] = 0.f;
-    cs[t][4] = sqrtf(cx * cx + cy * cy + cz * cz);
+    const float r2 = cx * cx + cy * cy + cz * cz;
+    cs[t][4] = FILM ? r2 : sqrtf(r2);
   }
   __syncthreads();
   auto zero = [](f32x16& c) {
@@ -132,8 +139,10 @@ __global__ __launch_bounds__(256) void nd_mlp_mfma_kernel(NdFilterArgs a) {
                                                  0, 0, 0);
     }
     const float bj = a.b1[j];
+    const float gj = FILM ? a.film[j] : 1.f, ej = FILM ? a.film[WW + j] : 0.f;
 #pragma unroll
-    for (int e = 0; e < 16; ++e) buf1[(rb * 32 + (e >> 2) * 8 + k2 * 4 + (e & 3)) * LDH + j] = sinf(acc[e] + bj);
+    for (int e = 0; e < 16; ++e)
+      buf1[(rb * 32 + (e >> 2) * 8 + k2 * 4 + (e & 3)) * LDH + j] = FILM ? sinf(gj * (acc[e] + bj) + ej) : sinf(acc[e] + bj);
   }
   __syncthreads();
   for (int blk = wave; blk < NB; blk += 4) {
@@ -145,8 +154,10 @@ __global__ __launch_bounds__(256) void nd_mlp_mfma_kernel(NdFilterArgs a) {
       acc = __builtin_amdgcn_mfma_f32_32x32x2f32(buf1[(rb * 32 + r32) * LDH + k + k2],
                                                  a.w2[(size_t)(k + k2) * WW + j], acc, 0, 0, 0);
     const float bj = a.b2[j];
+    const float gj = FILM ? a.film[2 * WW + j] : 1.f, ej = FILM ? a.film[3 * WW + j] : 0.f;
 #pragma unroll
-    for (int e = 0; e < 16; ++e) buf0[(rb * 32 + (e >> 2) * 8 + k2 * 4 + (e & 3)) * LDH + j] = sinf(acc[e] + bj);
+    for (int e = 0; e < 16; ++e)
+      buf0[(rb * 32 + (e >> 2) * 8 + k2 * 4 + (e & 3)) * LDH + j] = FILM ? sinf(gj * (acc[e] + bj) + ej) : sinf(acc[e] + bj);
   }
   __syncthreads();
   const int NC = a.N * a.C;  // a multiple of 64
@@ -190,6 +201,68 @@ __global__ __launch_bounds__(256) void nd_mlp_mfma_kernel(NdFilterArgs a) {
     if (!more) break;
     cb = nxt;
   }
+}
+
+// ======================================================= register conditioning
+// One workgroup per sample: scores s_r = reg_r . q (a wave per register, lanes
+// over channels), softmax weights over the registers, the control vector
+// z = sum_r w_r reg_r, then the four FiLM vectors film_b[k] + film_w[k]^T z
+// (k = gamma_1, beta_1, gamma_2, beta_2), gamma_1 times omega0.
+// LDS: z [C], scores [R], weights [R].
+__global__ __launch_bounds__(256) void nd_film_mod_kernel(const float* __restrict__ reg, const float* __restrict__ q,
+                                                          const float* __restrict__ fw, const float* __restrict__ fb,
+                                                          const float* __restrict__ om, float* __restrict__ mod,
+                                                          int R, int C, int W) {
+  extern __shared__ float sm[];
+  float* z = sm;
+  float* sc = sm + C;
+  float* wt = sc + R;
+  const int b = blockIdx.x, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const float* rb = reg + (size_t)b * R * C;
+  for (int r = wave; r < R; r += 4) {
+    float acc = 0.f;
+    for (int c = lane; c < C; c += 64) acc += rb[(size_t)r * C + c] * q[c];
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) acc += __shfl_xor(acc, o);
+    if (lane == 0) sc[r] = acc;
+  }
+  __syncthreads();
+  float mx = sc[0];
+  for (int r = 1; r < R; ++r) mx = fmaxf(mx, sc[r]);
+  float sum = 0.f;
+  for (int r = 0; r < R; ++r) sum += expf(sc[r] - mx);
+  for (int r = tid; r < R; r += 256) wt[r] = expf(sc[r] - mx) / sum;
+  __syncthreads();
+  for (int c = tid; c < C; c += 256) {
+    float acc = 0.f;
+    for (int r = 0; r < R; ++r) acc += wt[r] * rb[(size_t)r * C + c];
+    z[c] = acc;
+  }
+  __syncthreads();
+  for (int o = tid; o < 4 * W; o += 256) {
+    const int k = o / W, j = o - k * W;
+    const float* w = fw + (size_t)k * C * W + j;
+    float acc = fb[o];
+    for (int c = 0; c < C; ++c) acc += z[c] * w[(size_t)c * W];
+    mod[(size_t)b * 4 * W + o] = k == 0 ? om[j] * acc : acc;
+  }
+}
+
+hipError_t nd_film_mod(const float* reg, const float* q, const float* film_w, const float* film_b,
+                       const float* omega0, float* mod, int B, int R, int C, int W, hipStream_t s) {
+  const size_t lds = (size_t)(C + 2 * R) * sizeof(float);
+  hipLaunchKernelGGL(nd_film_mod_kernel, dim3(B), dim3(256), lds, s, reg, q, film_w, film_b, omega0, mod, R, C, W);
+  return hipGetLastError();
+}
+
+__global__ void fill_kernel(float* __restrict__ p, size_t n, float v) {
+  for (size_t i = blockIdx.x * (size_t)blockDim.x + threadIdx.x; i < n; i += (size_t)gridDim.x * blockDim.x) p[i] = v;
+}
+
+hipError_t fill(float* p, size_t n, float v, hipStream_t s) {
+  const unsigned g = (unsigned)((n + 255) / 256 < 4096 ? (n + 255) / 256 : 4096);
+  hipLaunchKernelGGL(fill_kernel, dim3(g ? g : 1), dim3(256), 0, s, p, n, v);
+  return hipGetLastError();
 }
 
 // Two channels of the offset-indexed kernel, wrapped (offset d stored at d mod M),
@@ -1093,12 +1166,14 @@ static hipError_t launch_pencil(const NdConvArgs& a, dim3 grid, hipStream_t s) {
 hipError_t nd_filter(const NdFilterArgs& f, float2* F, float2* kh, const float2* tw128, hipStream_t s) {
   const int MX = f.MX, MY = f.MY, MZ = f.MZ;
   const size_t P = (size_t)MX * MY * MZ;
-  if (f.W == 64)
-    hipLaunchKernelGGL(nd_mlp_mfma_kernel<64>, dim3((unsigned)(P / kNP)), dim3(256), 0, s, f);
-  else if (f.W == 128)
-    hipLaunchKernelGGL(nd_mlp_mfma_kernel<128>, dim3((unsigned)(P / kNP)), dim3(256), 0, s, f);
-  else
-    hipLaunchKernelGGL(nd_mlp_kernel, dim3((unsigned)(P / kNP)), dim3(256), 0, s, f);
+  const dim3 g((unsigned)(P / kNP));
+  const bool film = f.film != nullptr;
+  using MlpFn = void (*)(NdFilterArgs);
+  MlpFn fn;
+  if (f.W == 64) fn = film ? nd_mlp_mfma_kernel<64, true> : nd_mlp_mfma_kernel<64, false>;
+  else if (f.W == 128) fn = film ? nd_mlp_mfma_kernel<128, true> : nd_mlp_mfma_kernel<128, false>;
+  else fn = film ? nd_mlp_kernel<true> : nd_mlp_kernel<false>;
+  hipLaunchKernelGGL(fn, g, dim3(256), 0, s, f);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   const int npairs = f.N * f.C / 2;

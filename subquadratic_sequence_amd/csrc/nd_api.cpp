@@ -273,3 +273,152 @@ int hyena_nd_fwd_profiled(const hyena_nd_layer* layer, const float* u, const flo
 }
 
 }  // extern "C"
+
+// ------------------------------------------------- register-conditioned layer
+namespace {
+
+// one sample's kernel spectra: N C MX MY (MZ/2 + 1) complex fp32
+size_t film_kh_bytes(int X, int Y, int Z, int C, int N, int bd) {
+  const int p = pad_of(bd);
+  return align_up((size_t)N * C * mx_of(X, bd) * (p * Y) * (p * Z / 2 + 1) * 8, kAlign);
+}
+
+struct NdFilmWs {
+  size_t base, tw, mod, kh, fws, total;
+};
+NdFilmWs nd_film_ws(int B, int X, int Y, int Z, int C, int N, int W, int bd) {
+  NdFilmWs w{};
+  size_t off = 0;
+  w.base = off;
+  off = align_up(off + nd_ws(B, X, Y, Z, C, N, bd).total, kAlign);
+  w.tw = off;
+  off = align_up(off + 128 * 8, kAlign);
+  w.mod = off;
+  off = align_up(off + (size_t)B * 4 * W * 4, kAlign);
+  w.kh = off;
+  off = align_up(off + (size_t)B * film_kh_bytes(X, Y, Z, C, N, bd), kAlign);
+  w.fws = off;
+  off = align_up(off + nd_fws(X, Y, Z, C, N, bd).total, kAlign);
+  w.total = off;
+  return w;
+}
+
+bool film_shape_ok(int B, int X, int Y, int Z, int C, int N, int W, int bd) {
+  return nd_shape_ok(X, Y, Z, C, N, bd) && B >= 1 && W >= 1 && W <= 128 &&
+         (long long)B * X * Y * Z * (N + 1) * C < (1LL << 31);
+}
+
+int film_fwd_impl(int X, int Y, int Z, int C, int N, int bd, const hyena_nd_filter_params* p,
+                  const hyena_nd_film_params* fp, const float* u, const float* reg, const float* w_in,
+                  const float* dskip, const float* w_out, int B, float* y, float* k_out, void* ws, size_t ws_bytes,
+                  hipStream_t stream, const hipEvent_t* ev) {
+  if (p == nullptr || fp == nullptr) return HYENA_ERR_INVALID_ARG;
+  if (!boundary_ok(bd) || B < 1) return B < 1 ? HYENA_ERR_INVALID_ARG : HYENA_ERR_UNSUPPORTED;
+  const int W = p->width, R = fp->registers;
+  if (!film_shape_ok(B, X, Y, Z, C, N, W, bd) || R < 1 || R > 1024) return HYENA_ERR_UNSUPPORTED;
+  const void* ptrs[] = {p->w1, p->b1, p->w2, p->b2, p->w3, p->b3, p->decay, fp->q, fp->film_w, fp->film_b,
+                        fp->omega0, u, reg, w_in, dskip, w_out, y, ws};
+  for (const void* q : ptrs)
+    if (!aligned16(q)) return HYENA_ERR_INVALID_ARG;
+  if (k_out != nullptr && !aligned16(k_out)) return HYENA_ERR_INVALID_ARG;
+  const NdFilmWs fw = nd_film_ws(B, X, Y, Z, C, N, W, bd);
+  if (ws_bytes < fw.total) return HYENA_ERR_WORKSPACE;
+  if (device_ok() != HYENA_OK) return HYENA_ERR_HIP;
+
+  char* wsb = static_cast<char*>(ws);
+  const NdWs w = nd_ws(B, X, Y, Z, C, N, bd);
+  char* base = wsb + fw.base;
+  const NdFws fl = nd_fws(X, Y, Z, C, N, bd);
+  char* fbase = wsb + fw.fws;
+  const int pd = pad_of(bd), MX = mx_of(X, bd), MY = pd * Y, MZ = pd * Z;
+  const size_t P = (size_t)MX * MY * MZ;
+  const size_t khs = film_kh_bytes(X, Y, Z, C, N, bd);
+  float2* tw = reinterpret_cast<float2*>(wsb + fw.tw);
+  float* mod = reinterpret_cast<float*>(wsb + fw.mod);
+
+  // kernel synthesis: FiLM vectors of every sample, then each sample's kernels
+  // and their spectra (the synthesis buffers are reused in stream order)
+  if (ev) HY_CHECK_HIP(hipEventRecord(ev[0], stream));
+  HY_CHECK_HIP(hy::twiddles(tw, 128, 128, stream));
+  HY_CHECK_HIP(hy::nd_film_mod(reg, fp->q, fp->film_w, fp->film_b, fp->omega0, mod, B, R, C, W, stream));
+  for (int b = 0; b < B; ++b) {
+    hy::NdFilterArgs f{X, Y, Z, C, N, W, MX, MY, MZ, p->w1, p->b1, p->w2, p->b2, p->w3, p->b3, p->decay,
+                       k_out ? k_out + (size_t)b * N * C * P : reinterpret_cast<float*>(fbase + fl.k)};
+    f.film = mod + (size_t)b * 4 * W;
+    HY_CHECK_HIP(hy::nd_filter(f, reinterpret_cast<float2*>(fbase + fl.F),
+                               reinterpret_cast<float2*>(wsb + fw.kh + b * khs), tw, stream));
+  }
+  if (ev) HY_CHECK_HIP(hipEventRecord(ev[1], stream));
+
+  const int V = X * Y * Z, J = (N + 1) * C;
+  float* wt_in = reinterpret_cast<float*>(base + w.wt_in);
+  float* wt_out = reinterpret_cast<float*>(base + w.wt_out);
+  float* pbuf = reinterpret_cast<float*>(base + w.p);
+  float* zfin = reinterpret_cast<float*>(base + w.zfinal);
+  float* ones = reinterpret_cast<float*>(base + w.gate);
+  HY_CHECK_HIP(hy::transpose2d(w_in, wt_in, C, J, false, stream));
+  HY_CHECK_HIP(hy::transpose2d(w_out, wt_out, C, C, false, stream));
+  hy::GemmArgs gi{u, wt_in, pbuf, B * V, J, C, V, false, true, nullptr};
+  HY_CHECK_HIP(hy::gemm(gi, false, stream));
+  if (ev) HY_CHECK_HIP(hipEventRecord(ev[2], stream));
+
+  // one sample per launch sequence (a lone sample fills one half of the packed
+  // complex field), each with its own spectra; unit gates
+  HY_CHECK_HIP(hy::fill(ones, (size_t)N * C, 1.f, stream));
+  for (int b = 0; b < B; ++b) {
+    hy::NdConvArgs a{};
+    a.X = X;
+    a.Y = Y;
+    a.Z = Z;
+    a.MX = MX;
+    a.MY = MY;
+    a.MZ = MZ;
+    a.C = C;
+    a.NO = N;
+    a.B = 1;
+    a.p = pbuf + (size_t)b * J * V;
+    a.dskip = dskip;
+    a.gate = ones;
+    a.zbuf[0] = reinterpret_cast<float*>(base + w.z0) + (size_t)b * C * V;
+    a.zbuf[1] = reinterpret_cast<float*>(base + w.z1) + (size_t)b * C * V;
+    a.zfinal = zfin + (size_t)b * C * V;
+    a.Yint = reinterpret_cast<float2*>(base + w.Y);
+    a.kh = reinterpret_cast<const float2*>(wsb + fw.kh + b * khs);
+    a.tw128 = tw;
+    HY_CHECK_HIP(hy::nd_conv(a, stream));
+  }
+  if (ev) HY_CHECK_HIP(hipEventRecord(ev[3], stream));
+  hy::GemmArgs go{zfin, wt_out, y, B * V, C, C, V, true, false, nullptr};
+  HY_CHECK_HIP(hy::gemm(go, false, stream));
+  if (ev) HY_CHECK_HIP(hipEventRecord(ev[4], stream));
+  return HYENA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t hyena_nd_film_workspace_bytes(int B, int X, int Y, int Z, int C, int N, int width, int boundary) {
+  if (!film_shape_ok(B, X, Y, Z, C, N, width, boundary)) return 0;
+  return nd_film_ws(B, X, Y, Z, C, N, width, boundary).total;
+}
+
+int hyena_nd_film_fwd(int X, int Y, int Z, int C, int N, int boundary, const hyena_nd_filter_params* p,
+                      const hyena_nd_film_params* fp, const float* u, const float* reg, const float* w_in,
+                      const float* dskip, const float* w_out, int B, float* y, float* k_out, void* ws,
+                      size_t ws_bytes, hipStream_t stream) {
+  return film_fwd_impl(X, Y, Z, C, N, boundary, p, fp, u, reg, w_in, dskip, w_out, B, y, k_out, ws, ws_bytes,
+                       stream, nullptr);
+}
+
+int hyena_nd_film_fwd_profiled(int X, int Y, int Z, int C, int N, int boundary, const hyena_nd_filter_params* p,
+                               const hyena_nd_film_params* fp, const float* u, const float* reg,
+                               const float* w_in, const float* dskip, const float* w_out, int B, float* y,
+                               float* k_out, void* ws, size_t ws_bytes, hipStream_t stream,
+                               const hipEvent_t* events) {
+  if (events == nullptr) return HYENA_ERR_INVALID_ARG;
+  return film_fwd_impl(X, Y, Z, C, N, boundary, p, fp, u, reg, w_in, dskip, w_out, B, y, k_out, ws, ws_bytes,
+                       stream, events);
+}
+
+}  // extern "C"

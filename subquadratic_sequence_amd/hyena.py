@@ -54,6 +54,10 @@ ND_ZERO_PAD = 0
 ND_CIRCULAR = 1
 
 
+class NDFilmParams(ctypes.Structure):
+    _fields_ = [("registers", _i), ("q", _vp), ("film_w", _vp), ("film_b", _vp), ("omega0", _vp)]
+
+
 # name -> (restype, argtypes)
 SIGNATURES = {
     "hyena_status_str": (ctypes.c_char_p, [_i]),
@@ -79,6 +83,12 @@ SIGNATURES = {
     "hyena_nd_fwd": (_i, [ctypes.POINTER(NDLayer), _vp, _vp, _vp, _vp, _vp, _vp, _i, _vp, _vp, _sz, _vp]),
     "hyena_nd_fwd_profiled": (_i, [ctypes.POINTER(NDLayer), _vp, _vp, _vp, _vp, _vp, _vp, _i, _vp, _vp, _sz, _vp,
                                    ctypes.POINTER(_vp)]),
+    "hyena_nd_film_workspace_bytes": (_sz, [_i, _i, _i, _i, _i, _i, _i, _i]),
+    "hyena_nd_film_fwd": (_i, [_i, _i, _i, _i, _i, _i, ctypes.POINTER(NDFilterParams), ctypes.POINTER(NDFilmParams),
+                               _vp, _vp, _vp, _vp, _vp, _i, _vp, _vp, _vp, _sz, _vp]),
+    "hyena_nd_film_fwd_profiled": (_i, [_i, _i, _i, _i, _i, _i, ctypes.POINTER(NDFilterParams),
+                                        ctypes.POINTER(NDFilmParams), _vp, _vp, _vp, _vp, _vp, _i, _vp, _vp, _vp,
+                                        _sz, _vp, ctypes.POINTER(_vp)]),
 }
 
 _lib = None
@@ -293,3 +303,59 @@ def hyena_nd_fwd_profiled(layer: HyenaNDLayer, u, w_in, dskip, gate_a, gate_b, w
     st = lib().hyena_nd_fwd_profiled(ctypes.byref(layer.c), _ptr(u), _ptr(w_in), _ptr(dskip), _ptr(gate_a),
                                      _ptr(gate_b), _ptr(w_out), B, _ptr(y), _ptr(ws), ws.numel(), _stream(), handles)
     _check(st, "hyena_nd_fwd_profiled")
+
+
+def hyena_nd_film_workspace_bytes(B, X, Y, Z, C, N, width, boundary=ND_ZERO_PAD) -> int:
+    return lib().hyena_nd_film_workspace_bytes(B, X, Y, Z, C, N, width, boundary)
+
+
+class HyenaNDFilm:
+    """Weights of a register-conditioned 3D layer (device tensors, fp32): the SIREN
+    (w1 [3, W], b1, w2 [W, W], b2, w3 [W, N C], b3), the Gaussian window rates
+    [C], the register score vector q [C], the FiLM maps film_w [4, C, W] and
+    film_b [4, W], and omega0 [W]."""
+
+    def __init__(self, X, Y, Z, C, N, boundary, w1, b1, w2, b2, w3, b3, window, q, film_w, film_b, omega0):
+        self.X, self.Y, self.Z, self.C, self.N, self.boundary = X, Y, Z, C, N, boundary
+        self.t = (w1, b1, w2, b2, w3, b3, window, q, film_w, film_b, omega0)  # keeps the tensors alive
+        self.width = w1.shape[1]
+        self.p = NDFilterParams(self.width, _ptr(w1), _ptr(b1), _ptr(w2), _ptr(b2), _ptr(w3), _ptr(b3),
+                                _ptr(window))
+        self.registers = 0
+        self.fp = NDFilmParams(0, _ptr(q), _ptr(film_w), _ptr(film_b), _ptr(omega0))
+
+
+def _film_args(m: HyenaNDFilm, u, reg, w_in, dskip, w_out, y, k_out, ws):
+    B = u.shape[0]
+    m.fp.registers = reg.shape[1]
+    if y is None:
+        y = torch.empty_like(u)
+    if ws is None:
+        need = hyena_nd_film_workspace_bytes(B, m.X, m.Y, m.Z, m.C, m.N, m.width, m.boundary)
+        ws = torch.empty(max(need, 1), dtype=torch.uint8, device=u.device)
+    args = [m.X, m.Y, m.Z, m.C, m.N, m.boundary, ctypes.byref(m.p), ctypes.byref(m.fp), _ptr(u), _ptr(reg),
+            _ptr(w_in), _ptr(dskip), _ptr(w_out), B, _ptr(y), _ptr(k_out), _ptr(ws), ws.numel(), _stream()]
+    return y, args
+
+
+def hyena_nd_film_fwd(m: HyenaNDFilm, u, reg, w_in, dskip, w_out, y=None, k_out=None, ws=None):
+    """Register-conditioned forward; reg [B, R, C]. k_out, if given, receives every
+    sample's kernel [B, N, C, MX, MY, MZ]."""
+    y, args = _film_args(m, u, reg, w_in, dskip, w_out, y, k_out, ws)
+    _check(lib().hyena_nd_film_fwd(*args), "hyena_nd_film_fwd")
+    return y
+
+
+def hyena_nd_film_fwd_profiled(m: HyenaNDFilm, u, reg, w_in, dskip, w_out, y, ws, events):
+    """hyena_nd_film_fwd recording five torch.cuda.Event (enable_timing=True) on the
+    current stream: before the kernel synthesis, after it, after the in-projection,
+    after the convolutions, after the out-projection. Does not synchronise."""
+    if len(events) != 5:
+        raise ValueError("hyena_nd_film_fwd_profiled takes 5 events")
+    for ev in events:
+        if not ev.cuda_event:
+            ev.record()
+    handles = (_vp * 5)(*[ev.cuda_event for ev in events])
+    y, args = _film_args(m, u, reg, w_in, dskip, w_out, y, None, ws)
+    _check(lib().hyena_nd_film_fwd_profiled(*args, handles), "hyena_nd_film_fwd_profiled")
+    return y

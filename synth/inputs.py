@@ -253,6 +253,8 @@ TEST_SHAPES = {
                                             u_scale=1 / math.sqrt(768), causal=False),
     # 2D image grids (X = 1): 64 x 64 patch grids at a ViT-Small width, zero padded
     "nd2d_f32_B8_C384_64sq": dict(kind="nd", seed=34, B=8, X=1, Y=64, Z=64, C=384, N=2),
+    # register-conditioned (FiLM) kernels, one per sample, on the 3D workload's grid
+    "nd3d_film_f32_B2_C128_64cube": dict(kind="nd_film", seed=35, B=2, X=64, Y=64, Z=64, C=128, N=2, W=64, R=4),
 }
 
 
@@ -261,6 +263,8 @@ def make_config(name: str):
     kind = cfg.pop("kind")
     if kind == "1d":
         return make_1d(**cfg)
+    if kind == "nd_film":
+        return make_nd_film(**cfg)
     return make_nd(**cfg)
 
 

@@ -5,7 +5,8 @@
 Calls only the fp64 oracle (oracle/) on the seeded inputs of synth/. For the
 1D workloads the orders before the last run on the whole sequence with the
 FFT path and the last order is summed directly at the sampled times; for the
-3D workload the same holds over the grid. Output: tests/golden/sampled_<name>.npz
+3D workloads the same holds over the grid (the register-conditioned one with
+each sample's own kernel). Output: tests/golden/sampled_<name>.npz
 with the sampled indices and y at those indices (float64).
 """
 import os
@@ -46,6 +47,13 @@ def make(name):
         y = oracle.hyena_fwd_sampled(inp.u, inp.w_in, inp.short_w, inp.dskip, inp.w_out, h, ts, chunk=16,
                                      causal=inp.causal)
         np.savez(out, t=ts, y=y)
+    elif cfg["kind"] == "nd_film":
+        pts = points_3d(inp.X, inp.Y, inp.Z, COUNT, cfg["seed"])
+        Ks = oracle.film_kernels(inp.film_filter_params, inp.reg, inp.q, inp.film_w, inp.film_b, inp.X, inp.Y,
+                                 inp.Z, inp.N, inp.C, inp.circular)
+        y = oracle.hyena_nd_film_fwd_sampled(inp.u, inp.w_in, inp.dskip, inp.w_out, Ks, pts, chunk=4,
+                                             circular=inp.circular)
+        np.savez(out, points=pts, y=y)
     else:
         pts = points_3d(inp.X, inp.Y, inp.Z, COUNT, cfg["seed"])
         K = oracle.nd_filter(inp.filter_params, inp.X, inp.Y, inp.Z, inp.N, inp.C, circular=inp.circular)

@@ -98,3 +98,33 @@ def oracle_nd(inp, conv: str = "fft"):
     y = oracle.hyena_nd_fwd(inp.u, inp.w_in, inp.dskip, inp.gate_a, inp.gate_b, inp.w_out, K, conv=conv,
                             circular=inp.circular)
     return y, K
+
+
+def gpu_nd_film(inp, with_k: bool = False):
+    """Runs hyena_nd_film_fwd on cuda:0; returns y (float64 numpy) [and the kernels
+    [B, N, C, MX, MY, MZ]]."""
+    import torch
+    import subquadratic_sequence_amd as hs
+    bd = hs.ND_CIRCULAR if inp.circular else hs.ND_ZERO_PAD
+    pf = 1 if inp.circular else 2
+    mx = 1 if inp.X == 1 else pf * inp.X
+    m = hs.HyenaNDFilm(inp.X, inp.Y, inp.Z, inp.C, inp.N, bd, to_dev(inp.w1), to_dev(inp.b1), to_dev(inp.w2),
+                       to_dev(inp.b2), to_dev(inp.w3), to_dev(inp.b3), to_dev(inp.window), to_dev(inp.q),
+                       to_dev(inp.film_w), to_dev(inp.film_b), to_dev(inp.omega0))
+    k_out = (torch.empty(inp.B, inp.N, inp.C, mx, pf * inp.Y, pf * inp.Z, device="cuda") if with_k else None)
+    y = hs.hyena_nd_film_fwd(m, to_dev(inp.u), to_dev(inp.reg), to_dev(inp.w_in), to_dev(inp.dskip),
+                             to_dev(inp.w_out), k_out=k_out)
+    torch.cuda.synchronize()
+    yn = y.cpu().numpy().astype(np.float64)
+    if with_k:
+        return yn, k_out.cpu().numpy().astype(np.float64)
+    return yn
+
+
+def oracle_nd_film(inp):
+    """(y, Ks) of the register-conditioned oracle on the same inputs."""
+    import oracle
+    Ks = oracle.film_kernels(inp.film_filter_params, inp.reg, inp.q, inp.film_w, inp.film_b, inp.X, inp.Y, inp.Z,
+                             inp.N, inp.C, inp.circular)
+    y = oracle.hyena_nd_film_fwd(inp.u, inp.w_in, inp.dskip, inp.w_out, Ks, circular=inp.circular)
+    return y, Ks

@@ -229,3 +229,44 @@ def test_direction_sizes_and_init(hy):
     assert L.hyena_filter_gen(ctypes.byref(layer), ctypes.byref(fp), None, p, need - 1, None) == 3
     layer.direction = 4
     assert L.hyena_filter_gen(ctypes.byref(layer), ctypes.byref(fp), None, p, need, None) == 2
+
+
+# ------------------------------------------------------------- register conditioning
+
+def test_film_workspace_sizes(hy):
+    al = lambda x: (x + 255) // 256 * 256  # noqa: E731
+    X = Y = Z = 64
+    C, N, W = 128, 2, 64
+    w1 = hy.hyena_nd_film_workspace_bytes(1, X, Y, Z, C, N, W, hy.ND_ZERO_PAD)
+    w2 = hy.hyena_nd_film_workspace_bytes(2, X, Y, Z, C, N, W, hy.ND_ZERO_PAD)
+    # at least one more sample's spectra N C 128 128 65 complex64 per extra sample
+    assert w2 - w1 >= al(N * C * 128 * 128 * 65 * 8)
+    assert hy.hyena_nd_film_workspace_bytes(2, X, Y, Z, C, N, W, hy.ND_CIRCULAR) < w2
+    # widths 1..128, batch >= 1, the shapes of the gated layer
+    assert hy.hyena_nd_film_workspace_bytes(2, X, Y, Z, C, N, 0, hy.ND_ZERO_PAD) == 0
+    assert hy.hyena_nd_film_workspace_bytes(2, X, Y, Z, C, N, 129, hy.ND_ZERO_PAD) == 0
+    assert hy.hyena_nd_film_workspace_bytes(0, X, Y, Z, C, N, W, hy.ND_ZERO_PAD) == 0
+    assert hy.hyena_nd_film_workspace_bytes(2, 4, 4, 4, 64, 1, W, hy.ND_CIRCULAR) == 0
+    assert hy.hyena_nd_film_workspace_bytes(2, 1, 32, 32, 64, 2, W, hy.ND_ZERO_PAD) > 0
+
+
+def test_film_argument_errors_before_any_hip_call(hy):
+    L = hy.lib()
+    keep, p = _aligned_buffer(16)
+    fp = hy.NDFilterParams(64, p, p, p, p, p, p, p)
+    film = hy.NDFilmParams(4, p, p, p, p)
+    need = hy.hyena_nd_film_workspace_bytes(2, 8, 8, 8, 64, 2, 64, hy.ND_ZERO_PAD)
+    args = (p, p, p, p, p)  # u, reg, w_in, dskip, w_out
+    call = lambda f, r, ws=need, B=2, bd=hy.ND_ZERO_PAD: L.hyena_nd_film_fwd(  # noqa: E731
+        8, 8, 8, 64, 2, bd, f, r, *args, B, p, None, p, ws, None)
+    assert call(None, ctypes.byref(film)) == 1
+    assert call(ctypes.byref(fp), None) == 1
+    assert call(ctypes.byref(fp), ctypes.byref(film), B=0) == 1
+    assert call(ctypes.byref(fp), ctypes.byref(film), bd=2) == 2
+    assert call(ctypes.byref(fp), ctypes.byref(hy.NDFilmParams(0, p, p, p, p))) == 2
+    assert call(ctypes.byref(fp), ctypes.byref(hy.NDFilmParams(1025, p, p, p, p))) == 2
+    assert call(ctypes.byref(hy.NDFilterParams(200, p, p, p, p, p, p, p)), ctypes.byref(film)) == 2
+    assert call(ctypes.byref(fp), ctypes.byref(hy.NDFilmParams(4, p, None, p, p))) == 1
+    assert call(ctypes.byref(fp), ctypes.byref(film), ws=need - 1) == 3
+    assert L.hyena_nd_film_fwd_profiled(8, 8, 8, 64, 2, 0, ctypes.byref(fp), ctypes.byref(film), *args, 2, p, None,
+                                        p, need, None, None) == 1
