@@ -292,6 +292,126 @@ def main_nd(args, torch, hs, make_config):
     print(json.dumps(out), flush=True)
 
 
+def nd_film_conv_alg_bytes(B, X, Y, Z, C, N, circular: bool = False) -> float:
+    """nd_conv_alg_bytes with per-sample kernels: every sample reads its own spectra."""
+    V = X * Y * Z
+    p = 1 if circular else 2
+    spec = 8.0 * C * (1 if X == 1 else p * X) * (p * Y) * (p * Z // 2 + 1)
+    if X == 1:
+        return (N + 2) * B * C * V * 4.0 + N * B * spec
+    return N * (3.0 * B * C * V * 4 + B * spec)
+
+
+def film_mlp_flops(X, Y, Z, C, N, W, circular: bool = False) -> float:
+    """Flops of one sample's coordinate MLP over the offset grid (3 -> W -> W -> N C)."""
+    p = 1 if circular else 2
+    P = (1 if X == 1 else p * X) * (p * Y) * (p * Z)
+    return 2.0 * P * (3 * W + W * W + W * N * C)
+
+
+def cpu_baseline_nd_film(inp, channels: int):
+    """fp64 oracle of the register-conditioned layer on one sample and the first
+    `channels` channels (kernel outputs and projections restricted to them; the
+    control vector and FiLM vectors from all channels), full grid, 1 thread. The
+    kernel synthesis is inside the timed region, as on the GPU; voxel rate scaled
+    by channels / C."""
+    import oracle
+    from threadpoolctl import threadpool_limits
+    c = min(channels, inp.C)
+    N = inp.N
+    w_in = np.concatenate([inp.w_in[:c, j * inp.C:j * inp.C + c] for j in range(N + 1)], axis=1)
+    params = dict(inp.film_filter_params)
+    params["w3"] = np.concatenate([params["w3"][:, n * inp.C:n * inp.C + c] for n in range(N)], axis=1)
+    params["b3"] = np.concatenate([params["b3"][n * inp.C:n * inp.C + c] for n in range(N)])
+    params["window"] = params["window"][:c]
+    with threadpool_limits(limits=1):
+        t0 = time.perf_counter()
+        mod = oracle.film_modulation(oracle.film_control(inp.reg[:1], inp.q), inp.film_w, inp.film_b)
+        K = oracle.nd_filter_film(params, mod[0], inp.X, inp.Y, inp.Z, N, c, circular=inp.circular)
+        oracle.hyena_nd_film_fwd(inp.u[:1, ..., :c], w_in, inp.dskip[:, :c], inp.w_out[:c, :c], K[None],
+                                 circular=inp.circular)
+        dt = time.perf_counter() - t0
+    V = inp.X * inp.Y * inp.Z
+    return {"value": V / dt * c / inp.C, "unit": "voxels/s", "cores": 1, "kind": "oracle",
+            "sample": f"sample 0 of {inp.B}, channels 0..{c - 1} of {inp.C} (kernel outputs and projections "
+                      f"restricted to them), full {inp.X}x{inp.Y}x{inp.Z} grid, fp64 numpy, kernel synthesis "
+                      f"and FFT path, 1 thread, {dt:.1f} s; rate scaled by {c}/{inp.C}"}
+
+
+def main_nd_film(args, torch, hs, make_config):
+    log(f"generating inputs for {args.workload}")
+    inp = make_config(args.workload)
+    B, X, Y, Z, C, N, W = inp.B, inp.X, inp.Y, inp.Z, inp.C, inp.N, inp.W
+    V = X * Y * Z
+    f = lambda a: torch.from_numpy(np.ascontiguousarray(a, np.float32)).to("cuda")  # noqa: E731
+    bd = hs.ND_CIRCULAR if inp.circular else hs.ND_ZERO_PAD
+    m = hs.HyenaNDFilm(X, Y, Z, C, N, bd, *(f(a) for a in (inp.w1, inp.b1, inp.w2, inp.b2, inp.w3, inp.b3,
+                                                             inp.window, inp.q, inp.film_w, inp.film_b,
+                                                             inp.omega0)))
+    u, reg, w_in, dskip, w_out = (f(a) for a in (inp.u, inp.reg, inp.w_in, inp.dskip, inp.w_out))
+    y = torch.empty_like(u)
+    ws = torch.empty(hs.hyena_nd_film_workspace_bytes(B, X, Y, Z, C, N, W, bd), dtype=torch.uint8, device="cuda")
+    torch.cuda.synchronize()
+    log(f"warmup {args.warmup}")
+    for _ in range(args.warmup):
+        hs.hyena_nd_film_fwd(m, u, reg, w_in, dskip, w_out, y=y, ws=ws)
+    torch.cuda.synchronize()
+    events = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(args.steps)]
+    for evs in events:
+        for ev in evs:
+            ev.record()
+    torch.cuda.synchronize()
+    log(f"timing {args.steps} steps")
+    t0 = time.perf_counter()
+    for k in range(args.steps):
+        hs.hyena_nd_film_fwd_profiled(m, u, reg, w_in, dskip, w_out, y, ws, events[k])
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    st = np.mean([[evs[i].elapsed_time(evs[i + 1]) for i in range(4)] for evs in events], axis=0)
+    step_ms = np.array([evs[0].elapsed_time(evs[4]) for evs in events])
+    log(f"stages ms: synthesis {st[0]:.4f} in-proj {st[1]:.4f} conv {st[2]:.4f} out-proj {st[3]:.4f}")
+    alg = nd_film_conv_alg_bytes(B, X, Y, Z, C, N, inp.circular)
+    achieved = alg / (st[2] * 1e-3) / 1e9
+    mlp = B * film_mlp_flops(X, Y, Z, C, N, W, inp.circular)
+    proj = {}
+    for name, n_out, ms in (("in_proj", (N + 1) * C, st[1]), ("out_proj", C, st[3])):
+        tf = 2.0 * B * V * n_out * C / (ms * 1e-3) / 1e12
+        proj[name] = {"tflops": tf, "peak": MFMA_F32_PEAK_TFLOPS, "frac": tf / MFMA_F32_PEAK_TFLOPS}
+    out = {
+        "metric": (f"HyenaND fwd voxels/sec (3D, B={B}, C={C}, {X}x{Y}x{Z}"
+                   f"{', circular' if inp.circular else ''}, register-conditioned FiLM kernels synthesised "
+                   f"per sample in every step, 1 GPU); 3D FFT-conv HBM GB/s % of peak"),
+        "value": B * V * args.steps / elapsed,
+        "unit": "voxels/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": 1e3 * elapsed / args.steps,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {"workload": args.workload, "B": B, "X": X, "Y": Y, "Z": Z, "C": C, "N": N, "W": W,
+                   "registers": int(inp.reg.shape[1]), "boundary": "circular" if inp.circular else "zero-padded"},
+        "stage_ms": {"kernel_synthesis": st[0], "in_proj": st[1], "fft_conv": st[2], "out_proj": st[3]},
+        "step_ms_events": {"p10": float(np.percentile(step_ms, 10)), "p50": float(np.median(step_ms)),
+                           "p90": float(np.percentile(step_ms, 90))},
+        "roofline": {"bound": "hbm", "kernel": "3D fft_conv stage (all orders, every sample with its own spectra)",
+                     "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS,
+                     "alg_bytes": alg, "traffic": measured_traffic(args.workload)},
+        "kernel_synthesis": {"ms": st[0], "mlp_gflop": mlp / 1e9,
+                             "mlp_tflops_if_whole_stage": mlp / (st[0] * 1e-3) / 1e12,
+                             "mfma_f32_peak_tflops": MFMA_F32_PEAK_TFLOPS},
+        "projections_mfma": proj,
+        "copy_probe_gbs": copy_probe(torch),
+    }
+    if not args.no_cpu_baseline:
+        log("cpu baseline (oracle)")
+        out["cpu_baseline"] = cpu_baseline_nd_film(inp, args.cpu_channels or 4)
+    print(json.dumps(out), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -331,6 +451,8 @@ def main():
     cfg = CONFIGS.get(args.workload) or TEST_SHAPES[args.workload]
     if cfg["kind"] == "nd":
         return main_nd(args, torch, hs, make_config)
+    if cfg["kind"] == "nd_film":
+        return main_nd_film(args, torch, hs, make_config)
     log(f"generating inputs for {args.workload}")
     inp = make_config(args.workload)
     B, L, D, N = inp.B, inp.L, inp.D, inp.N
