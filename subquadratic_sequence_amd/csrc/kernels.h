@@ -91,6 +91,9 @@ struct NdFilterArgs {
   // [4][W] = omega0 * gamma_1, beta_1, gamma_2, beta_2 of one sample; `decay`
   // then holds the Gaussian window rates
   const float* film = nullptr;
+  // set by nd_filter: the matrix-core MLP writes the wrapped channel-pair fields
+  // of the transform here (F = K_{2cp} + i K_{2cp+1}) instead of `k`
+  float2* fdirect = nullptr;
 };
 // control vector and FiLM vectors of every sample: mod [B][4][W]
 hipError_t nd_film_mod(const float* reg, const float* q, const float* film_w, const float* film_b,
@@ -111,7 +114,11 @@ struct NdConvArgs {
   const float2* kh;      // half spectra [N*C][MX][MY][MZ/2+1]
   const float2* tw128;   // W_128^m
 };
-hipError_t nd_filter(const NdFilterArgs& f, float2* F, float2* kh, const float2* tw128, hipStream_t s);
+// Kernel spectra kh from the MLP. F: the transform buffer (N C / 2 pair fields).
+// keep_k: also leave the offset-indexed kernel in f.k (otherwise f.k may be
+// unused: the 64- and 128-wide MLPs write F directly).
+hipError_t nd_filter(const NdFilterArgs& f, float2* F, float2* kh, const float2* tw128, hipStream_t s,
+                     bool keep_k = true);
 hipError_t nd_gate(const float* u, float* part, const float* ga, const float* gb, float* gate, int B, int NO, int C,
                    int V, hipStream_t s);
 size_t nd_gate_partial_floats(int B, int C, int V);

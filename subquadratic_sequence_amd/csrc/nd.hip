@@ -97,11 +97,16 @@ __global__ __launch_bounds__(256) void nd_mlp_kernel(NdFilterArgs a) {
 // W3 in registers and the next block's slice in flight.
 typedef __attribute__((ext_vector_type(16))) float f32x16;
 
-template <int WW, bool FILM>
+// DIRECT: the output goes to the transform's wrapped channel-pair fields
+// a.fdirect[pair][w] = (K_{2 pair}, K_{2 pair + 1}) at w = (offset + M/2) mod M
+// per axis, the layout nd_pack_kernel produces; lanes holding columns 2 pair and
+// 2 pair + 1 are neighbours and swap halves of their four points.
+template <int WW, bool FILM, bool DIRECT>
 __global__ __launch_bounds__(256) void nd_mlp_mfma_kernel(NdFilterArgs a) {
   constexpr int LDH = WW + 1;
   constexpr int KW = WW / 2;
   __shared__ float cs[kNP][5];  // the three coordinates, a zero pad column, the radius (FILM: its square)
+  __shared__ int fidx[kNP];     // DIRECT: index of the point in the wrapped transform field
   __shared__ float buf0[kNP * LDH];  // layer 2
   __shared__ float buf1[kNP * LDH];  // layer 1
   const int MX = a.MX, MY = a.MY, MZ = a.MZ;
@@ -121,6 +126,7 @@ __global__ __launch_bounds__(256) void nd_mlp_mfma_kernel(NdFilterArgs a) {
     cs[t][3] = 0.f;
     const float r2 = cx * cx + cy * cy + cz * cz;
     cs[t][4] = FILM ? r2 : sqrtf(r2);
+    if (DIRECT) fidx[t] = (((i + MX / 2) % MX) * MY + (j + MY / 2) % MY) * MZ + (k + MZ / 2) % MZ;
   }
   __syncthreads();
   auto zero = [](f32x16& c) {
@@ -187,6 +193,8 @@ __global__ __launch_bounds__(256) void nd_mlp_mfma_kernel(NdFilterArgs a) {
     const float bias = a.b3[col];
     const float dc = a.decay[col % a.C];
     float* dst = a.k + (size_t)col * P + p0;  // K[n][c][i][j][k], col = n C + c
+    const bool odd = col & 1;
+    float* fdst = reinterpret_cast<float*>(a.fdirect + (size_t)(col >> 1) * P);
 #pragma unroll
     for (int rb = 0; rb < 2; ++rb) {
 #pragma unroll
@@ -195,7 +203,17 @@ __global__ __launch_bounds__(256) void nd_mlp_mfma_kernel(NdFilterArgs a) {
         float o[4];
 #pragma unroll
         for (int i = 0; i < 4; ++i) o[i] = ((rb ? acc1[4 * g + i] : acc0[4 * g + i]) + bias) * expf(-dc * cs[t + i][4]);
-        *reinterpret_cast<float4*>(dst + t) = make_float4(o[0], o[1], o[2], o[3]);
+        if (DIRECT) {
+          // the four points sit at consecutive field indices (M/2 is a multiple
+          // of 4); the even column's lane stores points 0-1, the odd one's 2-3
+          float pv[4];
+#pragma unroll
+          for (int i = 0; i < 4; ++i) pv[i] = __shfl_xor(o[i], 1);
+          const float4 v = odd ? make_float4(pv[2], o[2], pv[3], o[3]) : make_float4(o[0], pv[0], o[1], pv[1]);
+          *reinterpret_cast<float4*>(fdst + 2 * (size_t)fidx[t] + (odd ? 4 : 0)) = v;
+        } else {
+          *reinterpret_cast<float4*>(dst + t) = make_float4(o[0], o[1], o[2], o[3]);
+        }
       }
     }
     if (!more) break;
@@ -1163,24 +1181,35 @@ static hipError_t launch_pencil(const NdConvArgs& a, dim3 grid, hipStream_t s) {
   return launch_pencil_p<MODE, 2>(a, grid, s);
 }
 
-hipError_t nd_filter(const NdFilterArgs& f, float2* F, float2* kh, const float2* tw128, hipStream_t s) {
+hipError_t nd_filter(const NdFilterArgs& fin, float2* F, float2* kh, const float2* tw128, hipStream_t s,
+                     bool keep_k) {
+  NdFilterArgs f = fin;
   const int MX = f.MX, MY = f.MY, MZ = f.MZ;
   const size_t P = (size_t)MX * MY * MZ;
   const dim3 g((unsigned)(P / kNP));
   const bool film = f.film != nullptr;
+  const bool direct = !keep_k && (f.W == 64 || f.W == 128);
+  f.fdirect = direct ? F : nullptr;
   using MlpFn = void (*)(NdFilterArgs);
   MlpFn fn;
-  if (f.W == 64) fn = film ? nd_mlp_mfma_kernel<64, true> : nd_mlp_mfma_kernel<64, false>;
-  else if (f.W == 128) fn = film ? nd_mlp_mfma_kernel<128, true> : nd_mlp_mfma_kernel<128, false>;
-  else fn = film ? nd_mlp_kernel<true> : nd_mlp_kernel<false>;
+  if (f.W == 64)
+    fn = direct ? (film ? nd_mlp_mfma_kernel<64, true, true> : nd_mlp_mfma_kernel<64, false, true>)
+                : (film ? nd_mlp_mfma_kernel<64, true, false> : nd_mlp_mfma_kernel<64, false, false>);
+  else if (f.W == 128)
+    fn = direct ? (film ? nd_mlp_mfma_kernel<128, true, true> : nd_mlp_mfma_kernel<128, false, true>)
+                : (film ? nd_mlp_mfma_kernel<128, true, false> : nd_mlp_mfma_kernel<128, false, false>);
+  else
+    fn = film ? nd_mlp_kernel<true> : nd_mlp_kernel<false>;
   hipLaunchKernelGGL(fn, g, dim3(256), 0, s, f);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   const int npairs = f.N * f.C / 2;
   const size_t tot = P * npairs;
-  hipLaunchKernelGGL(nd_pack_kernel, dim3((unsigned)((tot + 255) / 256)), dim3(256), 0, s, (const float*)f.k, F,
-                     MX, MY, MZ, npairs);
-  if ((e = hipGetLastError()) != hipSuccess) return e;
+  if (!direct) {
+    hipLaunchKernelGGL(nd_pack_kernel, dim3((unsigned)((tot + 255) / 256)), dim3(256), 0, s, (const float*)f.k, F,
+                       MX, MY, MZ, npairs);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+  }
   NdConvArgs a{};
   a.X = f.X;
   a.Y = f.Y;

@@ -185,7 +185,7 @@ int hyena_nd_filter_gen(hyena_nd_layer* layer, const hyena_nd_filter_params* p, 
                      pd * Z, p->w1, p->b1, p->w2, p->b2, p->w3,    p->b3,    p->decay,
                      k_out ? k_out : reinterpret_cast<float*>(wsb + fw.k)};
   HY_CHECK_HIP(hy::nd_filter(f, reinterpret_cast<float2*>(wsb + fw.F), reinterpret_cast<float2*>(cb + cl.kh), tw,
-                             stream));
+                             stream, k_out != nullptr));
   layer->built = 1;
   return HYENA_OK;
 }
@@ -346,7 +346,7 @@ int film_fwd_impl(int X, int Y, int Z, int C, int N, int bd, const hyena_nd_filt
                        k_out ? k_out + (size_t)b * N * C * P : reinterpret_cast<float*>(fbase + fl.k)};
     f.film = mod + (size_t)b * 4 * W;
     HY_CHECK_HIP(hy::nd_filter(f, reinterpret_cast<float2*>(fbase + fl.F),
-                               reinterpret_cast<float2*>(wsb + fw.kh + b * khs), tw, stream));
+                               reinterpret_cast<float2*>(wsb + fw.kh + b * khs), tw, stream, k_out != nullptr));
   }
   if (ev) HY_CHECK_HIP(hipEventRecord(ev[1], stream));
 
