@@ -39,7 +39,7 @@ DEFAULT_WORKLOAD = "order2_bf16_L64k_D768"
 # Kernel sources of the long-convolution stage; a traffic figure measured on other
 # sources is stale and is not reported.
 CONV_SOURCES = ["fft1d.hip", "common.h", "kernels.h"]
-ND_CONV_SOURCES = ["nd.hip", "common.h", "kernels.h"]
+ND_CONV_SOURCES = ["nd.hip", "common.h", "kernels_nd.h"]
 METRIC = "Hyena fwd tokens/sec at L=64k,D=768 (1 GPU); FFT-conv HBM GB/s % of peak"
 HBM_PEAK_GBS = 8000.0
 MFMA_BF16_PEAK_TFLOPS = 2516.6  # 256 CUs x 2.4 GHz x 4096 flop/clk (dense)

@@ -23,7 +23,7 @@
 // order's forward plane DFT from the same LDS plane. With the circular boundary
 // the same passes run with no zero padding and no crop (M = G).
 #include "common.h"
-#include "kernels.h"
+#include "kernels_nd.h"
 
 namespace hy {
 

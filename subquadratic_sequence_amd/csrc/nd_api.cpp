@@ -6,6 +6,7 @@
 
 #include "common.h"
 #include "kernels.h"
+#include "kernels_nd.h"
 
 using hy::align_up;
 
