@@ -41,6 +41,11 @@ struct NdConvArgs {
   float2* Yint;          // [ceil(B/2)][C][X][MY][MZ]
   float2* F;             // filter pairs [N*C/2][MX][MY][MZ]
   const float2* kh;      // half spectra [N*C][MX][MY][MZ/2+1]
+  // float2 elements between consecutive samples' spectra in kh; 0: one set of
+  // spectra shared by every sample. Non-zero (per-sample kernels, 3D grids):
+  // the pencil pass filters the two samples of a packed field with their own
+  // kernels through the (P, Q) form.
+  size_t kh_stride;
   const float2* tw128;   // W_128^m
 };
 // Kernel spectra kh from the MLP. F: the transform buffer (N C / 2 pair fields).

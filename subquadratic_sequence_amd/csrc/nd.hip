@@ -1152,6 +1152,147 @@ static hipError_t launch_plane(const NdConvArgs& a, dim3 grid, hipStream_t s) {
   }
 }
 
+// Pencil pass with a kernel per sample. The packed field F = Z_b0 + i Z_b1
+// holds two samples whose real kernels differ, so the product is
+//   Y(k) = P(k) F(k) + Q(k) conj(F(-k)),  P = (K_b0 + K_b1) / 2,  Q = (K_b0 - K_b1) / 2,
+// whose inverse transform is (K_b0 * z_b0) + i (K_b1 * z_b1). F(-k) of pencil
+// (ky, kz) lies on the mirror pencil (-ky, -kz) at -kx, so each lane takes a
+// pencil and its mirror: both forward DFTs over x land in two [N1][64] LDS
+// buffers; the thread owning kx reads A(kx) and B(-kx), which are exactly the
+// inputs of pencil A's product at kx and pencil B's at -kx, and writes both
+// back in place (no other thread reads those two slots); then both inverse DFTs.
+// Each pair is taken once: lanes cover rows ky in [0, MY/2]; on rows 0 and MY/2
+// (their own mirrors) only kz <= MZ/2 is active, the other lanes compute on
+// pencil 0 and store nothing. Grid (ceil((MY/2 + 1) MZ / 64), C, sample pairs).
+template <int RA, int RB, int PAD>
+__global__ __launch_bounds__(64 * RA) void nd_pencil_pq_kernel(NdConvArgs a) {
+  constexpr int N1 = RA * RB;
+  extern __shared__ float4 smem4[];
+  float2* SA = reinterpret_cast<float2*>(smem4);  // [N1][64]: stage buffer, then pencil A's spectrum
+  float2* SB = SA + N1 * 64;                      // the same for the mirror pencil B
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const int X = a.X, MY = a.MY, MZ = a.MZ, ZH = MZ / 2 + 1;
+  const size_t plane = (size_t)MY * MZ;
+  const int c = blockIdx.y, bp = blockIdx.z;
+  const int fl = blockIdx.x * 64 + lane;
+  const int kyl = fl / MZ, kzl = fl % MZ;
+  const bool active = fl < (MY / 2 + 1) * MZ && !((kyl == 0 || kyl == MY / 2) && kzl > MZ / 2);
+  const int f = active ? fl : 0;
+  const int ky = f / MZ, kz = f % MZ;
+  const int kyb = (MY - ky) % MY, kzb = (MZ - kz) % MZ;
+  const int fb = kyb * MZ + kzb;
+  float2* base = a.Yint + (((size_t)bp * a.C + c) * X) * plane;
+  const int b0 = 2 * bp, b1 = b0 + 1 < a.B ? b0 + 1 : b0;
+  const size_t kofs = (size_t)(a.n * a.C + c) * N1 * MY * ZH;
+  const float2* K0 = a.kh + (size_t)b0 * a.kh_stride + kofs;
+  const float2* K1 = a.kh + (size_t)b1 * a.kh_stride + kofs;
+  // K^(kx, y, z) from the conjugate-symmetric half spectrum
+  auto kval = [&](const float2* K, int kx, int y, int z) {
+    const bool lower = z <= MZ / 2;
+    const int x2 = lower ? kx : (N1 - kx) % N1, y2 = lower ? y : (MY - y) % MY, z2 = lower ? z : MZ - z;
+    const float2 v = K[((size_t)x2 * MY + y2) * ZH + z2];
+    return lower ? v : conjf2(v);
+  };
+  // forward DFT over x of pencil g into D[kx][lane] (D is also its stage buffer)
+  auto forward = [&](int g, float2* D) {
+    float2 v[RB];
+#pragma unroll
+    for (int r = 0; r < RB; ++r) v[r] = (r < RB / PAD) ? base[(size_t)(w + RA * r) * plane + g] : make_float2(0.f, 0.f);
+    Dft<RB, false>::run(v);
+#pragma unroll
+    for (int ka = 0; ka < RB; ++ka) {
+      if (ka) v[ka] = cmul(v[ka], a.tw128[(w * ka * (128 / N1)) & 127]);
+      D[(w * RB + ka) * 64 + lane] = v[ka];
+    }
+    __syncthreads();
+    float2 u[RA];
+    if (w < RB) {
+#pragma unroll
+      for (int j = 0; j < RA; ++j) u[j] = D[(j * RB + w) * 64 + lane];
+      Dft<RA, false>::run(u);
+    }
+    __syncthreads();
+    if (w < RB) {
+#pragma unroll
+      for (int kb = 0; kb < RA; ++kb) D[(w + RB * kb) * 64 + lane] = u[kb];
+    }
+  };
+  // inverse DFT over x of the spectrum in D[kx][lane] (threads w < RB take
+  // kx = w + RB kb), SA as stage buffer, stored to pencil g (x < X)
+  auto inverse = [&](const float2* D, int g) {
+    float2 y[RA];
+    if (w < RB) {
+#pragma unroll
+      for (int kb = 0; kb < RA; ++kb) y[kb] = D[(w + RB * kb) * 64 + lane];
+    }
+    __syncthreads();  // D read before SA is written
+    if (w < RB) {
+      Dft<RA, true>::run(y);
+#pragma unroll
+      for (int na = 1; na < RA; ++na) y[na] = cmulc(y[na], a.tw128[(w * na * (128 / N1)) & 127]);
+#pragma unroll
+      for (int na = 0; na < RA; ++na) SA[(w * RA + na) * 64 + lane] = y[na];
+    }
+    __syncthreads();
+    float2 q[RB];
+#pragma unroll
+    for (int ka = 0; ka < RB; ++ka) q[ka] = SA[(ka * RA + w) * 64 + lane];
+    Dft<RB, true>::run(q);
+    if (active) {
+#pragma unroll
+      for (int nb = 0; nb < RB / PAD; ++nb) base[(size_t)(w + RA * nb) * plane + g] = q[nb];
+    }
+    __syncthreads();  // SA read before its next use
+  };
+
+  forward(f, SA);
+  forward(fb, SB);
+  __syncthreads();
+  if (w < RB) {
+#pragma unroll
+    for (int kb = 0; kb < RA; ++kb) {
+      const int kx = w + RB * kb, km = (N1 - kx) % N1;
+      const float2 A = SA[kx * 64 + lane], Bm = SB[km * 64 + lane];
+      // pencil A at k = (kx, ky, kz)
+      const float2 p0 = kval(K0, kx, ky, kz), p1 = kval(K1, kx, ky, kz);
+      const float2 P = make_float2(0.5f * (p0.x + p1.x), 0.5f * (p0.y + p1.y));
+      const float2 Q = make_float2(0.5f * (p0.x - p1.x), 0.5f * (p0.y - p1.y));
+      // pencil B at k' = (-kx, -ky, -kz): its own value B(-kx), partner A(kx)
+      const float2 m0 = kval(K0, km, kyb, kzb), m1 = kval(K1, km, kyb, kzb);
+      const float2 Pm = make_float2(0.5f * (m0.x + m1.x), 0.5f * (m0.y + m1.y));
+      const float2 Qm = make_float2(0.5f * (m0.x - m1.x), 0.5f * (m0.y - m1.y));
+      SA[kx * 64 + lane] = cadd(cmul(A, P), cmul(conjf2(Bm), Q));
+      SB[km * 64 + lane] = cadd(cmul(Bm, Pm), cmul(conjf2(A), Qm));
+    }
+  }
+  __syncthreads();
+  inverse(SA, f);
+  inverse(SB, fb);
+}
+
+template <int RA, int RB, int PAD>
+static hipError_t launch_pencil_pq_t(const NdConvArgs& a, hipStream_t s) {
+  const size_t lds = (size_t)2 * RA * RB * 64 * 8;
+  auto fn = nd_pencil_pq_kernel<RA, RB, PAD>;
+  hipError_t e = nd_allow_lds((const void*)fn, lds);
+  if (e != hipSuccess) return e;
+  const unsigned nb = (unsigned)(((a.MY / 2 + 1) * a.MZ + 63) / 64);
+  hipLaunchKernelGGL(fn, dim3(nb, a.C, (a.B + 1) / 2), dim3(64 * RA), lds, s, a);
+  return hipGetLastError();
+}
+
+template <int PAD>
+static hipError_t launch_pencil_pq_p(const NdConvArgs& a, hipStream_t s) {
+  switch (a.MX) {
+    case 8: return launch_pencil_pq_t<4, 2, PAD>(a, s);
+    case 16: return launch_pencil_pq_t<4, 4, PAD>(a, s);
+    case 32: return launch_pencil_pq_t<8, 4, PAD>(a, s);
+    case 64: return launch_pencil_pq_t<8, 8, PAD>(a, s);
+    case 128: return launch_pencil_pq_t<16, 8, PAD>(a, s);
+    default: return hipErrorInvalidValue;
+  }
+}
+
 template <int RA, int RB, int MODE, int PAD>
 static hipError_t launch_pencil_t(const NdConvArgs& a, dim3 grid, hipStream_t s) {
   const size_t lds = (size_t)RA * RB * 64 * 8;
@@ -1326,7 +1467,9 @@ hipError_t nd_conv(const NdConvArgs& in, hipStream_t s) {
   if (e != hipSuccess) return e;
   for (int n = 0; n < a.NO; ++n) {
     a.n = n;
-    if (a.MX == 128 && a.MX == 2 * a.X) {
+    if (a.kh_stride != 0) {
+      e = a.MX == a.X ? launch_pencil_pq_p<1>(a, s) : launch_pencil_pq_p<2>(a, s);
+    } else if (a.MX == 128 && a.MX == 2 * a.X) {
       e = launch_pencil128(a, (int)(nf * a.C * BP), s);
     } else {
       e = launch_pencil<PN_CONV>(a, dim3(nf, a.C, BP), s);

@@ -363,10 +363,13 @@ int film_fwd_impl(int X, int Y, int Z, int C, int N, int bd, const hyena_nd_filt
   HY_CHECK_HIP(hy::gemm(gi, false, stream));
   if (ev) HY_CHECK_HIP(hipEventRecord(ev[2], stream));
 
-  // one sample per launch sequence (a lone sample fills one half of the packed
-  // complex field), each with its own spectra; unit gates
-  HY_CHECK_HIP(hy::fill(ones, (size_t)N * C, 1.f, stream));
-  for (int b = 0; b < B; ++b) {
+  // unit gates. 3D grids: two samples per packed complex field as in
+  // hyena_nd_fwd, the pencil pass filtering each half with its own sample's
+  // spectra ((P, Q) form). 2D grids (fused plane kernel, one spectrum per
+  // channel): one sample per launch, alone in its field.
+  HY_CHECK_HIP(hy::fill(ones, (size_t)B * N * C, 1.f, stream));
+  const bool packed = X > 1;
+  for (int b = 0; b < (packed ? 1 : B); ++b) {
     hy::NdConvArgs a{};
     a.X = X;
     a.Y = Y;
@@ -376,7 +379,7 @@ int film_fwd_impl(int X, int Y, int Z, int C, int N, int bd, const hyena_nd_filt
     a.MZ = MZ;
     a.C = C;
     a.NO = N;
-    a.B = 1;
+    a.B = packed ? B : 1;
     a.p = pbuf + (size_t)b * J * V;
     a.dskip = dskip;
     a.gate = ones;
@@ -385,6 +388,7 @@ int film_fwd_impl(int X, int Y, int Z, int C, int N, int bd, const hyena_nd_filt
     a.zfinal = zfin + (size_t)b * C * V;
     a.Yint = reinterpret_cast<float2*>(base + w.Y);
     a.kh = reinterpret_cast<const float2*>(wsb + fw.kh + b * khs);
+    a.kh_stride = packed ? khs / sizeof(float2) : 0;
     a.tw128 = tw;
     HY_CHECK_HIP(hy::nd_conv(a, stream));
   }
