@@ -1164,7 +1164,13 @@ static hipError_t launch_plane(const NdConvArgs& a, dim3 grid, hipStream_t s) {
 // Each pair is taken once: lanes cover rows ky in [0, MY/2]; on rows 0 and MY/2
 // (their own mirrors) only kz <= MZ/2 is active, the other lanes compute on
 // pencil 0 and store nothing. Grid (ceil((MY/2 + 1) MZ / 64), C, sample pairs).
-template <int RA, int RB, int PAD>
+// SPLIT: the kernel-spectrum pass instead. F = K_a + i K_b is a channel pair's
+// full field (all N1 x inputs); after the forward DFTs the thread owning kx
+// forms both channels' half spectra, Ka = (F(k) + conj F(-k)) / 2 and
+// Kb = (F(k) - conj F(-k)) / 2i scaled by 1 / (MX MY MZ), for pencil A at kx and
+// pencil B at -kx wherever kz <= MZ/2, into a.kh; no inverse. Grid
+// (ceil((MY/2 + 1) MZ / 64), channel pairs).
+template <int RA, int RB, int PAD, bool SPLIT>
 __global__ __launch_bounds__(64 * RA) void nd_pencil_pq_kernel(NdConvArgs a) {
   constexpr int N1 = RA * RB;
   extern __shared__ float4 smem4[];
@@ -1181,7 +1187,7 @@ __global__ __launch_bounds__(64 * RA) void nd_pencil_pq_kernel(NdConvArgs a) {
   const int ky = f / MZ, kz = f % MZ;
   const int kyb = (MY - ky) % MY, kzb = (MZ - kz) % MZ;
   const int fb = kyb * MZ + kzb;
-  float2* base = a.Yint + (((size_t)bp * a.C + c) * X) * plane;
+  float2* base = SPLIT ? a.F + (size_t)c * N1 * plane : a.Yint + (((size_t)bp * a.C + c) * X) * plane;
   const int b0 = 2 * bp, b1 = b0 + 1 < a.B ? b0 + 1 : b0;
   const size_t kofs = (size_t)(a.n * a.C + c) * N1 * MY * ZH;
   const float2* K0 = a.kh + (size_t)b0 * a.kh_stride + kofs;
@@ -1248,6 +1254,32 @@ __global__ __launch_bounds__(64 * RA) void nd_pencil_pq_kernel(NdConvArgs a) {
   forward(f, SA);
   forward(fb, SB);
   __syncthreads();
+  if constexpr (SPLIT) {
+    if (w < RB && active) {
+      const size_t PH = (size_t)N1 * MY * ZH;
+      float2* Ka = const_cast<float2*>(a.kh) + (size_t)(2 * c) * PH;
+      float2* Kb = Ka + PH;
+      const float sc = 0.5f / (float)((size_t)N1 * plane);
+#pragma unroll
+      for (int kb = 0; kb < RA; ++kb) {
+        const int kx = w + RB * kb, km = (N1 - kx) % N1;
+        const float2 A = SA[kx * 64 + lane], Bm = SB[km * 64 + lane];
+        if (kz <= MZ / 2) {  // pencil A at (kx, ky, kz): partner conj(B(-kx))
+          const float2 fm = conjf2(Bm), h = cadd(A, fm), d = csub(A, fm);
+          const size_t o = ((size_t)kx * MY + ky) * ZH + kz;
+          Ka[o] = make_float2(sc * h.x, sc * h.y);
+          Kb[o] = make_float2(sc * d.y, -sc * d.x);
+        }
+        if (kzb <= MZ / 2) {  // pencil B at (-kx, -ky, -kz): partner conj(A(kx))
+          const float2 fm = conjf2(A), h = cadd(Bm, fm), d = csub(Bm, fm);
+          const size_t o = ((size_t)km * MY + kyb) * ZH + kzb;
+          Ka[o] = make_float2(sc * h.x, sc * h.y);
+          Kb[o] = make_float2(sc * d.y, -sc * d.x);
+        }
+      }
+    }
+    return;
+  }
   if (w < RB) {
 #pragma unroll
     for (int kb = 0; kb < RA; ++kb) {
@@ -1270,25 +1302,26 @@ __global__ __launch_bounds__(64 * RA) void nd_pencil_pq_kernel(NdConvArgs a) {
   inverse(SB, fb);
 }
 
-template <int RA, int RB, int PAD>
+template <int RA, int RB, int PAD, bool SPLIT>
 static hipError_t launch_pencil_pq_t(const NdConvArgs& a, hipStream_t s) {
   const size_t lds = (size_t)2 * RA * RB * 64 * 8;
-  auto fn = nd_pencil_pq_kernel<RA, RB, PAD>;
+  auto fn = nd_pencil_pq_kernel<RA, RB, PAD, SPLIT>;
   hipError_t e = nd_allow_lds((const void*)fn, lds);
   if (e != hipSuccess) return e;
   const unsigned nb = (unsigned)(((a.MY / 2 + 1) * a.MZ + 63) / 64);
-  hipLaunchKernelGGL(fn, dim3(nb, a.C, (a.B + 1) / 2), dim3(64 * RA), lds, s, a);
+  const dim3 grid = SPLIT ? dim3(nb, a.npairs, 1) : dim3(nb, a.C, (a.B + 1) / 2);
+  hipLaunchKernelGGL(fn, grid, dim3(64 * RA), lds, s, a);
   return hipGetLastError();
 }
 
-template <int PAD>
+template <int PAD, bool SPLIT = false>
 static hipError_t launch_pencil_pq_p(const NdConvArgs& a, hipStream_t s) {
   switch (a.MX) {
-    case 8: return launch_pencil_pq_t<4, 2, PAD>(a, s);
-    case 16: return launch_pencil_pq_t<4, 4, PAD>(a, s);
-    case 32: return launch_pencil_pq_t<8, 4, PAD>(a, s);
-    case 64: return launch_pencil_pq_t<8, 8, PAD>(a, s);
-    case 128: return launch_pencil_pq_t<16, 8, PAD>(a, s);
+    case 8: return launch_pencil_pq_t<4, 2, PAD, SPLIT>(a, s);
+    case 16: return launch_pencil_pq_t<4, 4, PAD, SPLIT>(a, s);
+    case 32: return launch_pencil_pq_t<8, 4, PAD, SPLIT>(a, s);
+    case 64: return launch_pencil_pq_t<8, 8, PAD, SPLIT>(a, s);
+    case 128: return launch_pencil_pq_t<16, 8, PAD, SPLIT>(a, s);
     default: return hipErrorInvalidValue;
   }
 }
@@ -1362,9 +1395,12 @@ hipError_t nd_filter(const NdFilterArgs& fin, float2* F, float2* kh, const float
   a.npairs = npairs;
   a.tw128 = tw128;
   if ((e = launch_plane<PL_FWD_FULL>(a, dim3(MX, npairs, 1), s)) != hipSuccess) return e;
+  if (MX > 1) {
+    // transform over x and the split into the channels' half spectra in one pass
+    a.kh = kh;
+    return launch_pencil_pq_p<1, true>(a, s);
+  }
   // 2D grids (MX = 1): the transform over x is the identity
-  if (MX > 1 && (e = launch_pencil<PN_FWD_FULL>(a, dim3((unsigned)(MY * MZ / 64), npairs, 1), s)) != hipSuccess)
-    return e;
   const size_t th = (size_t)MX * MY * (MZ / 2 + 1) * npairs;
   hipLaunchKernelGGL(nd_split_kernel, dim3((unsigned)((th + 255) / 256)), dim3(256), 0, s, (const float2*)F, kh,
                      MX, MY, MZ, npairs);
