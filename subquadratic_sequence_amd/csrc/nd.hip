@@ -1289,12 +1289,10 @@ __global__ __launch_bounds__(64 * RA) void nd_pencil_pq_kernel(NdConvArgs a) {
       const float2 p0 = kval(K0, kx, ky, kz), p1 = kval(K1, kx, ky, kz);
       const float2 P = make_float2(0.5f * (p0.x + p1.x), 0.5f * (p0.y + p1.y));
       const float2 Q = make_float2(0.5f * (p0.x - p1.x), 0.5f * (p0.y - p1.y));
-      // pencil B at k' = (-kx, -ky, -kz): its own value B(-kx), partner A(kx)
-      const float2 m0 = kval(K0, km, kyb, kzb), m1 = kval(K1, km, kyb, kzb);
-      const float2 Pm = make_float2(0.5f * (m0.x + m1.x), 0.5f * (m0.y + m1.y));
-      const float2 Qm = make_float2(0.5f * (m0.x - m1.x), 0.5f * (m0.y - m1.y));
+      // pencil B at -k: its own value B(-kx), partner A(kx); the kernels are
+      // real, so P(-k) = conj P(k) and Q(-k) = conj Q(k)
       SA[kx * 64 + lane] = cadd(cmul(A, P), cmul(conjf2(Bm), Q));
-      SB[km * 64 + lane] = cadd(cmul(Bm, Pm), cmul(conjf2(A), Qm));
+      SB[km * 64 + lane] = cadd(cmul(Bm, conjf2(P)), cmul(conjf2(A), conjf2(Q)));
     }
   }
   __syncthreads();
