@@ -26,6 +26,11 @@ taken here (the plainest ones the page supports):
     gate, and each sample is convolved with its own kernel.
 Offsets, coordinates, boundaries, projections and the recurrence are those of
 hyena_nd_oracle.
+
+The pins in tests/test_oracle_film.py tie these functions to the pinned plain
+kernel, closed forms and invariants; the conventions above (score form, FiLM
+placement, omega0 placement, the Gaussian rate form) are readings no page
+fixes: parity unpinned for those conventions.
 """
 from __future__ import annotations
 
