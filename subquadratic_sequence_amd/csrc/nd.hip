@@ -1199,91 +1199,114 @@ __global__ __launch_bounds__(64 * RA) void nd_pencil_pq_kernel(NdConvArgs a) {
     const float2 v = K[((size_t)x2 * MY + y2) * ZH + z2];
     return lower ? v : conjf2(v);
   };
-  // forward DFT over x of pencil g into D[kx][lane] (D is also its stage buffer)
-  auto forward = [&](int g, float2* D) {
+  // Waves [0, RB) work on pencil A and, when there are enough waves (RA >= 2 RB),
+  // waves [RB, 2 RB) on pencil B at the same time in the 16-point stages and the
+  // products; otherwise the same waves take B after A. All RA waves run the
+  // 8-point stages, A then B.
+  constexpr bool PAR = RA >= 2 * RB;
+  constexpr int NW = PAR ? 2 * RB : RB;  // waves of the product loop
+  const bool onB = PAR && w >= RB && w < 2 * RB;
+  const bool on16 = w < RB || onB;       // this wave runs a 16-point stage
+  const int ka = onB ? w - RB : w;
+  float2* D = onB ? SB : SA;
+
+  // forward stage 1 (x = w + RA r, r < RB / PAD non-zero) into the stage layout
+  auto stage1 = [&](int g, float2* E) {
     float2 v[RB];
 #pragma unroll
     for (int r = 0; r < RB; ++r) v[r] = (r < RB / PAD) ? base[(size_t)(w + RA * r) * plane + g] : make_float2(0.f, 0.f);
     Dft<RB, false>::run(v);
 #pragma unroll
-    for (int ka = 0; ka < RB; ++ka) {
-      if (ka) v[ka] = cmul(v[ka], a.tw128[(w * ka * (128 / N1)) & 127]);
-      D[(w * RB + ka) * 64 + lane] = v[ka];
+    for (int k = 0; k < RB; ++k) {
+      if (k) v[k] = cmul(v[k], a.tw128[(w * k * (128 / N1)) & 127]);
+      E[(w * RB + k) * 64 + lane] = v[k];
     }
-    __syncthreads();
+  };
+  // forward stage 2 of buffer E for column k (DFT over j), result to E[kx][lane]
+  auto stage2 = [&](float2* E, int k, bool run) {
     float2 u[RA];
-    if (w < RB) {
+    if (run) {
 #pragma unroll
-      for (int j = 0; j < RA; ++j) u[j] = D[(j * RB + w) * 64 + lane];
+      for (int j = 0; j < RA; ++j) u[j] = E[(j * RB + k) * 64 + lane];
       Dft<RA, false>::run(u);
     }
     __syncthreads();
-    if (w < RB) {
+    if (run) {
 #pragma unroll
-      for (int kb = 0; kb < RA; ++kb) D[(w + RB * kb) * 64 + lane] = u[kb];
+      for (int kb = 0; kb < RA; ++kb) E[(k + RB * kb) * 64 + lane] = u[kb];
     }
   };
-  // inverse DFT over x of the spectrum in D[kx][lane] (threads w < RB take
-  // kx = w + RB kb), SA as stage buffer, stored to pencil g (x < X)
-  auto inverse = [&](const float2* D, int g) {
+  // inverse stage 1 of buffer E for column k: spectrum E[kx] -> stage layout
+  auto istage1 = [&](float2* E, int k, bool run) {
     float2 y[RA];
-    if (w < RB) {
+    if (run) {
 #pragma unroll
-      for (int kb = 0; kb < RA; ++kb) y[kb] = D[(w + RB * kb) * 64 + lane];
-    }
-    __syncthreads();  // D read before SA is written
-    if (w < RB) {
-      Dft<RA, true>::run(y);
-#pragma unroll
-      for (int na = 1; na < RA; ++na) y[na] = cmulc(y[na], a.tw128[(w * na * (128 / N1)) & 127]);
-#pragma unroll
-      for (int na = 0; na < RA; ++na) SA[(w * RA + na) * 64 + lane] = y[na];
+      for (int kb = 0; kb < RA; ++kb) y[kb] = E[(k + RB * kb) * 64 + lane];
     }
     __syncthreads();
+    if (run) {
+      Dft<RA, true>::run(y);
+#pragma unroll
+      for (int na = 1; na < RA; ++na) y[na] = cmulc(y[na], a.tw128[(k * na * (128 / N1)) & 127]);
+#pragma unroll
+      for (int na = 0; na < RA; ++na) E[(k * RA + na) * 64 + lane] = y[na];
+    }
+  };
+  // inverse stage 2 (all waves): stage layout of E -> pencil g, x < X
+  auto istage2 = [&](const float2* E, int g) {
     float2 q[RB];
 #pragma unroll
-    for (int ka = 0; ka < RB; ++ka) q[ka] = SA[(ka * RA + w) * 64 + lane];
+    for (int k = 0; k < RB; ++k) q[k] = E[(k * RA + w) * 64 + lane];
     Dft<RB, true>::run(q);
     if (active) {
 #pragma unroll
       for (int nb = 0; nb < RB / PAD; ++nb) base[(size_t)(w + RA * nb) * plane + g] = q[nb];
     }
-    __syncthreads();  // SA read before its next use
   };
 
-  forward(f, SA);
-  forward(fb, SB);
+  stage1(f, SA);
+  stage1(fb, SB);
+  __syncthreads();
+  stage2(D, ka, on16);
+  if (!PAR) {
+    __syncthreads();
+    stage2(SB, w, w < RB);
+  }
   __syncthreads();
   if constexpr (SPLIT) {
-    if (w < RB && active) {
+    if (w < NW && active) {
       const size_t PH = (size_t)N1 * MY * ZH;
       float2* Ka = const_cast<float2*>(a.kh) + (size_t)(2 * c) * PH;
       float2* Kb = Ka + PH;
       const float sc = 0.5f / (float)((size_t)N1 * plane);
+      const int kc = w % RB, h = w / RB;
+      constexpr int KBN = RA * RB / NW;  // kb per wave
 #pragma unroll
-      for (int kb = 0; kb < RA; ++kb) {
-        const int kx = w + RB * kb, km = (N1 - kx) % N1;
+      for (int i = 0; i < KBN; ++i) {
+        const int kx = kc + RB * (h * KBN + i), km = (N1 - kx) % N1;
         const float2 A = SA[kx * 64 + lane], Bm = SB[km * 64 + lane];
         if (kz <= MZ / 2) {  // pencil A at (kx, ky, kz): partner conj(B(-kx))
-          const float2 fm = conjf2(Bm), h = cadd(A, fm), d = csub(A, fm);
+          const float2 fm = conjf2(Bm), hs = cadd(A, fm), d = csub(A, fm);
           const size_t o = ((size_t)kx * MY + ky) * ZH + kz;
-          Ka[o] = make_float2(sc * h.x, sc * h.y);
+          Ka[o] = make_float2(sc * hs.x, sc * hs.y);
           Kb[o] = make_float2(sc * d.y, -sc * d.x);
         }
         if (kzb <= MZ / 2) {  // pencil B at (-kx, -ky, -kz): partner conj(A(kx))
-          const float2 fm = conjf2(A), h = cadd(Bm, fm), d = csub(Bm, fm);
+          const float2 fm = conjf2(A), hs = cadd(Bm, fm), d = csub(Bm, fm);
           const size_t o = ((size_t)km * MY + kyb) * ZH + kzb;
-          Ka[o] = make_float2(sc * h.x, sc * h.y);
+          Ka[o] = make_float2(sc * hs.x, sc * hs.y);
           Kb[o] = make_float2(sc * d.y, -sc * d.x);
         }
       }
     }
     return;
   }
-  if (w < RB) {
+  if (w < NW) {
+    const int kc = w % RB, h = w / RB;
+    constexpr int KBN = RA * RB / NW;  // kb per wave
 #pragma unroll
-    for (int kb = 0; kb < RA; ++kb) {
-      const int kx = w + RB * kb, km = (N1 - kx) % N1;
+    for (int i = 0; i < KBN; ++i) {
+      const int kx = kc + RB * (h * KBN + i), km = (N1 - kx) % N1;
       const float2 A = SA[kx * 64 + lane], Bm = SB[km * 64 + lane];
       // pencil A at k = (kx, ky, kz)
       const float2 p0 = kval(K0, kx, ky, kz), p1 = kval(K1, kx, ky, kz);
@@ -1296,8 +1319,14 @@ __global__ __launch_bounds__(64 * RA) void nd_pencil_pq_kernel(NdConvArgs a) {
     }
   }
   __syncthreads();
-  inverse(SA, f);
-  inverse(SB, fb);
+  istage1(D, ka, on16);
+  if (!PAR) {
+    __syncthreads();
+    istage1(SB, w, w < RB);
+  }
+  __syncthreads();
+  istage2(SA, f);
+  istage2(SB, fb);
 }
 
 template <int RA, int RB, int PAD, bool SPLIT>
