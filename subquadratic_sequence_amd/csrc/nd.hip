@@ -1291,7 +1291,10 @@ __global__ __launch_bounds__(64 * RA) void nd_pencil_pq_kernel(NdConvArgs a) {
           Ka[o] = make_float2(sc * hs.x, sc * hs.y);
           Kb[o] = make_float2(sc * d.y, -sc * d.x);
         }
-        if (kzb <= MZ / 2) {  // pencil B at (-kx, -ky, -kz): partner conj(A(kx))
+        // pencil B at (-kx, -ky, -kz): partner conj(A(kx)); a pencil that is its
+        // own mirror has all its entries written as pencil A already (one
+        // writer per entry: the two copies' DFTs need not agree to the last bit)
+        if (kzb <= MZ / 2 && fb != f) {
           const float2 fm = conjf2(A), hs = cadd(Bm, fm), d = csub(Bm, fm);
           const size_t o = ((size_t)km * MY + kyb) * ZH + kzb;
           Ka[o] = make_float2(sc * hs.x, sc * hs.y);
@@ -1325,6 +1328,8 @@ __global__ __launch_bounds__(64 * RA) void nd_pencil_pq_kernel(NdConvArgs a) {
     istage1(SB, w, w < RB);
   }
   __syncthreads();
+  // a self-mirrored pencil (f == fb) is stored twice by the same thread, A then
+  // B: the last store in program order stands
   istage2(SA, f);
   istage2(SB, fb);
 }

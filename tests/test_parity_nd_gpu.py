@@ -131,3 +131,24 @@ def test_nd_2d_filter_matches_oracle():
 ])
 def test_nd_2d_sweep(B, Y, C, N, circ):
     _check(make_nd(500 + B + Y + C + N + 7 * circ, B, 1, Y, Y, C, N=N, W=64, u_mean_spread=0.5, circular=circ))
+
+
+# ------------------------------------------------------------- reproducibility
+
+@pytest.mark.parametrize("X,Y,circ", [(8, 16, False), (16, 16, False), (8, 16, True)])
+def test_nd_filter_spectra_are_bit_reproducible(X, Y, circ):
+    # every half-spectrum entry has one writer: two builds of the same layer agree bit for bit
+    import torch
+    import subquadratic_sequence_amd as hs
+    from tests.gpu_util import to_dev
+    inp = make_nd(80 + X + Y, 2, X, Y, Y, 64, N=2, W=64, circular=circ)
+    say(f"nd spectra reproducibility {X}x{Y}x{Y} circular={circ}")
+    bd = hs.ND_CIRCULAR if circ else hs.ND_ZERO_PAD
+    fa = [to_dev(a) for a in (inp.w1, inp.b1, inp.w2, inp.b2, inp.w3, inp.b3, inp.decay)]
+    caches = []
+    for _ in range(2):
+        layer = hs.HyenaNDLayer(X, Y, Y, 64, 2, boundary=bd)
+        hs.hyena_nd_filter_gen(layer, *fa)
+        caches.append(layer.cache)
+    torch.cuda.synchronize()
+    assert torch.equal(caches[0], caches[1])

@@ -1,5 +1,6 @@
-"""The stage-event entry points (hyena_fwd_profiled, hyena_nd_fwd_profiled) run the
-same launches as the plain ones: identical outputs, and four events that bracket
+"""The stage-event entry points (hyena_fwd_profiled, hyena_nd_fwd_profiled,
+hyena_nd_film_fwd_profiled) run the same launches as the plain ones: identical
+outputs, and events (four; five for the register-conditioned layer) that bracket
 the stages in order."""
 import numpy as np
 import pytest
@@ -64,3 +65,26 @@ def test_nd_fwd_profiled_matches_nd_fwd(X, Y, circ):
     assert torch.equal(y0, y1)
     assert np.isfinite(y1.cpu().numpy()).all()
     _check_events(evs)
+
+
+@pytest.mark.parametrize("X,circ", [(8, False), (1, True)])
+def test_nd_film_fwd_profiled_matches_film_fwd(X, circ):
+    import torch
+    import subquadratic_sequence_amd as hs
+    from synth import make_nd_film
+    inp = make_nd_film(47 + X, 3, X, 16, 16, 64, N=2, W=64, circular=circ)
+    say(f"case profiled film B=3 grid {X}x16x16 C=64 circular={circ}")
+    bd = hs.ND_CIRCULAR if circ else hs.ND_ZERO_PAD
+    m = hs.HyenaNDFilm(inp.X, inp.Y, inp.Z, inp.C, inp.N, bd, *(to_dev(a) for a in (
+        inp.w1, inp.b1, inp.w2, inp.b2, inp.w3, inp.b3, inp.window, inp.q, inp.film_w, inp.film_b, inp.omega0)))
+    u, reg, w_in, dskip, w_out = (to_dev(a) for a in (inp.u, inp.reg, inp.w_in, inp.dskip, inp.w_out))
+    y0 = hs.hyena_nd_film_fwd(m, u, reg, w_in, dskip, w_out)
+    y1 = torch.empty_like(y0)
+    ws = torch.empty(hs.hyena_nd_film_workspace_bytes(inp.B, inp.X, inp.Y, inp.Z, inp.C, inp.N, inp.W, bd),
+                     dtype=torch.uint8, device="cuda")
+    evs = [torch.cuda.Event(enable_timing=True) for _ in range(5)]
+    hs.hyena_nd_film_fwd_profiled(m, u, reg, w_in, dskip, w_out, y1, ws, evs)
+    torch.cuda.synchronize()
+    assert torch.equal(y0, y1)
+    t = [evs[0].elapsed_time(evs[i]) for i in range(1, 5)]
+    assert all(x >= 0 for x in t) and t[0] <= t[1] <= t[2] <= t[3], t
