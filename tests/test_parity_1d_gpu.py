@@ -155,3 +155,27 @@ def test_noncausal_future_reaches_past_on_gpu():
     y1 = gpu_1d(inp)
     scale = np.max(np.abs(y0))
     assert np.max(np.abs(y1[:, :t0 - 2] - y0[:, :t0 - 2])) > 1e-3 * scale
+
+
+@pytest.mark.parametrize("L,dt,causal", [(2048, "bf16", True), (16384, "bf16", True), (16384, "f32", False)])
+def test_filter_spectra_and_fwd_are_bit_reproducible(L, dt, causal):
+    # two filter generations give the same cache bit for bit, and two forwards the same output
+    import torch
+    import subquadratic_sequence_amd as hs
+    from tests.gpu_util import to_dev
+    inp = make_1d(90 + L, 2, L, 64, N=2, K=8, dtype=dt, causal=causal)
+    say(f"1D reproducibility L={L} dtype={dt} causal={causal}")
+    tdt = torch.bfloat16 if dt == "bf16" else torch.float32
+    layers = []
+    for _ in range(2):
+        layer = hs.HyenaLayer(L, 64, 2, direction=hs.CAUSAL if causal else hs.NONCAUSAL)
+        hs.hyena_filter_gen(layer, to_dev(inp.w1), to_dev(inp.b1), to_dev(inp.w2), to_dev(inp.b2),
+                            to_dev(inp.w3), to_dev(inp.b3), to_dev(inp.decay), inp.K)
+        layers.append(layer)
+    torch.cuda.synchronize()
+    assert torch.equal(layers[0].cache, layers[1].cache)
+    args = (to_dev(inp.u, tdt), to_dev(inp.w_in, tdt), to_dev(inp.short_w), to_dev(inp.dskip), to_dev(inp.w_out, tdt))
+    y0 = hs.hyena_fwd(layers[0], *args)
+    y1 = hs.hyena_fwd(layers[1], *args)
+    torch.cuda.synchronize()
+    assert torch.equal(y0, y1)
