@@ -1007,7 +1007,8 @@ template <int M> struct Plane2dCfg {
   static constexpr int PER = PlaneCfg<M>::PER;  // plane elements per thread
 };
 
-template <int M, bool CIRC>
+// PQ: a kernel per sample (a.kh_stride != 0), the (P, Q) spectral product.
+template <int M, bool CIRC, bool PQ>
 __global__ __launch_bounds__(Plane2dCfg<M>::THREADS) void nd_plane2d_kernel(NdConvArgs a, int per_xcd) {
   using C = PlaneCfg<M>;
   constexpr int NT = Plane2dCfg<M>::THREADS;
@@ -1060,7 +1061,7 @@ __global__ __launch_bounds__(Plane2dCfg<M>::THREADS) void nd_plane2d_kernel(NdCo
         kk[e] = lower ? kv : conjf2(kv);
       }
     };
-    if (EARLY) load_k();
+    if (EARLY && !PQ) load_k();
     if (!CIRC) {
       for (int i = tid; i < M * M; i += NT) P[(i / M) * C::RS + i % M] = make_float2(0.f, 0.f);
       __syncthreads();
@@ -1073,12 +1074,50 @@ __global__ __launch_bounds__(Plane2dCfg<M>::THREADS) void nd_plane2d_kernel(NdCo
     __syncthreads();
     plane_rows<M, false>(P, Y, tw);
     plane_cols<M, false>(P, tw);
-    if (!EARLY) load_k();
+    if constexpr (!PQ) {
+      if (!EARLY) load_k();
 #pragma unroll
-    for (int e = 0; e < PER; ++e) {
-      const int i = tid + e * NT;
-      float2* pe = P + (i / M) * C::RS + i % M;
-      *pe = cmul(*pe, kk[e]);
+      for (int e = 0; e < PER; ++e) {
+        const int i = tid + e * NT;
+        float2* pe = P + (i / M) * C::RS + i % M;
+        *pe = cmul(*pe, kk[e]);
+      }
+    } else {
+      // a kernel per sample: Y(k) = P F(k) + Q conj F(-k), P, Q the half sum and
+      // difference of the two samples' spectra (P(-k) = conj P(k), Q likewise).
+      // A thread takes whole bin pairs {k, -k} of the canonical half (rows 1 ..
+      // M/2 - 1, and kz <= M/2 on rows 0 and M/2, their own mirrors): it reads
+      // both bins and writes both, so every bin has one reader and one writer.
+      const float2* K0 = a.kh + (size_t)b0 * a.kh_stride + (size_t)(n * CC + c) * M * ZH;
+      const float2* K1 = a.kh + (size_t)b1 * a.kh_stride + (size_t)(n * CC + c) * M * ZH;
+      constexpr int INNER = (M / 2 - 1) * M, NPAIR = INNER + 2 * (M / 2 + 1);
+      for (int pr = tid; pr < NPAIR; pr += NT) {
+        int ky, kz;
+        if (pr < INNER) {
+          ky = 1 + pr / M;
+          kz = pr % M;
+        } else {
+          const int e2 = pr - INNER;
+          ky = e2 < M / 2 + 1 ? 0 : M / 2;
+          kz = e2 % (M / 2 + 1);
+        }
+        const int kym = (M - ky) % M, kzm = (M - kz) % M;
+        // half-spectrum entry at k (kz <= M/2) or the conjugate of the one at -k
+        const bool lower = kz <= M / 2;
+        const int o = lower ? ky * ZH + kz : kym * ZH + kzm;
+        float2 k0 = K0[o], k1 = K1[o];
+        if (!lower) {
+          k0 = conjf2(k0);
+          k1 = conjf2(k1);
+        }
+        const float2 Pk = make_float2(0.5f * (k0.x + k1.x), 0.5f * (k0.y + k1.y));
+        const float2 Qk = make_float2(0.5f * (k0.x - k1.x), 0.5f * (k0.y - k1.y));
+        float2* pa = P + ky * C::RS + kz;
+        float2* pb = P + kym * C::RS + kzm;
+        const float2 A = *pa, Bm = *pb;
+        *pa = cadd(cmul(A, Pk), cmul(conjf2(Bm), Qk));
+        if (pb != pa) *pb = cadd(cmul(Bm, conjf2(Pk)), cmul(conjf2(A), conjf2(Qk)));
+      }
     }
     // gate inputs, used after the inverse transform
     const float* x0 = s0 + (size_t)((n + 1) * CC + c) * V;
@@ -1498,7 +1537,7 @@ static hipError_t launch_pencil128(const NdConvArgs& a, int nitems, hipStream_t 
 template <int M, bool CIRC>
 static hipError_t launch_plane2d_t(const NdConvArgs& a, hipStream_t s) {
   using C = PlaneCfg<M>;
-  auto fn = nd_plane2d_kernel<M, CIRC>;
+  auto fn = a.kh_stride != 0 ? nd_plane2d_kernel<M, CIRC, true> : nd_plane2d_kernel<M, CIRC, false>;
   hipError_t e = nd_allow_lds((const void*)fn, C::LDS);
   if (e != hipSuccess) return e;
   const int items = (a.B + 1) / 2 * a.C;

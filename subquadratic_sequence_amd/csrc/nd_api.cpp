@@ -363,35 +363,31 @@ int film_fwd_impl(int X, int Y, int Z, int C, int N, int bd, const hyena_nd_filt
   HY_CHECK_HIP(hy::gemm(gi, false, stream));
   if (ev) HY_CHECK_HIP(hipEventRecord(ev[2], stream));
 
-  // unit gates. 3D grids: two samples per packed complex field as in
-  // hyena_nd_fwd, the pencil pass filtering each half with its own sample's
-  // spectra ((P, Q) form). 2D grids (fused plane kernel, one spectrum per
-  // channel): one sample per launch, alone in its field.
+  // unit gates; two samples per packed complex field as in hyena_nd_fwd, the
+  // spectral product filtering each half with its own sample's spectra ((P, Q)
+  // form: the pencil pass on 3D grids, the fused plane kernel on 2D grids)
   HY_CHECK_HIP(hy::fill(ones, (size_t)B * N * C, 1.f, stream));
-  const bool packed = X > 1;
-  for (int b = 0; b < (packed ? 1 : B); ++b) {
-    hy::NdConvArgs a{};
-    a.X = X;
-    a.Y = Y;
-    a.Z = Z;
-    a.MX = MX;
-    a.MY = MY;
-    a.MZ = MZ;
-    a.C = C;
-    a.NO = N;
-    a.B = packed ? B : 1;
-    a.p = pbuf + (size_t)b * J * V;
-    a.dskip = dskip;
-    a.gate = ones;
-    a.zbuf[0] = reinterpret_cast<float*>(base + w.z0) + (size_t)b * C * V;
-    a.zbuf[1] = reinterpret_cast<float*>(base + w.z1) + (size_t)b * C * V;
-    a.zfinal = zfin + (size_t)b * C * V;
-    a.Yint = reinterpret_cast<float2*>(base + w.Y);
-    a.kh = reinterpret_cast<const float2*>(wsb + fw.kh + b * khs);
-    a.kh_stride = packed ? khs / sizeof(float2) : 0;
-    a.tw128 = tw;
-    HY_CHECK_HIP(hy::nd_conv(a, stream));
-  }
+  hy::NdConvArgs a{};
+  a.X = X;
+  a.Y = Y;
+  a.Z = Z;
+  a.MX = MX;
+  a.MY = MY;
+  a.MZ = MZ;
+  a.C = C;
+  a.NO = N;
+  a.B = B;
+  a.p = pbuf;
+  a.dskip = dskip;
+  a.gate = ones;
+  a.zbuf[0] = reinterpret_cast<float*>(base + w.z0);
+  a.zbuf[1] = reinterpret_cast<float*>(base + w.z1);
+  a.zfinal = zfin;
+  a.Yint = reinterpret_cast<float2*>(base + w.Y);
+  a.kh = reinterpret_cast<const float2*>(wsb + fw.kh);
+  a.kh_stride = khs / sizeof(float2);
+  a.tw128 = tw;
+  HY_CHECK_HIP(hy::nd_conv(a, stream));
   if (ev) HY_CHECK_HIP(hipEventRecord(ev[3], stream));
   hy::GemmArgs go{zfin, wt_out, y, B * V, C, C, V, true, false, nullptr};
   HY_CHECK_HIP(hy::gemm(go, false, stream));
