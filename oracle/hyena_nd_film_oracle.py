@@ -36,8 +36,7 @@ from __future__ import annotations
 
 import numpy as np
 
-from .hyena_nd_oracle import (_nd_project, conv3d_circular_direct, conv3d_circular_fft, conv3d_direct, conv3d_fft,
-                              nd_offsets)
+from .hyena_nd_oracle import (_nd_project, conv3d_circular_fft, conv3d_fft, nd_offsets, nd_recurrence)
 
 
 def film_control(reg, q) -> np.ndarray:
@@ -82,25 +81,24 @@ def film_kernels(params: dict, reg, q, film_w, film_b, X, Y, Z, N, C, circular=F
     return np.stack([nd_filter_film(params, mod[b], X, Y, Z, N, C, circular) for b in range(mod.shape[0])])
 
 
-def hyena_nd_film_fwd(u, w_in, dskip, w_out, Ks, conv: str = "fft", circular: bool = False) -> np.ndarray:
+def hyena_nd_film_fwd(u, w_in, dskip, w_out, Ks, conv: str = "fft", circular: bool = False,
+                      workers: int = 1) -> np.ndarray:
     """y[B, X, Y, Z, C]; Ks [B, N, C, MX, MY, MZ] from film_kernels.
 
     z^1 = v; z^{n+1} = x^n * (K^n_b conv z^n) + D^n * z^n; y = z^{N+1} W_out.
+    workers > 1 runs the recurrence on channel shards in that many processes.
     """
     B, X, Y, Z, C = np.shape(u)
     N = np.shape(dskip)[0]
-    if circular:
-        convf = conv3d_circular_direct if conv == "direct" else conv3d_circular_fft
-    else:
-        convf = conv3d_direct if conv == "direct" else conv3d_fft
     dskip = np.asarray(dskip, dtype=np.float64)
     Ks = np.asarray(Ks, dtype=np.float64)
     z, xs = _nd_project(u, w_in, C, N)
-    for n in range(N):
-        out = np.empty_like(z)
-        for b in range(B):
-            out[b] = convf(Ks[b, n], z[b])
-        z = xs[n] * out + dskip[n][None, :, None, None, None] * z
+    if workers > 1:
+        from ._pool import channel_shards
+        z = channel_shards(nd_recurrence, C, workers,
+                           lambda sl: (z[:, sl], [x[:, sl] for x in xs], dskip[:, sl], Ks[:, :, sl], conv, circular))
+    else:
+        z = nd_recurrence(z, xs, dskip, Ks, conv, circular)
     return np.moveaxis(z, 1, -1) @ np.asarray(w_out, dtype=np.float64)
 
 

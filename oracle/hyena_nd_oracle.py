@@ -170,28 +170,55 @@ def _nd_project(u, w_in, C, N):
     return blocks[0], blocks[1:]
 
 
-def hyena_nd_fwd(u, w_in, dskip, gate_a, gate_b, w_out, K, conv: str = "fft",
-                 circular: bool = False) -> np.ndarray:
-    """y[B, X, Y, Z, C] of the 3D operator.
+def nd_recurrence(z, xs, dskip, Kg, conv: str = "fft", circular: bool = False) -> np.ndarray:
+    """z^{N+1} from z^1 = v on channel-major grids: for every sample b,
+    z^{n+1}_b = x^n_b * (Kg[b, n] conv z^n_b) + D^n * z^n_b.
 
-    u [B,X,Y,Z,C]; w_in [C,(N+1)C]; dskip, gate_a, gate_b [N,C]; w_out [C,C];
-    K [N, C, MX, MY, MZ] (nd_filter with the same `circular`).  conv: "direct" or "fft".
+    z [B, C, X, Y, Z]; xs: N arrays like z; dskip [N, C]; Kg [B, N, C, MX, MY, MZ]
+    (a sample's kernels: the gated kernel g * K, or its own conditioned kernel).
+    Channels are independent, so any channel subset can be run alone.
     """
-    B, X, Y, Z, C = np.shape(u)
-    N = np.shape(dskip)[0]
     if circular:
         convf = conv3d_circular_direct if conv == "direct" else conv3d_circular_fft
     else:
         convf = conv3d_direct if conv == "direct" else conv3d_fft
     dskip = np.asarray(dskip, dtype=np.float64)
+    for n in range(len(xs)):
+        out = np.empty_like(z)
+        for b in range(z.shape[0]):
+            out[b] = convf(np.asarray(Kg[b][n], dtype=np.float64), z[b])
+        z = xs[n] * out + dskip[n][None, :, None, None, None] * z
+    return z
+
+
+def _nd_gated_recurrence(z, xs, dskip, g, K, conv, circular):
+    """nd_recurrence with the kernels g[b, n, c] * K[n, c] of the channel-mean gate."""
+    K = np.asarray(K, dtype=np.float64)
+    Kg = [g[b][:, :, None, None, None] * K for b in range(z.shape[0])]
+    return nd_recurrence(z, xs, dskip, Kg, conv, circular)
+
+
+def hyena_nd_fwd(u, w_in, dskip, gate_a, gate_b, w_out, K, conv: str = "fft",
+                 circular: bool = False, workers: int = 1) -> np.ndarray:
+    """y[B, X, Y, Z, C] of the 3D operator.
+
+    u [B,X,Y,Z,C]; w_in [C,(N+1)C]; dskip, gate_a, gate_b [N,C]; w_out [C,C];
+    K [N, C, MX, MY, MZ] (nd_filter with the same `circular`).  conv: "direct" or
+    "fft".  workers > 1 runs the recurrence on channel shards in that many processes.
+    """
+    B, X, Y, Z, C = np.shape(u)
+    N = np.shape(dskip)[0]
+    dskip = np.asarray(dskip, dtype=np.float64)
     g = nd_gate(u, gate_a, gate_b)                                   # [B, N, C]
     z, xs = _nd_project(u, w_in, C, N)
     K = np.asarray(K, dtype=np.float64)
-    for n in range(N):
-        out = np.empty_like(z)
-        for b in range(B):
-            out[b] = convf(g[b, n][:, None, None, None] * K[n], z[b])
-        z = xs[n] * out + dskip[n][None, :, None, None, None] * z
+    if workers > 1:
+        from ._pool import channel_shards
+        z = channel_shards(_nd_gated_recurrence, C, workers,
+                           lambda sl: (z[:, sl], [x[:, sl] for x in xs], dskip[:, sl], g[:, :, sl], K[:, sl],
+                                       conv, circular))
+    else:
+        z = _nd_gated_recurrence(z, xs, dskip, g, K, conv, circular)
     return np.moveaxis(z, 1, -1) @ np.asarray(w_out, dtype=np.float64)
 
 

@@ -216,28 +216,51 @@ def _project_and_gate_inputs(u, w_in, short_w, D, N):
     return v, xs
 
 
-def hyena_fwd(u, w_in, short_w, dskip, w_out, h, conv: str = "auto", causal: bool = True) -> np.ndarray:
+def _conv_fn(conv: str, causal: bool, L: int):
+    if conv == "auto":
+        conv = "direct" if L <= 4096 else "fft"
+    if causal:
+        return causal_conv_direct if conv == "direct" else causal_conv_fft
+    return noncausal_conv_direct if conv == "direct" else noncausal_conv_fft
+
+
+def hyena_recurrence(z, xs, dskip, h, conv: str = "auto", causal: bool = True) -> np.ndarray:
+    """z^{N+1} from z^1 = v: z^{n+1} = x^n * (h^n conv z^n) + D^n * z^n, channel-major.
+
+    z [B, D, L]; xs: N arrays [B, D, L]; dskip [N, D]; h [N, D, L] (or
+    [N, D, 2L - 1] two-sided).  Every channel is independent of the others (the
+    filters and gates act depthwise), so any channel subset can be run alone.
+    """
+    convf = _conv_fn(conv, causal, np.shape(z)[-1])
+    dskip = np.asarray(dskip, dtype=np.float64)
+    h = np.asarray(h, dtype=np.float64)
+    for n in range(len(xs)):
+        c = convf(h[n][None], z)
+        z = xs[n] * c + dskip[n][None, :, None] * z
+    return z
+
+
+def hyena_fwd(u, w_in, short_w, dskip, w_out, h, conv: str = "auto", causal: bool = True,
+              workers: int = 1) -> np.ndarray:
     """y[B, L, D] of the order-N operator.
 
     u [B, L, D]; w_in [D, (N+1)D]; short_w [(N+1)D, 3]; dskip [N, D];
     w_out [D, D]; h [N, D, L] (implicit_filter) or, with causal=False,
     [N, D, 2L - 1] (implicit_filter_noncausal).  conv: "direct", "fft" or
-    "auto" (direct up to L = 4096, FFT above).
+    "auto" (direct up to L = 4096, FFT above).  workers > 1 runs the recurrence
+    on channel shards in that many processes (same arithmetic per channel).
     """
     B, L, D = np.shape(u)
     N = np.shape(dskip)[0]
-    if conv == "auto":
-        conv = "direct" if L <= 4096 else "fft"
-    if causal:
-        convf = causal_conv_direct if conv == "direct" else causal_conv_fft
-    else:
-        convf = noncausal_conv_direct if conv == "direct" else noncausal_conv_fft
+    z, xs = _project_and_gate_inputs(u, w_in, short_w, D, N)
     dskip = np.asarray(dskip, dtype=np.float64)
     h = np.asarray(h, dtype=np.float64)
-    z, xs = _project_and_gate_inputs(u, w_in, short_w, D, N)
-    for n in range(N):
-        c = convf(h[n][None], z)
-        z = xs[n] * c + dskip[n][None, :, None] * z
+    if workers > 1:
+        from ._pool import channel_shards
+        z = channel_shards(hyena_recurrence, D, workers,
+                           lambda sl: (z[:, sl], [x[:, sl] for x in xs], dskip[:, sl], h[:, sl], conv, causal))
+    else:
+        z = hyena_recurrence(z, xs, dskip, h, conv, causal)
     return z.transpose(0, 2, 1) @ np.asarray(w_out, dtype=np.float64)
 
 

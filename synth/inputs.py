@@ -255,6 +255,18 @@ TEST_SHAPES = {
     "nd2d_f32_B8_C384_64sq": dict(kind="nd", seed=34, B=8, X=1, Y=64, Z=64, C=384, N=2),
     # register-conditioned (FiLM) kernels, one per sample, on the 3D workload's grid
     "nd3d_film_f32_B2_C128_64cube": dict(kind="nd_film", seed=35, B=2, X=64, Y=64, Z=64, C=128, N=2, W=64, R=4),
+    # Full-length / full-grid shapes at the narrowest width the library takes
+    # (64 channels), checked at every output: the transform kernels that only the
+    # long and large workloads launch (64k bf16 four-step, 1M with 8192-point
+    # rows, zero-padded 64^3 planes and pencils, 128^3 periodic grids) run here
+    # with the same lengths, grids and storage types as there.
+    "order2_bf16_L64k_D64": dict(kind="1d", seed=36, B=1, L=65536, D=64, N=2, K=16, dtype="bf16", u_scale=1 / 8.0),
+    "order2_bf16_L64k_D64_noncausal": dict(kind="1d", seed=37, B=1, L=65536, D=64, N=2, K=16, dtype="bf16",
+                                           u_scale=1 / 8.0, causal=False),
+    "order2_bf16_L1M_D64_dna": dict(kind="1d", seed=38, B=1, L=1 << 20, D=64, N=2, K=16, dtype="bf16", tokens=4),
+    "nd3d_f32_B2_C64_64cube": dict(kind="nd", seed=39, B=2, X=64, Y=64, Z=64, C=64, N=2, u_mean_spread=0.5),
+    "nd3d_film_f32_B1_C64_64cube": dict(kind="nd_film", seed=40, B=1, X=64, Y=64, Z=64, C=64, N=2, W=64, R=4),
+    "nd3d_film_f32_B2_C64_64cube": dict(kind="nd_film", seed=41, B=2, X=64, Y=64, Z=64, C=64, N=2, W=64, R=4),
 }
 
 

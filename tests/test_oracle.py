@@ -651,3 +651,21 @@ def test_noncausal_operator_fft_equals_direct_and_sampled():
     u2[:, 100] += 1.0
     y2 = oracle.hyena_fwd(u2, *args[1:], conv="direct", causal=False)
     assert np.max(np.abs(y2[:, :99] - yd[:, :99])) > 1e-6
+
+
+# ------------------------------------------------------- channel-shard pools
+# The recurrence is depthwise, so running channel shards in separate processes
+# must give exactly the single-process result.
+
+def test_pooled_1d_equals_single_process():
+    inp = _small(L=128, D=10, N=2)
+    h = oracle.implicit_filter(inp.filter_params, inp.L, inp.N, inp.D)
+    args = (inp.u, inp.w_in, inp.short_w, inp.dskip, inp.w_out, h)
+    assert np.array_equal(oracle.hyena_fwd(*args, conv="fft", workers=3), oracle.hyena_fwd(*args, conv="fft"))
+
+
+def test_pooled_nd_equals_single_process():
+    inp = make_nd(19, 2, 4, 4, 4, 5, N=2, W=8, u_mean_spread=0.5)
+    K = oracle.nd_filter(inp.filter_params, 4, 4, 4, 2, 5)
+    args = (inp.u, inp.w_in, inp.dskip, inp.gate_a, inp.gate_b, inp.w_out, K)
+    assert np.array_equal(oracle.hyena_nd_fwd(*args, workers=2), oracle.hyena_nd_fwd(*args))

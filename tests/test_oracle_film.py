@@ -159,3 +159,10 @@ def test_fft_equals_direct_and_sampled_equals_full(circular):
     ys = oracle.hyena_nd_film_fwd_sampled(inp.u, inp.w_in, inp.dskip, inp.w_out, Ks, pts, chunk=3,
                                           circular=circular)
     assert rel(ys, y[:, pts[:, 0], pts[:, 1], pts[:, 2]]) < 1e-11
+
+
+def test_pooled_equals_single_process():
+    inp = make_nd_film(19, 2, 4, 4, 4, 6, N=2, W=16)
+    Ks = oracle.film_kernels(inp.film_filter_params, inp.reg, inp.q, inp.film_w, inp.film_b, 4, 4, 4, 2, 6)
+    args = (inp.u, inp.w_in, inp.dskip, inp.w_out, Ks)
+    assert np.array_equal(oracle.hyena_nd_film_fwd(*args, workers=4), oracle.hyena_nd_film_fwd(*args))

@@ -54,6 +54,9 @@ def test_film_kernels_match_oracle(W, circ, X):
     (3, 16, 16, 64, 2, 128, 16, True),
     (2, 1, 16, 64, 2, 64, 4, False),    # 2D grids
     (2, 1, 32, 64, 2, 64, 4, True),
+    (3, 1, 32, 64, 2, 64, 4, False),    # 2D, odd batch (a lone sample): 64-point planes
+    (3, 1, 64, 64, 2, 64, 4, False),    # 2D, odd batch: 128-point planes (1024-thread kernel)
+    (3, 1, 64, 64, 2, 64, 4, True),     # 2D circular, odd batch, 64-point planes
 ])
 def test_film_sweep(B, X, Y, C, N, W, R, circ):
     _check(make_nd_film(600 + B + X + Y + C + N + W + R + 7 * circ, B, X, Y, Y, C, N=N, W=W, R=R, circular=circ))
