@@ -56,18 +56,24 @@ def log(msg):
 
 def four_step_spectrum_bytes(s) -> float:
     """Bytes per channel and bin of the filter spectra the four-step row passes
-    read: the half spectrum (L + 1 bins) as complex fp32, or as bf16 pairs for
-    bf16 workloads unless HYENA_SPECTRUM_FP32=1."""
+    read as stored: the half spectrum (L + 1 bins) as complex fp32, or as bf16
+    pairs for bf16 workloads unless HYENA_SPECTRUM_FP32=1."""
     if s == 2 and os.environ.get("HYENA_SPECTRUM_FP32", "0") in ("", "0"):
         return 4.0
     return 8.0
 
 
-def conv_alg_bytes(B, L, D, N, s, lds_regime: bool) -> float:
+def conv_alg_bytes(B, L, D, N, s, lds_regime: bool, spectrum_bytes: float = 8.0) -> float:
+    """Algorithmic bytes of the long-convolution stage per call.
+
+    Four-step regime, per order: read z^n and x^n, write z^{n+1} (3 B L D s) and
+    read the filter's half spectrum, D (L + 1) bins of `spectrum_bytes` each
+    (8: complex fp32, the count the roofline is quoted on; 4: the bf16 copy the
+    row passes of bf16 workloads actually read). LDS regime (all orders fused
+    on chip): read v and x^1..x^N, write z^{N+1}, read N spectra."""
     if lds_regime:
-        # all orders fused on chip: read v and x^1..x^N, write z^{N+1}, read N spectra
         return (N + 1) * B * L * D * s + B * L * D * s + N * 8.0 * D * (L + 1)
-    return N * (3.0 * B * L * D * s + four_step_spectrum_bytes(s) * D * (L + 1))
+    return N * (3.0 * B * L * D * s + spectrum_bytes * D * (L + 1))
 
 
 def conv_source_hash(sources=None) -> str:
@@ -134,30 +140,54 @@ def copy_probe(torch, mib: int = 1024, reps: int = 5) -> float:
     return gbs
 
 
-def cpu_baseline(inp, budget_tokens: int):
-    """fp64 oracle on the first `budget_tokens` positions of the same workload.
+def cpu_model() -> str:
+    try:
+        with open("/proc/cpuinfo") as fh:
+            for line in fh:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def cpu_workers(requested: int = 0) -> int:
+    """Worker processes of the oracle baseline: the cores this process may run
+    on (at most 16), or `requested`."""
+    from oracle._pool import default_workers
+    return requested or default_workers()
+
+
+def cpu_baseline(inp, budget_tokens: int, workers: int):
+    """fp64 oracle on the first `budget_tokens` positions of the same workload,
+    channel shards in `workers` processes (one thread each; the parent's
+    projections use as many BLAS threads).
 
     By causality y[:, :T] depends only on u[:, :T] and on the first T filter taps,
-    so the oracle runs on that prefix with the full-length filters truncated to T
-    taps, FFT convolution path, one thread. A non-causal layer has no such prefix
-    property: the oracle then runs the operator on a length-T sequence (the first
-    T inputs, filters generated for length T), the same work per token."""
+    so the oracle runs on that prefix with the filters' first T taps, FFT
+    convolution path. A non-causal layer has no such prefix property: the oracle
+    then runs the operator on a length-T sequence (the first T inputs, filters
+    generated for length T), the same work per token. Filter generation runs
+    before the timed region (the GPU step reads cached spectra)."""
     import oracle
     from threadpoolctl import threadpool_limits
     T = min(budget_tokens, inp.L)
-    with threadpool_limits(limits=1):
+    if inp.causal:
+        h = oracle.implicit_filter(inp.filter_params, T, inp.N, inp.D) if T == inp.L else \
+            oracle.implicit_filter(inp.filter_params, inp.L, inp.N, inp.D)[:, :, :T]
+    else:
+        h = oracle.implicit_filter_noncausal(inp.filter_params, T, inp.N, inp.D)
+    with threadpool_limits(limits=workers):
         t0 = time.perf_counter()
-        if inp.causal:
-            h = oracle.implicit_filter(inp.filter_params, inp.L, inp.N, inp.D)[:, :, :T]
-        else:
-            h = oracle.implicit_filter_noncausal(inp.filter_params, T, inp.N, inp.D)
         oracle.hyena_fwd(inp.u[:, :T], inp.w_in, inp.short_w, inp.dskip, inp.w_out, h, conv="fft",
-                         causal=inp.causal)
+                         causal=inp.causal, workers=workers)
         dt = time.perf_counter() - t0
     what = "first" if inp.causal else "a non-causal operator of length T on the first"
-    return {"value": inp.B * T / dt, "unit": "tokens/s", "cores": 1, "kind": "oracle",
+    return {"value": inp.B * T / dt, "unit": "tokens/s", "cores": workers, "kind": "oracle",
+            "cpu_model": cpu_model(),
             "sample": f"{what} {T} of {inp.L} positions x B={inp.B} (all {inp.D} channels), fp64 numpy, "
-                      f"FFT path, 1 thread, {dt:.1f} s"}
+                      f"FFT path, channel shards in {workers} processes of 1 thread, filters generated "
+                      f"beforehand, {dt:.1f} s"}
 
 
 def nd_conv_alg_bytes(B, X, Y, Z, C, N, circular: bool = False) -> float:
@@ -175,34 +205,39 @@ def nd_conv_alg_bytes(B, X, Y, Z, C, N, circular: bool = False) -> float:
     return N * (3.0 * B * C * V * 4 + spec)
 
 
-def cpu_baseline_nd(inp, channels: int):
+def _restrict_channels(inp, params, c, per_channel_keys):
+    """Projections and kernel outputs restricted to channels 0..c-1 (indexing only)."""
+    N, C = inp.N, inp.C
+    w_in = np.concatenate([inp.w_in[:c, j * C:j * C + c] for j in range(N + 1)], axis=1)
+    params = dict(params)
+    params["w3"] = np.concatenate([params["w3"][:, n * C:n * C + c] for n in range(N)], axis=1)
+    params["b3"] = np.concatenate([params["b3"][n * C:n * C + c] for n in range(N)])
+    for k in per_channel_keys:
+        params[k] = params[k][:c]
+    return w_in, params
+
+
+def cpu_baseline_nd(inp, channels: int, workers: int):
     """fp64 oracle forward on one sample and the first `channels` channels (the
-    projections restricted to them), full grid, 1 thread, the kernel generated
-    before the timed region (as the GPU step uses a cached spectrum); voxel rate
-    scaled by channels / C."""
+    projections restricted to them), full grid, channel shards in `workers`
+    processes, the kernel generated before the timed region (as the GPU step
+    uses a cached spectrum); voxel rate scaled by channels / C."""
     import oracle
     from threadpoolctl import threadpool_limits
     c = min(channels, inp.C)
-    N = inp.N
-    blocks = [inp.w_in[:c, j * inp.C:j * inp.C + c] for j in range(N + 1)]
-    w_in = np.concatenate(blocks, axis=1)
-    params = dict(inp.filter_params)
-    params["w3"] = np.concatenate([params["w3"][:, n * inp.C:n * inp.C + c] for n in range(N)], axis=1)
-    params["b3"] = np.concatenate([params["b3"][n * inp.C:n * inp.C + c] for n in range(N)])
-    params["decay"] = params["decay"][:c]
-    with threadpool_limits(limits=1):
-        # the layer's kernel: outside the step
-        K = oracle.nd_filter(params, inp.X, inp.Y, inp.Z, N, c, circular=inp.circular)
+    w_in, params = _restrict_channels(inp, inp.filter_params, c, ["decay"])
+    K = oracle.nd_filter(params, inp.X, inp.Y, inp.Z, inp.N, c, circular=inp.circular)
+    with threadpool_limits(limits=workers):
         t0 = time.perf_counter()
         oracle.hyena_nd_fwd(inp.u[:1, ..., :c], w_in, inp.dskip[:, :c], inp.gate_a[:, :c], inp.gate_b[:, :c],
-                            inp.w_out[:c, :c], K, conv="fft", circular=inp.circular)
+                            inp.w_out[:c, :c], K, conv="fft", circular=inp.circular, workers=workers)
         dt = time.perf_counter() - t0
     V = inp.X * inp.Y * inp.Z
     unit = "pixels/s" if inp.X == 1 else "voxels/s"
-    return {"value": V / dt * c / inp.C, "unit": unit, "cores": 1, "kind": "oracle",
+    return {"value": V / dt * c / inp.C, "unit": unit, "cores": workers, "kind": "oracle", "cpu_model": cpu_model(),
             "sample": f"sample 0 of {inp.B}, channels 0..{c - 1} of {inp.C} (projections restricted to them), "
                       f"full {inp.X}x{inp.Y}x{inp.Z} grid, fp64 numpy, FFT path (kernel generated beforehand), "
-                      f"1 thread, {dt:.1f} s; rate scaled by {c}/{inp.C}"}
+                      f"channel shards in {workers} processes of 1 thread, {dt:.1f} s; rate scaled by {c}/{inp.C}"}
 
 
 def main_nd(args, torch, hs, make_config):
@@ -286,9 +321,11 @@ def main_nd(args, torch, hs, make_config):
     }
     if not args.no_cpu_baseline:
         log("cpu baseline (oracle)")
-        # about 10 s of oracle work: all channels of a 2D grid, 64 (circular) or 8 channels of a 3D grid
-        dflt = inp.C if X == 1 else (64 if inp.circular else 8)
-        out["cpu_baseline"] = cpu_baseline_nd(inp, args.cpu_channels or dflt)
+        # about 10-20 s of oracle work: all channels of a 2D grid or of a periodic 3D grid's
+        # sample, two channels per worker of a zero-padded 3D grid's sample
+        P = cpu_workers(args.cpu_workers)
+        dflt = inp.C if (X == 1 or inp.circular) else 2 * P
+        out["cpu_baseline"] = cpu_baseline_nd(inp, args.cpu_channels or dflt, P)
     print(json.dumps(out), flush=True)
 
 
@@ -309,33 +346,30 @@ def film_mlp_flops(X, Y, Z, C, N, W, circular: bool = False) -> float:
     return 2.0 * P * (3 * W + W * W + W * N * C)
 
 
-def cpu_baseline_nd_film(inp, channels: int):
+def cpu_baseline_nd_film(inp, channels: int, workers: int):
     """fp64 oracle of the register-conditioned layer on one sample and the first
     `channels` channels (kernel outputs and projections restricted to them; the
-    control vector and FiLM vectors from all channels), full grid, 1 thread. The
-    kernel synthesis is inside the timed region, as on the GPU; voxel rate scaled
-    by channels / C."""
+    control vector and FiLM vectors from all channels), full grid. The kernel
+    synthesis is inside the timed region, as on the GPU (its matrix products on
+    `workers` BLAS threads); the recurrence runs channel shards in `workers`
+    processes. Voxel rate scaled by channels / C."""
     import oracle
     from threadpoolctl import threadpool_limits
     c = min(channels, inp.C)
-    N = inp.N
-    w_in = np.concatenate([inp.w_in[:c, j * inp.C:j * inp.C + c] for j in range(N + 1)], axis=1)
-    params = dict(inp.film_filter_params)
-    params["w3"] = np.concatenate([params["w3"][:, n * inp.C:n * inp.C + c] for n in range(N)], axis=1)
-    params["b3"] = np.concatenate([params["b3"][n * inp.C:n * inp.C + c] for n in range(N)])
-    params["window"] = params["window"][:c]
-    with threadpool_limits(limits=1):
+    w_in, params = _restrict_channels(inp, inp.film_filter_params, c, ["window"])
+    with threadpool_limits(limits=workers):
         t0 = time.perf_counter()
         mod = oracle.film_modulation(oracle.film_control(inp.reg[:1], inp.q), inp.film_w, inp.film_b)
-        K = oracle.nd_filter_film(params, mod[0], inp.X, inp.Y, inp.Z, N, c, circular=inp.circular)
+        K = oracle.nd_filter_film(params, mod[0], inp.X, inp.Y, inp.Z, inp.N, c, circular=inp.circular)
         oracle.hyena_nd_film_fwd(inp.u[:1, ..., :c], w_in, inp.dskip[:, :c], inp.w_out[:c, :c], K[None],
-                                 circular=inp.circular)
+                                 circular=inp.circular, workers=workers)
         dt = time.perf_counter() - t0
     V = inp.X * inp.Y * inp.Z
-    return {"value": V / dt * c / inp.C, "unit": "voxels/s", "cores": 1, "kind": "oracle",
+    return {"value": V / dt * c / inp.C, "unit": "voxels/s", "cores": workers, "kind": "oracle",
+            "cpu_model": cpu_model(),
             "sample": f"sample 0 of {inp.B}, channels 0..{c - 1} of {inp.C} (kernel outputs and projections "
                       f"restricted to them), full {inp.X}x{inp.Y}x{inp.Z} grid, fp64 numpy, kernel synthesis "
-                      f"and FFT path, 1 thread, {dt:.1f} s; rate scaled by {c}/{inp.C}"}
+                      f"and FFT path, channel shards in {workers} processes, {dt:.1f} s; rate scaled by {c}/{inp.C}"}
 
 
 def main_nd_film(args, torch, hs, make_config):
@@ -408,7 +442,8 @@ def main_nd_film(args, torch, hs, make_config):
     }
     if not args.no_cpu_baseline:
         log("cpu baseline (oracle)")
-        out["cpu_baseline"] = cpu_baseline_nd_film(inp, args.cpu_channels or 4)
+        P = cpu_workers(args.cpu_workers)
+        out["cpu_baseline"] = cpu_baseline_nd_film(inp, args.cpu_channels or 2 * P, P)
     print(json.dumps(out), flush=True)
 
 
@@ -419,9 +454,13 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default=DEFAULT_WORKLOAD)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-tokens", type=int, default=16384)
+    ap.add_argument("--cpu-tokens", type=int, default=0,
+                    help="positions of the 1D oracle sample (default 0: the whole sequence)")
+    ap.add_argument("--cpu-workers", type=int, default=0,
+                    help="oracle worker processes (default: the cores this process may use, at most 16)")
     ap.add_argument("--cpu-channels", type=int, default=0,
-                    help="channels of the 3D oracle sample (default 8 zero padded, 64 circular, all on 2D grids)")
+                    help="channels of the 3D oracle sample (default: two per worker zero padded, all circular "
+                         "and on 2D grids)")
     ap.add_argument("--calib-copy", type=int, default=0, metavar="MIB",
                     help="only run a plain device copy of MIB MiB (reads and writes MIB MiB), for calibrating "
                          "the FETCH_SIZE / WRITE_SIZE counters, and exit")
@@ -494,6 +533,8 @@ def main():
     lds = L <= 4096
     alg = conv_alg_bytes(B, L, D, N, s, lds)
     achieved = alg / (stages[1] * 1e-3) / 1e9
+    alg_stored = conv_alg_bytes(B, L, D, N, s, lds, four_step_spectrum_bytes(s))
+    achieved_stored = alg_stored / (stages[1] * 1e-3) / 1e9
     log(f"stages ms: in-proj {stages[0]:.4f} conv {stages[1]:.4f} out-proj {stages[2]:.4f}")
 
     # filter generation (once per layer; outside the step) and a plain copy for scale
@@ -540,14 +581,18 @@ def main():
         "filter_gen_ms": filter_gen_ms,
         "roofline": {"bound": "hbm", "kernel": "fft_conv stage (all orders)", "achieved": achieved,
                      "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS,
-                     "alg_bytes": alg, "traffic": measured_traffic(args.workload)},
+                     "traffic": measured_traffic(args.workload),
+                     "alg_bytes": alg, "alg_bytes_basis": "per order 3 B L D s + 8 D (L + 1): spectrum as complex fp32",
+                     "stored_precision": {"alg_bytes": alg_stored, "achieved": achieved_stored,
+                                          "frac": achieved_stored / HBM_PEAK_GBS,
+                                          "basis": "spectrum counted at the precision the row passes read"}},
         "conv_valu": conv_valu,
         "projections_mfma": proj,
         "copy_probe_gbs": copy_gbs,
     }
     if not args.no_cpu_baseline:
         log("cpu baseline (oracle)")
-        out["cpu_baseline"] = cpu_baseline(inp, args.cpu_tokens)
+        out["cpu_baseline"] = cpu_baseline(inp, args.cpu_tokens or inp.L, cpu_workers(args.cpu_workers))
     print(json.dumps(out), flush=True)
 
 

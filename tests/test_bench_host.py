@@ -11,13 +11,29 @@ ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 
 def test_conv_alg_bytes_four_step(monkeypatch):
     # two orders, each reads z^n and x^n and writes z^{n+1} and reads one half spectrum
-    # per channel: bf16 complex with bf16 storage, fp32 complex otherwise or with the knob
+    # per channel, complex fp32 (8 bytes per bin): 704.6 MB per order at L = 64k, D = 768
     B, L, D, N = 1, 65536, 768, 2
-    monkeypatch.delenv("HYENA_SPECTRUM_FP32", raising=False)
-    assert bench.conv_alg_bytes(B, L, D, N, 2, False) == 2 * (3 * B * L * D * 2 + 4 * D * (L + 1))
-    assert bench.conv_alg_bytes(B, L, D, N, 4, False) == 2 * (3 * B * L * D * 4 + 8 * D * (L + 1))
-    monkeypatch.setenv("HYENA_SPECTRUM_FP32", "1")
     assert bench.conv_alg_bytes(B, L, D, N, 2, False) == 2 * (3 * B * L * D * 2 + 8 * D * (L + 1))
+    assert abs(bench.conv_alg_bytes(B, L, D, N, 2, False) / 2 - 704.6e6) < 0.1e6
+    assert bench.conv_alg_bytes(B, L, D, N, 4, False) == 2 * (3 * B * L * D * 4 + 8 * D * (L + 1))
+    # as stored: the bf16 copy the row passes of bf16 workloads read, unless the knob keeps fp32
+    monkeypatch.delenv("HYENA_SPECTRUM_FP32", raising=False)
+    assert bench.four_step_spectrum_bytes(2) == 4.0 and bench.four_step_spectrum_bytes(4) == 8.0
+    assert bench.conv_alg_bytes(B, L, D, N, 2, False, bench.four_step_spectrum_bytes(2)) == \
+        2 * (3 * B * L * D * 2 + 4 * D * (L + 1))
+    monkeypatch.setenv("HYENA_SPECTRUM_FP32", "1")
+    assert bench.four_step_spectrum_bytes(2) == 8.0
+
+
+def test_cpu_baseline_reports_workers_and_model():
+    # a tiny causal workload through the pooled oracle: the report names the
+    # process count and the CPU model
+    from synth import make_1d
+    inp = make_1d(3, 1, 256, 64, N=2, K=8)
+    r = bench.cpu_baseline(inp, 128, 2)
+    assert r["cores"] == 2 and r["kind"] == "oracle" and r["value"] > 0
+    assert isinstance(r["cpu_model"], str) and r["cpu_model"]
+    assert "2 processes" in r["sample"]
 
 
 def test_conv_alg_bytes_lds_regime():
