@@ -143,6 +143,28 @@ int hyena_fwd_profiled(const hyena_layer *layer, const void *u, const void *w_in
                        int B, int dtype, void *y, void *ws, size_t ws_bytes, hipStream_t stream,
                        const hipEvent_t *events);
 
+/* Size of the workspace array inside the library that hyena_fwd_noalloc uses:
+ * 128 MiB, which holds hyena_workspace_bytes of B = 8, L = 2048, D = 768, N = 2
+ * in bf16 (105 MB) and of every smaller call. */
+#define HYENA_NOALLOC_SCRATCH_BYTES ((size_t)128 << 20)
+
+/* For callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc): hyena_fwd
+ * without the ws argument. The workspace is a file-scope device array of
+ * HYENA_NOALLOC_SCRATCH_BYTES bytes inside the library, one copy per GPU,
+ * resolved on the first call on that GPU and held until the process ends; no
+ * allocation routine is called. The caller still owns every input, the output
+ * and the layer cache.
+ *  - A call whose hyena_workspace_bytes(B, L, D, N, dtype) exceeds the array
+ *    returns HYENA_ERR_WORKSPACE before any HIP call.
+ *  - Every call on one GPU uses the same array and leaves its contents behind:
+ *    calls that overlap on one GPU (other streams, other threads) race and
+ *    must be serialised by the caller.
+ *  - Other arguments, layouts and errors as hyena_fwd. */
+int hyena_fwd_noalloc(const hyena_layer *layer, const void *u, const void *w_in,
+                      const float *short_w, const float *dskip, const void *w_out,
+                      int B, int dtype, void *y, hipStream_t stream);
+
 /* ------------------------------------------------------------------ 3D ---- */
 /*
  * HyenaND on 3D grids (HyenaND explainer, gist.science, "Methodology: HyenaND"):

@@ -1,0 +1,56 @@
+// Forward pass for callers that cannot allocate device memory (code under
+// HIP graph capture, tight serving loops, harnesses that forbid hipMalloc):
+// hyena_fwd with its workspace taken from a file-scope device array instead of
+// a caller buffer. The launch sequence and the kernels are hyena_fwd's own.
+#include "../../include/hyena.h"
+
+#include <hip/hip_runtime.h>
+
+#include <mutex>
+
+// One copy per GPU, alive until the process ends. In host code this name is a
+// host-side stand-in, not a device address: only the pointer that
+// hipGetSymbolAddress returns for the current device may reach a kernel or a
+// copy.
+__device__ __align__(256) unsigned char scratch[HYENA_NOALLOC_SCRATCH_BYTES];
+
+namespace {
+
+constexpr int kMaxDevices = 64;
+std::mutex g_mutex;
+void* g_scratch[kMaxDevices] = {};
+
+// Device address of the current device's copy, resolved once per device.
+int scratch_for_current_device(void** out) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return HYENA_ERR_HIP;
+  std::lock_guard<std::mutex> lock(g_mutex);
+  if (g_scratch[dev] == nullptr) {
+    void* p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || p == nullptr) return HYENA_ERR_HIP;
+    g_scratch[dev] = p;
+  }
+  *out = g_scratch[dev];
+  return HYENA_OK;
+}
+
+}  // namespace
+
+extern "C" int hyena_fwd_noalloc(const hyena_layer* layer, const void* u, const void* w_in, const float* short_w,
+                                 const float* dskip, const void* w_out, int B, int dtype, void* y,
+                                 hipStream_t stream) {
+  if (layer == nullptr) return HYENA_ERR_INVALID_ARG;
+  if (dtype != HYENA_F32 && dtype != HYENA_BF16) return HYENA_ERR_INVALID_ARG;
+  if (B < 1) return HYENA_ERR_INVALID_ARG;
+  // size check on the host, before any HIP call
+  const size_t need = hyena_workspace_bytes(B, layer->L, layer->D, layer->N, dtype);
+  if (need == 0) return HYENA_ERR_UNSUPPORTED;
+  if (need > (size_t)HYENA_NOALLOC_SCRATCH_BYTES) return HYENA_ERR_WORKSPACE;
+  void* ws = nullptr;
+  const int st = scratch_for_current_device(&ws);
+  if (st != HYENA_OK) return st;
+  // hyena_fwd reads only workspace bytes its own launches wrote earlier in the
+  // same call, so the array needs no clearing between calls
+  return hyena_fwd(layer, u, w_in, short_w, dskip, w_out, B, dtype, y, ws, (size_t)HYENA_NOALLOC_SCRATCH_BYTES,
+                   stream);
+}

@@ -71,6 +71,7 @@ SIGNATURES = {
     "hyena_fwd": (_i, [ctypes.POINTER(Layer), _vp, _vp, _vp, _vp, _vp, _i, _i, _vp, _vp, _sz, _vp]),
     "hyena_fwd_profiled": (_i, [ctypes.POINTER(Layer), _vp, _vp, _vp, _vp, _vp, _i, _i, _vp, _vp, _sz, _vp,
                                 ctypes.POINTER(_vp)]),
+    "hyena_fwd_noalloc": (_i, [ctypes.POINTER(Layer), _vp, _vp, _vp, _vp, _vp, _i, _i, _vp, _vp]),
     "hyena_nd_cache_bytes": (_sz, [_i, _i, _i, _i, _i]),
     "hyena_nd_filter_workspace_bytes": (_sz, [_i, _i, _i, _i, _i]),
     "hyena_nd_workspace_bytes": (_sz, [_i, _i, _i, _i, _i, _i]),
@@ -202,6 +203,17 @@ def hyena_fwd(layer: HyenaLayer, u, w_in, short_w, dskip, w_out, y=None, ws=None
     st = lib().hyena_fwd(ctypes.byref(layer.c), _ptr(u), _ptr(w_in), _ptr(short_w), _ptr(dskip), _ptr(w_out),
                          B, dt, _ptr(y), _ptr(ws), ws.numel(), _stream())
     _check(st, "hyena_fwd")
+    return y
+
+
+def hyena_fwd_noalloc(layer: HyenaLayer, u, w_in, short_w, dskip, w_out, y=None):
+    """hyena_fwd with the workspace inside the library (no workspace argument)."""
+    B = u.shape[0]
+    if y is None:
+        y = torch.empty_like(u)
+    st = lib().hyena_fwd_noalloc(ctypes.byref(layer.c), _ptr(u), _ptr(w_in), _ptr(short_w), _ptr(dskip),
+                                 _ptr(w_out), B, _dtype_code(u), _ptr(y), _stream())
+    _check(st, "hyena_fwd_noalloc")
     return y
 
 

@@ -270,3 +270,44 @@ def test_film_argument_errors_before_any_hip_call(hy):
     assert call(ctypes.byref(fp), ctypes.byref(film), ws=need - 1) == 3
     assert L.hyena_nd_film_fwd_profiled(8, 8, 8, 64, 2, 0, ctypes.byref(fp), ctypes.byref(film), *args, 2, p, None,
                                         p, need, None, None) == 1
+
+
+def test_noalloc_rejects_before_any_hip_call(hy):
+    # the allocation-free forward: invalid arguments and workspaces larger than
+    # the library's array are refused on the host
+    L = hy.lib()
+    keep, p = _aligned_buffer(16)
+    layer = hy.Layer()
+    assert L.hyena_fwd_noalloc(None, p, p, p, p, p, 1, 0, p, None) == 1
+    assert L.hyena_layer_init(ctypes.byref(layer), 1024, 64, 2, p, 1 << 30) == 0
+    layer.built = 1
+    assert L.hyena_fwd_noalloc(ctypes.byref(layer), p, p, p, p, p, 1, 7, p, None) == 1    # dtype
+    assert L.hyena_fwd_noalloc(ctypes.byref(layer), p, p, p, p, p, 0, 0, p, None) == 1    # batch
+    big = hy.Layer()
+    assert L.hyena_layer_init(ctypes.byref(big), 65536, 768, 2, p, 1 << 40) == 0
+    big.built = 1
+    limit = 128 << 20
+    assert hy.hyena_workspace_bytes(1, 65536, 768, 2, 1) > limit
+    assert L.hyena_fwd_noalloc(ctypes.byref(big), p, p, p, p, p, 1, 1, p, None) == 3
+    # the call it documents fits (B = 8, L = 2048, D = 768, N = 2, bf16); the first
+    # batch size past the limit is refused
+    assert hy.hyena_workspace_bytes(8, 2048, 768, 2, 1) <= limit
+    mid = hy.Layer()
+    assert L.hyena_layer_init(ctypes.byref(mid), 2048, 768, 2, p, 1 << 40) == 0
+    mid.built = 1
+    b = 8
+    while hy.hyena_workspace_bytes(b + 1, 2048, 768, 2, 1) <= limit:
+        b += 1
+    assert L.hyena_fwd_noalloc(ctypes.byref(mid), p, p, p, p, p, b + 1, 1, p, None) == 3
+
+
+def test_noalloc_without_device_reports_hip_error(hy):
+    import torch
+    if torch.cuda.is_available():
+        pytest.skip("a GPU is present")
+    L = hy.lib()
+    keep, p = _aligned_buffer(16)
+    layer = hy.Layer()
+    assert L.hyena_layer_init(ctypes.byref(layer), 1024, 64, 2, p, 1 << 30) == 0
+    layer.built = 1
+    assert L.hyena_fwd_noalloc(ctypes.byref(layer), p, p, p, p, p, 1, 0, p, None) == 5
