@@ -38,3 +38,17 @@ from .hyena_nd_film_oracle import (  # noqa: F401
     hyena_nd_film_fwd,
     hyena_nd_film_fwd_sampled,
 )
+from .hyena_bwd_oracle import (  # noqa: F401
+    causal_corr_direct,
+    causal_corr_fft,
+    causal_xcorr_direct,
+    causal_xcorr_fft,
+    noncausal_corr_direct,
+    noncausal_corr_fft,
+    noncausal_xcorr_direct,
+    noncausal_xcorr_fft,
+    short_conv_bwd,
+    hyena_bwd,
+    implicit_filter_bwd,
+    implicit_filter_noncausal_bwd,
+)
