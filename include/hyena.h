@@ -165,6 +165,59 @@ int hyena_fwd_noalloc(const hyena_layer *layer, const void *u, const void *w_in,
                       const float *short_w, const float *dskip, const void *w_out,
                       int B, int dtype, void *y, hipStream_t stream);
 
+/* ------------------------------------------------------------ 1D backward ---- */
+/*
+ * Gradients of a scalar loss through the layer (its vector-Jacobian product).
+ * The pages' compute and speed claims are about training (Hyena Hierarchy
+ * abstract: training compute at sequence length 2K; HyenaDNA abstract: training
+ * speed at long contexts); they give no backward formulas, so these are the
+ * chain rule of the forward steps in reverse order. With g = dz^{n+1}:
+ *   dW_out = sum_b z^{N+1}_b^T dy_b,  dz^{N+1} = dy W_out^T
+ *   dx^n = g c^n,  dD^n = sum_{b,t} g z^n,
+ *   dz^n = D^n g + sum_{tau} h^n(tau) (g x^n)(t + tau)        (correlation: the
+ *          transpose of the convolution; two-sided filters over signed lags)
+ *   dh^n(tau) = sum_{b,t} (g x^n)(t) z^n(t - tau)
+ *   dp_j(t) = sum_k short_w[j][k] ds_j(t + k),  dshort_w[j][k] = sum_{b,t} ds_j(t) p_j(t - k)
+ *   du = dp W_in^T,  dW_in = sum_b u_b^T dp_b,   ds = (dz^1, dx^1 .. dx^N)
+ * The correlations run through the layer's cached filter spectra (conjugated).
+ * Supported: the on-chip regime, L a power of two in [32, 4096]; otherwise as
+ * hyena_fwd. Every gradient is recomputed from the inputs (nothing is kept from
+ * a forward call). The batch sums are taken in a fixed order, so results are
+ * bit-reproducible.
+ */
+size_t hyena_bwd_workspace_bytes(int B, int L, int D, int N, int dtype, int direction);
+
+/* Inputs as hyena_fwd, plus
+ *   dy       [B][L][D]      dtype, gradient of the loss with respect to y
+ * Outputs (overwritten, not accumulated into):
+ *   du       [B][L][D]      dtype
+ *   dw_in    [D][(N+1)*D]   fp32
+ *   dshort_w [(N+1)*D][3]   fp32
+ *   ddskip   [N][D]         fp32
+ *   dw_out   [D][D]         fp32
+ *   dh       [N][D][L] fp32 (causal) or the wrapped [N][D][2L] of h_out
+ *            (non-causal; entry L, no filter tap, is 0): gradient with respect
+ *            to the filters h^n; hyena_filter_bwd carries it to the generator's
+ *            parameters.
+ *   ws       scratch of hyena_bwd_workspace_bytes(B, L, D, N, dtype, layer->direction)
+ * The layer must be built (hyena_filter_gen) for the same (L, D, N). */
+int hyena_bwd(const hyena_layer *layer, const void *u, const void *w_in, const float *short_w,
+              const float *dskip, const void *w_out, const void *dy, int B, int dtype,
+              void *du, float *dw_in, float *dshort_w, float *ddskip, float *dw_out, float *dh,
+              void *ws, size_t ws_bytes, hipStream_t stream);
+
+/* Scratch for hyena_filter_bwd; 0 for unsupported sizes (those of hyena_cache_bytes;
+ * 1 <= pe_freqs <= 32; width a multiple of 16 in [16, 128]) or directions. */
+size_t hyena_filter_bwd_workspace_bytes(int L, int D, int N, int pe_freqs, int width, int direction);
+
+/* Gradients of sum(dh * h) with respect to the generator's parameters, h as
+ * hyena_filter_gen evaluates it for the layer's direction (dh in h_out's layout):
+ *   dw1 [1+2K][W], db1 [W], dw2 [W][W], db2 [W], dw3 [W][N*D], db3 [N*D], ddecay [D]
+ * all fp32, overwritten. p: the parameters the filters were generated from. */
+int hyena_filter_bwd(const hyena_layer *layer, const hyena_filter_params *p, const float *dh,
+                     float *dw1, float *db1, float *dw2, float *db2, float *dw3, float *db3, float *ddecay,
+                     void *ws, size_t ws_bytes, hipStream_t stream);
+
 /* ------------------------------------------------------------------ 3D ---- */
 /*
  * HyenaND on 3D grids (HyenaND explainer, gist.science, "Methodology: HyenaND"):

@@ -210,7 +210,7 @@ def hyena_bwd(u, w_in, short_w, dskip, w_out, h, dy, conv: str = "auto", causal:
         zs.append(xs[n] * c + dskip[n][None, :, None] * zs[-1])
 
     # backward
-    dw_out = np.einsum("bct,btd->cd", zs[N], dy)
+    dw_out = np.tensordot(zs[N], dy, axes=([0, 2], [0, 1]))              # sum over b, t
     g = np.ascontiguousarray((dy @ w_out.T).transpose(0, 2, 1))          # dz^{N+1}, [B, D, L]
     dxs = [None] * N
     ddskip = np.zeros((N, D))
@@ -224,7 +224,7 @@ def hyena_bwd(u, w_in, short_w, dskip, w_out, h, dy, conv: str = "auto", causal:
     ds_cm = np.concatenate([g] + dxs, axis=1)                              # [B, (N+1)D, L]
     dp, dshort = short_conv_bwd(p, ds_cm.transpose(0, 2, 1), short_w)
     du = dp @ w_in.T
-    dw_in = np.einsum("btd,btj->dj", u, dp)
+    dw_in = np.tensordot(u, dp, axes=([0, 1], [0, 1]))                  # sum over b, t
     return dict(du=du, dw_in=dw_in, dshort_w=dshort, ddskip=ddskip, dw_out=dw_out, dh=dh)
 
 

@@ -169,6 +169,77 @@ int group_pairs(int pairs_all, size_t y_bytes_per_pair) {
   return (int)((pairs_all + ng - 1) / ng);
 }
 
+// ---------------------------------------------------------------- backward
+constexpr int kBwdMinL = 32;  // the weight-gradient products take K = L in whole bf16 K tiles
+
+bool bwd_shape_ok(int L, int D, int N) { return shape_ok(L, D, N) && L >= kBwdMinL && L <= kLdsMaxL; }
+
+struct BwdWs {
+  size_t wt_in, s, p, gz, zsave, csave, zfin, sbar, pbar, dh_part, dd_part, dsw_part, dyT, uT, dwo_part, dwi_part,
+      total;
+};
+BwdWs bwd_ws(int B, int L, int D, int N, int dtype, int dir) {
+  BwdWs w{};
+  const size_t es = dtype == HYENA_BF16 ? 2 : 4;
+  const size_t J = (size_t)(N + 1) * D, HL = dir == HYENA_NONCAUSAL ? 2 * (size_t)L : L;
+  const size_t BDL = (size_t)B * D * L, BJL = (size_t)B * J * L;
+  size_t off = 0;
+  auto take = [&](size_t& at, size_t bytes) {
+    at = off;
+    off = align_up(off + bytes, kAlign);
+  };
+  take(w.wt_in, J * D * es);
+  take(w.s, BJL * es);
+  take(w.p, BJL * es);
+  take(w.gz, BDL * es);
+  take(w.zsave, (size_t)N * BDL * 4);
+  take(w.csave, (size_t)N * BDL * 4);
+  take(w.zfin, BDL * es);
+  take(w.sbar, BJL * 4);
+  take(w.pbar, BJL * es);
+  take(w.dh_part, (size_t)B * N * D * HL * 4);
+  take(w.dd_part, (size_t)B * N * D * 4);
+  take(w.dsw_part, (size_t)B * J * 3 * 4);
+  take(w.dyT, BDL * es);
+  take(w.uT, BDL * es);
+  take(w.dwo_part, (size_t)B * D * D * es);
+  take(w.dwi_part, (size_t)B * D * J * es);
+  w.total = off;
+  return w;
+}
+
+struct FilterBwdWs {
+  size_t e, a1, c1, a2, c2, w3t, o, dout, g2, g1, a2t, a1t, et, d2t, d1t, total;
+};
+FilterBwdWs filter_bwd_ws(int L, int D, int N, int K, int W, int dir) {
+  FilterBwdWs w{};
+  const size_t P = dir == HYENA_NONCAUSAL ? 2 * (size_t)L : L, F = 1 + 2 * (size_t)K, ND = (size_t)N * D;
+  size_t off = 0;
+  auto take = [&](size_t& at, size_t floats) {
+    at = off;
+    off = align_up(off + floats * 4, kAlign);
+  };
+  take(w.e, P * F);
+  take(w.a1, P * W);
+  take(w.c1, P * W);
+  take(w.a2, P * W);
+  take(w.c2, P * W);
+  take(w.w3t, ND * W);
+  take(w.o, ND * P);
+  take(w.dout, ND * P);
+  take(w.g2, P * W);
+  take(w.g1, P * W);
+  take(w.a2t, P * W);
+  take(w.a1t, P * W);
+  take(w.et, P * F);
+  take(w.d2t, P * W);
+  take(w.d1t, P * W);
+  w.total = off;
+  return w;
+}
+
+bool filter_bwd_params_ok(int K, int W) { return K >= 1 && K <= 32 && W >= 16 && W <= 128 && W % 16 == 0; }
+
 }  // namespace
 
 extern "C" {
@@ -342,6 +413,162 @@ int hyena_fwd_profiled(const hyena_layer* layer, const void* u, const void* w_in
                        hipStream_t stream, const hipEvent_t* events) {
   if (events == nullptr) return HYENA_ERR_INVALID_ARG;
   return fwd_impl(layer, u, w_in, short_w, dskip, w_out, B, dtype, y, ws, ws_bytes, stream, events);
+}
+
+size_t hyena_bwd_workspace_bytes(int B, int L, int D, int N, int dtype, int direction) {
+  if (!bwd_shape_ok(L, D, N) || B < 1 || (dtype != HYENA_F32 && dtype != HYENA_BF16) || !direction_ok(direction))
+    return 0;
+  if ((long long)B * L * (N + 1) * D >= (1LL << 31)) return 0;
+  return bwd_ws(B, L, D, N, dtype, direction).total;
+}
+
+int hyena_bwd(const hyena_layer* layer, const void* u, const void* w_in, const float* short_w, const float* dskip,
+              const void* w_out, const void* dy, int B, int dtype, void* du, float* dw_in, float* dshort_w,
+              float* ddskip, float* dw_out, float* dh, void* ws, size_t ws_bytes, hipStream_t stream) {
+  if (layer == nullptr) return HYENA_ERR_INVALID_ARG;
+  if (dtype != HYENA_F32 && dtype != HYENA_BF16) return HYENA_ERR_INVALID_ARG;
+  const void* ptrs[] = {u, w_in, short_w, dskip, w_out, dy, du, dw_in, dshort_w, ddskip, dw_out, dh, ws};
+  for (const void* q : ptrs)
+    if (!aligned16(q)) return HYENA_ERR_INVALID_ARG;
+  if (B < 1) return HYENA_ERR_INVALID_ARG;
+  const int L = layer->L, D = layer->D, N = layer->N, dir = layer->direction;
+  if (!bwd_shape_ok(L, D, N) || !direction_ok(dir)) return HYENA_ERR_UNSUPPORTED;
+  if (!layer->built || !aligned16(layer->cache)) return HYENA_ERR_LAYER_MISMATCH;
+  const CacheLayout cl = cache_layout(L, D, N);
+  if (layer->cache_bytes < cl.total) return HYENA_ERR_LAYER_MISMATCH;
+  if ((long long)B * L * (N + 1) * D >= (1LL << 31)) return HYENA_ERR_UNSUPPORTED;
+  const BwdWs w = bwd_ws(B, L, D, N, dtype, dir);
+  if (ws_bytes < w.total) return HYENA_ERR_WORKSPACE;
+  if (device_ok() != HYENA_OK) return HYENA_ERR_HIP;
+
+  const bool bf = dtype == HYENA_BF16;
+  const size_t es = bf ? 2 : 4;
+  char* wb = static_cast<char*>(ws);
+  char* cb = static_cast<char*>(layer->cache);
+  const int J = (N + 1) * D, HL = dir == HYENA_NONCAUSAL ? 2 * L : L;
+  // forward projections: s (with the short convolution) and p (without), channel-major
+  HY_CHECK_HIP(hy::transpose2d(w_in, wb + w.wt_in, D, J, bf, stream));
+  HY_CHECK_HIP(hy::gemm(hy::GemmArgs{u, wb + w.wt_in, wb + w.s, B * L, J, D, L, false, true, short_w}, bf, stream));
+  HY_CHECK_HIP(hy::gemm(hy::GemmArgs{u, wb + w.wt_in, wb + w.p, B * L, J, D, L, false, true, nullptr}, bf, stream));
+  // dz^{N+1} = dy W_out^T, channel-major (W_out as stored is the transposed operand)
+  HY_CHECK_HIP(hy::gemm(hy::GemmArgs{dy, w_out, wb + w.gz, B * L, D, D, L, false, true, nullptr}, bf, stream));
+  // forward recompute and the orders in reverse
+  hy::BwdConvArgs a{};
+  a.s = wb + w.s;
+  a.gz = wb + w.gz;
+  a.zsave = reinterpret_cast<float*>(wb + w.zsave);
+  a.csave = reinterpret_cast<float*>(wb + w.csave);
+  a.zfin = wb + w.zfin;
+  a.dskip = dskip;
+  a.pq = reinterpret_cast<const float4*>(cb + cl.pq);
+  a.tw = reinterpret_cast<const float2*>(cb + cl.tw);
+  a.sbar = reinterpret_cast<float*>(wb + w.sbar);
+  a.dh_part = reinterpret_cast<float*>(wb + w.dh_part);
+  a.dd_part = reinterpret_cast<float*>(wb + w.dd_part);
+  a.B = B;
+  a.L = L;
+  a.D = D;
+  a.NO = N;
+  a.HL = HL;
+  HY_CHECK_HIP(hy::bwd_lds_conv(a, bf, stream));
+  // short convolution transpose: dp, and per-sample tap gradients
+  HY_CHECK_HIP(hy::short_conv_bwd(a.sbar, wb + w.p, short_w, wb + w.pbar, reinterpret_cast<float*>(wb + w.dsw_part),
+                                  B * J, L, J, bf, stream));
+  // du = dp W_in^T (dp channel-major; W_in as stored is the transposed operand)
+  HY_CHECK_HIP(hy::gemm(hy::GemmArgs{wb + w.pbar, w_in, du, B * L, D, J, L, true, false, nullptr}, bf, stream));
+  // per-sample weight gradients: dW_out_b = z^{N+1}_b dy_b, dW_in_b = u_b^T dp_b (K = L)
+  for (int b = 0; b < B; ++b) {
+    const size_t ob = (size_t)b * L * D * es;
+    char* dyT = wb + w.dyT + ob;
+    char* uT = wb + w.uT + ob;
+    HY_CHECK_HIP(hy::transpose2d(static_cast<const char*>(dy) + ob, dyT, L, D, bf, stream));
+    HY_CHECK_HIP(hy::transpose2d(static_cast<const char*>(u) + ob, uT, L, D, bf, stream));
+    HY_CHECK_HIP(hy::gemm(hy::GemmArgs{wb + w.zfin + ob, dyT, wb + w.dwo_part + (size_t)b * D * D * es, D, D, L, L,
+                                       false, false, nullptr},
+                          bf, stream));
+    HY_CHECK_HIP(hy::gemm(hy::GemmArgs{uT, wb + w.pbar + (size_t)b * J * L * es, wb + w.dwi_part + (size_t)b * D * J * es,
+                                       D, J, L, L, false, false, nullptr},
+                          bf, stream));
+  }
+  // sums over the batch, in a fixed order
+  HY_CHECK_HIP(hy::sum_rows(wb + w.dwo_part, dw_out, B, (size_t)D * D, (size_t)D * D, bf, stream));
+  HY_CHECK_HIP(hy::sum_rows(wb + w.dwi_part, dw_in, B, (size_t)D * J, (size_t)D * J, bf, stream));
+  HY_CHECK_HIP(hy::sum_rows(a.dh_part, dh, B, (size_t)N * D * HL, (size_t)N * D * HL, false, stream));
+  HY_CHECK_HIP(hy::sum_rows(a.dd_part, ddskip, B, (size_t)N * D, (size_t)N * D, false, stream));
+  HY_CHECK_HIP(hy::sum_rows(wb + w.dsw_part, dshort_w, B, (size_t)J * 3, (size_t)J * 3, false, stream));
+  return HYENA_OK;
+}
+
+size_t hyena_filter_bwd_workspace_bytes(int L, int D, int N, int pe_freqs, int width, int direction) {
+  if (!shape_ok(L, D, N) || !direction_ok(direction) || !filter_bwd_params_ok(pe_freqs, width)) return 0;
+  return filter_bwd_ws(L, D, N, pe_freqs, width, direction).total;
+}
+
+int hyena_filter_bwd(const hyena_layer* layer, const hyena_filter_params* p, const float* dh, float* dw1, float* db1,
+                     float* dw2, float* db2, float* dw3, float* db3, float* ddecay, void* ws, size_t ws_bytes,
+                     hipStream_t stream) {
+  if (layer == nullptr || p == nullptr) return HYENA_ERR_INVALID_ARG;
+  const int L = layer->L, D = layer->D, N = layer->N, dir = layer->direction;
+  if (!shape_ok(L, D, N) || !direction_ok(dir)) return HYENA_ERR_UNSUPPORTED;
+  if (!filter_bwd_params_ok(p->pe_freqs, p->width)) return HYENA_ERR_UNSUPPORTED;
+  const void* ptrs[] = {p->w1, p->b1, p->w2, p->b2, p->w3, p->b3, p->decay, dh, dw1, db1, dw2, db2, dw3, db3, ddecay,
+                        ws};
+  for (const void* q : ptrs)
+    if (!aligned16(q)) return HYENA_ERR_INVALID_ARG;
+  const FilterBwdWs w = filter_bwd_ws(L, D, N, p->pe_freqs, p->width, dir);
+  if (ws_bytes < w.total) return HYENA_ERR_WORKSPACE;
+  if (device_ok() != HYENA_OK) return HYENA_ERR_HIP;
+
+  char* wb = static_cast<char*>(ws);
+  auto f = [&](size_t off) { return reinterpret_cast<float*>(wb + off); };
+  const int W = p->width, F = 1 + 2 * p->pe_freqs, ND = N * D;
+  const int P = dir == HYENA_NONCAUSAL ? 2 * L : L;
+  hy::FilterBwdArgs a{};
+  a.L = L;
+  a.D = D;
+  a.NO = N;
+  a.K = p->pe_freqs;
+  a.W = W;
+  a.noncausal = dir == HYENA_NONCAUSAL ? 1 : 0;
+  a.w1 = p->w1;
+  a.b1 = p->b1;
+  a.w2 = p->w2;
+  a.b2 = p->b2;
+  a.b3 = p->b3;
+  a.decay = p->decay;
+  a.dh = dh;
+  a.o = f(w.o);
+  a.e = f(w.e);
+  a.a1 = f(w.a1);
+  a.c1 = f(w.c1);
+  a.a2 = f(w.a2);
+  a.c2 = f(w.c2);
+  a.dout = f(w.dout);
+  a.ddecay = ddecay;
+  // features and hidden layers; output layer o = a2 W3 (channel-major, without b3)
+  HY_CHECK_HIP(hy::filter_bwd_feat(a, stream));
+  HY_CHECK_HIP(hy::transpose2d(p->w3, f(w.w3t), W, ND, false, stream));
+  HY_CHECK_HIP(hy::gemm(hy::GemmArgs{a.a2, f(w.w3t), f(w.o), P, ND, W, P, false, true, nullptr}, false, stream));
+  // dL/do = dh * window (and the decay gradient)
+  HY_CHECK_HIP(hy::filter_bwd_out(a, stream));
+  // back through the hidden layers: dq2 = (do W3^T) cos(q2), dq1 = (dq2 W2^T) cos(q1)
+  HY_CHECK_HIP(hy::gemm(hy::GemmArgs{f(w.dout), p->w3, f(w.g2), P, W, ND, P, true, false, nullptr}, false, stream));
+  HY_CHECK_HIP(hy::mul_inplace(f(w.g2), a.c2, (size_t)P * W, stream));
+  HY_CHECK_HIP(hy::gemm(hy::GemmArgs{f(w.g2), p->w2, f(w.g1), P, W, W, P, false, false, nullptr}, false, stream));
+  HY_CHECK_HIP(hy::mul_inplace(f(w.g1), a.c1, (size_t)P * W, stream));
+  // weight gradients as products over the positions (K = P)
+  HY_CHECK_HIP(hy::transpose2d(a.a2, f(w.a2t), P, W, false, stream));
+  HY_CHECK_HIP(hy::transpose2d(a.a1, f(w.a1t), P, W, false, stream));
+  HY_CHECK_HIP(hy::transpose2d(a.e, f(w.et), P, F, false, stream));
+  HY_CHECK_HIP(hy::transpose2d(f(w.g2), f(w.d2t), P, W, false, stream));
+  HY_CHECK_HIP(hy::transpose2d(f(w.g1), f(w.d1t), P, W, false, stream));
+  HY_CHECK_HIP(hy::gemm(hy::GemmArgs{f(w.a2t), f(w.dout), dw3, W, ND, P, P, false, false, nullptr}, false, stream));
+  HY_CHECK_HIP(hy::gemm(hy::GemmArgs{f(w.a1t), f(w.d2t), dw2, W, W, P, P, false, false, nullptr}, false, stream));
+  HY_CHECK_HIP(hy::gemm(hy::GemmArgs{f(w.et), f(w.d1t), dw1, F, W, P, P, false, false, nullptr}, false, stream));
+  HY_CHECK_HIP(hy::row_sums(f(w.dout), db3, ND, P, stream));
+  HY_CHECK_HIP(hy::row_sums(f(w.d2t), db2, W, P, stream));
+  HY_CHECK_HIP(hy::row_sums(f(w.d1t), db1, W, P, stream));
+  return HYENA_OK;
 }
 
 }  // extern "C"

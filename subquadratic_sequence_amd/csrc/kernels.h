@@ -80,4 +80,42 @@ hipError_t fourstep_conv(const FourStepTables& tb, const FourStepConvArgs& c, bo
 hipError_t fourstep_spec(const FourStepTables& tb, const float* h, float2* Y, float4* pq, void* pq_bf16, int L,
                          int D, int NO, bool wrapped, hipStream_t s);
 
+// --------------------------------------------------------- backward (2L <= 8192)
+struct BwdConvArgs {
+  const void* s;         // short-convolved projections [B][(NO+1)D][L] (storage type)
+  const void* gz;        // dz^{NO+1} [B][D][L] (storage type)
+  float* zsave;          // z^1 .. z^NO [NO][B][D][L]
+  float* csave;          // c^1 .. c^NO [NO][B][D][L]
+  void* zfin;            // z^{NO+1} [B][D][L] (storage type)
+  const float* dskip;    // [NO][D]
+  const float4* pq;      // [NO][D/2][L+1]
+  const float2* tw;      // [2L]
+  float* sbar;           // ds = (dz^1, dx^1 .. dx^NO) [B][(NO+1)D][L]
+  float* dh_part;        // per-sample filter gradients [B][NO][D][HL]
+  float* dd_part;        // per-sample skip gradients [B][NO][D]
+  int B, L, D, NO, HL;   // HL = L causal, 2L wrapped two-sided
+};
+hipError_t bwd_lds_conv(const BwdConvArgs& a, bool bf16, hipStream_t s);
+// dp and per-row short-conv tap gradients from ds (rows = B (NO+1) D of length L)
+hipError_t short_conv_bwd(const float* sbar, const void* p, const float* short_w, void* pbar, float* dsw_part, int rows,
+                          int L, int J, bool bf16, hipStream_t s);
+// out[i] = sum_{r < R} in[r stride + i], i < n (in: fp32 or bf16)
+hipError_t sum_rows(const void* in, float* out, int R, size_t stride, size_t n, bool in_bf16, hipStream_t s);
+// out[r] = sum_k in[r K + k]
+hipError_t row_sums(const float* in, float* out, int rows, int K, hipStream_t s);
+
+struct FilterBwdArgs {
+  int L, D, NO, K, W, noncausal;
+  const float *w1, *b1, *w2, *b2, *b3, *decay;
+  const float* dh;       // [NO][D][P], P = L or 2L (wrapped two-sided)
+  const float* o;        // MLP output, channel-major [NO D][P]
+  float* e;              // features [P][1 + 2K]
+  float *a1, *c1, *a2, *c2;  // hidden activations and cosines of their pre-activations [P][W]
+  float* dout;           // dL/do [NO D][P]
+  float* ddecay;         // [D]
+};
+hipError_t filter_bwd_feat(const FilterBwdArgs& a, hipStream_t s);
+hipError_t filter_bwd_out(const FilterBwdArgs& a, hipStream_t s);
+hipError_t mul_inplace(float* x, const float* y, size_t n, hipStream_t s);
+
 }  // namespace hy

@@ -72,6 +72,12 @@ SIGNATURES = {
     "hyena_fwd_profiled": (_i, [ctypes.POINTER(Layer), _vp, _vp, _vp, _vp, _vp, _i, _i, _vp, _vp, _sz, _vp,
                                 ctypes.POINTER(_vp)]),
     "hyena_fwd_noalloc": (_i, [ctypes.POINTER(Layer), _vp, _vp, _vp, _vp, _vp, _i, _i, _vp, _vp]),
+    "hyena_bwd_workspace_bytes": (_sz, [_i, _i, _i, _i, _i, _i]),
+    "hyena_bwd": (_i, [ctypes.POINTER(Layer), _vp, _vp, _vp, _vp, _vp, _vp, _i, _i, _vp, _vp, _vp, _vp, _vp, _vp, _vp,
+                       _sz, _vp]),
+    "hyena_filter_bwd_workspace_bytes": (_sz, [_i, _i, _i, _i, _i, _i]),
+    "hyena_filter_bwd": (_i, [ctypes.POINTER(Layer), ctypes.POINTER(FilterParams), _vp, _vp, _vp, _vp, _vp, _vp, _vp,
+                              _vp, _vp, _sz, _vp]),
     "hyena_nd_cache_bytes": (_sz, [_i, _i, _i, _i, _i]),
     "hyena_nd_filter_workspace_bytes": (_sz, [_i, _i, _i, _i, _i]),
     "hyena_nd_workspace_bytes": (_sz, [_i, _i, _i, _i, _i, _i]),
@@ -231,6 +237,56 @@ def hyena_fwd_profiled(layer: HyenaLayer, u, w_in, short_w, dskip, w_out, y, ws,
     st = lib().hyena_fwd_profiled(ctypes.byref(layer.c), _ptr(u), _ptr(w_in), _ptr(short_w), _ptr(dskip),
                                   _ptr(w_out), B, _dtype_code(u), _ptr(y), _ptr(ws), ws.numel(), _stream(), handles)
     _check(st, "hyena_fwd_profiled")
+
+
+# ------------------------------------------------------------------ 1D backward
+
+
+def hyena_bwd_workspace_bytes(B, L, D, N, dtype, direction=CAUSAL) -> int:
+    return lib().hyena_bwd_workspace_bytes(B, L, D, N, dtype, direction)
+
+
+def hyena_bwd(layer: HyenaLayer, u, w_in, short_w, dskip, w_out, dy, ws=None):
+    """Gradients of sum(dy * y), y = hyena_fwd(layer, u, ...): a dict with du
+    (dtype of u) and fp32 dw_in, dshort_w, ddskip, dw_out, dh."""
+    B = u.shape[0]
+    dt = _dtype_code(u)
+    L, D, N = layer.L, layer.D, layer.N
+    dev = u.device
+    f32 = dict(dtype=torch.float32, device=dev)
+    hl = L if layer.direction == CAUSAL else 2 * L
+    g = dict(du=torch.empty_like(u), dw_in=torch.empty(D, (N + 1) * D, **f32),
+             dshort_w=torch.empty((N + 1) * D, 3, **f32), ddskip=torch.empty(N, D, **f32),
+             dw_out=torch.empty(D, D, **f32), dh=torch.empty(N, D, hl, **f32))
+    if ws is None:
+        need = hyena_bwd_workspace_bytes(B, L, D, N, dt, layer.direction)
+        ws = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
+    st = lib().hyena_bwd(ctypes.byref(layer.c), _ptr(u), _ptr(w_in), _ptr(short_w), _ptr(dskip), _ptr(w_out),
+                         _ptr(dy), B, dt, _ptr(g["du"]), _ptr(g["dw_in"]), _ptr(g["dshort_w"]), _ptr(g["ddskip"]),
+                         _ptr(g["dw_out"]), _ptr(g["dh"]), _ptr(ws), ws.numel(), _stream())
+    _check(st, "hyena_bwd")
+    return g
+
+
+def hyena_filter_bwd_workspace_bytes(L, D, N, pe_freqs, width, direction=CAUSAL) -> int:
+    return lib().hyena_filter_bwd_workspace_bytes(L, D, N, pe_freqs, width, direction)
+
+
+def hyena_filter_bwd(layer: HyenaLayer, w1, b1, w2, b2, w3, b3, decay, pe_freqs: int, dh, ws=None):
+    """Gradients of sum(dh * h) with respect to the filter generator's parameters:
+    a dict with w1, b1, w2, b2, w3, b3, decay (fp32, shapes of the parameters)."""
+    width = w1.shape[1]
+    p = FilterParams(pe_freqs, width, _ptr(w1), _ptr(b1), _ptr(w2), _ptr(b2), _ptr(w3), _ptr(b3), _ptr(decay))
+    g = {k: torch.empty_like(v) for k, v in (("w1", w1), ("b1", b1), ("w2", w2), ("b2", b2), ("w3", w3), ("b3", b3),
+                                              ("decay", decay))}
+    if ws is None:
+        need = hyena_filter_bwd_workspace_bytes(layer.L, layer.D, layer.N, pe_freqs, width, layer.direction)
+        ws = torch.empty(max(need, 1), dtype=torch.uint8, device=dh.device)
+    st = lib().hyena_filter_bwd(ctypes.byref(layer.c), ctypes.byref(p), _ptr(dh), _ptr(g["w1"]), _ptr(g["b1"]),
+                                _ptr(g["w2"]), _ptr(g["b2"]), _ptr(g["w3"]), _ptr(g["b3"]), _ptr(g["decay"]),
+                                _ptr(ws), ws.numel(), _stream())
+    _check(st, "hyena_filter_bwd")
+    return g
 
 
 # ------------------------------------------------------------------ 3D

@@ -311,3 +311,46 @@ def test_noalloc_without_device_reports_hip_error(hy):
     assert L.hyena_layer_init(ctypes.byref(layer), 1024, 64, 2, p, 1 << 30) == 0
     layer.built = 1
     assert L.hyena_fwd_noalloc(ctypes.byref(layer), p, p, p, p, p, 1, 0, p, None) == 5
+
+
+def test_bwd_validation_before_any_hip_call(hy):
+    L = hy.lib()
+    keep, p = _aligned_buffer(16)
+    # sizes: on-chip regime only, L >= 32
+    assert hy.hyena_bwd_workspace_bytes(1, 1024, 64, 2, 0, 0) > 0
+    assert hy.hyena_bwd_workspace_bytes(1, 8192, 64, 2, 0, 0) == 0
+    assert hy.hyena_bwd_workspace_bytes(1, 16, 64, 2, 0, 0) == 0
+    assert hy.hyena_bwd_workspace_bytes(1, 1024, 64, 2, 0, 9) == 0
+    # two-sided filters need the wrapped 2L gradient rows
+    assert hy.hyena_bwd_workspace_bytes(1, 1024, 64, 2, 0, 1) > hy.hyena_bwd_workspace_bytes(1, 1024, 64, 2, 0, 0)
+    layer = hy.Layer()
+    assert L.hyena_layer_init(ctypes.byref(layer), 1024, 64, 2, p, 1 << 30) == 0
+    need = hy.hyena_bwd_workspace_bytes(1, 1024, 64, 2, 0, 0)
+    args = [p] * 6
+    outs = [p] * 6
+    assert L.hyena_bwd(ctypes.byref(layer), *args, 1, 0, *outs, p, need, None) == 4        # not built
+    layer.built = 1
+    assert L.hyena_bwd(ctypes.byref(layer), *args, 1, 0, *outs, p, need - 1, None) == 3    # workspace
+    assert L.hyena_bwd(ctypes.byref(layer), *args, 0, 0, *outs, p, need, None) == 1        # batch
+    assert L.hyena_bwd(ctypes.byref(layer), *args, 1, 5, *outs, p, need, None) == 1        # dtype
+    assert L.hyena_bwd(ctypes.byref(layer), None, *args[1:], 1, 0, *outs, p, need, None) == 1
+    big = hy.Layer()
+    assert L.hyena_layer_init(ctypes.byref(big), 8192, 64, 2, p, 1 << 40) == 0
+    big.built = 1
+    assert L.hyena_bwd(ctypes.byref(big), *args, 1, 0, *outs, p, 1 << 40, None) == 2       # four-step regime
+
+
+def test_filter_bwd_validation_before_any_hip_call(hy):
+    L = hy.lib()
+    keep, p = _aligned_buffer(16)
+    assert hy.hyena_filter_bwd_workspace_bytes(1024, 64, 2, 8, 64, 0) > 0
+    assert hy.hyena_filter_bwd_workspace_bytes(1024, 64, 2, 8, 24, 0) == 0   # width not a multiple of 16
+    assert hy.hyena_filter_bwd_workspace_bytes(1024, 64, 2, 33, 64, 0) == 0
+    layer = hy.Layer()
+    assert L.hyena_layer_init(ctypes.byref(layer), 1024, 64, 2, p, 1 << 30) == 0
+    fp = hy.FilterParams(8, 64, p, p, p, p, p, p, p)
+    need = hy.hyena_filter_bwd_workspace_bytes(1024, 64, 2, 8, 64, 0)
+    assert L.hyena_filter_bwd(ctypes.byref(layer), ctypes.byref(fp), p, *([p] * 7), p, need - 1, None) == 3
+    assert L.hyena_filter_bwd(ctypes.byref(layer), ctypes.byref(fp), None, *([p] * 7), p, need, None) == 1
+    fp.width = 40
+    assert L.hyena_filter_bwd(ctypes.byref(layer), ctypes.byref(fp), p, *([p] * 7), p, need, None) == 2
