@@ -254,14 +254,15 @@ typedef struct {
   int boundary;  /* hyena_nd_boundary, set by the init call */
 } hyena_nd_layer;
 
-/* Supported: Y = Z; X, Y, Z powers of two in [4, 64] (zero padded) or in [8, 128]
- * (circular); C a multiple of 64 in [64, 4096]; 1 <= N <= 4; B >= 1. The size
- * queries return 0 for unsupported shapes or boundaries. The calls without _ex
- * are the zero-padded boundary.
+/* Supported: X, Y, Z powers of two, each on its own, in [4, 64] (zero padded)
+ * or in [8, 128] (circular); C a multiple of 64 in [64, 4096]; 1 <= N <= 4;
+ * B >= 1. The size queries return 0 for unsupported shapes or boundaries. The
+ * calls without _ex are the zero-padded boundary.
  * X = 1 is a 2D grid (Y x Z; "Native ND Convolution" covers any dimension):
  * every offset has dx = 0 (coordinate 0, so the x row of w1 does not act), the
  * x axis is never padded, and u, y [B][1][Y][Z][C] are the same memory as
- * [B][Y][Z][C]. All orders of a 2D grid run in one launch. */
+ * [B][Y][Z][C]. All orders of a 2D grid run in one launch, on square planes
+ * (Y = Z). */
 size_t hyena_nd_cache_bytes(int X, int Y, int Z, int C, int N);
 size_t hyena_nd_filter_workspace_bytes(int X, int Y, int Z, int C, int N);
 size_t hyena_nd_workspace_bytes(int B, int X, int Y, int Z, int C, int N);

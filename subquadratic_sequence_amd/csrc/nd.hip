@@ -4,9 +4,10 @@
 // Convolution, Input-Dependent Kernels, Kernel Synthesis, Handling Boundaries).
 //
 // Layouts: activations channel-major [B][C][X][Y][Z] (z contiguous); transform
-// size (MX, MY, MZ) = (2X, 2Y, 2Z) zero padded or (X, Y, Z) circular, square
-// planes (Y = Z). The kernel lives on the matching offset grid, offset d at
-// index d + M/2 per axis, at coordinates d / (M/2).
+// size (MX, MY, MZ) = (2X, 2Y, 2Z) zero padded or (X, Y, Z) circular; the
+// three axes are independent (MY x MZ planes), except on 2D grids (X = 1),
+// whose fused kernel takes square planes. The kernel lives on the matching
+// offset grid, offset d at index d + M/2 per axis, at coordinates d / (M/2).
 //
 // The gate g_{b,c} is one scalar per sample and channel, so it commutes with
 // the convolution and is applied to the convolution output in the spatial
@@ -370,57 +371,72 @@ template <int M, int E, bool INV> struct LineFrom<M, E, M, INV> {
 
 // ======================================================== plane pass
 // One workgroup per (sample pair or filter pair, channel, x-plane). The plane
-// (M x M complex, M = MY = MZ) lives in LDS at [y][z] with row stride M + 1.
-// Thread t works on line t % nlines (one of the lines of a direction) as its
+// (MY x MZ complex) lives in LDS at [y][z] with row stride MZ + 1. Thread t
+// works on line t % nlines (one of the lines of a direction) as its
 // (t / nlines)-th FFT thread, so the 64 lanes of a wave sit on 64 lines.
 enum { PL_FWD_V = 0, PL_FWD_FULL = 1, PL_INV = 2, PL_INV_FWD = 3 };
 
-template <int M> struct PlaneCfg {
-  static constexpr int E = M >= 16 ? 16 : M;
-  static constexpr int T = M / E;       // threads per line
-  static constexpr int RS = M + 1;      // LDS row stride
+template <int MY, int MZ = MY> struct PlaneCfg {
+  static constexpr int EZ = MZ >= 16 ? 16 : MZ;  // values per thread along a row (z)
+  static constexpr int TZ = MZ / EZ;             // threads per row
+  static constexpr int EY = MY >= 16 ? 16 : MY;  // along a column (y)
+  static constexpr int TY = MY / EY;
+  static constexpr int E = EZ, T = TZ;           // the square planes' names
+  static constexpr int RS = MZ + 1;              // LDS row stride
   // every thread owns part of a line in the line stages (at least one wave)
-  static constexpr int THREADS = M * T < 64 ? 64 : M * T;
-  static constexpr int PER = M * M / THREADS;  // plane elements per thread
-  static constexpr size_t LDS = (size_t)M * RS * 8 + 128 * 8;  // plane + W_128 table
+  static constexpr int LT = MY * TZ > MZ * TY ? MY * TZ : MZ * TY;
+  static constexpr int THREADS = LT < 64 ? 64 : LT;
+  static constexpr int PER = MY * MZ / THREADS;  // plane elements per thread
+  static constexpr size_t LDS = (size_t)MY * RS * 8 + 128 * 8;  // plane + W_128 table
 };
+
+// rows (lines along z, MZ points), the first nrows of them
+template <int MY, int MZ, bool INV>
+__device__ __forceinline__ void plane_rows_r(float2* P, int nrows, const float2* tw) {
+  using C = PlaneCfg<MY, MZ>;
+  const int line = threadIdx.x % MY, lt = threadIdx.x / MY;
+  const bool active = line < nrows && lt < C::TZ;
+  LineFrom<MZ, C::EZ, 1, INV>::run(P, line * C::RS, 1, lt, active, tw);
+}
+
+// columns (lines along y, MY points), all MZ of them
+template <int MY, int MZ, bool INV>
+__device__ __forceinline__ void plane_cols_r(float2* P, const float2* tw) {
+  using C = PlaneCfg<MY, MZ>;
+  const int line = threadIdx.x % MZ, lt = threadIdx.x / MZ;
+  const bool active = lt < C::TY;
+  LineFrom<MY, C::EY, 1, INV>::run(P, line, C::RS, lt, active, tw);
+}
 
 template <int M, bool INV>
 __device__ __forceinline__ void plane_rows(float2* P, int nrows, const float2* tw) {
-  using C = PlaneCfg<M>;
-  const int line = threadIdx.x % M, lt = threadIdx.x / M;
-  // rows are lines of length M along z; nrows of them
-  const bool active = line < nrows && lt < C::T;
-  LineFrom<M, C::E, 1, INV>::run(P, line * C::RS, 1, lt, active, tw);
+  plane_rows_r<M, M, INV>(P, nrows, tw);
 }
 
 template <int M, bool INV>
 __device__ __forceinline__ void plane_cols(float2* P, const float2* tw) {
-  using C = PlaneCfg<M>;
-  const int line = threadIdx.x % M, lt = threadIdx.x / M;
-  const bool active = lt < C::T;
-  LineFrom<M, C::E, 1, INV>::run(P, line, C::RS, lt, active, tw);
+  plane_cols_r<M, M, INV>(P, tw);
 }
 
 // Plane element loops run a fixed count per thread (element tid + k THREADS),
 // unrolled, so that all of a thread's loads are in flight together.
-template <int M, int MODE>
-__global__ __launch_bounds__(PlaneCfg<M>::THREADS) void nd_plane_kernel(NdConvArgs a) {
-  using C = PlaneCfg<M>;
+template <int MY, int MZ, int MODE>
+__global__ __launch_bounds__((PlaneCfg<MY, MZ>::THREADS)) void nd_plane_kernel(NdConvArgs a) {
+  using C = PlaneCfg<MY, MZ>;
   constexpr int PER = C::PER;
   extern __shared__ float4 smem4[];
   float2* P = reinterpret_cast<float2*>(smem4);
-  float2* tw = P + M * C::RS;  // W_128^m, m < 128
+  float2* tw = P + MY * C::RS;  // W_128^m, m < 128
   const int X = a.X, Y = a.Y, Z = a.Z;
   const size_t V = (size_t)X * Y * Z;
-  const size_t plane = (size_t)M * M;
+  const size_t plane = (size_t)MY * MZ;
   const int x = blockIdx.x;          // plane index
   const int c = blockIdx.y;          // channel (or filter pair)
   const int bp = blockIdx.z;         // sample pair (or order of the filter)
   const int tid = threadIdx.x;
   for (int i = tid; i < 128; i += C::THREADS) tw[i] = a.tw128[i];  // visible after the next barrier
   auto el = [&](int k) { return tid + k * C::THREADS; };           // this thread's k-th element
-  auto lds = [&](int i) { return (i / M) * C::RS + i % M; };
+  auto lds = [&](int i) { return (i / MZ) * C::RS + i % MZ; };
 
   if constexpr (MODE == PL_FWD_FULL) {
     // filter: full M x M complex plane, all MX planes
@@ -431,8 +447,8 @@ __global__ __launch_bounds__(PlaneCfg<M>::THREADS) void nd_plane_kernel(NdConvAr
 #pragma unroll
     for (int k = 0; k < PER; ++k) P[lds(el(k))] = t[k];
     __syncthreads();
-    plane_rows<M, false>(P, M, tw);
-    plane_cols<M, false>(P, tw);
+    plane_rows_r<MY, MZ, false>(P, MY, tw);
+    plane_cols_r<MY, MZ, false>(P, tw);
 #pragma unroll
     for (int k = 0; k < PER; ++k) Fp[el(k)] = P[lds(el(k))];
     return;
@@ -453,7 +469,7 @@ __global__ __launch_bounds__(PlaneCfg<M>::THREADS) void nd_plane_kernel(NdConvAr
     float2 t[PER];
 #pragma unroll
     for (int k = 0; k < PER; ++k) {
-      const int y = el(k) / M, z = el(k) % M;
+      const int y = el(k) / MZ, z = el(k) % MZ;
       t[k] = make_float2(0.f, 0.f);
       if (y < Y && z < Z) t[k] = make_float2(v0[y * Z + z], has_b1 ? v1[y * Z + z] : 0.f);
     }
@@ -469,8 +485,8 @@ __global__ __launch_bounds__(PlaneCfg<M>::THREADS) void nd_plane_kernel(NdConvAr
       for (int k = 0; k < PER; ++k) P[lds(el(k))] = t[k];
     }
     __syncthreads();
-    plane_cols<M, true>(P, tw);
-    plane_rows<M, true>(P, Y, tw);
+    plane_cols_r<MY, MZ, true>(P, tw);
+    plane_rows_r<MY, MZ, true>(P, Y, tw);
     // gate and skip on the kept Y x Z block
     const int n = a.n;
     const float* x0 = s0 + (size_t)((n + 1) * CC + c) * V + xoff;
@@ -490,7 +506,7 @@ __global__ __launch_bounds__(PlaneCfg<M>::THREADS) void nd_plane_kernel(NdConvAr
     constexpr int NB = BATCH ? PER : 1;
     float gx0[NB], gx1[NB], gz0[NB], gz1[NB];
     auto gate_in = [&](int k, int j) {
-      const int y = el(k) / M, z = el(k) % M;
+      const int y = el(k) / MZ, z = el(k) % MZ;
       const int q = (y < Y && z < Z) ? y * Z + z : 0;
       gx0[j] = x0[q];
       gz0[j] = z0[q];
@@ -503,7 +519,7 @@ __global__ __launch_bounds__(PlaneCfg<M>::THREADS) void nd_plane_kernel(NdConvAr
     }
 #pragma unroll
     for (int k = 0; k < PER; ++k) {
-      const int y = el(k) / M, z = el(k) % M;
+      const int y = el(k) / MZ, z = el(k) % MZ;
       const int j = BATCH ? k : 0;
       if (!BATCH) gate_in(k, 0);
       float2 nv = make_float2(0.f, 0.f);
@@ -525,8 +541,8 @@ __global__ __launch_bounds__(PlaneCfg<M>::THREADS) void nd_plane_kernel(NdConvAr
     __syncthreads();
   }
   // forward plane DFT of the (zero padded) Y x Z block
-  plane_rows<M, false>(P, Y, tw);
-  plane_cols<M, false>(P, tw);
+  plane_rows_r<MY, MZ, false>(P, Y, tw);
+  plane_cols_r<MY, MZ, false>(P, tw);
 #pragma unroll
   for (int k = 0; k < PER; ++k) Yp[el(k)] = P[lds(el(k))];
 }
@@ -1169,24 +1185,36 @@ static hipError_t nd_allow_lds(const void* fn, size_t bytes) {
   return hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)bytes);
 }
 
-template <int M, int MODE>
+template <int MY, int MZ, int MODE>
 static hipError_t launch_plane_t(const NdConvArgs& a, dim3 grid, hipStream_t s) {
-  using C = PlaneCfg<M>;
-  auto fn = nd_plane_kernel<M, MODE>;
+  using C = PlaneCfg<MY, MZ>;
+  auto fn = nd_plane_kernel<MY, MZ, MODE>;
   hipError_t e = nd_allow_lds((const void*)fn, C::LDS);
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(fn, grid, dim3(C::THREADS), C::LDS, s, a);
   return hipGetLastError();
 }
 
+template <int MY, int MODE>
+static hipError_t launch_plane_z(const NdConvArgs& a, dim3 grid, hipStream_t s) {
+  switch (a.MZ) {
+    case 8: return launch_plane_t<MY, 8, MODE>(a, grid, s);
+    case 16: return launch_plane_t<MY, 16, MODE>(a, grid, s);
+    case 32: return launch_plane_t<MY, 32, MODE>(a, grid, s);
+    case 64: return launch_plane_t<MY, 64, MODE>(a, grid, s);
+    case 128: return launch_plane_t<MY, 128, MODE>(a, grid, s);
+    default: return hipErrorInvalidValue;
+  }
+}
+
 template <int MODE>
 static hipError_t launch_plane(const NdConvArgs& a, dim3 grid, hipStream_t s) {
   switch (a.MY) {
-    case 8: return launch_plane_t<8, MODE>(a, grid, s);
-    case 16: return launch_plane_t<16, MODE>(a, grid, s);
-    case 32: return launch_plane_t<32, MODE>(a, grid, s);
-    case 64: return launch_plane_t<64, MODE>(a, grid, s);
-    case 128: return launch_plane_t<128, MODE>(a, grid, s);
+    case 8: return launch_plane_z<8, MODE>(a, grid, s);
+    case 16: return launch_plane_z<16, MODE>(a, grid, s);
+    case 32: return launch_plane_z<32, MODE>(a, grid, s);
+    case 64: return launch_plane_z<64, MODE>(a, grid, s);
+    case 128: return launch_plane_z<128, MODE>(a, grid, s);
     default: return hipErrorInvalidValue;
   }
 }

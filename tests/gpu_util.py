@@ -92,11 +92,19 @@ def gpu_nd(inp, with_k: bool = False):
     return yn
 
 
+def _oracle_workers(inp):
+    """Channel-shard processes for the oracle on large grids (1 on small ones)."""
+    if inp.X * inp.Y * inp.Z * inp.B < (1 << 16):
+        return 1
+    from oracle._pool import default_workers
+    return default_workers()
+
+
 def oracle_nd(inp, conv: str = "fft"):
     import oracle
     K = oracle.nd_filter(inp.filter_params, inp.X, inp.Y, inp.Z, inp.N, inp.C, circular=inp.circular)
     y = oracle.hyena_nd_fwd(inp.u, inp.w_in, inp.dskip, inp.gate_a, inp.gate_b, inp.w_out, K, conv=conv,
-                            circular=inp.circular)
+                            circular=inp.circular, workers=_oracle_workers(inp) if conv == "fft" else 1)
     return y, K
 
 
@@ -126,5 +134,6 @@ def oracle_nd_film(inp):
     import oracle
     Ks = oracle.film_kernels(inp.film_filter_params, inp.reg, inp.q, inp.film_w, inp.film_b, inp.X, inp.Y, inp.Z,
                              inp.N, inp.C, inp.circular)
-    y = oracle.hyena_nd_film_fwd(inp.u, inp.w_in, inp.dskip, inp.w_out, Ks, circular=inp.circular)
+    y = oracle.hyena_nd_film_fwd(inp.u, inp.w_in, inp.dskip, inp.w_out, Ks, circular=inp.circular,
+                                 workers=_oracle_workers(inp))
     return y, Ks

@@ -171,18 +171,25 @@ def test_nd_size_queries_by_boundary(hy):
             == hy.hyena_nd_filter_workspace_bytes(X, Y, Z, C, N))
     assert (hy.hyena_nd_workspace_bytes_ex(2, X, Y, Z, C, N, hy.ND_CIRCULAR)
             < hy.hyena_nd_workspace_bytes(2, X, Y, Z, C, N))
-    # ranges: zero padded X in [4, 64], circular X in [8, 128]; Y = Z; unknown boundary
+    # ranges: zero padded X, Y, Z in [4, 64], circular in [8, 128], each axis on its
+    # own (3D grids); unknown boundary
     assert hy.hyena_nd_cache_bytes_ex(4, 4, 4, 64, 1, hy.ND_ZERO_PAD) > 0
     assert hy.hyena_nd_cache_bytes_ex(4, 4, 4, 64, 1, hy.ND_CIRCULAR) == 0
     assert hy.hyena_nd_cache_bytes_ex(128, 128, 128, 64, 1, hy.ND_ZERO_PAD) == 0
     assert hy.hyena_nd_cache_bytes_ex(128, 128, 128, 64, 1, hy.ND_CIRCULAR) > 0
-    assert hy.hyena_nd_cache_bytes_ex(8, 8, 16, 64, 1, hy.ND_CIRCULAR) == 0
+    assert hy.hyena_nd_cache_bytes_ex(8, 8, 16, 64, 1, hy.ND_CIRCULAR) == al(128 * 8) + al(64 * 8 * 8 * 9 * 8)
+    assert hy.hyena_nd_cache_bytes_ex(8, 16, 32, 64, 2, hy.ND_ZERO_PAD) == al(128 * 8) + al(2 * 64 * 16 * 32 * 33 * 8)
+    assert hy.hyena_nd_cache_bytes_ex(16, 64, 4, 64, 1, hy.ND_ZERO_PAD) > 0
+    assert hy.hyena_nd_cache_bytes_ex(16, 64, 2, 64, 1, hy.ND_ZERO_PAD) == 0      # Z below the range
+    assert hy.hyena_nd_cache_bytes_ex(16, 8, 256, 64, 1, hy.ND_CIRCULAR) == 0     # Z above the range
+    assert hy.hyena_nd_cache_bytes_ex(16, 8, 24, 64, 1, hy.ND_CIRCULAR) == 0      # not a power of two
     assert hy.hyena_nd_cache_bytes_ex(8, 8, 8, 64, 1, 2) == 0
     assert hy.hyena_nd_workspace_bytes_ex(1, 8, 8, 8, 64, 1, -1) == 0
     # 2D grids: X = 1 in both boundaries, no padding along x
     assert hy.hyena_nd_cache_bytes(1, 64, 64, 64, 2) == al(128 * 8) + al(2 * 64 * 1 * 128 * 65 * 8)
     assert hy.hyena_nd_cache_bytes_ex(1, 128, 128, 64, 2, hy.ND_CIRCULAR) == al(128 * 8) + al(2 * 64 * 128 * 65 * 8)
     assert hy.hyena_nd_cache_bytes(2, 8, 8, 64, 2) == 0            # X = 2 is not a 2D grid
+    assert hy.hyena_nd_cache_bytes(1, 16, 32, 64, 2) == 0          # 2D grids take square planes
     assert hy.hyena_nd_filter_workspace_bytes(1, 4, 4, 64, 1) > 0
 
 

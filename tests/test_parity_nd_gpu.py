@@ -152,3 +152,48 @@ def test_nd_filter_spectra_are_bit_reproducible(X, Y, circ):
         caches.append(layer.cache)
     torch.cuda.synchronize()
     assert torch.equal(caches[0], caches[1])
+
+
+# ------------------------------------------------------- non-square grids
+# X, Y and Z are independent on 3D grids (HyenaND explainer, "Native ND
+# Convolution": the convolution runs on the native grid, any shape).
+
+@pytest.mark.parametrize("B,X,Y,Z,C,N,circ", [
+    (2, 8, 16, 32, 64, 2, False),    # 32 x 64 planes
+    (2, 16, 32, 8, 64, 2, False),    # 64 x 16 planes
+    (1, 8, 4, 16, 64, 2, False),     # odd batch, 8 x 32 planes
+    (3, 16, 64, 8, 64, 1, False),    # 128 x 16 planes
+    (1, 64, 32, 16, 64, 1, False),   # 128-point x transforms (the persistent pencil pass)
+    (2, 8, 16, 32, 64, 2, True),     # circular: 16 x 32 planes
+    (2, 16, 8, 64, 128, 2, True),
+    (1, 8, 128, 16, 64, 1, True),    # circular 128 x 16 planes
+])
+def test_nd_non_square_sweep(B, X, Y, Z, C, N, circ):
+    _check(make_nd(400 + B + X + 3 * Y + 5 * Z + N + 7 * circ, B, X, Y, Z, C, N=N, W=64, u_mean_spread=0.5,
+                   circular=circ))
+
+
+@pytest.mark.parametrize("circ", [False, True])
+def test_nd_non_square_filter_matches_oracle(circ):
+    inp = make_nd(46, 1, 8, 16, 32, 64, N=2, W=64, circular=circ)
+    say(f"nd filter 8x16x32 C=64 N=2 circular={circ}")
+    _, k = gpu_nd(inp, with_k=True)
+    _, kref = oracle_nd(inp)
+    assert k.shape == kref.shape
+    assert rel_err(k, kref) < 1e-5
+
+
+def test_nd_non_square_spectra_are_bit_reproducible():
+    import torch
+    import subquadratic_sequence_amd as hs
+    from tests.gpu_util import to_dev
+    inp = make_nd(47, 2, 16, 8, 32, 64, N=2, W=64)
+    say("nd spectra reproducibility 16x8x32")
+    fa = [to_dev(a) for a in (inp.w1, inp.b1, inp.w2, inp.b2, inp.w3, inp.b3, inp.decay)]
+    caches = []
+    for _ in range(2):
+        layer = hs.HyenaNDLayer(16, 8, 32, 64, 2)
+        hs.hyena_nd_filter_gen(layer, *fa)
+        caches.append(layer.cache)
+    torch.cuda.synchronize()
+    assert torch.equal(caches[0], caches[1])
