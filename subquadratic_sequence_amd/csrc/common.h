@@ -2,6 +2,8 @@
 #pragma once
 
 #include <hip/hip_runtime.h>
+
+#include <atomic>
 #include <stdint.h>
 #include <stddef.h>
 
@@ -267,6 +269,25 @@ template <> struct BufIO<float2> {
 };
 
 // ---------------------------------------------------------------- host side
+
+// Launch-configuration values (resident workgroups of a persistent launch,
+// compute-unit counts) cached per device: each entry is written once per
+// device with the value computed for that device; concurrent first calls may
+// both compute it and store the same value.
+constexpr int kMaxDevices = 64;
+struct DeviceCache {
+  std::atomic<int> v[kMaxDevices];
+  template <typename F> int get(F compute) {
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return compute();
+    int x = v[dev].load(std::memory_order_relaxed);
+    if (x == 0) {
+      x = compute();
+      v[dev].store(x, std::memory_order_relaxed);
+    }
+    return x;
+  }
+};
 
 #define HY_CHECK_HIP(expr)                         \
   do {                                             \

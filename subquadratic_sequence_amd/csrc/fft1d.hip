@@ -1165,13 +1165,14 @@ hipError_t lds_spec(const float* h, const float2* tw, float4* pq, int L, int D, 
 
 // Workgroups of a persistent launch: as many as are resident at once.
 static int resident_grid(const void* fn, int block, size_t lds, int items) {
-  static int cus = 0;
-  if (cus == 0) {
-    int dev = 0;
+  static DeviceCache cus_cache;
+  const int cus = cus_cache.get([] {
+    int dev = 0, n = 0;
     if (hipGetDevice(&dev) != hipSuccess ||
-        hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0)
-      cus = 256;
-  }
+        hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0)
+      n = 256;
+    return n;
+  });
   int per_cu = 0;
   if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, fn, block, lds) != hipSuccess || per_cu <= 0) per_cu = 1;
   const long long g = (long long)cus * per_cu;
@@ -1186,8 +1187,8 @@ static hipError_t launch_col_t(const ColArgs& a, int pairs, hipStream_t s) {
   hipError_t e = allow_lds((const void*)fn, lds);
   if (e != hipSuccess) return e;
   const int items = pairs * (a.N2 / kCW);
-  static int grid = 0;
-  if (grid == 0) grid = resident_grid((const void*)fn, R * kCW, lds, 1 << 30);
+  static DeviceCache grid_cache;
+  const int grid = grid_cache.get([&] { return resident_grid((const void*)fn, R * kCW, lds, 1 << 30); });
   hipLaunchKernelGGL(fn, dim3(grid < items ? grid : items), dim3(R * kCW), lds, s, a, items);
   return hipGetLastError();
 }
@@ -1228,9 +1229,9 @@ static hipError_t launch_row_t(void* Y, void* pqv, const float2* tw_row, int pq_
   if constexpr (N2 >= 8192) {
     const int items = pairs * (N1 / 2);
     auto fn = mode == ROW_CONV ? rowpass_seq_kernel<YT, N1, N2, ROW_CONV> : rowpass_seq_kernel<YT, N1, N2, ROW_SPEC>;
-    static int grid[2] = {0, 0};
-    int& g = grid[mode == ROW_CONV ? 0 : 1];
-    if (g == 0) g = resident_grid((const void*)fn, RowSeqCfg<N2>::T, 0, 1 << 30);
+    static DeviceCache grid_cache[2];
+    const int g = grid_cache[mode == ROW_CONV ? 0 : 1].get(
+        [&] { return resident_grid((const void*)fn, RowSeqCfg<N2>::T, 0, 1 << 30); });
     hipLaunchKernelGGL(fn, dim3(g < items ? g : items), dim3(RowSeqCfg<N2>::T), 0, s, y, pq, tw_row, pq_off,
                        pair_off, pq_mod, items);
     return hipGetLastError();
@@ -1252,9 +1253,9 @@ static hipError_t launch_row_t(void* Y, void* pqv, const float2* tw_row, int pq_
     else if (pf == 3) fn = rowpass_kernel<YT, N1, N2, ROW_CONV, 3>;
     else fn = rowpass_kernel<YT, N1, N2, ROW_CONV, 0>;
     // LDS is static in the kernel
-    static int grid[2] = {0, 0};
-    int& g = grid[mode == ROW_CONV ? 0 : 1];
-    if (g == 0) g = resident_grid((const void*)fn, C::WG, 0, 1 << 30);
+    static DeviceCache grid_cache[2];
+    const int g = grid_cache[mode == ROW_CONV ? 0 : 1].get(
+        [&] { return resident_grid((const void*)fn, C::WG, 0, 1 << 30); });
     hipLaunchKernelGGL(fn, dim3(g < items ? g : items), dim3(C::WG), 0, s, y, pq, tw_row, pq_off, pair_off,
                        pq_mod, items);
     return hipGetLastError();

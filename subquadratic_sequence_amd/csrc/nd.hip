@@ -1532,14 +1532,14 @@ static hipError_t launch_plane128(const NdConvArgs& a, int nitems, hipStream_t s
   auto fn = nd_plane128_kernel<MODE>;
   hipError_t e = nd_allow_lds((const void*)fn, C::LDS);
   if (e != hipSuccess) return e;
-  static int grid = 0;
-  if (grid == 0) {
+  static DeviceCache grid_cache;
+  const int grid = grid_cache.get([] {
     int cus = 0, dev = 0;
     if (hipGetDevice(&dev) != hipSuccess ||
         hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0)
       cus = 256;
-    grid = cus;  // one 1024-thread workgroup per CU (LDS)
-  }
+    return cus;  // one 1024-thread workgroup per CU (LDS)
+  });
   hipLaunchKernelGGL(fn, dim3(grid < nitems ? grid : nitems), dim3(C::THREADS), C::LDS, s, a, nitems);
   return hipGetLastError();
 }
@@ -1549,15 +1549,16 @@ static hipError_t launch_pencil128(const NdConvArgs& a, int nitems, hipStream_t 
   auto fn = nd_pencil128_kernel;
   hipError_t e = nd_allow_lds((const void*)fn, lds);
   if (e != hipSuccess) return e;
-  static int grid = 0;
-  if (grid == 0) {
+  static DeviceCache grid_cache;
+  const int grid = grid_cache.get([&] {
     int cus = 0, dev = 0, per_cu = 0;
     if (hipGetDevice(&dev) != hipSuccess ||
         hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0)
       cus = 256;
-    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, fn, 512, lds) != hipSuccess || per_cu <= 0) per_cu = 1;
-    grid = cus * per_cu;
-  }
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, (const void*)fn, 512, lds) != hipSuccess || per_cu <= 0)
+      per_cu = 1;
+    return cus * per_cu;
+  });
   hipLaunchKernelGGL(fn, dim3(grid < nitems ? grid : nitems), dim3(512), lds, s, a, nitems);
   return hipGetLastError();
 }
