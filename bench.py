@@ -447,6 +447,54 @@ def main_nd_film(args, torch, hs, make_config):
     print(json.dumps(out), flush=True)
 
 
+def main_bwd(args, torch, hs, make_config):
+    """Times hyena_bwd (and hyena_filter_bwd) on a 1D workload of the on-chip regime."""
+    log(f"generating inputs for {args.workload} (backward)")
+    inp = make_config(args.workload)
+    B, L, D, N = inp.B, inp.L, inp.D, inp.N
+    tdt = torch.bfloat16 if inp.dtype == "bf16" else torch.float32
+    f = lambda a, d=torch.float32: torch.from_numpy(np.ascontiguousarray(a, np.float32)).to("cuda", d)  # noqa: E731
+    layer = hs.HyenaLayer(L, D, N, direction=hs.CAUSAL if inp.causal else hs.NONCAUSAL)
+    fp = [f(a) for a in (inp.w1, inp.b1, inp.w2, inp.b2, inp.w3, inp.b3, inp.decay)]
+    hs.hyena_filter_gen(layer, *fp, inp.K)
+    u, w_in, w_out = f(inp.u, tdt), f(inp.w_in, tdt), f(inp.w_out, tdt)
+    short_w, dskip = f(inp.short_w), f(inp.dskip)
+    dy = torch.randn(B, L, D, device="cuda").to(tdt)
+    dt = hs.HYENA_BF16 if inp.dtype == "bf16" else hs.HYENA_F32
+    ws = torch.empty(hs.hyena_bwd_workspace_bytes(B, L, D, N, dt, layer.direction), dtype=torch.uint8, device="cuda")
+    fws = torch.empty(hs.hyena_filter_bwd_workspace_bytes(L, D, N, inp.K, inp.W, layer.direction),
+                      dtype=torch.uint8, device="cuda")
+    y = torch.empty_like(u)
+    fws_fwd = torch.empty(hs.hyena_workspace_bytes(B, L, D, N, dt), dtype=torch.uint8, device="cuda")
+    for _ in range(args.warmup):
+        g = hs.hyena_bwd(layer, u, w_in, short_w, dskip, w_out, dy, ws=ws)
+        hs.hyena_filter_bwd(layer, *fp, inp.K, g["dh"], ws=fws)
+    torch.cuda.synchronize()
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(4)]
+    ev[0].record()
+    for _ in range(args.steps):
+        hs.hyena_fwd(layer, u, w_in, short_w, dskip, w_out, y=y, ws=fws_fwd)
+    ev[1].record()
+    for _ in range(args.steps):
+        g = hs.hyena_bwd(layer, u, w_in, short_w, dskip, w_out, dy, ws=ws)
+    ev[2].record()
+    for _ in range(args.steps):
+        hs.hyena_filter_bwd(layer, *fp, inp.K, g["dh"], ws=fws)
+    ev[3].record()
+    torch.cuda.synchronize()
+    fwd_ms, bwd_ms, fbwd_ms = (ev[i].elapsed_time(ev[i + 1]) / args.steps for i in range(3))
+    out = {
+        "metric": "Hyena bwd tokens/sec (hyena_bwd: gradients of u, W_in, short conv, skips, W_out and the filters)",
+        "value": B * L / (bwd_ms * 1e-3), "unit": "tokens/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": bwd_ms, "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": inp.dtype,
+        "data": "synthetic",
+        "config": {"workload": args.workload, "B": B, "L": L, "D": D, "N": N,
+                   "direction": "causal" if inp.causal else "non-causal"},
+        "fwd_ms": fwd_ms, "bwd_ms": bwd_ms, "filter_bwd_ms": fbwd_ms, "bwd_over_fwd": bwd_ms / fwd_ms,
+    }
+    print(json.dumps(out), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -454,6 +502,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default=DEFAULT_WORKLOAD)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--backward", action="store_true",
+                    help="time hyena_bwd and hyena_filter_bwd instead (1D workloads with L <= 4096)")
     ap.add_argument("--cpu-tokens", type=int, default=0,
                     help="positions of the 1D oracle sample (default 0: the whole sequence)")
     ap.add_argument("--cpu-workers", type=int, default=0,
@@ -488,6 +538,11 @@ def main():
         print(f"unknown workload {args.workload}; one of {sorted(CONFIGS) + sorted(TEST_SHAPES)}", file=sys.stderr)
         sys.exit(2)
     cfg = CONFIGS.get(args.workload) or TEST_SHAPES[args.workload]
+    if args.backward:
+        if cfg["kind"] != "1d" or cfg["L"] > 4096:
+            print("--backward: the backward pass covers 1D workloads with L <= 4096", file=sys.stderr)
+            sys.exit(2)
+        return main_bwd(args, torch, hs, make_config)
     if cfg["kind"] == "nd":
         return main_nd(args, torch, hs, make_config)
     if cfg["kind"] == "nd_film":

@@ -174,6 +174,20 @@ constexpr int kBwdMinL = 32;  // the weight-gradient products take K = L in whol
 
 bool bwd_shape_ok(int L, int D, int N) { return shape_ok(L, D, N) && L >= kBwdMinL && L <= kLdsMaxL; }
 
+// K splits of a reduction product (weight gradients: K runs over positions)
+// so that about 512 workgroups share it: powers of two that keep whole K
+// tiles of kt elements and at least 128 elements per split.
+int ksplit(int K, int kt, long long tiles) {
+  int s = 1;
+  while (tiles * s < 512 && K % (2 * s * kt) == 0 && K / (2 * s) >= 128) s *= 2;
+  return s;
+}
+long long tiles_of(int M, int N) { return (long long)((M + 255) / 256) * ((N + 127) / 128); }
+int bwd_split_out(int B, int L, int D, int dtype) { return ksplit(L, dtype == HYENA_BF16 ? 32 : 16, tiles_of(D, D) * B); }
+int bwd_split_in(int B, int L, int D, int N, int dtype) {
+  return ksplit(L, dtype == HYENA_BF16 ? 32 : 16, tiles_of(D, (N + 1) * D) * B);
+}
+
 struct BwdWs {
   size_t wt_in, s, p, gz, zsave, csave, zfin, sbar, pbar, dh_part, dd_part, dsw_part, dyT, uT, dwo_part, dwi_part,
       total;
@@ -202,14 +216,15 @@ BwdWs bwd_ws(int B, int L, int D, int N, int dtype, int dir) {
   take(w.dsw_part, (size_t)B * J * 3 * 4);
   take(w.dyT, BDL * es);
   take(w.uT, BDL * es);
-  take(w.dwo_part, (size_t)B * D * D * es);
-  take(w.dwi_part, (size_t)B * D * J * es);
+  take(w.dwo_part, (size_t)B * bwd_split_out(B, L, D, dtype) * D * D * es);
+  take(w.dwi_part, (size_t)B * bwd_split_in(B, L, D, N, dtype) * D * J * es);
   w.total = off;
   return w;
 }
 
 struct FilterBwdWs {
-  size_t e, a1, c1, a2, c2, w3t, o, dout, g2, g1, a2t, a1t, et, d2t, d1t, total;
+  size_t e, a1, c1, a2, c2, w3t, o, dout, g2, g1, a2t, a1t, et, d2t, d1t, part, total;
+  int s3, s2, s1, sg;  // K splits of dW3, dW2, dW1 (over positions) and of dL/da2 (over N D)
 };
 FilterBwdWs filter_bwd_ws(int L, int D, int N, int K, int W, int dir) {
   FilterBwdWs w{};
@@ -234,6 +249,15 @@ FilterBwdWs filter_bwd_ws(int L, int D, int N, int K, int W, int dir) {
   take(w.et, P * F);
   take(w.d2t, P * W);
   take(w.d1t, P * W);
+  w.s3 = ksplit((int)P, 16, tiles_of(W, (int)ND));
+  w.s2 = ksplit((int)P, 16, tiles_of(W, W));
+  w.s1 = ksplit((int)P, 16, tiles_of((int)F, W));
+  w.sg = ksplit((int)ND, 16, tiles_of((int)P, W));
+  size_t part = (size_t)w.s3 * W * ND;
+  part = part > (size_t)w.s2 * W * W ? part : (size_t)w.s2 * W * W;
+  part = part > (size_t)w.s1 * F * W ? part : (size_t)w.s1 * F * W;
+  part = part > (size_t)w.sg * P * W ? part : (size_t)w.sg * P * W;
+  take(w.part, part);
   w.total = off;
   return w;
 }
@@ -442,7 +466,6 @@ int hyena_bwd(const hyena_layer* layer, const void* u, const void* w_in, const f
   if (device_ok() != HYENA_OK) return HYENA_ERR_HIP;
 
   const bool bf = dtype == HYENA_BF16;
-  const size_t es = bf ? 2 : 4;
   char* wb = static_cast<char*>(ws);
   char* cb = static_cast<char*>(layer->cache);
   const int J = (N + 1) * D, HL = dir == HYENA_NONCAUSAL ? 2 * L : L;
@@ -476,23 +499,32 @@ int hyena_bwd(const hyena_layer* layer, const void* u, const void* w_in, const f
                                   B * J, L, J, bf, stream));
   // du = dp W_in^T (dp channel-major; W_in as stored is the transposed operand)
   HY_CHECK_HIP(hy::gemm(hy::GemmArgs{wb + w.pbar, w_in, du, B * L, D, J, L, true, false, nullptr}, bf, stream));
-  // per-sample weight gradients: dW_out_b = z^{N+1}_b dy_b, dW_in_b = u_b^T dp_b (K = L)
-  for (int b = 0; b < B; ++b) {
-    const size_t ob = (size_t)b * L * D * es;
-    char* dyT = wb + w.dyT + ob;
-    char* uT = wb + w.uT + ob;
-    HY_CHECK_HIP(hy::transpose2d(static_cast<const char*>(dy) + ob, dyT, L, D, bf, stream));
-    HY_CHECK_HIP(hy::transpose2d(static_cast<const char*>(u) + ob, uT, L, D, bf, stream));
-    HY_CHECK_HIP(hy::gemm(hy::GemmArgs{wb + w.zfin + ob, dyT, wb + w.dwo_part + (size_t)b * D * D * es, D, D, L, L,
-                                       false, false, nullptr},
-                          bf, stream));
-    HY_CHECK_HIP(hy::gemm(hy::GemmArgs{uT, wb + w.pbar + (size_t)b * J * L * es, wb + w.dwi_part + (size_t)b * D * J * es,
-                                       D, J, L, L, false, false, nullptr},
-                          bf, stream));
-  }
+  // weight gradients dW_out = sum_b z^{N+1}_b dy_b and dW_in = sum_b u_b^T dp_b
+  // (K = L): one launch per product over the samples and K splits, the
+  // partial results summed below
+  HY_CHECK_HIP(hy::transpose2d(dy, wb + w.dyT, L, D, bf, stream, B));
+  HY_CHECK_HIP(hy::transpose2d(u, wb + w.uT, L, D, bf, stream, B));
+  const int so = bwd_split_out(B, L, D, dtype), si = bwd_split_in(B, L, D, N, dtype);
+  hy::GemmArgs go{wb + w.zfin, wb + w.dyT, wb + w.dwo_part, D, D, L / so, L, false, false, nullptr};
+  go.batch = B;
+  go.nsplit = so;
+  go.sa = go.sb = (size_t)D * L;
+  go.sc = (size_t)D * D;
+  go.ka = go.kb = (size_t)(L / so);
+  go.lda = go.ldb = L;
+  HY_CHECK_HIP(hy::gemm(go, bf, stream));
+  hy::GemmArgs gw{wb + w.uT, wb + w.pbar, wb + w.dwi_part, D, J, L / si, L, false, false, nullptr};
+  gw.batch = B;
+  gw.nsplit = si;
+  gw.sa = (size_t)D * L;
+  gw.sb = (size_t)J * L;
+  gw.sc = (size_t)D * J;
+  gw.ka = gw.kb = (size_t)(L / si);
+  gw.lda = gw.ldb = L;
+  HY_CHECK_HIP(hy::gemm(gw, bf, stream));
   // sums over the batch, in a fixed order
-  HY_CHECK_HIP(hy::sum_rows(wb + w.dwo_part, dw_out, B, (size_t)D * D, (size_t)D * D, bf, stream));
-  HY_CHECK_HIP(hy::sum_rows(wb + w.dwi_part, dw_in, B, (size_t)D * J, (size_t)D * J, bf, stream));
+  HY_CHECK_HIP(hy::sum_rows(wb + w.dwo_part, dw_out, B * so, (size_t)D * D, (size_t)D * D, bf, stream));
+  HY_CHECK_HIP(hy::sum_rows(wb + w.dwi_part, dw_in, B * si, (size_t)D * J, (size_t)D * J, bf, stream));
   HY_CHECK_HIP(hy::sum_rows(a.dh_part, dh, B, (size_t)N * D * HL, (size_t)N * D * HL, false, stream));
   HY_CHECK_HIP(hy::sum_rows(a.dd_part, ddskip, B, (size_t)N * D, (size_t)N * D, false, stream));
   HY_CHECK_HIP(hy::sum_rows(wb + w.dsw_part, dshort_w, B, (size_t)J * 3, (size_t)J * 3, false, stream));
@@ -552,7 +584,17 @@ int hyena_filter_bwd(const hyena_layer* layer, const hyena_filter_params* p, con
   // dL/do = dh * window (and the decay gradient)
   HY_CHECK_HIP(hy::filter_bwd_out(a, stream));
   // back through the hidden layers: dq2 = (do W3^T) cos(q2), dq1 = (dq2 W2^T) cos(q1)
-  HY_CHECK_HIP(hy::gemm(hy::GemmArgs{f(w.dout), p->w3, f(w.g2), P, W, ND, P, true, false, nullptr}, false, stream));
+  {
+    // dL/da2 = dout^T W3^T over K = N D, split; partial results summed in order
+    hy::GemmArgs g{f(w.dout), p->w3, f(w.part), P, W, ND / w.sg, P, true, false, nullptr};
+    g.nsplit = w.sg;
+    g.ka = (size_t)(ND / w.sg) * P;  // channel-major A: a split is N D / sg channels
+    g.kb = (size_t)(ND / w.sg);
+    g.sc = (size_t)P * W;
+    g.lda = g.ldb = ND;
+    HY_CHECK_HIP(hy::gemm(g, false, stream));
+    HY_CHECK_HIP(hy::sum_rows(f(w.part), f(w.g2), w.sg, (size_t)P * W, (size_t)P * W, false, stream));
+  }
   HY_CHECK_HIP(hy::mul_inplace(f(w.g2), a.c2, (size_t)P * W, stream));
   HY_CHECK_HIP(hy::gemm(hy::GemmArgs{f(w.g2), p->w2, f(w.g1), P, W, W, P, false, false, nullptr}, false, stream));
   HY_CHECK_HIP(hy::mul_inplace(f(w.g1), a.c1, (size_t)P * W, stream));
@@ -562,9 +604,19 @@ int hyena_filter_bwd(const hyena_layer* layer, const hyena_filter_params* p, con
   HY_CHECK_HIP(hy::transpose2d(a.e, f(w.et), P, F, false, stream));
   HY_CHECK_HIP(hy::transpose2d(f(w.g2), f(w.d2t), P, W, false, stream));
   HY_CHECK_HIP(hy::transpose2d(f(w.g1), f(w.d1t), P, W, false, stream));
-  HY_CHECK_HIP(hy::gemm(hy::GemmArgs{f(w.a2t), f(w.dout), dw3, W, ND, P, P, false, false, nullptr}, false, stream));
-  HY_CHECK_HIP(hy::gemm(hy::GemmArgs{f(w.a1t), f(w.d2t), dw2, W, W, P, P, false, false, nullptr}, false, stream));
-  HY_CHECK_HIP(hy::gemm(hy::GemmArgs{f(w.et), f(w.d1t), dw1, F, W, P, P, false, false, nullptr}, false, stream));
+  auto wgrad = [&](const float* A, const float* Bt, float* out, int M, int Nn, int S) -> hipError_t {
+    hy::GemmArgs g{A, Bt, f(w.part), M, Nn, P / S, P, false, false, nullptr};
+    g.nsplit = S;
+    g.ka = g.kb = (size_t)(P / S);
+    g.sc = (size_t)M * Nn;
+    g.lda = g.ldb = P;
+    hipError_t e = hy::gemm(g, false, stream);
+    if (e != hipSuccess) return e;
+    return hy::sum_rows(f(w.part), out, S, (size_t)M * Nn, (size_t)M * Nn, false, stream);
+  };
+  HY_CHECK_HIP(wgrad(f(w.a2t), f(w.dout), dw3, W, ND, w.s3));
+  HY_CHECK_HIP(wgrad(f(w.a1t), f(w.d2t), dw2, W, W, w.s2));
+  HY_CHECK_HIP(wgrad(f(w.et), f(w.d1t), dw1, F, W, w.s1));
   HY_CHECK_HIP(hy::row_sums(f(w.dout), db3, ND, P, stream));
   HY_CHECK_HIP(hy::row_sums(f(w.d2t), db2, W, P, stream));
   HY_CHECK_HIP(hy::row_sums(f(w.d1t), db1, W, P, stream));

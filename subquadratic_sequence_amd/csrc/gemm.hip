@@ -81,7 +81,9 @@ __device__ __forceinline__ int xcd_tile(int bid, int total) {
 template <typename T, bool A_CM, bool C_CM, bool SC, int TN = GBN>
 __global__ __launch_bounds__(512, TN == 64 ? 4 : 1) void gemm_kernel(const T* __restrict__ A, const T* __restrict__ Bt,
                                                       T* __restrict__ C, int M, int N, int K, int Lseq,
-                                                      const float* __restrict__ short_w, int ntn, int ntiles) {
+                                                      const float* __restrict__ short_w, int ntn, int ntiles,
+                                                      size_t sa, size_t sb, size_t sc, size_t ka, size_t kb,
+                                                      int nsplit, int lda, int ldb) {
   using Cfg = GemmCfg<T>;
   using WC = WaveCfg<TN>;
   constexpr int BK = Cfg::BK, LDK = Cfg::LDK, VEC = Cfg::VEC, NCH = Cfg::CHUNKS;
@@ -94,6 +96,13 @@ __global__ __launch_bounds__(512, TN == 64 ? 4 : 1) void gemm_kernel(const T* __
   T* As0 = reinterpret_cast<T*>(smem);  // [kBufs][GBM][LDK] then Bs [kBufs][TN][LDK]
   T* Bs0 = As0 + kBufs * Cfg::TILE;
 
+  {
+    // product and K split of this grid row
+    const int y = blockIdx.y, bz = y / nsplit, sz = y - bz * nsplit;
+    A += bz * sa + sz * ka;
+    Bt += bz * sb + sz * kb;
+    C += (size_t)y * sc;
+  }
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int wm = wave / WC::WCOLS, wn = wave % WC::WCOLS;  // waves of WR x 64
   const int tile = xcd_tile(blockIdx.x, ntiles);
@@ -132,7 +141,7 @@ __global__ __launch_bounds__(512, TN == 64 ? 4 : 1) void gemm_kernel(const T* __
       // stored (with the short convolution, rows before a sequence start are
       // masked by position), and unconditional loads keep the compiler's count
       // of loads in flight exact
-      pa[i] = A + (size_t)(m >= 0 && m < M ? m : 0) * K + kc;
+      pa[i] = A + (size_t)(m >= 0 && m < M ? m : 0) * lda + kc;
       la[i] = row * LDK + kc;
     } else {
       // chunks of VEC consecutive m for one k; ra[2j] and ra[2j + 1] hold
@@ -145,12 +154,12 @@ __global__ __launch_bounds__(512, TN == 64 ? 4 : 1) void gemm_kernel(const T* __
       const int m = m0 + mc;
       const int mm = m >= 0 && m < M ? m : 0;
       const int b = mm / Lseq, t = mm - b * Lseq;
-      pa[i] = A + ((size_t)b * K + k) * Lseq + t;
+      pa[i] = A + ((size_t)b * lda + k) * Lseq + t;
       la[i] = mc * LDK + (k & ~1);
     }
     if (i < NCHB) {
       const int n = n0 + (BPART && c >= BCH ? 0 : row);
-      pb[i] = Bt + (size_t)(n < N ? n : 0) * K + kc;  // columns >= N are not stored
+      pb[i] = Bt + (size_t)(n < N ? n : 0) * ldb + kc;  // columns >= N are not stored
       lb[i] = row * LDK + kc;
     }
   }
@@ -394,7 +403,9 @@ static hipError_t launch_gemm(const GemmArgs& g, hipStream_t s) {
   const int mtiles = sc ? (g.M + kScRows - 1) / kScRows : (g.M + GBM - 1) / GBM;
   const int ntn = (g.N + TN - 1) / TN;
   const int ntiles = ntn * mtiles;
-  dim3 grid(ntiles), block(512);
+  if (g.batch < 1 || g.nsplit < 1) return hipErrorInvalidValue;
+  dim3 grid(ntiles, g.batch * g.nsplit), block(512);
+  const int lda = g.lda ? g.lda : g.K, ldb = g.ldb ? g.ldb : g.K;
   const T* A = static_cast<const T*>(g.A);
   const T* B = static_cast<const T*>(g.Bt);
   T* C = static_cast<T*>(g.C);
@@ -405,7 +416,7 @@ static hipError_t launch_gemm(const GemmArgs& g, hipStream_t s) {
                                        (int)gemm_lds_bytes(TN));                                      \
     if (e != hipSuccess) return e;                                                                    \
     hipLaunchKernelGGL(fn, grid, block, gemm_lds_bytes(TN), s, A, B, C, g.M, g.N, g.K, g.Lseq,        \
-                       g.short_w, ntn, ntiles);                                                       \
+                       g.short_w, ntn, ntiles, g.sa, g.sb, g.sc, g.ka, g.kb, g.nsplit, lda, ldb);       \
   } while (0)
   if (sc) {
     if (!g.c_cm || g.a_cm) return hipErrorInvalidValue;
@@ -440,6 +451,9 @@ template <typename U>
 __global__ __launch_bounds__(256) void transpose_kernel(const U* __restrict__ src, U* __restrict__ dst, int rows,
                                                         int cols) {
   __shared__ U tile[32][33];
+  // blockIdx.z: matrix of a batch, each rows x cols
+  src += (size_t)blockIdx.z * rows * cols;
+  dst += (size_t)blockIdx.z * rows * cols;
   const int c0 = blockIdx.x * 32, r0 = blockIdx.y * 32;
   const int tx = threadIdx.x & 31, ty = threadIdx.x >> 5;
   for (int i = ty; i < 32; i += 8) {
@@ -453,8 +467,8 @@ __global__ __launch_bounds__(256) void transpose_kernel(const U* __restrict__ sr
   }
 }
 
-hipError_t transpose2d(const void* src, void* dst, int rows, int cols, bool bf16, hipStream_t s) {
-  dim3 grid((cols + 31) / 32, (rows + 31) / 32), block(256);
+hipError_t transpose2d(const void* src, void* dst, int rows, int cols, bool bf16, hipStream_t s, int batch) {
+  dim3 grid((cols + 31) / 32, (rows + 31) / 32, batch), block(256);
   if (bf16)
     hipLaunchKernelGGL(transpose_kernel<unsigned short>, grid, block, 0, s, (const unsigned short*)src,
                        (unsigned short*)dst, rows, cols);

@@ -21,10 +21,19 @@ struct GemmArgs {
   int M, N, K, Lseq;
   bool a_cm, c_cm;
   const float* short_w;
+  // Several products in one launch (grid row y = b * nsplit + s): product b of
+  // a batch reads A + b sa and Bt + b sb, its K split s starts at + s ka and
+  // + s kb (K elements each), and writes C + y sc (the splits' partial results,
+  // summed by the caller). lda: row stride of a row-major A, or the channel
+  // count of a channel-major A; ldb: row stride of Bt; 0 means K.
+  int batch = 1, nsplit = 1;
+  size_t sa = 0, sb = 0, sc = 0, ka = 0, kb = 0;
+  int lda = 0, ldb = 0;
 };
 hipError_t gemm(const GemmArgs& g, bool bf16, hipStream_t s);
-// dst [cols][rows] = transpose of src [rows][cols] (storage type of the dtype)
-hipError_t transpose2d(const void* src, void* dst, int rows, int cols, bool bf16, hipStream_t s);
+// dst [cols][rows] = transpose of src [rows][cols] (storage type of the dtype), for
+// each of `batch` matrices stored back to back
+hipError_t transpose2d(const void* src, void* dst, int rows, int cols, bool bf16, hipStream_t s, int batch = 1);
 
 // ---------------------------------------------------------- filter (1D)
 struct Filter1DArgs {
