@@ -27,6 +27,11 @@ int ilog2(long long x) {
   return r;
 }
 bool aligned16(const void* p) { return p != nullptr && ((uintptr_t)p & 15u) == 0; }
+// B * L * (N+1) * D < 2^31 (element offsets fit int32), for B >= 1 and a valid
+// shape, tested by division: the product itself can exceed 64 bits
+bool fits_i32(int B, int L, int D, int N) {
+  return (long long)B <= ((1LL << 31) - 1) / ((long long)L * (N + 1) * D);
+}
 
 bool shape_ok(int L, int D, int N) {
   return is_pow2(L) && L >= 16 && L <= (1 << 20) && D >= 64 && D <= 8192 && D % 64 == 0 && N >= 1 && N <= 4;
@@ -296,7 +301,7 @@ size_t hyena_filter_workspace_bytes(int L, int D, int N) {
 
 size_t hyena_workspace_bytes(int B, int L, int D, int N, int dtype) {
   if (!shape_ok(L, D, N) || B < 1 || (dtype != HYENA_F32 && dtype != HYENA_BF16)) return 0;
-  if ((long long)B * L * (N + 1) * D >= (1LL << 31)) return 0;
+  if (!fits_i32(B, L, D, N)) return 0;
   return fwd_ws(B, L, D, N, dtype).total;
 }
 
@@ -363,24 +368,43 @@ int hyena_filter_gen(hyena_layer* layer, const hyena_filter_params* p, float* h_
   return HYENA_OK;
 }
 
-static int fwd_impl(const hyena_layer* layer, const void* u, const void* w_in, const float* short_w,
-                    const float* dskip, const void* w_out, int B, int dtype, void* y, void* ws, size_t ws_bytes,
-                    hipStream_t stream, const hipEvent_t* ev) {
+}  // extern "C"
+
+namespace hy {
+
+// Every host-side check of a forward call except the workspace pointer (no HIP
+// call): hyena_fwd and the allocation-free entry point both run it first.
+int fwd_validate(const hyena_layer* layer, const void* u, const void* w_in, const float* short_w,
+                 const float* dskip, const void* w_out, int B, int dtype, const void* y, size_t ws_bytes) {
   if (layer == nullptr) return HYENA_ERR_INVALID_ARG;
   if (dtype != HYENA_F32 && dtype != HYENA_BF16) return HYENA_ERR_INVALID_ARG;
-  const void* ptrs[] = {u, w_in, short_w, dskip, w_out, y, ws};
+  const void* ptrs[] = {u, w_in, short_w, dskip, w_out, y};
   for (const void* q : ptrs)
     if (!aligned16(q)) return HYENA_ERR_INVALID_ARG;
   if (B < 1) return HYENA_ERR_INVALID_ARG;
   const int L = layer->L, D = layer->D, N = layer->N;
   if (!shape_ok(L, D, N)) return HYENA_ERR_UNSUPPORTED;
   if (!layer->built || !aligned16(layer->cache)) return HYENA_ERR_LAYER_MISMATCH;
-  const CacheLayout cl = cache_layout(L, D, N);
-  if (layer->cache_bytes < cl.total) return HYENA_ERR_LAYER_MISMATCH;
-  if ((long long)B * L * (N + 1) * D >= (1LL << 31)) return HYENA_ERR_UNSUPPORTED;
-  const FwdWs fw = fwd_ws(B, L, D, N, dtype);
-  if (ws_bytes < fw.total) return HYENA_ERR_WORKSPACE;
+  if (layer->cache_bytes < cache_layout(L, D, N).total) return HYENA_ERR_LAYER_MISMATCH;
+  if (!fits_i32(B, L, D, N)) return HYENA_ERR_UNSUPPORTED;
+  if (ws_bytes < fwd_ws(B, L, D, N, dtype).total) return HYENA_ERR_WORKSPACE;
+  return HYENA_OK;
+}
+
+}  // namespace hy
+
+extern "C" {
+
+static int fwd_impl(const hyena_layer* layer, const void* u, const void* w_in, const float* short_w,
+                    const float* dskip, const void* w_out, int B, int dtype, void* y, void* ws, size_t ws_bytes,
+                    hipStream_t stream, const hipEvent_t* ev) {
+  if (!aligned16(ws)) return HYENA_ERR_INVALID_ARG;
+  const int st = hy::fwd_validate(layer, u, w_in, short_w, dskip, w_out, B, dtype, y, ws_bytes);
+  if (st != HYENA_OK) return st;
   if (device_ok() != HYENA_OK) return HYENA_ERR_HIP;
+  const int L = layer->L, D = layer->D, N = layer->N;
+  const CacheLayout cl = cache_layout(L, D, N);
+  const FwdWs fw = fwd_ws(B, L, D, N, dtype);
 
   const bool bf = dtype == HYENA_BF16;
   char* wsb = static_cast<char*>(ws);
@@ -442,7 +466,7 @@ int hyena_fwd_profiled(const hyena_layer* layer, const void* u, const void* w_in
 size_t hyena_bwd_workspace_bytes(int B, int L, int D, int N, int dtype, int direction) {
   if (!bwd_shape_ok(L, D, N) || B < 1 || (dtype != HYENA_F32 && dtype != HYENA_BF16) || !direction_ok(direction))
     return 0;
-  if ((long long)B * L * (N + 1) * D >= (1LL << 31)) return 0;
+  if (!fits_i32(B, L, D, N)) return 0;
   return bwd_ws(B, L, D, N, dtype, direction).total;
 }
 
@@ -460,7 +484,7 @@ int hyena_bwd(const hyena_layer* layer, const void* u, const void* w_in, const f
   if (!layer->built || !aligned16(layer->cache)) return HYENA_ERR_LAYER_MISMATCH;
   const CacheLayout cl = cache_layout(L, D, N);
   if (layer->cache_bytes < cl.total) return HYENA_ERR_LAYER_MISMATCH;
-  if ((long long)B * L * (N + 1) * D >= (1LL << 31)) return HYENA_ERR_UNSUPPORTED;
+  if (!fits_i32(B, L, D, N)) return HYENA_ERR_UNSUPPORTED;
   const BwdWs w = bwd_ws(B, L, D, N, dtype, dir);
   if (ws_bytes < w.total) return HYENA_ERR_WORKSPACE;
   if (device_ok() != HYENA_OK) return HYENA_ERR_HIP;

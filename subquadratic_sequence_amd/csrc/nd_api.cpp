@@ -16,6 +16,11 @@ constexpr size_t kAlign = 256;
 
 bool pow2_in(int v, int lo, int hi) { return v >= lo && v <= hi && (v & (v - 1)) == 0; }
 bool aligned16(const void* p) { return p != nullptr && ((uintptr_t)p & 15u) == 0; }
+// B * X * Y * Z * (N+1) * C < 2^31 (element offsets fit int32), for B >= 1 and a
+// valid shape, tested by division: the product itself can exceed 64 bits
+bool fits_i32(int B, int X, int Y, int Z, int C, int N) {
+  return (long long)B <= ((1LL << 31) - 1) / ((long long)X * Y * Z * (N + 1) * C);
+}
 
 bool boundary_ok(int bd) { return bd == HYENA_ND_ZERO_PAD || bd == HYENA_ND_CIRCULAR; }
 // transform length per grid length: 2 (zero padded) or 1 (circular)
@@ -122,7 +127,7 @@ size_t hyena_nd_filter_workspace_bytes_ex(int X, int Y, int Z, int C, int N, int
 
 size_t hyena_nd_workspace_bytes_ex(int B, int X, int Y, int Z, int C, int N, int boundary) {
   if (!nd_shape_ok(X, Y, Z, C, N, boundary) || B < 1) return 0;
-  if ((long long)B * X * Y * Z * (N + 1) * C >= (1LL << 31)) return 0;
+  if (!fits_i32(B, X, Y, Z, C, N)) return 0;
   return nd_ws(B, X, Y, Z, C, N, boundary).total;
 }
 
@@ -209,7 +214,7 @@ int nd_fwd_impl(const hyena_nd_layer* layer, const float* u, const float* w_in, 
   if (!layer->built || !aligned16(layer->cache)) return HYENA_ERR_LAYER_MISMATCH;
   const NdCache cl = nd_cache(X, Y, Z, C, N, bd);
   if (layer->cache_bytes < cl.total) return HYENA_ERR_LAYER_MISMATCH;
-  if ((long long)B * X * Y * Z * (N + 1) * C >= (1LL << 31)) return HYENA_ERR_UNSUPPORTED;
+  if (!fits_i32(B, X, Y, Z, C, N)) return HYENA_ERR_UNSUPPORTED;
   const NdWs w = nd_ws(B, X, Y, Z, C, N, bd);
   if (ws_bytes < w.total) return HYENA_ERR_WORKSPACE;
   if (device_ok() != HYENA_OK) return HYENA_ERR_HIP;
@@ -307,7 +312,7 @@ NdFilmWs nd_film_ws(int B, int X, int Y, int Z, int C, int N, int W, int bd) {
 
 bool film_shape_ok(int B, int X, int Y, int Z, int C, int N, int W, int bd) {
   return nd_shape_ok(X, Y, Z, C, N, bd) && B >= 1 && W >= 1 && W <= 128 &&
-         (long long)B * X * Y * Z * (N + 1) * C < (1LL << 31);
+         fits_i32(B, X, Y, Z, C, N);
 }
 
 int film_fwd_impl(int X, int Y, int Z, int C, int N, int bd, const hyena_nd_filter_params* p,

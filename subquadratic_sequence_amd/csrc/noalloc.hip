@@ -14,6 +14,12 @@
 // copy.
 __device__ __align__(256) unsigned char scratch[HYENA_NOALLOC_SCRATCH_BYTES];
 
+namespace hy {
+// host-side checks of a forward call, defined with hyena_fwd
+int fwd_validate(const hyena_layer* layer, const void* u, const void* w_in, const float* short_w,
+                 const float* dskip, const void* w_out, int B, int dtype, const void* y, size_t ws_bytes);
+}  // namespace hy
+
 namespace {
 
 constexpr int kMaxDevices = 64;
@@ -39,13 +45,11 @@ int scratch_for_current_device(void** out) {
 extern "C" int hyena_fwd_noalloc(const hyena_layer* layer, const void* u, const void* w_in, const float* short_w,
                                  const float* dskip, const void* w_out, int B, int dtype, void* y,
                                  hipStream_t stream) {
-  if (layer == nullptr) return HYENA_ERR_INVALID_ARG;
-  if (dtype != HYENA_F32 && dtype != HYENA_BF16) return HYENA_ERR_INVALID_ARG;
-  if (B < 1) return HYENA_ERR_INVALID_ARG;
-  // size check on the host, before any HIP call
-  const size_t need = hyena_workspace_bytes(B, layer->L, layer->D, layer->N, dtype);
-  if (need == 0) return HYENA_ERR_UNSUPPORTED;
-  if (need > (size_t)HYENA_NOALLOC_SCRATCH_BYTES) return HYENA_ERR_WORKSPACE;
+  // every argument on the host, before any HIP call; a workspace beyond the
+  // array is HYENA_ERR_WORKSPACE
+  const int chk = hy::fwd_validate(layer, u, w_in, short_w, dskip, w_out, B, dtype, y,
+                                   (size_t)HYENA_NOALLOC_SCRATCH_BYTES);
+  if (chk != HYENA_OK) return chk;
   void* ws = nullptr;
   const int st = scratch_for_current_device(&ws);
   if (st != HYENA_OK) return st;
