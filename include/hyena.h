@@ -261,8 +261,7 @@ typedef struct {
  * X = 1 is a 2D grid (Y x Z; "Native ND Convolution" covers any dimension):
  * every offset has dx = 0 (coordinate 0, so the x row of w1 does not act), the
  * x axis is never padded, and u, y [B][1][Y][Z][C] are the same memory as
- * [B][Y][Z][C]. All orders of a 2D grid run in one launch, on square planes
- * (Y = Z). */
+ * [B][Y][Z][C]. All orders of a 2D grid run in one launch. */
 size_t hyena_nd_cache_bytes(int X, int Y, int Z, int C, int N);
 size_t hyena_nd_filter_workspace_bytes(int X, int Y, int Z, int C, int N);
 size_t hyena_nd_workspace_bytes(int B, int X, int Y, int Z, int C, int N);

@@ -5,9 +5,9 @@
 //
 // Layouts: activations channel-major [B][C][X][Y][Z] (z contiguous); transform
 // size (MX, MY, MZ) = (2X, 2Y, 2Z) zero padded or (X, Y, Z) circular; the
-// three axes are independent (MY x MZ planes), except on 2D grids (X = 1),
-// whose fused kernel takes square planes. The kernel lives on the matching
-// offset grid, offset d at index d + M/2 per axis, at coordinates d / (M/2).
+// three axes are independent (MY x MZ planes; MX = 1 for 2D grids, X = 1).
+// The kernel lives on the matching offset grid, offset d at index d + M/2 per
+// axis (M the axis' transform length), at coordinates d / (M/2).
 //
 // The gate g_{b,c} is one scalar per sample and channel, so it commutes with
 // the convolution and is applied to the convolution output in the spatial
@@ -1017,28 +1017,25 @@ __global__ __launch_bounds__(256) void nd_gate256_kernel(const float* __restrict
 // next order from the same plane. HBM sees v, x^n, the spectra and z^{N+1}
 // only. Items (channel, sample pair), pair index fastest, are dealt so that the
 // workgroups of one XCD (blockIdx mod 8) take consecutive items: the pairs of
-// a channel read its spectrum through that XCD's L2.
-template <int M> struct Plane2dCfg {
-  static constexpr int THREADS = PlaneCfg<M>::THREADS;
-  static constexpr int PER = PlaneCfg<M>::PER;  // plane elements per thread
-};
-
+// a channel read its spectrum through that XCD's L2. The plane is MY x MZ
+// (transform lengths along y and z), each side on its own.
+//
 // PQ: a kernel per sample (a.kh_stride != 0), the (P, Q) spectral product.
-template <int M, bool CIRC, bool PQ>
-__global__ __launch_bounds__(Plane2dCfg<M>::THREADS) void nd_plane2d_kernel(NdConvArgs a, int per_xcd) {
-  using C = PlaneCfg<M>;
-  constexpr int NT = Plane2dCfg<M>::THREADS;
-  constexpr int PER = Plane2dCfg<M>::PER;
+template <int MY, int MZ, bool CIRC, bool PQ>
+__global__ __launch_bounds__((PlaneCfg<MY, MZ>::THREADS)) void nd_plane2d_kernel(NdConvArgs a, int per_xcd) {
+  using C = PlaneCfg<MY, MZ>;
+  constexpr int NT = C::THREADS;
+  constexpr int PER = C::PER;                       // plane elements per thread
   constexpr int KEPT = CIRC ? PER : (PER + 3) / 4;  // kept positions per thread (a quarter when padded)
-  constexpr int ZH = M / 2 + 1;
+  constexpr int ZH = MZ / 2 + 1;
   // Smaller planes fetch the spectrum entries before the forward transform and
-  // the gate inputs before the inverse; 128-point planes (1024 threads, 128
-  // registers each) fetch them where they are used.
-  constexpr bool EARLY = M < 128;
-  static_assert(PER * NT == M * M, "plane split");
+  // the gate inputs before the inverse; 1024-thread planes (128 x 128, 128
+  // registers per thread) fetch them where they are used.
+  constexpr bool EARLY = NT < 1024;
+  static_assert(PER * NT == MY * MZ, "plane split");
   extern __shared__ float4 smem4[];
   float2* P = reinterpret_cast<float2*>(smem4);
-  float2* tw = P + M * C::RS;
+  float2* tw = P + MY * C::RS;
   const int tid = threadIdx.x;
   const int BP = (a.B + 1) / 2, CC = a.C;
   const int item = (int)(blockIdx.x % 8) * per_xcd + (int)(blockIdx.x / 8);
@@ -1061,25 +1058,25 @@ __global__ __launch_bounds__(Plane2dCfg<M>::THREADS) void nd_plane2d_kernel(NdCo
     z1[k] = (q < V && has_b1) ? s1[(size_t)c * V + q] : 0.f;
   }
   for (int n = 0; n < a.NO; ++n) {
-    // spectrum entries of this thread's bins i = tid + e NT; bins with kz > M/2
+    // spectrum entries of this thread's bins i = tid + e NT; bins with kz > MZ/2
     // come from the conjugate of bin -k
-    const float2* Kc = a.kh + (size_t)(n * CC + c) * M * ZH;
+    const float2* Kc = a.kh + (size_t)(n * CC + c) * MY * ZH;
     float2 kk[PER];
     auto load_k = [&]() {
 #pragma unroll
       for (int e = 0; e < PER; ++e) {
         const int i = tid + e * NT;
-        const int ky = i / M, kz = i % M;
-        const bool lower = kz <= M / 2;
-        const int ky2 = lower ? ky : (M - ky) % M;
-        const int kz2 = lower ? kz : M - kz;
+        const int ky = i / MZ, kz = i % MZ;
+        const bool lower = kz <= MZ / 2;
+        const int ky2 = lower ? ky : (MY - ky) % MY;
+        const int kz2 = lower ? kz : MZ - kz;
         const float2 kv = Kc[ky2 * ZH + kz2];
         kk[e] = lower ? kv : conjf2(kv);
       }
     };
     if (EARLY && !PQ) load_k();
     if (!CIRC) {
-      for (int i = tid; i < M * M; i += NT) P[(i / M) * C::RS + i % M] = make_float2(0.f, 0.f);
+      for (int i = tid; i < MY * MZ; i += NT) P[(i / MZ) * C::RS + i % MZ] = make_float2(0.f, 0.f);
       __syncthreads();
     }
 #pragma unroll
@@ -1088,38 +1085,38 @@ __global__ __launch_bounds__(Plane2dCfg<M>::THREADS) void nd_plane2d_kernel(NdCo
       if (q < V) P[(q / Z) * C::RS + q % Z] = make_float2(z0[k], z1[k]);
     }
     __syncthreads();
-    plane_rows<M, false>(P, Y, tw);
-    plane_cols<M, false>(P, tw);
+    plane_rows_r<MY, MZ, false>(P, Y, tw);
+    plane_cols_r<MY, MZ, false>(P, tw);
     if constexpr (!PQ) {
       if (!EARLY) load_k();
 #pragma unroll
       for (int e = 0; e < PER; ++e) {
         const int i = tid + e * NT;
-        float2* pe = P + (i / M) * C::RS + i % M;
+        float2* pe = P + (i / MZ) * C::RS + i % MZ;
         *pe = cmul(*pe, kk[e]);
       }
     } else {
       // a kernel per sample: Y(k) = P F(k) + Q conj F(-k), P, Q the half sum and
       // difference of the two samples' spectra (P(-k) = conj P(k), Q likewise).
       // A thread takes whole bin pairs {k, -k} of the canonical half (rows 1 ..
-      // M/2 - 1, and kz <= M/2 on rows 0 and M/2, their own mirrors): it reads
+      // MY/2 - 1, and kz <= MZ/2 on rows 0 and MY/2, their own mirrors): it reads
       // both bins and writes both, so every bin has one reader and one writer.
-      const float2* K0 = a.kh + (size_t)b0 * a.kh_stride + (size_t)(n * CC + c) * M * ZH;
-      const float2* K1 = a.kh + (size_t)b1 * a.kh_stride + (size_t)(n * CC + c) * M * ZH;
-      constexpr int INNER = (M / 2 - 1) * M, NPAIR = INNER + 2 * (M / 2 + 1);
+      const float2* K0 = a.kh + (size_t)b0 * a.kh_stride + (size_t)(n * CC + c) * MY * ZH;
+      const float2* K1 = a.kh + (size_t)b1 * a.kh_stride + (size_t)(n * CC + c) * MY * ZH;
+      constexpr int INNER = (MY / 2 - 1) * MZ, NPAIR = INNER + 2 * (MZ / 2 + 1);
       for (int pr = tid; pr < NPAIR; pr += NT) {
         int ky, kz;
         if (pr < INNER) {
-          ky = 1 + pr / M;
-          kz = pr % M;
+          ky = 1 + pr / MZ;
+          kz = pr % MZ;
         } else {
           const int e2 = pr - INNER;
-          ky = e2 < M / 2 + 1 ? 0 : M / 2;
-          kz = e2 % (M / 2 + 1);
+          ky = e2 < MZ / 2 + 1 ? 0 : MY / 2;
+          kz = e2 % (MZ / 2 + 1);
         }
-        const int kym = (M - ky) % M, kzm = (M - kz) % M;
-        // half-spectrum entry at k (kz <= M/2) or the conjugate of the one at -k
-        const bool lower = kz <= M / 2;
+        const int kym = (MY - ky) % MY, kzm = (MZ - kz) % MZ;
+        // half-spectrum entry at k (kz <= MZ/2) or the conjugate of the one at -k
+        const bool lower = kz <= MZ / 2;
         const int o = lower ? ky * ZH + kz : kym * ZH + kzm;
         float2 k0 = K0[o], k1 = K1[o];
         if (!lower) {
@@ -1149,8 +1146,8 @@ __global__ __launch_bounds__(Plane2dCfg<M>::THREADS) void nd_plane2d_kernel(NdCo
     };
     if (EARLY) load_x();
     __syncthreads();
-    plane_cols<M, true>(P, tw);
-    plane_rows<M, true>(P, Y, tw);
+    plane_cols_r<MY, MZ, true>(P, tw);
+    plane_rows_r<MY, MZ, true>(P, Y, tw);
     if (!EARLY) load_x();
     const float g0 = a.gate[((size_t)b0 * a.NO + n) * CC + c];
     const float g1 = has_b1 ? a.gate[((size_t)b1 * a.NO + n) * CC + c] : 0.f;
@@ -1563,26 +1560,38 @@ static hipError_t launch_pencil128(const NdConvArgs& a, int nitems, hipStream_t 
   return hipGetLastError();
 }
 
-template <int M, bool CIRC>
+template <int MY, int MZ, bool CIRC>
 static hipError_t launch_plane2d_t(const NdConvArgs& a, hipStream_t s) {
-  using C = PlaneCfg<M>;
-  auto fn = a.kh_stride != 0 ? nd_plane2d_kernel<M, CIRC, true> : nd_plane2d_kernel<M, CIRC, false>;
+  using C = PlaneCfg<MY, MZ>;
+  auto fn = a.kh_stride != 0 ? nd_plane2d_kernel<MY, MZ, CIRC, true> : nd_plane2d_kernel<MY, MZ, CIRC, false>;
   hipError_t e = nd_allow_lds((const void*)fn, C::LDS);
   if (e != hipSuccess) return e;
   const int items = (a.B + 1) / 2 * a.C;
   const int per_xcd = (items + 7) / 8;
-  hipLaunchKernelGGL(fn, dim3(8 * per_xcd), dim3(Plane2dCfg<M>::THREADS), C::LDS, s, a, per_xcd);
+  hipLaunchKernelGGL(fn, dim3(8 * per_xcd), dim3(C::THREADS), C::LDS, s, a, per_xcd);
   return hipGetLastError();
+}
+
+template <int MY, bool CIRC>
+static hipError_t launch_plane2d_z(const NdConvArgs& a, hipStream_t s) {
+  switch (a.MZ) {
+    case 8: return launch_plane2d_t<MY, 8, CIRC>(a, s);
+    case 16: return launch_plane2d_t<MY, 16, CIRC>(a, s);
+    case 32: return launch_plane2d_t<MY, 32, CIRC>(a, s);
+    case 64: return launch_plane2d_t<MY, 64, CIRC>(a, s);
+    case 128: return launch_plane2d_t<MY, 128, CIRC>(a, s);
+    default: return hipErrorInvalidValue;
+  }
 }
 
 template <bool CIRC>
 static hipError_t launch_plane2d(const NdConvArgs& a, hipStream_t s) {
   switch (a.MY) {
-    case 8: return launch_plane2d_t<8, CIRC>(a, s);
-    case 16: return launch_plane2d_t<16, CIRC>(a, s);
-    case 32: return launch_plane2d_t<32, CIRC>(a, s);
-    case 64: return launch_plane2d_t<64, CIRC>(a, s);
-    case 128: return launch_plane2d_t<128, CIRC>(a, s);
+    case 8: return launch_plane2d_z<8, CIRC>(a, s);
+    case 16: return launch_plane2d_z<16, CIRC>(a, s);
+    case 32: return launch_plane2d_z<32, CIRC>(a, s);
+    case 64: return launch_plane2d_z<64, CIRC>(a, s);
+    case 128: return launch_plane2d_z<128, CIRC>(a, s);
     default: return hipErrorInvalidValue;
   }
 }

@@ -27,13 +27,13 @@ bool boundary_ok(int bd) { return bd == HYENA_ND_ZERO_PAD || bd == HYENA_ND_CIRC
 int pad_of(int bd) { return bd == HYENA_ND_CIRCULAR ? 1 : 2; }
 
 // Transform lengths up to 128 (the twiddle table W_128); at least 8 points per
-// axis, except X = 1: a 2D grid (one x-plane, every offset with dx = 0), whose
-// fused kernel takes square planes (Y = Z). 3D grids take X, Y, Z independently.
+// axis, except X = 1: a 2D grid (one x-plane, every offset with dx = 0). Y and Z
+// (and X for 3D grids) are independent.
 bool nd_shape_ok(int X, int Y, int Z, int C, int N, int bd) {
   if (!boundary_ok(bd)) return false;
   const int lo = 8 / pad_of(bd), hi = 128 / pad_of(bd);
-  return (X == 1 || pow2_in(X, lo, hi)) && pow2_in(Y, lo, hi) && pow2_in(Z, lo, hi) && (X > 1 || Z == Y) &&
-         C >= 64 && C <= 4096 && C % 64 == 0 && N >= 1 && N <= 4;
+  return (X == 1 || pow2_in(X, lo, hi)) && pow2_in(Y, lo, hi) && pow2_in(Z, lo, hi) && C >= 64 && C <= 4096 &&
+         C % 64 == 0 && N >= 1 && N <= 4;
 }
 
 // transform length along x: no padding of a one-point axis

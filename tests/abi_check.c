@@ -103,7 +103,7 @@ static void sweep_1d_sizes(void) {
 static int shape_nd(int X, int Y, int Z, int C, int N, int bd) {
   if (bd != HYENA_ND_ZERO_PAD && bd != HYENA_ND_CIRCULAR) return 0;
   const int lo = bd == HYENA_ND_CIRCULAR ? 8 : 4, hi = bd == HYENA_ND_CIRCULAR ? 128 : 64;
-  const int axes = (X == 1 ? Y == Z : pow2_in(X, lo, hi)) && pow2_in(Y, lo, hi) && pow2_in(Z, lo, hi);
+  const int axes = (X == 1 || pow2_in(X, lo, hi)) && pow2_in(Y, lo, hi) && pow2_in(Z, lo, hi);
   return axes && C >= 64 && C <= 4096 && C % 64 == 0 && N >= 1 && N <= 4;
 }
 
@@ -307,7 +307,7 @@ static void checks_nd(void) {
   memset(&nd, 0, sizeof(nd));
   EXPECT_EQ(hyena_nd_layer_init(NULL, X, Y, Z, C, N, P, cache), HYENA_ERR_INVALID_ARG);
   EXPECT_EQ(hyena_nd_layer_init(&nd, X, Y, 24, C, N, P, cache), HYENA_ERR_UNSUPPORTED);
-  EXPECT_EQ(hyena_nd_layer_init(&nd, 1, Y, Z, C, N, P, cache), HYENA_ERR_UNSUPPORTED);  /* 2D takes Y = Z */
+  EXPECT_EQ(hyena_nd_layer_init(&nd, 2, Y, Z, C, N, P, cache), HYENA_ERR_UNSUPPORTED);  /* X = 2 is no grid */
   EXPECT_EQ(hyena_nd_layer_init_ex(&nd, X, Y, Z, C, N, 9, P, cache), HYENA_ERR_UNSUPPORTED);
   EXPECT_EQ(hyena_nd_layer_init(&nd, X, Y, Z, C, N, NULL, cache), HYENA_ERR_INVALID_ARG);
   EXPECT_EQ(hyena_nd_layer_init(&nd, X, Y, Z, C, N, P, cache - 1), HYENA_ERR_WORKSPACE);

@@ -189,7 +189,9 @@ def test_nd_size_queries_by_boundary(hy):
     assert hy.hyena_nd_cache_bytes(1, 64, 64, 64, 2) == al(128 * 8) + al(2 * 64 * 1 * 128 * 65 * 8)
     assert hy.hyena_nd_cache_bytes_ex(1, 128, 128, 64, 2, hy.ND_CIRCULAR) == al(128 * 8) + al(2 * 64 * 128 * 65 * 8)
     assert hy.hyena_nd_cache_bytes(2, 8, 8, 64, 2) == 0            # X = 2 is not a 2D grid
-    assert hy.hyena_nd_cache_bytes(1, 16, 32, 64, 2) == 0          # 2D grids take square planes
+    # 2D grids take Y and Z independently
+    assert hy.hyena_nd_cache_bytes(1, 16, 32, 64, 2) == al(128 * 8) + al(2 * 64 * 1 * 32 * 33 * 8)
+    assert hy.hyena_nd_cache_bytes_ex(1, 128, 8, 64, 1, hy.ND_CIRCULAR) == al(128 * 8) + al(64 * 128 * 5 * 8)
     assert hy.hyena_nd_filter_workspace_bytes(1, 4, 4, 64, 1) > 0
 
 

@@ -48,9 +48,11 @@ SWEEP = [
     (1, 16, 64, 2, "f32"), (3, 32, 64, 1, "f32"), (1, 64, 128, 3, "f32"), (2, 128, 64, 2, "f32"),
     (1, 256, 64, 2, "f32"), (3, 512, 128, 2, "f32"), (1, 2048, 64, 3, "f32"), (2, 4096, 64, 2, "f32"),
     (2, 1024, 128, 2, "bf16"), (1, 4096, 192, 4, "f32"), (2, 512, 64, 1, "bf16"), (1, 2048, 128, 4, "bf16"),
-    # four-step regime (2L >= 16384): N2 = 64, 128, 256, 512
+    # four-step regime (2L >= 16384, N1 = 64): rows of N2 = 256, 512, 1024, 2048 points
     (1, 8192, 64, 2, "f32"), (3, 16384, 64, 1, "f32"), (1, 32768, 128, 2, "f32"), (1, 65536, 64, 2, "f32"),
     (2, 16384, 64, 2, "bf16"),
+    # bf16 rows of 1024 and 2048 points: the one-wave-per-row kernel
+    (3, 32768, 64, 2, "bf16"), (2, 65536, 128, 1, "bf16"),
 ]
 
 
@@ -137,7 +139,7 @@ NONCAUSAL = [
     (1, 16, 64, 2, "f32"), (2, 64, 64, 2, "f32"), (2, 1024, 128, 2, "f32"), (1, 4096, 64, 3, "f32"),
     (2, 2048, 128, 2, "bf16"),
     # four-step regime
-    (1, 8192, 64, 2, "f32"), (2, 16384, 64, 1, "bf16"), (1, 65536, 64, 2, "f32"),
+    (1, 8192, 64, 2, "f32"), (2, 16384, 64, 1, "bf16"), (1, 65536, 64, 2, "f32"), (1, 32768, 64, 2, "bf16"),
 ]
 
 

@@ -62,7 +62,8 @@ def test_film_sweep(B, X, Y, C, N, W, R, circ):
     _check(make_nd_film(600 + B + X + Y + C + N + W + R + 7 * circ, B, X, Y, Y, C, N=N, W=W, R=R, circular=circ))
 
 
-@pytest.mark.parametrize("B,X,Y,Z,circ", [(2, 8, 16, 32, False), (3, 16, 8, 4, False), (2, 16, 32, 8, True)])
+@pytest.mark.parametrize("B,X,Y,Z,circ", [(2, 8, 16, 32, False), (3, 16, 8, 4, False), (2, 16, 32, 8, True),
+                                           (3, 1, 16, 64, False), (2, 1, 64, 8, True)])  # 2D: 32 x 128, 64 x 8
 def test_film_non_square(B, X, Y, Z, circ):
     # independent grid axes with per-sample kernels (the (P, Q) pencil pass)
     _check(make_nd_film(640 + B + X + 3 * Y + 5 * Z + 7 * circ, B, X, Y, Z, 64, N=2, W=64, R=4, circular=circ))

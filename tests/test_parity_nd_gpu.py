@@ -133,6 +133,21 @@ def test_nd_2d_sweep(B, Y, C, N, circ):
     _check(make_nd(500 + B + Y + C + N + 7 * circ, B, 1, Y, Y, C, N=N, W=64, u_mean_spread=0.5, circular=circ))
 
 
+@pytest.mark.parametrize("B,Y,Z,C,N,circ", [
+    (2, 4, 64, 64, 2, False),     # 8 x 128 planes (the widest and flattest)
+    (3, 64, 4, 64, 1, False),     # 128 x 8, odd batch
+    (2, 16, 32, 64, 2, False),    # 32 x 64
+    (1, 32, 8, 128, 3, False),    # 64 x 16, three orders
+    (2, 8, 128, 64, 2, True),     # circular 8 x 128
+    (3, 64, 16, 64, 2, True),     # circular 64 x 16, odd batch
+    (2, 128, 64, 64, 1, True),    # circular 128 x 64 (1024-line transforms)
+])
+def test_nd_2d_non_square_sweep(B, Y, Z, C, N, circ):
+    # 2D grids take Y and Z independently, like 3D grids
+    _check(make_nd(520 + B + 3 * Y + 5 * Z + C + N + 7 * circ, B, 1, Y, Z, C, N=N, W=64, u_mean_spread=0.5,
+                   circular=circ))
+
+
 # ------------------------------------------------------------- reproducibility
 
 @pytest.mark.parametrize("X,Y,circ", [(8, 16, False), (16, 16, False), (8, 16, True)])
