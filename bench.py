@@ -448,7 +448,7 @@ def main_nd_film(args, torch, hs, make_config):
 
 
 def main_bwd(args, torch, hs, make_config):
-    """Times hyena_bwd (and hyena_filter_bwd) on a 1D workload of the on-chip regime."""
+    """Times hyena_bwd (and hyena_filter_bwd) on a 1D workload (two-sided filters up to L = 4096)."""
     log(f"generating inputs for {args.workload} (backward)")
     inp = make_config(args.workload)
     B, L, D, N = inp.B, inp.L, inp.D, inp.N
@@ -503,7 +503,7 @@ def main():
     ap.add_argument("--workload", default=DEFAULT_WORKLOAD)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--backward", action="store_true",
-                    help="time hyena_bwd and hyena_filter_bwd instead (1D workloads with L <= 4096)")
+                    help="time hyena_bwd and hyena_filter_bwd instead (1D workloads)")
     ap.add_argument("--cpu-tokens", type=int, default=0,
                     help="positions of the 1D oracle sample (default 0: the whole sequence)")
     ap.add_argument("--cpu-workers", type=int, default=0,

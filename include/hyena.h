@@ -179,11 +179,14 @@ int hyena_fwd_noalloc(const hyena_layer *layer, const void *u, const void *w_in,
  *   dh^n(tau) = sum_{b,t} (g x^n)(t) z^n(t - tau)
  *   dp_j(t) = sum_k short_w[j][k] ds_j(t + k),  dshort_w[j][k] = sum_{b,t} ds_j(t) p_j(t - k)
  *   du = dp W_in^T,  dW_in = sum_b u_b^T dp_b,   ds = (dz^1, dx^1 .. dx^N)
- * The correlations run through the layer's cached filter spectra (conjugated).
- * Supported: the on-chip regime, L a power of two in [32, 4096]; otherwise as
- * hyena_fwd. Every gradient is recomputed from the inputs (nothing is kept from
- * a forward call). The batch sums are taken in a fixed order, so results are
- * bit-reproducible.
+ * The correlations run through the layer's cached filter spectra: conjugated
+ * in the on-chip regime (L <= 4096); beyond it, through the forward's
+ * four-step passes as R conv R with R the time reversal on [0, L), and dh^n as
+ * the convolution of R(g x^n) with z^n taken as a filter, transformed per
+ * sample. Supported: L a power of two in [32, 2^20], two-sided filters up to
+ * L = 4096; D, N and B as hyena_fwd. Every gradient is recomputed from the
+ * inputs (nothing is kept from a forward call). The batch sums are taken in a
+ * fixed order, so results are bit-reproducible.
  */
 size_t hyena_bwd_workspace_bytes(int B, int L, int D, int N, int dtype, int direction);
 

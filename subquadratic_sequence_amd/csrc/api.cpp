@@ -9,6 +9,7 @@
 
 #include "common.h"
 #include "kernels.h"
+#include "kernels_bwd.h"
 
 using hy::align_up;
 
@@ -177,7 +178,11 @@ int group_pairs(int pairs_all, size_t y_bytes_per_pair) {
 // ---------------------------------------------------------------- backward
 constexpr int kBwdMinL = 32;  // the weight-gradient products take K = L in whole bf16 K tiles
 
-bool bwd_shape_ok(int L, int D, int N) { return shape_ok(L, D, N) && L >= kBwdMinL && L <= kLdsMaxL; }
+// The on-chip regime takes both directions; the four-step regime (the
+// forward's passes, below) causal filters.
+bool bwd_shape_ok(int L, int D, int N, int dir) {
+  return shape_ok(L, D, N) && L >= kBwdMinL && direction_ok(dir) && (L <= kLdsMaxL || dir == HYENA_CAUSAL);
+}
 
 // K splits of a reduction product (weight gradients: K runs over positions)
 // so that about 512 workgroups share it: powers of two that keep whole K
@@ -194,8 +199,11 @@ int bwd_split_in(int B, int L, int D, int N, int dtype) {
 }
 
 struct BwdWs {
-  size_t wt_in, s, p, gz, zsave, csave, zfin, sbar, pbar, dh_part, dd_part, dsw_part, dyT, uT, dwo_part, dwi_part,
-      total;
+  size_t wt_in, s, p, gz, zsave, csave, zfin, sbar, pbar, dh_part, dd_part, dsw_part, dyT, uT, dwo_part, dwi_part;
+  // four-step regime: convolution staging and output, the passes' intermediate,
+  // dz ping-pong (fp32), one sample's z spectrum (fp32 and bf16), zero skips
+  size_t tmp, cout, Y, g0, g1, pq_tmp, pqb_tmp, zeros;
+  size_t total;
 };
 BwdWs bwd_ws(int B, int L, int D, int N, int dtype, int dir) {
   BwdWs w{};
@@ -223,6 +231,18 @@ BwdWs bwd_ws(int B, int L, int D, int N, int dtype, int dir) {
   take(w.uT, BDL * es);
   take(w.dwo_part, (size_t)B * bwd_split_out(B, L, D, dtype) * D * D * es);
   take(w.dwi_part, (size_t)B * bwd_split_in(B, L, D, N, dtype) * D * J * es);
+  if (L > kLdsMaxL) {
+    const int n1 = hy::fourstep_n1(L);
+    const size_t entries = (size_t)(D / 2) * (n1 / 2 + 1) * (2 * (size_t)L / n1);
+    take(w.tmp, 2 * BDL * es);
+    take(w.cout, BDL * es);
+    take(w.Y, (size_t)B * (D / 2) * 2 * (size_t)L * 8);
+    take(w.g0, BDL * 4);
+    take(w.g1, BDL * 4);
+    take(w.pq_tmp, entries * 16);
+    take(w.pqb_tmp, entries * 8);
+    take(w.zeros, (size_t)D * 4);
+  }
   w.total = off;
   return w;
 }
@@ -268,6 +288,90 @@ FilterBwdWs filter_bwd_ws(int L, int D, int N, int K, int W, int dir) {
 }
 
 bool filter_bwd_params_ok(int K, int W) { return K >= 1 && K <= 32 && W >= 16 && W <= 128 && W % 16 == 0; }
+
+// Backward through the orders in the four-step regime (causal filters), built
+// on the forward's four-step convolution: every convolution below is
+// fourstep_conv on one order with gates of one and skips of zero, its input in
+// block 0 of tmp [B][2D][L] (block 1 holds the ones). With R the reversal
+// t -> L - 1 - t on [0, L), the transposed convolution is R conv_h R, and the
+// filter gradient dh(tau) = sum_t dc(t) z(t - tau) = conv(R dc, z)(L - 1 - tau)
+// takes z^n as the filter, its spectrum made per sample by the filter-spectrum
+// passes. Outputs as bwd_lds_conv: z^{N+1}, ds = (dz^1, dx^1 .. dx^N) and the
+// per-sample dh and dD partials. Returns a status.
+int bwd_fourstep(const hyena_layer* layer, const CacheLayout& cl, const BwdWs& w, char* wb, const float* dskip,
+                 int B, bool bf, hipStream_t stream) {
+  const int L = layer->L, D = layer->D, N = layer->N, half = D / 2, J = (N + 1) * D;
+  const size_t es = bf ? 2 : 4, DL = (size_t)D * L, BDL = (size_t)B * DL;
+  char* cb = static_cast<char*>(layer->cache);
+  const hy::FourStepTables tb = tables(cl, layer->cache);
+  const size_t per_order = (size_t)half * (hy::fourstep_n1(L) / 2 + 1) * cl.N2;  // spectrum entries per order
+  const float4* pq = reinterpret_cast<const float4*>(cb + cl.pq);
+  const char* pqb = cb + cl.pq_bf16;  // 8-byte bf16 entries
+  char* tmp = wb + w.tmp;
+  void* cout = wb + w.cout;
+  float* zs = reinterpret_cast<float*>(wb + w.zsave);  // z^1 .. z^N, fp32
+  char* cs = wb + w.csave;                              // c^1 .. c^N, storage type
+  float* sbar = reinterpret_cast<float*>(wb + w.sbar);
+  float* dd_part = reinterpret_cast<float*>(wb + w.dd_part);
+  float* dh_part = reinterpret_cast<float*>(wb + w.dh_part);
+  const bool ybf = bf && tuning().y_bf16;
+  auto conv = [&](const void* in, int Bc, const float4* p, const void* pb, void* out) {
+    hy::FourStepConvArgs a{};
+    a.s = in;
+    a.dskip = reinterpret_cast<const float*>(wb + w.zeros);
+    a.pq = p;
+    a.pq_bf16 = pb;
+    a.z[0] = a.z[1] = out;  // one order: only zfinal is written
+    a.zfinal = out;
+    a.Y = wb + w.Y;
+    a.B = Bc;
+    a.L = L;
+    a.D = D;
+    a.NO = 1;
+    a.y_bf16 = tuning().y_bf16;
+    a.group_pairs = group_pairs(Bc * half, (size_t)2 * L * (ybf ? 4 : 8));
+    return hy::fourstep_conv(tb, a, bf, stream);
+  };
+  HY_CHECK_HIP(hy::bwd4_fill(wb + w.zeros, 0.f, 1, D, D, false, stream));
+  HY_CHECK_HIP(hy::bwd4_fill(tmp + DL * es, 1.f, B, DL, 2 * DL, bf, stream));
+  // forward orders, keeping z^n (fp32) and c^n (storage type)
+  HY_CHECK_HIP(hy::bwd4_z_init(wb + w.s, zs, tmp, B, D, L, N, bf, stream));
+  for (int n = 0; n < N; ++n) {
+    char* cn = cs + (size_t)n * BDL * es;
+    HY_CHECK_HIP(conv(tmp, B, pq + n * per_order, pqb + n * per_order * 8, cn));
+    float* znext = n == N - 1 ? nullptr : zs + (size_t)(n + 1) * BDL;
+    HY_CHECK_HIP(hy::bwd4_z_next(wb + w.s, cn, zs + (size_t)n * BDL, dskip + (size_t)n * D, znext, tmp,
+                                 wb + w.zfin, B, D, L, N, n, bf, stream));
+  }
+  // orders in reverse, g = dz^{n+1} in fp32
+  float* g = reinterpret_cast<float*>(wb + w.g0);
+  float* gn = reinterpret_cast<float*>(wb + w.g1);
+  HY_CHECK_HIP(hy::bwd4_to_f32(wb + w.gz, g, BDL, bf, stream));
+  for (int n = N - 1; n >= 0; --n) {
+    const float* zn = zs + (size_t)n * BDL;
+    // dx^n = g c^n, staging R(g x^n), sum_t g z^n
+    HY_CHECK_HIP(hy::bwd4_rev_prep(g, wb + w.s, cs + (size_t)n * BDL * es, zn, sbar, tmp, dd_part, B, D, L, N, n, bf,
+                                   stream));
+    // dz^n = D^n g + R conv_h R(g x^n); dz^1 is block 0 of ds
+    HY_CHECK_HIP(conv(tmp, B, pq + n * per_order, pqb + n * per_order * 8, cout));
+    float* out = n == 0 ? sbar : gn;
+    HY_CHECK_HIP(hy::bwd4_rev_finish(g, cout, dskip + (size_t)n * D, out, n == 0 ? (size_t)J * L : DL, B, D, L, bf,
+                                     stream));
+    // dh^n of each sample: z^n_b as the filter, R(g x^n)_b as the input
+    for (int b = 0; b < B; ++b) {
+      HY_CHECK_HIP(hy::fourstep_spec(tb, zn + (size_t)b * DL, reinterpret_cast<float2*>(wb + w.Y),
+                                     reinterpret_cast<float4*>(wb + w.pq_tmp), wb + w.pqb_tmp, L, D, 1, false,
+                                     stream));
+      HY_CHECK_HIP(conv(tmp + (size_t)b * 2 * DL * es, 1, reinterpret_cast<const float4*>(wb + w.pq_tmp),
+                        wb + w.pqb_tmp, cout));
+      HY_CHECK_HIP(hy::bwd4_dh_store(cout, dh_part + ((size_t)b * N + n) * DL, D, L, bf, stream));
+    }
+    float* t = g;
+    g = gn;
+    gn = t;
+  }
+  return HYENA_OK;
+}
 
 }  // namespace
 
@@ -464,8 +568,7 @@ int hyena_fwd_profiled(const hyena_layer* layer, const void* u, const void* w_in
 }
 
 size_t hyena_bwd_workspace_bytes(int B, int L, int D, int N, int dtype, int direction) {
-  if (!bwd_shape_ok(L, D, N) || B < 1 || (dtype != HYENA_F32 && dtype != HYENA_BF16) || !direction_ok(direction))
-    return 0;
+  if (!bwd_shape_ok(L, D, N, direction) || B < 1 || (dtype != HYENA_F32 && dtype != HYENA_BF16)) return 0;
   if (!fits_i32(B, L, D, N)) return 0;
   return bwd_ws(B, L, D, N, dtype, direction).total;
 }
@@ -480,7 +583,7 @@ int hyena_bwd(const hyena_layer* layer, const void* u, const void* w_in, const f
     if (!aligned16(q)) return HYENA_ERR_INVALID_ARG;
   if (B < 1) return HYENA_ERR_INVALID_ARG;
   const int L = layer->L, D = layer->D, N = layer->N, dir = layer->direction;
-  if (!bwd_shape_ok(L, D, N) || !direction_ok(dir)) return HYENA_ERR_UNSUPPORTED;
+  if (!bwd_shape_ok(L, D, N, dir)) return HYENA_ERR_UNSUPPORTED;
   if (!layer->built || !aligned16(layer->cache)) return HYENA_ERR_LAYER_MISMATCH;
   const CacheLayout cl = cache_layout(L, D, N);
   if (layer->cache_bytes < cl.total) return HYENA_ERR_LAYER_MISMATCH;
@@ -500,26 +603,34 @@ int hyena_bwd(const hyena_layer* layer, const void* u, const void* w_in, const f
   // dz^{N+1} = dy W_out^T, channel-major (W_out as stored is the transposed operand)
   HY_CHECK_HIP(hy::gemm(hy::GemmArgs{dy, w_out, wb + w.gz, B * L, D, D, L, false, true, nullptr}, bf, stream));
   // forward recompute and the orders in reverse
-  hy::BwdConvArgs a{};
-  a.s = wb + w.s;
-  a.gz = wb + w.gz;
-  a.zsave = reinterpret_cast<float*>(wb + w.zsave);
-  a.csave = reinterpret_cast<float*>(wb + w.csave);
-  a.zfin = wb + w.zfin;
-  a.dskip = dskip;
-  a.pq = reinterpret_cast<const float4*>(cb + cl.pq);
-  a.tw = reinterpret_cast<const float2*>(cb + cl.tw);
-  a.sbar = reinterpret_cast<float*>(wb + w.sbar);
-  a.dh_part = reinterpret_cast<float*>(wb + w.dh_part);
-  a.dd_part = reinterpret_cast<float*>(wb + w.dd_part);
-  a.B = B;
-  a.L = L;
-  a.D = D;
-  a.NO = N;
-  a.HL = HL;
-  HY_CHECK_HIP(hy::bwd_lds_conv(a, bf, stream));
+  float* sbar = reinterpret_cast<float*>(wb + w.sbar);
+  float* dh_part = reinterpret_cast<float*>(wb + w.dh_part);
+  float* dd_part = reinterpret_cast<float*>(wb + w.dd_part);
+  if (!cl.lds) {
+    const int st = bwd_fourstep(layer, cl, w, wb, dskip, B, bf, stream);
+    if (st != HYENA_OK) return st;
+  } else {
+    hy::BwdConvArgs a{};
+    a.s = wb + w.s;
+    a.gz = wb + w.gz;
+    a.zsave = reinterpret_cast<float*>(wb + w.zsave);
+    a.csave = reinterpret_cast<float*>(wb + w.csave);
+    a.zfin = wb + w.zfin;
+    a.dskip = dskip;
+    a.pq = reinterpret_cast<const float4*>(cb + cl.pq);
+    a.tw = reinterpret_cast<const float2*>(cb + cl.tw);
+    a.sbar = sbar;
+    a.dh_part = dh_part;
+    a.dd_part = dd_part;
+    a.B = B;
+    a.L = L;
+    a.D = D;
+    a.NO = N;
+    a.HL = HL;
+    HY_CHECK_HIP(hy::bwd_lds_conv(a, bf, stream));
+  }
   // short convolution transpose: dp, and per-sample tap gradients
-  HY_CHECK_HIP(hy::short_conv_bwd(a.sbar, wb + w.p, short_w, wb + w.pbar, reinterpret_cast<float*>(wb + w.dsw_part),
+  HY_CHECK_HIP(hy::short_conv_bwd(sbar, wb + w.p, short_w, wb + w.pbar, reinterpret_cast<float*>(wb + w.dsw_part),
                                   B * J, L, J, bf, stream));
   // du = dp W_in^T (dp channel-major; W_in as stored is the transposed operand)
   HY_CHECK_HIP(hy::gemm(hy::GemmArgs{wb + w.pbar, w_in, du, B * L, D, J, L, true, false, nullptr}, bf, stream));
@@ -549,8 +660,8 @@ int hyena_bwd(const hyena_layer* layer, const void* u, const void* w_in, const f
   // sums over the batch, in a fixed order
   HY_CHECK_HIP(hy::sum_rows(wb + w.dwo_part, dw_out, B * so, (size_t)D * D, (size_t)D * D, bf, stream));
   HY_CHECK_HIP(hy::sum_rows(wb + w.dwi_part, dw_in, B * si, (size_t)D * J, (size_t)D * J, bf, stream));
-  HY_CHECK_HIP(hy::sum_rows(a.dh_part, dh, B, (size_t)N * D * HL, (size_t)N * D * HL, false, stream));
-  HY_CHECK_HIP(hy::sum_rows(a.dd_part, ddskip, B, (size_t)N * D, (size_t)N * D, false, stream));
+  HY_CHECK_HIP(hy::sum_rows(dh_part, dh, B, (size_t)N * D * HL, (size_t)N * D * HL, false, stream));
+  HY_CHECK_HIP(hy::sum_rows(dd_part, ddskip, B, (size_t)N * D, (size_t)N * D, false, stream));
   HY_CHECK_HIP(hy::sum_rows(wb + w.dsw_part, dshort_w, B, (size_t)J * 3, (size_t)J * 3, false, stream));
   return HYENA_OK;
 }

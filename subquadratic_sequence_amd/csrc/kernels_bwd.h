@@ -1,0 +1,31 @@
+// Launchers of the elementwise kernels of the four-step backward (bwd4.hip).
+// Layouts: rows of L positions; s [B][(NO+1)D][L] and ds [B][(NO+1)D][L] in the
+// block order (v, x^1 .. x^NO); the staging buffer tmp [B][2D][L] holds a
+// convolution input in block 0 and ones in block 1. T is the storage type.
+#pragma once
+#include <hip/hip_runtime.h>
+
+namespace hy {
+
+// p[r * stride + i] = v for r < rows, i < len (fp32 or bf16 elements)
+hipError_t bwd4_fill(void* p, float v, int rows, size_t len, size_t stride, bool bf16, hipStream_t s);
+// z^1 = v block of s: zf [B][D][L] fp32 and tmp block 0 (storage type)
+hipError_t bwd4_z_init(const void* sp, float* zf, void* tmp, int B, int D, int L, int NO, bool bf16, hipStream_t s);
+// z^{n+1} = x^n c^n + D^n z^n from s block n+1, c (storage) and zf (fp32 z^n):
+// into zf_next (fp32) and tmp block 0 (storage), or, for the last order, into
+// zfin (storage) when zf_next is null
+hipError_t bwd4_z_next(const void* sp, const void* c, const float* zf, const float* dskip_n, float* zf_next,
+                       void* tmp, void* zfin, int B, int D, int L, int NO, int n, bool bf16, hipStream_t s);
+// storage -> fp32 copy of n elements
+hipError_t bwd4_to_f32(const void* in, float* out, size_t n, bool bf16, hipStream_t s);
+// with g = dz^{n+1} (fp32 [B][D][L]): ds block n+1 = g c^n, tmp block 0 =
+// R(g x^n) (storage, R the reversal t -> L - 1 - t), dd_part[b][n][d] = sum_t g z^n
+hipError_t bwd4_rev_prep(const float* g, const void* sp, const void* c, const float* zf, float* sbar, void* tmp,
+                         float* dd_part, int B, int D, int L, int NO, int n, bool bf16, hipStream_t s);
+// out[b][d][t] (row stride ostride) = D^n_d g[b][d][t] + conv[b][d][L - 1 - t]
+hipError_t bwd4_rev_finish(const float* g, const void* conv, const float* dskip_n, float* out, size_t ostride, int B,
+                           int D, int L, bool bf16, hipStream_t s);
+// dh[d][tau] = conv[d][L - 1 - tau] (one sample, fp32 out)
+hipError_t bwd4_dh_store(const void* conv, float* dh, int D, int L, bool bf16, hipStream_t s);
+
+}  // namespace hy

@@ -94,6 +94,31 @@ def test_bwd_sweep(B, L, D, N, dt, causal):
     _check(make_1d(700 + B + L + D + N, B, L, D, N=N, K=8, dtype=dt, causal=causal))
 
 
+# Four-step regime (L > 4096, causal filters): the transposed convolution and the
+# filter gradient run on the forward's four-step passes (reversal, one order,
+# unit gates) with per-sample spectra of z^n for dh.
+@pytest.mark.parametrize("B,L,D,N,dt", [
+    (2, 8192, 64, 2, "f32"),       # 256-point rows, two samples' spectra for dh
+    (1, 8192, 64, 3, "f32"),       # three orders
+    (1, 16384, 128, 1, "bf16"),
+    (3, 32768, 64, 2, "bf16"),     # odd batch, 1024-point rows
+    (1, 65536, 64, 2, "bf16"),     # the 64k length, 2048-point rows
+])
+def test_bwd_four_step(B, L, D, N, dt):
+    _check(make_1d(730 + B + L // 1024 + D + N, B, L, D, N=N, K=8, dtype=dt))
+
+
+def test_bwd_four_step_is_bit_reproducible():
+    import torch
+    inp = make_1d(741, 2, 8192, 64, N=2, K=8, dtype="bf16")
+    dy = _dy(inp, 11)
+    a, _ = _gpu_bwd(inp, dy)
+    b, _ = _gpu_bwd(inp, dy)
+    torch.cuda.synchronize()
+    for k in KEYS:
+        assert np.array_equal(a[k], b[k]), k
+
+
 def test_bwd_is_bit_reproducible():
     import torch
     inp = make_1d(711, 2, 512, 128, N=2, K=8)
