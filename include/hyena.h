@@ -183,8 +183,9 @@ int hyena_fwd_noalloc(const hyena_layer *layer, const void *u, const void *w_in,
  * in the on-chip regime (L <= 4096); beyond it, through the forward's
  * four-step passes as R conv R with R the time reversal on [0, L), and dh^n as
  * the convolution of R(g x^n) with z^n taken as a filter, transformed per
- * sample. Supported: L a power of two in [32, 2^20], two-sided filters up to
- * L = 4096; D, N and B as hyena_fwd. Every gradient is recomputed from the
+ * sample (negative lags: R z^n with g x^n as the filter). Supported: L a power
+ * of two in [32, 2^20], both directions; D, N and B as hyena_fwd. Every
+ * gradient is recomputed from the
  * inputs (nothing is kept from a forward call). The batch sums are taken in a
  * fixed order, so results are bit-reproducible.
  */

@@ -178,11 +178,7 @@ int group_pairs(int pairs_all, size_t y_bytes_per_pair) {
 // ---------------------------------------------------------------- backward
 constexpr int kBwdMinL = 32;  // the weight-gradient products take K = L in whole bf16 K tiles
 
-// The on-chip regime takes both directions; the four-step regime (the
-// forward's passes, below) causal filters.
-bool bwd_shape_ok(int L, int D, int N, int dir) {
-  return shape_ok(L, D, N) && L >= kBwdMinL && direction_ok(dir) && (L <= kLdsMaxL || dir == HYENA_CAUSAL);
-}
+bool bwd_shape_ok(int L, int D, int N, int dir) { return shape_ok(L, D, N) && L >= kBwdMinL && direction_ok(dir); }
 
 // K splits of a reduction product (weight gradients: K runs over positions)
 // so that about 512 workgroups share it: powers of two that keep whole K
@@ -201,8 +197,9 @@ int bwd_split_in(int B, int L, int D, int N, int dtype) {
 struct BwdWs {
   size_t wt_in, s, p, gz, zsave, csave, zfin, sbar, pbar, dh_part, dd_part, dsw_part, dyT, uT, dwo_part, dwi_part;
   // four-step regime: convolution staging and output, the passes' intermediate,
-  // dz ping-pong (fp32), one sample's z spectrum (fp32 and bf16), zero skips
-  size_t tmp, cout, Y, g0, g1, pq_tmp, pqb_tmp, zeros;
+  // dz ping-pong (fp32), one sample's z (or dc) spectrum (fp32 and bf16), zero
+  // skips; two-sided filters: g x^n in fp32
+  size_t tmp, cout, Y, g0, g1, pq_tmp, pqb_tmp, zeros, dcf;
   size_t total;
 };
 BwdWs bwd_ws(int B, int L, int D, int N, int dtype, int dir) {
@@ -242,6 +239,7 @@ BwdWs bwd_ws(int B, int L, int D, int N, int dtype, int dir) {
     take(w.pq_tmp, entries * 16);
     take(w.pqb_tmp, entries * 8);
     take(w.zeros, (size_t)D * 4);
+    if (dir == HYENA_NONCAUSAL) take(w.dcf, BDL * 4);
   }
   w.total = off;
   return w;
@@ -289,15 +287,18 @@ FilterBwdWs filter_bwd_ws(int L, int D, int N, int K, int W, int dir) {
 
 bool filter_bwd_params_ok(int K, int W) { return K >= 1 && K <= 32 && W >= 16 && W <= 128 && W % 16 == 0; }
 
-// Backward through the orders in the four-step regime (causal filters), built
-// on the forward's four-step convolution: every convolution below is
-// fourstep_conv on one order with gates of one and skips of zero, its input in
-// block 0 of tmp [B][2D][L] (block 1 holds the ones). With R the reversal
-// t -> L - 1 - t on [0, L), the transposed convolution is R conv_h R, and the
-// filter gradient dh(tau) = sum_t dc(t) z(t - tau) = conv(R dc, z)(L - 1 - tau)
-// takes z^n as the filter, its spectrum made per sample by the filter-spectrum
-// passes. Outputs as bwd_lds_conv: z^{N+1}, ds = (dz^1, dx^1 .. dx^N) and the
-// per-sample dh and dD partials. Returns a status.
+// Backward through the orders in the four-step regime, built on the forward's
+// four-step convolution: every convolution below is fourstep_conv on one order
+// with gates of one and skips of zero, its input in block 0 of tmp [B][2D][L]
+// (block 1 holds the ones). With R the reversal t -> L - 1 - t on [0, L), the
+// transposed convolution is R conv_h R (causal and two-sided filters alike: the
+// layer's spectra hold either), and the filter gradient
+// dh(tau) = sum_t dc(t) z(t - tau) is conv(R dc, z)(L - 1 - tau) for tau >= 0,
+// z^n taken as the filter with its spectrum made per sample by the
+// filter-spectrum passes; the negative lags of two-sided filters are
+// dh(-tau) = conv(R z, dc)(L - 1 - tau), dc taken as the filter. Outputs as
+// bwd_lds_conv: z^{N+1}, ds = (dz^1, dx^1 .. dx^N) and the per-sample dh and dD
+// partials. Returns a status.
 int bwd_fourstep(const hyena_layer* layer, const CacheLayout& cl, const BwdWs& w, char* wb, const float* dskip,
                  int B, bool bf, hipStream_t stream) {
   const int L = layer->L, D = layer->D, N = layer->N, half = D / 2, J = (N + 1) * D;
@@ -314,6 +315,9 @@ int bwd_fourstep(const hyena_layer* layer, const CacheLayout& cl, const BwdWs& w
   float* sbar = reinterpret_cast<float*>(wb + w.sbar);
   float* dd_part = reinterpret_cast<float*>(wb + w.dd_part);
   float* dh_part = reinterpret_cast<float*>(wb + w.dh_part);
+  const bool two = layer->direction == HYENA_NONCAUSAL;
+  const int HL = two ? 2 * L : L;
+  float* dcf = two ? reinterpret_cast<float*>(wb + w.dcf) : nullptr;
   const bool ybf = bf && tuning().y_bf16;
   auto conv = [&](const void* in, int Bc, const float4* p, const void* pb, void* out) {
     hy::FourStepConvArgs a{};
@@ -350,21 +354,32 @@ int bwd_fourstep(const hyena_layer* layer, const CacheLayout& cl, const BwdWs& w
   for (int n = N - 1; n >= 0; --n) {
     const float* zn = zs + (size_t)n * BDL;
     // dx^n = g c^n, staging R(g x^n), sum_t g z^n
-    HY_CHECK_HIP(hy::bwd4_rev_prep(g, wb + w.s, cs + (size_t)n * BDL * es, zn, sbar, tmp, dd_part, B, D, L, N, n, bf,
-                                   stream));
+    HY_CHECK_HIP(hy::bwd4_rev_prep(g, wb + w.s, cs + (size_t)n * BDL * es, zn, sbar, tmp, dcf, dd_part, B, D, L, N,
+                                   n, bf, stream));
     // dz^n = D^n g + R conv_h R(g x^n); dz^1 is block 0 of ds
     HY_CHECK_HIP(conv(tmp, B, pq + n * per_order, pqb + n * per_order * 8, cout));
     float* out = n == 0 ? sbar : gn;
     HY_CHECK_HIP(hy::bwd4_rev_finish(g, cout, dskip + (size_t)n * D, out, n == 0 ? (size_t)J * L : DL, B, D, L, bf,
                                      stream));
     // dh^n of each sample: z^n_b as the filter, R(g x^n)_b as the input
+    // (then, two-sided, (g x^n)_b as the filter, R z^n_b as the input)
+    const float4* pq_t = reinterpret_cast<const float4*>(wb + w.pq_tmp);
     for (int b = 0; b < B; ++b) {
+      char* tb_b = tmp + (size_t)b * 2 * DL * es;
+      float* dh_b = dh_part + ((size_t)b * N + n) * D * HL;
       HY_CHECK_HIP(hy::fourstep_spec(tb, zn + (size_t)b * DL, reinterpret_cast<float2*>(wb + w.Y),
                                      reinterpret_cast<float4*>(wb + w.pq_tmp), wb + w.pqb_tmp, L, D, 1, false,
                                      stream));
-      HY_CHECK_HIP(conv(tmp + (size_t)b * 2 * DL * es, 1, reinterpret_cast<const float4*>(wb + w.pq_tmp),
-                        wb + w.pqb_tmp, cout));
-      HY_CHECK_HIP(hy::bwd4_dh_store(cout, dh_part + ((size_t)b * N + n) * DL, D, L, bf, stream));
+      HY_CHECK_HIP(conv(tb_b, 1, pq_t, wb + w.pqb_tmp, cout));
+      HY_CHECK_HIP(hy::bwd4_dh_store(cout, dh_b, D, L, HL, bf, stream));
+      if (two) {
+        HY_CHECK_HIP(hy::bwd4_stage_rev(zn + (size_t)b * DL, tb_b, D, L, bf, stream));
+        HY_CHECK_HIP(hy::fourstep_spec(tb, dcf + (size_t)b * DL, reinterpret_cast<float2*>(wb + w.Y),
+                                       reinterpret_cast<float4*>(wb + w.pq_tmp), wb + w.pqb_tmp, L, D, 1, false,
+                                       stream));
+        HY_CHECK_HIP(conv(tb_b, 1, pq_t, wb + w.pqb_tmp, cout));
+        HY_CHECK_HIP(hy::bwd4_dh_store_neg(cout, dh_b, D, L, bf, stream));
+      }
     }
     float* t = g;
     g = gn;

@@ -1,13 +1,14 @@
 // Elementwise parts of the 1D backward pass in the four-step regime
-// (2L >= 16384, causal filters). The long convolutions themselves run on the
-// forward's four-step passes: with R the time reversal t -> L - 1 - t on
-// [0, L), the transpose of the causal convolution with h is R conv_h R, and
-// the filter gradient dh(tau) = sum_t dc(t) z(t - tau), tau in [0, L), is
-// conv(R dc, z)(L - 1 - tau): a causal convolution of R dc with z taken as the
-// filter. The kernels here stage the inputs of those convolutions (reversed
-// where needed), apply gates and skips, and read the results back reversed.
-// Rows are L positions long; every access walks a row in order (the reversed
-// ones backwards), so loads and stores stay coalesced.
+// (2L >= 16384). The long convolutions themselves run on the forward's
+// four-step passes: with R the time reversal t -> L - 1 - t on [0, L), the
+// transpose of the convolution with h is R conv_h R, and the filter gradient
+// dh(tau) = sum_t dc(t) z(t - tau) is conv(R dc, z)(L - 1 - tau) for tau in
+// [0, L), a causal convolution of R dc with z taken as the filter (the negative
+// lags of two-sided filters: dh(-tau) = conv(R z, dc)(L - 1 - tau)). The
+// kernels here stage the inputs of those convolutions (reversed where needed),
+// apply gates and skips, and read the results back reversed. Rows are L
+// positions long; every access walks a row in order (the reversed ones
+// backwards), so loads and stores stay coalesced.
 #include "common.h"
 #include "kernels_bwd.h"
 
@@ -70,13 +71,14 @@ __global__ __launch_bounds__(256) void bwd4_to_f32_kernel(const T* __restrict__ 
 }
 
 // One workgroup per row (b, d) of g = dz^{n+1}: dx^n = g c^n into ds block n+1,
-// R(g x^n) into tmp block 0, and sum_t g z^n (a fixed-order tree sum).
+// R(g x^n) into tmp block 0 (and g x^n into dcf, fp32, unless null), and
+// sum_t g z^n (a fixed-order tree sum).
 template <typename T>
 __global__ __launch_bounds__(256) void bwd4_rev_prep_kernel(const float* __restrict__ g, const T* __restrict__ sp,
                                                             const T* __restrict__ c, const float* __restrict__ zf,
                                                             float* __restrict__ sbar, T* __restrict__ tmp,
-                                                            float* __restrict__ dd_part, int D, int L, int NO,
-                                                            int n) {
+                                                            float* __restrict__ dcf, float* __restrict__ dd_part,
+                                                            int D, int L, int NO, int n) {
   __shared__ float sh[256];
   const int row = blockIdx.x, b = row / D, d = row - b * D;
   const size_t J = (size_t)(NO + 1) * D;
@@ -88,10 +90,13 @@ __global__ __launch_bounds__(256) void bwd4_rev_prep_kernel(const float* __restr
   float* dxr = sbar + xrow;
   T* vr = tmp + ((size_t)b * 2 * D + d) * L;
   float acc = 0.f;
+  float* dcr = dcf != nullptr ? dcf + (size_t)row * L : nullptr;
   for (int t = threadIdx.x; t < L; t += 256) {
     const float gv = gr[t];
+    const float dc = gv * ldf(xr + t);
     dxr[t] = gv * ldf(cr + t);
-    stf(vr + (L - 1 - t), gv * ldf(xr + t));
+    stf(vr + (L - 1 - t), dc);
+    if (dcr != nullptr) dcr[t] = dc;
     acc += gv * zr[t];
   }
   sh[threadIdx.x] = acc;
@@ -116,13 +121,38 @@ __global__ __launch_bounds__(256) void bwd4_rev_finish_kernel(const float* __res
   }
 }
 
+// Lags tau in [0, L) of rows of length HL: dh[d][tau] = conv[d][L - 1 - tau].
 template <typename T>
 __global__ __launch_bounds__(256) void bwd4_dh_store_kernel(const T* __restrict__ conv, float* __restrict__ dh, int D,
-                                                            int L) {
+                                                            int L, int HL) {
   const size_t n = (size_t)D * L;
   for (size_t i = (size_t)blockIdx.x * 256 + threadIdx.x; i < n; i += (size_t)gridDim.x * 256) {
     const size_t row = i / L, tau = i - row * L;
-    dh[i] = ldf(conv + row * L + (L - 1 - tau));
+    dh[row * HL + tau] = ldf(conv + row * L + (L - 1 - tau));
+  }
+}
+
+// Lags -(L-1) .. -1 of wrapped two-sided rows [2L] (lag -tau at 2L - tau), from
+// conv = conv(R z, dc): dh[d][j] = conv[d][j - L - 1] for j in (L, 2L), and the
+// entry L, no tap, zero.
+template <typename T>
+__global__ __launch_bounds__(256) void bwd4_dh_store_neg_kernel(const T* __restrict__ conv, float* __restrict__ dh,
+                                                                int D, int L) {
+  const size_t n = (size_t)D * L;
+  for (size_t i = (size_t)blockIdx.x * 256 + threadIdx.x; i < n; i += (size_t)gridDim.x * 256) {
+    const size_t row = i / L, k = i - row * L;  // j = L + k
+    dh[row * 2 * L + L + k] = k == 0 ? 0.f : ldf(conv + row * L + (k - 1));
+  }
+}
+
+// tmp block 0 of one sample = R z (z fp32 [D][L])
+template <typename T>
+__global__ __launch_bounds__(256) void bwd4_stage_rev_kernel(const float* __restrict__ zf, T* __restrict__ tmp, int D,
+                                                             int L) {
+  const size_t n = (size_t)D * L;
+  for (size_t i = (size_t)blockIdx.x * 256 + threadIdx.x; i < n; i += (size_t)gridDim.x * 256) {
+    const size_t row = i / L, t = i - row * L;
+    stf(tmp + row * L + (L - 1 - t), zf[i]);
   }
 }
 
@@ -170,13 +200,13 @@ hipError_t bwd4_to_f32(const void* in, float* out, size_t n, bool bf16, hipStrea
 }
 
 hipError_t bwd4_rev_prep(const float* g, const void* sp, const void* c, const float* zf, float* sbar, void* tmp,
-                         float* dd_part, int B, int D, int L, int NO, int n, bool bf16, hipStream_t s) {
+                         float* dcf, float* dd_part, int B, int D, int L, int NO, int n, bool bf16, hipStream_t s) {
   if (bf16)
     hipLaunchKernelGGL(bwd4_rev_prep_kernel<hy::bf16>, dim3(B * D), dim3(256), 0, s, g, (const hy::bf16*)sp,
-                       (const hy::bf16*)c, zf, sbar, (hy::bf16*)tmp, dd_part, D, L, NO, n);
+                       (const hy::bf16*)c, zf, sbar, (hy::bf16*)tmp, dcf, dd_part, D, L, NO, n);
   else
     hipLaunchKernelGGL(bwd4_rev_prep_kernel<float>, dim3(B * D), dim3(256), 0, s, g, (const float*)sp,
-                       (const float*)c, zf, sbar, (float*)tmp, dd_part, D, L, NO, n);
+                       (const float*)c, zf, sbar, (float*)tmp, dcf, dd_part, D, L, NO, n);
   return hipGetLastError();
 }
 
@@ -192,13 +222,34 @@ hipError_t bwd4_rev_finish(const float* g, const void* conv, const float* dskip_
   return hipGetLastError();
 }
 
-hipError_t bwd4_dh_store(const void* conv, float* dh, int D, int L, bool bf16, hipStream_t s) {
+hipError_t bwd4_dh_store(const void* conv, float* dh, int D, int L, int HL, bool bf16, hipStream_t s) {
   const size_t n = (size_t)D * L;
   if (bf16)
     hipLaunchKernelGGL(bwd4_dh_store_kernel<hy::bf16>, dim3(grid_of(n)), dim3(256), 0, s, (const hy::bf16*)conv, dh,
-                       D, L);
+                       D, L, HL);
   else
-    hipLaunchKernelGGL(bwd4_dh_store_kernel<float>, dim3(grid_of(n)), dim3(256), 0, s, (const float*)conv, dh, D, L);
+    hipLaunchKernelGGL(bwd4_dh_store_kernel<float>, dim3(grid_of(n)), dim3(256), 0, s, (const float*)conv, dh, D, L,
+                       HL);
+  return hipGetLastError();
+}
+
+hipError_t bwd4_dh_store_neg(const void* conv, float* dh, int D, int L, bool bf16, hipStream_t s) {
+  const size_t n = (size_t)D * L;
+  if (bf16)
+    hipLaunchKernelGGL(bwd4_dh_store_neg_kernel<hy::bf16>, dim3(grid_of(n)), dim3(256), 0, s, (const hy::bf16*)conv,
+                       dh, D, L);
+  else
+    hipLaunchKernelGGL(bwd4_dh_store_neg_kernel<float>, dim3(grid_of(n)), dim3(256), 0, s, (const float*)conv, dh, D,
+                       L);
+  return hipGetLastError();
+}
+
+hipError_t bwd4_stage_rev(const float* zf, void* tmp, int D, int L, bool bf16, hipStream_t s) {
+  const size_t n = (size_t)D * L;
+  if (bf16)
+    hipLaunchKernelGGL(bwd4_stage_rev_kernel<hy::bf16>, dim3(grid_of(n)), dim3(256), 0, s, zf, (hy::bf16*)tmp, D, L);
+  else
+    hipLaunchKernelGGL(bwd4_stage_rev_kernel<float>, dim3(grid_of(n)), dim3(256), 0, s, zf, (float*)tmp, D, L);
   return hipGetLastError();
 }
 

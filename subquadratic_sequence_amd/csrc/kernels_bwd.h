@@ -19,13 +19,19 @@ hipError_t bwd4_z_next(const void* sp, const void* c, const float* zf, const flo
 // storage -> fp32 copy of n elements
 hipError_t bwd4_to_f32(const void* in, float* out, size_t n, bool bf16, hipStream_t s);
 // with g = dz^{n+1} (fp32 [B][D][L]): ds block n+1 = g c^n, tmp block 0 =
-// R(g x^n) (storage, R the reversal t -> L - 1 - t), dd_part[b][n][d] = sum_t g z^n
+// R(g x^n) (storage, R the reversal t -> L - 1 - t), dcf = g x^n (fp32, unless
+// null), dd_part[b][n][d] = sum_t g z^n
 hipError_t bwd4_rev_prep(const float* g, const void* sp, const void* c, const float* zf, float* sbar, void* tmp,
-                         float* dd_part, int B, int D, int L, int NO, int n, bool bf16, hipStream_t s);
+                         float* dcf, float* dd_part, int B, int D, int L, int NO, int n, bool bf16, hipStream_t s);
 // out[b][d][t] (row stride ostride) = D^n_d g[b][d][t] + conv[b][d][L - 1 - t]
 hipError_t bwd4_rev_finish(const float* g, const void* conv, const float* dskip_n, float* out, size_t ostride, int B,
                            int D, int L, bool bf16, hipStream_t s);
-// dh[d][tau] = conv[d][L - 1 - tau] (one sample, fp32 out)
-hipError_t bwd4_dh_store(const void* conv, float* dh, int D, int L, bool bf16, hipStream_t s);
+// dh[d][tau] = conv[d][L - 1 - tau], tau < L, rows of HL (one sample, fp32 out)
+hipError_t bwd4_dh_store(const void* conv, float* dh, int D, int L, int HL, bool bf16, hipStream_t s);
+// negative lags of wrapped two-sided rows [2L]: dh[d][j] = conv[d][j - L - 1],
+// L < j < 2L, dh[d][L] = 0
+hipError_t bwd4_dh_store_neg(const void* conv, float* dh, int D, int L, bool bf16, hipStream_t s);
+// one sample's tmp block 0 = R z (z fp32 [D][L])
+hipError_t bwd4_stage_rev(const float* zf, void* tmp, int D, int L, bool bf16, hipStream_t s);
 
 }  // namespace hy

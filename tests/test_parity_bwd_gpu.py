@@ -97,15 +97,17 @@ def test_bwd_sweep(B, L, D, N, dt, causal):
 # Four-step regime (L > 4096, causal filters): the transposed convolution and the
 # filter gradient run on the forward's four-step passes (reversal, one order,
 # unit gates) with per-sample spectra of z^n for dh.
-@pytest.mark.parametrize("B,L,D,N,dt", [
-    (2, 8192, 64, 2, "f32"),       # 256-point rows, two samples' spectra for dh
-    (1, 8192, 64, 3, "f32"),       # three orders
-    (1, 16384, 128, 1, "bf16"),
-    (3, 32768, 64, 2, "bf16"),     # odd batch, 1024-point rows
-    (1, 65536, 64, 2, "bf16"),     # the 64k length, 2048-point rows
+@pytest.mark.parametrize("B,L,D,N,dt,causal", [
+    (2, 8192, 64, 2, "f32", True),       # 256-point rows, two samples' spectra for dh
+    (1, 8192, 64, 3, "f32", True),       # three orders
+    (1, 16384, 128, 1, "bf16", True),
+    (3, 32768, 64, 2, "bf16", True),     # odd batch, 1024-point rows
+    (1, 65536, 64, 2, "bf16", True),     # the 64k length, 2048-point rows
+    (2, 8192, 64, 2, "f32", False),      # two-sided filters: negative lags from a second convolution
+    (1, 16384, 64, 2, "bf16", False),
 ])
-def test_bwd_four_step(B, L, D, N, dt):
-    _check(make_1d(730 + B + L // 1024 + D + N, B, L, D, N=N, K=8, dtype=dt))
+def test_bwd_four_step(B, L, D, N, dt, causal):
+    _check(make_1d(730 + B + L // 1024 + D + N + 5 * causal, B, L, D, N=N, K=8, dtype=dt, causal=causal))
 
 
 def test_bwd_four_step_is_bit_reproducible():
