@@ -611,10 +611,10 @@ int hyena_bwd(const hyena_layer* layer, const void* u, const void* w_in, const f
   char* wb = static_cast<char*>(ws);
   char* cb = static_cast<char*>(layer->cache);
   const int J = (N + 1) * D, HL = dir == HYENA_NONCAUSAL ? 2 * L : L;
-  // forward projections: s (with the short convolution) and p (without), channel-major
+  // forward projections, channel-major: p = u W_in, and s its short convolution
   HY_CHECK_HIP(hy::transpose2d(w_in, wb + w.wt_in, D, J, bf, stream));
-  HY_CHECK_HIP(hy::gemm(hy::GemmArgs{u, wb + w.wt_in, wb + w.s, B * L, J, D, L, false, true, short_w}, bf, stream));
   HY_CHECK_HIP(hy::gemm(hy::GemmArgs{u, wb + w.wt_in, wb + w.p, B * L, J, D, L, false, true, nullptr}, bf, stream));
+  HY_CHECK_HIP(hy::short_conv_rows(wb + w.p, short_w, wb + w.s, B * J, L, J, bf, stream));
   // dz^{N+1} = dy W_out^T, channel-major (W_out as stored is the transposed operand)
   HY_CHECK_HIP(hy::gemm(hy::GemmArgs{dy, w_out, wb + w.gz, B * L, D, D, L, false, true, nullptr}, bf, stream));
   // forward recompute and the orders in reverse

@@ -22,6 +22,8 @@
 // a channel pair's transforms in LDS, as the forward kernel does.
 #include "common.h"
 #include "kernels.h"
+#include "kernels_bwd.h"
+#include "vec8.h"
 
 namespace hy {
 
@@ -249,7 +251,8 @@ __device__ __forceinline__ float block_sum256(float v, float* sh) {
 
 // s_j(t) = sum_k w[j,k] p_j(t - k): dp_j(t) = sum_k w[j,k] ds_j(t + k) (zero past
 // L - 1) and this sample's dw[j,k] = sum_t ds_j(t) p_j(t - k). One workgroup per
-// (sample, column j).
+// (sample, column j); each thread takes 8 consecutive positions per step in
+// 16-byte accesses, the two neighbours past its block from the cache.
 template <typename T>
 __global__ __launch_bounds__(256) void short_conv_bwd_kernel(const float* __restrict__ sbar, const T* __restrict__ p,
                                                              const float* __restrict__ short_w, T* __restrict__ pbar,
@@ -261,14 +264,24 @@ __global__ __launch_bounds__(256) void short_conv_bwd_kernel(const float* __rest
   T* o = pbar + (size_t)row * L;
   const float w0 = short_w[j * 3], w1 = short_w[j * 3 + 1], w2 = short_w[j * 3 + 2];
   float a0 = 0.f, a1 = 0.f, a2 = 0.f;
-  for (int t = threadIdx.x; t < L; t += 256) {
-    const float s0 = s[t];
-    const float s1 = t + 1 < L ? s[t + 1] : 0.f;
-    const float s2 = t + 2 < L ? s[t + 2] : 0.f;
-    stf(o + t, w0 * s0 + w1 * s1 + w2 * s2);
-    a0 += s0 * ldf(pr + t);
-    if (t >= 1) a1 += s0 * ldf(pr + t - 1);
-    if (t >= 2) a2 += s0 * ldf(pr + t - 2);
+  for (int t0 = 8 * (int)threadIdx.x; t0 < L; t0 += 8 * 256) {
+    float sv[8], pv[8], out[8];
+    ld8(s + t0, sv);
+    ld8(pr + t0, pv);
+    const float s8 = t0 + 8 < L ? s[t0 + 8] : 0.f, s9 = t0 + 9 < L ? s[t0 + 9] : 0.f;
+    const float pm1 = t0 >= 1 ? ldf(pr + t0 - 1) : 0.f, pm2 = t0 >= 2 ? ldf(pr + t0 - 2) : 0.f;
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+      const float s1 = k + 1 < 8 ? sv[k + 1] : s8;
+      const float s2 = k + 2 < 8 ? sv[k + 2] : (k + 2 == 8 ? s8 : s9);
+      out[k] = w0 * sv[k] + w1 * s1 + w2 * s2;
+      const float p1 = k >= 1 ? pv[k - 1] : pm1;
+      const float p2 = k >= 2 ? pv[k - 2] : (k == 1 ? pm1 : pm2);
+      a0 += sv[k] * pv[k];
+      a1 += sv[k] * p1;
+      a2 += sv[k] * p2;
+    }
+    st8(o + t0, out);
   }
   a0 = block_sum256(a0, sh);
   a1 = block_sum256(a1, sh);
@@ -277,6 +290,31 @@ __global__ __launch_bounds__(256) void short_conv_bwd_kernel(const float* __rest
     dsw_part[(size_t)row * 3] = a0;
     dsw_part[(size_t)row * 3 + 1] = a1;
     dsw_part[(size_t)row * 3 + 2] = a2;
+  }
+}
+
+// The forward's short convolution from p (channel-major rows of L): s_j(t) =
+// w0 p_j(t) + w1 p_j(t-1) + w2 p_j(t-2), zero history; 8 positions per thread
+// per step. One workgroup per row.
+template <typename T>
+__global__ __launch_bounds__(256) void short_conv_rows_kernel(const T* __restrict__ p,
+                                                              const float* __restrict__ short_w, T* __restrict__ s,
+                                                              int L, int J) {
+  const int row = blockIdx.x, j = row % J;
+  const T* pr = p + (size_t)row * L;
+  T* o = s + (size_t)row * L;
+  const float w0 = short_w[j * 3], w1 = short_w[j * 3 + 1], w2 = short_w[j * 3 + 2];
+  for (int t0 = 8 * (int)threadIdx.x; t0 < L; t0 += 8 * 256) {
+    float pv[8], out[8];
+    ld8(pr + t0, pv);
+    const float pm1 = t0 >= 1 ? ldf(pr + t0 - 1) : 0.f, pm2 = t0 >= 2 ? ldf(pr + t0 - 2) : 0.f;
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+      const float p1 = k >= 1 ? pv[k - 1] : pm1;
+      const float p2 = k >= 2 ? pv[k - 2] : (k == 1 ? pm1 : pm2);
+      out[k] = w0 * pv[k] + w1 * p1 + w2 * p2;
+    }
+    st8(o + t0, out);
   }
 }
 
@@ -462,6 +500,17 @@ hipError_t short_conv_bwd(const float* sbar, const void* p, const float* short_w
   else
     hipLaunchKernelGGL(short_conv_bwd_kernel<float>, dim3(rows), dim3(256), 0, s, sbar, (const float*)p, short_w,
                        (float*)pbar, dsw_part, L, J);
+  return hipGetLastError();
+}
+
+hipError_t short_conv_rows(const void* p, const float* short_w, void* s_out, int rows, int L, int J, bool is_bf16,
+                           hipStream_t s) {
+  if (is_bf16)
+    hipLaunchKernelGGL(short_conv_rows_kernel<bf16>, dim3(rows), dim3(256), 0, s, (const bf16*)p, short_w,
+                       (bf16*)s_out, L, J);
+  else
+    hipLaunchKernelGGL(short_conv_rows_kernel<float>, dim3(rows), dim3(256), 0, s, (const float*)p, short_w,
+                       (float*)s_out, L, J);
   return hipGetLastError();
 }
 

@@ -11,6 +11,7 @@
 // backwards), so loads and stores stay coalesced.
 #include "common.h"
 #include "kernels_bwd.h"
+#include "vec8.h"
 
 namespace hy {
 namespace {
@@ -91,13 +92,24 @@ __global__ __launch_bounds__(256) void bwd4_rev_prep_kernel(const float* __restr
   T* vr = tmp + ((size_t)b * 2 * D + d) * L;
   float acc = 0.f;
   float* dcr = dcf != nullptr ? dcf + (size_t)row * L : nullptr;
-  for (int t = threadIdx.x; t < L; t += 256) {
-    const float gv = gr[t];
-    const float dc = gv * ldf(xr + t);
-    dxr[t] = gv * ldf(cr + t);
-    stf(vr + (L - 1 - t), dc);
-    if (dcr != nullptr) dcr[t] = dc;
-    acc += gv * zr[t];
+  // 8 consecutive positions per thread and step; their reversed images
+  // L - 1 - t are the 8 consecutive positions from L - 8 - t0, in reverse order
+  for (int t0 = 8 * (int)threadIdx.x; t0 < L; t0 += 8 * 256) {
+    float gv[8], xv[8], cv[8], zv[8], dx[8], dc[8], rv[8];
+    ld8(gr + t0, gv);
+    ld8(xr + t0, xv);
+    ld8(cr + t0, cv);
+    ld8(zr + t0, zv);
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+      dx[k] = gv[k] * cv[k];
+      dc[k] = gv[k] * xv[k];
+      rv[7 - k] = dc[k];
+      acc += gv[k] * zv[k];
+    }
+    st8(dxr + t0, dx);
+    st8(vr + (L - 8 - t0), rv);
+    if (dcr != nullptr) st8(dcr + t0, dc);
   }
   sh[threadIdx.x] = acc;
   __syncthreads();

@@ -1,4 +1,5 @@
-// Launchers of the elementwise kernels of the four-step backward (bwd4.hip).
+// Launchers of elementwise kernels of the backward pass (bwd4.hip: the
+// four-step regime; short_conv_rows: bwd.hip).
 // Layouts: rows of L positions; s [B][(NO+1)D][L] and ds [B][(NO+1)D][L] in the
 // block order (v, x^1 .. x^NO); the staging buffer tmp [B][2D][L] holds a
 // convolution input in block 0 and ones in block 1. T is the storage type.
@@ -7,6 +8,11 @@
 
 namespace hy {
 
+// The forward's causal length-3 short convolution of channel-major rows p
+// [rows][L] (row r is column j = r mod J of W_in's blocks): s = w0 p_t + w1
+// p_{t-1} + w2 p_{t-2}, zero history (bwd.hip)
+hipError_t short_conv_rows(const void* p, const float* short_w, void* s_out, int rows, int L, int J, bool bf16,
+                           hipStream_t s);
 // p[r * stride + i] = v for r < rows, i < len (fp32 or bf16 elements)
 hipError_t bwd4_fill(void* p, float v, int rows, size_t len, size_t stride, bool bf16, hipStream_t s);
 // z^1 = v block of s: zf [B][D][L] fp32 and tmp block 0 (storage type)
