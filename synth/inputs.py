@@ -265,6 +265,8 @@ TEST_SHAPES = {
                                            u_scale=1 / 8.0, causal=False),
     "order2_bf16_L1M_D64_dna": dict(kind="1d", seed=38, B=1, L=1 << 20, D=64, N=2, K=16, dtype="bf16", tokens=4),
     "nd3d_f32_B2_C64_64cube": dict(kind="nd", seed=39, B=2, X=64, Y=64, Z=64, C=64, N=2, u_mean_spread=0.5),
+    # a lone sample: the packed field's second half is empty
+    "nd3d_f32_B1_C64_64cube": dict(kind="nd", seed=42, B=1, X=64, Y=64, Z=64, C=64, N=2, u_mean_spread=0.5),
     "nd3d_film_f32_B1_C64_64cube": dict(kind="nd_film", seed=40, B=1, X=64, Y=64, Z=64, C=64, N=2, W=64, R=4),
     "nd3d_film_f32_B2_C64_64cube": dict(kind="nd_film", seed=41, B=2, X=64, Y=64, Z=64, C=64, N=2, W=64, R=4),
 }

@@ -45,7 +45,7 @@ def test_full_length_1d_every_output(name):
     assert err <= TOL[inp.dtype], err
 
 
-@pytest.mark.parametrize("name", ["nd3d_f32_B2_C64_64cube", "nd3d_circ_f32_B1_C64_128cube"])
+@pytest.mark.parametrize("name", ["nd3d_f32_B2_C64_64cube", "nd3d_f32_B1_C64_64cube", "nd3d_circ_f32_B1_C64_128cube"])
 def test_full_grid_nd_every_output(name):
     import oracle
     inp = make_config(name)
