@@ -916,6 +916,143 @@ __global__ __launch_bounds__(512) void nd_pencil128_kernel(NdConvArgs a, int nit
   }
 }
 
+// Persistent pencil pass for 2X = 2Z = 128 with mirrored pencil blocks in one
+// item. The kernel spectrum is kept for kz <= Z only; a pencil with kz > Z
+// uses the conjugates of the entries of its mirror image (-ky, MZ - kz). An
+// item is the block pair A = (ky, kz < 64) and B = (MY - ky, kz >= 64) of one
+// (sample pair, channel): pencil kz in [1, 63] of A and pencil 128 - kz of B
+// are mirror images, so A reads their spectrum entries once and leaves them in
+// LDS for B (B's entry at kx is A's at -kx, conjugated; B's kz = 64 pencil,
+// which lies on the kept plane, reads its own). The workgroup runs A, then B,
+// each with the decomposition of nd_pencil128_kernel; every block's inputs are
+// fetched while the block before it runs.
+__global__ __launch_bounds__(512) void nd_pencil128p_kernel(NdConvArgs a, int nitems) {
+  constexpr int N1 = 128, RA = 16, RB = 8;
+  extern __shared__ float4 smem4[];
+  float2* S = reinterpret_cast<float2*>(smem4);  // [RA][RB][64] forward, [RB][RA][64] inverse
+  float2* KA = S + RA * RB * 64;                  // A's spectrum entries [kx][lane], read by B
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const int X = a.X, MY = a.MY;
+  constexpr int MZ = 128, ZH = 65;
+  const size_t plane = (size_t)MY * MZ;
+  struct Blk {
+    float2* base;      // Yint of (pair, channel), plane 0
+    const float2* Kr;  // kept entries read by this lane: row (kx = 0, ky or B's row, kz)
+    int f;             // this lane's pencil (ky, kz) = (f / MZ, f % MZ)
+  };
+  // block q of this workgroup's sequence: item blockIdx.x + (q / 2) gridDim.x, A for even q
+  auto blk_of = [&](int item, bool isB) {
+    Blk bk;
+    const int ky = item % MY, pc = item / MY;  // pc = bp * C + c
+    const int c = pc % a.C;
+    const int kyb = (MY - ky) % MY;
+    bk.base = a.Yint + (size_t)pc * X * plane;
+    // every lane of B reads the kz = 64 column (only its lane 0 uses it), so
+    // that the loads stay unconditional
+    bk.Kr = a.kh + (size_t)(a.n * a.C + c) * N1 * MY * ZH + (size_t)(isB ? kyb : ky) * ZH + (isB ? 64 : lane);
+    bk.f = isB ? kyb * MZ + 64 + lane : ky * MZ + lane;
+    return bk;
+  };
+  struct In {
+    float2 y[2][RB / 2];  // x = j + 16 r, j in {w, w + 8}, r < 4 (x < X = 64)
+    float2 k[RA];         // kept entries at kx = w + 8 kb
+  };
+  auto load_y = [&](const Blk& bk, In& in) {
+#pragma unroll
+    for (int jj = 0; jj < 2; ++jj)
+#pragma unroll
+      for (int r = 0; r < RB / 2; ++r) in.y[jj][r] = bk.base[(size_t)(w + 8 * jj + RA * r) * plane + bk.f];
+  };
+  auto load_k = [&](const Blk& bk, In& in) {
+#pragma unroll
+    for (int kb = 0; kb < RA; ++kb) in.k[kb] = bk.Kr[(size_t)(w + RB * kb) * MY * ZH];
+  };
+
+  // one block; nb: the block after it (itself for the last one)
+  auto run = [&](auto isBc, const Blk& bk, const Blk& nb, In& in) {
+    constexpr bool isB = decltype(isBc)::value;
+    // forward stage 1: DFT-8 over r of j = w and w + 8, inner twiddles W_128^(j ka)
+    float2 v[2][RB];
+#pragma unroll
+    for (int jj = 0; jj < 2; ++jj)
+#pragma unroll
+      for (int r = 0; r < RB; ++r) v[jj][r] = r < RB / 2 ? in.y[jj][r] : make_float2(0.f, 0.f);
+    load_y(nb, in);
+#pragma unroll
+    for (int jj = 0; jj < 2; ++jj) {
+      const int j = w + 8 * jj;
+      Dft<RB, false>::run(v[jj]);
+#pragma unroll
+      for (int ka = 0; ka < RB; ++ka) {
+        if (ka) v[jj][ka] = cmul(v[jj][ka], a.tw128[(j * ka) & 127]);
+        S[(j * RB + ka) * 64 + lane] = v[jj][ka];
+      }
+    }
+    __syncthreads();
+    // stage 2: DFT-16 over j for ka = w: X[w + 8 kb]
+    float2 u[RA];
+#pragma unroll
+    for (int j = 0; j < RA; ++j) u[j] = S[(j * RB + w) * 64 + lane];
+    Dft<RA, false>::run(u);
+    if constexpr (!isB) {
+#pragma unroll
+      for (int kb = 0; kb < RA; ++kb) {
+        KA[(w + RB * kb) * 64 + lane] = in.k[kb];
+        u[kb] = cmul(u[kb], in.k[kb]);
+      }
+    } else {
+      // pencil 64 + lane of B mirrors pencil 64 - lane of A
+#pragma unroll
+      for (int kb = 0; kb < RA; ++kb) {
+        const int kxm = (N1 - (w + RB * kb)) & (N1 - 1);
+        const float2 km = conjf2(KA[kxm * 64 + ((64 - lane) & 63)]);
+        u[kb] = cmul(u[kb], lane ? km : in.k[kb]);
+      }
+    }
+    load_k(nb, in);
+    // inverse stage 2 on the same threads, then the inner twiddles
+    Dft<RA, true>::run(u);
+#pragma unroll
+    for (int na = 1; na < RA; ++na) u[na] = cmulc(u[na], a.tw128[(w * na) & 127]);
+    __syncthreads();  // everyone finished reading S (and, after B, KA)
+#pragma unroll
+    for (int na = 0; na < RA; ++na) S[(w * RA + na) * 64 + lane] = u[na];
+    __syncthreads();
+    // inverse stage 1: DFT-8 over ka for na = w and w + 8 -> x = na + 16 nb, nb < 4
+#pragma unroll
+    for (int jj = 0; jj < 2; ++jj) {
+      const int na = w + 8 * jj;
+      float2 q[RB];
+#pragma unroll
+      for (int ka = 0; ka < RB; ++ka) q[ka] = S[(ka * RA + na) * 64 + lane];
+      Dft<RB, true>::run(q);
+#pragma unroll
+      for (int nb2 = 0; nb2 < RB / 2; ++nb2) bk.base[(size_t)(na + RA * nb2) * plane + bk.f] = q[nb2];
+    }
+    __syncthreads();  // S fully read before the next block writes it
+  };
+
+  using TA = std::integral_constant<bool, false>;
+  using TB = std::integral_constant<bool, true>;
+  int item = blockIdx.x;
+  if (item >= nitems) return;
+  In in;
+  {
+    const Blk bk = blk_of(item, false);
+    load_y(bk, in);
+    load_k(bk, in);
+  }
+  while (true) {
+    const int next = item + gridDim.x;
+    const bool more = next < nitems;
+    const Blk ba = blk_of(item, false), bb = blk_of(item, true);
+    run(TA{}, ba, bb, in);
+    run(TB{}, bb, blk_of(more ? next : item, !more), in);
+    if (!more) break;
+    item = next;
+  }
+}
+
 // ========================================================= channel mean
 __global__ __launch_bounds__(256) void nd_mean_partial_kernel(const float* __restrict__ u, float* __restrict__ part,
                                                               int C, int V, int chunk) {
@@ -1541,6 +1678,25 @@ static hipError_t launch_plane128(const NdConvArgs& a, int nitems, hipStream_t s
   return hipGetLastError();
 }
 
+static hipError_t launch_pencil128p(const NdConvArgs& a, int nitems, hipStream_t s) {
+  const size_t lds = (size_t)2 * 16 * 8 * 64 * 8;  // exchange buffer + A's spectrum entries
+  auto fn = nd_pencil128p_kernel;
+  hipError_t e = nd_allow_lds((const void*)fn, lds);
+  if (e != hipSuccess) return e;
+  static DeviceCache grid_cache;
+  const int grid = grid_cache.get([&] {
+    int cus = 0, dev = 0, per_cu = 0;
+    if (hipGetDevice(&dev) != hipSuccess ||
+        hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0)
+      cus = 256;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, (const void*)fn, 512, lds) != hipSuccess || per_cu <= 0)
+      per_cu = 1;
+    return cus * per_cu;
+  });
+  hipLaunchKernelGGL(fn, dim3(grid < nitems ? grid : nitems), dim3(512), lds, s, a, nitems);
+  return hipGetLastError();
+}
+
 static hipError_t launch_pencil128(const NdConvArgs& a, int nitems, hipStream_t s) {
   const size_t lds = (size_t)16 * 8 * 64 * 8;
   auto fn = nd_pencil128_kernel;
@@ -1614,6 +1770,8 @@ hipError_t nd_conv(const NdConvArgs& in, hipStream_t s) {
     a.n = n;
     if (a.kh_stride != 0) {
       e = a.MX == a.X ? launch_pencil_pq_p<1>(a, s) : launch_pencil_pq_p<2>(a, s);
+    } else if (a.MX == 128 && a.MX == 2 * a.X && a.MZ == 128 && a.MZ == 2 * a.Z) {
+      e = launch_pencil128p(a, a.MY * a.C * BP, s);
     } else if (a.MX == 128 && a.MX == 2 * a.X) {
       e = launch_pencil128(a, (int)(nf * a.C * BP), s);
     } else {

@@ -179,6 +179,8 @@ def test_nd_filter_spectra_are_bit_reproducible(X, Y, circ):
     (1, 8, 4, 16, 64, 2, False),     # odd batch, 8 x 32 planes
     (3, 16, 64, 8, 64, 1, False),    # 128 x 16 planes
     (1, 64, 32, 16, 64, 1, False),   # 128-point x transforms (the persistent pencil pass)
+    (1, 64, 16, 64, 64, 1, False),   # 128-point x and z: mirrored pencil blocks in one item, 32-point y
+    (3, 64, 8, 64, 64, 2, False),    # the same with an odd batch (second packed field half empty)
     (2, 8, 16, 32, 64, 2, True),     # circular: 16 x 32 planes
     (2, 16, 8, 64, 128, 2, True),
     (1, 8, 128, 16, 64, 1, True),    # circular 128 x 16 planes
