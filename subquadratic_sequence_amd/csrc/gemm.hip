@@ -56,14 +56,18 @@ template <int TN> struct WaveCfg {
   static constexpr int MI = WR / 32;          // 32-row accumulator blocks per wave
 };
 
-constexpr int kCsLd = GBM + 4;  // staging row (floats), channel-major output: [64 n][256 m]
-constexpr int kRmLd = 64 + 4;   // staging row (floats), row-major output: [256 m][64 n]
+constexpr int kCsLd = GBM + 4;  // staging row (floats), channel-major output: [RN n][256 m]
 constexpr int kBufs = 3;                                 // LDS tile buffers
-constexpr size_t kStageBytes = 64 * kCsLd * 4 > 256 * kRmLd * 4 ? 64 * kCsLd * 4 : 256 * kRmLd * 4;
+// staging of one epilogue round: RN = 128 columns (64 for 64-wide tiles) as
+// [RN][kCsLd] (channel-major output) or [256][RN + 4] (row-major output)
+constexpr size_t stage_bytes(int TN) {
+  return TN >= 128 ? (128 * kCsLd * 4 > 256 * 132 * 4 ? 128 * kCsLd * 4 : 256 * 132 * 4)
+                   : (64 * kCsLd * 4 > 256 * 68 * 4 ? 64 * kCsLd * 4 : 256 * 68 * 4);
+}
 // A (GBM rows) and B (TN rows) tiles per buffer, 80-byte rows; the epilogue
 // staging reuses the space; then the short-conv taps of the tile's columns
 constexpr size_t gemm_main_bytes(int TN) {
-  return (size_t)kBufs * (GBM + TN) * 80 > kStageBytes ? (size_t)kBufs * (GBM + TN) * 80 : kStageBytes;
+  return (size_t)kBufs * (GBM + TN) * 80 > stage_bytes(TN) ? (size_t)kBufs * (GBM + TN) * 80 : stage_bytes(TN);
 }
 constexpr size_t gemm_lds_bytes(int TN) { return gemm_main_bytes(TN) + (size_t)TN * 3 * 4; }
 
@@ -104,7 +108,11 @@ __global__ __launch_bounds__(512, TN == 64 ? 4 : 1) void gemm_kernel(const T* __
     C += (size_t)y * sc;
   }
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int wm = wave / WC::WCOLS, wn = wave % WC::WCOLS;  // waves of WR x 64
+  // waves of WR x 64; consecutive waves (which sit on different SIMDs) take
+  // consecutive wave rows first, so that the waves staging one epilogue round
+  // are spread over the four SIMDs
+  constexpr int WROWS = 8 / WC::WCOLS;
+  const int wm = wave % WROWS, wn = wave / WROWS;
   const int tile = xcd_tile(blockIdx.x, ntiles);
   const int tm = tile / ntn, tn = tile - tm * ntn;
   const int n0 = tn * TN;
@@ -304,12 +312,31 @@ __global__ __launch_bounds__(512, TN == 64 ? 4 : 1) void gemm_kernel(const T* __
 
   // Epilogue. Accumulator element e of lane l in block (i, j):
   //   row = i*32 + (e/4)*8 + (l/32)*4 + e%4, col = j*32 + l%32 (within the wave tile).
-  // One round per 64-column slice (the waves with wn == h hold it); the slice
-  // is staged in LDS as fp32 and written with 16-byte stores.
+  // One round per RN-column slice (the waves whose 64 columns lie in it stage
+  // them in LDS as fp32); the slice is written with 16-byte stores.
+  constexpr int HC = WC::WCOLS < 2 ? WC::WCOLS : 2;  // wave columns per round
+  constexpr int RN = HC * 64;                         // columns per round
+  constexpr int RLD = RN + 4;                         // staging row (floats), row-major output
   float* Cs = reinterpret_cast<float*>(smem);
+  // channel-major output: every thread keeps one chunk of 8 consecutive m for
+  // the whole epilogue (only its n varies), so its sequence and position are
+  // computed once; with the short convolution the first chunk of every row
+  // (the 8 overlap rows) is not written
+  const int mc = (tid & 31) * 8;
+  const int mg = m0 + mc;
+  const bool m_ok = mg >= 0 && mg < M && (!SC || mc >= 8);
+  size_t cbase = 0;
+  int tq = 0;
+  if (C_CM) {
+    const int mm = m_ok ? mg : 0;
+    const int bq = mm / Lseq;
+    tq = mm - bq * Lseq;
+    cbase = (size_t)bq * N * Lseq + tq;
+  }
 #pragma unroll
-  for (int h = 0; h < WC::WCOLS; ++h) {
-    if (wn == h) {
+  for (int h = 0; h < WC::WCOLS / HC; ++h) {
+    if (wn / HC == h) {
+      const int nb = (wn % HC) * 64;
 #pragma unroll
       for (int i = 0; i < MI; ++i)
 #pragma unroll
@@ -317,7 +344,7 @@ __global__ __launch_bounds__(512, TN == 64 ? 4 : 1) void gemm_kernel(const T* __
 #pragma unroll
           for (int e4 = 0; e4 < 4; ++e4) {
             const int ml = wm * WC::WR + i * 32 + e4 * 8 + (lane >> 5) * 4;
-            const int nl = j * 32 + (lane & 31);
+            const int nl = nb + j * 32 + (lane & 31);
             const float4 q = make_float4(acc[i][j][4 * e4], acc[i][j][4 * e4 + 1], acc[i][j][4 * e4 + 2],
                                          acc[i][j][4 * e4 + 3]);
             if (C_CM) {
@@ -325,32 +352,33 @@ __global__ __launch_bounds__(512, TN == 64 ? 4 : 1) void gemm_kernel(const T* __
               *reinterpret_cast<float4*>(Cs + nl * kCsLd + ml) = q;
             } else {
               // [m][n]
-              Cs[(ml + 0) * kRmLd + nl] = q.x;
-              Cs[(ml + 1) * kRmLd + nl] = q.y;
-              Cs[(ml + 2) * kRmLd + nl] = q.z;
-              Cs[(ml + 3) * kRmLd + nl] = q.w;
+              Cs[(ml + 0) * RLD + nl] = q.x;
+              Cs[(ml + 1) * RLD + nl] = q.y;
+              Cs[(ml + 2) * RLD + nl] = q.z;
+              Cs[(ml + 3) * RLD + nl] = q.w;
             }
           }
     }
     __syncthreads();
     if (C_CM) {
-      // 64 rows (n) x 256 (m) in chunks of 8 consecutive m; with SC the first
-      // chunk of every row (the 8 overlap rows) is not written
-      for (int c = tid; c < 64 * 32; c += 512) {
-        const int nl = c >> 5, mc = (c & 31) * 8;
-        const int n = n0 + h * 64 + nl, m = m0 + mc;
-        if (n < N && m >= 0 && m < M && (!SC || mc >= 8)) {
-          const int b = m / Lseq, t = m - b * Lseq;
-          T* dst = C + ((size_t)b * N + n) * Lseq + t;
+      // RN rows (n) x 256 (m): 16 rows per pass of the workgroup
+#pragma unroll
+      for (int it = 0; it < RN / 16; ++it) {
+        const int nl = (tid >> 5) + it * 16;
+        const int n = n0 + h * RN + nl;
+        if (m_ok && n < N) {
+          T* dst = C + cbase + (size_t)n * Lseq;
           const float* src = Cs + nl * kCsLd + mc;
           const float4 s0 = *reinterpret_cast<const float4*>(src);
           const float4 s1 = *reinterpret_cast<const float4*>(src + 4);
           float o[8] = {s0.x, s0.y, s0.z, s0.w, s1.x, s1.y, s1.z, s1.w};
           if (SC) {
+            // mc >= 8 here, so the two previous rows are in the staged row;
+            // chunks start on multiples of 8, so only tq == 0 starts a sequence
             const float* wn3 = sw + 3 * (n - n0);
             const float w0 = wn3[0], w1 = wn3[1], w2 = wn3[2];
-            const float pm1 = (t >= 1) ? src[-1] : 0.f, pm2 = (t >= 2) ? src[-2] : 0.f;
-            float prev1 = pm1, prev2 = pm2;
+            const float r1 = src[-1], r2 = src[-2];
+            float prev1 = tq ? r1 : 0.f, prev2 = tq ? r2 : 0.f;
 #pragma unroll
             for (int v = 0; v < 8; ++v) {
               const float cur = o[v];
@@ -371,12 +399,15 @@ __global__ __launch_bounds__(512, TN == 64 ? 4 : 1) void gemm_kernel(const T* __
         }
       }
     } else {
-      // 256 rows (m) x 64 (n) in chunks of 8 consecutive n
-      for (int c = tid; c < 256 * 8; c += 512) {
-        const int ml = c >> 3, nc = (c & 7) * 8;
-        const int m = m0 + ml, n = n0 + h * 64 + nc;
+      // 256 rows (m) x RN (n) in chunks of 8 consecutive n
+      constexpr int CPR = RN / 8;  // chunks per row
+#pragma unroll
+      for (int it = 0; it < 256 * CPR / 512; ++it) {
+        const int c = tid + it * 512;
+        const int ml = c / CPR, nc = (c % CPR) * 8;
+        const int m = m0 + ml, n = n0 + h * RN + nc;
         if (m >= 0 && m < M && n < N) {
-          const float* src = Cs + ml * kRmLd + nc;
+          const float* src = Cs + ml * RLD + nc;
           const float4 s0 = *reinterpret_cast<const float4*>(src);
           const float4 s1 = *reinterpret_cast<const float4*>(src + 4);
           T* dst = C + (size_t)m * N + n;
