@@ -221,9 +221,11 @@ BwdWs bwd_ws(int B, int L, int D, int N, int dtype, int dir) {
   take(w.zfin, BDL * es);
   take(w.sbar, BJL * 4);
   take(w.pbar, BJL * es);
-  take(w.dh_part, (size_t)B * N * D * HL * 4);
-  take(w.dd_part, (size_t)B * N * D * 4);
-  take(w.dsw_part, (size_t)B * J * 3 * 4);
+  // per-sample partial results (with one sample the outputs take them)
+  const size_t parts = B == 1 ? 0 : (size_t)B;
+  take(w.dh_part, parts * N * D * HL * 4);
+  take(w.dd_part, parts * N * D * 4);
+  take(w.dsw_part, parts * J * 3 * 4);
   take(w.dyT, BDL * es);
   take(w.uT, BDL * es);
   take(w.dwo_part, (size_t)B * bwd_split_out(B, L, D, dtype) * D * D * es);
@@ -300,7 +302,7 @@ bool filter_bwd_params_ok(int K, int W) { return K >= 1 && K <= 32 && W >= 16 &&
 // bwd_lds_conv: z^{N+1}, ds = (dz^1, dx^1 .. dx^N) and the per-sample dh and dD
 // partials. Returns a status.
 int bwd_fourstep(const hyena_layer* layer, const CacheLayout& cl, const BwdWs& w, char* wb, const float* dskip,
-                 int B, bool bf, hipStream_t stream) {
+                 float* dh_part, float* dd_part, int B, bool bf, hipStream_t stream) {
   const int L = layer->L, D = layer->D, N = layer->N, half = D / 2, J = (N + 1) * D;
   const size_t es = bf ? 2 : 4, DL = (size_t)D * L, BDL = (size_t)B * DL;
   char* cb = static_cast<char*>(layer->cache);
@@ -313,8 +315,6 @@ int bwd_fourstep(const hyena_layer* layer, const CacheLayout& cl, const BwdWs& w
   float* zs = reinterpret_cast<float*>(wb + w.zsave);  // z^1 .. z^N, fp32
   char* cs = wb + w.csave;                              // c^1 .. c^N, storage type
   float* sbar = reinterpret_cast<float*>(wb + w.sbar);
-  float* dd_part = reinterpret_cast<float*>(wb + w.dd_part);
-  float* dh_part = reinterpret_cast<float*>(wb + w.dh_part);
   const bool two = layer->direction == HYENA_NONCAUSAL;
   const int HL = two ? 2 * L : L;
   float* dcf = two ? reinterpret_cast<float*>(wb + w.dcf) : nullptr;
@@ -619,10 +619,14 @@ int hyena_bwd(const hyena_layer* layer, const void* u, const void* w_in, const f
   HY_CHECK_HIP(hy::gemm(hy::GemmArgs{dy, w_out, wb + w.gz, B * L, D, D, L, false, true, nullptr}, bf, stream));
   // forward recompute and the orders in reverse
   float* sbar = reinterpret_cast<float*>(wb + w.sbar);
-  float* dh_part = reinterpret_cast<float*>(wb + w.dh_part);
-  float* dd_part = reinterpret_cast<float*>(wb + w.dd_part);
+  // per-sample partial results, summed over the batch at the end; with one
+  // sample they are written to the outputs directly
+  const bool one = B == 1;
+  float* dh_part = one ? dh : reinterpret_cast<float*>(wb + w.dh_part);
+  float* dd_part = one ? ddskip : reinterpret_cast<float*>(wb + w.dd_part);
+  float* dsw_part = one ? dshort_w : reinterpret_cast<float*>(wb + w.dsw_part);
   if (!cl.lds) {
-    const int st = bwd_fourstep(layer, cl, w, wb, dskip, B, bf, stream);
+    const int st = bwd_fourstep(layer, cl, w, wb, dskip, dh_part, dd_part, B, bf, stream);
     if (st != HYENA_OK) return st;
   } else {
     hy::BwdConvArgs a{};
@@ -645,8 +649,7 @@ int hyena_bwd(const hyena_layer* layer, const void* u, const void* w_in, const f
     HY_CHECK_HIP(hy::bwd_lds_conv(a, bf, stream));
   }
   // short convolution transpose: dp, and per-sample tap gradients
-  HY_CHECK_HIP(hy::short_conv_bwd(sbar, wb + w.p, short_w, wb + w.pbar, reinterpret_cast<float*>(wb + w.dsw_part),
-                                  B * J, L, J, bf, stream));
+  HY_CHECK_HIP(hy::short_conv_bwd(sbar, wb + w.p, short_w, wb + w.pbar, dsw_part, B * J, L, J, bf, stream));
   // du = dp W_in^T (dp channel-major; W_in as stored is the transposed operand)
   HY_CHECK_HIP(hy::gemm(hy::GemmArgs{wb + w.pbar, w_in, du, B * L, D, J, L, true, false, nullptr}, bf, stream));
   // weight gradients dW_out = sum_b z^{N+1}_b dy_b and dW_in = sum_b u_b^T dp_b
@@ -675,9 +678,11 @@ int hyena_bwd(const hyena_layer* layer, const void* u, const void* w_in, const f
   // sums over the batch, in a fixed order
   HY_CHECK_HIP(hy::sum_rows(wb + w.dwo_part, dw_out, B * so, (size_t)D * D, (size_t)D * D, bf, stream));
   HY_CHECK_HIP(hy::sum_rows(wb + w.dwi_part, dw_in, B * si, (size_t)D * J, (size_t)D * J, bf, stream));
-  HY_CHECK_HIP(hy::sum_rows(dh_part, dh, B, (size_t)N * D * HL, (size_t)N * D * HL, false, stream));
-  HY_CHECK_HIP(hy::sum_rows(dd_part, ddskip, B, (size_t)N * D, (size_t)N * D, false, stream));
-  HY_CHECK_HIP(hy::sum_rows(wb + w.dsw_part, dshort_w, B, (size_t)J * 3, (size_t)J * 3, false, stream));
+  if (!one) {
+    HY_CHECK_HIP(hy::sum_rows(dh_part, dh, B, (size_t)N * D * HL, (size_t)N * D * HL, false, stream));
+    HY_CHECK_HIP(hy::sum_rows(dd_part, ddskip, B, (size_t)N * D, (size_t)N * D, false, stream));
+    HY_CHECK_HIP(hy::sum_rows(dsw_part, dshort_w, B, (size_t)J * 3, (size_t)J * 3, false, stream));
+  }
   return HYENA_OK;
 }
 

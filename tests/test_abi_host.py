@@ -331,8 +331,9 @@ def test_bwd_validation_before_any_hip_call(hy):
     assert hy.hyena_bwd_workspace_bytes(1, 8192, 64, 2, 0, 1) > hy.hyena_bwd_workspace_bytes(1, 8192, 64, 2, 0, 0)
     assert hy.hyena_bwd_workspace_bytes(1, 16, 64, 2, 0, 0) == 0
     assert hy.hyena_bwd_workspace_bytes(1, 1024, 64, 2, 0, 9) == 0
-    # two-sided filters need the wrapped 2L gradient rows
-    assert hy.hyena_bwd_workspace_bytes(1, 1024, 64, 2, 0, 1) > hy.hyena_bwd_workspace_bytes(1, 1024, 64, 2, 0, 0)
+    # two-sided filters have 2L taps: a larger per-sample filter-gradient partial
+    # (with one sample the gradient is written to dh directly, so B = 2 here)
+    assert hy.hyena_bwd_workspace_bytes(2, 1024, 64, 2, 0, 1) > hy.hyena_bwd_workspace_bytes(2, 1024, 64, 2, 0, 0)
     layer = hy.Layer()
     assert L.hyena_layer_init(ctypes.byref(layer), 1024, 64, 2, p, 1 << 30) == 0
     need = hy.hyena_bwd_workspace_bytes(1, 1024, 64, 2, 0, 0)
