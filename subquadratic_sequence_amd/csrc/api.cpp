@@ -195,7 +195,7 @@ int bwd_split_in(int B, int L, int D, int N, int dtype) {
 }
 
 struct BwdWs {
-  size_t wt_in, s, p, gz, zsave, csave, zfin, sbar, pbar, dh_part, dd_part, dsw_part, dyT, uT, dwo_part, dwi_part;
+  size_t wt_in, s, p, gz, zsave, csave, zfin, sbar, pbar, dh_part, dd_part, dsw_part, dwo_part, dwi_part;
   // four-step regime: convolution staging and output, the passes' intermediate,
   // dz ping-pong (fp32), one sample's z (or dc) spectrum (fp32 and bf16), zero
   // skips; two-sided filters: g x^n in fp32
@@ -226,8 +226,6 @@ BwdWs bwd_ws(int B, int L, int D, int N, int dtype, int dir) {
   take(w.dh_part, parts * N * D * HL * 4);
   take(w.dd_part, parts * N * D * 4);
   take(w.dsw_part, parts * J * 3 * 4);
-  take(w.dyT, BDL * es);
-  take(w.uT, BDL * es);
   take(w.dwo_part, (size_t)B * bwd_split_out(B, L, D, dtype) * D * D * es);
   take(w.dwi_part, (size_t)B * bwd_split_in(B, L, D, N, dtype) * D * J * es);
   if (L > kLdsMaxL) {
@@ -654,26 +652,31 @@ int hyena_bwd(const hyena_layer* layer, const void* u, const void* w_in, const f
   HY_CHECK_HIP(hy::gemm(hy::GemmArgs{wb + w.pbar, w_in, du, B * L, D, J, L, true, false, nullptr}, bf, stream));
   // weight gradients dW_out = sum_b z^{N+1}_b dy_b and dW_in = sum_b u_b^T dp_b
   // (K = L): one launch per product over the samples and K splits, the
-  // partial results summed below
-  HY_CHECK_HIP(hy::transpose2d(dy, wb + w.dyT, L, D, bf, stream, B));
-  HY_CHECK_HIP(hy::transpose2d(u, wb + w.uT, L, D, bf, stream, B));
+  // partial results summed below. dy and u are read as stored, [L][D], by the
+  // GEMM's channel-major A path (K = positions, M = the D channels of a row):
+  // dW_out is formed as dy^T z^{N+1} and written transposed (channel-major
+  // output), dW_in as u^T dp with dp channel-major as the transposed operand.
   const int so = bwd_split_out(B, L, D, dtype), si = bwd_split_in(B, L, D, N, dtype);
-  hy::GemmArgs go{wb + w.zfin, wb + w.dyT, wb + w.dwo_part, D, D, L / so, L, false, false, nullptr};
+  hy::GemmArgs go{dy, wb + w.zfin, wb + w.dwo_part, D, D, L / so, D, true, true, nullptr};
   go.batch = B;
   go.nsplit = so;
   go.sa = go.sb = (size_t)D * L;
   go.sc = (size_t)D * D;
-  go.ka = go.kb = (size_t)(L / so);
-  go.lda = go.ldb = L;
+  go.ka = (size_t)(L / so) * D;
+  go.kb = (size_t)(L / so);
+  go.lda = L / so;
+  go.ldb = L;
   HY_CHECK_HIP(hy::gemm(go, bf, stream));
-  hy::GemmArgs gw{wb + w.uT, wb + w.pbar, wb + w.dwi_part, D, J, L / si, L, false, false, nullptr};
+  hy::GemmArgs gw{u, wb + w.pbar, wb + w.dwi_part, D, J, L / si, D, true, false, nullptr};
   gw.batch = B;
   gw.nsplit = si;
   gw.sa = (size_t)D * L;
   gw.sb = (size_t)J * L;
   gw.sc = (size_t)D * J;
-  gw.ka = gw.kb = (size_t)(L / si);
-  gw.lda = gw.ldb = L;
+  gw.ka = (size_t)(L / si) * D;
+  gw.kb = (size_t)(L / si);
+  gw.lda = L / si;
+  gw.ldb = L;
   HY_CHECK_HIP(hy::gemm(gw, bf, stream));
   // sums over the batch, in a fixed order
   HY_CHECK_HIP(hy::sum_rows(wb + w.dwo_part, dw_out, B * so, (size_t)D * D, (size_t)D * D, bf, stream));
