@@ -362,19 +362,21 @@ int bwd_fourstep(const hyena_layer* layer, const CacheLayout& cl, const BwdWs& w
     // dh^n of each sample: z^n_b as the filter, R(g x^n)_b as the input
     // (then, two-sided, (g x^n)_b as the filter, R z^n_b as the input)
     const float4* pq_t = reinterpret_cast<const float4*>(wb + w.pq_tmp);
+    // only the spectrum form the convolution reads (bf16 entries straight from
+    // the spectrum pass, or fp32 ones)
+    float4* spec32 = ybf ? nullptr : reinterpret_cast<float4*>(wb + w.pq_tmp);
+    void* spec16 = ybf ? wb + w.pqb_tmp : nullptr;
     for (int b = 0; b < B; ++b) {
       char* tb_b = tmp + (size_t)b * 2 * DL * es;
       float* dh_b = dh_part + ((size_t)b * N + n) * D * HL;
-      HY_CHECK_HIP(hy::fourstep_spec(tb, zn + (size_t)b * DL, reinterpret_cast<float2*>(wb + w.Y),
-                                     reinterpret_cast<float4*>(wb + w.pq_tmp), wb + w.pqb_tmp, L, D, 1, false,
-                                     stream));
+      HY_CHECK_HIP(hy::fourstep_spec(tb, zn + (size_t)b * DL, reinterpret_cast<float2*>(wb + w.Y), spec32, spec16, L,
+                                     D, 1, false, stream));
       HY_CHECK_HIP(conv(tb_b, 1, pq_t, wb + w.pqb_tmp, cout));
       HY_CHECK_HIP(hy::bwd4_dh_store(cout, dh_b, D, L, HL, bf, stream));
       if (two) {
         HY_CHECK_HIP(hy::bwd4_stage_rev(zn + (size_t)b * DL, tb_b, D, L, bf, stream));
-        HY_CHECK_HIP(hy::fourstep_spec(tb, dcf + (size_t)b * DL, reinterpret_cast<float2*>(wb + w.Y),
-                                       reinterpret_cast<float4*>(wb + w.pq_tmp), wb + w.pqb_tmp, L, D, 1, false,
-                                       stream));
+        HY_CHECK_HIP(hy::fourstep_spec(tb, dcf + (size_t)b * DL, reinterpret_cast<float2*>(wb + w.Y), spec32,
+                                       spec16, L, D, 1, false, stream));
         HY_CHECK_HIP(conv(tb_b, 1, pq_t, wb + w.pqb_tmp, cout));
         HY_CHECK_HIP(hy::bwd4_dh_store_neg(cout, dh_b, D, L, bf, stream));
       }

@@ -621,12 +621,13 @@ template <int N, int E, int SI, int W, bool INV, bool ONE> struct RowFrom<N, E, 
 };
 
 // Persistent row pass; items are (channel pair, group of SP slots).
-template <typename YT, int N1, int N2, int MODE, int PF>
-__global__ __launch_bounds__(RowCfg<N2>::WG) void rowpass_kernel(YT* __restrict__ Y, typename PqOf<YT>::type* __restrict__ pq,
+// PT: the spectrum entry type, by default the one stored next to YT; the
+// spectrum pass may write bf16 entries from an fp32 intermediate.
+template <typename YT, int N1, int N2, int MODE, int PF, typename PT = typename PqOf<YT>::type>
+__global__ __launch_bounds__(RowCfg<N2>::WG) void rowpass_kernel(YT* __restrict__ Y, PT* __restrict__ pq,
                                                                  const float2* __restrict__ tw_row, int pq_off,
                                                                  int pair_off, int pq_mod, int nitems) {
   using C = RowCfg<N2>;
-  using PT = typename PqOf<YT>::type;
   constexpr int E = C::E, T = C::T;
   constexpr int HALF = N1 / 2;
   constexpr int PQROWS = HALF + 1;
@@ -822,13 +823,11 @@ template <int N2> struct RowSeqCfg {
   static constexpr int RB = padded_len(N2);
 };
 
-template <typename YT, int N1, int N2, int MODE>
-__global__ __launch_bounds__(RowSeqCfg<N2>::T) void rowpass_seq_kernel(YT* __restrict__ Y,
-                                                                       typename PqOf<YT>::type* __restrict__ pq,
+template <typename YT, int N1, int N2, int MODE, typename PT = typename PqOf<YT>::type>
+__global__ __launch_bounds__(RowSeqCfg<N2>::T) void rowpass_seq_kernel(YT* __restrict__ Y, PT* __restrict__ pq,
                                                                        const float2* __restrict__ tw_row, int pq_off,
                                                                        int pair_off, int pq_mod, int nitems) {
   using C = RowSeqCfg<N2>;
-  using PT = typename PqOf<YT>::type;
   constexpr int E = C::E, T = C::T;
   constexpr int HALF = N1 / 2;
   constexpr int PQROWS = HALF + 1;
@@ -1220,15 +1219,19 @@ static hipError_t launch_col(const ColArgs& a, int N1, int mode, bool act_bf16, 
   return hipErrorInvalidValue;
 }
 
-template <typename YT, int N1, int N2>
+// PT other than the entry type stored next to YT: the spectrum pass only (bf16
+// entries written from an fp32 intermediate).
+template <typename YT, int N1, int N2, typename PT = typename PqOf<YT>::type>
 static hipError_t launch_row_t(void* Y, void* pqv, const float2* tw_row, int pq_off, int pair_off, int pq_mod,
                                int pairs, int mode, hipStream_t s) {
-  using PT = typename PqOf<YT>::type;
+  constexpr bool SPEC_ONLY = !std::is_same<PT, typename PqOf<YT>::type>::value;
+  if (SPEC_ONLY && mode != ROW_SPEC) return hipErrorInvalidValue;
   YT* y = static_cast<YT*>(Y);
   PT* pq = static_cast<PT*>(pqv);
   if constexpr (N2 >= 8192) {
     const int items = pairs * (N1 / 2);
-    auto fn = mode == ROW_CONV ? rowpass_seq_kernel<YT, N1, N2, ROW_CONV> : rowpass_seq_kernel<YT, N1, N2, ROW_SPEC>;
+    auto fn = SPEC_ONLY || mode != ROW_CONV ? rowpass_seq_kernel<YT, N1, N2, ROW_SPEC, PT>
+                                            : rowpass_seq_kernel<YT, N1, N2, ROW_CONV, PT>;
     static DeviceCache grid_cache[2];
     const int g = grid_cache[mode == ROW_CONV ? 0 : 1].get(
         [&] { return resident_grid((const void*)fn, RowSeqCfg<N2>::T, 0, 1 << 30); });
@@ -1247,11 +1250,15 @@ static hipError_t launch_row_t(void* Y, void* pqv, const float2* tw_row, int pq_
     }();
     using Fn = void (*)(YT*, PT*, const float2*, int, int, int, int);
     Fn fn;
-    if (mode != ROW_CONV) fn = rowpass_kernel<YT, N1, N2, ROW_SPEC, 0>;
-    else if (pf == 1) fn = rowpass_kernel<YT, N1, N2, ROW_CONV, 1>;
-    else if (pf == 2) fn = rowpass_kernel<YT, N1, N2, ROW_CONV, 2>;
-    else if (pf == 3) fn = rowpass_kernel<YT, N1, N2, ROW_CONV, 3>;
-    else fn = rowpass_kernel<YT, N1, N2, ROW_CONV, 0>;
+    if constexpr (SPEC_ONLY) {
+      fn = rowpass_kernel<YT, N1, N2, ROW_SPEC, 0, PT>;
+    } else {
+      if (mode != ROW_CONV) fn = rowpass_kernel<YT, N1, N2, ROW_SPEC, 0>;
+      else if (pf == 1) fn = rowpass_kernel<YT, N1, N2, ROW_CONV, 1>;
+      else if (pf == 2) fn = rowpass_kernel<YT, N1, N2, ROW_CONV, 2>;
+      else if (pf == 3) fn = rowpass_kernel<YT, N1, N2, ROW_CONV, 3>;
+      else fn = rowpass_kernel<YT, N1, N2, ROW_CONV, 0>;
+    }
     // LDS is static in the kernel
     static DeviceCache grid_cache[2];
     const int g = grid_cache[mode == ROW_CONV ? 0 : 1].get(
@@ -1262,12 +1269,12 @@ static hipError_t launch_row_t(void* Y, void* pqv, const float2* tw_row, int pq_
   }
 }
 
-template <typename YT>
+template <typename YT, typename PT = typename PqOf<YT>::type>
 static hipError_t launch_row_y(int N1, int N2, void* Y, void* pq, const float2* tw_row, int pq_off, int pair_off,
                                int pq_mod, int pairs, int mode, hipStream_t s) {
 #define ROWCASE(n1, n2)                                                                                  \
   if (N1 == n1 && N2 == n2)                                                                              \
-    return launch_row_t<YT, n1, n2>(Y, pq, tw_row, pq_off, pair_off, pq_mod, pairs, mode, s);
+    return launch_row_t<YT, n1, n2, PT>(Y, pq, tw_row, pq_off, pair_off, pq_mod, pairs, mode, s);
   ROWCASE(64, 256)
   ROWCASE(64, 512)
   ROWCASE(64, 1024)
@@ -1307,10 +1314,13 @@ hipError_t fourstep_spec(const FourStepTables& tb, const float* h, float2* Y, fl
   a.h = h;
   a.Y = Y;
   const int pairs = NO * D / 2;
+  if (pq == nullptr && pq_bf16 == nullptr) return hipErrorInvalidValue;
   hipError_t e = launch_col(a, N1, wrapped ? COL_FWD_HW : COL_FWD_H, false, false, pairs, s);
   if (e != hipSuccess) return e;
+  if (pq == nullptr)  // bf16 entries only, written by the spectrum pass itself
+    return launch_row_y<float2, pq16>(N1, a.N2, Y, pq_bf16, tb.tw_row, 0, 0, pairs, pairs, ROW_SPEC, s);
   e = launch_row_y<float2>(N1, a.N2, Y, pq, tb.tw_row, 0, 0, pairs, pairs, ROW_SPEC, s);
-  if (e != hipSuccess) return e;
+  if (e != hipSuccess || pq_bf16 == nullptr) return e;
   const size_t n = (size_t)pairs * (N1 / 2 + 1) * a.N2;
   hipLaunchKernelGGL(pq_bf16_kernel, dim3(2048), dim3(256), 0, s, pq, static_cast<pq16*>(pq_bf16), n);
   return hipGetLastError();

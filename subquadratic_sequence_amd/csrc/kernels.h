@@ -85,7 +85,9 @@ struct FourStepConvArgs {
   bool y_bf16;           // bf16 workloads: keep the intermediate as bf16 pairs
 };
 hipError_t fourstep_conv(const FourStepTables& tb, const FourStepConvArgs& c, bool bf16, hipStream_t s);
-// filter spectra into pq (fp32) and pq_bf16 (the same entries as four bf16)
+// filter spectra into pq (fp32) and pq_bf16 (the same entries as four bf16);
+// either may be null (not both): with pq null the spectrum pass writes the bf16
+// entries itself
 hipError_t fourstep_spec(const FourStepTables& tb, const float* h, float2* Y, float4* pq, void* pq_bf16, int L,
                          int D, int NO, bool wrapped, hipStream_t s);
 
