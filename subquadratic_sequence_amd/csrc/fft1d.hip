@@ -473,6 +473,12 @@ __device__ __forceinline__ void stpq(pq16* p, float4 x) {
   stc(&b, make_float2(x.z, x.w));
   *p = pq16{a.v, b.v};
 }
+// spectrum entry i: into p and, unless pb is null, its bf16 copy into pb
+template <typename PT>
+__device__ __forceinline__ void stspec(PT* p, pq16* pb, size_t i, float4 x) {
+  stpq(p + i, x);
+  if (pb != nullptr) stpq(pb + i, x);
+}
 
 // value of x held by the lane 32 apart: a backward permute through the LDS
 // crossbar (an LDS-pipe instruction, no VALU work); `sw` is the byte address
@@ -626,7 +632,8 @@ template <int N, int E, int SI, int W, bool INV, bool ONE> struct RowFrom<N, E, 
 template <typename YT, int N1, int N2, int MODE, int PF, typename PT = typename PqOf<YT>::type>
 __global__ __launch_bounds__(RowCfg<N2>::WG) void rowpass_kernel(YT* __restrict__ Y, PT* __restrict__ pq,
                                                                  const float2* __restrict__ tw_row, int pq_off,
-                                                                 int pair_off, int pq_mod, int nitems) {
+                                                                 int pair_off, int pq_mod, int nitems,
+                                                                 pq16* __restrict__ pqb) {
   using C = RowCfg<N2>;
   constexpr int E = C::E, T = C::T;
   constexpr int HALF = N1 / 2;
@@ -693,6 +700,7 @@ __global__ __launch_bounds__(RowCfg<N2>::WG) void rowpass_kernel(YT* __restrict_
     int pl, sg, s;
     const int k1 = row_of(item, pl, sg, s);
     PT* pqp = spectrum(pl, 0);
+    pq16* pqbp = pqb == nullptr ? nullptr : pqb + (pqp - pq);  // ROW_SPEC: the bf16 copy
     float2 v[E];
 #pragma unroll
     for (int q = 0; q < E; ++q) v[q] = cvt2(in.y[q]);
@@ -722,9 +730,9 @@ __global__ __launch_bounds__(RowCfg<N2>::WG) void rowpass_kernel(YT* __restrict_
             const float2 xk = h ? v[q2] : v[q], fm = conjf2(h ? pm2 : pm);
             const float2 ha2 = cadd(xk, fm), d = csub(xk, fm);
             const float2 hb2 = make_float2(d.y, -d.x);
-            stpq(pqp + (size_t)s * N2 + i + (h ? q2 : q) * T,
-                 make_float4(nrm * (ha2.x + hb2.x), nrm * (ha2.y + hb2.y), nrm * (ha2.x - hb2.x),
-                             nrm * (ha2.y - hb2.y)));
+            stspec(pqp, pqbp, (size_t)s * N2 + i + (h ? q2 : q) * T,
+                   make_float4(nrm * (ha2.x + hb2.x), nrm * (ha2.y + hb2.y), nrm * (ha2.x - hb2.x),
+                               nrm * (ha2.y - hb2.y)));
           }
         }
       }
@@ -764,8 +772,9 @@ __global__ __launch_bounds__(RowCfg<N2>::WG) void rowpass_kernel(YT* __restrict_
             const float2 fm = conjf2(xm);
             const float2 ha2 = cadd(xk, fm), d = csub(xk, fm);
             const float2 hb2 = make_float2(d.y, -d.x);
-            stpq(pqp + (size_t)pqrow * N2 + k2, make_float4(nrm * (ha2.x + hb2.x), nrm * (ha2.y + hb2.y),
-                                                           nrm * (ha2.x - hb2.x), nrm * (ha2.y - hb2.y)));
+            stspec(pqp, pqbp, (size_t)pqrow * N2 + k2,
+                   make_float4(nrm * (ha2.x + hb2.x), nrm * (ha2.y + hb2.y), nrm * (ha2.x - hb2.x),
+                               nrm * (ha2.y - hb2.y)));
           }
         }
       }
@@ -826,7 +835,8 @@ template <int N2> struct RowSeqCfg {
 template <typename YT, int N1, int N2, int MODE, typename PT = typename PqOf<YT>::type>
 __global__ __launch_bounds__(RowSeqCfg<N2>::T) void rowpass_seq_kernel(YT* __restrict__ Y, PT* __restrict__ pq,
                                                                        const float2* __restrict__ tw_row, int pq_off,
-                                                                       int pair_off, int pq_mod, int nitems) {
+                                                                       int pair_off, int pq_mod, int nitems,
+                                                                       pq16* __restrict__ pqb) {
   using C = RowSeqCfg<N2>;
   constexpr int E = C::E, T = C::T;
   constexpr int HALF = N1 / 2;
@@ -861,6 +871,7 @@ __global__ __launch_bounds__(RowSeqCfg<N2>::T) void rowpass_seq_kernel(YT* __res
     const int pl = item / HALF, s = item - pl * HALF;
     const int next = item + gridDim.x < nitems ? item + gridDim.x : item;
     PT* pqp = pq + ((size_t)pq_off + (pl + pair_off) % pq_mod) * PQROWS * N2;
+    pq16* pqbp = pqb == nullptr ? nullptr : pqb + (pqp - pq);  // ROW_SPEC: the bf16 copy
     YT* Ya = row_ptr(item, 0);
     YT* Yb = row_ptr(item, 1);
     // forward DFTs, results to the row buffers in natural order (one row at a
@@ -898,8 +909,9 @@ __global__ __launch_bounds__(RowSeqCfg<N2>::T) void rowpass_seq_kernel(YT* __res
           const float2 fm = conjf2(xm);
           const float2 ha2 = cadd(xk, fm), d = csub(xk, fm);
           const float2 hb2 = make_float2(d.y, -d.x);
-          stpq(pqp + (size_t)s * N2 + k2, make_float4(nrm * (ha2.x + hb2.x), nrm * (ha2.y + hb2.y),
-                                                      nrm * (ha2.x - hb2.x), nrm * (ha2.y - hb2.y)));
+          stspec(pqp, pqbp, (size_t)s * N2 + k2,
+                 make_float4(nrm * (ha2.x + hb2.x), nrm * (ha2.y + hb2.y), nrm * (ha2.x - hb2.x),
+                             nrm * (ha2.y - hb2.y)));
         }
       }
     } else {
@@ -926,8 +938,9 @@ __global__ __launch_bounds__(RowSeqCfg<N2>::T) void rowpass_seq_kernel(YT* __res
             const float2 fm = conjf2(xm);
             const float2 ha2 = cadd(xk, fm), d = csub(xk, fm);
             const float2 hb2 = make_float2(d.y, -d.x);
-            stpq(pqp + (size_t)pqrow * N2 + k2, make_float4(nrm * (ha2.x + hb2.x), nrm * (ha2.y + hb2.y),
-                                                           nrm * (ha2.x - hb2.x), nrm * (ha2.y - hb2.y)));
+            stspec(pqp, pqbp, (size_t)pqrow * N2 + k2,
+                   make_float4(nrm * (ha2.x + hb2.x), nrm * (ha2.y + hb2.y), nrm * (ha2.x - hb2.x),
+                               nrm * (ha2.y - hb2.y)));
           }
         }
       }
@@ -1223,7 +1236,7 @@ static hipError_t launch_col(const ColArgs& a, int N1, int mode, bool act_bf16, 
 // entries written from an fp32 intermediate).
 template <typename YT, int N1, int N2, typename PT = typename PqOf<YT>::type>
 static hipError_t launch_row_t(void* Y, void* pqv, const float2* tw_row, int pq_off, int pair_off, int pq_mod,
-                               int pairs, int mode, hipStream_t s) {
+                               int pairs, int mode, hipStream_t s, void* pqb) {
   constexpr bool SPEC_ONLY = !std::is_same<PT, typename PqOf<YT>::type>::value;
   if (SPEC_ONLY && mode != ROW_SPEC) return hipErrorInvalidValue;
   YT* y = static_cast<YT*>(Y);
@@ -1236,7 +1249,7 @@ static hipError_t launch_row_t(void* Y, void* pqv, const float2* tw_row, int pq_
     const int g = grid_cache[mode == ROW_CONV ? 0 : 1].get(
         [&] { return resident_grid((const void*)fn, RowSeqCfg<N2>::T, 0, 1 << 30); });
     hipLaunchKernelGGL(fn, dim3(g < items ? g : items), dim3(RowSeqCfg<N2>::T), 0, s, y, pq, tw_row, pq_off,
-                       pair_off, pq_mod, items);
+                       pair_off, pq_mod, items, static_cast<pq16*>(pqb));
     return hipGetLastError();
   } else {
     using C = RowCfg<N2>;
@@ -1248,7 +1261,7 @@ static hipError_t launch_row_t(void* Y, void* pqv, const float2* tw_row, int pq_
       const char* v = getenv("HYENA_ROW_PREFETCH");
       return v ? atoi(v) & 3 : 1;
     }();
-    using Fn = void (*)(YT*, PT*, const float2*, int, int, int, int);
+    using Fn = void (*)(YT*, PT*, const float2*, int, int, int, int, pq16*);
     Fn fn;
     if constexpr (SPEC_ONLY) {
       fn = rowpass_kernel<YT, N1, N2, ROW_SPEC, 0, PT>;
@@ -1264,17 +1277,17 @@ static hipError_t launch_row_t(void* Y, void* pqv, const float2* tw_row, int pq_
     const int g = grid_cache[mode == ROW_CONV ? 0 : 1].get(
         [&] { return resident_grid((const void*)fn, C::WG, 0, 1 << 30); });
     hipLaunchKernelGGL(fn, dim3(g < items ? g : items), dim3(C::WG), 0, s, y, pq, tw_row, pq_off, pair_off,
-                       pq_mod, items);
+                       pq_mod, items, static_cast<pq16*>(pqb));
     return hipGetLastError();
   }
 }
 
 template <typename YT, typename PT = typename PqOf<YT>::type>
 static hipError_t launch_row_y(int N1, int N2, void* Y, void* pq, const float2* tw_row, int pq_off, int pair_off,
-                               int pq_mod, int pairs, int mode, hipStream_t s) {
+                               int pq_mod, int pairs, int mode, hipStream_t s, void* pqb = nullptr) {
 #define ROWCASE(n1, n2)                                                                                  \
   if (N1 == n1 && N2 == n2)                                                                              \
-    return launch_row_t<YT, n1, n2, PT>(Y, pq, tw_row, pq_off, pair_off, pq_mod, pairs, mode, s);
+    return launch_row_t<YT, n1, n2, PT>(Y, pq, tw_row, pq_off, pair_off, pq_mod, pairs, mode, s, pqb);
   ROWCASE(64, 256)
   ROWCASE(64, 512)
   ROWCASE(64, 1024)
@@ -1302,11 +1315,6 @@ static ColArgs col_args(const FourStepTables& tb, int L, int D, int NO) {
 
 // bf16 copy of the filter spectra (rounded to nearest even), read by the row
 // passes of bf16 workloads
-__global__ __launch_bounds__(256) void pq_bf16_kernel(const float4* __restrict__ in, pq16* __restrict__ out,
-                                                      size_t n) {
-  for (size_t k = blockIdx.x * (size_t)256 + threadIdx.x; k < n; k += (size_t)gridDim.x * 256) stpq(out + k, in[k]);
-}
-
 hipError_t fourstep_spec(const FourStepTables& tb, const float* h, float2* Y, float4* pq, void* pq_bf16, int L,
                          int D, int NO, bool wrapped, hipStream_t s) {
   ColArgs a = col_args(tb, L, D, NO);
@@ -1319,11 +1327,8 @@ hipError_t fourstep_spec(const FourStepTables& tb, const float* h, float2* Y, fl
   if (e != hipSuccess) return e;
   if (pq == nullptr)  // bf16 entries only, written by the spectrum pass itself
     return launch_row_y<float2, pq16>(N1, a.N2, Y, pq_bf16, tb.tw_row, 0, 0, pairs, pairs, ROW_SPEC, s);
-  e = launch_row_y<float2>(N1, a.N2, Y, pq, tb.tw_row, 0, 0, pairs, pairs, ROW_SPEC, s);
-  if (e != hipSuccess || pq_bf16 == nullptr) return e;
-  const size_t n = (size_t)pairs * (N1 / 2 + 1) * a.N2;
-  hipLaunchKernelGGL(pq_bf16_kernel, dim3(2048), dim3(256), 0, s, pq, static_cast<pq16*>(pq_bf16), n);
-  return hipGetLastError();
+  // fp32 entries, and the bf16 copy (if asked for) from the same values
+  return launch_row_y<float2>(N1, a.N2, Y, pq, tb.tw_row, 0, 0, pairs, pairs, ROW_SPEC, s, pq_bf16);
 }
 
 hipError_t fourstep_conv(const FourStepTables& tb, const FourStepConvArgs& c, bool is_bf16, hipStream_t s) {
