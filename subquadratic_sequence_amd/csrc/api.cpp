@@ -742,7 +742,7 @@ int hyena_filter_bwd(const hyena_layer* layer, const hyena_filter_params* p, con
   HY_CHECK_HIP(hy::transpose2d(p->w3, f(w.w3t), W, ND, false, stream));
   HY_CHECK_HIP(hy::gemm(hy::GemmArgs{a.a2, f(w.w3t), f(w.o), P, ND, W, P, false, true, nullptr}, false, stream));
   // dL/do = dh * window (and the decay gradient)
-  HY_CHECK_HIP(hy::filter_bwd_out(a, stream));
+  HY_CHECK_HIP(hy::filter_bwd_out(a, f(w.part), stream));
   // back through the hidden layers: dq2 = (do W3^T) cos(q2), dq1 = (dq2 W2^T) cos(q1)
   {
     // dL/da2 = dout^T W3^T over K = N D, split; partial results summed in order
@@ -772,14 +772,14 @@ int hyena_filter_bwd(const hyena_layer* layer, const hyena_filter_params* p, con
     g.lda = g.ldb = P;
     hipError_t e = hy::gemm(g, false, stream);
     if (e != hipSuccess) return e;
-    return hy::sum_rows(f(w.part), out, S, (size_t)M * Nn, (size_t)M * Nn, false, stream);
+    return hy::sum_rows_tall(f(w.part), out, S, (size_t)M * Nn, stream);
   };
   HY_CHECK_HIP(wgrad(f(w.a2t), f(w.dout), dw3, W, ND, w.s3));
   HY_CHECK_HIP(wgrad(f(w.a1t), f(w.d2t), dw2, W, W, w.s2));
   HY_CHECK_HIP(wgrad(f(w.et), f(w.d1t), dw1, F, W, w.s1));
-  HY_CHECK_HIP(hy::row_sums(f(w.dout), db3, ND, P, stream));
-  HY_CHECK_HIP(hy::row_sums(f(w.d2t), db2, W, P, stream));
-  HY_CHECK_HIP(hy::row_sums(f(w.d1t), db1, W, P, stream));
+  HY_CHECK_HIP(hy::row_sums(f(w.dout), db3, ND, P, f(w.part), stream));
+  HY_CHECK_HIP(hy::row_sums(f(w.d2t), db2, W, P, f(w.part), stream));
+  HY_CHECK_HIP(hy::row_sums(f(w.d1t), db1, W, P, f(w.part), stream));
   return HYENA_OK;
 }
 

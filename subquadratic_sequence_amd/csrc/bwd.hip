@@ -329,6 +329,30 @@ __global__ __launch_bounds__(256) void sum_rows_kernel(const T* __restrict__ in,
   }
 }
 
+// part[r * S + seg] = sum of in[r * K + k] over segment seg of K / S entries
+__global__ __launch_bounds__(256) void row_sum_seg_kernel(const float* __restrict__ in, float* __restrict__ part,
+                                                          int K, int S) {
+  __shared__ float sh[256];
+  const int r = blockIdx.x / S, seg = blockIdx.x - r * S, SK = K / S;
+  const float* x = in + (size_t)r * K + (size_t)seg * SK;
+  float v = 0.f;
+  for (int k = threadIdx.x; k < SK; k += 256) v += x[k];
+  v = block_sum256(v, sh);
+  if (threadIdx.x == 0) part[blockIdx.x] = v;
+}
+
+// Band sums of a tall [R][n] array of partial results, in place: workgroup
+// (column block, g) adds rows [g R/G, (g+1) R/G) in order and writes the sum
+// into row g R/G (a row of its own band).
+__global__ __launch_bounds__(256) void sum_bands_kernel(float* __restrict__ part, int R, int G, size_t n) {
+  const size_t col = (size_t)blockIdx.x * 256 + threadIdx.x;
+  if (col >= n) return;
+  const int RG = R / G, r0 = (int)blockIdx.y * RG;
+  float v = 0.f;
+  for (int r = r0; r < r0 + RG; ++r) v += part[(size_t)r * n + col];
+  part[(size_t)r0 * n + col] = v;
+}
+
 // out[r] = sum_k in[r * K + k]; one workgroup per row.
 __global__ __launch_bounds__(256) void row_sum_kernel(const float* __restrict__ in, float* __restrict__ out, int K) {
   __shared__ float sh[256];
@@ -407,18 +431,22 @@ __global__ __launch_bounds__(256) void filter_bwd_feat_kernel(FilterBwdArgs a) {
 // the non-tap entry L of a wrapped two-sided filter) and
 // ddecay[c] = sum_{n,t} dh * o * (-|tau|) * win, win = exp(-decay_c |tau|);
 // o = (a2 W3) [N D][P] channel-major, plus b3.
-__global__ __launch_bounds__(256) void filter_bwd_out_kernel(FilterBwdArgs a) {
+// One workgroup per (channel c, segment of P / S positions): dL/do = dh x window
+// and the segment's share of the decay gradient, into part[c][seg] (summed in
+// segment order by row_sum_kernel). L is a power of two, so tau = t * (1/L)
+// equals t / L exactly.
+__global__ __launch_bounds__(256) void filter_bwd_out_kernel(FilterBwdArgs a, float* __restrict__ part, int S) {
   __shared__ float sh[256];
-  const int c = blockIdx.x, L = a.L, D = a.D;
-  const int P = a.noncausal ? 2 * L : L;
-  const float dc = a.decay[c];
+  const int c = blockIdx.x, seg = blockIdx.y, L = a.L, D = a.D;
+  const int P = a.noncausal ? 2 * L : L, SL = P / S;
+  const float dc = a.decay[c], invL = 1.f / (float)L;
   float acc = 0.f;
   for (int n = 0; n < a.NO; ++n) {
     const size_t row = ((size_t)n * D + c) * P;
     const float ob = a.b3[n * D + c];
-    for (int t = threadIdx.x; t < P; t += 256) {
+    for (int t = seg * SL + threadIdx.x; t < (seg + 1) * SL; t += 256) {
       const bool tap = !(a.noncausal && t == L);
-      const float tau = fabsf((float)(t > L ? t - 2 * L : t) / (float)L);
+      const float tau = fabsf((float)(t > L ? t - 2 * L : t) * invL);
       const float win = expf(-dc * tau);
       const float g = tap ? a.dh[row + t] : 0.f;
       a.dout[row + t] = g * win;
@@ -426,7 +454,7 @@ __global__ __launch_bounds__(256) void filter_bwd_out_kernel(FilterBwdArgs a) {
     }
   }
   acc = block_sum256(acc, sh);
-  if (threadIdx.x == 0) a.ddecay[c] = acc;
+  if (threadIdx.x == 0) part[(size_t)c * S + seg] = acc;
 }
 
 // x[i] *= y[i]
@@ -523,9 +551,33 @@ hipError_t sum_rows(const void* in, float* out, int R, size_t stride, size_t n, 
   return hipGetLastError();
 }
 
-hipError_t row_sums(const float* in, float* out, int rows, int K, hipStream_t s) {
-  hipLaunchKernelGGL(row_sum_kernel, dim3(rows), dim3(256), 0, s, in, out, K);
+hipError_t row_sums(const float* in, float* out, int rows, int K, float* part, hipStream_t s) {
+  // few rows: each row in S segments (power of two, at least 1024 entries each),
+  // the segment sums then added in order
+  int S = 1;
+  while (rows * S * 2 <= 1024 && K % (S * 2) == 0 && K / (S * 2) >= 1024) S *= 2;
+  if (S == 1 || part == nullptr) {
+    hipLaunchKernelGGL(row_sum_kernel, dim3(rows), dim3(256), 0, s, in, out, K);
+    return hipGetLastError();
+  }
+  hipLaunchKernelGGL(row_sum_seg_kernel, dim3(rows * S), dim3(256), 0, s, in, part, K, S);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(row_sum_kernel, dim3(rows), dim3(256), 0, s, part, out, S);
   return hipGetLastError();
+}
+
+hipError_t sum_rows_tall(float* part, float* out, int R, size_t n, hipStream_t s) {
+  // bands G (a power of two dividing R) so that about 512 workgroups run
+  const size_t cb = (n + 255) / 256;
+  int G = 1;
+  while ((size_t)G * 2 * cb <= 512 && R % (G * 2) == 0 && R / (G * 2) >= 4) G *= 2;
+  if (G == 1) return sum_rows(part, out, R, n, n, false, s);
+  hipLaunchKernelGGL(sum_bands_kernel, dim3((unsigned)cb, G), dim3(256), 0, s, part, R, G, n);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  // the G band sums sit in rows 0, R/G, 2 R/G, ...
+  return sum_rows(part, out, G, (size_t)(R / G) * n, n, false, s);
 }
 
 hipError_t filter_bwd_feat(const FilterBwdArgs& a, hipStream_t s) {
@@ -534,8 +586,15 @@ hipError_t filter_bwd_feat(const FilterBwdArgs& a, hipStream_t s) {
   return hipGetLastError();
 }
 
-hipError_t filter_bwd_out(const FilterBwdArgs& a, hipStream_t s) {
-  hipLaunchKernelGGL(filter_bwd_out_kernel, dim3(a.D), dim3(256), 0, s, a);
+hipError_t filter_bwd_out(const FilterBwdArgs& a, float* part, hipStream_t s) {
+  // position segments of at least 2048 (P is a power of two)
+  const int P = a.noncausal ? 2 * a.L : a.L;
+  int S = 1;
+  while (S < 16 && P / (S * 2) >= 2048) S *= 2;
+  hipLaunchKernelGGL(filter_bwd_out_kernel, dim3(a.D, S), dim3(256), 0, s, a, part, S);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(row_sum_kernel, dim3(a.D), dim3(256), 0, s, part, a.ddecay, S);
   return hipGetLastError();
 }
 

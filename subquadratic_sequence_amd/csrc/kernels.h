@@ -113,7 +113,12 @@ hipError_t short_conv_bwd(const float* sbar, const void* p, const float* short_w
 // out[i] = sum_{r < R} in[r stride + i], i < n (in: fp32 or bf16)
 hipError_t sum_rows(const void* in, float* out, int R, size_t stride, size_t n, bool in_bf16, hipStream_t s);
 // out[r] = sum_k in[r K + k]
-hipError_t row_sums(const float* in, float* out, int rows, int K, hipStream_t s);
+// out[r] = sum over row r of in [rows][K], in a fixed order; with few rows the
+// rows are summed in segments through part (rows * 1024 floats at most)
+hipError_t row_sums(const float* in, float* out, int rows, int K, float* part, hipStream_t s);
+// out[i] = sum_r part[r][i] over R rows of n, in a fixed order; part is
+// overwritten (a tall array of partial results, R a power of two)
+hipError_t sum_rows_tall(float* part, float* out, int R, size_t n, hipStream_t s);
 
 struct FilterBwdArgs {
   int L, D, NO, K, W, noncausal;
@@ -126,7 +131,8 @@ struct FilterBwdArgs {
   float* ddecay;         // [D]
 };
 hipError_t filter_bwd_feat(const FilterBwdArgs& a, hipStream_t s);
-hipError_t filter_bwd_out(const FilterBwdArgs& a, hipStream_t s);
+// dL/do and the decay gradient; part: scratch of D * 16 floats
+hipError_t filter_bwd_out(const FilterBwdArgs& a, float* part, hipStream_t s);
 hipError_t mul_inplace(float* x, const float* y, size_t n, hipStream_t s);
 
 }  // namespace hy

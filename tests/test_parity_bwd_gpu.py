@@ -133,7 +133,10 @@ def test_bwd_is_bit_reproducible():
 
 
 @pytest.mark.parametrize("L,D,N,K,W,causal", [(1024, 64, 2, 8, 64, True), (2048, 128, 2, 16, 64, True),
-                                               (256, 64, 3, 4, 32, False), (64, 64, 1, 32, 128, True)])
+                                               (256, 64, 3, 4, 32, False), (64, 64, 1, 32, 128, True),
+                                               # long filters: the output-layer pass in position segments,
+                                               # banded sums of the weight-gradient splits, segmented bias sums
+                                               (16384, 64, 1, 8, 64, True), (8192, 64, 2, 16, 32, False)])
 def test_filter_bwd_matches_oracle(L, D, N, K, W, causal):
     import torch
     import oracle
