@@ -7,8 +7,9 @@
 // lags of two-sided filters: dh(-tau) = conv(R z, dc)(L - 1 - tau)). The
 // kernels here stage the inputs of those convolutions (reversed where needed),
 // apply gates and skips, and read the results back reversed. Rows are L
-// positions long; every access walks a row in order (the reversed ones
-// backwards), so loads and stores stay coalesced.
+// positions long (a multiple of 8); every thread takes 8 consecutive positions
+// of a row per step in 16-byte accesses (a reversed run of 8 is the aligned run
+// of 8 that ends where the forward one starts, read or written backwards).
 #include "common.h"
 #include "kernels_bwd.h"
 #include "vec8.h"
@@ -16,18 +17,28 @@
 namespace hy {
 namespace {
 
+// grid for n elements taken 8 at a time
 int grid_of(size_t n) {
-  const size_t g = (n + 255) / 256;
+  const size_t g = (n / 8 + 255) / 256;
   return (int)(g < 8192 ? (g > 0 ? g : 1) : 8192);
+}
+
+// grid-stride loop over the 8-element chunks of n elements
+#define FOR_CHUNKS(i, n) \
+  for (size_t i = ((size_t)blockIdx.x * 256 + threadIdx.x) * 8; i < (n); i += (size_t)gridDim.x * 256 * 8)
+
+__device__ __forceinline__ void rev8(const float (&a)[8], float (&b)[8]) {
+#pragma unroll
+  for (int k = 0; k < 8; ++k) b[7 - k] = a[k];
 }
 
 template <typename T>
 __global__ __launch_bounds__(256) void bwd4_fill_kernel(T* __restrict__ p, float v, int rows, size_t len,
                                                         size_t stride) {
-  const size_t n = (size_t)rows * len;
-  for (size_t i = (size_t)blockIdx.x * 256 + threadIdx.x; i < n; i += (size_t)gridDim.x * 256) {
+  const float vv[8] = {v, v, v, v, v, v, v, v};
+  FOR_CHUNKS(i, (size_t)rows * len) {
     const size_t r = i / len;
-    stf(p + r * stride + (i - r * len), v);
+    st8(p + r * stride + (i - r * len), vv);
   }
 }
 
@@ -35,12 +46,13 @@ __global__ __launch_bounds__(256) void bwd4_fill_kernel(T* __restrict__ p, float
 template <typename T>
 __global__ __launch_bounds__(256) void bwd4_z_init_kernel(const T* __restrict__ sp, float* __restrict__ zf,
                                                           T* __restrict__ tmp, int B, int D, int L, int NO) {
-  const size_t DL = (size_t)D * L, n = (size_t)B * DL, JL = (size_t)(NO + 1) * DL;
-  for (size_t i = (size_t)blockIdx.x * 256 + threadIdx.x; i < n; i += (size_t)gridDim.x * 256) {
+  const size_t DL = (size_t)D * L, JL = (size_t)(NO + 1) * DL;
+  FOR_CHUNKS(i, (size_t)B * DL) {
     const size_t b = i / DL, r = i - b * DL;
-    const T v = sp[b * JL + r];
-    zf[i] = ldf(&v);
-    tmp[b * 2 * DL + r] = v;
+    float v[8];
+    ld8(sp + b * JL + r, v);
+    st8(zf + i, v);
+    st8(tmp + b * 2 * DL + r, v);
   }
 }
 
@@ -50,17 +62,21 @@ __global__ __launch_bounds__(256) void bwd4_z_next_kernel(const T* __restrict__ 
                                                           const float* __restrict__ dskip_n, float* __restrict__ zfn,
                                                           T* __restrict__ tmp, T* __restrict__ zfin, int B, int D,
                                                           int L, int NO, int n) {
-  const size_t DL = (size_t)D * L, N = (size_t)B * DL, JL = (size_t)(NO + 1) * DL;
-  for (size_t i = (size_t)blockIdx.x * 256 + threadIdx.x; i < N; i += (size_t)gridDim.x * 256) {
+  const size_t DL = (size_t)D * L, JL = (size_t)(NO + 1) * DL;
+  FOR_CHUNKS(i, (size_t)B * DL) {
     const size_t b = i / DL, r = i - b * DL;
-    const int d = (int)(r / L);
-    const float x = ldf(sp + b * JL + (size_t)(n + 1) * DL + r);
-    const float z = x * ldf(c + i) + dskip_n[d] * zf[i];
+    const float dd = dskip_n[r / L];
+    float x[8], cv[8], z[8];
+    ld8(sp + b * JL + (size_t)(n + 1) * DL + r, x);
+    ld8(c + i, cv);
+    ld8(zf + i, z);
+#pragma unroll
+    for (int k = 0; k < 8; ++k) z[k] = x[k] * cv[k] + dd * z[k];
     if (zfn != nullptr) {
-      zfn[i] = z;
-      stf(tmp + b * 2 * DL + r, z);
+      st8(zfn + i, z);
+      st8(tmp + b * 2 * DL + r, z);
     } else {
-      stf(zfin + i, z);
+      st8(zfin + i, z);
     }
   }
 }
@@ -68,7 +84,11 @@ __global__ __launch_bounds__(256) void bwd4_z_next_kernel(const T* __restrict__ 
 template <typename T>
 __global__ __launch_bounds__(256) void bwd4_to_f32_kernel(const T* __restrict__ in, float* __restrict__ out,
                                                           size_t n) {
-  for (size_t i = (size_t)blockIdx.x * 256 + threadIdx.x; i < n; i += (size_t)gridDim.x * 256) out[i] = ldf(in + i);
+  FOR_CHUNKS(i, n) {
+    float v[8];
+    ld8(in + i, v);
+    st8(out + i, v);
+  }
 }
 
 // One workgroup per row (b, d) of g = dz^{n+1}: dx^n = g c^n into ds block n+1,
@@ -125,11 +145,17 @@ __global__ __launch_bounds__(256) void bwd4_rev_finish_kernel(const float* __res
                                                               const float* __restrict__ dskip_n,
                                                               float* __restrict__ out, size_t ostride, int B, int D,
                                                               int L) {
-  const size_t n = (size_t)B * D * L;
-  for (size_t i = (size_t)blockIdx.x * 256 + threadIdx.x; i < n; i += (size_t)gridDim.x * 256) {
+  FOR_CHUNKS(i, (size_t)B * D * L) {
     const size_t row = i / L, t = i - row * L;
     const size_t b = row / D, d = row - b * D;
-    out[b * ostride + d * L + t] = dskip_n[d] * g[i] + ldf(conv + row * L + (L - 1 - t));
+    const float dd = dskip_n[d];
+    float gv[8], cr[8], cv[8], o[8];
+    ld8(g + i, gv);
+    ld8(conv + row * L + (L - 8 - t), cr);
+    rev8(cr, cv);
+#pragma unroll
+    for (int k = 0; k < 8; ++k) o[k] = dd * gv[k] + cv[k];
+    st8(out + b * ostride + d * L + t, o);
   }
 }
 
@@ -137,10 +163,12 @@ __global__ __launch_bounds__(256) void bwd4_rev_finish_kernel(const float* __res
 template <typename T>
 __global__ __launch_bounds__(256) void bwd4_dh_store_kernel(const T* __restrict__ conv, float* __restrict__ dh, int D,
                                                             int L, int HL) {
-  const size_t n = (size_t)D * L;
-  for (size_t i = (size_t)blockIdx.x * 256 + threadIdx.x; i < n; i += (size_t)gridDim.x * 256) {
+  FOR_CHUNKS(i, (size_t)D * L) {
     const size_t row = i / L, tau = i - row * L;
-    dh[row * HL + tau] = ldf(conv + row * L + (L - 1 - tau));
+    float cr[8], o[8];
+    ld8(conv + row * L + (L - 8 - tau), cr);
+    rev8(cr, o);
+    st8(dh + row * HL + tau, o);
   }
 }
 
@@ -150,10 +178,15 @@ __global__ __launch_bounds__(256) void bwd4_dh_store_kernel(const T* __restrict_
 template <typename T>
 __global__ __launch_bounds__(256) void bwd4_dh_store_neg_kernel(const T* __restrict__ conv, float* __restrict__ dh,
                                                                 int D, int L) {
-  const size_t n = (size_t)D * L;
-  for (size_t i = (size_t)blockIdx.x * 256 + threadIdx.x; i < n; i += (size_t)gridDim.x * 256) {
+  FOR_CHUNKS(i, (size_t)D * L) {
     const size_t row = i / L, k = i - row * L;  // j = L + k
-    dh[row * 2 * L + L + k] = k == 0 ? 0.f : ldf(conv + row * L + (k - 1));
+    const T* cr = conv + row * L;
+    float cv[8], o[8];
+    ld8(cr + k, cv);
+    o[0] = k == 0 ? 0.f : ldf(cr + (k - 1));
+#pragma unroll
+    for (int q = 1; q < 8; ++q) o[q] = cv[q - 1];
+    st8(dh + row * 2 * L + L + k, o);
   }
 }
 
@@ -161,10 +194,12 @@ __global__ __launch_bounds__(256) void bwd4_dh_store_neg_kernel(const T* __restr
 template <typename T>
 __global__ __launch_bounds__(256) void bwd4_stage_rev_kernel(const float* __restrict__ zf, T* __restrict__ tmp, int D,
                                                              int L) {
-  const size_t n = (size_t)D * L;
-  for (size_t i = (size_t)blockIdx.x * 256 + threadIdx.x; i < n; i += (size_t)gridDim.x * 256) {
+  FOR_CHUNKS(i, (size_t)D * L) {
     const size_t row = i / L, t = i - row * L;
-    stf(tmp + row * L + (L - 1 - t), zf[i]);
+    float z[8], o[8];
+    ld8(zf + i, z);
+    rev8(z, o);
+    st8(tmp + row * L + (L - 8 - t), o);
   }
 }
 
