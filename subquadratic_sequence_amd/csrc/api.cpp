@@ -535,8 +535,7 @@ static int fwd_impl(const hyena_layer* layer, const void* u, const void* w_in, c
   void* zfin = wsb + fw.zfinal;
 
   if (ev) HY_CHECK_HIP(hipEventRecord(ev[0], stream));
-  HY_CHECK_HIP(hy::transpose2d(w_in, wt_in, D, J, bf, stream));
-  HY_CHECK_HIP(hy::transpose2d(w_out, wt_out, D, D, bf, stream));
+  HY_CHECK_HIP(hy::transpose2d_pair(w_in, wt_in, D, J, w_out, wt_out, D, D, bf, stream));
   // in-projection with the short convolution in the epilogue: pbuf holds s
   hy::GemmArgs gi{u, wt_in, pbuf, B * L, J, D, L, false, true, short_w};
   HY_CHECK_HIP(hy::gemm(gi, bf, stream));

@@ -498,6 +498,44 @@ __global__ __launch_bounds__(256) void transpose_kernel(const U* __restrict__ sr
   }
 }
 
+// Two matrices of different shapes in one launch (blockIdx.z picks the
+// matrix; the grid covers the larger and the other's surplus blocks return).
+template <typename U>
+__global__ __launch_bounds__(256) void transpose_pair_kernel(const U* __restrict__ s0, U* __restrict__ d0, int r0,
+                                                             int c0, const U* __restrict__ s1, U* __restrict__ d1,
+                                                             int r1, int c1) {
+  __shared__ U tile[32][33];
+  const bool second = blockIdx.z == 1;
+  const U* src = second ? s1 : s0;
+  U* dst = second ? d1 : d0;
+  const int rows = second ? r1 : r0, cols = second ? c1 : c0;
+  const int c00 = blockIdx.x * 32, r00 = blockIdx.y * 32;
+  if (c00 >= cols || r00 >= rows) return;  // uniform per workgroup
+  const int tx = threadIdx.x & 31, ty = threadIdx.x >> 5;
+  for (int i = ty; i < 32; i += 8) {
+    const int r = r00 + i, c = c00 + tx;
+    if (r < rows && c < cols) tile[i][tx] = src[(size_t)r * cols + c];
+  }
+  __syncthreads();
+  for (int i = ty; i < 32; i += 8) {
+    const int c = c00 + i, r = r00 + tx;
+    if (r < rows && c < cols) dst[(size_t)c * rows + r] = tile[tx][i];
+  }
+}
+
+hipError_t transpose2d_pair(const void* s0, void* d0, int r0, int c0, const void* s1, void* d1, int r1, int c1,
+                            bool bf16, hipStream_t s) {
+  const int cols = c0 > c1 ? c0 : c1, rows = r0 > r1 ? r0 : r1;
+  dim3 grid((cols + 31) / 32, (rows + 31) / 32, 2), block(256);
+  if (bf16)
+    hipLaunchKernelGGL(transpose_pair_kernel<unsigned short>, grid, block, 0, s, (const unsigned short*)s0,
+                       (unsigned short*)d0, r0, c0, (const unsigned short*)s1, (unsigned short*)d1, r1, c1);
+  else
+    hipLaunchKernelGGL(transpose_pair_kernel<float>, grid, block, 0, s, (const float*)s0, (float*)d0, r0, c0,
+                       (const float*)s1, (float*)d1, r1, c1);
+  return hipGetLastError();
+}
+
 hipError_t transpose2d(const void* src, void* dst, int rows, int cols, bool bf16, hipStream_t s, int batch) {
   dim3 grid((cols + 31) / 32, (rows + 31) / 32, batch), block(256);
   if (bf16)

@@ -230,8 +230,7 @@ int nd_fwd_impl(const hyena_nd_layer* layer, const float* u, const float* w_in, 
 
   if (ev) HY_CHECK_HIP(hipEventRecord(ev[0], stream));
   HY_CHECK_HIP(hy::nd_gate(u, reinterpret_cast<float*>(wsb + w.part), gate_a, gate_b, gate, B, N, C, V, stream));
-  HY_CHECK_HIP(hy::transpose2d(w_in, wt_in, C, J, false, stream));
-  HY_CHECK_HIP(hy::transpose2d(w_out, wt_out, C, C, false, stream));
+  HY_CHECK_HIP(hy::transpose2d_pair(w_in, wt_in, C, J, w_out, wt_out, C, C, false, stream));
   hy::GemmArgs gi{u, wt_in, pbuf, B * V, J, C, V, false, true, nullptr};
   HY_CHECK_HIP(hy::gemm(gi, false, stream));
   if (ev) HY_CHECK_HIP(hipEventRecord(ev[1], stream));
@@ -363,8 +362,7 @@ int film_fwd_impl(int X, int Y, int Z, int C, int N, int bd, const hyena_nd_filt
   float* pbuf = reinterpret_cast<float*>(base + w.p);
   float* zfin = reinterpret_cast<float*>(base + w.zfinal);
   float* ones = reinterpret_cast<float*>(base + w.gate);
-  HY_CHECK_HIP(hy::transpose2d(w_in, wt_in, C, J, false, stream));
-  HY_CHECK_HIP(hy::transpose2d(w_out, wt_out, C, C, false, stream));
+  HY_CHECK_HIP(hy::transpose2d_pair(w_in, wt_in, C, J, w_out, wt_out, C, C, false, stream));
   hy::GemmArgs gi{u, wt_in, pbuf, B * V, J, C, V, false, true, nullptr};
   HY_CHECK_HIP(hy::gemm(gi, false, stream));
   if (ev) HY_CHECK_HIP(hipEventRecord(ev[2], stream));
