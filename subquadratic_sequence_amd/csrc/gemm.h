@@ -32,7 +32,8 @@ hipError_t gemm(const GemmArgs& g, bool bf16, hipStream_t s);
 // dst [cols][rows] = transpose of src [rows][cols] (storage type of the dtype), for
 // each of `batch` matrices stored back to back
 hipError_t transpose2d(const void* src, void* dst, int rows, int cols, bool bf16, hipStream_t s, int batch = 1);
-// the transposes of two matrices (rows0 x cols0 and rows1 x cols1) in one launch
+// the transposes of two matrices (rows0 x cols0 and rows1 x cols1) in one launch;
+// every dimension a multiple of 64
 hipError_t transpose2d_pair(const void* src0, void* dst0, int rows0, int cols0, const void* src1, void* dst1,
                             int rows1, int cols1, bool bf16, hipStream_t s);
 

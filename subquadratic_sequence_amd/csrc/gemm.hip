@@ -500,33 +500,50 @@ __global__ __launch_bounds__(256) void transpose_kernel(const U* __restrict__ sr
 
 // Two matrices of different shapes in one launch (blockIdx.z picks the
 // matrix; the grid covers the larger and the other's surplus blocks return).
+// 64 x 64 tiles in 16-byte accesses: VEC consecutive columns of a source row
+// per load, VEC consecutive rows of a source column per store (dimensions are
+// multiples of 64; the padded LDS rows keep every row 16-byte aligned).
 template <typename U>
 __global__ __launch_bounds__(256) void transpose_pair_kernel(const U* __restrict__ s0, U* __restrict__ d0, int r0,
                                                              int c0, const U* __restrict__ s1, U* __restrict__ d1,
                                                              int r1, int c1) {
-  __shared__ U tile[32][33];
+  constexpr int T = 64, VEC = 16 / (int)sizeof(U), CPR = T / VEC, LD = T + VEC;
+  typedef unsigned int u32x4v __attribute__((ext_vector_type(4)));
+  __shared__ __attribute__((aligned(16))) U tile[T * LD];
   const bool second = blockIdx.z == 1;
   const U* src = second ? s1 : s0;
   U* dst = second ? d1 : d0;
   const int rows = second ? r1 : r0, cols = second ? c1 : c0;
-  const int c00 = blockIdx.x * 32, r00 = blockIdx.y * 32;
-  if (c00 >= cols || r00 >= rows) return;  // uniform per workgroup
-  const int tx = threadIdx.x & 31, ty = threadIdx.x >> 5;
-  for (int i = ty; i < 32; i += 8) {
-    const int r = r00 + i, c = c00 + tx;
-    if (r < rows && c < cols) tile[i][tx] = src[(size_t)r * cols + c];
+  const int col0 = blockIdx.x * T, row0 = blockIdx.y * T;
+  if (col0 >= cols || row0 >= rows) return;  // uniform per workgroup
+#pragma unroll
+  for (int q = threadIdx.x; q < T * CPR; q += 256) {
+    const int r = q / CPR, c = (q % CPR) * VEC;
+    *reinterpret_cast<u32x4v*>(tile + r * LD + c) =
+        *reinterpret_cast<const u32x4v*>(src + (size_t)(row0 + r) * cols + col0 + c);
   }
   __syncthreads();
-  for (int i = ty; i < 32; i += 8) {
-    const int c = c00 + i, r = r00 + tx;
-    if (r < rows && c < cols) dst[(size_t)c * rows + r] = tile[tx][i];
+#pragma unroll
+  for (int q = threadIdx.x; q < T * CPR; q += 256) {
+    // CPR consecutive lanes write one destination row's 64 elements
+    const int c = q / CPR, r = (q % CPR) * VEC;
+    u32x4v o;
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      if constexpr (sizeof(U) == 2)
+        o[k] = (unsigned)tile[(r + 2 * k) * LD + c] | ((unsigned)tile[(r + 2 * k + 1) * LD + c] << 16);
+      else
+        o[k] = __float_as_uint(tile[(r + k) * LD + c]);
+    }
+    *reinterpret_cast<u32x4v*>(dst + (size_t)(col0 + c) * rows + row0 + r) = o;
   }
 }
 
 hipError_t transpose2d_pair(const void* s0, void* d0, int r0, int c0, const void* s1, void* d1, int r1, int c1,
                             bool bf16, hipStream_t s) {
+  if (r0 % 64 || c0 % 64 || r1 % 64 || c1 % 64) return hipErrorInvalidValue;
   const int cols = c0 > c1 ? c0 : c1, rows = r0 > r1 ? r0 : r1;
-  dim3 grid((cols + 31) / 32, (rows + 31) / 32, 2), block(256);
+  dim3 grid(cols / 64, rows / 64, 2), block(256);
   if (bf16)
     hipLaunchKernelGGL(transpose_pair_kernel<unsigned short>, grid, block, 0, s, (const unsigned short*)s0,
                        (unsigned short*)d0, r0, c0, (const unsigned short*)s1, (unsigned short*)d1, r1, c1);
