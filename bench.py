@@ -466,6 +466,24 @@ def main_bwd(args, torch, hs, make_config):
                       dtype=torch.uint8, device="cuda")
     y = torch.empty_like(u)
     fws_fwd = torch.empty(hs.hyena_workspace_bytes(B, L, D, N, dt), dtype=torch.uint8, device="cuda")
+    if args.bwd_only:
+        # hyena_bwd alone, back to back (for a kernel trace of its launches)
+        for _ in range(args.warmup):
+            hs.hyena_bwd(layer, u, w_in, short_w, dskip, w_out, dy, ws=ws)
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(args.steps):
+            hs.hyena_bwd(layer, u, w_in, short_w, dskip, w_out, dy, ws=ws)
+        e1.record()
+        torch.cuda.synchronize()
+        bwd_ms = e0.elapsed_time(e1) / args.steps
+        print(json.dumps({"metric": "Hyena bwd tokens/sec (hyena_bwd only)", "value": B * L / (bwd_ms * 1e-3),
+                          "unit": "tokens/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+                          "ms_per_step": bwd_ms, "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+                          "dtype": inp.dtype, "data": "synthetic",
+                          "config": {"workload": args.workload, "B": B, "L": L, "D": D, "N": N}}), flush=True)
+        return
     for _ in range(args.warmup):
         g = hs.hyena_bwd(layer, u, w_in, short_w, dskip, w_out, dy, ws=ws)
         hs.hyena_filter_bwd(layer, *fp, inp.K, g["dh"], ws=fws)
@@ -504,6 +522,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--backward", action="store_true",
                     help="time hyena_bwd and hyena_filter_bwd instead (1D workloads)")
+    ap.add_argument("--bwd-only", action="store_true",
+                    help="with --backward: run and time hyena_bwd alone, back to back")
     ap.add_argument("--cpu-tokens", type=int, default=0,
                     help="positions of the 1D oracle sample (default 0: the whole sequence)")
     ap.add_argument("--cpu-workers", type=int, default=0,
