@@ -197,9 +197,9 @@ int bwd_split_in(int B, int L, int D, int N, int dtype) {
 struct BwdWs {
   size_t wt_in, s, p, gz, zsave, csave, zfin, sbar, pbar, dh_part, dd_part, dsw_part, dwo_part, dwi_part;
   // four-step regime: convolution staging and output, the passes' intermediate,
-  // dz ping-pong (fp32), one sample's z (or dc) spectrum (fp32 and bf16), zero
-  // skips; two-sided filters: g x^n in fp32
-  size_t tmp, cout, Y, g0, g1, pq_tmp, pqb_tmp, zeros, dcf;
+  // dz ping-pong (fp32), one sample's z (or dc) spectrum (fp32 and bf16);
+  // two-sided filters: g x^n in fp32
+  size_t tmp, cout, Y, g0, g1, pq_tmp, pqb_tmp, dcf;
   size_t total;
 };
 BwdWs bwd_ws(int B, int L, int D, int N, int dtype, int dir) {
@@ -238,7 +238,6 @@ BwdWs bwd_ws(int B, int L, int D, int N, int dtype, int dir) {
     take(w.g1, BDL * 4);
     take(w.pq_tmp, entries * 16);
     take(w.pqb_tmp, entries * 8);
-    take(w.zeros, (size_t)D * 4);
     if (dir == HYENA_NONCAUSAL) take(w.dcf, BDL * 4);
   }
   w.total = off;
@@ -289,8 +288,9 @@ bool filter_bwd_params_ok(int K, int W) { return K >= 1 && K <= 32 && W >= 16 &&
 
 // Backward through the orders in the four-step regime, built on the forward's
 // four-step convolution: every convolution below is fourstep_conv on one order
-// with gates of one and skips of zero, its input in block 0 of tmp [B][2D][L]
-// (block 1 holds the ones). With R the reversal t -> L - 1 - t on [0, L), the
+// with no gate and no skip (plain: the last column pass writes h * z), its
+// input in block 0 of tmp [B][2D][L] (the layout of s with N = 1; block 1 is
+// not read). With R the reversal t -> L - 1 - t on [0, L), the
 // transposed convolution is R conv_h R (causal and two-sided filters alike: the
 // layer's spectra hold either), and the filter gradient
 // dh(tau) = sum_t dc(t) z(t - tau) is conv(R dc, z)(L - 1 - tau) for tau >= 0,
@@ -320,7 +320,8 @@ int bwd_fourstep(const hyena_layer* layer, const CacheLayout& cl, const BwdWs& w
   auto conv = [&](const void* in, int Bc, const float4* p, const void* pb, void* out) {
     hy::FourStepConvArgs a{};
     a.s = in;
-    a.dskip = reinterpret_cast<const float*>(wb + w.zeros);
+    a.dskip = nullptr;  // not read by the plain pass
+    a.plain = true;
     a.pq = p;
     a.pq_bf16 = pb;
     a.z[0] = a.z[1] = out;  // one order: only zfinal is written
@@ -334,8 +335,6 @@ int bwd_fourstep(const hyena_layer* layer, const CacheLayout& cl, const BwdWs& w
     a.group_pairs = group_pairs(Bc * half, (size_t)2 * L * (ybf ? 4 : 8));
     return hy::fourstep_conv(tb, a, bf, stream);
   };
-  HY_CHECK_HIP(hy::bwd4_fill(wb + w.zeros, 0.f, 1, D, D, false, stream));
-  HY_CHECK_HIP(hy::bwd4_fill(tmp + DL * es, 1.f, B, DL, 2 * DL, bf, stream));
   // forward orders, keeping z^n (fp32) and c^n (storage type)
   HY_CHECK_HIP(hy::bwd4_z_init(wb + w.s, zs, tmp, B, D, L, N, bf, stream));
   for (int n = 0; n < N; ++n) {

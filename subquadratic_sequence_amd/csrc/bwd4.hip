@@ -32,16 +32,6 @@ __device__ __forceinline__ void rev8(const float (&a)[8], float (&b)[8]) {
   for (int k = 0; k < 8; ++k) b[7 - k] = a[k];
 }
 
-template <typename T>
-__global__ __launch_bounds__(256) void bwd4_fill_kernel(T* __restrict__ p, float v, int rows, size_t len,
-                                                        size_t stride) {
-  const float vv[8] = {v, v, v, v, v, v, v, v};
-  FOR_CHUNKS(i, (size_t)rows * len) {
-    const size_t r = i / len;
-    st8(p + r * stride + (i - r * len), vv);
-  }
-}
-
 // i runs over [B][D][L]; r = d L + t is the offset inside a sample's D rows
 template <typename T>
 __global__ __launch_bounds__(256) void bwd4_z_init_kernel(const T* __restrict__ sp, float* __restrict__ zf,
@@ -204,16 +194,6 @@ __global__ __launch_bounds__(256) void bwd4_stage_rev_kernel(const float* __rest
 }
 
 }  // namespace
-
-hipError_t bwd4_fill(void* p, float v, int rows, size_t len, size_t stride, bool bf16, hipStream_t s) {
-  const size_t n = (size_t)rows * len;
-  if (bf16)
-    hipLaunchKernelGGL(bwd4_fill_kernel<hy::bf16>, dim3(grid_of(n)), dim3(256), 0, s, (hy::bf16*)p, v, rows, len,
-                       stride);
-  else
-    hipLaunchKernelGGL(bwd4_fill_kernel<float>, dim3(grid_of(n)), dim3(256), 0, s, (float*)p, v, rows, len, stride);
-  return hipGetLastError();
-}
 
 hipError_t bwd4_z_init(const void* sp, float* zf, void* tmp, int B, int D, int L, int NO, bool bf16, hipStream_t s) {
   const size_t n = (size_t)B * D * L;

@@ -165,8 +165,10 @@ struct ColArgs {
   int pair_off;           // global index of the first channel pair of this launch
 };
 
-// COL_FWD_HW: forward column pass of two-sided filters (wrapped rows of 2L, no zero half)
-enum { COL_FWD_V = 0, COL_FWD_H = 1, COL_INV = 2, COL_INV_FWD = 3, COL_FWD_HW = 4 };
+// COL_FWD_HW: forward column pass of two-sided filters (wrapped rows of 2L, no zero half);
+// COL_INV_PLAIN: inverse only, z^{n+1} = h * z^n with no gate and no skip (the
+// backward pass's one-order convolutions)
+enum { COL_FWD_V = 0, COL_FWD_H = 1, COL_INV = 2, COL_INV_FWD = 3, COL_FWD_HW = 4, COL_INV_PLAIN = 5 };
 
 __device__ __forceinline__ float2 cvt2(float2 v) { return v; }
 __device__ __forceinline__ float2 cvt2(cbf16 v) {
@@ -256,7 +258,8 @@ __device__ __forceinline__ void col_inverse(float2 (&u)[R], float2* S, const flo
 template <typename T, typename YT, int R, int MODE>
 __global__ __launch_bounds__(R * col_width<R>()) void colpass_kernel(ColArgs a, int nitems) {
   constexpr int N1 = R * R, H = R / 2;
-  constexpr bool INVERSE = (MODE == COL_INV || MODE == COL_INV_FWD);
+  constexpr bool INVERSE = (MODE == COL_INV || MODE == COL_INV_FWD || MODE == COL_INV_PLAIN);
+  constexpr bool GATE = INVERSE && MODE != COL_INV_PLAIN;
   constexpr bool FILT = (MODE == COL_FWD_H || MODE == COL_FWD_HW);
   constexpr int HF = MODE == COL_FWD_HW ? R : H;  // non-zero filter rows per thread
   constexpr int sT = (int)sizeof(T), sY = (int)sizeof(YT);
@@ -279,7 +282,7 @@ __global__ __launch_bounds__(R * col_width<R>()) void colpass_kernel(ColArgs a, 
 
   struct In {
     YT y[INVERSE ? R : 1];                    // inverse: column of the intermediate
-    T xa[INVERSE ? H : 1], xb[INVERSE ? H : 1];  // inverse: gates x^n
+    T xa[GATE ? H : 1], xb[GATE ? H : 1];     // inverse: gates x^n
     T za[H], zb[H];                           // z^n (forward of z^1: the v block)
     float ha[FILT ? HF : 1], hb[FILT ? HF : 1];  // filter modes
     float da, db;                             // inverse: skip weights D^n of the pair
@@ -335,7 +338,7 @@ __global__ __launch_bounds__(R * col_width<R>()) void colpass_kernel(ColArgs a, 
   };
   // second part (inverse modes): gate and skip inputs
   auto load_gate = [&](const Item& it, In& in) {
-    if constexpr (INVERSE) {
+    if constexpr (GATE) {
       const int b = it.pr / half, cp = it.pr % half;
       const int n = a.n;
       const brsrc rx = pair_rows(a.s, (size_t)b * J + (size_t)(n + 1) * D + 2 * cp, sT);
@@ -384,8 +387,13 @@ __global__ __launch_bounds__(R * col_width<R>()) void colpass_kernel(ColArgs a, 
       float na[H], nbv[H];
 #pragma unroll
       for (int nb = 0; nb < H; ++nb) {
-        na[nb] = cvt1(in.xa[nb]) * u[nb].x + in.da * cvt1(in.za[nb]);
-        nbv[nb] = cvt1(in.xb[nb]) * u[nb].y + in.db * cvt1(in.zb[nb]);
+        if constexpr (GATE) {
+          na[nb] = cvt1(in.xa[nb]) * u[nb].x + in.da * cvt1(in.za[nb]);
+          nbv[nb] = cvt1(in.xb[nb]) * u[nb].y + in.db * cvt1(in.zb[nb]);
+        } else {
+          na[nb] = u[nb].x;
+          nbv[nb] = u[nb].y;
+        }
       }
       load_gate(nt, in);
 #pragma unroll
@@ -1212,6 +1220,7 @@ static hipError_t launch_col_r(const ColArgs& a, int mode, int pairs, hipStream_
     case COL_FWD_H: return launch_col_t<float, float2, R, COL_FWD_H>(a, pairs, s);
     case COL_FWD_HW: return launch_col_t<float, float2, R, COL_FWD_HW>(a, pairs, s);
     case COL_INV: return launch_col_t<T, YT, R, COL_INV>(a, pairs, s);
+    case COL_INV_PLAIN: return launch_col_t<T, YT, R, COL_INV_PLAIN>(a, pairs, s);
     default: return launch_col_t<T, YT, R, COL_INV_FWD>(a, pairs, s);
   }
 }
@@ -1359,7 +1368,8 @@ hipError_t fourstep_conv(const FourStepTables& tb, const FourStepConvArgs& c, bo
       gi.n = n;
       gi.zin = (n == 0) ? nullptr : c.z[(n - 1) & 1];
       gi.zout = (n == c.NO - 1) ? c.zfinal : c.z[n & 1];
-      e = launch_col(gi, N1, (n == c.NO - 1) ? COL_INV : COL_INV_FWD, is_bf16, ybf, np, s);
+      e = launch_col(gi, N1, (n == c.NO - 1) ? (c.plain ? COL_INV_PLAIN : COL_INV) : COL_INV_FWD, is_bf16, ybf,
+                     np, s);
       if (e != hipSuccess) return e;
     }
   }

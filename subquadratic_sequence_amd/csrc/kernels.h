@@ -58,6 +58,9 @@ struct FourStepConvArgs {
   int B, L, D, NO;
   int group_pairs;       // channel pairs per group (0: all)
   bool y_bf16;           // bf16 workloads: keep the intermediate as bf16 pairs
+  // one order with no gate and no skip (NO = 1): z^2 = h * z^1; gates and
+  // dskip are not read
+  bool plain = false;
 };
 hipError_t fourstep_conv(const FourStepTables& tb, const FourStepConvArgs& c, bool bf16, hipStream_t s);
 // filter spectra into pq (fp32) and pq_bf16 (the same entries as four bf16);

@@ -2,7 +2,7 @@
 // four-step regime; short_conv_rows: bwd.hip).
 // Layouts: rows of L positions; s [B][(NO+1)D][L] and ds [B][(NO+1)D][L] in the
 // block order (v, x^1 .. x^NO); the staging buffer tmp [B][2D][L] holds a
-// convolution input in block 0 and ones in block 1. T is the storage type.
+// convolution input in block 0 (block 1 is not read). T is the storage type.
 #pragma once
 #include <hip/hip_runtime.h>
 
@@ -13,8 +13,6 @@ namespace hy {
 // p_{t-1} + w2 p_{t-2}, zero history (bwd.hip)
 hipError_t short_conv_rows(const void* p, const float* short_w, void* s_out, int rows, int L, int J, bool bf16,
                            hipStream_t s);
-// p[r * stride + i] = v for r < rows, i < len (fp32 or bf16 elements)
-hipError_t bwd4_fill(void* p, float v, int rows, size_t len, size_t stride, bool bf16, hipStream_t s);
 // z^1 = v block of s: zf [B][D][L] fp32 and tmp block 0 (storage type)
 hipError_t bwd4_z_init(const void* sp, float* zf, void* tmp, int B, int D, int L, int NO, bool bf16, hipStream_t s);
 // z^{n+1} = x^n c^n + D^n z^n from s block n+1, c (storage) and zf (fp32 z^n):
