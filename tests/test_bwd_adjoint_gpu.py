@@ -8,12 +8,13 @@ For every input and parameter P of the layer, the gradient g_P that hyena_bwd
 returns must give the directional derivative of phi = sum(dy * y) along a
 random direction V:  <g_P, V> = d/de phi(P + e V) at e = 0, which the test
 takes as a central difference of two hyena_fwd calls (through the C ABI).
-phi is a polynomial of degree at most three in each P (the operator is a
-product of projections, and linear in each filter and in the generator's last
-layer), so the central difference of step e is exact up to e^2 |phi'''| / 6,
-far below the bar at e = 1e-2 of P's scale; fp32 storage keeps the rounding
-noise of the two forwards small. A kernel that computes the wrong thing gives
-an error of order one.
+phi is a polynomial of degree at most three in each P but the generator's
+hidden weights w2 (the operator is a product of projections, linear in each
+filter and in the generator's last layer; w2 enters through sines), so the
+central difference of step e is exact up to e^2 |phi'''| / 6, far below the
+bar at e = 1e-2 of P's scale; fp32 storage keeps the rounding noise of the two
+forwards small. A kernel that computes the wrong thing gives an error of order
+one.
 
 Bar: |FD - <g_P, V>| <= 5e-3 max(|<g_P, V>|, |FD|) (measured: at most 6.2e-4)."""
 import numpy as np
