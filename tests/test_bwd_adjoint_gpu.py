@@ -35,14 +35,14 @@ def _phi(hs, torch, layer, t, dy, fp, K):
     return float(torch.sum(dy.double() * y.double()))
 
 
-@pytest.mark.parametrize("L,N", [(1 << 17, 2), (1 << 20, 1)])
-def test_bwd_directional_derivatives(L, N):
+@pytest.mark.parametrize("L,N,causal", [(1 << 17, 2, True), (1 << 20, 1, True), (1 << 17, 2, False)])
+def test_bwd_directional_derivatives(L, N, causal):
     import torch
     import subquadratic_sequence_amd as hs
-    inp = make_1d(790 + L // 4096 + N, 1, L, 64, N=N, K=8, dtype="f32")
-    say(f"bwd adjoint case B=1 L={L} D=64 N={N} f32 seed={inp.meta['seed']}")
+    inp = make_1d(790 + L // 4096 + N, 1, L, 64, N=N, K=8, dtype="f32", causal=causal)
+    say(f"bwd adjoint case B=1 L={L} D=64 N={N} f32 causal={causal} seed={inp.meta['seed']}")
     rng = np.random.default_rng(17)
-    layer = hs.HyenaLayer(inp.L, inp.D, inp.N)
+    layer = hs.HyenaLayer(inp.L, inp.D, inp.N, direction=hs.CAUSAL if causal else hs.NONCAUSAL)
     t = {k: to_dev(getattr(inp, k)) for k in ("u", "w_in", "short_w", "dskip", "w_out")}
     fnames = ("w1", "b1", "w2", "b2", "w3", "b3", "decay")
     fp = [to_dev(getattr(inp, k)) for k in fnames]
