@@ -668,6 +668,10 @@ def main():
     if not args.no_cpu_baseline:
         log("cpu baseline (oracle)")
         out["cpu_baseline"] = cpu_baseline(inp, args.cpu_tokens or inp.L, cpu_workers(args.cpu_workers))
+        # the same oracle on one thread, on a prefix with about the same work
+        one = cpu_baseline(inp, min(inp.L, 4096), 1)
+        out["cpu_baseline"]["one_thread"] = {"value": one["value"], "unit": one["unit"], "cores": 1,
+                                             "sample": one["sample"]}
     print(json.dumps(out), flush=True)
 
 
